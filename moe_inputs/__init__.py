@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the MoE layer: the one module shared by the
+HIP path's tests/benchmark and the CPU oracle.
+
+It holds workload shapes and random draws only (no routing, no FFN, no
+reduction: none of the method's arithmetic). Every tensor comes from its own
+counter-addressed numpy PCG64 stream, ``SeedSequence(seed, spawn_key=(slot,
+index))``, so any one tensor (or one expert's weights) can be regenerated
+alone and shapes never shift other tensors' draws.
+
+Distributions (the workload presets below):
+  x ~ N(0, 1); router weight W_r ~ N(0, 0.02^2) in fp32; expert weights
+  ~ N(0, 1/fan_in) (std 1/sqrt(fan_in), fan_in = d for the gate/up/first
+  matrix and f for the down matrix); selection bias b ~ U(-0.01, 0.01);
+  upstream gradient dY ~ N(0, 1).  bf16 tensors are drawn in fp32 and
+  rounded once, round-to-nearest-even, to bf16; both sides consume the same
+  bits.
+
+Workloads (the five layer shapes benchmarked and parity-tested):
+  tiny_fp32        T=256  d=128  E=8   k=2 softmax, SwiGLU f=256, fp32
+  mixtral_bf16     T=8192 d=4096 E=8   k=2 softmax, SwiGLU f=14336, cf 1.25
+  skewed_bf16      T=4096 d=4096 E=8   k=2 softmax + logit bias +2 on experts
+                   0 and 3, GELU two-matrix f=16384, cf 1.0 or none
+  finegrained_bf16 T=16384 d=4096 E=128 k=8 softmax, SwiGLU f=1536, aux stats
+                   with coefficient 0.01
+  dsv3_bf16        T=8192 d=7168 E=256 k=8 sigmoid + selection bias, one shared
+                   expert, SwiGLU f=2048
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+# stream slots of SeedSequence(seed, spawn_key=(slot, index))
+_SLOT_X, _SLOT_WR, _SLOT_SEL, _SLOT_DY, _SLOT_W13, _SLOT_W2, _SLOT_SW13, _SLOT_SW2 = range(8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    dtype: str = "bf16"           # "bf16" or "fp32": x, expert weights, Y, dY, dX, dW
+    score: str = "softmax"        # "softmax" or "sigmoid"
+    act: str = "swiglu"           # "swiglu" or "gelu"
+    n_shared: int = 0             # always-on shared experts (0 or 1)
+    cf: Optional[float] = None    # capacity factor; None = no capacity limit
+    logit_bias: Optional[dict] = None   # {expert: value} added to router logits
+    sel_bias: bool = False        # draw a per-expert selection bias b ~ U(-0.01, 0.01)
+    aux_coef: float = 0.0         # weight of the load-balance loss in the backward
+    seed: int = 0
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", T=256, d=128, E=8, k=2, f=256, dtype="fp32"),
+    "mixtral_bf16": Workload("mixtral_bf16", T=8192, d=4096, E=8, k=2, f=14336, cf=1.25),
+    "skewed_bf16": Workload("skewed_bf16", T=4096, d=4096, E=8, k=2, f=16384, act="gelu",
+                            cf=1.0, logit_bias={0: 2.0, 3: 2.0}),
+    "skewed_nocap_bf16": Workload("skewed_nocap_bf16", T=4096, d=4096, E=8, k=2, f=16384,
+                                  act="gelu", cf=None, logit_bias={0: 2.0, 3: 2.0}),
+    "finegrained_bf16": Workload("finegrained_bf16", T=16384, d=4096, E=128, k=8, f=1536,
+                                 aux_coef=0.01),
+    "dsv3_bf16": Workload("dsv3_bf16", T=8192, d=7168, E=256, k=8, f=2048, score="sigmoid",
+                          n_shared=1, sel_bias=True),
+}
+
+
+# ---------------------------------------------------------------- bf16 bits
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+    Inputs here are finite normal draws, so no NaN handling is needed."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, slot: int, index: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(slot, index))))
+
+
+def _normal(seed, slot, index, shape, std, dtype):
+    g = _rng(seed, slot, index)
+    v = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    return to_bf16_bits(v) if dtype == "bf16" else v
+
+
+# ------------------------------------------------------------- tensor draws
+def gen_x(w: Workload, T: Optional[int] = None) -> np.ndarray:
+    return _normal(w.seed, _SLOT_X, 0, (T or w.T, w.d), 1.0, w.dtype)
+
+
+def gen_dy(w: Workload, T: Optional[int] = None) -> np.ndarray:
+    return _normal(w.seed, _SLOT_DY, 0, (T or w.T, w.d), 1.0, w.dtype)
+
+
+def gen_router_weight(w: Workload) -> np.ndarray:
+    g = _rng(w.seed, _SLOT_WR)
+    return (g.standard_normal(size=(w.E, w.d), dtype=np.float32) * np.float32(0.02))
+
+
+def gen_logit_bias(w: Workload) -> Optional[np.ndarray]:
+    if not w.logit_bias:
+        return None
+    b = np.zeros(w.E, dtype=np.float32)
+    for e, v in w.logit_bias.items():
+        b[e] = v
+    return b
+
+
+def gen_sel_bias(w: Workload) -> Optional[np.ndarray]:
+    if not w.sel_bias:
+        return None
+    return _rng(w.seed, _SLOT_SEL).uniform(-0.01, 0.01, size=w.E).astype(np.float32)
+
+
+def first_matrix_rows(w: Workload) -> int:
+    """Rows of one expert's first weight: gate and up stacked (2f) for SwiGLU, f for GELU."""
+    return 2 * w.f if w.act == "swiglu" else w.f
+
+
+def gen_expert_w13(w: Workload, e: int, shared: bool = False) -> np.ndarray:
+    """One expert's first weight, [2f, d] (rows [0,f) gate, [f,2f) up) or [f, d]."""
+    slot = _SLOT_SW13 if shared else _SLOT_W13
+    return _normal(w.seed, slot, e, (first_matrix_rows(w), w.d), 1.0 / np.sqrt(w.d), w.dtype)
+
+
+def gen_expert_w2(w: Workload, e: int, shared: bool = False) -> np.ndarray:
+    """One expert's down weight, [d, f]."""
+    slot = _SLOT_SW2 if shared else _SLOT_W2
+    return _normal(w.seed, slot, e, (w.d, w.f), 1.0 / np.sqrt(w.f), w.dtype)
+
+
+def _stack(fn, w: Workload, n: int, shared: bool, threads: Optional[int]) -> np.ndarray:
+    first = fn(w, 0, shared)
+    out = np.empty((n,) + first.shape, dtype=first.dtype)
+    out[0] = first
+    if n > 1:
+        nt = threads or min(16, os.cpu_count() or 1)
+
+        def fill(e):
+            out[e] = fn(w, e, shared)
+
+        with ThreadPoolExecutor(max_workers=nt) as ex:
+            list(ex.map(fill, range(1, n)))
+    return out
+
+
+def gen_w13(w: Workload, threads: Optional[int] = None) -> np.ndarray:
+    return _stack(gen_expert_w13, w, w.E, False, threads)
+
+
+def gen_w2(w: Workload, threads: Optional[int] = None) -> np.ndarray:
+    return _stack(gen_expert_w2, w, w.E, False, threads)
+
+
+def gen_shared_w13(w: Workload) -> Optional[np.ndarray]:
+    return _stack(gen_expert_w13, w, w.n_shared, True, 1) if w.n_shared else None
+
+
+def gen_shared_w2(w: Workload) -> Optional[np.ndarray]:
+    return _stack(gen_expert_w2, w, w.n_shared, True, 1) if w.n_shared else None
+
+
+def gen_all(w: Workload, threads: Optional[int] = None) -> dict:
+    """Every input of one layer fwd+bwd, as numpy arrays (bf16 as uint16 bits)."""
+    return dict(
+        x=gen_x(w), w_r=gen_router_weight(w), logit_bias=gen_logit_bias(w),
+        sel_bias=gen_sel_bias(w), w13=gen_w13(w, threads), w2=gen_w2(w, threads),
+        sw13=gen_shared_w13(w), sw2=gen_shared_w2(w), dy=gen_dy(w),
+    )
+
+
+def as_f64(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    """Exact float64 values of a drawn tensor (bf16 bits or fp32)."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)

@@ -1,0 +1,368 @@
+"""CPU oracle of one Mixture-of-Experts layer, forward and backward.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+CPU-baseline leg may import or call this module. It shares no code with the
+HIP library (no kernels, headers, helpers or constants): it is the method's
+plain definition, written out in float64 NumPy so that a reader can check it
+against the pages by eye. No blocking, fusion or reordering beyond what each
+step states.
+
+Pages cited (titles as printed on them):
+  [Recipe]  "MoE 训练加速实战：DeepEP + Grouped GeMM + Aux-Loss-Free 的 Qwen3.5 配方"
+  [Balance] "负载均衡策略：MoE训练稳定性保障"
+  [ETP]     "ETP专家并行加速MoE模型：ms-swift中稀疏架构的极致优化"
+  [VPP]     "MoE模型训练加速10倍？看ms-swift如何通过ETP和VPP实现突破"
+
+Readings taken where the pages are silent, garbled or disagree are listed in
+the repository's design notes; each function names the one it uses.
+
+Parity pins: every public function here is pinned by tests/test_oracle_pins.py
+against a dense brute force, closed forms, invariants, central finite
+differences or the worked capacity example of [Balance]; none is unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+from scipy.special import erf
+
+NEAR_TIE = 1e-5   # fp32 score gap under which two ranks count as a near-tie
+
+
+# ------------------------------------------------------------------ router
+def router_forward(x, w_r, k, score="softmax", logit_bias=None, sel_bias=None):
+    """Router of [Recipe] §2.2: g(x) = x W_r, scores = softmax(g), top-k,
+    gate weights renormalised over the chosen k.
+
+    x [T, d], w_r [E, d] (stored out x in, so g = x w_r^T), optional
+    logit_bias [E] added to the logits (a fixed shift: it moves both the
+    choice and the gate values), optional sel_bias [E] added to the scores for
+    the choice only ([Recipe] §5.3, the aux-loss-free bias: b takes no gradient
+    and only steers top-k; the gates use the unbiased scores).
+    score="sigmoid" replaces softmax by an elementwise logistic.
+
+    Top-k orders experts by (key descending, expert index ascending) and keeps
+    the first k in that rank order.
+    Returns dict(logits, scores, key, topk_idx [T,k] int64, gates [T,k]).
+    """
+    logits = x @ w_r.T
+    if logit_bias is not None:
+        logits = logits + logit_bias[None, :]
+    if score == "softmax":
+        # max-subtracted so exp never overflows ([Recipe] §1: fp32 router against 0/0)
+        m = logits.max(axis=1, keepdims=True)
+        ex = np.exp(logits - m)
+        scores = ex / ex.sum(axis=1, keepdims=True)
+    elif score == "sigmoid":
+        scores = 1.0 / (1.0 + np.exp(-logits))
+    else:
+        raise ValueError(score)
+    key = scores + sel_bias[None, :] if sel_bias is not None else scores
+    # stable sort on -key: equal keys keep ascending expert index
+    order = np.argsort(-key, axis=1, kind="stable")
+    topk_idx = order[:, :k]
+    chosen = np.take_along_axis(scores, topk_idx, axis=1)
+    gates = chosen / chosen.sum(axis=1, keepdims=True)
+    return dict(logits=logits, scores=scores, key=key, topk_idx=topk_idx, gates=gates)
+
+
+def near_tie_tokens(key, k, thresh=NEAR_TIE):
+    """Tokens whose top-(k+1) keys hold an adjacent pair closer than thresh:
+    there the fp32 router may legitimately order experts differently."""
+    E = key.shape[1]
+    srt = -np.sort(-key, axis=1)[:, : min(k + 1, E)]
+    if srt.shape[1] < 2:
+        return np.zeros(key.shape[0], dtype=bool)
+    return (np.abs(np.diff(srt, axis=1)) < thresh).any(axis=1)
+
+
+# --------------------------------------------------------------- aux stats
+def aux_stats(scores, topk_idx, E):
+    """Load-balance statistics of [Balance] (辅助损失函数) and [Recipe] §5.2.
+
+    counts_i = assignments routed to expert i (before any capacity drop);
+    y_i = counts_i / (T k), the fraction of routed assignments (sums to 1);
+    z_i = mean over tokens of expert i's score (full pre-top-k scores);
+    S = sum_i y_i z_i;  L_aux = E * S (the [Recipe] §5.2 normalisation,
+    equal to 1 at uniform load). [Balance]'s own constant (N/E) * S with
+    N = tokens is S times T/E, formed by the caller from S.
+    """
+    T, k = topk_idx.shape
+    counts = np.bincount(topk_idx.ravel(), minlength=E).astype(np.int64)
+    y = counts / float(T * k)
+    z = scores.mean(axis=0)
+    S = float((y * z).sum())
+    return dict(counts=counts, y=y, z=z, S=S, L_aux=E * S)
+
+
+# ---------------------------------------------------------------- capacity
+def capacity(T, k, E, cf):
+    """Per-expert token limit of [Balance] (专家容量裁剪): capacity_factor
+    times the ideal load T k / E, rounded up. cf None -> no limit.
+    The product is evaluated left to right in binary64: ((cf*T)*k)/E."""
+    if cf is None:
+        return None
+    return int(math.ceil(cf * T * k / E))
+
+
+# ----------------------------------------------------------------- permute
+def permute(topk_idx, E, cap=None):
+    """Local dispatch: sort assignments into expert-contiguous rows
+    ([Balance] 负载感知调度: tokens pre-sorted by destination before the
+    exchange; [Recipe] §3.2 dispatch). Within an expert, rows follow token
+    order. With a capacity, an assignment is kept when fewer than `cap`
+    earlier tokens were already routed to the same expert; the rest are
+    dropped ([Balance] 专家容量裁剪).
+
+    Returns dict(offsets [E+1], row_of [T,k] (-1 = dropped), token_of [A],
+    n_dropped). x_perm = x[token_of].
+    """
+    T, k = topk_idx.shape
+    seen = [0] * E
+    kept = [[] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            e = int(topk_idx[t, j])
+            rank = seen[e]
+            seen[e] += 1
+            if cap is None or rank < cap:
+                kept[e].append((t, j))
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + len(kept[e])
+    A = int(offsets[E])
+    row_of = -np.ones((T, k), dtype=np.int64)
+    token_of = np.zeros(A, dtype=np.int64)
+    for e in range(E):
+        for i, (t, j) in enumerate(kept[e]):
+            row_of[t, j] = offsets[e] + i
+            token_of[offsets[e] + i] = t
+    return dict(offsets=offsets, row_of=row_of, token_of=token_of, n_dropped=T * k - A)
+
+
+# ------------------------------------------------------------- expert FFN
+def silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def dsilu(a):
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def gelu(a):
+    """Exact (erf) GELU."""
+    return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+
+
+def dgelu(a):
+    cdf = 0.5 * (1.0 + erf(a / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * a * a) / math.sqrt(2.0 * math.pi)
+    return cdf + a * pdf
+
+
+def expert_forward(X, w13, w2, act):
+    """One expert's two-matrix FFN ([ETP]: up-projection w1 then down-projection
+    w2). SwiGLU: H = silu(X W1^T) * (X W3^T), with w13 = [W1; W3] stacked
+    [2f, d]; GELU: H = gelu(X W1^T), w13 = W1 [f, d]. Output O = H W2^T,
+    w2 [d, f]. Returns (O, saved) with the pre-activations and H kept for
+    the backward."""
+    f = w2.shape[1]
+    if act == "swiglu":
+        ab = X @ w13.T
+        a, b = ab[:, :f], ab[:, f:]
+        H = silu(a) * b
+        saved = dict(a=a, b=b, H=H)
+    elif act == "gelu":
+        a = X @ w13.T
+        H = gelu(a)
+        saved = dict(a=a, H=H)
+    else:
+        raise ValueError(act)
+    return H @ w2.T, saved
+
+
+def expert_backward(X, w13, w2, saved, dO, act):
+    """Backward of expert_forward for upstream dO [n, d].
+    Returns (dX [n,d], dw13 (w13's shape), dw2 [d,f], dpre (gradient of the
+    pre-activations, [n, 2f] or [n, f]))."""
+    H = saved["H"]
+    a = saved["a"]
+    dH = dO @ w2                      # [n, f]
+    if act == "swiglu":
+        b = saved["b"]
+        da = dH * b * dsilu(a)
+        db = dH * silu(a)
+        dpre = np.concatenate([da, db], axis=1)
+    else:
+        dpre = dH * dgelu(a)
+    dX = dpre @ w13
+    dw2 = dO.T @ H
+    dw13 = dpre.T @ X
+    return dX, dw13, dw2, dpre
+
+
+def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None):
+    """Grouped GEMM of [Recipe] §4.2: the same result as running every
+    expert's GEMMs on its own contiguous rows. Optional shared experts
+    ([Recipe] §2.3 / §9.1: an expert every token passes through) read all of
+    x. Returns (O [A,d], Os [T,d] or None, saved)."""
+    E = w13.shape[0]
+    A = int(offsets[E])
+    d = w2.shape[1]
+    O = np.zeros((A, d))
+    saved = []
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        o, s = expert_forward(x_perm[lo:hi], w13[e], w2[e], act)
+        O[lo:hi] = o
+        saved.append(s)
+    Os, ssaved = None, []
+    if sw13 is not None:
+        Os = np.zeros((x.shape[0], d))
+        for s in range(sw13.shape[0]):
+            o, sv = expert_forward(x, sw13[s], sw2[s], act)
+            Os += o
+            ssaved.append(sv)
+    return O, Os, dict(routed=saved, shared=ssaved)
+
+
+def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=None,
+                         sw2=None, dY=None):
+    """Backward of grouped_ffn_forward: per-expert dgrad and wgrad.
+    The shared expert's upstream gradient is dY itself (gate 1)."""
+    E = w13.shape[0]
+    dX_perm = np.zeros_like(x_perm)
+    dw13 = np.zeros_like(w13)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        dx, g13, g2, _ = expert_backward(x_perm[lo:hi], w13[e], w2[e], saved["routed"][e],
+                                         dO[lo:hi], act)
+        dX_perm[lo:hi] = dx
+        dw13[e] = g13
+        dw2[e] = g2
+    dXs = dsw13 = dsw2 = None
+    if sw13 is not None:
+        dXs = np.zeros_like(x)
+        dsw13 = np.zeros_like(sw13)
+        dsw2 = np.zeros_like(sw2)
+        for s in range(sw13.shape[0]):
+            dx, g13, g2, _ = expert_backward(x, sw13[s], sw2[s], saved["shared"][s], dY, act)
+            dXs += dx
+            dsw13[s] = g13
+            dsw2[s] = g2
+    return dict(dx_perm=dX_perm, dw13=dw13, dw2=dw2, dx_shared=dXs, dsw13=dsw13, dsw2=dsw2)
+
+
+# ----------------------------------------------------------------- combine
+def combine(O, gates, row_of, Os=None):
+    """Weighted sum of [Recipe] §2.1/§2.2: Y[t] = Os[t] + sum over kept slots
+    j of g_tj * O[row(t,j)]. A dropped slot adds nothing (no renormalisation)."""
+    T, k = row_of.shape
+    Y = np.zeros((T, O.shape[1])) if Os is None else Os.copy()
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                Y[t] += gates[t, j] * O[r]
+    return Y
+
+
+def combine_backward(dY, O, gates, row_of):
+    """dgate_tj = <dY[t], O[row(t,j)]> (0 if dropped); dO[row(t,j)] = g_tj dY[t]."""
+    T, k = row_of.shape
+    dgate = np.zeros((T, k))
+    dO = np.zeros_like(O)
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                dgate[t, j] = float(dY[t] @ O[r])
+                dO[r] = gates[t, j] * dY[t]
+    return dgate, dO
+
+
+# ---------------------------------------------------------- router backward
+def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux_coef=0.0,
+                    y=None):
+    """Gradient of the router through the renormalised gates of [Recipe] §2.2
+    (the top-k choice itself is piecewise constant), plus aux_coef times the
+    gradient of L_aux = E sum_i y_i z_i with the counts y held fixed.
+
+    Softmax: the renormalised gates equal a softmax over the chosen logits,
+      dl_e = g_e (dg_e - sum_j g_j dg_j) for chosen e, 0 otherwise.
+    Sigmoid: g_j = s_j / sum_S s,
+      dl_e = s_e (1 - s_e) (dg_e - sum_j g_j dg_j) / sum_S s for chosen e.
+    Aux (z_i = mean_t s_ti):
+      softmax: dl_te += aux_coef (E/T) s_te (y_e - sum_i y_i s_ti)
+      sigmoid: dl_te += aux_coef (E/T) y_e s_te (1 - s_te)
+    Returns dict(dlogits [T,E], dw_r [E,d] = dl^T x, dx_router [T,d] = dl W_r).
+    """
+    T, E = scores.shape
+    k = topk_idx.shape[1]
+    dl = np.zeros((T, E))
+    for t in range(T):
+        sel = topk_idx[t]
+        g = gates[t]
+        dg = dgate[t]
+        inner = float((g * dg).sum())
+        if score == "softmax":
+            dl[t, sel] = g * (dg - inner)
+        else:
+            s = scores[t, sel]
+            dl[t, sel] = s * (1.0 - s) * (dg - inner) / s.sum()
+    if aux_coef != 0.0:
+        if score == "softmax":
+            ys = scores @ y
+            dl += aux_coef * (E / T) * scores * (y[None, :] - ys[:, None])
+        else:
+            dl += aux_coef * (E / T) * y[None, :] * scores * (1.0 - scores)
+    return dict(dlogits=dl, dw_r=dl.T @ x, dx_router=dl @ w_r)
+
+
+def permute_backward(dx_perm, row_of, dx_shared=None, dx_router=None):
+    """Un-permute: dX[t] = dXs[t] + sum over kept j of dX_perm[row(t,j)] + dx_router[t]."""
+    T, k = row_of.shape
+    dX = np.zeros((T, dx_perm.shape[1]))
+    if dx_shared is not None:
+        dX += dx_shared
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                dX[t] += dx_perm[r]
+    if dx_router is not None:
+        dX += dx_router
+    return dX
+
+
+# ------------------------------------------------------------- whole layer
+def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
+                  logit_bias=None, sel_bias=None, sw13=None, sw2=None):
+    """Forward of the layer: router, stats, permute, grouped FFN, combine.
+    All arrays float64 (exact values of the fp32/bf16 inputs)."""
+    E = w13.shape[0]
+    r = router_forward(x, w_r, k, score, logit_bias, sel_bias)
+    st = aux_stats(r["scores"], r["topk_idx"], E)
+    p = permute(r["topk_idx"], E, cap)
+    x_perm = x[p["token_of"]]
+    O, Os, saved = grouped_ffn_forward(x_perm, p["offsets"], w13, w2, act, x, sw13, sw2)
+    Y = combine(O, r["gates"], p["row_of"], Os)
+    return dict(router=r, stats=st, perm=p, x_perm=x_perm, O=O, Os=Os, saved=saved, Y=Y)
+
+
+def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
+                   sw13=None, sw2=None):
+    """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
+    router bwd, un-permute."""
+    r, p = fwd["router"], fwd["perm"]
+    dgate, dO = combine_backward(dY, fwd["O"], r["gates"], p["row_of"])
+    g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
+                             sw13, sw2, dY)
+    rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
+                         aux_coef, fwd["stats"]["y"])
+    dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])
+    return dict(dgate=dgate, dO=dO, dX=dX, **g, **rb)

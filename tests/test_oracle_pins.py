@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* a dense brute force (every expert run on every token, then masked by an
+  independently computed routing and weighted by closed-form gates);
+* closed forms (zero router weight, k = E, E = k = 1 textbook FFN via torch,
+  identical experts, shared expert alone);
+* invariants (gates sum to 1, counts sum to T k, permutation bijection,
+  un-permute of permute);
+* the worked capacity example and the uniform top-2 ratio printed on the
+  pages (tests/golden);
+* central finite differences of a scalar loss for every gradient.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import scipy.stats as sst
+import torch
+
+import oracle as O
+from moe_inputs import Workload, gen_all, as_f64, to_bf16_bits, bf16_bits_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _tiny(T=24, d=16, E=6, k=2, f=12, **kw):
+    w = Workload("t", T=T, d=d, E=E, k=k, f=f, dtype="fp32", **kw)
+    g = gen_all(w)
+    conv = {n: as_f64(v, w.dtype) for n, v in g.items()}
+    return w, conv
+
+
+# --------------------------------------------------------------- brute force
+def _brute_select(key, k):
+    """Per token: repeatedly take the largest key, lowest index on equal keys."""
+    T, E = key.shape
+    idx = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        remaining = list(range(E))
+        for j in range(k):
+            best = remaining[0]
+            for e in remaining[1:]:
+                if key[t, e] > key[t, best]:
+                    best = e
+            idx[t, j] = best
+            remaining.remove(best)
+    return idx
+
+
+def _brute_ffn(x, w13, w2, act):
+    f = w2.shape[1]
+    if act == "swiglu":
+        g = np.einsum("td,fd->tf", x, w13[:f])
+        u = np.einsum("td,fd->tf", x, w13[f:])
+        h = g * sps.expit(g) * u
+    else:
+        a = np.einsum("td,fd->tf", x, w13)
+        h = a * sst.norm.cdf(a)
+    return np.einsum("tf,df->td", h, w2)
+
+
+def brute_layer(x, w_r, w13, w2, k, score, act, cap, logit_bias=None, sel_bias=None,
+                sw13=None, sw2=None):
+    T = x.shape[0]
+    E = w13.shape[0]
+    logits = np.einsum("td,ed->te", x, w_r)
+    if logit_bias is not None:
+        logits = logits + logit_bias
+    scores = sps.softmax(logits, axis=1) if score == "softmax" else sps.expit(logits)
+    key = scores + (sel_bias if sel_bias is not None else 0.0)
+    idx = _brute_select(key, k)
+    sel = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(sel, idx, True, axis=1)
+    gate = np.zeros((T, E))
+    for t in range(T):
+        ch = idx[t]
+        if score == "softmax":   # renormalised softmax top-k == softmax over chosen logits
+            gate[t, ch] = np.exp(logits[t, ch] - sps.logsumexp(logits[t, ch]))
+        else:
+            gate[t, ch] = scores[t, ch] / scores[t, ch].sum()
+    earlier = np.cumsum(sel, axis=0) - sel          # tokens before t routed to e
+    kept = sel if cap is None else sel & (earlier < cap)
+    Y = np.zeros_like(x)
+    for e in range(E):
+        Y += (kept[:, e] * gate[:, e])[:, None] * _brute_ffn(x, w13[e], w2[e], act)
+    if sw13 is not None:
+        for s in range(sw13.shape[0]):
+            Y += _brute_ffn(x, sw13[s], sw2[s], act)
+    return dict(Y=Y, idx=idx, kept=kept, scores=scores)
+
+
+VARIANTS = [
+    dict(score="softmax", act="swiglu", cf=None),
+    dict(score="softmax", act="gelu", cf=None),
+    dict(score="softmax", act="swiglu", cf=0.75),
+    dict(score="softmax", act="gelu", cf=1.0, logit_bias={0: 2.0, 3: 2.0}),
+    dict(score="sigmoid", act="swiglu", cf=None, sel_bias=True, n_shared=1),
+    dict(score="softmax", act="swiglu", cf=1.25, n_shared=1),
+]
+
+
+@pytest.mark.parametrize("var", VARIANTS)
+def test_sparse_oracle_equals_dense_brute_force(var):
+    w, g = _tiny(T=40, d=16, E=6, k=2, f=12, **var)
+    cap = O.capacity(w.T, w.k, w.E, w.cf)
+    fwd = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], w.k, w.score, w.act, cap,
+                          g["logit_bias"], g["sel_bias"], g["sw13"], g["sw2"])
+    bf = brute_layer(g["x"], g["w_r"], g["w13"], g["w2"], w.k, w.score, w.act, cap,
+                     g["logit_bias"], g["sel_bias"], g["sw13"], g["sw2"])
+    np.testing.assert_array_equal(fwd["router"]["topk_idx"], bf["idx"])
+    np.testing.assert_allclose(fwd["router"]["scores"], bf["scores"], rtol=1e-13, atol=1e-15)
+    kept_o = np.zeros_like(bf["kept"])
+    for t in range(w.T):
+        for j in range(w.k):
+            if fwd["perm"]["row_of"][t, j] >= 0:
+                kept_o[t, fwd["router"]["topk_idx"][t, j]] = True
+    np.testing.assert_array_equal(kept_o, bf["kept"])
+    np.testing.assert_allclose(fwd["Y"], bf["Y"], rtol=1e-11, atol=1e-12)
+
+
+def test_tiny_fp32_workload_full_size_brute_force():
+    """The whole tiny fp32 workload (T=256, d=128, E=8, k=2, f=256)."""
+    from moe_inputs import WORKLOADS
+    w = WORKLOADS["tiny_fp32"]
+    g = {n: as_f64(v, w.dtype) for n, v in gen_all(w).items()}
+    fwd = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], w.k, w.score, w.act, None)
+    bf = brute_layer(g["x"], g["w_r"], g["w13"], g["w2"], w.k, w.score, w.act, None)
+    np.testing.assert_array_equal(fwd["router"]["topk_idx"], bf["idx"])
+    np.testing.assert_allclose(fwd["Y"], bf["Y"], rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+def test_zero_router_weight_tie_break_and_stats():
+    w, g = _tiny(T=10, E=5, k=3)
+    r = O.router_forward(g["x"], np.zeros_like(g["w_r"]), w.k)
+    assert (r["topk_idx"] == np.arange(3)[None, :]).all()
+    np.testing.assert_allclose(r["gates"], 1.0 / 3.0, rtol=0, atol=1e-15)
+    st = O.aux_stats(r["scores"], r["topk_idx"], w.E)
+    np.testing.assert_allclose(st["z"], 1.0 / w.E, rtol=1e-15)
+    np.testing.assert_allclose(st["y"], [1 / 3, 1 / 3, 1 / 3, 0, 0], rtol=1e-15)
+    assert abs(st["S"] - 1.0 / w.E) < 1e-15 and abs(st["L_aux"] - 1.0) < 1e-14
+
+
+def test_k_equals_E_gives_full_softmax():
+    w, g = _tiny(T=12, E=5, k=5)
+    r = O.router_forward(g["x"], g["w_r"], 5)
+    full = sps.softmax(g["x"] @ g["w_r"].T, axis=1)
+    np.testing.assert_allclose(np.take_along_axis(full, r["topk_idx"], 1), r["gates"], rtol=1e-13)
+    assert (np.diff(np.take_along_axis(full, r["topk_idx"], 1), axis=1) <= 0).all()
+
+
+def test_uniform_counts_give_unit_aux_loss():
+    T, E, k = 64, 8, 2
+    idx = np.stack([(np.arange(T) * k + j) % E for j in range(k)], axis=1)
+    rng = np.random.default_rng(3)
+    scores = sps.softmax(rng.standard_normal((T, E)), axis=1)
+    st = O.aux_stats(scores, idx, E)
+    np.testing.assert_array_equal(st["counts"], np.full(E, T * k // E))
+    assert abs(st["L_aux"] - 1.0) < 1e-14
+
+
+def test_golden_uniform_top2_ratio():
+    (T, k, E, want), = _read_golden("uniform_top2_ratio.txt")
+    T, k, E, want = int(T), int(k), int(E), float(want)
+    idx = np.stack([(np.arange(T) * k + j) % E for j in range(k)], axis=1)
+    st = O.aux_stats(np.full((T, E), 1.0 / E), idx, E)
+    assert abs(np.sort(st["y"])[-2:].sum() - want) < 1e-15
+    assert abs(st["y"].sum() - 1.0) < 1e-15
+
+
+def test_hand_computed_aux_stats():
+    # T=4, E=2, k=1: tokens 0,1,2 -> expert 0, token 3 -> expert 1
+    scores = np.array([[0.9, 0.1], [0.6, 0.4], [0.7, 0.3], [0.2, 0.8]])
+    idx = np.array([[0], [0], [0], [1]])
+    st = O.aux_stats(scores, idx, 2)
+    assert list(st["counts"]) == [3, 1]
+    np.testing.assert_allclose(st["y"], [0.75, 0.25])
+    np.testing.assert_allclose(st["z"], [0.6, 0.4])
+    assert abs(st["S"] - (0.75 * 0.6 + 0.25 * 0.4)) < 1e-15
+    assert abs(st["L_aux"] - 2 * 0.55) < 1e-15
+
+
+def test_golden_capacity_worked_example():
+    (T, k, E, cf, ideal, capv), = _read_golden("capacity_worked_example.txt")
+    T, k, E, cf, ideal, capv = int(T), int(k), int(E), float(cf), int(ideal), int(capv)
+    assert T * k // E == ideal
+    assert O.capacity(T, k, E, cf) == capv
+    assert O.capacity(T, k, E, None) is None
+
+
+def test_capacity_keeps_first_tokens_when_all_go_to_one_expert():
+    T, E, k, cap = 50, 4, 1, 7
+    idx = np.full((T, k), 2)
+    p = O.permute(idx, E, cap)
+    assert list(p["offsets"]) == [0, 0, 0, cap, cap]
+    assert list(p["token_of"]) == list(range(cap))
+    assert (p["row_of"][:cap, 0] == np.arange(cap)).all() and (p["row_of"][cap:] == -1).all()
+    assert p["n_dropped"] == T - cap
+
+
+def test_capacity_zero_drops_everything():
+    idx = np.array([[0, 1], [1, 2], [2, 0]])
+    p = O.permute(idx, 3, 0)
+    assert (p["row_of"] == -1).all() and p["n_dropped"] == 6 and p["offsets"][-1] == 0
+
+
+def _torch_ffn(x, w13, w2, act):
+    xt, a, b = torch.from_numpy(x), torch.from_numpy(w13), torch.from_numpy(w2)
+    f = w2.shape[1]
+    if act == "swiglu":
+        h = torch.nn.functional.silu(xt @ a[:f].T) * (xt @ a[f:].T)
+    else:
+        h = torch.nn.functional.gelu(xt @ a.T, approximate="none")
+    return (h @ b.T).numpy()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_single_expert_is_textbook_ffn(act):
+    w, g = _tiny(T=9, E=1, k=1, act=act)
+    fwd = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], 1, act=act)
+    np.testing.assert_allclose(fwd["Y"], _torch_ffn(g["x"], g["w13"][0], g["w2"][0], act),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_identical_experts_give_plain_ffn():
+    w, g = _tiny(T=20, E=5, k=3)
+    w13 = np.repeat(g["w13"][:1], 5, axis=0)
+    w2 = np.repeat(g["w2"][:1], 5, axis=0)
+    fwd = O.layer_forward(g["x"], g["w_r"], w13, w2, 3)
+    np.testing.assert_allclose(fwd["Y"], _torch_ffn(g["x"], w13[0], w2[0], "swiglu"),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_shared_expert_alone_when_everything_drops():
+    w, g = _tiny(T=16, E=4, k=2, n_shared=1)
+    fwd = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], 2, cap=0, sw13=g["sw13"],
+                          sw2=g["sw2"])
+    np.testing.assert_allclose(fwd["Y"], _torch_ffn(g["x"], g["sw13"][0], g["sw2"][0], "swiglu"),
+                               rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------- invariants
+@pytest.mark.parametrize("cf", [None, 0.5, 1.0])
+def test_routing_and_permutation_invariants(cf):
+    w, g = _tiny(T=64, E=8, k=3, cf=cf)
+    cap = O.capacity(w.T, w.k, w.E, cf)
+    r = O.router_forward(g["x"], g["w_r"], w.k)
+    np.testing.assert_allclose(r["gates"].sum(1), 1.0, rtol=0, atol=1e-14)
+    for t in range(w.T):
+        assert len(set(r["topk_idx"][t])) == w.k
+    st = O.aux_stats(r["scores"], r["topk_idx"], w.E)
+    assert st["counts"].sum() == w.T * w.k
+    p = O.permute(r["topk_idx"], w.E, cap)
+    A = p["offsets"][-1]
+    assert (np.diff(p["offsets"]) >= 0).all() and A == w.T * w.k - p["n_dropped"]
+    kept = p["row_of"][p["row_of"] >= 0]
+    assert sorted(kept.tolist()) == list(range(A))
+    for t in range(w.T):
+        for j in range(w.k):
+            rr = p["row_of"][t, j]
+            if rr >= 0:
+                assert p["token_of"][rr] == t
+                e = r["topk_idx"][t, j]
+                assert p["offsets"][e] <= rr < p["offsets"][e + 1]
+    for e in range(w.E):
+        seg = p["token_of"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert (np.diff(seg) > 0).all()
+        if cap is not None:
+            assert len(seg) == min(cap, st["counts"][e])
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_unpermute_of_permute_is_k_times_identity(k):
+    w, g = _tiny(T=30, E=6, k=k)
+    r = O.router_forward(g["x"], g["w_r"], k)
+    p = O.permute(r["topk_idx"], w.E)
+    x_perm = g["x"][p["token_of"]]
+    np.testing.assert_array_equal(O.permute_backward(x_perm, p["row_of"]), k * g["x"])
+
+
+# --------------------------------------------------------- finite differences
+def test_activation_derivatives():
+    a = np.linspace(-6, 6, 101)
+    h = 1e-6
+    np.testing.assert_allclose(O.dsilu(a), (O.silu(a + h) - O.silu(a - h)) / (2 * h), atol=1e-8)
+    np.testing.assert_allclose(O.dgelu(a), (O.gelu(a + h) - O.gelu(a - h)) / (2 * h), atol=1e-8)
+    np.testing.assert_allclose(O.gelu(a), a * sst.norm.cdf(a), rtol=1e-13, atol=1e-15)
+
+
+FD_VARIANTS = [
+    dict(score="softmax", act="swiglu", cf=None, aux_coef=0.0),
+    dict(score="softmax", act="swiglu", cf=0.75, aux_coef=0.3),
+    dict(score="softmax", act="gelu", cf=None, aux_coef=0.0, logit_bias={1: 0.5}),
+    dict(score="sigmoid", act="swiglu", cf=None, aux_coef=0.2, sel_bias=True, n_shared=1),
+]
+
+
+@pytest.mark.parametrize("var", FD_VARIANTS)
+def test_gradients_by_central_differences(var):
+    aux = var.pop("aux_coef")
+    # seed chosen so no token sits within 1e-3 of a top-k boundary
+    for seed in range(50):
+        w, g = _tiny(T=10, d=6, E=5, k=2, f=4, seed=seed, **var)
+        # scale the router up so its gradient is not tiny next to the FFN's
+        g["w_r"] = g["w_r"] * 40.0
+        r = O.router_forward(g["x"], g["w_r"], w.k, w.score, g["logit_bias"], g["sel_bias"])
+        if not O.near_tie_tokens(r["key"], w.k, 1e-3).any():
+            break
+    else:
+        pytest.fail("no tie-free seed")
+    cap = O.capacity(w.T, w.k, w.E, w.cf)
+    params = dict(x=g["x"], w_r=g["w_r"], w13=g["w13"], w2=g["w2"])
+    if w.n_shared:
+        params.update(sw13=g["sw13"], sw2=g["sw2"])
+    dY = g["dy"]
+
+    def loss(p):
+        f = O.layer_forward(p["x"], p["w_r"], p["w13"], p["w2"], w.k, w.score, w.act, cap,
+                            g["logit_bias"], g["sel_bias"], p.get("sw13"), p.get("sw2"))
+        return float((f["Y"] * dY).sum()) + aux * f["stats"]["L_aux"], f
+
+    _, fwd = loss(params)
+    bwd = O.layer_backward(fwd, params["x"], params["w_r"], params["w13"], params["w2"], dY,
+                           w.score, w.act, aux, params.get("sw13"), params.get("sw2"))
+    analytic = dict(x=bwd["dX"], w_r=bwd["dw_r"], w13=bwd["dw13"], w2=bwd["dw2"],
+                    sw13=bwd["dsw13"], sw2=bwd["dsw2"])
+    h = 1e-6
+    for name, val in params.items():
+        num = np.zeros_like(val)
+        for i in np.ndindex(val.shape):
+            p2 = {n: v.copy() for n, v in params.items()}
+            p2[name][i] += h
+            lp, _ = loss(p2)
+            p2[name][i] -= 2 * h
+            lm, _ = loss(p2)
+            num[i] = (lp - lm) / (2 * h)
+        scale = max(1.0, np.abs(num).max())
+        np.testing.assert_allclose(analytic[name], num, rtol=0, atol=2e-6 * scale,
+                                   err_msg=name)
+
+
+def test_aux_gradient_is_not_dropped():
+    """The aux term must change dW_r (a dropped aux term fails this)."""
+    w, g = _tiny(T=12, d=6, E=4, k=2, f=4)
+    fwd = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], 2)
+    b0 = O.layer_backward(fwd, g["x"], g["w_r"], g["w13"], g["w2"], g["dy"], aux_coef=0.0)
+    b1 = O.layer_backward(fwd, g["x"], g["w_r"], g["w13"], g["w2"], g["dy"], aux_coef=1.0)
+    assert np.abs(b1["dw_r"] - b0["dw_r"]).max() > 1e-6
+
+
+# ------------------------------------------------------------- near ties
+def test_near_tie_flags():
+    key = np.array([[0.5, 0.3, 0.2 + 5e-6, 0.2, 0.0],
+                    [0.5, 0.3, 0.1, 0.05, 0.05],
+                    [0.4, 0.4 - 1e-7, 0.1, 0.05, 0.05]])
+    flags = O.near_tie_tokens(key, 2)
+    assert list(flags) == [False, False, True]
+    assert list(O.near_tie_tokens(key, 3)) == [True, False, True]
+
+
+# ---------------------------------------------------------------- generator
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    v = (rng.standard_normal(100000) * 3).astype(np.float32)
+    v[:4] = [1.00390625, 1.01171875, -1.00390625, 0.0]   # exact ties
+    ours = to_bf16_bits(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(bf16_bits_to_f32(ours),
+                                  torch.from_numpy(v).to(torch.bfloat16).float().numpy())
+
+
+def test_generator_is_deterministic_and_per_expert():
+    from moe_inputs import gen_expert_w13, gen_w13
+    w = Workload("g", T=8, d=16, E=4, k=2, f=8)
+    a = gen_w13(w)
+    np.testing.assert_array_equal(a[2], gen_expert_w13(w, 2))
+    np.testing.assert_array_equal(a, gen_w13(w, threads=1))
+    assert not np.array_equal(a[0], a[1])
