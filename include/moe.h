@@ -1,0 +1,246 @@
+/*
+ * moe.h - C ABI of libmoe: one Mixture-of-Experts layer, forward and backward,
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as printed on them):
+ *   [Recipe]  "MoE 训练加速实战：DeepEP + Grouped GeMM + Aux-Loss-Free 的 Qwen3.5 配方"
+ *   [Balance] "负载均衡策略：MoE训练稳定性保障"
+ *   [ETP]     "ETP专家并行加速MoE模型：ms-swift中稀疏架构的极致优化"
+ *   [VPP]     "MoE模型训练加速10倍？看ms-swift如何通过ETP和VPP实现突破"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers. `desc` and the size/out-parameters of the utility calls are host
+ *   pointers. Every tensor pointer is a device pointer (HBM), 16-byte aligned,
+ *   row-major and densely packed with the shape given below. The caller
+ *   allocates and frees every buffer; the library never allocates, frees or
+ *   keeps a pointer after a call returns. Scratch memory comes from the
+ *   caller's workspace `ws` of at least moe_workspace_size(desc, op) bytes.
+ * Dtypes. "dt" means the layer dtype desc->dtype (MOE_F32: float, MOE_BF16:
+ *   bfloat16 bit patterns). Router weight, biases, scores, gates, dgate,
+ *   statistics, logits and their gradients are always float32. Indices,
+ *   counts and offsets are int32.
+ * Weights are stored out x in (the product is x W^T): router W_r [E, d];
+ *   expert first matrix w13 [E, 2f, d] for SwiGLU (rows [0,f) gate W1, rows
+ *   [f,2f) up W3) or w1 [E, f, d] for GELU; down matrix w2 [E, d, f]. The
+ *   shared expert (desc->n_shared == 1) has sw13 [1, 2f, d] / [1, f, d] and
+ *   sw2 [1, d, f].
+ * Routed rows. Kept assignments are laid out expert-major and, inside an
+ *   expert, by ascending token ("rows"). Buffers of routed rows are sized for
+ *   the worst case T*k rows; only the first A = offsets[E] rows are written
+ *   or read, so no device-to-host read is ever needed.
+ * Streams. Every call enqueues its kernels on `stream` (a hipStream_t, NULL =
+ *   the null stream) and returns without synchronising. Outputs are written,
+ *   never accumulated into. Results are deterministic: the same inputs give
+ *   the same bits (no floating-point atomics; fixed summation orders).
+ * Errors. Every call returns a moe_status. Arguments are validated before any
+ *   HIP call; on failure nothing is enqueued and moe_last_error() (a
+ *   thread-local string) says why. A launch failure returns MOE_ERR_HIP.
+ *   Device faults surface at the caller's next synchronisation. T == 0 is a
+ *   successful no-op. No C++ exception crosses this ABI.
+ * Limits. 1 <= k <= E <= 1024; n_shared in {0, 1}; d and f multiples of 8;
+ *   T*k < 2^31.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad shape or enum */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented combination */
+  MOE_ERR_WORKSPACE = 3,     /* ws smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_fn;
+typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_activation;
+
+/* Layer description (host struct, read during the call only). */
+typedef struct {
+  int64_t T;         /* tokens */
+  int64_t d;         /* model width */
+  int64_t E;         /* routed experts */
+  int64_t k;         /* experts per token */
+  int64_t f;         /* expert hidden width (d_ff) */
+  int64_t n_shared;  /* always-on shared experts: 0 or 1 */
+  int32_t dtype;     /* moe_dtype */
+  int32_t score;     /* moe_score_fn */
+  int32_t act;       /* moe_activation */
+  int32_t reserved;  /* must be 0 */
+  int64_t capacity;  /* per-expert limit on kept assignments; < 0: no limit */
+} moe_desc;
+
+/* Which call a workspace is for (moe_workspace_size). */
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_AUX_STATS = 1,
+  MOE_OP_PERMUTE = 2,
+  MOE_OP_FFN_FWD = 3,
+  MOE_OP_FFN_BWD = 4,
+  MOE_OP_ROUTE_BWD = 5
+} moe_op;
+
+/* ---------------------------------------------------------------- router
+ * moe_route: [Recipe] §2.2 (router math): logits l = x W_r^T (+ logit_bias),
+ * computed in float32 ([Recipe] §1 and §9.2: router kept in fp32);
+ * scores s = softmax(l) (max-subtracted) or sigmoid(l); selection key
+ * s (+ sel_bias, the aux-loss-free bias of [Recipe] §5.3 that steers top-k
+ * only); the k experts with the largest keys, ties to the lower index, kept
+ * in rank order; gate weights renormalised over the chosen k from the
+ * unbiased scores: g_j = s_{e_j} / sum_j' s_{e_j'}.
+ *   x          [T, d] dt                     in
+ *   w_r        [E, d] float                  in
+ *   logit_bias [E] float or NULL             in  (added to the logits)
+ *   sel_bias   [E] float or NULL             in  (added to the key only)
+ *   topk_idx   [T, k] int32                  out (expert of each slot)
+ *   gate       [T, k] float                  out
+ *   scores     [T, E] float                  out
+ *   ws         MOE_OP_ROUTE bytes            scratch
+ */
+int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* moe_aux_stats: load-balance statistics of [Balance] (section 辅助损失函数)
+ * and [Recipe] §5.2: counts_i = assignments routed to expert i before any
+ * capacity drop; y_i = counts_i / (T k); z_i = mean over tokens of s_ti;
+ * out2[0] = S = sum_i y_i z_i; out2[1] = L_aux = E * S. Sums run in a fixed
+ * order (deterministic).
+ *   scores [T, E] float, topk_idx [T, k] int32             in
+ *   counts [E] int32, y [E] float, z [E] float, out2 [2]   out
+ */
+int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk_idx,
+                  int32_t* counts, float* y, float* z, float* out2, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------- permute
+ * moe_permute: local dispatch ([Recipe] §3.2; [Balance] section 负载感知调度,
+ * tokens sorted by destination expert before the exchange) with the capacity
+ * limit of [Balance] section 专家容量裁剪: assignment (t, j) to expert e is
+ * kept when fewer than desc->capacity earlier tokens were routed to e.
+ * Histogram -> exclusive scan -> stable scatter; the row order is fixed by
+ * (expert, token), never by thread timing.
+ *   x         [T, d] dt                     in
+ *   topk_idx  [T, k] int32                  in
+ *   offsets   [E + 1] int32                 out (rows of expert e: [offsets[e], offsets[e+1]))
+ *   row_of    [T, k] int32                  out (row of (t, j), or -1 if dropped)
+ *   token_of  [T*k] int32                   out (token of each row; first A entries)
+ *   n_dropped [1] int32                     out (T*k - A)
+ *   x_perm    [T*k, d] dt                   out (x_perm[row] = x[token_of[row]]; first A rows)
+ */
+int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, int32_t* offsets,
+                int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* x_perm, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ grouped FFN
+ * moe_grouped_ffn_fwd: the grouped GEMM of [Recipe] §4.2 - every expert's FFN
+ * on its own contiguous rows in one launch per matrix - for the two-matrix
+ * expert of [ETP] (up-projection then down-projection): SwiGLU
+ * H = silu(X W1^T) * (X W3^T) or GELU H = gelu(X W1^T) (exact erf form),
+ * O = H W2^T. bf16 in, float32 accumulate, dt out. The shared expert
+ * ([Recipe] §2.3 / §9.1) runs on all T rows of x when desc->n_shared == 1.
+ *   x_perm   [T*k, d] dt, offsets [E+1] int32 (from moe_permute)   in
+ *   x        [T, d] dt (shared expert input; NULL if n_shared == 0) in
+ *   w13, w2  routed weights; sw13, sw2 shared weights or NULL       in
+ *   save_pre [T*k, 2f] (SwiGLU: [a | b]) or [T*k, f] (GELU: a) dt   out (for the backward)
+ *   save_h   [T*k, f] dt                                            out (H, for the backward)
+ *   save_pre_s, save_h_s: the same for the shared expert ([T, ...]) out or NULL
+ *   out      [T*k, d] dt                                            out (O per row)
+ *   out_shared [T, d] dt or NULL                                    out
+ */
+int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                        const void* x, const void* w13, const void* w2, const void* sw13,
+                        const void* sw2, void* save_pre, void* save_h, void* save_pre_s,
+                        void* save_h_s, void* out, void* out_shared, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* moe_grouped_ffn_bwd: backward of moe_grouped_ffn_fwd ([VPP]: each device
+ * runs forward and backward of its local experts between the exchanges).
+ * dgrad: dH = dO W2; SwiGLU da = dH * b * silu'(a), db = dH * silu(a)
+ * (GELU da = dH * gelu'(a)); dX = [da db] W13. wgrad: dW2 = dO^T H,
+ * dW13 = [da db]^T X. The shared expert's upstream gradient is dy itself.
+ * Gradients are written in dt (an expert with no rows gets dW = 0).
+ *   dout [T*k, d] dt (from moe_combine_bwd), dy [T, d] dt (shared; may be NULL if n_shared == 0)
+ *   dx_perm [T*k, d] dt, dx_shared [T, d] dt or NULL                out
+ *   dw13, dw2 (routed weight shapes), dsw13, dsw2 or NULL           out
+ */
+int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                        const void* x, const void* w13, const void* w2, const void* sw13,
+                        const void* sw2, const void* save_pre, const void* save_h,
+                        const void* save_pre_s, const void* save_h_s, const void* dout,
+                        const void* dy, void* dx_perm, void* dx_shared, void* dw13, void* dw2,
+                        void* dsw13, void* dsw2, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine
+ * moe_combine: the weighted sum of [Recipe] §2.1/§2.2 (the combine step of
+ * [Recipe] §3.2): y[t] = out_shared[t] + sum over kept slots j (in slot
+ * order) of gate[t,j] * out[row_of[t,j]], float32 accumulate, one rounding.
+ * A dropped slot adds nothing (gates are not renormalised after a drop).
+ *   out [T*k, d] dt, out_shared [T, d] dt or NULL, gate [T, k], row_of [T, k]   in
+ *   y [T, d] dt                                                               out
+ */
+int moe_combine(const moe_desc* desc, const void* out, const void* out_shared, const float* gate,
+                const int32_t* row_of, void* y, void* stream);
+
+/* moe_combine_bwd: dgate[t,j] = <dy[t], out[row_of[t,j]]> (0 if dropped),
+ * dout[row_of[t,j]] = gate[t,j] * dy[t].
+ *   dy [T, d] dt, out [T*k, d] dt, gate [T, k], row_of [T, k]   in
+ *   dgate [T, k] float, dout [T*k, d] dt                         out
+ */
+int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const float* gate,
+                    const int32_t* row_of, float* dgate, void* dout, void* stream);
+
+/* ------------------------------------------------------- router backward
+ * moe_route_bwd: gradient of the router through the renormalised gates of
+ * [Recipe] §2.2 (top-k selection itself has no gradient), plus aux_coef
+ * times the gradient of L_aux = E sum_i y_i z_i with y held fixed
+ * ([Recipe] §5.2; the total loss is main + lambda * aux).
+ *   softmax: dl_e = g_e (dg_e - sum_j g_j dg_j) on chosen e, else 0;
+ *            aux: dl_te += aux_coef (E/T) s_te (y_e - sum_i y_i s_ti)
+ *   sigmoid: dl_e = s_e (1 - s_e) (dg_e - sum_j g_j dg_j) / sum_chosen s;
+ *            aux: dl_te += aux_coef (E/T) y_e s_te (1 - s_te)
+ * dw_r = dl^T x, dx_router = dl W_r (float32).
+ *   x [T, d] dt, w_r [E, d], scores [T, E], topk_idx, gate, dgate [T, k]   in
+ *   y [E] float (from moe_aux_stats; may be NULL when aux_coef == 0)        in
+ *   dlogits [T, E] float, dx_router [T, d] float, dw_r [E, d] float          out
+ */
+int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const float* scores,
+                  const int32_t* topk_idx, const float* gate, const float* dgate, const float* y,
+                  float aux_coef, float* dlogits, float* dx_router, float* dw_r, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* moe_permute_bwd: un-permute, dx[t] = dx_shared[t] + sum over kept slots j
+ * (slot order) of dx_perm[row_of[t,j]] + dx_router[t], float32 accumulate,
+ * one rounding to dt.
+ *   dx_perm [T*k, d] dt, row_of [T, k], dx_shared [T, d] dt or NULL,
+ *   dx_router [T, d] float or NULL                                     in
+ *   dx [T, d] dt                                                        out
+ */
+int moe_permute_bwd(const moe_desc* desc, const void* dx_perm, const int32_t* row_of,
+                    const void* dx_shared, const float* dx_router, void* dx, void* stream);
+
+/* -------------------------------------------------------------- utilities */
+/* Workspace bytes `op` needs for this desc (0 is a valid answer). */
+int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes);
+/* [Balance] section 专家容量裁剪: capacity = ceil(cf * T * k / E), evaluated
+ * left to right in binary64; cf < 0 gives -1 (no limit). */
+int moe_capacity(int64_t T, int64_t k, int64_t E, double cf, int64_t* capacity);
+const char* moe_status_str(int status);
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* moe_last_error(void);
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

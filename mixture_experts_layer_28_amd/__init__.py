@@ -1,0 +1,206 @@
+"""Thin Python binding of libmoe (include/moe.h): the same entry points, with
+torch tensors in place of raw device pointers. Argument marshalling only:
+every step runs in the library's HIP kernels. PyTorch supplies device memory
+and the current stream.
+
+The library is required: importing works without it (so the package can be
+inspected), but every call raises if libmoe.so is missing or was built for
+another target. There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_SWIGLU, MOE_GELU = 0, 1
+(MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
+ MOE_OP_ROUTE_BWD) = range(6)
+
+# every symbol include/moe.h declares
+EXPORTS = (
+    "moe_route", "moe_aux_stats", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine",
+    "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
+    "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
+)
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+        ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("n_shared", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("score", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("capacity", ctypes.c_int64),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (once). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_28_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        DP = ctypes.POINTER(MoeDesc)
+        sig = {
+            "moe_route": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
+            "moe_aux_stats": [DP] + [_P] * 7 + [ctypes.c_size_t, _P],
+            "moe_permute": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
+            "moe_grouped_ffn_fwd": [DP] + [_P] * 14 + [ctypes.c_size_t, _P],
+            "moe_combine": [DP] + [_P] * 6,
+            "moe_combine_bwd": [DP] + [_P] * 7,
+            "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
+            "moe_route_bwd": [DP] + [_P] * 7 + [ctypes.c_float] + [_P] * 4 + [ctypes.c_size_t, _P],
+            "moe_permute_bwd": [DP] + [_P] * 6,
+            "moe_workspace_size": [DP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+            "moe_capacity": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                             ctypes.POINTER(ctypes.c_int64)],
+            "moe_status_str": [ctypes.c_int],
+            "moe_last_error": [],
+            "moe_abi_version": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name in ("moe_status_str", "moe_last_error") else ctypes.c_int
+        if L.moe_abi_version() != 1:
+            raise RuntimeError("libmoe ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status, lib().moe_last_error().decode())
+
+
+def make_desc(T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
+              capacity=None) -> MoeDesc:
+    return MoeDesc(T=T, d=d, E=E, k=k, f=f, n_shared=n_shared,
+                   dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
+                   score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
+                   act=MOE_SWIGLU if act == "swiglu" else MOE_GELU, reserved=0,
+                   capacity=-1 if capacity is None else int(capacity))
+
+
+def capacity(T: int, k: int, E: int, cf: Optional[float]) -> Optional[int]:
+    """Per-expert capacity ceil(cf*T*k/E) as the library computes it (None = no limit)."""
+    if cf is None:
+        return None
+    out = ctypes.c_int64()
+    _check("moe_capacity", lib().moe_capacity(T, k, E, float(cf), ctypes.byref(out)))
+    return int(out.value)
+
+
+def workspace_size(desc: MoeDesc, op: int) -> int:
+    out = ctypes.c_size_t()
+    _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(desc), op, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+# ------------------------------------------------------------- entry points
+def route(desc, x, w_r, logit_bias, sel_bias, topk_idx, gate, scores, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_route", lib().moe_route(ctypes.byref(desc), _p(x), _p(w_r), _p(logit_bias),
+                                        _p(sel_bias), _p(topk_idx), _p(gate), _p(scores), wp, wn,
+                                        _stream(stream)))
+
+
+def aux_stats(desc, scores, topk_idx, counts, y, z, out2, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_aux_stats", lib().moe_aux_stats(ctypes.byref(desc), _p(scores), _p(topk_idx),
+                                                _p(counts), _p(y), _p(z), _p(out2), wp, wn,
+                                                _stream(stream)))
+
+
+def permute(desc, x, topk_idx, offsets, row_of, token_of, n_dropped, x_perm, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_permute", lib().moe_permute(ctypes.byref(desc), _p(x), _p(topk_idx), _p(offsets),
+                                            _p(row_of), _p(token_of), _p(n_dropped), _p(x_perm),
+                                            wp, wn, _stream(stream)))
+
+
+def grouped_ffn_fwd(desc, x_perm, offsets, x, w13, w2, sw13, sw2, save_pre, save_h, save_pre_s,
+                    save_h_s, out, out_shared, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_grouped_ffn_fwd", lib().moe_grouped_ffn_fwd(
+        ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13), _p(w2), _p(sw13), _p(sw2),
+        _p(save_pre), _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
+        _stream(stream)))
+
+
+def combine(desc, out, out_shared, gate, row_of, y, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(desc), _p(out), _p(out_shared), _p(gate),
+                                            _p(row_of), _p(y), _stream(stream)))
+
+
+def combine_bwd(desc, dy, out, gate, row_of, dgate, dout, stream=None):
+    _check("moe_combine_bwd", lib().moe_combine_bwd(ctypes.byref(desc), _p(dy), _p(out), _p(gate),
+                                                    _p(row_of), _p(dgate), _p(dout),
+                                                    _stream(stream)))
+
+
+def grouped_ffn_bwd(desc, x_perm, offsets, x, w13, w2, sw13, sw2, save_pre, save_h, save_pre_s,
+                    save_h_s, dout, dy, dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws=None,
+                    stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_grouped_ffn_bwd", lib().moe_grouped_ffn_bwd(
+        ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13), _p(w2), _p(sw13), _p(sw2),
+        _p(save_pre), _p(save_h), _p(save_pre_s), _p(save_h_s), _p(dout), _p(dy), _p(dx_perm),
+        _p(dx_shared), _p(dw13), _p(dw2), _p(dsw13), _p(dsw2), wp, wn, _stream(stream)))
+
+
+def route_bwd(desc, x, w_r, scores, topk_idx, gate, dgate, y, aux_coef, dlogits, dx_router, dw_r,
+              ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_route_bwd", lib().moe_route_bwd(
+        ctypes.byref(desc), _p(x), _p(w_r), _p(scores), _p(topk_idx), _p(gate), _p(dgate), _p(y),
+        float(aux_coef), _p(dlogits), _p(dx_router), _p(dw_r), wp, wn, _stream(stream)))
+
+
+def permute_bwd(desc, dx_perm, row_of, dx_shared, dx_router, dx, stream=None):
+    _check("moe_permute_bwd", lib().moe_permute_bwd(ctypes.byref(desc), _p(dx_perm), _p(row_of),
+                                                    _p(dx_shared), _p(dx_router), _p(dx),
+                                                    _stream(stream)))
+
+
+from .layer import MoELayer  # noqa: E402,F401

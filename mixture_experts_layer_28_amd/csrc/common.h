@@ -1,0 +1,133 @@
+// Device helpers shared by the libmoe kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// 8 consecutive elements <-> 8 floats, for either storage type
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf2f(u.x & 0xffff); v[1] = bf2f(u.x >> 16);
+    v[2] = bf2f(u.y & 0xffff); v[3] = bf2f(u.y >> 16);
+    v[4] = bf2f(u.z & 0xffff); v[5] = bf2f(u.z >> 16);
+    v[6] = bf2f(u.w & 0xffff); v[7] = bf2f(u.w >> 16);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    uint4 u;
+    u.x = pack_bf2(v[0], v[1]); u.y = pack_bf2(v[2], v[3]);
+    u.z = pack_bf2(v[4], v[5]); u.w = pack_bf2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
+
+// ------------------------------------------------------------ activations
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + expf(-a)); }
+__device__ __forceinline__ float silu_f(float a) { return a * sigmoidf_(a); }
+__device__ __forceinline__ float dsilu_f(float a) {
+  float s = sigmoidf_(a);
+  return s * (1.0f + a * (1.0f - s));
+}
+// exact (erf) GELU and its derivative
+__device__ __forceinline__ float gelu_f(float a) {
+  return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+}
+__device__ __forceinline__ float dgelu_f(float a) {
+  float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+  float pdf = expf(-0.5f * a * a) * 0.39894228040143268f;
+  return cdf + a * pdf;
+}
+
+// ------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ------------------------------------------------------------ GEMM plumbing
+// Epilogue kinds of the grouped GEMMs (applied to float32 accumulators).
+enum Epi : int {
+  EPI_STORE = 0,       // C = acc (+ col_bias)
+  EPI_SWIGLU_FWD = 1,  // fused gate/up tile: C = H = silu(a) * b, aux = [a | b]
+  EPI_GELU_FWD = 2,    // C = H = gelu(acc), aux = a = acc
+  EPI_SWIGLU_BWD = 3,  // acc = dH; reads aux = [a | b]; C = [da | db]
+  EPI_GELU_BWD = 4,    // acc = dH; reads aux = a; C = da
+};
+
+// How the groups (experts) of one grouped GEMM are shaped.
+enum Rag : int {
+  RAG_M = 0,       // group g has M_g = off[g+1]-off[g] rows (forward, dgrad)
+  RAG_K = 1,       // group g has K_g = off[g+1]-off[g] (wgrad: reduce over the expert's rows)
+  RAG_NONE = 2,    // G groups of identical M x N x K; group g's first row is g*M (or g*K)
+};
+
+// One operand of a grouped GEMM. Element (i, kk) of A (i = row of C) lives at
+// base + i*ld + kk when kmajor, else base + kk*ld + i; likewise for B with
+// i = column of C. Per group the base moves by r0*ld ("row-indexed": the
+// operand is a routed-row tensor whose rows start at the group's first row
+// r0) or by g*gstride (a stacked per-expert weight).
+struct Operand {
+  const void* base;
+  int64_t ld;
+  int64_t gstride;
+  int rowidx;
+};
+
+struct GemmArgs {
+  Operand a, b;
+  void* c; int64_t ldc; int64_t c_gstride; int c_rowidx;
+  void* aux; int64_t ldaux; int64_t aux_gstride; int aux_rowidx;  // epilogue side tensor
+  const int32_t* offsets;   // [G+1] device (RAG_M / RAG_K)
+  int G;
+  int64_t M, N, K;          // the non-ragged sizes; for EPI_SWIGLU_FWD N = f (H columns)
+  int64_t fdim;             // f (column split of [a | b]) for the SwiGLU epilogues
+  const float* col_bias;    // EPI_STORE: added per output column, or null
+  int64_t max_rows;         // RAG_M: upper bound of sum of M_g (grid sizing)
+  int k_splits;             // split-K partitions (fp32 GEMM, RAG_NONE only); 1 = none
+};
+
+}  // namespace moe

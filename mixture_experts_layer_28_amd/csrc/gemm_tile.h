@@ -1,0 +1,204 @@
+// Tile scheduling and the row-contiguous epilogue shared by the grouped GEMMs.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8). Give
+// each XCD a contiguous range of logical tiles so that the tiles resident on
+// one XCD at a time share A/B panels in that XCD's L2. nb is a multiple of 8.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb) {
+  return (b & 7) * (nb >> 3) + (b >> 3);
+}
+
+// Bands of kBandM m-tiles, n-tiles outer inside a band: consecutive logical
+// tiles reuse the same B panel across kBandM A panels.
+constexpr int kBandM = 8;
+__device__ __forceinline__ void band_order(int64_t L, int64_t mt_total, int64_t nt,
+                                           int64_t& mt, int64_t& ntile) {
+  int64_t band = L / (kBandM * nt);
+  int64_t within = L - band * kBandM * nt;
+  int64_t rem = mt_total - band * kBandM;
+  int64_t h = rem < kBandM ? rem : kBandM;
+  mt = band * kBandM + within % h;
+  ntile = within / h;
+}
+
+// Exclusive prefix over groups of ceil(M_g / BM) (M_g from offsets), written
+// to s_tiles[0..G] (s_tiles[G] = total). 256 threads, G <= 1024.
+template <int BM>
+__device__ __forceinline__ void group_tile_prefix(const int32_t* __restrict__ off, int G,
+                                                  int* s_tiles, int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt[4];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int gi = tid * 4 + i;
+    int c = 0;
+    if (gi < G) {
+      int n = off[gi + 1] - off[gi];
+      c = (n + BM - 1) / BM;
+    }
+    cnt[i] = c;
+    s += c;
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  int ex = base + incl - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int gi = tid * 4 + i;
+    if (gi <= G) s_tiles[gi] = ex;
+    ex += cnt[i];
+  }
+  __syncthreads();
+}
+
+// largest g in [0, G) with s_tiles[g] <= mt
+__device__ __forceinline__ int find_group(const int* s_tiles, int G, int64_t mt) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Resolved tile of a grouped GEMM.
+struct Tile {
+  int g;
+  int64_t r0;      // first routed row of the group
+  int64_t M, K;    // this group's M and K
+  int64_t m0, n0;  // tile origin (n0 in output columns; H columns for the fused SwiGLU)
+};
+
+// Map this workgroup to a tile; false = no tile (surplus workgroup).
+// BNo: output columns per tile. s_tiles must hold >= G+1 ints, s_wsum 4 ints.
+template <int BM, int BNo, int RAG>
+__device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, int* s_wsum,
+                                             Tile& t) {
+  const int64_t nt = (p.N + BNo - 1) / BNo;
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  if (RAG == RAG_M) {
+    group_tile_prefix<BM>(p.offsets, p.G, s_tiles, s_wsum);
+    const int64_t total = s_tiles[p.G];
+    if (L >= total * nt) return false;
+    int64_t mt, ntile;
+    band_order(L, total, nt, mt, ntile);
+    t.g = find_group(s_tiles, p.G, mt);
+    t.r0 = p.offsets[t.g];
+    t.M = p.offsets[t.g + 1] - t.r0;
+    t.K = p.K;
+    t.m0 = (mt - s_tiles[t.g]) * BM;
+    t.n0 = ntile * BNo;
+    return true;
+  }
+  const int64_t mtg = (p.M + BM - 1) / BM;
+  const int64_t per = mtg * nt;
+  if (L >= per * p.G) return false;
+  t.g = (int)(L / per);
+  int64_t mt, ntile;
+  band_order(L - (int64_t)t.g * per, mtg, nt, mt, ntile);
+  t.m0 = mt * BM;
+  t.n0 = ntile * BNo;
+  t.M = p.M;
+  if (RAG == RAG_K) {
+    t.r0 = p.offsets[t.g];
+    t.K = p.offsets[t.g + 1] - t.r0;
+  } else {
+    t.r0 = (int64_t)t.g * p.M;
+    t.K = p.K;
+  }
+  return true;
+}
+
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(bf16_t* p, float v) { *p = (bf16_t)f2bf(v); }
+
+template <typename T>
+__device__ __forceinline__ const T* operand_base(const Operand& o, const Tile& t) {
+  const T* b = reinterpret_cast<const T*>(o.base);
+  return o.rowidx ? b + t.r0 * o.ld : b + (int64_t)t.g * o.gstride;
+}
+
+// Row-contiguous epilogue over a float32 tile staged in LDS.
+// stage[rho * lds + c], rho in [0, nrows), c in [0, ncols) (EPI_SWIGLU_FWD:
+// ncols H columns with the gate at c and the up value at ncols + c).
+// Stage row rho is output row m0 + rho, stage column c is output column n0 + c.
+// Work items are 8-column segments spread over `nthr` threads from `me`.
+template <typename TC, int EPI>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& p, const Tile& t, const float* stage,
+                                              int lds, int nrows, int ncols, int64_t m0,
+                                              int64_t n0, int me, int nthr) {
+  TC* cb = reinterpret_cast<TC*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
+  TC* ab = reinterpret_cast<TC*>(p.aux);
+  if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
+  const int segs_per_row = ncols >> 3;
+  const int nseg = nrows * segs_per_row;
+  for (int s = me; s < nseg; s += nthr) {
+    const int rho = s / segs_per_row;
+    const int c = (s - rho * segs_per_row) << 3;
+    const int64_t gm = m0 + rho, gn = n0 + c;
+    if (gm >= t.M || gn >= p.N) continue;
+    const float* sv = stage + rho * lds + c;
+    float v[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = sv[i];
+    if (EPI == EPI_STORE) {
+      const int nv = p.N - gn < 8 ? (int)(p.N - gn) : 8;
+      if (p.col_bias) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nv) v[i] += p.col_bias[gn + i];
+      }
+      if (nv == 8 && (p.ldc & 7) == 0) {
+        Vec8<TC>::store(cb + gm * p.ldc + gn, v);
+      } else {
+        for (int i = 0; i < nv; ++i) store1(cb + gm * p.ldc + gn + i, v[i]);
+      }
+    } else if (EPI == EPI_SWIGLU_FWD) {
+      float u[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        u[i] = sv[ncols + i];
+        o[i] = silu_f(v[i]) * u[i];
+      }
+      Vec8<TC>::store(cb + gm * p.ldc + gn, o);
+      Vec8<TC>::store(ab + gm * p.ldaux + gn, v);
+      Vec8<TC>::store(ab + gm * p.ldaux + p.fdim + gn, u);
+    } else if (EPI == EPI_GELU_FWD) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = gelu_f(v[i]);
+      Vec8<TC>::store(cb + gm * p.ldc + gn, o);
+      Vec8<TC>::store(ab + gm * p.ldaux + gn, v);
+    } else if (EPI == EPI_SWIGLU_BWD) {
+      float a[8], b[8], db[8];
+      Vec8<TC>::load(ab + gm * p.ldaux + gn, a);
+      Vec8<TC>::load(ab + gm * p.ldaux + p.fdim + gn, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o[i] = v[i] * b[i] * dsilu_f(a[i]);
+        db[i] = v[i] * silu_f(a[i]);
+      }
+      Vec8<TC>::store(cb + gm * p.ldc + gn, o);
+      Vec8<TC>::store(cb + gm * p.ldc + p.fdim + gn, db);
+    } else if (EPI == EPI_GELU_BWD) {
+      float a[8];
+      Vec8<TC>::load(ab + gm * p.ldaux + gn, a);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = v[i] * dgelu_f(a[i]);
+      Vec8<TC>::store(cb + gm * p.ldc + gn, o);
+    }
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,574 @@
+// C ABI of libmoe (declared in include/moe.h): argument validation before any
+// HIP call, workspace layout, and the ordered kernel launches of each call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
+hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
+hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
+hipError_t gemm_router_dw(const GemmArgs& p, bool x_bf16, hipStream_t s);
+hipError_t gemm_router_dx(const GemmArgs& p, hipStream_t s);
+hipError_t launch_router_topk(const float*, int, int, int, int, const float*, int32_t*, float*,
+                              float*, hipStream_t);
+hipError_t launch_aux_stats(const float*, const int32_t*, int, int, int, double*, int32_t*,
+                            int32_t*, float*, float*, float*, hipStream_t);
+hipError_t launch_permute(const void*, bool, const int32_t*, int, int, int, int64_t, int64_t,
+                          int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
+hipError_t launch_combine(const void*, const void*, bool, const float*, const int32_t*, int, int,
+                          int64_t, void*, hipStream_t);
+hipError_t launch_combine_bwd(const void*, const void*, bool, const float*, const int32_t*, int,
+                              int, int64_t, float*, void*, hipStream_t);
+hipError_t launch_unpermute(const void*, const int32_t*, const void*, const float*, bool, int, int,
+                            int64_t, void*, hipStream_t);
+hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, const float*,
+                                 const float*, float, int, int, int, int, float*, hipStream_t);
+hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
+                                   int64_t, float*, hipStream_t);
+hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
+hipError_t launch_fill_zero(void*, size_t, hipStream_t);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    int _s = (expr);                  \
+    if (_s != MOE_OK) return _s;      \
+  } while (0)
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxK = 16;
+
+int check_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)d->T);
+  if (d->E < 1 || d->E > kMaxE)
+    return fail(MOE_ERR_INVALID_ARG, "E must be in [1, %lld] (got %lld)", (long long)kMaxE,
+                (long long)d->E);
+  if (d->k < 1 || d->k > d->E)
+    return fail(MOE_ERR_INVALID_ARG, "k must be in [1, E] (got k=%lld, E=%lld)",
+                (long long)d->k, (long long)d->E);
+  if (d->k > kMaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "k > %lld is not supported (got %lld)", (long long)kMaxK,
+                (long long)d->k);
+  if (d->d < 8 || d->d % 8)
+    return fail(MOE_ERR_INVALID_ARG, "d must be a positive multiple of 8 (got %lld)",
+                (long long)d->d);
+  if (d->f < 8 || d->f % 8)
+    return fail(MOE_ERR_INVALID_ARG, "f must be a positive multiple of 8 (got %lld)",
+                (long long)d->f);
+  if (d->n_shared != 0 && d->n_shared != 1)
+    return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1 (got %lld)", (long long)d->n_shared);
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->score != MOE_SOFTMAX && d->score != MOE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", d->score);
+  if (d->act != MOE_SWIGLU && d->act != MOE_GELU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", d->act);
+  if (d->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
+  if (d->T * d->k >= (int64_t(1) << 31) || d->T * d->E >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k and T*E must be < 2^31");
+  return MOE_OK;
+}
+
+int need(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+int opt(const void* p, const char* name) { return p ? need(p, name) : MOE_OK; }
+
+size_t esize(const moe_desc* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+int64_t pre_cols(const moe_desc* d) { return d->act == MOE_SWIGLU ? 2 * d->f : d->f; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int route_bwd_splits(const moe_desc* d) {
+  const int64_t tiles = ((d->E + 63) / 64) * ((d->d + 63) / 64);
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t smax = d->T / 256 > 1 ? d->T / 256 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t ws_bytes_for(const moe_desc* d, int op) {
+  const int64_t T = d->T, E = d->E;
+  switch (op) {
+    case MOE_OP_ROUTE: return align256((size_t)T * E * 4);
+    case MOE_OP_AUX_STATS: {
+      const size_t nb = (size_t)(T + 255) / 256;
+      return align256(nb * E * 8) + align256(nb * E * 4);
+    }
+    case MOE_OP_PERMUTE: return align256((size_t)((T + 63) / 64) * E * 4);
+    case MOE_OP_FFN_FWD: return 0;
+    case MOE_OP_FFN_BWD:
+      return align256((size_t)T * d->k * pre_cols(d) * esize(d)) +
+             (d->n_shared ? align256((size_t)T * pre_cols(d) * esize(d)) : 0);
+    case MOE_OP_ROUTE_BWD: {
+      const int S = route_bwd_splits(d);
+      return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
+    }
+  }
+  return 0;
+}
+
+int check_ws(const moe_desc* d, int op, const void* ws, size_t bytes) {
+  const size_t want = ws_bytes_for(d, op);
+  if (bytes < want)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", want, bytes);
+  if (want && !ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255))
+    return fail(MOE_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  return MOE_OK;
+}
+
+Operand opnd(const void* base, int64_t ld, int64_t gstride, int rowidx) {
+  Operand o;
+  o.base = base;
+  o.ld = ld;
+  o.gstride = gstride;
+  o.rowidx = rowidx;
+  return o;
+}
+
+GemmArgs blank() {
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.k_splits = 1;
+  return p;
+}
+
+int run_gemm(const moe_desc* d, const GemmArgs& p, bool akm, bool bkm, int epi, int rag,
+             hipStream_t s, const char* what) {
+  hipError_t e = d->dtype == MOE_BF16 ? gemm_bf16(p, akm, bkm, epi, rag, s)
+                                      : gemm_f32(p, akm, bkm, epi, rag, s);
+  return hip_check(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_BWD)
+    return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
+  *bytes = ws_bytes_for(desc, op);
+  return MOE_OK;
+}
+
+int moe_capacity(int64_t T, int64_t k, int64_t E, double cf, int64_t* capacity) {
+  g_err[0] = 0;
+  if (!capacity) return fail(MOE_ERR_INVALID_ARG, "capacity is NULL");
+  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "bad T/k/E");
+  if (!(cf == cf)) return fail(MOE_ERR_INVALID_ARG, "cf is NaN");
+  if (cf < 0) {
+    *capacity = -1;
+    return MOE_OK;
+  }
+  const double c = cf * (double)T * (double)k / (double)E;
+  *capacity = (int64_t)std::ceil(c);
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, void* ws,
+              size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(w_r, "w_r"));
+  MOE_TRY(opt(logit_bias, "logit_bias"));
+  MOE_TRY(opt(sel_bias, "sel_bias"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(gate, "gate"));
+  MOE_TRY(need(scores, "scores"));
+  MOE_TRY(check_ws(desc, MOE_OP_ROUTE, ws, ws_bytes));
+  if (desc->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = (float*)ws;
+  GemmArgs p = blank();
+  p.a = opnd(x, desc->d, 0, 1);
+  p.b = opnd(w_r, desc->d, 0, 0);
+  p.c = logits;
+  p.ldc = desc->E;
+  p.G = 1;
+  p.M = desc->T;
+  p.N = desc->E;
+  p.K = desc->d;
+  p.col_bias = logit_bias;
+  MOE_TRY(hip_check(gemm_router_logits(p, desc->dtype == MOE_BF16, s), "router logits"));
+  return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,
+                                      desc->score, sel_bias, topk_idx, gate, scores, s),
+                   "router top-k");
+}
+
+int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk_idx,
+                  int32_t* counts, float* y, float* z, float* out2, void* ws, size_t ws_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(scores, "scores"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(counts, "counts"));
+  MOE_TRY(need(y, "y"));
+  MOE_TRY(need(z, "z"));
+  MOE_TRY(need(out2, "out2"));
+  MOE_TRY(check_ws(desc, MOE_OP_AUX_STATS, ws, ws_bytes));
+  if (desc->T == 0) return MOE_OK;
+  const size_t nb = (size_t)(desc->T + 255) / 256;
+  double* pz = (double*)ws;
+  int32_t* pc = (int32_t*)((char*)ws + align256(nb * desc->E * 8));
+  return hip_check(launch_aux_stats(scores, topk_idx, (int)desc->T, (int)desc->E, (int)desc->k,
+                                    pz, pc, counts, y, z, out2, (hipStream_t)stream),
+                   "aux stats");
+}
+
+int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, int32_t* offsets,
+                int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* x_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(row_of, "row_of"));
+  MOE_TRY(need(token_of, "token_of"));
+  MOE_TRY(need(n_dropped, "n_dropped"));
+  MOE_TRY(need(x_perm, "x_perm"));
+  MOE_TRY(check_ws(desc, MOE_OP_PERMUTE, ws, ws_bytes));
+  if (desc->T == 0) return MOE_OK;
+  return hip_check(launch_permute(x, desc->dtype == MOE_BF16, topk_idx, (int)desc->T,
+                                  (int)desc->E, (int)desc->k, desc->d, desc->capacity,
+                                  (int32_t*)ws, offsets, row_of, token_of, n_dropped, x_perm,
+                                  (hipStream_t)stream),
+                   "permute");
+}
+
+int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                        const void* x, const void* w13, const void* w2, const void* sw13,
+                        const void* sw2, void* save_pre, void* save_h, void* save_pre_s,
+                        void* save_h_s, void* out, void* out_shared, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x_perm, "x_perm"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(w13, "w13"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(need(save_pre, "save_pre"));
+  MOE_TRY(need(save_h, "save_h"));
+  MOE_TRY(need(out, "out"));
+  if (desc->n_shared) {
+    MOE_TRY(need(x, "x"));
+    MOE_TRY(need(sw13, "sw13"));
+    MOE_TRY(need(sw2, "sw2"));
+    MOE_TRY(need(save_pre_s, "save_pre_s"));
+    MOE_TRY(need(save_h_s, "save_h_s"));
+    MOE_TRY(need(out_shared, "out_shared"));
+  }
+  MOE_TRY(check_ws(desc, MOE_OP_FFN_FWD, ws, ws_bytes));
+  if (desc->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t d = desc->d, f = desc->f, P = pre_cols(desc);
+  const int epi1 = desc->act == MOE_SWIGLU ? EPI_SWIGLU_FWD : EPI_GELU_FWD;
+  for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
+    const int rag = shared ? RAG_NONE : RAG_M;
+    GemmArgs p = blank();
+    p.a = opnd(shared ? x : x_perm, d, 0, 1);
+    p.b = opnd(shared ? sw13 : w13, d, P * d, 0);
+    p.c = shared ? save_h_s : save_h;
+    p.ldc = f;
+    p.c_rowidx = 1;
+    p.aux = shared ? save_pre_s : save_pre;
+    p.ldaux = P;
+    p.aux_rowidx = 1;
+    p.offsets = offsets;
+    p.G = shared ? 1 : (int)desc->E;
+    p.M = desc->T;
+    p.N = f;
+    p.K = d;
+    p.fdim = f;
+    p.max_rows = desc->T * desc->k;
+    MOE_TRY(run_gemm(desc, p, true, true, epi1, rag, s, "ffn fwd first matrix"));
+    GemmArgs q = blank();
+    q.a = opnd(shared ? save_h_s : save_h, f, 0, 1);
+    q.b = opnd(shared ? sw2 : w2, f, d * f, 0);
+    q.c = shared ? out_shared : out;
+    q.ldc = d;
+    q.c_rowidx = 1;
+    q.offsets = offsets;
+    q.G = p.G;
+    q.M = desc->T;
+    q.N = d;
+    q.K = f;
+    q.max_rows = p.max_rows;
+    MOE_TRY(run_gemm(desc, q, true, true, EPI_STORE, rag, s, "ffn fwd down matrix"));
+  }
+  return MOE_OK;
+}
+
+int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                        const void* x, const void* w13, const void* w2, const void* sw13,
+                        const void* sw2, const void* save_pre, const void* save_h,
+                        const void* save_pre_s, const void* save_h_s, const void* dout,
+                        const void* dy, void* dx_perm, void* dx_shared, void* dw13, void* dw2,
+                        void* dsw13, void* dsw2, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x_perm, "x_perm"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(w13, "w13"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(need(save_pre, "save_pre"));
+  MOE_TRY(need(save_h, "save_h"));
+  MOE_TRY(need(dout, "dout"));
+  MOE_TRY(need(dx_perm, "dx_perm"));
+  MOE_TRY(need(dw13, "dw13"));
+  MOE_TRY(need(dw2, "dw2"));
+  if (desc->n_shared) {
+    MOE_TRY(need(x, "x"));
+    MOE_TRY(need(sw13, "sw13"));
+    MOE_TRY(need(sw2, "sw2"));
+    MOE_TRY(need(save_pre_s, "save_pre_s"));
+    MOE_TRY(need(save_h_s, "save_h_s"));
+    MOE_TRY(need(dy, "dy"));
+    MOE_TRY(need(dx_shared, "dx_shared"));
+    MOE_TRY(need(dsw13, "dsw13"));
+    MOE_TRY(need(dsw2, "dsw2"));
+  }
+  MOE_TRY(check_ws(desc, MOE_OP_FFN_BWD, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t d = desc->d, f = desc->f, P = pre_cols(desc);
+  if (desc->T == 0) {
+    // no rows: every weight gradient is zero
+    MOE_TRY(hip_check(launch_fill_zero(dw13, (size_t)desc->E * P * d * esize(desc), s), "zero dw13"));
+    MOE_TRY(hip_check(launch_fill_zero(dw2, (size_t)desc->E * d * f * esize(desc), s), "zero dw2"));
+    if (desc->n_shared) {
+      MOE_TRY(hip_check(launch_fill_zero(dsw13, (size_t)P * d * esize(desc), s), "zero dsw13"));
+      MOE_TRY(hip_check(launch_fill_zero(dsw2, (size_t)d * f * esize(desc), s), "zero dsw2"));
+    }
+    return MOE_OK;
+  }
+  void* dpre_r = ws;
+  void* dpre_s = (char*)ws + align256((size_t)desc->T * desc->k * P * esize(desc));
+  const int epi_b = desc->act == MOE_SWIGLU ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
+  for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
+    const int ragm = shared ? RAG_NONE : RAG_M;
+    const int ragk = shared ? RAG_NONE : RAG_K;
+    const int G = shared ? 1 : (int)desc->E;
+    void* dpre = shared ? dpre_s : dpre_r;
+    const void* go = shared ? dy : dout;            // upstream gradient rows
+    const void* xin = shared ? x : x_perm;
+    const void* hs = shared ? save_h_s : save_h;
+    // dgrad 1: dH = dO W2 (W2 read K-strided), activation backward in the epilogue
+    GemmArgs p = blank();
+    p.a = opnd(go, d, 0, 1);
+    p.b = opnd(shared ? sw2 : w2, f, d * f, 0);
+    p.c = dpre;
+    p.ldc = P;
+    p.c_rowidx = 1;
+    p.aux = (void*)(shared ? save_pre_s : save_pre);
+    p.ldaux = P;
+    p.aux_rowidx = 1;
+    p.offsets = offsets;
+    p.G = G;
+    p.M = desc->T;
+    p.N = f;
+    p.K = d;
+    p.fdim = f;
+    p.max_rows = desc->T * desc->k;
+    MOE_TRY(run_gemm(desc, p, true, false, epi_b, ragm, s, "ffn dgrad down matrix"));
+    // dgrad 2: dX = dpre W13 (W13 read K-strided)
+    GemmArgs q = blank();
+    q.a = opnd(dpre, P, 0, 1);
+    q.b = opnd(shared ? sw13 : w13, d, P * d, 0);
+    q.c = shared ? dx_shared : dx_perm;
+    q.ldc = d;
+    q.c_rowidx = 1;
+    q.offsets = offsets;
+    q.G = G;
+    q.M = desc->T;
+    q.N = d;
+    q.K = P;
+    q.max_rows = p.max_rows;
+    MOE_TRY(run_gemm(desc, q, true, false, EPI_STORE, ragm, s, "ffn dgrad first matrix"));
+    // wgrad 2: dW2 = dO^T H (reduce over the expert's rows)
+    GemmArgs r = blank();
+    r.a = opnd(go, d, 0, 1);
+    r.b = opnd(hs, f, 0, 1);
+    r.c = shared ? dsw2 : dw2;
+    r.ldc = f;
+    r.c_gstride = d * f;
+    r.offsets = offsets;
+    r.G = G;
+    r.M = d;
+    r.N = f;
+    r.K = desc->T;
+    MOE_TRY(run_gemm(desc, r, false, false, EPI_STORE, ragk, s, "ffn wgrad down matrix"));
+    // wgrad 1: dW13 = dpre^T X
+    GemmArgs w = blank();
+    w.a = opnd(dpre, P, 0, 1);
+    w.b = opnd(xin, d, 0, 1);
+    w.c = shared ? dsw13 : dw13;
+    w.ldc = d;
+    w.c_gstride = P * d;
+    w.offsets = offsets;
+    w.G = G;
+    w.M = P;
+    w.N = d;
+    w.K = desc->T;
+    MOE_TRY(run_gemm(desc, w, false, false, EPI_STORE, ragk, s, "ffn wgrad first matrix"));
+  }
+  return MOE_OK;
+}
+
+int moe_combine(const moe_desc* desc, const void* out, const void* out_shared, const float* gate,
+                const int32_t* row_of, void* y, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(out, "out"));
+  MOE_TRY(opt(out_shared, "out_shared"));
+  MOE_TRY(need(gate, "gate"));
+  MOE_TRY(need(row_of, "row_of"));
+  MOE_TRY(need(y, "y"));
+  if (desc->T == 0) return MOE_OK;
+  return hip_check(launch_combine(out, out_shared, desc->dtype == MOE_BF16, gate, row_of,
+                                  (int)desc->T, (int)desc->k, desc->d, y, (hipStream_t)stream),
+                   "combine");
+}
+
+int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const float* gate,
+                    const int32_t* row_of, float* dgate, void* dout, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(dy, "dy"));
+  MOE_TRY(need(out, "out"));
+  MOE_TRY(need(gate, "gate"));
+  MOE_TRY(need(row_of, "row_of"));
+  MOE_TRY(need(dgate, "dgate"));
+  MOE_TRY(need(dout, "dout"));
+  if (desc->T == 0) return MOE_OK;
+  return hip_check(launch_combine_bwd(dy, out, desc->dtype == MOE_BF16, gate, row_of,
+                                      (int)desc->T, (int)desc->k, desc->d, dgate, dout,
+                                      (hipStream_t)stream),
+                   "combine bwd");
+}
+
+int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const float* scores,
+                  const int32_t* topk_idx, const float* gate, const float* dgate, const float* y,
+                  float aux_coef, float* dlogits, float* dx_router, float* dw_r, void* ws,
+                  size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(w_r, "w_r"));
+  MOE_TRY(need(scores, "scores"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(gate, "gate"));
+  MOE_TRY(need(dgate, "dgate"));
+  if (aux_coef != 0.0f) MOE_TRY(need(y, "y"));
+  if (!(aux_coef == aux_coef)) return fail(MOE_ERR_INVALID_ARG, "aux_coef is NaN");
+  MOE_TRY(need(dlogits, "dlogits"));
+  MOE_TRY(need(dx_router, "dx_router"));
+  MOE_TRY(need(dw_r, "dw_r"));
+  MOE_TRY(check_ws(desc, MOE_OP_ROUTE_BWD, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->T == 0)
+    return hip_check(launch_fill_zero(dw_r, (size_t)desc->E * desc->d * 4, s), "zero dw_r");
+  const int T = (int)desc->T, E = (int)desc->E, k = (int)desc->k;
+  MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, T, E, k,
+                                          desc->score, dlogits, s),
+                    "router dlogits"));
+  // dw_r = dl^T x, split over tokens, partials folded in a fixed order
+  const int S = route_bwd_splits(desc);
+  GemmArgs p = blank();
+  p.a = opnd(dlogits, E, 0, 1);
+  p.b = opnd(x, desc->d, 0, 1);
+  p.c = S > 1 ? ws : (void*)dw_r;
+  p.ldc = desc->d;
+  p.G = 1;
+  p.M = E;
+  p.N = desc->d;
+  p.K = T;
+  p.k_splits = S;
+  MOE_TRY(hip_check(gemm_router_dw(p, desc->dtype == MOE_BF16, s), "router dw"));
+  if (S > 1)
+    MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
+                      "router dw reduce"));
+  // dx_router = dl W_r
+  if (aux_coef == 0.0f)
+    return hip_check(launch_router_dx_sparse(dlogits, topk_idx, w_r, T, E, k, desc->d, dx_router, s),
+                     "router dx");
+  GemmArgs q = blank();
+  q.a = opnd(dlogits, E, 0, 1);
+  q.b = opnd(w_r, desc->d, 0, 0);
+  q.c = dx_router;
+  q.ldc = desc->d;
+  q.G = 1;
+  q.M = T;
+  q.N = desc->d;
+  q.K = E;
+  return hip_check(gemm_router_dx(q, s), "router dx");
+}
+
+int moe_permute_bwd(const moe_desc* desc, const void* dx_perm, const int32_t* row_of,
+                    const void* dx_shared, const float* dx_router, void* dx, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(dx_perm, "dx_perm"));
+  MOE_TRY(need(row_of, "row_of"));
+  MOE_TRY(opt(dx_shared, "dx_shared"));
+  MOE_TRY(opt(dx_router, "dx_router"));
+  MOE_TRY(need(dx, "dx"));
+  if (desc->T == 0) return MOE_OK;
+  return hip_check(launch_unpermute(dx_perm, row_of, dx_shared, dx_router,
+                                    desc->dtype == MOE_BF16, (int)desc->T, (int)desc->k, desc->d,
+                                    dx, (hipStream_t)stream),
+                   "un-permute");
+}
+
+}  // extern "C"

@@ -1,0 +1,584 @@
+// Router top-k, load-balance statistics, permute (local dispatch), combine,
+// and their backward companions. All HBM-bound or latency-bound; each is a
+// plain streaming kernel with 16-byte accesses and fixed reduction orders.
+#include "common.h"
+
+namespace moe {
+
+// --------------------------------------------------------------- router
+// One wave per token. Experts e = lane + 64*i live in registers (EPL per lane).
+// Softmax is max-subtracted; top-k is k rounds of a wave arg-max on the
+// selection key with ties to the lower expert index.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int k, int score,
+                                                          const float* __restrict__ sel_bias,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ gate,
+                                                          float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* lrow = logits + t * E;
+  float s[EPL], key[EPL];
+  if (score == 0) {
+    float l[EPL], m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = e < E ? lrow[e] : -INFINITY;
+      m = fmaxf(m, l[i]);
+    }
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      s[i] = e < E ? expf(l[i] - m) : 0.f;
+      sum += s[i];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s[i] *= inv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      s[i] = e < E ? 1.0f / (1.0f + expf(-lrow[e])) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      scores[t * E + e] = s[i];
+      key[i] = s[i] + (sel_bias ? sel_bias[e] : 0.f);
+    } else {
+      key[i] = -INFINITY;
+    }
+  }
+  float chosen_sum = 0.f;
+  float my_s = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] > bk) { bk = key[i]; be = lane + 64 * i; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; }
+    }
+    const int owner = be & 63, slot = be >> 6;
+    float sv = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i == slot) {
+        sv = s[i];
+        if (lane == owner) key[i] = -INFINITY;
+      }
+    sv = __shfl(sv, owner, 64);
+    chosen_sum += sv;
+    if (lane == j) { my_s = sv; my_e = be; }
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_e;
+    gate[t * k + lane] = my_s / chosen_sum;
+  }
+}
+
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
+                              const float* sel_bias, int32_t* topk, float* gate, float* scores,
+                              hipStream_t st) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(router_topk_kernel<1>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+  else if (E <= 128)
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+  else if (E <= 256)
+    hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ aux stats
+// Pass 1: block b sums scores over tokens [256b, 256b+256) per expert
+// (float64, sequential in token order) and counts its assignments.
+__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ topk, int T,
+                                                          int E, int k, double* __restrict__ pz,
+                                                          int32_t* __restrict__ pc) {
+  __shared__ int hist[1024];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int t0 = b * 256, t1 = min(T, t0 + 256);
+  for (int i = t0 * k + tid; i < t1 * k; i += 256) atomicAdd(&hist[topk[i]], 1);
+  for (int e = tid; e < E; e += 256) {
+    double z = 0.0;
+    for (int t = t0; t < t1; ++t) z += (double)scores[(int64_t)t * E + e];
+    pz[(int64_t)b * E + e] = z;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) pc[(int64_t)b * E + e] = hist[e];
+}
+
+// Pass 2 (one block): fold the partials in block order.
+__global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict__ pz,
+                                                        const int32_t* __restrict__ pc, int nb,
+                                                        int T, int E, int k,
+                                                        int32_t* __restrict__ counts,
+                                                        float* __restrict__ y,
+                                                        float* __restrict__ z,
+                                                        float* __restrict__ out2) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  for (int e = tid; e < E; e += 256) {
+    double zs = 0.0;
+    int64_t c = 0;
+    for (int b = 0; b < nb; ++b) {
+      zs += pz[(int64_t)b * E + e];
+      c += pc[(int64_t)b * E + e];
+    }
+    const double zz = zs / (double)T;
+    const double yy = (double)c / ((double)T * (double)k);
+    counts[e] = (int32_t)c;
+    y[e] = (float)yy;
+    z[e] = (float)zz;
+    acc += yy * zz;
+  }
+  red[tid] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out2[0] = (float)red[0];
+    out2[1] = (float)(red[0] * (double)E);
+  }
+}
+
+hipError_t launch_aux_stats(const float* scores, const int32_t* topk, int T, int E, int k,
+                            double* pz, int32_t* pc, int32_t* counts, float* y, float* z,
+                            float* out2, hipStream_t st) {
+  const int nb = (T + 255) / 256;
+  hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, st, scores, topk, T, E, k, pz, pc);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, st, pz, pc, nb, T, E, k, counts, y, z, out2);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- permute
+// 64-token blocks. (1) per-block histogram; (2) per expert, exclusive scan
+// over blocks (in place) and capacity-clipped exclusive scan over experts;
+// (3) per block, rank of each assignment among earlier tokens of the block
+// routed to the same expert (wave ballot), giving its row.
+__global__ __launch_bounds__(64) void perm_hist_kernel(const int32_t* __restrict__ topk, int T,
+                                                       int E, int k, int32_t* __restrict__ hist) {
+  __shared__ int h[1024];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  const int t = b * 64 + lane;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicAdd(&h[topk[(int64_t)t * k + j]], 1);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) hist[(int64_t)b * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ hist, int nb, int T,
+                                                         int E, int k, int64_t cap,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ n_dropped) {
+  __shared__ int sc[1024];
+  const int tid = threadIdx.x;
+  int kept = 0;
+  if (tid < E) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int v = hist[(int64_t)b * E + tid];
+      hist[(int64_t)b * E + tid] = run;
+      run += v;
+    }
+    kept = (cap >= 0 && (int64_t)run > cap) ? (int)cap : run;
+  }
+  sc[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid + 1] = sc[tid];
+  if (tid == 0) {
+    offsets[0] = 0;
+    n_dropped[0] = T * k - sc[E - 1];
+  }
+}
+
+__global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ topk, int T,
+                                                       int E, int k, int64_t cap,
+                                                       const int32_t* __restrict__ base,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ row_of,
+                                                       int32_t* __restrict__ token_of) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int t = b * 64 + lane;
+  int mine[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mine[j] = (t < T && j < k) ? topk[(int64_t)t * k + j] : -1;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = 0; e < E; ++e) {
+    int slot = -1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (mine[j] == e) slot = j;
+    const uint64_t m = __ballot(slot >= 0);
+    if (m == 0) continue;
+    if (slot >= 0) {
+      const int64_t rank = (int64_t)base[(int64_t)b * E + e] + __popcll(m & lt);
+      if (cap < 0 || rank < cap) {
+        const int row = offsets[e] + (int)rank;
+        row_of[(int64_t)t * k + slot] = row;
+        token_of[row] = t;
+      } else {
+        row_of[(int64_t)t * k + slot] = -1;
+      }
+    }
+  }
+}
+
+// One block per token: read x[t] once, write it to each kept row.
+template <typename T>
+__global__ __launch_bounds__(256) void perm_gather_kernel(const T* __restrict__ x,
+                                                          const int32_t* __restrict__ row_of,
+                                                          int k, int64_t d,
+                                                          T* __restrict__ x_perm) {
+  const int64_t t = blockIdx.x;
+  int rows[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rows[j] = j < k ? row_of[t * k + j] : -1;
+  constexpr int EL = 16 / sizeof(T);
+  const int64_t nch = d / EL;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    const uint4 v = src[c];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (rows[j] >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)rows[j] * d)[c] = v;
+  }
+}
+
+hipError_t launch_permute(const void* x, bool bf16, const int32_t* topk, int T, int E, int k,
+                          int64_t d, int64_t cap, int32_t* hist, int32_t* offsets,
+                          int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* x_perm,
+                          hipStream_t st) {
+  const int nb = (T + 63) / 64;
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(64), 0, st, topk, T, E, k, hist);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nb, T, E, k, cap, offsets, n_dropped);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(64), 0, st, topk, T, E, k, cap, hist, offsets, row_of, token_of);
+  if (bf16)
+    hipLaunchKernelGGL(perm_gather_kernel<bf16_t>, dim3(T), dim3(256), 0, st,
+                       (const bf16_t*)x, row_of, k, d, (bf16_t*)x_perm);
+  else
+    hipLaunchKernelGGL(perm_gather_kernel<float>, dim3(T), dim3(256), 0, st,
+                       (const float*)x, row_of, k, d, (float*)x_perm);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- combine
+// y[t] = out_shared[t] + sum_j gate[t,j] * out[row_of[t,j]] (slot order).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
+                                                      const T* __restrict__ out_shared,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ row_of, int k,
+                                                      int64_t d, T* __restrict__ y) {
+  const int64_t t = blockIdx.x;
+  int rows[16];
+  float g[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    rows[j] = j < k ? row_of[t * k + j] : -1;
+    g[j] = j < k ? gate[t * k + j] : 0.f;
+  }
+  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8], v[8];
+    if (out_shared) {
+      Vec8<T>::load(out_shared + t * d + c, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rows[j] < 0) continue;
+      Vec8<T>::load(out + (int64_t)rows[j] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+    }
+    Vec8<T>::store(y + t * d + c, acc);
+  }
+}
+
+// dgate[t,j] = <dy[t], out[row]>, dout[row] = gate * dy[t]; one block per token.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
+                                                          const T* __restrict__ out,
+                                                          const float* __restrict__ gate,
+                                                          const int32_t* __restrict__ row_of,
+                                                          int k, int64_t d,
+                                                          float* __restrict__ dgate,
+                                                          T* __restrict__ dout) {
+  __shared__ float red[4][16];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int rows[16];
+  float g[16], part[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    rows[j] = j < k ? row_of[t * k + j] : -1;
+    g[j] = j < k ? gate[t * k + j] : 0.f;
+    part[j] = 0.f;
+  }
+  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float vy[8], vo[8], w[8];
+    Vec8<T>::load(dy + t * d + c, vy);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rows[j] < 0) continue;
+      Vec8<T>::load(out + (int64_t)rows[j] * d + c, vo);
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p = fmaf(vy[i], vo[i], p);
+        w[i] = g[j] * vy[i];
+      }
+      part[j] += p;
+      Vec8<T>::store(dout + (int64_t)rows[j] * d + c, w);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= k) break;
+    const float s = wave_sum(part[j]);
+    if (lane == 0) red[wave][j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x;
+    dgate[t * k + j] = rows[j] < 0 ? 0.f : ((red[0][j] + red[1][j]) + (red[2][j] + red[3][j]));
+  }
+}
+
+// dx[t] = dx_shared[t] + sum_j dx_perm[row_of[t,j]] + dx_router[t]; one rounding.
+template <typename T>
+__global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dx_perm,
+                                                        const int32_t* __restrict__ row_of,
+                                                        const T* __restrict__ dx_shared,
+                                                        const float* __restrict__ dx_router,
+                                                        int k, int64_t d, T* __restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  int rows[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rows[j] = j < k ? row_of[t * k + j] : -1;
+  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8], v[8];
+    if (dx_shared) {
+      Vec8<T>::load(dx_shared + t * d + c, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rows[j] < 0) continue;
+      Vec8<T>::load(dx_perm + (int64_t)rows[j] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (dx_router) {
+      Vec8<float>::load(dx_router + t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<T>::store(dx + t * d + c, acc);
+  }
+}
+
+hipError_t launch_combine(const void* out, const void* out_shared, bool bf16, const float* gate,
+                          const int32_t* row_of, int T, int k, int64_t d, void* y, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)out,
+                       (const bf16_t*)out_shared, gate, row_of, k, d, (bf16_t*)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)out,
+                       (const float*)out_shared, gate, row_of, k, d, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dy, const void* out, bool bf16, const float* gate,
+                              const int32_t* row_of, int T, int k, int64_t d, float* dgate,
+                              void* dout, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)dy,
+                       (const bf16_t*)out, gate, row_of, k, d, dgate, (bf16_t*)dout);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)dy,
+                       (const float*)out, gate, row_of, k, d, dgate, (float*)dout);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const void* dx_perm, const int32_t* row_of, const void* dx_shared,
+                            const float* dx_router, bool bf16, int T, int k, int64_t d, void* dx,
+                            hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(unpermute_kernel<bf16_t>, dim3(T), dim3(256), 0, st,
+                       (const bf16_t*)dx_perm, row_of, (const bf16_t*)dx_shared, dx_router, k, d,
+                       (bf16_t*)dx);
+  else
+    hipLaunchKernelGGL(unpermute_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)dx_perm,
+                       row_of, (const float*)dx_shared, dx_router, k, d, (float*)dx);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- router backward
+// One wave per token: dlogits[t, :] from the renormalised-gate gradient and
+// the optional aux term (y held fixed).
+template <int EPL>
+__global__ __launch_bounds__(256) void router_dlogits_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ topk,
+    const float* __restrict__ gate, const float* __restrict__ dgate, const float* __restrict__ y,
+    float aux_coef, int T, int E, int k, int score, float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float inner = 0.f, ssum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    inner = fmaf(gate[t * k + j], dgate[t * k + j], inner);
+    ssum += scores[t * E + topk[t * k + j]];
+  }
+  float s[EPL], out[EPL];
+  float ys = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    s[i] = e < E ? scores[t * E + e] : 0.f;
+    out[i] = 0.f;
+    if (aux_coef != 0.f && e < E) ys = fmaf(y[e], s[i], ys);
+  }
+  if (aux_coef != 0.f && score == 0) ys = wave_sum(ys);
+  for (int j = 0; j < k; ++j) {
+    const int e = topk[t * k + j];
+    const float g = gate[t * k + j], dg = dgate[t * k + j];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (lane + 64 * i != e) continue;
+      if (score == 0) out[i] = g * (dg - inner);
+      else out[i] = s[i] * (1.f - s[i]) * (dg - inner) / ssum;
+    }
+  }
+  const float c = aux_coef * (float)E / (float)T;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) continue;
+    if (aux_coef != 0.f) {
+      if (score == 0) out[i] += c * s[i] * (y[e] - ys);
+      else out[i] += c * y[e] * s[i] * (1.f - s[i]);
+    }
+    dl[t * E + e] = out[i];
+  }
+}
+
+hipError_t launch_router_dlogits(const float* scores, const int32_t* topk, const float* gate,
+                                 const float* dgate, const float* y, float aux_coef, int T, int E,
+                                 int k, int score, float* dl, hipStream_t st) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(router_dlogits_kernel<1>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+  else if (E <= 128)
+    hipLaunchKernelGGL(router_dlogits_kernel<2>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+  else if (E <= 256)
+    hipLaunchKernelGGL(router_dlogits_kernel<4>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+  else
+    hipLaunchKernelGGL(router_dlogits_kernel<16>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+  return hipGetLastError();
+}
+
+// dx_router[t] = sum_j dl[t, e_j] W_r[e_j] when dl is zero off the chosen
+// experts (no aux term): a k-row gather of W_r per token.
+__global__ __launch_bounds__(256) void router_dx_sparse_kernel(const float* __restrict__ dl,
+                                                               const int32_t* __restrict__ topk,
+                                                               const float* __restrict__ w_r,
+                                                               int E, int k, int64_t d,
+                                                               float* __restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  int es[16];
+  float c[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    es[j] = j < k ? topk[t * k + j] : -1;
+    c[j] = j < k ? dl[t * E + es[j]] : 0.f;
+  }
+  for (int64_t col = threadIdx.x * 8; col < d; col += 256 * 8) {
+    float acc[8], v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (es[j] < 0) continue;
+      Vec8<float>::load(w_r + (int64_t)es[j] * d + col, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(c[j], v[i], acc[i]);
+    }
+    Vec8<float>::store(dx + t * d + col, acc);
+  }
+}
+
+hipError_t launch_router_dx_sparse(const float* dl, const int32_t* topk, const float* w_r, int T,
+                                   int E, int k, int64_t d, float* dx, hipStream_t st) {
+  hipLaunchKernelGGL(router_dx_sparse_kernel, dim3(T), dim3(256), 0, st, dl, topk, w_r, E, k, d, dx);
+  return hipGetLastError();
+}
+
+// zero n 16-byte words (a kernel, so the call stays graph-capturable)
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  int64_t nb = (n + 255) / 256;
+  if (nb > 65536) nb = 65536;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nb), dim3(256), 0, st, (uint4*)p, n);
+  return hipGetLastError();
+}
+
+// out[i] = sum_s part[s][i], s ascending
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int S, int64_t n,
+                                                            float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < S; ++s) acc += part[(int64_t)s * n + i];
+  out[i] = acc;
+}
+
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     part, S, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+"""One MoE layer's forward and backward as an ordered sequence of libmoe
+calls on one stream. Buffers come from torch (device memory only); the
+routed-row buffers are sized for the worst case T*k rows, so no call ever
+waits on the device to learn how many rows were kept.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE, MOE_OP_ROUTE,
+               MOE_OP_ROUTE_BWD, aux_stats, combine, combine_bwd, grouped_ffn_bwd,
+               grouped_ffn_fwd, make_desc, permute, permute_bwd, route, route_bwd,
+               workspace_size)
+
+
+class MoELayer:
+    """Buffers and call order of one layer.
+
+    Weights/inputs are passed at call time (the layer owns no parameters):
+    x [T,d], w_r [E,d] fp32, w13 [E,2f|f,d], w2 [E,d,f], optional shared
+    sw13/sw2, optional logit_bias/sel_bias [E] fp32, dy [T,d].
+    """
+
+    def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
+                 capacity: Optional[int] = None, aux_coef: float = 0.0, device="cuda"):
+        self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity)
+        self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
+        self.n_shared, self.aux_coef = n_shared, aux_coef
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.dt = dt
+        P = 2 * f if act == "swiglu" else f
+        R = T * k
+        dev = torch.device(device)
+        i32, f32 = torch.int32, torch.float32
+
+        def z(*shape, dtype=dt):
+            # never hand out a NULL pointer: zero-row buffers are views of one row
+            full = (max(shape[0], 1),) + tuple(shape[1:])
+            return torch.empty(*full, dtype=dtype, device=dev)[: shape[0]]
+
+        # forward
+        self.topk_idx = z(T, k, dtype=i32)
+        self.gate = z(T, k, dtype=f32)
+        self.scores = z(T, E, dtype=f32)
+        self.counts = z(E, dtype=i32)
+        self.y_frac = z(E, dtype=f32)
+        self.z_mean = z(E, dtype=f32)
+        self.aux_out = z(2, dtype=f32)
+        self.offsets = z(E + 1, dtype=i32)
+        self.row_of = z(T, k, dtype=i32)
+        self.token_of = z(max(R, 1), dtype=i32)
+        self.n_dropped = z(1, dtype=i32)
+        self.x_perm = z(R, d)
+        self.save_pre = z(R, P)
+        self.save_h = z(R, f)
+        self.out = z(R, d)
+        self.save_pre_s = z(T, P) if n_shared else None
+        self.save_h_s = z(T, f) if n_shared else None
+        self.out_shared = z(T, d) if n_shared else None
+        self.Y = z(T, d)
+        # backward
+        self.dgate = z(T, k, dtype=f32)
+        self.dout = z(R, d)
+        self.dx_perm = z(R, d)
+        self.dx_shared = z(T, d) if n_shared else None
+        self.dw13 = z(E, P, d)
+        self.dw2 = z(E, d, f)
+        self.dsw13 = z(1, P, d) if n_shared else None
+        self.dsw2 = z(1, d, f) if n_shared else None
+        self.dlogits = z(T, E, dtype=f32)
+        self.dx_router = z(T, d, dtype=f32)
+        self.dw_r = z(E, d, dtype=f32)
+        self.dX = z(T, d)
+        wsb = max(workspace_size(self.desc, op) for op in (
+            MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
+            MOE_OP_ROUTE_BWD))
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    # ------------------------------------------------------------ stages
+    def forward(self, x, w_r, w13, w2, sw13=None, sw2=None, logit_bias=None, sel_bias=None):
+        D = self.desc
+        route(D, x, w_r, logit_bias, sel_bias, self.topk_idx, self.gate, self.scores, self.ws)
+        aux_stats(D, self.scores, self.topk_idx, self.counts, self.y_frac, self.z_mean,
+                  self.aux_out, self.ws)
+        permute(D, x, self.topk_idx, self.offsets, self.row_of, self.token_of, self.n_dropped,
+                self.x_perm, self.ws)
+        grouped_ffn_fwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
+                        self.save_h, self.save_pre_s, self.save_h_s, self.out, self.out_shared,
+                        self.ws)
+        combine(D, self.out, self.out_shared, self.gate, self.row_of, self.Y)
+        return self.Y
+
+    def backward(self, dy, x, w_r, w13, w2, sw13=None, sw2=None):
+        D = self.desc
+        combine_bwd(D, dy, self.out, self.gate, self.row_of, self.dgate, self.dout)
+        grouped_ffn_bwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
+                        self.save_h, self.save_pre_s, self.save_h_s, self.dout, dy, self.dx_perm,
+                        self.dx_shared, self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws)
+        route_bwd(D, x, w_r, self.scores, self.topk_idx, self.gate, self.dgate, self.y_frac,
+                  self.aux_coef, self.dlogits, self.dx_router, self.dw_r, self.ws)
+        permute_bwd(D, self.dx_perm, self.row_of, self.dx_shared, self.dx_router, self.dX)
+        return self.dX
+
+    def step(self, inp: dict):
+        """Forward then backward over one batch; inp holds the device tensors."""
+        self.forward(inp["x"], inp["w_r"], inp["w13"], inp["w2"], inp.get("sw13"),
+                     inp.get("sw2"), inp.get("logit_bias"), inp.get("sel_bias"))
+        self.backward(inp["dy"], inp["x"], inp["w_r"], inp["w13"], inp["w2"], inp.get("sw13"),
+                      inp.get("sw2"))

@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_28_amd as moe
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = _declared()
+    assert len(names) == 14
+    assert sorted(moe.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+# fake, aligned, non-null device addresses: validation must fail (or, for
+# T = 0, succeed) before anything touches them
+FAKE = 0x100000
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def _desc(**kw):
+    base = dict(T=64, d=64, E=8, k=2, f=64)
+    base.update(kw)
+    return moe.make_desc(**base)
+
+
+def test_desc_validation():
+    L = moe.lib()
+    bad = [
+        _desc(d=60), _desc(f=12), _desc(k=0), _desc(k=9), _desc(E=0), _desc(E=2000),
+        _desc(T=-1), _desc(n_shared=2),
+    ]
+    for d in bad:
+        out = ctypes.c_size_t()
+        s = L.moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(out))
+        assert s in (1, 2), (d.d, d.f, d.k, d.E, d.T)
+        assert L.moe_last_error().decode()
+    d = _desc()
+    d.dtype = 7
+    assert L.moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(ctypes.c_size_t())) == 1
+    d = _desc(k=17, E=32)
+    assert L.moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(ctypes.c_size_t())) == 2
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = moe.lib()
+    d = _desc()
+    ws = moe.workspace_size(d, moe.MOE_OP_ROUTE)
+    # x NULL
+    s = L.moe_route(ctypes.byref(d), None, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert s == 1 and "x is NULL" in L.moe_last_error().decode()
+    # misaligned gate
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE + 4, FAKE, FAKE, ws, None)
+    assert s == 1 and "aligned" in L.moe_last_error().decode()
+    # workspace too small
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws - 1, None)
+    assert s == 3
+    # combine without row_of
+    s = L.moe_combine(ctypes.byref(d), FAKE, None, FAKE, None, FAKE, None)
+    assert s == 1 and "row_of" in L.moe_last_error().decode()
+    # shared expert requested but its weights missing
+    ds = _desc(n_shared=1)
+    s = L.moe_grouped_ffn_fwd(ctypes.byref(ds), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert s == 1 and "sw13" in L.moe_last_error().decode()
+
+
+def test_zero_tokens_is_a_noop_without_touching_memory():
+    L = moe.lib()
+    d = _desc(T=0)
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.moe_aux_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.moe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.moe_combine(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None) == 0
+    assert L.moe_combine_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
+    assert L.moe_permute_bwd(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None) == 0
+
+
+@pytest.mark.parametrize("T,k,E,cf", [(1024, 1, 8, 1.25), (8192, 2, 8, 1.25), (4096, 2, 8, 1.0),
+                                      (1000, 3, 7, 1.1), (37, 2, 5, 0.33), (64, 2, 8, 0.0)])
+def test_capacity_matches_oracle(T, k, E, cf):
+    assert moe.capacity(T, k, E, cf) == O.capacity(T, k, E, cf)
+    assert moe.capacity(T, k, E, None) is None
+
+
+def test_workspace_sizes_cover_the_layer():
+    d = moe.make_desc(8192, 4096, 8, 2, 14336, capacity=2560)
+    sizes = [moe.workspace_size(d, op) for op in range(6)]
+    # backward needs the [T*k, 2f] activation-gradient buffer
+    assert sizes[moe.MOE_OP_FFN_BWD] >= 8192 * 2 * 2 * 14336 * 2
+    assert sizes[moe.MOE_OP_ROUTE] >= 8192 * 8 * 4
+    with pytest.raises(moe.MoeError):
+        moe.workspace_size(d, 99)
+
+
+def test_status_strings():
+    L = moe.lib()
+    assert L.moe_status_str(0) == b"ok"
+    assert L.moe_status_str(3) == b"workspace too small"
+
+
+def _header_params():
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(([^)]*)\)\s*;", text, re.M | re.S):
+        params = [p.strip() for p in m.group(2).replace("\n", " ").split(",") if p.strip()]
+        if params == ["void"]:
+            params = []
+        out[m.group(1)] = params
+    return out
+
+
+def _kind(param):
+    if "*" in param:
+        return "ptr"
+    if param.startswith("size_t"):
+        return "size_t"
+    if param.startswith("float"):
+        return "float"
+    if param.startswith("double"):
+        return "double"
+    if param.startswith("int64_t"):
+        return "int64"
+    if param.startswith("int"):
+        return "int"
+    raise AssertionError(param)
+
+
+def test_binding_signatures_match_header():
+    L = moe.lib()
+    ct = {ctypes.c_void_p: "ptr", ctypes.c_size_t: "size_t", ctypes.c_float: "float",
+          ctypes.c_double: "double", ctypes.c_int64: "int64", ctypes.c_int: "int"}
+    for name, params in _header_params().items():
+        want = [_kind(p) for p in params]
+        got = []
+        for a in getattr(L, name).argtypes:
+            got.append(ct.get(a, "ptr"))  # POINTER(...) types are pointers
+        assert got == want, (name, got, want)
