@@ -1,0 +1,236 @@
+"""Benchmark one MoE layer step (forward + backward, every stage of the hot
+path) on one MI355X, and print one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_bf16]
+
+A step = router, load-balance stats, permute, grouped FFN forward, combine,
+combine backward, grouped FFN backward, router backward, un-permute, over
+one batch of seeded synthetic inputs already resident in HBM. W untimed
+steps, then K steps between two synchronisations. Per-kernel durations come
+from the library's timing events (recorded on the launch stream) over the
+same timed steps; the roofline object is for the dominant kernel. The CPU
+oracle is timed on a bounded token sample of the same workload on the host
+cores (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from moe_inputs import WORKLOADS, as_f64, gen_all  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM % bf16 MFMA peak"
+GEMM_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_tile.h", "csrc/common.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(w, A):
+    """Algorithmic flops of each grouped-GEMM launch (only selected experts)."""
+    P = 2 * w.f if w.act == "swiglu" else w.f
+    d, f = w.d, w.f
+    out = {
+        "gemm_fwd_up": 2 * A * d * P, "gemm_fwd_down": 2 * A * f * d,
+        "gemm_dgrad_down": 2 * A * d * f, "gemm_dgrad_up": 2 * A * P * d,
+        "gemm_wgrad_down": 2 * A * d * f, "gemm_wgrad_up": 2 * A * P * d,
+    }
+    if w.n_shared:
+        T = w.T
+        out.update({
+            "gemm_shared_fwd_up": 2 * T * d * P, "gemm_shared_fwd_down": 2 * T * f * d,
+            "gemm_shared_dgrad_down": 2 * T * d * f, "gemm_shared_dgrad_up": 2 * T * P * d,
+            "gemm_shared_wgrad_down": 2 * T * d * f, "gemm_shared_wgrad_up": 2 * T * P * d,
+        })
+    return out
+
+
+def hbm_bytes(w, A):
+    """Algorithmic HBM bytes of the streaming stages (each tensor read or
+    written once)."""
+    s = 2 if w.dtype == "bf16" else 4
+    T, d, k = w.T, w.d, w.k
+    ns = T * d * s if w.n_shared else 0
+    return {
+        "permute": T * d * s + A * d * s + T * k * 4 * 3 + A * 4,
+        "combine": A * d * s + T * d * s + ns + T * k * 8,
+        "combine_bwd": T * d * s + 2 * A * d * s + T * k * 12,
+        "unpermute": A * d * s + T * d * 4 + ns + T * d * s + T * k * 4,
+    }
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_28_amd", rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current GEMM sources; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    try:
+        with open(path) as fh:
+            tr = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if tr.get("source_sha") != gemm_source_hash() or tr.get("workload") != workload:
+        return None
+    k = tr.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["bytes_per_launch"])
+
+
+def cpu_baseline(w, g, tokens):
+    """The oracle, as it stands, on the first `tokens` tokens of the workload
+    (same weights; capacity recomputed for the sample)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ws = w.replace(T=tokens)
+    f = {n: (as_f64(v, w.dtype) if v is not None else None) for n, v in g.items()}
+    x, dy = f["x"][:tokens], f["dy"][:tokens]
+    cap = O.capacity(ws.T, ws.k, ws.E, ws.cf)
+    t0 = time.perf_counter()
+    fwd = O.layer_forward(x, f["w_r"], f["w13"], f["w2"], ws.k, ws.score, ws.act, cap,
+                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"])
+    O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act, ws.aux_coef,
+                     f["sw13"], f["sw2"])
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {tokens} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in "
+                      f"float64 NumPy ({dt:.1f} s; bf16->float64 input conversion untimed)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without per-kernel events (roofline object omitted)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_28_amd as moe
+    from mixture_experts_layer_28_amd import MoELayer
+
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w}")
+    t0 = time.perf_counter()
+    g = gen_all(w)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    inp = {n: dev(v) for n, v in g.items()}
+    cap = moe.capacity(w.T, w.k, w.E, w.cf)
+    layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
+                     w.aux_coef)
+    for _ in range(args.warmup):
+        layer.step(inp)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.no_profile:
+        moe.profile_enable(True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer.step(inp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = moe.profile_read() if not args.no_profile else []
+    moe.profile_enable(False)
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    value = w.T * args.steps / (ms / 1e3)
+    A = int(layer.offsets[-1].item())
+    log(f"[bench] {ms_step:.3f} ms/step, {value:.0f} tokens/s, kept rows {A}")
+
+    flops = gemm_flops(w, A)
+    stages = {}
+    for name, tot, n in prof:
+        stages[name] = {"avg_ms": round(tot / n, 4), "launches": n}
+    roofline = None
+    gemm_tot_ms = sum(tot for name, tot, n in prof if name in flops)
+    gemm_flops_step = sum(flops.values())
+    if prof:
+        gk = [(tot, name, n) for name, tot, n in prof if name in flops]
+        tot, dom, n = max(gk)
+        avg_s = tot / n / 1e3
+        achieved = flops[dom] / avg_s / 1e12
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": dom,
+                    "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4),
+                    "traffic": traffic_for(dom, w.name),
+                    "flops_per_launch": flops[dom], "avg_ms": round(tot / n, 4)}
+        hb = hbm_bytes(w, A)
+        for name, b in hb.items():
+            if name in stages:
+                gbs = b / (stages[name]["avg_ms"] / 1e3) / 1e9
+                stages[name]["GB/s"] = round(gbs, 1)
+                stages[name]["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 3)
+        for name in flops:
+            if name in stages:
+                tf = flops[name] / (stages[name]["avg_ms"] / 1e3) / 1e12
+                stages[name]["TFLOP/s"] = round(tf, 1)
+    gemm_tflops = gemm_flops_step * args.steps / (gemm_tot_ms / 1e3) / 1e12 if gemm_tot_ms else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(w, g, args.cpu_tokens)
+        log(f"[bench] oracle: {cpu['value']:.2f} tokens/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
+                   "act": w.act, "score": w.score, "n_shared": w.n_shared,
+                   "capacity": cap, "kept_rows": A, "parallelism": "none (1 GPU)"},
+        "gemm_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
+        "gemm_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4) if gemm_tflops and w.dtype == "bf16" else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -240,6 +240,18 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void);
 int moe_abi_version(void);
 
+/* Per-kernel timing, for measurement and observability. While enabled
+ * (on != 0), every kernel launch the library makes is bracketed by two HIP
+ * timing events recorded on that launch's stream; enabling or disabling
+ * drops any unread records. moe_profile_read waits for the recorded events,
+ * then reports, per kernel name in first-launch order, the summed duration
+ * in milliseconds and the launch count, and clears the records. Up to `cap`
+ * entries are written to names/total_ms/launches (host arrays); *n receives
+ * the number of distinct kernels. The name strings are static. Not meant to
+ * be enabled while another thread launches through the library. */
+int moe_profile_enable(int on);
+int moe_profile_read(int cap, int* n, const char** names, double* total_ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_route", "moe_aux_stats", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
+    "moe_profile_enable", "moe_profile_read",
 )
 
 
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
             "moe_status_str": [ctypes.c_int],
             "moe_last_error": [],
             "moe_abi_version": [],
+            "moe_profile_enable": [ctypes.c_int],
+            "moe_profile_read": [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                 ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -114,6 +119,22 @@ def workspace_size(desc: MoeDesc, op: int) -> int:
     return int(out.value)
 
 
+def profile_enable(on: bool = True):
+    """Start (or stop) recording per-kernel timing events; drops unread records."""
+    _check("moe_profile_enable", lib().moe_profile_enable(1 if on else 0))
+
+
+def profile_read() -> list:
+    """[(kernel name, total ms, launches)] since profile_enable(True); clears them."""
+    cap = 64
+    n = ctypes.c_int()
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int * cap)()
+    _check("moe_profile_read", lib().moe_profile_read(cap, ctypes.byref(n), names, ms, cnt))
+    return [(names[i].decode(), float(ms[i]), int(cnt[i])) for i in range(min(n.value, cap))]
+
+
 def _p(t):
     """Device pointer of a tensor (None -> NULL)."""
     if t is None:
@@ -122,6 +143,8 @@ def _p(t):
         raise ValueError("tensors passed to libmoe must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors passed to libmoe must be contiguous")
+    if t.numel() == 0:   # torch reports 0 for empty views; hand over their storage
+        return t.untyped_storage().data_ptr() or None
     return t.data_ptr()
 
 

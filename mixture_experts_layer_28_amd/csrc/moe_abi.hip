@@ -4,7 +4,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -59,6 +62,74 @@ int hip_check(hipError_t e, const char* what) {
     int _s = (expr);                  \
     if (_s != MOE_OK) return _s;      \
   } while (0)
+
+// ------------------------------------------------------ kernel timing
+// While enabled, each kernel launch is bracketed by two timing events
+// recorded on the launch stream (moe_profile_enable / moe_profile_read).
+enum KernelId {
+  K_ROUTER_LOGITS, K_ROUTER_TOPK, K_AUX_STATS, K_PERMUTE,
+  K_FWD_UP, K_FWD_DOWN, K_DGRAD_DOWN, K_DGRAD_UP, K_WGRAD_DOWN, K_WGRAD_UP,
+  K_SH_FWD_UP, K_SH_FWD_DOWN, K_SH_DGRAD_DOWN, K_SH_DGRAD_UP, K_SH_WGRAD_DOWN, K_SH_WGRAD_UP,
+  K_COMBINE, K_COMBINE_BWD, K_ROUTER_DLOGITS, K_ROUTER_DW, K_ROUTER_DW_REDUCE, K_ROUTER_DX,
+  K_UNPERMUTE, K_FILL, K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {
+  "router_logits", "router_topk", "aux_stats", "permute",
+  "gemm_fwd_up", "gemm_fwd_down", "gemm_dgrad_down", "gemm_dgrad_up", "gemm_wgrad_down",
+  "gemm_wgrad_up",
+  "gemm_shared_fwd_up", "gemm_shared_fwd_down", "gemm_shared_dgrad_down", "gemm_shared_dgrad_up",
+  "gemm_shared_wgrad_down", "gemm_shared_wgrad_up",
+  "combine", "combine_bwd", "router_dlogits", "router_dw", "router_dw_reduce", "router_dx",
+  "unpermute", "fill_zero",
+};
+
+struct ProfRec {
+  int id;
+  hipEvent_t a, b;
+};
+struct Prof {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t take() {
+    std::lock_guard<std::mutex> g(mu);
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+
+class Scope {
+ public:
+  Scope(int id, hipStream_t s) : id_(id), s_(s) {
+    Prof& P = prof();
+    if (!P.on.load(std::memory_order_relaxed)) return;
+    a_ = P.take();
+    b_ = P.take();
+    if (a_ && b_) hipEventRecord(a_, s_);
+  }
+  ~Scope() {
+    if (!a_ || !b_) return;
+    hipEventRecord(b_, s_);
+    Prof& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    P.recs.push_back({id_, a_, b_});
+  }
+ private:
+  int id_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
 
 constexpr int64_t kMaxE = 1024;
 constexpr int64_t kMaxK = 16;
@@ -165,7 +236,8 @@ GemmArgs blank() {
 }
 
 int run_gemm(const moe_desc* d, const GemmArgs& p, bool akm, bool bkm, int epi, int rag,
-             hipStream_t s, const char* what) {
+             hipStream_t s, const char* what, int kid) {
+  Scope sc(kid, s);
   hipError_t e = d->dtype == MOE_BF16 ? gemm_bf16(p, akm, bkm, epi, rag, s)
                                       : gemm_f32(p, akm, bkm, epi, rag, s);
   return hip_check(e, what);
@@ -176,6 +248,52 @@ int run_gemm(const moe_desc* d, const GemmArgs& p, bool akm, bool bkm, int epi, 
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int moe_profile_enable(int on) {
+  g_err[0] = 0;
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (auto& r : P.recs) {
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.recs.clear();
+  P.on.store(on != 0);
+  return MOE_OK;
+}
+
+int moe_profile_read(int cap, int* n, const char** names, double* total_ms, int* launches) {
+  g_err[0] = 0;
+  if (!n || cap < 0 || (cap > 0 && (!names || !total_ms || !launches)))
+    return fail(MOE_ERR_INVALID_ARG, "bad output arrays");
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  double tot[K_COUNT] = {0};
+  int cnt[K_COUNT] = {0};
+  int order[K_COUNT];
+  int nk = 0;
+  for (auto& r : P.recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_check(e, "profile read");
+    if (cnt[r.id] == 0) order[nk++] = r.id;
+    tot[r.id] += ms;
+    cnt[r.id] += 1;
+  }
+  for (auto& r : P.recs) {
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.recs.clear();
+  *n = nk;
+  for (int i = 0; i < nk && i < cap; ++i) {
+    names[i] = kKernelNames[order[i]];
+    total_ms[i] = tot[order[i]];
+    launches[i] = cnt[order[i]];
+  }
+  return MOE_OK;
+}
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -240,7 +358,11 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   p.N = desc->E;
   p.K = desc->d;
   p.col_bias = logit_bias;
-  MOE_TRY(hip_check(gemm_router_logits(p, desc->dtype == MOE_BF16, s), "router logits"));
+  {
+    Scope sc(K_ROUTER_LOGITS, s);
+    MOE_TRY(hip_check(gemm_router_logits(p, desc->dtype == MOE_BF16, s), "router logits"));
+  }
+  Scope sc(K_ROUTER_TOPK, s);
   return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,
                                       desc->score, sel_bias, topk_idx, gate, scores, s),
                    "router top-k");
@@ -262,6 +384,7 @@ int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk
   const size_t nb = (size_t)(desc->T + 255) / 256;
   double* pz = (double*)ws;
   int32_t* pc = (int32_t*)((char*)ws + align256(nb * desc->E * 8));
+  Scope sc(K_AUX_STATS, (hipStream_t)stream);
   return hip_check(launch_aux_stats(scores, topk_idx, (int)desc->T, (int)desc->E, (int)desc->k,
                                     pz, pc, counts, y, z, out2, (hipStream_t)stream),
                    "aux stats");
@@ -281,6 +404,7 @@ int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, in
   MOE_TRY(need(x_perm, "x_perm"));
   MOE_TRY(check_ws(desc, MOE_OP_PERMUTE, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
+  Scope sc(K_PERMUTE, (hipStream_t)stream);
   return hip_check(launch_permute(x, desc->dtype == MOE_BF16, topk_idx, (int)desc->T,
                                   (int)desc->E, (int)desc->k, desc->d, desc->capacity,
                                   (int32_t*)ws, offsets, row_of, token_of, n_dropped, x_perm,
@@ -333,7 +457,8 @@ int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t*
     p.K = d;
     p.fdim = f;
     p.max_rows = desc->T * desc->k;
-    MOE_TRY(run_gemm(desc, p, true, true, epi1, rag, s, "ffn fwd first matrix"));
+    MOE_TRY(run_gemm(desc, p, true, true, epi1, rag, s, "ffn fwd first matrix",
+                     shared ? K_SH_FWD_UP : K_FWD_UP));
     GemmArgs q = blank();
     q.a = opnd(shared ? save_h_s : save_h, f, 0, 1);
     q.b = opnd(shared ? sw2 : w2, f, d * f, 0);
@@ -346,7 +471,8 @@ int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t*
     q.N = d;
     q.K = f;
     q.max_rows = p.max_rows;
-    MOE_TRY(run_gemm(desc, q, true, true, EPI_STORE, rag, s, "ffn fwd down matrix"));
+    MOE_TRY(run_gemm(desc, q, true, true, EPI_STORE, rag, s, "ffn fwd down matrix",
+                     shared ? K_SH_FWD_DOWN : K_FWD_DOWN));
   }
   return MOE_OK;
 }
@@ -421,7 +547,8 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     p.K = d;
     p.fdim = f;
     p.max_rows = desc->T * desc->k;
-    MOE_TRY(run_gemm(desc, p, true, false, epi_b, ragm, s, "ffn dgrad down matrix"));
+    MOE_TRY(run_gemm(desc, p, true, false, epi_b, ragm, s, "ffn dgrad down matrix",
+                     shared ? K_SH_DGRAD_DOWN : K_DGRAD_DOWN));
     // dgrad 2: dX = dpre W13 (W13 read K-strided)
     GemmArgs q = blank();
     q.a = opnd(dpre, P, 0, 1);
@@ -435,7 +562,8 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     q.N = d;
     q.K = P;
     q.max_rows = p.max_rows;
-    MOE_TRY(run_gemm(desc, q, true, false, EPI_STORE, ragm, s, "ffn dgrad first matrix"));
+    MOE_TRY(run_gemm(desc, q, true, false, EPI_STORE, ragm, s, "ffn dgrad first matrix",
+                     shared ? K_SH_DGRAD_UP : K_DGRAD_UP));
     // wgrad 2: dW2 = dO^T H (reduce over the expert's rows)
     GemmArgs r = blank();
     r.a = opnd(go, d, 0, 1);
@@ -448,7 +576,8 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     r.M = d;
     r.N = f;
     r.K = desc->T;
-    MOE_TRY(run_gemm(desc, r, false, false, EPI_STORE, ragk, s, "ffn wgrad down matrix"));
+    MOE_TRY(run_gemm(desc, r, false, false, EPI_STORE, ragk, s, "ffn wgrad down matrix",
+                     shared ? K_SH_WGRAD_DOWN : K_WGRAD_DOWN));
     // wgrad 1: dW13 = dpre^T X
     GemmArgs w = blank();
     w.a = opnd(dpre, P, 0, 1);
@@ -461,7 +590,8 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     w.M = P;
     w.N = d;
     w.K = desc->T;
-    MOE_TRY(run_gemm(desc, w, false, false, EPI_STORE, ragk, s, "ffn wgrad first matrix"));
+    MOE_TRY(run_gemm(desc, w, false, false, EPI_STORE, ragk, s, "ffn wgrad first matrix",
+                     shared ? K_SH_WGRAD_UP : K_WGRAD_UP));
   }
   return MOE_OK;
 }
@@ -476,6 +606,7 @@ int moe_combine(const moe_desc* desc, const void* out, const void* out_shared, c
   MOE_TRY(need(row_of, "row_of"));
   MOE_TRY(need(y, "y"));
   if (desc->T == 0) return MOE_OK;
+  Scope sc(K_COMBINE, (hipStream_t)stream);
   return hip_check(launch_combine(out, out_shared, desc->dtype == MOE_BF16, gate, row_of,
                                   (int)desc->T, (int)desc->k, desc->d, y, (hipStream_t)stream),
                    "combine");
@@ -492,6 +623,7 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
   MOE_TRY(need(dgate, "dgate"));
   MOE_TRY(need(dout, "dout"));
   if (desc->T == 0) return MOE_OK;
+  Scope sc(K_COMBINE_BWD, (hipStream_t)stream);
   return hip_check(launch_combine_bwd(dy, out, desc->dtype == MOE_BF16, gate, row_of,
                                       (int)desc->T, (int)desc->k, desc->d, dgate, dout,
                                       (hipStream_t)stream),
@@ -520,9 +652,12 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
   if (desc->T == 0)
     return hip_check(launch_fill_zero(dw_r, (size_t)desc->E * desc->d * 4, s), "zero dw_r");
   const int T = (int)desc->T, E = (int)desc->E, k = (int)desc->k;
-  MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, T, E, k,
-                                          desc->score, dlogits, s),
-                    "router dlogits"));
+  {
+    Scope sc(K_ROUTER_DLOGITS, s);
+    MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, T, E, k,
+                                            desc->score, dlogits, s),
+                      "router dlogits"));
+  }
   // dw_r = dl^T x, split over tokens, partials folded in a fixed order
   const int S = route_bwd_splits(desc);
   GemmArgs p = blank();
@@ -535,10 +670,16 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
   p.N = desc->d;
   p.K = T;
   p.k_splits = S;
-  MOE_TRY(hip_check(gemm_router_dw(p, desc->dtype == MOE_BF16, s), "router dw"));
-  if (S > 1)
+  {
+    Scope sc(K_ROUTER_DW, s);
+    MOE_TRY(hip_check(gemm_router_dw(p, desc->dtype == MOE_BF16, s), "router dw"));
+  }
+  if (S > 1) {
+    Scope sc(K_ROUTER_DW_REDUCE, s);
     MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
                       "router dw reduce"));
+  }
+  Scope sc(K_ROUTER_DX, s);
   // dx_router = dl W_r
   if (aux_coef == 0.0f)
     return hip_check(launch_router_dx_sparse(dlogits, topk_idx, w_r, T, E, k, desc->d, dx_router, s),
@@ -565,6 +706,7 @@ int moe_permute_bwd(const moe_desc* desc, const void* dx_perm, const int32_t* ro
   MOE_TRY(opt(dx_router, "dx_router"));
   MOE_TRY(need(dx, "dx"));
   if (desc->T == 0) return MOE_OK;
+  Scope sc(K_UNPERMUTE, (hipStream_t)stream);
   return hip_check(launch_unpermute(dx_perm, row_of, dx_shared, dx_router,
                                     desc->dtype == MOE_BF16, (int)desc->T, (int)desc->k, desc->d,
                                     dx, (hipStream_t)stream),

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
