@@ -163,6 +163,13 @@ int check_desc(const moe_desc* d) {
   if (d->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
   if (d->T * d->k >= (int64_t(1) << 31) || d->T * d->E >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k and T*E must be < 2^31");
+  {
+    // the GEMMs address each operand of one expert through 32-bit byte offsets
+    const int64_t es = d->dtype == MOE_BF16 ? 2 : 4;
+    const int64_t wid = d->d > 2 * d->f ? d->d : 2 * d->f;
+    if (d->T * d->k * wid * es >= (int64_t(1) << 31) || 2 * d->f * d->d * es >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "routed activations or one expert's weights exceed 2 GiB");
+  }
   return MOE_OK;
 }
 
