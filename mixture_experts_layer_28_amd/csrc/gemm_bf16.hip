@@ -196,25 +196,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   Strided<BN> sb;
   const int64_t nk = (t.K + kBK - 1) / kBK;
 
-  auto issue = [&](int64_t kt, bf16_t* as) {
+  auto issue = [&](int64_t kt, bf16_t* as) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK;
     if (AKM) direct_load<BM, false, WN>(ra, as, p.a.ld, t.M, t.m0, k0, t.K, p.fdim, wave, lane);
     else strided_load<BM>(sa, ra, p.a.ld, t.M, t.m0, k0, t.K);
     if (BKM) direct_load<BN, FUSED, WN>(rb, as + A_EL, p.b.ld, b_rows, t.n0, k0, t.K, p.fdim, wave, lane);
     else strided_load<BN>(sb, rb, p.b.ld, p.N, t.n0, k0, t.K);
   };
-  auto finish = [&](bf16_t* as) {
+  auto finish = [&](bf16_t* as) __attribute__((always_inline)) {
     if (!AKM) strided_store<BM>(sa, as);
     if (!BKM) strided_store<BN>(sb, as + A_EL);
   };
   // one k-step: loads of tile kt+1 into `nxt` (for kt+1 == nk every lane is
   // out of range and zeros land in the idle stage), MFMAs on `cur`
-  auto kstep = [&](int64_t kt, const bf16_t* cur, bf16_t* nxt) {
+  auto kstep = [&](int64_t kt, const bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
     issue(kt + 1, nxt);
     const bf16_t* as = cur;
     const bf16_t* bs = cur + A_EL;
     bf16x8 fa[2][MI], fb[2][NI];
-    auto ldfrag = [&](int buf, int kk) {
+    auto ldfrag = [&](int buf, int kk) __attribute__((always_inline)) {
       const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- epilogue: stage 32 rows of the wave's sub-tile at a time in LDS
   // (waves 0-1 in the first stage's space, waves 2-3 in the second's)
   float* stage = reinterpret_cast<float*>(wave < 2 ? lds0 : lds1) + (wave & 1) * (32 * LDST);
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  static_for<MI>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
 #pragma unroll
     for (int j = 0; j < NI; ++j)
 #pragma unroll
@@ -282,10 +282,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (FUSED)
       epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN / 2, m0,
                                  t.n0 + (wave & 1) * (WN / 2), lane, 64);
+    else if (EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD)
+      epilogue_act_bwd<(EPI == EPI_SWIGLU_BWD ? EPI_SWIGLU_BWD : EPI_GELU_BWD), 32, WN, 64>(
+          p, t, stage, LDST, m0, t.n0 + wn0, lane);
     else
       epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN, m0, t.n0 + wn0, lane, 64);
     __syncthreads();
-  }
+  });
 }
 
 // ------------------------------------------------------------------ launch

@@ -36,6 +36,8 @@ hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, i
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
+hipError_t launch_router_small(const void*, bool, const float*, const float*, const float*, int,
+                               int, int64_t, int, int, int32_t*, float*, float*, hipStream_t);
 }  // namespace moe
 
 using namespace moe;
@@ -354,6 +356,14 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   MOE_TRY(check_ws(desc, MOE_OP_ROUTE, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (desc->E <= 8) {
+    // few experts: logits, scores and top-k fused in one streaming pass over x
+    Scope sc(K_ROUTER_TOPK, s);
+    return hip_check(launch_router_small(x, desc->dtype == MOE_BF16, w_r, logit_bias, sel_bias,
+                                         (int)desc->T, (int)desc->E, desc->d, (int)desc->k,
+                                         desc->score, topk_idx, gate, scores, s),
+                     "router (fused)");
+  }
   float* logits = (float*)ws;
   GemmArgs p = blank();
   p.a = opnd(x, desc->d, 0, 1);

@@ -1,7 +1,7 @@
 // Router top-k, load-balance statistics, permute (local dispatch), combine,
 // and their backward companions. All HBM-bound or latency-bound; each is a
 // plain streaming kernel with 16-byte accesses and fixed reduction orders.
-#include "common.h"
+#include "gemm_tile.h"
 
 namespace moe {
 
@@ -103,6 +103,121 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int scor
     hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
   else
     hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+  return hipGetLastError();
+}
+
+// Fused router for few experts (E <= EMAX = 8): logits, scores and top-k in one
+// pass. A wave owns TPW tokens; lane l covers columns 8*(l + 64*q); the
+// per-lane partial dot products are summed across the wave (butterfly), then
+// every lane holds all E logits of its tokens and lanes 0..TPW-1 finish one
+// token each. x is read once from HBM; W_r rows are re-read from cache.
+template <typename TX, int EMAX, int TPW>
+__global__ __launch_bounds__(256) void router_small_kernel(
+    const TX* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ logit_bias,
+    const float* __restrict__ sel_bias, int T, int E, int64_t d, int k, int score,
+    int32_t* __restrict__ topk_idx, float* __restrict__ gate, float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= T) return;
+  float acc[TPW][EMAX];
+#pragma unroll
+  for (int a = 0; a < TPW; ++a)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[a][e] = 0.f;
+  for (int64_t c = lane * 8; c < d; c += 512) {
+    float xv[TPW][8];
+#pragma unroll
+    for (int a = 0; a < TPW; ++a) {
+      const int64_t t = t0 + a < T ? t0 + a : T - 1;
+      Vec8<TX>::load(x + t * d + c, xv[a]);
+    }
+    static_for<EMAX>([&](auto EI) __attribute__((always_inline)) {
+      constexpr int e = decltype(EI)::value;
+      if (e < E) {
+        float wv[8];
+        Vec8<float>::load(w_r + (int64_t)e * d + c, wv);
+#pragma unroll
+        for (int a = 0; a < TPW; ++a)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[a][e] = fmaf(xv[a][i], wv[i], acc[a][e]);
+      }
+    });
+  }
+#pragma unroll
+  for (int a = 0; a < TPW; ++a)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[a][e] = wave_sum(acc[a][e]);
+  // lane a < TPW finishes token t0 + a (a select chain keeps acc in registers)
+  float l[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    float v = acc[0][e];
+#pragma unroll
+    for (int a = 1; a < TPW; ++a) v = lane == a ? acc[a][e] : v;
+    l[e] = v;
+  }
+  const int64_t t = t0 + lane;
+  if (lane >= TPW || t >= T) return;
+  float sc[EMAX], key[EMAX];
+  if (score == 0) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) {
+        l[e] += logit_bias ? logit_bias[e] : 0.f;
+        m = fmaxf(m, l[e]);
+      }
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      sc[e] = e < E ? expf(l[e] - m) : 0.f;
+      sum += sc[e];
+    }
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) sc[e] *= inv;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      sc[e] = e < E ? 1.0f / (1.0f + expf(-(l[e] + (logit_bias ? logit_bias[e] : 0.f)))) : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E) scores[t * E + e] = sc[e];
+    key[e] = e < E ? sc[e] + (sel_bias ? sel_bias[e] : 0.f) : -INFINITY;
+  }
+  float chosen = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY;
+    int be = 0;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (key[e] > bk) { bk = key[e]; be = e; }
+    float sv = 0.f;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e == be) { sv = sc[e]; key[e] = -INFINITY; }
+    topk_idx[t * k + j] = be;
+    gate[t * k + j] = sv;
+    chosen += sv;
+  }
+  const float inv = 1.0f / chosen;
+  for (int j = 0; j < k; ++j) gate[t * k + j] *= inv;
+}
+
+hipError_t launch_router_small(const void* x, bool bf16, const float* w_r, const float* logit_bias,
+                               const float* sel_bias, int T, int E, int64_t d, int k, int score,
+                               int32_t* topk, float* gate, float* scores, hipStream_t st) {
+  constexpr int TPW = 8;
+  const dim3 grid((unsigned)((T + 4 * TPW - 1) / (4 * TPW))), block(256);
+  if (bf16)
+    hipLaunchKernelGGL((router_small_kernel<bf16_t, 8, TPW>), grid, block, 0, st,
+                       (const bf16_t*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
+                       scores);
+  else
+    hipLaunchKernelGGL((router_small_kernel<float, 8, TPW>), grid, block, 0, st,
+                       (const float*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
+                       scores);
   return hipGetLastError();
 }
 
