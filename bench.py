@@ -95,6 +95,64 @@ def traffic_for(kernel, workload):
     return None if k is None else int(k["bytes_per_launch"])
 
 
+def gemm_roles(w):
+    """Order of the grouped-GEMM launches in one layer step (library call order)."""
+    fwd = ["gemm_fwd_up", "gemm_fwd_down"]
+    bwd = ["gemm_dgrad_down", "gemm_dgrad_up", "gemm_wgrad_down", "gemm_wgrad_up"]
+    if w.n_shared:
+        fwd += ["gemm_shared_" + r[5:] for r in fwd]
+        bwd += ["gemm_shared_" + r[5:] for r in bwd]
+    return fwd + bwd
+
+
+CALIB_BYTES = 1 << 30   # plain device copy used to scale the HBM byte counters
+
+
+def summarize_pmc(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of each grouped-GEMM role from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the calibration copy of CALIB_BYTES (read once, written
+    once). Writes profiles/gemm_traffic.json."""
+    import csv
+    w = WORKLOADS[workload]
+    roles = gemm_roles(w)
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        # the calibration pass is the last multiply kernel before the layer's own
+        calib = [float(r["Counter_Value"]) for r in rows
+                 if "elementwise" in r["Kernel_Name"] and "Mul" in r["Kernel_Name"]]
+        gem = [float(r["Counter_Value"]) for r in rows if "gemm_bf16_kernel" in r["Kernel_Name"]]
+        per_role = {}
+        for i, v in enumerate(gem):
+            per_role.setdefault(roles[i % len(roles)], []).append(v)
+        return calib, per_role
+
+    fc, fr = load(fetch_csv, "FETCH_SIZE")
+    wc, wr = load(write_csv, "WRITE_SIZE")
+    if not fc or not wc:
+        raise SystemExit("calibration copy not found in the counter files")
+    f_scale = CALIB_BYTES / (fc[-1] * 1024.0)
+    w_scale = CALIB_BYTES / (wc[-1] * 1024.0)
+    out = {"workload": workload, "source_sha": gemm_source_hash(),
+           "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch), two separate rocprofv3 --pmc runs",
+           "calibration": {"bytes": CALIB_BYTES, "fetch_kib": fc[-1], "write_kib": wc[-1],
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {}}
+    for role in roles:
+        if role not in fr or role not in wr:
+            continue
+        fk = sum(fr[role]) / len(fr[role])
+        wk = sum(wr[role]) / len(wr[role])
+        out["kernels"][role] = {"fetch_kib": fk, "write_kib": wk,
+                                "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, g, tokens):
     """The oracle, as it stands, on the first `tokens` tokens of the workload
     (same weights; capacity recomputed for the sample)."""
@@ -125,11 +183,18 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_bf16", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events (roofline object omitted)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/gemm_traffic.json from two counter runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -153,6 +218,13 @@ def main():
         return torch.from_numpy(a).cuda()
 
     inp = {n: dev(v) for n, v in g.items()}
+    if args.calibrate_copy:
+        # one elementwise pass reading and writing CALIB_BYTES each
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef)
