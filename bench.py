@@ -227,7 +227,7 @@ def main():
         del src, dst
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef)
+                     w.aux_coef, w.z_coef, w.bias_gamma)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -105,23 +105,36 @@ typedef enum {
  *   topk_idx   [T, k] int32                  out (expert of each slot)
  *   gate       [T, k] float                  out
  *   scores     [T, E] float                  out
+ *   lse        [T] float or NULL             out (log sum_e exp(l_te), for the z-loss)
  *   ws         MOE_OP_ROUTE bytes            scratch
  */
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
-              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, void* ws,
-              size_t ws_bytes, void* stream);
+              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, float* lse,
+              void* ws, size_t ws_bytes, void* stream);
 
 /* moe_aux_stats: load-balance statistics of [Balance] (section 辅助损失函数)
  * and [Recipe] §5.2: counts_i = assignments routed to expert i before any
  * capacity drop; y_i = counts_i / (T k); z_i = mean over tokens of s_ti;
- * out2[0] = S = sum_i y_i z_i; out2[1] = L_aux = E * S. Sums run in a fixed
- * order (deterministic).
- *   scores [T, E] float, topk_idx [T, k] int32             in
- *   counts [E] int32, y [E] float, z [E] float, out2 [2]   out
+ * out3[0] = S = sum_i y_i z_i; out3[1] = L_aux = E * S; out3[2] = router
+ * z-loss mean_t lse_t^2 when lse is given, else 0 (the z-loss is named with
+ * weight 1e-3 in [Recipe] §9.1 but not defined there; this is the common
+ * definition). Sums run in a fixed order (deterministic).
+ *   scores [T, E] float, topk_idx [T, k] int32, lse [T] float or NULL   in
+ *   counts [E] int32, y [E] float, z [E] float, out3 [3] float           out
  */
 int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk_idx,
-                  int32_t* counts, float* y, float* z, float* out2, void* ws, size_t ws_bytes,
-                  void* stream);
+                  const float* lse, int32_t* counts, float* y, float* z, float* out3, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* moe_bias_update: the aux-loss-free balancing step of [Recipe] §5.4:
+ * b_i <- b_i + gamma * sign(1/E - f_i) with the load f_i = counts_i / (T k);
+ * an exactly balanced expert keeps b_i. The comparison is exact
+ * (counts_i * E against T * k). In place on `bias`.
+ *   counts [E] int32 (from moe_aux_stats)   in
+ *   bias   [E] float                         in/out (the sel_bias of moe_route)
+ */
+int moe_bias_update(const moe_desc* desc, const int32_t* counts, float gamma, float* bias,
+                    void* stream);
 
 /* ---------------------------------------------------------------- permute
  * moe_permute: local dispatch ([Recipe] §3.2; [Balance] section 负载感知调度,
@@ -209,15 +222,19 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
  *            aux: dl_te += aux_coef (E/T) s_te (y_e - sum_i y_i s_ti)
  *   sigmoid: dl_e = s_e (1 - s_e) (dg_e - sum_j g_j dg_j) / sum_chosen s;
  *            aux: dl_te += aux_coef (E/T) y_e s_te (1 - s_te)
+ * Plus z_coef times the gradient of the z-loss mean_t lse_t^2:
+ *   dl_te += z_coef (2/T) lse_t softmax(l_t)_e   (softmax scoring only;
+ *   z_coef != 0 with sigmoid scoring returns MOE_ERR_UNSUPPORTED).
  * dw_r = dl^T x, dx_router = dl W_r (float32).
  *   x [T, d] dt, w_r [E, d], scores [T, E], topk_idx, gate, dgate [T, k]   in
  *   y [E] float (from moe_aux_stats; may be NULL when aux_coef == 0)        in
+ *   lse [T] float (from moe_route; may be NULL when z_coef == 0)            in
  *   dlogits [T, E] float, dx_router [T, d] float, dw_r [E, d] float          out
  */
 int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const float* scores,
                   const int32_t* topk_idx, const float* gate, const float* dgate, const float* y,
-                  float aux_coef, float* dlogits, float* dx_router, float* dw_r, void* ws,
-                  size_t ws_bytes, void* stream);
+                  float aux_coef, const float* lse, float z_coef, float* dlogits,
+                  float* dx_router, float* dw_r, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_permute_bwd: un-permute, dx[t] = dx_shared[t] + sum over kept slots j
  * (slot order) of dx_perm[row_of[t,j]] + dx_router[t], float32 accumulate,

@@ -16,6 +16,7 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
+ABI_VERSION = 2
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
@@ -24,7 +25,7 @@ MOE_SWIGLU, MOE_GELU = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
-    "moe_route", "moe_aux_stats", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine",
+    "moe_route", "moe_aux_stats", "moe_bias_update", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_profile_enable", "moe_profile_read",
@@ -60,14 +61,16 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         DP = ctypes.POINTER(MoeDesc)
         sig = {
-            "moe_route": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
-            "moe_aux_stats": [DP] + [_P] * 7 + [ctypes.c_size_t, _P],
+            "moe_route": [DP] + [_P] * 9 + [ctypes.c_size_t, _P],
+            "moe_aux_stats": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
+            "moe_bias_update": [DP, _P, ctypes.c_float, _P, _P],
             "moe_permute": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
             "moe_grouped_ffn_fwd": [DP] + [_P] * 14 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
             "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
-            "moe_route_bwd": [DP] + [_P] * 7 + [ctypes.c_float] + [_P] * 4 + [ctypes.c_size_t, _P],
+            "moe_route_bwd": [DP] + [_P] * 7 + [ctypes.c_float, _P, ctypes.c_float] + [_P] * 4
+                             + [ctypes.c_size_t, _P],
             "moe_permute_bwd": [DP] + [_P] * 6,
             "moe_workspace_size": [DP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
             "moe_capacity": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
@@ -84,7 +87,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_char_p if name in ("moe_status_str", "moe_last_error") else ctypes.c_int
-        if L.moe_abi_version() != 1:
+        if L.moe_abi_version() != ABI_VERSION:
             raise RuntimeError("libmoe ABI version mismatch")
         _lib = L
     return _lib
@@ -161,18 +164,24 @@ def _ws(ws):
 
 
 # ------------------------------------------------------------- entry points
-def route(desc, x, w_r, logit_bias, sel_bias, topk_idx, gate, scores, ws=None, stream=None):
+def route(desc, x, w_r, logit_bias, sel_bias, topk_idx, gate, scores, lse=None, ws=None,
+          stream=None):
     wp, wn = _ws(ws)
     _check("moe_route", lib().moe_route(ctypes.byref(desc), _p(x), _p(w_r), _p(logit_bias),
-                                        _p(sel_bias), _p(topk_idx), _p(gate), _p(scores), wp, wn,
-                                        _stream(stream)))
+                                        _p(sel_bias), _p(topk_idx), _p(gate), _p(scores), _p(lse),
+                                        wp, wn, _stream(stream)))
 
 
-def aux_stats(desc, scores, topk_idx, counts, y, z, out2, ws=None, stream=None):
+def aux_stats(desc, scores, topk_idx, lse, counts, y, z, out3, ws=None, stream=None):
     wp, wn = _ws(ws)
     _check("moe_aux_stats", lib().moe_aux_stats(ctypes.byref(desc), _p(scores), _p(topk_idx),
-                                                _p(counts), _p(y), _p(z), _p(out2), wp, wn,
-                                                _stream(stream)))
+                                                _p(lse), _p(counts), _p(y), _p(z), _p(out3), wp,
+                                                wn, _stream(stream)))
+
+
+def bias_update(desc, counts, gamma, bias, stream=None):
+    _check("moe_bias_update", lib().moe_bias_update(ctypes.byref(desc), _p(counts), float(gamma),
+                                                    _p(bias), _stream(stream)))
 
 
 def permute(desc, x, topk_idx, offsets, row_of, token_of, n_dropped, x_perm, ws=None, stream=None):
@@ -212,12 +221,13 @@ def grouped_ffn_bwd(desc, x_perm, offsets, x, w13, w2, sw13, sw2, save_pre, save
         _p(dx_shared), _p(dw13), _p(dw2), _p(dsw13), _p(dsw2), wp, wn, _stream(stream)))
 
 
-def route_bwd(desc, x, w_r, scores, topk_idx, gate, dgate, y, aux_coef, dlogits, dx_router, dw_r,
-              ws=None, stream=None):
+def route_bwd(desc, x, w_r, scores, topk_idx, gate, dgate, y, aux_coef, lse, z_coef, dlogits,
+              dx_router, dw_r, ws=None, stream=None):
     wp, wn = _ws(ws)
     _check("moe_route_bwd", lib().moe_route_bwd(
         ctypes.byref(desc), _p(x), _p(w_r), _p(scores), _p(topk_idx), _p(gate), _p(dgate), _p(y),
-        float(aux_coef), _p(dlogits), _p(dx_router), _p(dw_r), wp, wn, _stream(stream)))
+        float(aux_coef), _p(lse), float(z_coef), _p(dlogits), _p(dx_router), _p(dw_r), wp, wn,
+        _stream(stream)))
 
 
 def permute_bwd(desc, dx_perm, row_of, dx_shared, dx_router, dx, stream=None):

@@ -19,9 +19,10 @@ hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dw(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dx(const GemmArgs& p, hipStream_t s);
 hipError_t launch_router_topk(const float*, int, int, int, int, const float*, int32_t*, float*,
-                              float*, hipStream_t);
-hipError_t launch_aux_stats(const float*, const int32_t*, int, int, int, double*, int32_t*,
-                            int32_t*, float*, float*, float*, hipStream_t);
+                              float*, float*, hipStream_t);
+hipError_t launch_aux_stats(const float*, const int32_t*, const float*, int, int, int, double*,
+                            int32_t*, double*, int32_t*, float*, float*, float*, hipStream_t);
+hipError_t launch_bias_update(const int32_t*, int, int64_t, float, float*, hipStream_t);
 hipError_t launch_permute(const void*, bool, const int32_t*, int, int, int, int64_t, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_combine(const void*, const void*, bool, const float*, const int32_t*, int, int,
@@ -31,13 +32,15 @@ hipError_t launch_combine_bwd(const void*, const void*, bool, const float*, cons
 hipError_t launch_unpermute(const void*, const int32_t*, const void*, const float*, bool, int, int,
                             int64_t, void*, hipStream_t);
 hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, const float*,
-                                 const float*, float, int, int, int, int, float*, hipStream_t);
+                                 const float*, float, const float*, float, int, int, int, int,
+                                 float*, hipStream_t);
 hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 hipError_t launch_router_small(const void*, bool, const float*, const float*, const float*, int,
-                               int, int64_t, int, int, int32_t*, float*, float*, hipStream_t);
+                               int, int64_t, int, int, int32_t*, float*, float*, float*,
+                               hipStream_t);
 }  // namespace moe
 
 using namespace moe;
@@ -73,7 +76,7 @@ enum KernelId {
   K_FWD_UP, K_FWD_DOWN, K_DGRAD_DOWN, K_DGRAD_UP, K_WGRAD_DOWN, K_WGRAD_UP,
   K_SH_FWD_UP, K_SH_FWD_DOWN, K_SH_DGRAD_DOWN, K_SH_DGRAD_UP, K_SH_WGRAD_DOWN, K_SH_WGRAD_UP,
   K_COMBINE, K_COMBINE_BWD, K_ROUTER_DLOGITS, K_ROUTER_DW, K_ROUTER_DW_REDUCE, K_ROUTER_DX,
-  K_UNPERMUTE, K_FILL, K_COUNT
+  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
   "router_logits", "router_topk", "aux_stats", "permute",
@@ -82,7 +85,7 @@ const char* const kKernelNames[K_COUNT] = {
   "gemm_shared_fwd_up", "gemm_shared_fwd_down", "gemm_shared_dgrad_down", "gemm_shared_dgrad_up",
   "gemm_shared_wgrad_down", "gemm_shared_wgrad_up",
   "combine", "combine_bwd", "router_dlogits", "router_dw", "router_dw_reduce", "router_dx",
-  "unpermute", "fill_zero",
+  "unpermute", "fill_zero", "bias_update",
 };
 
 struct ProfRec {
@@ -203,7 +206,7 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
     case MOE_OP_ROUTE: return align256((size_t)T * E * 4);
     case MOE_OP_AUX_STATS: {
       const size_t nb = (size_t)(T + 255) / 256;
-      return align256(nb * E * 8) + align256(nb * E * 4);
+      return align256(nb * E * 8) + align256(nb * E * 4) + align256(nb * 8);
     }
     case MOE_OP_PERMUTE: return align256((size_t)((T + 63) / 64) * E * 4);
     case MOE_OP_FFN_FWD: return 0;
@@ -342,8 +345,8 @@ int moe_capacity(int64_t T, int64_t k, int64_t E, double cf, int64_t* capacity) 
 }
 
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
-              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, void* ws,
-              size_t ws_bytes, void* stream) {
+              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, float* lse,
+              void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   MOE_TRY(need(x, "x"));
@@ -353,6 +356,7 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   MOE_TRY(need(topk_idx, "topk_idx"));
   MOE_TRY(need(gate, "gate"));
   MOE_TRY(need(scores, "scores"));
+  MOE_TRY(opt(lse, "lse"));
   MOE_TRY(check_ws(desc, MOE_OP_ROUTE, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -361,7 +365,7 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
     Scope sc(K_ROUTER_TOPK, s);
     return hip_check(launch_router_small(x, desc->dtype == MOE_BF16, w_r, logit_bias, sel_bias,
                                          (int)desc->T, (int)desc->E, desc->d, (int)desc->k,
-                                         desc->score, topk_idx, gate, scores, s),
+                                         desc->score, topk_idx, gate, scores, lse, s),
                      "router (fused)");
   }
   float* logits = (float*)ws;
@@ -381,13 +385,13 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   }
   Scope sc(K_ROUTER_TOPK, s);
   return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,
-                                      desc->score, sel_bias, topk_idx, gate, scores, s),
+                                      desc->score, sel_bias, topk_idx, gate, scores, lse, s),
                    "router top-k");
 }
 
 int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk_idx,
-                  int32_t* counts, float* y, float* z, float* out2, void* ws, size_t ws_bytes,
-                  void* stream) {
+                  const float* lse, int32_t* counts, float* y, float* z, float* out3, void* ws,
+                  size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   MOE_TRY(need(scores, "scores"));
@@ -395,16 +399,33 @@ int moe_aux_stats(const moe_desc* desc, const float* scores, const int32_t* topk
   MOE_TRY(need(counts, "counts"));
   MOE_TRY(need(y, "y"));
   MOE_TRY(need(z, "z"));
-  MOE_TRY(need(out2, "out2"));
+  MOE_TRY(opt(lse, "lse"));
+  MOE_TRY(need(out3, "out3"));
   MOE_TRY(check_ws(desc, MOE_OP_AUX_STATS, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
   const size_t nb = (size_t)(desc->T + 255) / 256;
   double* pz = (double*)ws;
   int32_t* pc = (int32_t*)((char*)ws + align256(nb * desc->E * 8));
+  double* pl = (double*)((char*)pc + align256(nb * desc->E * 4));
   Scope sc(K_AUX_STATS, (hipStream_t)stream);
-  return hip_check(launch_aux_stats(scores, topk_idx, (int)desc->T, (int)desc->E, (int)desc->k,
-                                    pz, pc, counts, y, z, out2, (hipStream_t)stream),
+  return hip_check(launch_aux_stats(scores, topk_idx, lse, (int)desc->T, (int)desc->E,
+                                    (int)desc->k, pz, pc, pl, counts, y, z, out3,
+                                    (hipStream_t)stream),
                    "aux stats");
+}
+
+int moe_bias_update(const moe_desc* desc, const int32_t* counts, float gamma, float* bias,
+                    void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(counts, "counts"));
+  MOE_TRY(need(bias, "bias"));
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma is not finite");
+  if (desc->T == 0) return MOE_OK;
+  Scope sc(K_BIAS_UPDATE, (hipStream_t)stream);
+  return hip_check(launch_bias_update(counts, (int)desc->E, desc->T * desc->k, gamma, bias,
+                                      (hipStream_t)stream),
+                   "bias update");
 }
 
 int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, int32_t* offsets,
@@ -649,8 +670,8 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
 
 int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const float* scores,
                   const int32_t* topk_idx, const float* gate, const float* dgate, const float* y,
-                  float aux_coef, float* dlogits, float* dx_router, float* dw_r, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  float aux_coef, const float* lse, float z_coef, float* dlogits,
+                  float* dx_router, float* dw_r, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   MOE_TRY(need(x, "x"));
@@ -661,6 +682,12 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
   MOE_TRY(need(dgate, "dgate"));
   if (aux_coef != 0.0f) MOE_TRY(need(y, "y"));
   if (!(aux_coef == aux_coef)) return fail(MOE_ERR_INVALID_ARG, "aux_coef is NaN");
+  if (!(z_coef == z_coef)) return fail(MOE_ERR_INVALID_ARG, "z_coef is NaN");
+  if (z_coef != 0.0f) {
+    if (desc->score != MOE_SOFTMAX)
+      return fail(MOE_ERR_UNSUPPORTED, "z-loss gradient needs softmax scoring");
+    MOE_TRY(need(lse, "lse"));
+  }
   MOE_TRY(need(dlogits, "dlogits"));
   MOE_TRY(need(dx_router, "dx_router"));
   MOE_TRY(need(dw_r, "dw_r"));
@@ -671,8 +698,8 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
   const int T = (int)desc->T, E = (int)desc->E, k = (int)desc->k;
   {
     Scope sc(K_ROUTER_DLOGITS, s);
-    MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, T, E, k,
-                                            desc->score, dlogits, s),
+    MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, lse,
+                                            z_coef, T, E, k, desc->score, dlogits, s),
                       "router dlogits"));
   }
   // dw_r = dl^T x, split over tokens, partials folded in a fixed order
@@ -697,8 +724,8 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
                       "router dw reduce"));
   }
   Scope sc(K_ROUTER_DX, s);
-  // dx_router = dl W_r
-  if (aux_coef == 0.0f)
+  // dx_router = dl W_r; dl is nonzero only on the chosen experts unless a loss term is dense
+  if (aux_coef == 0.0f && z_coef == 0.0f)
     return hip_check(launch_router_dx_sparse(dlogits, topk_idx, w_r, T, E, k, desc->d, dx_router, s),
                      "router dx");
   GemmArgs q = blank();

@@ -15,37 +15,38 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           const float* __restrict__ sel_bias,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ gate,
-                                                          float* __restrict__ scores) {
+                                                          float* __restrict__ scores,
+                                                          float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* lrow = logits + t * E;
-  float s[EPL], key[EPL];
+  float s[EPL], key[EPL], l[EPL], m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    l[i] = e < E ? lrow[e] : -INFINITY;
+    m = fmaxf(m, l[i]);
+  }
+  m = wave_max(m);
+  float ex[EPL], sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    ex[i] = e < E ? expf(l[i] - m) : 0.f;
+    sum += ex[i];
+  }
+  sum = wave_sum(sum);
+  if (lse && lane == 0) lse[t] = m + logf(sum);
   if (score == 0) {
-    float l[EPL], m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      l[i] = e < E ? lrow[e] : -INFINITY;
-      m = fmaxf(m, l[i]);
-    }
-    m = wave_max(m);
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      s[i] = e < E ? expf(l[i] - m) : 0.f;
-      sum += s[i];
-    }
-    sum = wave_sum(sum);
     const float inv = 1.0f / sum;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) s[i] *= inv;
+    for (int i = 0; i < EPL; ++i) s[i] = ex[i] * inv;
   } else {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      s[i] = e < E ? 1.0f / (1.0f + expf(-lrow[e])) : 0.f;
+      s[i] = e < E ? 1.0f / (1.0f + expf(-l[i])) : 0.f;
     }
   }
 #pragma unroll
@@ -93,16 +94,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               const float* sel_bias, int32_t* topk, float* gate, float* scores,
-                              hipStream_t st) {
+                              float* lse, hipStream_t st) {
   dim3 grid((T + 3) / 4), block(256);
   if (E <= 64)
-    hipLaunchKernelGGL(router_topk_kernel<1>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+    hipLaunchKernelGGL(router_topk_kernel<1>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_topk_kernel<2>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
   else if (E <= 256)
-    hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+    hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
   else
-    hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores);
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
   return hipGetLastError();
 }
 
@@ -115,7 +116,8 @@ template <typename TX, int EMAX, int TPW>
 __global__ __launch_bounds__(256) void router_small_kernel(
     const TX* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ logit_bias,
     const float* __restrict__ sel_bias, int T, int E, int64_t d, int k, int score,
-    int32_t* __restrict__ topk_idx, float* __restrict__ gate, float* __restrict__ scores) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ gate, float* __restrict__ scores,
+    float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
   if (t0 >= T) return;
@@ -158,28 +160,28 @@ __global__ __launch_bounds__(256) void router_small_kernel(
   }
   const int64_t t = t0 + lane;
   if (lane >= TPW || t >= T) return;
-  float sc[EMAX], key[EMAX];
-  if (score == 0) {
-    float m = -INFINITY;
+  float sc[EMAX], key[EMAX], ex[EMAX];
+  float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-      if (e < E) {
-        l[e] += logit_bias ? logit_bias[e] : 0.f;
-        m = fmaxf(m, l[e]);
-      }
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      sc[e] = e < E ? expf(l[e] - m) : 0.f;
-      sum += sc[e];
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) {
+      l[e] += logit_bias ? logit_bias[e] : 0.f;
+      m = fmaxf(m, l[e]);
     }
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    ex[e] = e < E ? expf(l[e] - m) : 0.f;
+    sum += ex[e];
+  }
+  if (lse) lse[t] = m + logf(sum);
+  if (score == 0) {
     const float inv = 1.0f / sum;
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) sc[e] *= inv;
+    for (int e = 0; e < EMAX; ++e) sc[e] = ex[e] * inv;
   } else {
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-      sc[e] = e < E ? 1.0f / (1.0f + expf(-(l[e] + (logit_bias ? logit_bias[e] : 0.f)))) : 0.f;
+    for (int e = 0; e < EMAX; ++e) sc[e] = e < E ? 1.0f / (1.0f + expf(-l[e])) : 0.f;
   }
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
@@ -207,17 +209,18 @@ __global__ __launch_bounds__(256) void router_small_kernel(
 
 hipError_t launch_router_small(const void* x, bool bf16, const float* w_r, const float* logit_bias,
                                const float* sel_bias, int T, int E, int64_t d, int k, int score,
-                               int32_t* topk, float* gate, float* scores, hipStream_t st) {
+                               int32_t* topk, float* gate, float* scores, float* lse,
+                               hipStream_t st) {
   constexpr int TPW = 8;
   const dim3 grid((unsigned)((T + 4 * TPW - 1) / (4 * TPW))), block(256);
   if (bf16)
     hipLaunchKernelGGL((router_small_kernel<bf16_t, 8, TPW>), grid, block, 0, st,
                        (const bf16_t*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
-                       scores);
+                       scores, lse);
   else
     hipLaunchKernelGGL((router_small_kernel<float, 8, TPW>), grid, block, 0, st,
                        (const float*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
-                       scores);
+                       scores, lse);
   return hipGetLastError();
 }
 
@@ -225,9 +228,11 @@ hipError_t launch_router_small(const void* x, bool bf16, const float* w_r, const
 // Pass 1: block b sums scores over tokens [256b, 256b+256) per expert
 // (float64, sequential in token order) and counts its assignments.
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ scores,
-                                                          const int32_t* __restrict__ topk, int T,
+                                                          const int32_t* __restrict__ topk,
+                                                          const float* __restrict__ lse, int T,
                                                           int E, int k, double* __restrict__ pz,
-                                                          int32_t* __restrict__ pc) {
+                                                          int32_t* __restrict__ pc,
+                                                          double* __restrict__ pl) {
   __shared__ int hist[1024];
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
@@ -241,16 +246,23 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) pc[(int64_t)b * E + e] = hist[e];
+  if (tid == 0) {
+    double zl = 0.0;
+    if (lse)
+      for (int t = t0; t < t1; ++t) zl += (double)lse[t] * (double)lse[t];
+    pl[b] = zl;
+  }
 }
 
 // Pass 2 (one block): fold the partials in block order.
 __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict__ pz,
-                                                        const int32_t* __restrict__ pc, int nb,
+                                                        const int32_t* __restrict__ pc,
+                                                        const double* __restrict__ pl, int nb,
                                                         int T, int E, int k,
                                                         int32_t* __restrict__ counts,
                                                         float* __restrict__ y,
                                                         float* __restrict__ z,
-                                                        float* __restrict__ out2) {
+                                                        float* __restrict__ out3) {
   __shared__ double red[256];
   const int tid = threadIdx.x;
   double acc = 0.0;
@@ -275,17 +287,40 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
     __syncthreads();
   }
   if (tid == 0) {
-    out2[0] = (float)red[0];
-    out2[1] = (float)(red[0] * (double)E);
+    double zl = 0.0;
+    for (int b = 0; b < nb; ++b) zl += pl[b];
+    out3[0] = (float)red[0];
+    out3[1] = (float)(red[0] * (double)E);
+    out3[2] = (float)(zl / (double)T);
   }
 }
 
-hipError_t launch_aux_stats(const float* scores, const int32_t* topk, int T, int E, int k,
-                            double* pz, int32_t* pc, int32_t* counts, float* y, float* z,
-                            float* out2, hipStream_t st) {
+hipError_t launch_aux_stats(const float* scores, const int32_t* topk, const float* lse, int T,
+                            int E, int k, double* pz, int32_t* pc, double* pl, int32_t* counts,
+                            float* y, float* z, float* out3, hipStream_t st) {
   const int nb = (T + 255) / 256;
-  hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, st, scores, topk, T, E, k, pz, pc);
-  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, st, pz, pc, nb, T, E, k, counts, y, z, out2);
+  hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, st, scores, topk, lse, T, E, k,
+                     pz, pc, pl);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, st, pz, pc, pl, nb, T, E, k, counts,
+                     y, z, out3);
+  return hipGetLastError();
+}
+
+// b_e += gamma * sign(1/E - counts_e/(T k)), compared exactly as counts_e*E vs T*k
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts,
+                                                          int E, int64_t Tk, float gamma,
+                                                          float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = (int64_t)counts[e] * E;
+  const float step = load < Tk ? 1.0f : (load > Tk ? -1.0f : 0.0f);
+  bias[e] = bias[e] + gamma * step;
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int E, int64_t Tk, float gamma, float* bias,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, st, counts, E, Tk,
+                     gamma, bias);
   return hipGetLastError();
 }
 
@@ -571,7 +606,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void router_dlogits_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ topk,
     const float* __restrict__ gate, const float* __restrict__ dgate, const float* __restrict__ y,
-    float aux_coef, int T, int E, int k, int score, float* __restrict__ dl) {
+    float aux_coef, const float* __restrict__ lse, float z_coef, int T, int E, int k, int score,
+    float* __restrict__ dl) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -601,6 +637,8 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
     }
   }
   const float c = aux_coef * (float)E / (float)T;
+  // z-loss term; only softmax scoring takes it, where the scores are softmax(logits)
+  const float zc = z_coef != 0.f ? z_coef * 2.0f / (float)T * lse[t] : 0.f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
@@ -609,22 +647,24 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
       if (score == 0) out[i] += c * s[i] * (y[e] - ys);
       else out[i] += c * y[e] * s[i] * (1.f - s[i]);
     }
+    if (z_coef != 0.f) out[i] += zc * s[i];
     dl[t * E + e] = out[i];
   }
 }
 
 hipError_t launch_router_dlogits(const float* scores, const int32_t* topk, const float* gate,
-                                 const float* dgate, const float* y, float aux_coef, int T, int E,
-                                 int k, int score, float* dl, hipStream_t st) {
+                                 const float* dgate, const float* y, float aux_coef,
+                                 const float* lse, float z_coef, int T, int E, int k, int score,
+                                 float* dl, hipStream_t st) {
   dim3 grid((T + 3) / 4), block(256);
   if (E <= 64)
-    hipLaunchKernelGGL(router_dlogits_kernel<1>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<1>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_dlogits_kernel<2>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<2>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
   else if (E <= 256)
-    hipLaunchKernelGGL(router_dlogits_kernel<4>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<4>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
   else
-    hipLaunchKernelGGL(router_dlogits_kernel<16>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<16>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ from typing import Optional
 import torch
 
 from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE, MOE_OP_ROUTE,
-               MOE_OP_ROUTE_BWD, aux_stats, combine, combine_bwd, grouped_ffn_bwd,
+               MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine, combine_bwd, grouped_ffn_bwd,
                grouped_ffn_fwd, make_desc, permute, permute_bwd, route, route_bwd,
                workspace_size)
 
@@ -21,13 +21,19 @@ class MoELayer:
     Weights/inputs are passed at call time (the layer owns no parameters):
     x [T,d], w_r [E,d] fp32, w13 [E,2f|f,d], w2 [E,d,f], optional shared
     sw13/sw2, optional logit_bias/sel_bias [E] fp32, dy [T,d].
+
+    aux_coef weights the load-balance loss and z_coef the router z-loss in
+    the router gradient; bias_gamma > 0 makes step() apply the aux-loss-free
+    bias update to sel_bias (in place) from this batch's expert loads.
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
-                 capacity: Optional[int] = None, aux_coef: float = 0.0, device="cuda"):
+                 capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
+                 bias_gamma: float = 0.0, device="cuda"):
         self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
-        self.n_shared, self.aux_coef = n_shared, aux_coef
+        self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
+        self.bias_gamma = bias_gamma
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dt = dt
         P = 2 * f if act == "swiglu" else f
@@ -44,10 +50,11 @@ class MoELayer:
         self.topk_idx = z(T, k, dtype=i32)
         self.gate = z(T, k, dtype=f32)
         self.scores = z(T, E, dtype=f32)
+        self.lse = z(T, dtype=f32)
         self.counts = z(E, dtype=i32)
         self.y_frac = z(E, dtype=f32)
         self.z_mean = z(E, dtype=f32)
-        self.aux_out = z(2, dtype=f32)
+        self.aux_out = z(3, dtype=f32)
         self.offsets = z(E + 1, dtype=i32)
         self.row_of = z(T, k, dtype=i32)
         self.token_of = z(max(R, 1), dtype=i32)
@@ -81,8 +88,9 @@ class MoELayer:
     # ------------------------------------------------------------ stages
     def forward(self, x, w_r, w13, w2, sw13=None, sw2=None, logit_bias=None, sel_bias=None):
         D = self.desc
-        route(D, x, w_r, logit_bias, sel_bias, self.topk_idx, self.gate, self.scores, self.ws)
-        aux_stats(D, self.scores, self.topk_idx, self.counts, self.y_frac, self.z_mean,
+        route(D, x, w_r, logit_bias, sel_bias, self.topk_idx, self.gate, self.scores, self.lse,
+              self.ws)
+        aux_stats(D, self.scores, self.topk_idx, self.lse, self.counts, self.y_frac, self.z_mean,
                   self.aux_out, self.ws)
         permute(D, x, self.topk_idx, self.offsets, self.row_of, self.token_of, self.n_dropped,
                 self.x_perm, self.ws)
@@ -99,9 +107,14 @@ class MoELayer:
                         self.save_h, self.save_pre_s, self.save_h_s, self.dout, dy, self.dx_perm,
                         self.dx_shared, self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws)
         route_bwd(D, x, w_r, self.scores, self.topk_idx, self.gate, self.dgate, self.y_frac,
-                  self.aux_coef, self.dlogits, self.dx_router, self.dw_r, self.ws)
+                  self.aux_coef, self.lse, self.z_coef, self.dlogits, self.dx_router, self.dw_r,
+                  self.ws)
         permute_bwd(D, self.dx_perm, self.row_of, self.dx_shared, self.dx_router, self.dX)
         return self.dX
+
+    def update_bias(self, sel_bias, gamma=None):
+        """Aux-loss-free balancing: nudge sel_bias (in place) by the last forward's loads."""
+        bias_update(self.desc, self.counts, self.bias_gamma if gamma is None else gamma, sel_bias)
 
     def step(self, inp: dict):
         """Forward then backward over one batch; inp holds the device tensors."""
@@ -109,3 +122,5 @@ class MoELayer:
                      inp.get("sw2"), inp.get("logit_bias"), inp.get("sel_bias"))
         self.backward(inp["dy"], inp["x"], inp["w_r"], inp["w13"], inp["w2"], inp.get("sw13"),
                       inp.get("sw2"))
+        if self.bias_gamma and inp.get("sel_bias") is not None:
+            self.update_bias(inp["sel_bias"])

@@ -54,6 +54,8 @@ class Workload:
     logit_bias: Optional[dict] = None   # {expert: value} added to router logits
     sel_bias: bool = False        # draw a per-expert selection bias b ~ U(-0.01, 0.01)
     aux_coef: float = 0.0         # weight of the load-balance loss in the backward
+    z_coef: float = 0.0           # weight of the router z-loss in the backward (softmax only)
+    bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -68,9 +70,9 @@ WORKLOADS = {
     "skewed_nocap_bf16": Workload("skewed_nocap_bf16", T=4096, d=4096, E=8, k=2, f=16384,
                                   act="gelu", cf=None, logit_bias={0: 2.0, 3: 2.0}),
     "finegrained_bf16": Workload("finegrained_bf16", T=16384, d=4096, E=128, k=8, f=1536,
-                                 aux_coef=0.01),
+                                 aux_coef=0.01, z_coef=1e-3),
     "dsv3_bf16": Workload("dsv3_bf16", T=8192, d=7168, E=256, k=8, f=2048, score="sigmoid",
-                          n_shared=1, sel_bias=True),
+                          n_shared=1, sel_bias=True, bias_gamma=1e-3),
 }
 
 

@@ -287,7 +287,7 @@ def combine_backward(dY, O, gates, row_of):
 
 # ---------------------------------------------------------- router backward
 def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux_coef=0.0,
-                    y=None):
+                    y=None, z_coef=0.0, logits=None):
     """Gradient of the router through the renormalised gates of [Recipe] §2.2
     (the top-k choice itself is piecewise constant), plus aux_coef times the
     gradient of L_aux = E sum_i y_i z_i with the counts y held fixed.
@@ -299,6 +299,7 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
     Aux (z_i = mean_t s_ti):
       softmax: dl_te += aux_coef (E/T) s_te (y_e - sum_i y_i s_ti)
       sigmoid: dl_te += aux_coef (E/T) y_e s_te (1 - s_te)
+    Plus z_coef times the gradient of z_loss(logits) when z_coef != 0.
     Returns dict(dlogits [T,E], dw_r [E,d] = dl^T x, dx_router [T,d] = dl W_r).
     """
     T, E = scores.shape
@@ -320,7 +321,43 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
             dl += aux_coef * (E / T) * scores * (y[None, :] - ys[:, None])
         else:
             dl += aux_coef * (E / T) * y[None, :] * scores * (1.0 - scores)
+    if z_coef != 0.0:
+        dl += z_coef * z_loss_grad(logits)
     return dict(dlogits=dl, dw_r=dl.T @ x, dx_router=dl @ w_r)
+
+
+# ------------------------------------------- aux-loss-free bias, z-loss
+def bias_update(bias, counts, T, k, gamma):
+    """Aux-loss-free balancing of [Recipe] §5.3/§5.4: with the load f_i of
+    expert i (here y_i = counts_i / (T k)) and target 1/E,
+    b_i <- b_i + gamma * sign(1/E - f_i); an exactly balanced expert keeps b_i.
+    The comparison f_i < 1/E is made exactly as counts_i * E < T * k."""
+    E = bias.shape[0]
+    load = np.asarray(counts, dtype=np.int64) * E
+    target = T * k
+    step = np.where(load < target, 1.0, np.where(load > target, -1.0, 0.0))
+    return bias + gamma * step
+
+
+def router_logsumexp(logits):
+    """log sum_e exp(l_te) per token (max-subtracted)."""
+    m = logits.max(axis=1)
+    return m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+
+
+def z_loss(logits):
+    """Router z-loss, named by [Recipe] §9.1/§9.2 with weight 1e-3 but without a
+    formula on the pages; read as mean_t (logsumexp_e l_te)^2 (the common
+    definition). Gradient: d/dl_te = (2/T) lse_t softmax(l_t)_e."""
+    lse = router_logsumexp(logits)
+    return float(np.mean(lse * lse))
+
+
+def z_loss_grad(logits):
+    T = logits.shape[0]
+    lse = router_logsumexp(logits)
+    sm = np.exp(logits - lse[:, None])
+    return (2.0 / T) * lse[:, None] * sm
 
 
 def permute_backward(dx_perm, row_of, dx_shared=None, dx_router=None):
@@ -355,7 +392,7 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
 
 
 def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
-                   sw13=None, sw2=None):
+                   sw13=None, sw2=None, z_coef=0.0):
     """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
     router bwd, un-permute."""
     r, p = fwd["router"], fwd["perm"]
@@ -363,6 +400,6 @@ def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_
     g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
                              sw13, sw2, dY)
     rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
-                         aux_coef, fwd["stats"]["y"])
+                         aux_coef, fwd["stats"]["y"], z_coef, r["logits"])
     dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])
     return dict(dgate=dgate, dO=dO, dX=dX, **g, **rb)

@@ -7,7 +7,8 @@ Tolerances:
     scores closer than 1e-5), where a flip is counted, checked for validity
     and excluded downstream;
   * x_perm: bitwise (a copy);
-  * float32 router outputs (scores, gates, z, S, L_aux): max|d| <= 1e-5 max|ref|;
+  * float32 router outputs (scores, gates, lse, z, S, L_aux, L_z, updated
+    selection bias): max|d| <= 1e-5 max|ref|;
   * fp32 layer: every float output max|d| <= 1e-5 max|ref|;
   * bf16 layer: max|d| <= 2e-2 max|ref| and sum|d| / sum|ref| <= 5e-3.
 """
@@ -51,7 +52,7 @@ def gpu_layer(w: Workload, g: dict):
     import mixture_experts_layer_28_amd as moe
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef)
+                     w.aux_coef, w.z_coef, w.bias_gamma)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -64,7 +65,7 @@ def oracle_layer(w: Workload, g: dict):
     fwd = O.layer_forward(f["x"], f["w_r"], f["w13"], f["w2"], w.k, w.score, w.act, cap,
                           f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"])
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
-                           w.aux_coef, f["sw13"], f["sw2"])
+                           w.aux_coef, f["sw13"], f["sw2"], w.z_coef)
     return fwd, bwd, f
 
 
@@ -130,6 +131,8 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     e_ok = np.array([e not in bad_e for e in range(E)])
 
     assert_close("scores", to_np(L.scores), r["scores"], dt, rep, rel=1e-5)
+    lse_ref = O.router_logsumexp(r["logits"])
+    assert_close("lse", to_np(L.lse), lse_ref, dt, rep, rel=1e-5)
     assert_close("gate", to_np(L.gate)[tok_ok], r["gates"][tok_ok], dt, rep, rel=1e-5)
     # ---- stats
     counts = L.counts.cpu().numpy()
@@ -139,7 +142,11 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     assert_close("z", to_np(L.z_mean), st["z"], dt, rep, rel=1e-5)
     if not bad_e:
         aux = to_np(L.aux_out)
-        assert_close("S,L_aux", aux, np.array([st["S"], st["L_aux"]]), dt, rep, rel=1e-5)
+        assert_close("S,L_aux,L_z", aux, np.array([st["S"], st["L_aux"], O.z_loss(r["logits"])]),
+                     dt, rep, rel=1e-5)
+    if w.bias_gamma and f.get("sel_bias") is not None and not bad_e:
+        ref_b = O.bias_update(f["sel_bias"], st["counts"], T, k, w.bias_gamma)
+        assert_close("sel_bias update", to_np(dev["sel_bias"]), ref_b, dt, rep, rel=1e-6)
     # ---- permute (integer, bitwise copy)
     off = L.offsets.cpu().numpy().astype(np.int64)
     A = int(off[-1])

@@ -21,11 +21,11 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -66,13 +66,16 @@ def test_null_and_misaligned_pointers_rejected():
     d = _desc()
     ws = moe.workspace_size(d, moe.MOE_OP_ROUTE)
     # x NULL
-    s = L.moe_route(ctypes.byref(d), None, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws, None)
+    s = L.moe_route(ctypes.byref(d), None, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, ws,
+                    None)
     assert s == 1 and "x is NULL" in L.moe_last_error().decode()
     # misaligned gate
-    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE + 4, FAKE, FAKE, ws, None)
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE + 4, FAKE, None, FAKE, ws,
+                    None)
     assert s == 1 and "aligned" in L.moe_last_error().decode()
     # workspace too small
-    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws - 1, None)
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+                    None)
     assert s == 3
     # combine without row_of
     s = L.moe_combine(ctypes.byref(d), FAKE, None, FAKE, None, FAKE, None)
@@ -82,13 +85,38 @@ def test_null_and_misaligned_pointers_rejected():
     s = L.moe_grouped_ffn_fwd(ctypes.byref(ds), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
                               FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
     assert s == 1 and "sw13" in L.moe_last_error().decode()
+    # misaligned lse
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE + 2, FAKE, ws,
+                    None)
+    assert s == 1 and "lse" in L.moe_last_error().decode()
+    # bias update without a bias vector
+    assert L.moe_bias_update(ctypes.byref(d), FAKE, 1e-3, None, None) == 1
+    assert "bias" in L.moe_last_error().decode()
+    assert L.moe_bias_update(ctypes.byref(d), FAKE, float("nan"), FAKE, None) == 1
+
+
+def test_z_loss_needs_softmax_scoring_and_lse():
+    L = moe.lib()
+    ws = moe.workspace_size(_desc(score="sigmoid"), moe.MOE_OP_ROUTE_BWD)
+    args = [FAKE] * 6 + [None, 0.0]
+    tail = [FAKE, FAKE, FAKE, FAKE if ws else None, ws, None]
+    d = _desc(score="sigmoid")
+    assert L.moe_route_bwd(ctypes.byref(d), *args, FAKE, 1e-3, *tail) == 2
+    assert "softmax" in L.moe_last_error().decode()
+    d = _desc()
+    assert L.moe_route_bwd(ctypes.byref(d), *args, None, 1e-3, *tail) == 1
+    assert "lse" in L.moe_last_error().decode()
+    assert L.moe_route_bwd(ctypes.byref(d), *args, None, float("nan"), *tail) == 1
 
 
 def test_zero_tokens_is_a_noop_without_touching_memory():
     L = moe.lib()
     d = _desc(T=0)
-    assert L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 0, None) == 0
-    assert L.moe_aux_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                       None) == 0
+    assert L.moe_aux_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == 0
+    assert L.moe_bias_update(ctypes.byref(d), FAKE, 1e-3, FAKE, None) == 0
     assert L.moe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
     assert L.moe_combine(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None) == 0
     assert L.moe_combine_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0

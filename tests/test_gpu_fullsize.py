@@ -44,7 +44,9 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
     assert_close("gate", to_np(L.gate), r["gates"], dt, rep, rel=1e-5)
     assert (L.counts.cpu().numpy() == st["counts"]).all()
     assert_close("z", to_np(L.z_mean), st["z"], dt, rep, rel=1e-5)
-    assert_close("S,L_aux", to_np(L.aux_out), np.array([st["S"], st["L_aux"]]), dt, rep, rel=1e-5)
+    assert_close("lse", to_np(L.lse), O.router_logsumexp(r["logits"]), dt, rep, rel=1e-5)
+    assert_close("S,L_aux,L_z", to_np(L.aux_out),
+                 np.array([st["S"], st["L_aux"], O.z_loss(r["logits"])]), dt, rep, rel=1e-5)
     off = L.offsets.cpu().numpy().astype(np.int64)
     assert (off == pm["offsets"]).all()
     assert int(L.n_dropped.cpu()[0]) == pm["n_dropped"]

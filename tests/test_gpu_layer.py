@@ -25,9 +25,10 @@ REDUCED = {
 EDGE = {
     # ragged everything: T, E, d (K tail of 8), f (N tails), k=3, shared GELU, sigmoid
     "ragged_gelu_shared": Workload("ragged", T=1000, d=136, E=6, k=3, f=200, act="gelu",
-                                   score="sigmoid", n_shared=1, sel_bias=True, aux_coef=0.1),
+                                   score="sigmoid", n_shared=1, sel_bias=True, aux_coef=0.1,
+                                   bias_gamma=0.01),
     "ragged_swiglu_fp32": Workload("ragged32", T=333, d=72, E=5, k=2, f=40, dtype="fp32",
-                                   cf=0.8, aux_coef=0.05),
+                                   cf=0.8, aux_coef=0.05, z_coef=0.05),
     # capacity 0: every assignment dropped, only the shared expert remains
     "all_dropped_shared": Workload("drop", T=512, d=256, E=8, k=2, f=256, cf=0.0, n_shared=1),
     # all tokens on one expert (logit bias), top-1, capacity keeps the first C
@@ -36,7 +37,7 @@ EDGE = {
     # one expert, top-1: a dense FFN
     "single_expert": Workload("single", T=300, d=128, E=1, k=1, f=384),
     # E at the router's 1024-expert limit region and k at 16
-    "wide_router": Workload("wide", T=256, d=64, E=320, k=16, f=64, aux_coef=0.02),
+    "wide_router": Workload("wide", T=256, d=64, E=320, k=16, f=64, aux_coef=0.02, z_coef=0.01),
 }
 
 
@@ -72,7 +73,7 @@ def test_determinism_bitwise():
     outs = []
     for _ in range(2):
         L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act,
-                         moe.capacity(w.T, w.k, w.E, w.cf), w.aux_coef)
+                         moe.capacity(w.T, w.k, w.E, w.cf), w.aux_coef, w.z_coef)
         L.step(dev)
         torch.cuda.synchronize()
         outs.append({n: bits(getattr(L, n)) for n in

@@ -389,3 +389,76 @@ def test_generator_is_deterministic_and_per_expert():
     np.testing.assert_array_equal(a[2], gen_expert_w13(w, 2))
     np.testing.assert_array_equal(a, gen_w13(w, threads=1))
     assert not np.array_equal(a[0], a[1])
+
+
+# -------------------------------------------- bias update and z-loss pins
+def test_bias_update_rule():
+    # T k = 12 assignments over E = 4 experts: target 3 each
+    b = np.array([0.5, 0.0, -0.25, 0.1])
+    counts = np.array([5, 3, 1, 3])
+    nb = O.bias_update(b, counts, T=6, k=2, gamma=1e-3)
+    np.testing.assert_allclose(nb, [0.5 - 1e-3, 0.0, -0.25 + 1e-3, 0.1], rtol=0, atol=1e-15)
+    # uniform load leaves the bias unchanged
+    assert (O.bias_update(b, np.full(4, 3), 6, 2, 1e-3) == b).all()
+
+
+def test_bias_update_balances_a_skewed_router():
+    """Repeated updates move the selection toward balance ([Recipe] §5.3)."""
+    rng = np.random.default_rng(5)
+    T, E, k = 400, 8, 2
+    logits = rng.standard_normal((T, E)) * 0.3
+    logits[:, 0] += 1.5
+    scores = sps.softmax(logits, axis=1)
+    b = np.zeros(E)
+    spread = []
+    for _ in range(300):
+        idx = np.argsort(-(scores + b), axis=1, kind="stable")[:, :k]
+        counts = np.bincount(idx.ravel(), minlength=E)
+        spread.append(counts.max() - counts.min())
+        b = O.bias_update(b, counts, T, k, 2e-3)
+    assert spread[-1] < spread[0] / 3
+
+
+def test_z_loss_closed_form_and_gradient():
+    T, E = 5, 6
+    assert abs(O.z_loss(np.zeros((T, E))) - np.log(E) ** 2) < 1e-14
+    rng = np.random.default_rng(2)
+    l = rng.standard_normal((T, E)) * 2
+    g = O.z_loss_grad(l)
+    h = 1e-6
+    num = np.zeros_like(l)
+    for i in np.ndindex(l.shape):
+        lp = l.copy(); lp[i] += h
+        lm = l.copy(); lm[i] -= h
+        num[i] = (O.z_loss(lp) - O.z_loss(lm)) / (2 * h)
+    np.testing.assert_allclose(g, num, rtol=0, atol=1e-8)
+    # shifting every logit of a token by c shifts its lse by c
+    np.testing.assert_allclose(O.router_logsumexp(l + 3.0), O.router_logsumexp(l) + 3.0, rtol=1e-14)
+
+
+def test_layer_gradient_with_z_loss_by_central_differences():
+    for seed in range(50):
+        w, g = _tiny(T=8, d=6, E=5, k=2, f=4, seed=seed)
+        g["w_r"] = g["w_r"] * 40.0
+        r = O.router_forward(g["x"], g["w_r"], w.k)
+        if not O.near_tie_tokens(r["key"], w.k, 1e-3).any():
+            break
+    zc = 0.5
+
+    def loss(x, w_r):
+        f = O.layer_forward(x, w_r, g["w13"], g["w2"], w.k)
+        return float((f["Y"] * g["dy"]).sum()) + zc * O.z_loss(f["router"]["logits"]), f
+
+    _, fwd = loss(g["x"], g["w_r"])
+    bwd = O.layer_backward(fwd, g["x"], g["w_r"], g["w13"], g["w2"], g["dy"], z_coef=zc)
+    h = 1e-6
+    for name, val, ana in (("x", g["x"], bwd["dX"]), ("w_r", g["w_r"], bwd["dw_r"])):
+        num = np.zeros_like(val)
+        for i in np.ndindex(val.shape):
+            v2 = val.copy(); v2[i] += h
+            lp, _ = loss(v2, g["w_r"]) if name == "x" else loss(g["x"], v2)
+            v2[i] -= 2 * h
+            lm, _ = loss(v2, g["w_r"]) if name == "x" else loss(g["x"], v2)
+            num[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(ana, num, rtol=0, atol=2e-6 * max(1.0, np.abs(num).max()),
+                                   err_msg=name)
