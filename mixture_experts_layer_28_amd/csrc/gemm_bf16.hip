@@ -2,40 +2,50 @@
 // float32 accumulation. One launch covers every expert ("grouped GEMM": each
 // expert's GEMM on its own contiguous rows, tiled per expert, one kernel).
 //
-// Workgroup: 256 threads = 4 waves in a 2x2 grid; tile BM x BN x 64; each
-// wave owns a (BM/2) x (BN/2) sub-tile of 32x32 MFMA blocks whose
-// accumulators live in the AGPR file.
+// Workgroup: 256 threads = 4 waves in a 2x2 grid; tile 256 x 256; each wave
+// owns a 128 x 128 sub-tile of 32x32 MFMA blocks whose accumulators fill the
+// AGPR file.
 //
-// LDS holds both operands K-contiguous ([rows][64] bf16 = 128 B per row) in
-// two stages. Each 16-byte chunk c of row r sits at position
-// c ^ (r & 7) ^ ((r >> 3) & 7): the fragment reads (32 consecutive rows, one
-// chunk), the row-wise stores (one row, all chunks) and the transposed
-// stores (8 rows 8 apart, one chunk) all spread over every bank.
+// Operands stream through a ring of five LDS stages, each holding 32 k of
+// both tiles (32 KiB), filled by buffer_load ... lds (global -> LDS with no
+// staging registers). Loads for k-step kt+4 are issued during k-step kt into
+// the stage k-step kt-1 released, one instruction after every fourth MFMA,
+// so the memory queue sees a steady stream instead of a burst per barrier.
+// Per k-step:
+//   slice 0 (k 0..15): 16 MFMAs, slice 1's fragments read in between;
+//   wait for stage kt+1's loads, barrier;
+//   slice 1 (k 16..31): 16 MFMAs, stage kt+1's slice-0 fragments read in
+//   between (they have a whole slice of MFMAs to arrive).
 //
-// A K-contiguous operand is copied global -> LDS by buffer_load ... lds
-// (no staging registers, no LDS store instructions); lane l of a wave
-// instruction lands at LDS byte 16*l of that instruction's 1 KiB block, so the
-// swizzle is realised by choosing which global chunk each lane fetches.
-// Out-of-range lanes (ragged rows, K tail) point past the buffer's extent and
-// read zeros. A K-strided operand (the transposed reads of the backward) goes
-// through registers: 8x8 blocks loaded row-wise, transposed in registers,
-// stored as K-contiguous chunks.
-//
-// Per k-step the next stage's loads are issued first, then the MFMAs run on
-// the current stage with the fragments of k-slice s+1 read from LDS while the
-// MFMAs of slice s execute.
+// LDS layouts (bank-conflict free for the fragment reads, measured):
+//   K-contiguous operand, [rows][32] bf16: 16-byte chunk c of row r at
+//     r*64 + ((c ^ ((r >> 2) & 3)) << 4).
+//   K-strided operand (the transposed reads of the backward), [32][rows]:
+//     16-byte slot s (8 rows) of k-row k at k*rows*2 + ((s ^ ((k & 3) << 1)) << 4);
+//     fragments are built by ds_read_b64_tr_b16, which transposes 4x4
+//     blocks of bf16 across each 16-lane group.
+// A DMA instruction fills a contiguous 1 KiB with lane l at byte 16*l, so a
+// layout's swizzle is realised by choosing the global chunk each lane fetches.
+// Lanes that fall outside the operand (ragged rows, the K tail, k-steps past
+// the end) point past the buffer's extent and read zeros.
 #include "gemm_tile.h"
 
 namespace moe {
 
-constexpr int kBK = 64;
-constexpr uint32_t kOOB = 0x80000000u;   // byte offset beyond any buffer extent
+constexpr int kBK = 32;                   // k per stage
+constexpr uint32_t kOOB = 0x80000000u;    // byte offset beyond any buffer extent
+constexpr int kRows = 256;                // tile rows of either operand
 
-__device__ __forceinline__ int swz_pos(int row, int chunk) {
-  return chunk ^ (row & 7) ^ ((row >> 3) & 7);
-}
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kBK + (swz_pos(row, chunk) << 3);
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// byte offset of chunk c (0..3) of row r in a K-contiguous [rows][32] tile
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [32][kRows] tile
+__device__ __forceinline__ int ks_off(int k, int s) {
+  return k * (kRows * 2) + ((s ^ ((k & 3) << 1)) << 4);
 }
 
 // raw buffer resource over [base, base + bytes)
@@ -44,9 +54,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// weight row of fused tile row j; -1 when beyond f
+// weight row of fused tile row j (gate rows then up rows per wave column); -1 when beyond f
 __device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t fdim) {
   const int wc = j / WN, w = j - wc * WN, half = WN >> 1;
   const bool up = w >= half;
@@ -55,134 +63,99 @@ __device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t
   return up ? fdim + col : col;
 }
 
-// ---- K-contiguous operand: global -> LDS directly.
-// The tile has ROWS rows of 8 chunks; ROWS/8 blocks of 1 KiB; each of the 4
-// waves issues ROWS/32 instructions.
-template <int ROWS, bool FUSED, int WN>
-__device__ __forceinline__ void direct_load(__amdgpu_buffer_rsrc_t rs, bf16_t* lds_tile, int64_t ld,
-                                            int64_t rows_valid, int64_t r0, int64_t k0, int64_t K,
-                                            int64_t fdim, int wave_u, int lane) {
-#pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int blk = wave_u * (ROWS / 32) + i;
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (lane >> 3) ^ (blk & 7);
-    int64_t grow;
-    bool ok;
-    if (FUSED) {
-      grow = fused_row(r, WN, r0, fdim);
-      ok = grow >= 0;
-    } else {
-      grow = r0 + r;
-      ok = grow < rows_valid;
-    }
-    const int64_t kk = k0 + c * 8;
-    ok = ok && kk < K;
-    const uint32_t off = ok ? (uint32_t)((grow * ld + kk) * 2) : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + blk * 512), 16, off, 0, 0, 0);
-  }
-}
-
-// ---- K-strided operand: element (row, kk) at base + kk*ld + row.
-template <int ROWS>
-struct Strided {
-  static constexpr int NIT = (ROWS + 255) / 256;
-  uint4 r[NIT * 8];
+// Per-lane DMA source of one operand tile. A wave issues kRows/64 = 4
+// instructions per stage; instruction i fills block blk = wave*4 + i (1 KiB).
+//   K-contiguous: block = rows blk*16 .. +15, lane l -> row blk*16 + (l>>2),
+//     logical chunk (l&3) ^ ((l>>4)&3); k offset inside the stage = 8*chunk.
+//   K-strided: block = k-rows 2*blk, 2*blk+1, lane l -> k-row 2*blk + (l>>5),
+//     logical slot (l&31) ^ ((k&3)<<1), i.e. rows 8*slot .. 8*slot+7.
+// off[i] is the byte offset at k0 = 0 (kOOB when the rows lie outside the
+// operand); kk[i] is the lane's k inside a stage, for the K-tail test.
+struct DmaSrc {
+  uint32_t off[4];
+  int kk[4];
 };
 
-template <int ROWS>
-__device__ __forceinline__ void strided_load(Strided<ROWS>& L, __amdgpu_buffer_rsrc_t rs, int64_t ld,
-                                             int64_t rows_valid, int64_t r0, int64_t k0, int64_t K) {
-  const int tid = threadIdx.x;
+template <bool KC, bool FUSED, int WN>
+__device__ __forceinline__ void dma_src(DmaSrc& d, int64_t ld, int64_t rows_valid, int64_t r0,
+                                        int64_t fdim, int wave, int lane) {
 #pragma unroll
-  for (int it = 0; it < Strided<ROWS>::NIT; ++it) {
-    const int q = tid + 256 * it;
-    const int kb = q / (ROWS / 8), mb = q - kb * (ROWS / 8);
-    const int64_t grow = r0 + mb * 8;
-    const bool okq = q < ROWS && grow < rows_valid;
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int64_t kk = k0 + kb * 8 + rr;
-      const uint32_t off = (okq && kk < K) ? (uint32_t)((kk * ld + grow) * 2) : kOOB;
-      L.r[it * 8 + rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
-template <int ROWS>
-__device__ __forceinline__ void strided_store(const Strided<ROWS>& L, bf16_t* lds) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < Strided<ROWS>::NIT; ++it) {
-    const int q = tid + 256 * it;
-    if (q >= ROWS) continue;
-    const int kb = q / (ROWS / 8), mb = q - kb * (ROWS / 8);
-    const uint4* R = &L.r[it * 8];
-    // R[rr] holds k = kb*8+rr for rows mb*8 .. mb*8+7 (two rows per dword)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1;
-      auto pick = [&](const uint4& v) -> uint32_t {
-        return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-      };
-      uint4 o;
-      if ((i & 1) == 0) {
-        o.x = lo_pair(pick(R[0]), pick(R[1]));
-        o.y = lo_pair(pick(R[2]), pick(R[3]));
-        o.z = lo_pair(pick(R[4]), pick(R[5]));
-        o.w = lo_pair(pick(R[6]), pick(R[7]));
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    if (KC) {
+      const int r = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((lane >> 4) & 3);
+      int64_t grow;
+      bool ok;
+      if (FUSED) {
+        grow = fused_row(r, WN, r0, fdim);
+        ok = grow >= 0;
       } else {
-        o.x = hi_pair(pick(R[0]), pick(R[1]));
-        o.y = hi_pair(pick(R[2]), pick(R[3]));
-        o.z = hi_pair(pick(R[4]), pick(R[5]));
-        o.w = hi_pair(pick(R[6]), pick(R[7]));
+        grow = r0 + r;
+        ok = grow < rows_valid;
       }
-      *reinterpret_cast<uint4*>(lds + swz(mb * 8 + i, kb)) = o;
+      d.off[i] = ok ? (uint32_t)((grow * ld + c * 8) * 2) : kOOB;
+      d.kk[i] = c * 8;
+    } else {
+      const int k = blk * 2 + (lane >> 5);
+      const int s = (lane & 31) ^ ((k & 3) << 1);
+      const int64_t grow = r0 + s * 8;
+      d.off[i] = grow < rows_valid ? (uint32_t)((k * ld + grow) * 2) : kOOB;
+      d.kk[i] = k;
     }
   }
 }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-template <int BM, int BN, bool AKM, bool BKM, int EPI, int RAG>
+__device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int EPI, bool AKM, bool BKM, int RAG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int BM = kRows, BN = kRows;
+  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
   constexpr bool FUSED = EPI == EPI_SWIGLU_FWD;
   constexpr int BNo = FUSED ? BN / 2 : BN;      // output columns per tile
   constexpr int A_EL = BM * kBK, B_EL = BN * kBK;
-  constexpr int BUF = A_EL + B_EL;              // one stage: A tile then B tile
-  constexpr int LDST = WN + 4;                  // staging row stride (floats)
-  static_assert(2 * 32 * LDST * 4 <= BUF * 2, "staging does not fit");
+  constexpr int ST = A_EL + B_EL;               // one stage (bf16 elements)
+  constexpr int NLD = 8;                        // DMA instructions per wave per stage
+  constexpr int LDST = WN + 4;                  // epilogue staging row stride (floats)
+  static_assert(32 * LDST * 4 <= ST * 2, "staging does not fit a stage");
   static_assert(!FUSED || BKM, "fused SwiGLU needs a K-contiguous weight");
-  // The two stages are separate objects so that the compiler can tell the
-  // stage being filled by direct loads from the stage being read (it would
-  // otherwise wait for every in-flight load before each LDS read).
-  __shared__ __attribute__((aligned(1024))) bf16_t lds0[BUF];
-  __shared__ __attribute__((aligned(1024))) bf16_t lds1[BUF];
-  __shared__ int s_tiles[1028];
-  __shared__ int s_wsum[4];
+  static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
+  // Five stages, separate objects so that the compiler can tell a stage being
+  // filled by DMA from the stage being read.
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[ST];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[ST];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[ST];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[ST];
+  __shared__ __attribute__((aligned(1024))) bf16_t st4[ST];
 
   Tile t;
-  if (!resolve_tile<BM, BNo, RAG>(p, s_tiles, s_wsum, t)) return;
+  {
+    // the group-tile scan runs before any load and borrows the last stage
+    int* s_tiles = reinterpret_cast<int*>(st4);
+    const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
+    __syncthreads();
+    if (!have) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
   const bf16_t* Ab = operand_base<bf16_t>(p.a, t);
   const bf16_t* Bb = operand_base<bf16_t>(p.b, t);
-  const int64_t b_rows = FUSED ? p.fdim : p.N;
   // buffer extents: K-contiguous operands span rows x ld, K-strided span K x ld
-  const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(Ab, (AKM ? t.M : t.K) * p.a.ld * 2);
-  const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(Bb, (BKM ? (FUSED ? 2 * p.fdim : p.N) : t.K) * p.b.ld * 2);
+  const int64_t b_rows = FUSED ? 2 * p.fdim : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, (AKM ? t.M : t.K) * p.a.ld * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, (BKM ? b_rows : t.K) * p.b.ld * 2);
+  DmaSrc da, db;
+  dma_src<AKM, false, WN>(da, p.a.ld, t.M, t.m0, p.fdim, wave, lane);
+  dma_src<BKM, FUSED, WN>(db, p.b.ld, FUSED ? p.fdim : p.N, t.n0, p.fdim, wave, lane);
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -192,82 +165,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  Strided<BM> sa;
-  Strided<BN> sb;
   const int64_t nk = (t.K + kBK - 1) / kBK;
+  const int64_t nk5 = (nk + 4) / 5 * 5;         // whole trips of the ring; extra steps read zeros
 
-  auto issue = [&](int64_t kt, bf16_t* as) __attribute__((always_inline)) {
+  // DMA instruction q (0..7: A blocks then B blocks) of k-step kt into stage s
+  auto dma = [&](int64_t kt, bf16_t* s, int q) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK;
-    if (AKM) direct_load<BM, false, WN>(ra, as, p.a.ld, t.M, t.m0, k0, t.K, p.fdim, wave, lane);
-    else strided_load<BM>(sa, ra, p.a.ld, t.M, t.m0, k0, t.K);
-    if (BKM) direct_load<BN, FUSED, WN>(rb, as + A_EL, p.b.ld, b_rows, t.n0, k0, t.K, p.fdim, wave, lane);
-    else strided_load<BN>(sb, rb, p.b.ld, p.N, t.n0, k0, t.K);
+    const bool isA = q < 4;
+    const int i = q & 3;
+    const DmaSrc& d = isA ? da : db;
+    const bool kc = isA ? AKM : BKM;
+    const int64_t ld = isA ? p.a.ld : p.b.ld;
+    const bool kin = d.kk[i] < t.K - k0;
+    const uint32_t so = (uint32_t)(kc ? k0 * 2 : k0 * ld * 2);
+    bf16_t* tile = isA ? s : s + A_EL;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 4 + i) * 512), 16,
+                                             kin ? d.off[i] : kOOB, so, 0, 0);
   };
-  auto finish = [&](bf16_t* as) __attribute__((always_inline)) {
-    if (!AKM) strided_store<BM>(sa, as);
-    if (!BKM) strided_store<BN>(sb, as + A_EL);
+
+  // fragment of 32 rows (base .. base+31) for k slice sl of a stage tile
+  auto frag = [&](const bf16_t* tile, bool kc, int base, int sl) __attribute__((always_inline)) -> bf16x8 {
+    const char* tb = reinterpret_cast<const char*>(tile);
+    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc_off(base + (lane & 31), sl * 2 + (lane >> 5)));
+    const int g = lane >> 4, i = lane & 15;
+    const int row = base + 16 * (g & 1) + 4 * (i & 3);
+    const int k = 16 * sl + 8 * (g >> 1) + (i >> 2);
+    const int b0 = ks_off(k, row >> 3) + (row & 7) * 2;
+    const int b1 = ks_off(k + 4, row >> 3) + (row & 7) * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tb + b0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tb + b1));
+    return join(lo, hi);
   };
-  // one k-step: loads of tile kt+1 into `nxt` (for kt+1 == nk every lane is
-  // out of range and zeros land in the idle stage), MFMAs on `cur`
-  auto kstep = [&](int64_t kt, const bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
-    issue(kt + 1, nxt);
-    const bf16_t* as = cur;
-    const bf16_t* bs = cur + A_EL;
-    bf16x8 fa[2][MI], fb[2][NI];
-    auto ldfrag = [&](int buf, int kk) __attribute__((always_inline)) {
-      const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(as + swz(wm0 + i * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        fb[buf][j] = *reinterpret_cast<const bf16x8*>(bs + swz(wn0 + j * 32 + (lane & 31), ch));
-    };
-    ldfrag(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      // one scheduling region per slice: the next slice's fragment reads are
-      // issued, then this slice's MFMAs run while they are in flight
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 1 < kBK / 16) ldfrag((kk + 1) & 1, kk + 1);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-      if (kk + 1 < kBK / 16) {
-        // start the reads early: one after each of the first MI+NI MFMAs
-#pragma unroll
-        for (int x = 0; x < MI + NI; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
-      }
-    }
+
+  bf16x8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+  auto ldfrag_q = [&](bf16x8* fa, bf16x8* fb, const bf16_t* s, int sl, int q) __attribute__((always_inline)) {
+    if (q < MI) fa[q] = frag(s, AKM, wm0 + q * 32, sl);
+    else fb[q - MI] = frag(s + A_EL, BKM, wn0 + (q - MI) * 32, sl);
+  };
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb, int q) __attribute__((always_inline)) {
+    const int i = q / NI, j = q % NI;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // one k-step on stage `cur` (slice-0 fragments already in fa0/fb0); the
+  // loads of k-step kt+4 go to stage `fill`
+  auto kstep = [&](int64_t kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    finish(nxt);
-    wait_vm_all();
-    __syncthreads();
+    static_for<NM>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      mma(fa0, fb0, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < MI + NI) ldfrag_q(fa1, fb1, cur, 1, q);
+      if ((q & 3) == 3) dma(kt + 4, fill, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // stage kt+1's loads were followed by those of kt+2, kt+3 and half of kt+4
+    wait_vm<2 * NLD + NLD / 2>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      mma(fa1, fb1, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < MI + NI) ldfrag_q(fa0, fb0, nxt, 0, q);
+      if ((q & 3) == 3) dma(kt + 4, fill, NLD / 2 + (q >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
-  if (nk > 0) {
-    issue(0, lds0);
-    finish(lds0);
-    wait_vm_all();
-    __syncthreads();
-  }
-  // two k-steps per trip, so each names its stages statically; for odd nk
-  // the last step multiplies the all-zero stage left by out-of-range loads
-  for (int64_t kt = 0; kt < nk; kt += 2) {
-    kstep(kt, lds0, lds1);
-    kstep(kt + 1, lds1, lds0);
+  if (nk5 > 0) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(0, st0, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(2, st2, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(3, st3, q);
+    wait_vm<3 * NLD>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, st0, 0, q);
+    for (int64_t kt = 0; kt < nk5; kt += 5) {
+      kstep(kt, st0, st1, st4);
+      kstep(kt + 1, st1, st2, st0);
+      kstep(kt + 2, st2, st3, st1);
+      kstep(kt + 3, st3, st4, st2);
+      kstep(kt + 4, st4, st0, st3);
+    }
+    // the last loads (past the end: zeros) must land before the stages are reused
+    wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
   }
 
-  // ---- epilogue: stage 32 rows of the wave's sub-tile at a time in LDS
-  // (waves 0-1 in the first stage's space, waves 2-3 in the second's)
-  float* stage = reinterpret_cast<float*>(wave < 2 ? lds0 : lds1) + (wave & 1) * (32 * LDST);
+  // ---- epilogue: each wave stages 32 rows of its sub-tile at a time in a
+  // stage of its own
+  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
   static_for<MI>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
 #pragma unroll
@@ -277,7 +272,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int row = ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
         stage[row * LDST + j * 32 + (lane & 31)] = acc[i][j][r];
       }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     const int64_t m0 = t.m0 + wm0 + i * 32;
     if (FUSED)
       epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN / 2, m0,
@@ -287,24 +282,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           p, t, stage, LDST, m0, t.n0 + wn0, lane);
     else
       epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN, m0, t.n0 + wn0, lane, 64);
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   });
 }
 
 // ------------------------------------------------------------------ launch
-template <int BM, int BN, bool AKM, bool BKM, int EPI, int RAG>
+template <bool AKM, bool BKM, int EPI, int RAG>
 static hipError_t launch_one(const GemmArgs& p, hipStream_t s) {
-  constexpr int BNo = EPI == EPI_SWIGLU_FWD ? BN / 2 : BN;
+  constexpr int BNo = EPI == EPI_SWIGLU_FWD ? kRows / 2 : kRows;
   const int64_t nt = (p.N + BNo - 1) / BNo;
   int64_t tiles;
   if (RAG == RAG_M)
-    tiles = ((p.max_rows + BM - 1) / BM + p.G) * nt;
+    tiles = ((p.max_rows + kRows - 1) / kRows + p.G) * nt;
   else
-    tiles = (int64_t)p.G * ((p.M + BM - 1) / BM) * nt;
+    tiles = (int64_t)p.G * ((p.M + kRows - 1) / kRows) * nt;
   const int64_t nb = (tiles + 7) / 8 * 8;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKM, BKM, EPI, RAG>), dim3((unsigned)nb),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, AKM, BKM, RAG>), dim3((unsigned)nb), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -312,7 +306,7 @@ static hipError_t launch_one(const GemmArgs& p, hipStream_t s) {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s) {
 #define MOE_CASE(AK, BK_, E_, R_)                                          \
   if (akm == AK && bkm == BK_ && epi == E_ && rag == R_)                   \
-    return launch_one<256, 256, AK, BK_, E_, R_>(p, s);
+    return launch_one<AK, BK_, E_, R_>(p, s);
   MOE_CASE(true, true, EPI_SWIGLU_FWD, RAG_M)
   MOE_CASE(true, true, EPI_GELU_FWD, RAG_M)
   MOE_CASE(true, true, EPI_STORE, RAG_M)
