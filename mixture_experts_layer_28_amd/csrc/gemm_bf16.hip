@@ -166,7 +166,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int64_t nk = (t.K + kBK - 1) / kBK;
-  const int64_t nk5 = (nk + 4) / 5 * 5;         // whole trips of the ring; extra steps read zeros
 
   // DMA instruction q (0..7: A blocks then B blocks) of k-step kt into stage s
   auto dma = [&](int64_t kt, bf16_t* s, int q) __attribute__((always_inline)) {
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
   };
 
-  if (nk5 > 0) {
+  if (nk > 0) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) dma(0, st0, q);
 #pragma unroll
@@ -247,14 +246,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, st0, 0, q);
-    for (int64_t kt = 0; kt < nk5; kt += 5) {
+    // five k-steps per trip name their stages statically (up to four extra
+    // k-steps at the end multiply the zeros their out-of-range loads left)
+    for (int64_t kt = 0; kt < nk; kt += 5) {
       kstep(kt, st0, st1, st4);
       kstep(kt + 1, st1, st2, st0);
       kstep(kt + 2, st2, st3, st1);
       kstep(kt + 3, st3, st4, st2);
       kstep(kt + 4, st4, st0, st3);
     }
-    // the last loads (past the end: zeros) must land before the stages are reused
+    // every load (including those past the end) must land before the stages are reused
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
