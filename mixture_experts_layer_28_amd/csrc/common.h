@@ -60,7 +60,12 @@ __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
 
 // ------------------------------------------------------------ activations
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + expf(-a)); }
+// logistic function from the hardware exp2 and reciprocal (a few ulp in
+// float32; used by the GEMM epilogues, whose outputs are rounded to bf16 or
+// compared at 1e-5). Saturates cleanly: a -> -inf gives 1/inf = 0.
+__device__ __forceinline__ float sigmoidf_(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
 __device__ __forceinline__ float silu_f(float a) { return a * sigmoidf_(a); }
 __device__ __forceinline__ float dsilu_f(float a) {
   float s = sigmoidf_(a);

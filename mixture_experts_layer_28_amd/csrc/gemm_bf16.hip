@@ -106,6 +106,20 @@ __device__ __forceinline__ void dma_src(DmaSrc& d, int64_t ld, int64_t rows_vali
   }
 }
 
+// four floats -> four bf16 (round to nearest even) in one 8-byte store
+__device__ __forceinline__ void store4_bf16(bf16_t* dst, const float* v) {
+  uint2 w;
+  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+__device__ __forceinline__ void unpack4_bf16(uint2 w, float* v) {
+  v[0] = bf2f(w.x & 0xffffu);
+  v[1] = bf2f(w.x >> 16);
+  v[2] = bf2f(w.y & 0xffffu);
+  v[3] = bf2f(w.y >> 16);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
@@ -123,8 +137,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int A_EL = BM * kBK, B_EL = BN * kBK;
   constexpr int ST = A_EL + B_EL;               // one stage (bf16 elements)
   constexpr int NLD = 8;                        // DMA instructions per wave per stage
-  constexpr int LDST = WN + 4;                  // epilogue staging row stride (floats)
-  static_assert(32 * LDST * 4 <= ST * 2, "staging does not fit a stage");
   static_assert(!FUSED || BKM, "fused SwiGLU needs a K-contiguous weight");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
   // Five stages, separate objects so that the compiler can tell a stage being
@@ -201,9 +213,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (q < MI) fa[q] = frag(s, AKM, wm0 + q * 32, sl);
     else fb[q - MI] = frag(s + A_EL, BKM, wn0 + (q - MI) * 32, sl);
   };
+  // Each block is accumulated transposed (B fragment as the MFMA's first
+  // operand), so lane l holds row wm0+32i+(l&31) and, in acc[i][j][4g..4g+3],
+  // the four consecutive columns wn0+32j+8g+4(l>>5) .. +3: the epilogue then
+  // writes 8-byte row pieces straight from the accumulators.
   auto mma = [&](const bf16x8* fa, const bf16x8* fb, int q) __attribute__((always_inline)) {
     const int i = q / NI, j = q % NI;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
   // one k-step on stage `cur` (slice-0 fragments already in fa0/fb0); the
@@ -261,28 +277,112 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_s_barrier();
   }
 
-  // ---- epilogue: each wave stages 32 rows of its sub-tile at a time in a
-  // stage of its own
-  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  // ---- epilogue: per 32-row block row i, the wave stages its 32 x 128 fp32
+  // results in a stage of its own (one 16-byte write per (j, g): the four
+  // consecutive columns the transposed accumulators hold), then reads them
+  // back row-contiguous: lane l takes 16-byte slot l&31 of row 2q + (l>>5),
+  // so every global access of an instruction covers two whole 256-byte rows.
+  // Slot s of row r sits at r*512 + ((s ^ (r & 7)) << 4).
+  char* stg = reinterpret_cast<char*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
+  bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
+  if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
+  const int lr = lane & 31, lh = lane >> 5;
   static_for<MI>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-        stage[row * LDST + j * 32 + (lane & 31)] = acc[i][j][r];
-      }
+    static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int j = decltype(Q)::value / 4, g = decltype(Q)::value % 4;
+      const int sl = 8 * j + 2 * g + lh;
+      f32x4 v;
+      v[0] = acc[i][j][4 * g];
+      v[1] = acc[i][j][4 * g + 1];
+      v[2] = acc[i][j][4 * g + 2];
+      v[3] = acc[i][j][4 * g + 3];
+      *reinterpret_cast<f32x4*>(stg + lr * 512 + ((sl ^ (lr & 7)) << 4)) = v;
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    const int64_t m0 = t.m0 + wm0 + i * 32;
-    if (FUSED)
-      epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN / 2, m0,
-                                 t.n0 + (wave & 1) * (WN / 2), lane, 64);
-    else if (EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD)
-      epilogue_act_bwd<(EPI == EPI_SWIGLU_BWD ? EPI_SWIGLU_BWD : EPI_GELU_BWD), 32, WN, 64>(
-          p, t, stage, LDST, m0, t.n0 + wn0, lane);
-    else
-      epilogue_rows<bf16_t, EPI>(p, t, stage, LDST, 32, WN, m0, t.n0 + wn0, lane, 64);
+    const int64_t mrow0 = t.m0 + wm0 + 32 * i;
+    if (EPI == EPI_SWIGLU_FWD) {
+      // slots 0..15 hold gate columns, 16..31 the matching up columns: lane l
+      // takes gate slot l&15 and up slot (l&15)+16 of row 4q + (l>>4)
+      const int sg = lane & 15, rr = lane >> 4;
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        const int r = 4 * q + rr;
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((sg ^ (r & 7)) << 4));
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((sg + 16) ^ (r & 7)) << 4));
+        const int64_t m = mrow0 + r;
+        const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 4 * sg;
+        if (m >= t.M || hc >= p.N) return;
+        float a[4], b[4], h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a4[e];
+          b[e] = b4[e];
+          h[e] = silu_f(a[e]) * b[e];
+        }
+        store4_bf16(cb + m * p.ldc + hc, h);
+        store4_bf16(ab + m * p.ldaux + hc, a);
+        store4_bf16(ab + m * p.ldaux + p.fdim + hc, b);
+      });
+    } else {
+      constexpr bool BWD = EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD;
+      constexpr bool SW = EPI == EPI_SWIGLU_BWD;
+      const int64_t n = t.n0 + wn0 + 4 * lr;
+      const bool nok = n < p.N;
+      // backward: this block row's saved pre-activations, all loads issued
+      // before any math (rows/columns clamped into range when out)
+      uint2 ra[BWD ? 16 : 1], rb[SW ? 16 : 1];
+      if (BWD) {
+        const int64_t nc = nok ? n : p.N - 4;
+        static_for<16>([&](auto Q) __attribute__((always_inline)) {
+          constexpr int q = decltype(Q)::value;
+          int64_t m = mrow0 + 2 * q + lh;
+          m = m < t.M ? m : t.M - 1;
+          ra[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + nc);
+          if (SW) rb[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + p.fdim + nc);
+        });
+      }
+      static_for<16>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        const int r = 2 * q + lh;
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((lr ^ (r & 7)) << 4));
+        const int64_t m = mrow0 + r;
+        if (m >= t.M || !nok) return;
+        float v[4], o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v4[e];
+        if (EPI == EPI_STORE) {
+          store4_bf16(cb + m * p.ldc + n, v);
+        } else if (EPI == EPI_GELU_FWD) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = gelu_f(v[e]);
+          store4_bf16(cb + m * p.ldc + n, o);
+          store4_bf16(ab + m * p.ldaux + n, v);
+        } else {
+          float a[4];
+          unpack4_bf16(ra[BWD ? q : 0], a);
+          if (SW) {
+            float b[4], o2[4];
+            unpack4_bf16(rb[SW ? q : 0], b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = v[e] * b[e] * dsilu_f(a[e]);
+              o2[e] = v[e] * silu_f(a[e]);
+            }
+            store4_bf16(cb + m * p.ldc + n, o);
+            store4_bf16(cb + m * p.ldc + p.fdim + n, o2);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = v[e] * dgelu_f(a[e]);
+            store4_bf16(cb + m * p.ldc + n, o);
+          }
+        }
+      });
+    }
+    // the next block row overwrites the stage: finish this one's reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
   });
 }
@@ -305,6 +405,7 @@ static hipError_t launch_one(const GemmArgs& p, hipStream_t s) {
 
 // Dispatch over the layouts/epilogues the layer uses.
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s) {
+  if (p.col_bias) return hipErrorInvalidValue;   // column bias is an fp32-GEMM feature only
 #define MOE_CASE(AK, BK_, E_, R_)                                          \
   if (akm == AK && bkm == BK_ && epi == E_ && rag == R_)                   \
     return launch_one<AK, BK_, E_, R_>(p, s);
