@@ -35,7 +35,8 @@ from typing import Optional
 import numpy as np
 
 # stream slots of SeedSequence(seed, spawn_key=(slot, index))
-_SLOT_X, _SLOT_WR, _SLOT_SEL, _SLOT_DY, _SLOT_W13, _SLOT_W2, _SLOT_SW13, _SLOT_SW2 = range(8)
+(_SLOT_X, _SLOT_WR, _SLOT_SEL, _SLOT_DY, _SLOT_W13, _SLOT_W2, _SLOT_SW13, _SLOT_SW2,
+ _SLOT_GUMBEL) = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -56,6 +57,7 @@ class Workload:
     aux_coef: float = 0.0         # weight of the load-balance loss in the backward
     z_coef: float = 0.0           # weight of the router z-loss in the backward (softmax only)
     bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
+    gumbel_tau: Optional[float] = None   # noisy gate temperature; draws uniforms [T, E]
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -178,12 +180,19 @@ def gen_shared_w2(w: Workload) -> Optional[np.ndarray]:
     return _stack(gen_expert_w2, w, w.n_shared, True, 1) if w.n_shared else None
 
 
+def gen_gumbel_u(w: Workload, T: Optional[int] = None) -> Optional[np.ndarray]:
+    """Uniforms in [0, 1) for the noisy gate, fp32 [T, E] (None when the workload has no noise)."""
+    if w.gumbel_tau is None:
+        return None
+    return _rng(w.seed, _SLOT_GUMBEL, 0).random(size=(T or w.T, w.E), dtype=np.float32)
+
+
 def gen_all(w: Workload, threads: Optional[int] = None) -> dict:
     """Every input of one layer fwd+bwd, as numpy arrays (bf16 as uint16 bits)."""
     return dict(
         x=gen_x(w), w_r=gen_router_weight(w), logit_bias=gen_logit_bias(w),
         sel_bias=gen_sel_bias(w), w13=gen_w13(w, threads), w2=gen_w2(w, threads),
-        sw13=gen_shared_w13(w), sw2=gen_shared_w2(w), dy=gen_dy(w),
+        sw13=gen_shared_w13(w), sw2=gen_shared_w2(w), dy=gen_dy(w), gumbel_u=gen_gumbel_u(w),
     )
 
 

@@ -32,9 +32,26 @@ NEAR_TIE = 1e-5   # fp32 score gap under which two ranks count as a near-tie
 
 
 # ------------------------------------------------------------------ router
-def router_forward(x, w_r, k, score="softmax", logit_bias=None, sel_bias=None):
+GUMBEL_EPS = 1e-10   # the eps of [Balance]'s noisy gate (section 噪声注入)
+
+
+def gumbel_noise(u):
+    """Gumbel noise of [Balance] (section 噪声注入) from uniforms u in [0, 1):
+    g = -log(-log(u + eps) + eps). The uniforms are an input (drawn by the
+    caller), so both sides see the same draws."""
+    u = np.asarray(u, dtype=np.float64)
+    return -np.log(-np.log(u + GUMBEL_EPS) + GUMBEL_EPS)
+
+
+def router_forward(x, w_r, k, score="softmax", logit_bias=None, sel_bias=None,
+                   gumbel_u=None, tau=None):
     """Router of [Recipe] §2.2: g(x) = x W_r, scores = softmax(g), top-k,
     gate weights renormalised over the chosen k.
+
+    Noisy gate of [Balance] (section 噪声注入): with uniforms gumbel_u [T, E]
+    and temperature tau, the logits become (l + gumbel_noise(u)) / tau and
+    everything downstream (scores, choice, gates, statistics, z-loss) uses
+    them; the returned "logits" are these. Softmax scoring only.
 
     x [T, d], w_r [E, d] (stored out x in, so g = x w_r^T), optional
     logit_bias [E] added to the logits (a fixed shift: it moves both the
@@ -50,6 +67,10 @@ def router_forward(x, w_r, k, score="softmax", logit_bias=None, sel_bias=None):
     logits = x @ w_r.T
     if logit_bias is not None:
         logits = logits + logit_bias[None, :]
+    if gumbel_u is not None:
+        if score != "softmax" or not tau or tau <= 0:
+            raise ValueError("the noisy gate needs softmax scoring and tau > 0")
+        logits = (logits + gumbel_noise(gumbel_u)) / tau
     if score == "softmax":
         # max-subtracted so exp never overflows ([Recipe] §1: fp32 router against 0/0)
         m = logits.max(axis=1, keepdims=True)
@@ -287,7 +308,7 @@ def combine_backward(dY, O, gates, row_of):
 
 # ---------------------------------------------------------- router backward
 def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux_coef=0.0,
-                    y=None, z_coef=0.0, logits=None):
+                    y=None, z_coef=0.0, logits=None, tau=None):
     """Gradient of the router through the renormalised gates of [Recipe] §2.2
     (the top-k choice itself is piecewise constant), plus aux_coef times the
     gradient of L_aux = E sum_i y_i z_i with the counts y held fixed.
@@ -300,7 +321,10 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
       softmax: dl_te += aux_coef (E/T) s_te (y_e - sum_i y_i s_ti)
       sigmoid: dl_te += aux_coef (E/T) y_e s_te (1 - s_te)
     Plus z_coef times the gradient of z_loss(logits) when z_coef != 0.
-    Returns dict(dlogits [T,E], dw_r [E,d] = dl^T x, dx_router [T,d] = dl W_r).
+    With the noisy gate (tau given) these are gradients with respect to the
+    noisy logits (l + g) / tau; the chain rule to l divides them by tau.
+    Returns dict(dlogits [T,E], dw_r [E,d] = dl^T x, dx_router [T,d] = dl W_r),
+    dlogits being the gradient with respect to l.
     """
     T, E = scores.shape
     k = topk_idx.shape[1]
@@ -323,6 +347,8 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
             dl += aux_coef * (E / T) * y[None, :] * scores * (1.0 - scores)
     if z_coef != 0.0:
         dl += z_coef * z_loss_grad(logits)
+    if tau is not None:
+        dl = dl / tau
     return dict(dlogits=dl, dw_r=dl.T @ x, dx_router=dl @ w_r)
 
 
@@ -378,11 +404,11 @@ def permute_backward(dx_perm, row_of, dx_shared=None, dx_router=None):
 
 # ------------------------------------------------------------- whole layer
 def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
-                  logit_bias=None, sel_bias=None, sw13=None, sw2=None):
+                  logit_bias=None, sel_bias=None, sw13=None, sw2=None, gumbel_u=None, tau=None):
     """Forward of the layer: router, stats, permute, grouped FFN, combine.
     All arrays float64 (exact values of the fp32/bf16 inputs)."""
     E = w13.shape[0]
-    r = router_forward(x, w_r, k, score, logit_bias, sel_bias)
+    r = router_forward(x, w_r, k, score, logit_bias, sel_bias, gumbel_u, tau)
     st = aux_stats(r["scores"], r["topk_idx"], E)
     p = permute(r["topk_idx"], E, cap)
     x_perm = x[p["token_of"]]
@@ -392,7 +418,7 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
 
 
 def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
-                   sw13=None, sw2=None, z_coef=0.0):
+                   sw13=None, sw2=None, z_coef=0.0, tau=None):
     """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
     router bwd, un-permute."""
     r, p = fwd["router"], fwd["perm"]
@@ -400,6 +426,6 @@ def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_
     g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
                              sw13, sw2, dY)
     rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
-                         aux_coef, fwd["stats"]["y"], z_coef, r["logits"])
+                         aux_coef, fwd["stats"]["y"], z_coef, r["logits"], tau)
     dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])
     return dict(dgate=dgate, dO=dO, dX=dX, **g, **rb)

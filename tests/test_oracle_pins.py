@@ -462,3 +462,80 @@ def test_layer_gradient_with_z_loss_by_central_differences():
             num[i] = (lp - lm) / (2 * h)
         np.testing.assert_allclose(ana, num, rtol=0, atol=2e-6 * max(1.0, np.abs(num).max()),
                                    err_msg=name)
+
+
+# ------------------------------------------------------------ noisy gate
+def test_gumbel_noise_hand_values():
+    """u = exp(-exp(-c)) gives Gumbel noise c (up to the eps of [Balance])."""
+    c = np.array([-1.5, 0.0, 0.7, 2.0])
+    u = np.exp(-np.exp(-c))
+    np.testing.assert_allclose(O.gumbel_noise(u), c, rtol=0, atol=1e-8)
+    # u -> 0 and u -> 1 stay finite thanks to eps
+    assert np.isfinite(O.gumbel_noise(np.array([0.0, 1.0 - 2**-24]))).all()
+
+
+def test_gumbel_max_samples_the_softmax():
+    """Gumbel-max: argmax(l + g) with g from uniform draws is distributed as
+    softmax(l) (a property of the Gumbel law, checked statistically)."""
+    rng = np.random.default_rng(11)
+    l = np.array([0.3, -1.0, 1.2, 0.0, -0.4])
+    n = 200_000
+    u = rng.random((n, l.size))
+    pick = np.argmax(l[None, :] + O.gumbel_noise(u), axis=1)
+    freq = np.bincount(pick, minlength=l.size) / n
+    p = np.exp(l) / np.exp(l).sum()
+    assert (np.abs(freq - p) < 5 * np.sqrt(p * (1 - p) / n)).all(), (freq, p)
+
+
+def test_noisy_router_worked_example_and_top1():
+    """One token, three experts, noise c = (0, 1, -1), tau = 0.5: scores are
+    softmax((l + c) / tau) by hand; with k = 1 the choice is argmax(l + c)."""
+    x = np.array([[1.0, 0.0]])
+    w_r = np.array([[0.2, 0.0], [-0.3, 0.0], [0.9, 0.0]])
+    c = np.array([0.0, 1.0, -1.0])
+    u = np.exp(-np.exp(-c))[None, :]
+    r = O.router_forward(x, w_r, 1, gumbel_u=u, tau=0.5)
+    z = (np.array([0.2, -0.3, 0.9]) + c) / 0.5
+    want = np.exp(z) / np.exp(z).sum()
+    np.testing.assert_allclose(r["scores"][0], want, rtol=1e-8)
+    assert r["topk_idx"][0, 0] == int(np.argmax(np.array([0.2, -0.3, 0.9]) + c)) == 1
+    assert r["gates"][0, 0] == 1.0
+    with pytest.raises(ValueError):
+        O.router_forward(x, w_r, 1, score="sigmoid", gumbel_u=u, tau=0.5)
+
+
+def test_layer_gradient_with_noisy_gate_by_central_differences():
+    """Fixed draws make the noisy layer deterministic: its dX and dW_r
+    (including the aux and z-loss terms and the 1/tau chain factor) match
+    central differences."""
+    for seed in range(50):
+        w, g = _tiny(T=8, d=6, E=5, k=2, f=4, seed=seed, gumbel_tau=0.7)
+        g["w_r"] = g["w_r"] * 40.0
+        r = O.router_forward(g["x"], g["w_r"], w.k, gumbel_u=g["gumbel_u"], tau=0.7)
+        if not O.near_tie_tokens(r["key"], w.k, 1e-3).any():
+            break
+    ac, zc, tau = 0.3, 0.2, 0.7
+
+    def loss(x, w_r):
+        f = O.layer_forward(x, w_r, g["w13"], g["w2"], w.k, gumbel_u=g["gumbel_u"], tau=tau)
+        st = f["stats"]
+        # the aux gradient holds y fixed: differentiate E * sum_i y_i z_i with y frozen
+        aux = w.E * float((y_fixed * st["z"]).sum())
+        return (float((f["Y"] * g["dy"]).sum()) + ac * aux
+                + zc * O.z_loss(f["router"]["logits"])), f
+
+    y_fixed = O.layer_forward(g["x"], g["w_r"], g["w13"], g["w2"], w.k, gumbel_u=g["gumbel_u"],
+                              tau=tau)["stats"]["y"]
+    _, fwd = loss(g["x"], g["w_r"])
+    bwd = O.layer_backward(fwd, g["x"], g["w_r"], g["w13"], g["w2"], g["dy"], aux_coef=ac,
+                           z_coef=zc, tau=tau)
+    h = 1e-6
+    for name, val, ana in (("x", g["x"], bwd["dX"]), ("w_r", g["w_r"], bwd["dw_r"])):
+        num = np.zeros_like(val)
+        for i in np.ndindex(val.shape):
+            v2 = val.copy(); v2[i] += h
+            lp, _ = loss(v2, g["w_r"]) if name == "x" else loss(g["x"], v2)
+            v2[i] -= 2 * h
+            lm, _ = loss(v2, g["w_r"]) if name == "x" else loss(g["x"], v2)
+            num[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(ana, num, rtol=1e-5, atol=1e-7, err_msg=name)
