@@ -174,12 +174,13 @@ def cpu_baseline(w, g, tokens):
     ws = w.replace(T=tokens)
     f = {n: (as_f64(v, w.dtype) if v is not None else None) for n, v in g.items()}
     x, dy = f["x"][:tokens], f["dy"][:tokens]
+    gu = f["gumbel_u"][:tokens] if f["gumbel_u"] is not None else None
     cap = O.capacity(ws.T, ws.k, ws.E, ws.cf)
     t0 = time.perf_counter()
     fwd = O.layer_forward(x, f["w_r"], f["w13"], f["w2"], ws.k, ws.score, ws.act, cap,
-                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"])
+                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau)
     O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act, ws.aux_coef,
-                     f["sw13"], f["sw2"])
+                     f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau)
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {tokens} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in "
@@ -236,7 +237,7 @@ def main():
         del src, dst
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -76,7 +76,8 @@ typedef struct {
   int32_t dtype;     /* moe_dtype */
   int32_t score;     /* moe_score_fn */
   int32_t act;       /* moe_activation */
-  int32_t reserved;  /* must be 0 */
+  float gumbel_tau;  /* noisy-gate temperature ([Balance], section 噪声注入);
+                        0 = plain router, > 0 = moe_route takes Gumbel uniforms */
   int64_t capacity;  /* per-expert limit on kept assignments; < 0: no limit */
 } moe_desc;
 
@@ -102,6 +103,12 @@ typedef enum {
  *   w_r        [E, d] float                  in
  *   logit_bias [E] float or NULL             in  (added to the logits)
  *   sel_bias   [E] float or NULL             in  (added to the key only)
+ *   gumbel_u   [T, E] float in [0, 1)        in  (required iff desc->gumbel_tau > 0)
+ * Noisy gate ([Balance], section 噪声注入): with desc->gumbel_tau = tau > 0
+ * the logits become (l + g) / tau, g = -log(-log(u + 1e-10) + 1e-10) (g is
+ * evaluated in float64 from the float32 draw); scores, key, gates and lse all
+ * use them. Softmax scoring only (sigmoid returns MOE_ERR_UNSUPPORTED). The
+ * caller draws u, so the noise is reproducible and testable.
  *   topk_idx   [T, k] int32                  out (expert of each slot)
  *   gate       [T, k] float                  out
  *   scores     [T, E] float                  out
@@ -109,8 +116,8 @@ typedef enum {
  *   ws         MOE_OP_ROUTE bytes            scratch
  */
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
-              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, float* lse,
-              void* ws, size_t ws_bytes, void* stream);
+              const float* sel_bias, const float* gumbel_u, int32_t* topk_idx, float* gate,
+              float* scores, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_aux_stats: load-balance statistics of [Balance] (section 辅助损失函数)
  * and [Recipe] §5.2: counts_i = assignments routed to expert i before any
@@ -225,6 +232,9 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
  * Plus z_coef times the gradient of the z-loss mean_t lse_t^2:
  *   dl_te += z_coef (2/T) lse_t softmax(l_t)_e   (softmax scoring only;
  *   z_coef != 0 with sigmoid scoring returns MOE_ERR_UNSUPPORTED).
+ * With the noisy gate (desc->gumbel_tau = tau > 0) the terms above are taken
+ * with respect to the noisy logits (l + g) / tau, and dlogits (the gradient
+ * with respect to l) is their sum divided by tau.
  * dw_r = dl^T x, dx_router = dl W_r (float32).
  *   x [T, d] dt, w_r [E, d], scores [T, E], topk_idx, gate, dgate [T, k]   in
  *   y [E] float (from moe_aux_stats; may be NULL when aux_coef == 0)        in

@@ -16,7 +16,7 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
@@ -37,7 +37,7 @@ class MoeDesc(ctypes.Structure):
         ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
         ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("n_shared", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("score", ctypes.c_int32), ("act", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("capacity", ctypes.c_int64),
+        ("gumbel_tau", ctypes.c_float), ("capacity", ctypes.c_int64),
     ]
 
 
@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         DP = ctypes.POINTER(MoeDesc)
         sig = {
-            "moe_route": [DP] + [_P] * 9 + [ctypes.c_size_t, _P],
+            "moe_route": [DP] + [_P] * 10 + [ctypes.c_size_t, _P],
             "moe_aux_stats": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
             "moe_bias_update": [DP, _P, ctypes.c_float, _P, _P],
             "moe_permute": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
@@ -99,11 +99,12 @@ def _check(fn: str, status: int):
 
 
 def make_desc(T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
-              capacity=None) -> MoeDesc:
+              capacity=None, gumbel_tau=0.0) -> MoeDesc:
     return MoeDesc(T=T, d=d, E=E, k=k, f=f, n_shared=n_shared,
                    dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
                    score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
-                   act=MOE_SWIGLU if act == "swiglu" else MOE_GELU, reserved=0,
+                   act=MOE_SWIGLU if act == "swiglu" else MOE_GELU,
+                   gumbel_tau=float(gumbel_tau or 0.0),
                    capacity=-1 if capacity is None else int(capacity))
 
 
@@ -165,11 +166,11 @@ def _ws(ws):
 
 # ------------------------------------------------------------- entry points
 def route(desc, x, w_r, logit_bias, sel_bias, topk_idx, gate, scores, lse=None, ws=None,
-          stream=None):
+          stream=None, gumbel_u=None):
     wp, wn = _ws(ws)
     _check("moe_route", lib().moe_route(ctypes.byref(desc), _p(x), _p(w_r), _p(logit_bias),
-                                        _p(sel_bias), _p(topk_idx), _p(gate), _p(scores), _p(lse),
-                                        wp, wn, _stream(stream)))
+                                        _p(sel_bias), _p(gumbel_u), _p(topk_idx), _p(gate),
+                                        _p(scores), _p(lse), wp, wn, _stream(stream)))
 
 
 def aux_stats(desc, scores, topk_idx, lse, counts, y, z, out3, ws=None, stream=None):

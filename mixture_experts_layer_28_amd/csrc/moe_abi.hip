@@ -19,7 +19,7 @@ hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dw(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dx(const GemmArgs& p, hipStream_t s);
 hipError_t launch_router_topk(const float*, int, int, int, int, const float*, int32_t*, float*,
-                              float*, float*, hipStream_t);
+                              float*, float*, const float*, float, hipStream_t);
 hipError_t launch_aux_stats(const float*, const int32_t*, const float*, int, int, int, double*,
                             int32_t*, double*, int32_t*, float*, float*, float*, hipStream_t);
 hipError_t launch_bias_update(const int32_t*, int, int64_t, float, float*, hipStream_t);
@@ -32,15 +32,15 @@ hipError_t launch_combine_bwd(const void*, const void*, bool, const float*, cons
 hipError_t launch_unpermute(const void*, const int32_t*, const void*, const float*, bool, int, int,
                             int64_t, void*, hipStream_t);
 hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, const float*,
-                                 const float*, float, const float*, float, int, int, int, int,
-                                 float*, hipStream_t);
+                                 const float*, float, const float*, float, float, int, int, int,
+                                 int, float*, hipStream_t);
 hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 hipError_t launch_router_small(const void*, bool, const float*, const float*, const float*, int,
                                int, int64_t, int, int, int32_t*, float*, float*, float*,
-                               hipStream_t);
+                               const float*, float, hipStream_t);
 }  // namespace moe
 
 using namespace moe;
@@ -161,11 +161,14 @@ int check_desc(const moe_desc* d) {
     return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1 (got %lld)", (long long)d->n_shared);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!(d->gumbel_tau >= 0.0f) || !std::isfinite(d->gumbel_tau))
+    return fail(MOE_ERR_INVALID_ARG, "gumbel_tau must be finite and >= 0");
+  if (d->gumbel_tau > 0.0f && d->score != MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the noisy gate needs softmax scoring");
   if (d->score != MOE_SOFTMAX && d->score != MOE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", d->score);
   if (d->act != MOE_SWIGLU && d->act != MOE_GELU)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", d->act);
-  if (d->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
   if (d->T * d->k >= (int64_t(1) << 31) || d->T * d->E >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k and T*E must be < 2^31");
   {
@@ -345,8 +348,8 @@ int moe_capacity(int64_t T, int64_t k, int64_t E, double cf, int64_t* capacity) 
 }
 
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
-              const float* sel_bias, int32_t* topk_idx, float* gate, float* scores, float* lse,
-              void* ws, size_t ws_bytes, void* stream) {
+              const float* sel_bias, const float* gumbel_u, int32_t* topk_idx, float* gate,
+              float* scores, float* lse, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   MOE_TRY(need(x, "x"));
@@ -357,6 +360,8 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   MOE_TRY(need(gate, "gate"));
   MOE_TRY(need(scores, "scores"));
   MOE_TRY(opt(lse, "lse"));
+  if (desc->gumbel_tau > 0.0f) MOE_TRY(need(gumbel_u, "gumbel_u"));
+  else if (gumbel_u) return fail(MOE_ERR_INVALID_ARG, "gumbel_u given but desc->gumbel_tau is 0");
   MOE_TRY(check_ws(desc, MOE_OP_ROUTE, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -365,7 +370,8 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
     Scope sc(K_ROUTER_TOPK, s);
     return hip_check(launch_router_small(x, desc->dtype == MOE_BF16, w_r, logit_bias, sel_bias,
                                          (int)desc->T, (int)desc->E, desc->d, (int)desc->k,
-                                         desc->score, topk_idx, gate, scores, lse, s),
+                                         desc->score, topk_idx, gate, scores, lse, gumbel_u,
+                                         desc->gumbel_tau, s),
                      "router (fused)");
   }
   float* logits = (float*)ws;
@@ -385,7 +391,8 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
   }
   Scope sc(K_ROUTER_TOPK, s);
   return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,
-                                      desc->score, sel_bias, topk_idx, gate, scores, lse, s),
+                                      desc->score, sel_bias, topk_idx, gate, scores, lse, gumbel_u,
+                                      desc->gumbel_tau, s),
                    "router top-k");
 }
 
@@ -698,8 +705,9 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
   const int T = (int)desc->T, E = (int)desc->E, k = (int)desc->k;
   {
     Scope sc(K_ROUTER_DLOGITS, s);
+    const float inv_tau = desc->gumbel_tau > 0.0f ? 1.0f / desc->gumbel_tau : 1.0f;
     MOE_TRY(hip_check(launch_router_dlogits(scores, topk_idx, gate, dgate, y, aux_coef, lse,
-                                            z_coef, T, E, k, desc->score, dlogits, s),
+                                            z_coef, inv_tau, T, E, k, desc->score, dlogits, s),
                       "router dlogits"));
   }
   // dw_r = dl^T x, split over tokens, partials folded in a fixed order

@@ -9,6 +9,11 @@ namespace moe {
 // One wave per token. Experts e = lane + 64*i live in registers (EPL per lane).
 // Softmax is max-subtracted; top-k is k rounds of a wave arg-max on the
 // selection key with ties to the lower expert index.
+// noisy-gate noise from a uniform draw, evaluated in float64
+__device__ __forceinline__ float gumbel_g(float u) {
+  return (float)(-log(-log((double)u + 1e-10) + 1e-10));
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int score,
@@ -16,7 +21,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ gate,
                                                           float* __restrict__ scores,
-                                                          float* __restrict__ lse) {
+                                                          float* __restrict__ lse,
+                                                          const float* __restrict__ gumbel_u,
+                                                          float tau) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -26,6 +33,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     l[i] = e < E ? lrow[e] : -INFINITY;
+    if (gumbel_u && e < E) l[i] = (l[i] + gumbel_g(gumbel_u[t * E + e])) / tau;
     m = fmaxf(m, l[i]);
   }
   m = wave_max(m);
@@ -94,16 +102,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int score,
                               const float* sel_bias, int32_t* topk, float* gate, float* scores,
-                              float* lse, hipStream_t st) {
+                              float* lse, const float* gumbel_u, float tau, hipStream_t st) {
   dim3 grid((T + 3) / 4), block(256);
   if (E <= 64)
-    hipLaunchKernelGGL(router_topk_kernel<1>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
+    hipLaunchKernelGGL(router_topk_kernel<1>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse, gumbel_u, tau);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_topk_kernel<2>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
+    hipLaunchKernelGGL(router_topk_kernel<2>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse, gumbel_u, tau);
   else if (E <= 256)
-    hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
+    hipLaunchKernelGGL(router_topk_kernel<4>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse, gumbel_u, tau);
   else
-    hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse);
+    hipLaunchKernelGGL(router_topk_kernel<16>, grid, block, 0, st, logits, T, E, k, score, sel_bias, topk, gate, scores, lse, gumbel_u, tau);
   return hipGetLastError();
 }
 
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(
     const TX* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ logit_bias,
     const float* __restrict__ sel_bias, int T, int E, int64_t d, int k, int score,
     int32_t* __restrict__ topk_idx, float* __restrict__ gate, float* __restrict__ scores,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const float* __restrict__ gumbel_u, float tau) {
   const int lane = threadIdx.x & 63;
   const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
   if (t0 >= T) return;
@@ -166,6 +174,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(
   for (int e = 0; e < EMAX; ++e)
     if (e < E) {
       l[e] += logit_bias ? logit_bias[e] : 0.f;
+      if (gumbel_u) l[e] = (l[e] + gumbel_g(gumbel_u[(int64_t)t * E + e])) / tau;
       m = fmaxf(m, l[e]);
     }
   float sum = 0.f;
@@ -210,17 +219,17 @@ __global__ __launch_bounds__(256) void router_small_kernel(
 hipError_t launch_router_small(const void* x, bool bf16, const float* w_r, const float* logit_bias,
                                const float* sel_bias, int T, int E, int64_t d, int k, int score,
                                int32_t* topk, float* gate, float* scores, float* lse,
-                               hipStream_t st) {
+                               const float* gumbel_u, float tau, hipStream_t st) {
   constexpr int TPW = 8;
   const dim3 grid((unsigned)((T + 4 * TPW - 1) / (4 * TPW))), block(256);
   if (bf16)
     hipLaunchKernelGGL((router_small_kernel<bf16_t, 8, TPW>), grid, block, 0, st,
                        (const bf16_t*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
-                       scores, lse);
+                       scores, lse, gumbel_u, tau);
   else
     hipLaunchKernelGGL((router_small_kernel<float, 8, TPW>), grid, block, 0, st,
                        (const float*)x, w_r, logit_bias, sel_bias, T, E, d, k, score, topk, gate,
-                       scores, lse);
+                       scores, lse, gumbel_u, tau);
   return hipGetLastError();
 }
 
@@ -606,8 +615,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void router_dlogits_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ topk,
     const float* __restrict__ gate, const float* __restrict__ dgate, const float* __restrict__ y,
-    float aux_coef, const float* __restrict__ lse, float z_coef, int T, int E, int k, int score,
-    float* __restrict__ dl) {
+    float aux_coef, const float* __restrict__ lse, float z_coef, float inv_tau, int T, int E,
+    int k, int score, float* __restrict__ dl) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -648,23 +657,23 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
       else out[i] += c * y[e] * s[i] * (1.f - s[i]);
     }
     if (z_coef != 0.f) out[i] += zc * s[i];
-    dl[t * E + e] = out[i];
+    dl[t * E + e] = out[i] * inv_tau;
   }
 }
 
 hipError_t launch_router_dlogits(const float* scores, const int32_t* topk, const float* gate,
                                  const float* dgate, const float* y, float aux_coef,
-                                 const float* lse, float z_coef, int T, int E, int k, int score,
-                                 float* dl, hipStream_t st) {
+                                 const float* lse, float z_coef, float inv_tau, int T, int E, int k,
+                                 int score, float* dl, hipStream_t st) {
   dim3 grid((T + 3) / 4), block(256);
   if (E <= 64)
-    hipLaunchKernelGGL(router_dlogits_kernel<1>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<1>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, inv_tau, T, E, k, score, dl);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_dlogits_kernel<2>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<2>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, inv_tau, T, E, k, score, dl);
   else if (E <= 256)
-    hipLaunchKernelGGL(router_dlogits_kernel<4>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<4>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, inv_tau, T, E, k, score, dl);
   else
-    hipLaunchKernelGGL(router_dlogits_kernel<16>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, T, E, k, score, dl);
+    hipLaunchKernelGGL(router_dlogits_kernel<16>, grid, block, 0, st, scores, topk, gate, dgate, y, aux_coef, lse, z_coef, inv_tau, T, E, k, score, dl);
   return hipGetLastError();
 }
 

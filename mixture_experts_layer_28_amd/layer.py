@@ -24,13 +24,15 @@ class MoELayer:
 
     aux_coef weights the load-balance loss and z_coef the router z-loss in
     the router gradient; bias_gamma > 0 makes step() apply the aux-loss-free
-    bias update to sel_bias (in place) from this batch's expert loads.
+    bias update to sel_bias (in place) from this batch's expert loads;
+    gumbel_tau > 0 turns on the noisy gate, whose uniforms [T, E] fp32 the
+    caller passes to forward() (inp["gumbel_u"] for step()).
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
-                 bias_gamma: float = 0.0, device="cuda"):
-        self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity)
+                 bias_gamma: float = 0.0, gumbel_tau: float = 0.0, device="cuda"):
+        self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
         self.bias_gamma = bias_gamma
@@ -86,10 +88,11 @@ class MoELayer:
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------ stages
-    def forward(self, x, w_r, w13, w2, sw13=None, sw2=None, logit_bias=None, sel_bias=None):
+    def forward(self, x, w_r, w13, w2, sw13=None, sw2=None, logit_bias=None, sel_bias=None,
+                gumbel_u=None):
         D = self.desc
         route(D, x, w_r, logit_bias, sel_bias, self.topk_idx, self.gate, self.scores, self.lse,
-              self.ws)
+              self.ws, gumbel_u=gumbel_u)
         aux_stats(D, self.scores, self.topk_idx, self.lse, self.counts, self.y_frac, self.z_mean,
                   self.aux_out, self.ws)
         permute(D, x, self.topk_idx, self.offsets, self.row_of, self.token_of, self.n_dropped,
@@ -119,7 +122,8 @@ class MoELayer:
     def step(self, inp: dict):
         """Forward then backward over one batch; inp holds the device tensors."""
         self.forward(inp["x"], inp["w_r"], inp["w13"], inp["w2"], inp.get("sw13"),
-                     inp.get("sw2"), inp.get("logit_bias"), inp.get("sel_bias"))
+                     inp.get("sw2"), inp.get("logit_bias"), inp.get("sel_bias"),
+                     inp.get("gumbel_u"))
         self.backward(inp["dy"], inp["x"], inp["w_r"], inp["w13"], inp["w2"], inp.get("sw13"),
                       inp.get("sw2"))
         if self.bias_gamma and inp.get("sel_bias") is not None:

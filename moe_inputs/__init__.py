@@ -24,6 +24,13 @@ Workloads (the five layer shapes benchmarked and parity-tested):
                    with coefficient 0.01
   dsv3_bf16        T=8192 d=7168 E=256 k=8 sigmoid + selection bias, one shared
                    expert, SwiGLU f=2048
+Routing variants and the per-GPU shard:
+  mixtral_noisy_bf16  the Mixtral-like layer with the noisy (Gumbel) gate, tau 1,
+                      aux 0.01 and z-loss 1e-3 (uniforms drawn per token/expert)
+  top1_bf16           the Mixtral-like layer with top-1 routing
+  skewed_cf15_bf16    the skewed GELU layer with capacity factor 1.5
+  dsv3_ep8_shard_bf16 the DeepSeek-like layer's local share under 8-way expert
+                      parallelism: 32 experts, about 2048 rows each
 """
 from __future__ import annotations
 
@@ -75,6 +82,16 @@ WORKLOADS = {
                                  aux_coef=0.01, z_coef=1e-3),
     "dsv3_bf16": Workload("dsv3_bf16", T=8192, d=7168, E=256, k=8, f=2048, score="sigmoid",
                           n_shared=1, sel_bias=True, bias_gamma=1e-3),
+    # routing variants
+    "mixtral_noisy_bf16": Workload("mixtral_noisy_bf16", T=8192, d=4096, E=8, k=2, f=14336,
+                                   cf=1.25, gumbel_tau=1.0, aux_coef=0.01, z_coef=1e-3),
+    "top1_bf16": Workload("top1_bf16", T=8192, d=4096, E=8, k=1, f=14336, cf=1.25),
+    "skewed_cf15_bf16": Workload("skewed_cf15_bf16", T=4096, d=4096, E=8, k=2, f=16384,
+                                 act="gelu", cf=1.5, logit_bias={0: 2.0, 3: 2.0}),
+    # one GPU's share of the DeepSeek-like layer under 8-way expert parallelism:
+    # 32 local experts of about 2048 rows each
+    "dsv3_ep8_shard_bf16": Workload("dsv3_ep8_shard_bf16", T=8192, d=7168, E=32, k=8, f=2048,
+                                    score="sigmoid", n_shared=1, sel_bias=True),
 }
 
 

@@ -10,7 +10,11 @@ Tolerances:
   * float32 router outputs (scores, gates, lse, z, S, L_aux, L_z, updated
     selection bias): max|d| <= 1e-5 max|ref|;
   * fp32 layer: every float output max|d| <= 1e-5 max|ref|;
-  * bf16 layer: max|d| <= 2e-2 max|ref| and sum|d| / sum|ref| <= 5e-3.
+  * bf16 layer: max|d| <= 2e-2 max|ref| and sum|d| / sum|ref| <= 5e-3;
+  * router gradients (dlogits, dW_r) also get an absolute floor of
+    2e-6 max|dgate| (times the largest column sum of |x| for dW_r): with top-1
+    routing the exact gradient is identically zero and the GPU holds only
+    fp32 rounding of g (1 - g) dg.
 """
 from __future__ import annotations
 
@@ -52,7 +56,7 @@ def gpu_layer(w: Workload, g: dict):
     import mixture_experts_layer_28_amd as moe
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -63,9 +67,10 @@ def oracle_layer(w: Workload, g: dict):
     f = {n: as_f64(v, w.dtype) for n, v in g.items()}
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     fwd = O.layer_forward(f["x"], f["w_r"], f["w13"], f["w2"], w.k, w.score, w.act, cap,
-                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"])
+                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], f["gumbel_u"],
+                          w.gumbel_tau)
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
-                           w.aux_coef, f["sw13"], f["sw2"], w.z_coef)
+                           w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau)
     return fwd, bwd, f
 
 
@@ -82,7 +87,7 @@ class Report:
                          for n, kv in self.lines)
 
 
-def assert_close(name, got, ref, dtype, rep: Report, rel=None):
+def assert_close(name, got, ref, dtype, rep: Report, rel=None, atol=0.0):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -97,10 +102,12 @@ def assert_close(name, got, ref, dtype, rep: Report, rel=None):
             l1_rel=f"{l1:.2e}")
     if rel is not None or dtype == "fp32":
         r = rel if rel is not None else 1e-5
-        assert emax <= r * mx + 1e-30, f"{name}: max|d| {emax:.3e} > {r} * {mx:.3e}"
+        assert emax <= r * mx + atol + 1e-30, f"{name}: max|d| {emax:.3e} > {r} * {mx:.3e} + {atol:.1e}"
     else:
-        assert emax <= 2e-2 * mx + 1e-30, f"{name}: max|d| {emax:.3e} > 2e-2 * {mx:.3e}"
-        assert l1 <= 5e-3, f"{name}: mean relative error {l1:.3e} > 5e-3"
+        assert emax <= 2e-2 * mx + atol + 1e-30, \
+            f"{name}: max|d| {emax:.3e} > 2e-2 * {mx:.3e} + {atol:.1e}"
+        if atol == 0.0 or mx > 1e3 * atol:
+            assert l1 <= 5e-3, f"{name}: mean relative error {l1:.3e} > 5e-3"
 
 
 def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
@@ -206,14 +213,20 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
         assert_close("dX_shared", to_np(L.dx_shared), bwd["dx_shared"], dt, rep)
         assert_close("dSW13", to_np(L.dsw13), bwd["dsw13"], dt, rep)
         assert_close("dSW2", to_np(L.dsw2), bwd["dsw2"], dt, rep)
-    assert_close("dlogits", to_np(L.dlogits)[tok_ok], bwd["dlogits"][tok_ok], dt, rep)
+    # The router gradient can vanish identically (top-1: the one renormalised
+    # gate is constant 1), leaving only fp32 rounding of g (1 - g) dg on the
+    # GPU; an absolute floor scaled by the formula's inputs covers that case.
+    dl_floor = 2e-6 * float(np.abs(bwd["dgate"]).max(initial=0.0))
+    assert_close("dlogits", to_np(L.dlogits)[tok_ok], bwd["dlogits"][tok_ok], dt, rep,
+                 atol=dl_floor)
     # router weight gradient: against the oracle, and exactly dl^T x of the
     # GPU's own dl (a property of the definition that holds at any size)
     gdl = to_np(L.dlogits)
     assert_close("dW_r(own dl)", to_np(L.dw_r), gdl.T @ f["x"], dt, rep, rel=2e-5)
     assert_close("dx_router(own dl)", to_np(L.dx_router), gdl @ f["w_r"], dt, rep, rel=2e-5)
     if not bad_e:
-        assert_close("dW_r", to_np(L.dw_r), bwd["dw_r"], dt, rep)
+        assert_close("dW_r", to_np(L.dw_r), bwd["dw_r"], dt, rep,
+                     atol=dl_floor * float(np.abs(f["x"]).sum(axis=0).max(initial=0.0)))
     assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep)
     return len(flips)
 

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -66,15 +66,15 @@ def test_null_and_misaligned_pointers_rejected():
     d = _desc()
     ws = moe.workspace_size(d, moe.MOE_OP_ROUTE)
     # x NULL
-    s = L.moe_route(ctypes.byref(d), None, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, ws,
+    s = L.moe_route(ctypes.byref(d), None, FAKE, None, None, None, FAKE, FAKE, FAKE, None, FAKE, ws,
                     None)
     assert s == 1 and "x is NULL" in L.moe_last_error().decode()
     # misaligned gate
-    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE + 4, FAKE, None, FAKE, ws,
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE + 4, FAKE, None, FAKE, ws,
                     None)
     assert s == 1 and "aligned" in L.moe_last_error().decode()
     # workspace too small
-    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
                     None)
     assert s == 3
     # combine without row_of
@@ -86,13 +86,34 @@ def test_null_and_misaligned_pointers_rejected():
                               FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
     assert s == 1 and "sw13" in L.moe_last_error().decode()
     # misaligned lse
-    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE + 2, FAKE, ws,
+    s = L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE + 2, FAKE, ws,
                     None)
     assert s == 1 and "lse" in L.moe_last_error().decode()
     # bias update without a bias vector
     assert L.moe_bias_update(ctypes.byref(d), FAKE, 1e-3, None, None) == 1
     assert "bias" in L.moe_last_error().decode()
     assert L.moe_bias_update(ctypes.byref(d), FAKE, float("nan"), FAKE, None) == 1
+
+
+def test_noisy_gate_validation():
+    L = moe.lib()
+    ws = moe.workspace_size(_desc(), moe.MOE_OP_ROUTE)
+    route = lambda d, u: L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, u, FAKE, FAKE, FAKE,
+                                     None, FAKE, ws, None)
+    # temperature set but no draws
+    assert route(_desc(gumbel_tau=0.5), None) == 1 and "gumbel_u" in L.moe_last_error().decode()
+    # draws without a temperature
+    assert route(_desc(), FAKE) == 1 and "gumbel_tau" in L.moe_last_error().decode()
+    # misaligned draws
+    assert route(_desc(gumbel_tau=0.5), FAKE + 2) == 1
+    # negative or non-finite temperature, and sigmoid scoring, are refused at the descriptor
+    out = ctypes.c_size_t()
+    for bad, code in ((_desc(gumbel_tau=-1.0), 1), (_desc(gumbel_tau=float("inf")), 1),
+                      (_desc(gumbel_tau=1.0, score="sigmoid"), 2)):
+        assert L.moe_workspace_size(ctypes.byref(bad), 0, ctypes.byref(out)) == code
+    # a zero-token call with the noisy gate on is a no-op that touches nothing
+    assert L.moe_route(ctypes.byref(_desc(T=0, gumbel_tau=0.5)), FAKE, FAKE, None, None, FAKE,
+                       FAKE, FAKE, FAKE, None, None, 0, None) == 0
 
 
 def test_z_loss_needs_softmax_scoring_and_lse():
@@ -112,7 +133,7 @@ def test_z_loss_needs_softmax_scoring_and_lse():
 def test_zero_tokens_is_a_noop_without_touching_memory():
     L = moe.lib()
     d = _desc(T=0)
-    assert L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, None, 0,
                        None) == 0
     assert L.moe_aux_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                            None) == 0

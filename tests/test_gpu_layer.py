@@ -20,6 +20,11 @@ REDUCED = {
     "skewed_nocap_small": WORKLOADS["skewed_nocap_bf16"].replace(T=1024, d=512, f=1024),
     "finegrained_small": WORKLOADS["finegrained_bf16"].replace(T=2048, d=512, f=256),
     "dsv3_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256),
+    # the noisy (Gumbel) gate on the Mixtral-like structure, with aux and z-loss terms
+    "mixtral_noisy_small": WORKLOADS["mixtral_noisy_bf16"].replace(T=1536, d=512, f=768),
+    # top-1 routing and a 1.5 capacity factor on the skewed load
+    "top1_small": WORKLOADS["top1_bf16"].replace(T=1536, d=512, f=768),
+    "skewed_cf15_small": WORKLOADS["skewed_cf15_bf16"].replace(T=1024, d=512, f=1024),
 }
 
 EDGE = {
@@ -38,6 +43,9 @@ EDGE = {
     "single_expert": Workload("single", T=300, d=128, E=1, k=1, f=384),
     # E at the router's 1024-expert limit region and k at 16
     "wide_router": Workload("wide", T=256, d=64, E=320, k=16, f=64, aux_coef=0.02, z_coef=0.01),
+    # noisy gate through the GEMM-logits router (E > 8), fp32, low temperature
+    "noisy_fp32": Workload("noisy32", T=300, d=64, E=40, k=4, f=64, dtype="fp32", gumbel_tau=0.5,
+                           aux_coef=0.05, z_coef=0.02),
 }
 
 
