@@ -308,7 +308,7 @@ def combine_backward(dY, O, gates, row_of):
 
 # ---------------------------------------------------------- router backward
 def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux_coef=0.0,
-                    y=None, z_coef=0.0, logits=None, tau=None):
+                    y=None, z_coef=0.0, logits=None, tau=None, n_tokens=None):
     """Gradient of the router through the renormalised gates of [Recipe] §2.2
     (the top-k choice itself is piecewise constant), plus aux_coef times the
     gradient of L_aux = E sum_i y_i z_i with the counts y held fixed.
@@ -325,11 +325,15 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
     noisy logits (l + g) / tau; the chain rule to l divides them by tau.
     Returns dict(dlogits [T,E], dw_r [E,d] = dl^T x, dx_router [T,d] = dl W_r),
     dlogits being the gradient with respect to l.
+    n_tokens: the batch's token count in the 1/T factors of the aux and z-loss
+    terms when the rows given are a subset of the batch (default: all rows).
     """
     T, E = scores.shape
+    if n_tokens is not None:
+        T = n_tokens
     k = topk_idx.shape[1]
-    dl = np.zeros((T, E))
-    for t in range(T):
+    dl = np.zeros(scores.shape)
+    for t in range(scores.shape[0]):
         sel = topk_idx[t]
         g = gates[t]
         dg = dgate[t]
@@ -346,7 +350,7 @@ def router_backward(x, w_r, scores, topk_idx, gates, dgate, score="softmax", aux
         else:
             dl += aux_coef * (E / T) * y[None, :] * scores * (1.0 - scores)
     if z_coef != 0.0:
-        dl += z_coef * z_loss_grad(logits)
+        dl += z_coef * z_loss_grad(logits, T)
     if tau is not None:
         dl = dl / tau
     return dict(dlogits=dl, dw_r=dl.T @ x, dx_router=dl @ w_r)
@@ -379,8 +383,8 @@ def z_loss(logits):
     return float(np.mean(lse * lse))
 
 
-def z_loss_grad(logits):
-    T = logits.shape[0]
+def z_loss_grad(logits, n_tokens=None):
+    T = logits.shape[0] if n_tokens is None else n_tokens
     lse = router_logsumexp(logits)
     sm = np.exp(logits - lse[:, None])
     return (2.0 / T) * lse[:, None] * sm

@@ -539,3 +539,35 @@ def test_layer_gradient_with_noisy_gate_by_central_differences():
             lm, _ = loss(v2, g["w_r"]) if name == "x" else loss(g["x"], v2)
             num[i] = (lp - lm) / (2 * h)
         np.testing.assert_allclose(ana, num, rtol=1e-5, atol=1e-7, err_msg=name)
+
+
+def test_router_backward_on_a_token_subset():
+    """Rows of the router gradient are independent given the batch's y and T:
+    evaluating a subset with n_tokens = T reproduces those rows of the full
+    batch (aux and z-loss terms included)."""
+    w, g = _tiny(T=40, d=8, E=6, k=2, f=4, seed=3)
+    r = O.router_forward(g["x"], g["w_r"], w.k)
+    st = O.aux_stats(r["scores"], r["topk_idx"], w.E)
+    dgate = np.random.default_rng(4).standard_normal((w.T, w.k))
+    full = O.router_backward(g["x"], g["w_r"], r["scores"], r["topk_idx"], r["gates"], dgate,
+                             aux_coef=0.3, y=st["y"], z_coef=0.2, logits=r["logits"])
+    sub = np.array([1, 7, 22, 39])
+    part = O.router_backward(g["x"][sub], g["w_r"], r["scores"][sub], r["topk_idx"][sub],
+                             r["gates"][sub], dgate[sub], aux_coef=0.3, y=st["y"], z_coef=0.2,
+                             logits=r["logits"][sub], n_tokens=w.T)
+    np.testing.assert_allclose(part["dlogits"], full["dlogits"][sub], rtol=1e-13, atol=1e-15)
+
+
+def test_row_comparison_ignores_slot_order_only():
+    """The GPU-vs-oracle row comparison keys rows by (token, expert): a
+    swapped slot order with the same rows passes, a wrong row does not."""
+    import pytest
+    from parity_util import assert_rows_match
+    o_idx = np.array([[3, 1], [0, 2]])
+    o_row = np.array([[5, 1], [0, 3]])
+    g_idx = np.array([[1, 3], [0, 2]])
+    assert_rows_match(g_idx, np.array([[1, 5], [0, 3]]), o_idx, o_row)
+    with pytest.raises(AssertionError):
+        assert_rows_match(g_idx, np.array([[5, 1], [0, 3]]), o_idx, o_row)
+    with pytest.raises(AssertionError):
+        assert_rows_match(np.array([[1, 4], [0, 2]]), np.array([[1, 5], [0, 3]]), o_idx, o_row)
