@@ -162,6 +162,90 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     print(json.dumps(out, indent=1))
 
 
+def gpu_clock_info():
+    """GPU clocks and power limit as the vendor tool reports them (best effort;
+    None where the tool is absent or refuses)."""
+    import subprocess
+    out = {}
+    for key, cmd in (("metric", ["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"]),
+                     ("limit", ["amd-smi", "static", "-g", "0", "--limit", "--json"])):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            txt = r.stdout.strip()
+            try:
+                out[key] = json.loads(txt)
+            except ValueError:
+                out[key] = txt[-2000:] or None
+        except (OSError, subprocess.SubprocessError):
+            out[key] = None
+    return out
+
+
+def stage_detail(layer, inp, moe, w, A, iters=20):
+    """Median time of each streaming stage as one C-ABI call, with and without a
+    512 MiB write before every timed call (that write evicts the 256 MB MALL, so
+    the flushed figure reads its inputs from HBM), and a per-expert loop of
+    torch's own GEMM (hipBLASLt) on the two forward shapes, as context."""
+    import torch
+    import torch.nn.functional as F
+    D = layer.desc
+    x, dy = inp["x"], inp["dy"]
+    calls = {
+        "permute": lambda: moe.permute(D, x, layer.topk_idx, layer.offsets, layer.row_of,
+                                       layer.token_of, layer.n_dropped, layer.x_perm, layer.ws),
+        "combine": lambda: moe.combine(D, layer.out, layer.out_shared, layer.gate, layer.row_of,
+                                       layer.Y),
+        "combine_bwd": lambda: moe.combine_bwd(D, dy, layer.out, layer.gate, layer.row_of,
+                                               layer.dgate, layer.dout),
+        "unpermute": lambda: moe.permute_bwd(D, layer.dx_perm, layer.row_of, layer.dx_shared,
+                                             layer.dx_router, layer.dX),
+    }
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def median_ms(fn, flushed):
+        ts = []
+        for i in range(iters + 2):
+            if flushed:
+                flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    hb = hbm_bytes(w, A)
+    out = {}
+    for name, fn in calls.items():
+        r = {}
+        for tag, fl in (("unflushed", False), ("flushed", True)):
+            ms = median_ms(fn, fl)
+            gbs = hb[name] / (ms / 1e3) / 1e9
+            r[tag] = {"median_ms": round(ms, 4), "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)}
+        out[name] = r
+    # context only: torch's GEMM per expert, same operands as the forward launches
+    off = layer.offsets.cpu().tolist()
+    w13, w2 = inp["w13"], inp["w2"]
+    H = layer.save_h
+    up = lambda: [F.linear(layer.x_perm[off[e]:off[e + 1]], w13[e]) for e in range(w.E)]
+    down = lambda: [F.linear(H[off[e]:off[e + 1]], w2[e]) for e in range(w.E)]
+    fl = gemm_flops(w, A)
+    cmp_ = {}
+    for name, fn in (("gemm_fwd_up", up), ("gemm_fwd_down", down)):
+        ms = median_ms(fn, False)
+        cmp_[name] = {"median_ms": round(ms, 4), "TFLOP/s": round(fl[name] / (ms / 1e3) / 1e12, 1),
+                      "note": "torch.nn.functional.linear per expert (hipBLASLt), no fused "
+                              "epilogue; context, not part of the library"}
+    del flush
+    return {"iters": iters, "stages": out, "torch_gemm_per_expert": cmp_,
+            "gpu_clocks": gpu_clock_info()}
+
+
 def cpu_baseline(w, g, tokens):
     """The oracle, as it stands, on the first `tokens` tokens of the workload
     (same weights; capacity recomputed for the sample)."""
@@ -197,6 +281,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events (roofline object omitted)")
+    ap.add_argument("--stage-detail", action="store_true",
+                    help="also time each streaming stage alone, MALL-flushed and not, "
+                         "torch's per-expert GEMM as context, and record GPU clocks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -291,6 +378,12 @@ def main():
                 stages[name]["TFLOP/s"] = round(tf, 1)
     gemm_tflops = gemm_flops_step * args.steps / (gemm_tot_ms / 1e3) / 1e12 if gemm_tot_ms else None
 
+    detail = None
+    if args.stage_detail:
+        log("[bench] stage detail (flushed / unflushed, torch GEMM context, clocks)")
+        detail = stage_detail(layer, inp, moe, w, A)
+        log("[bench] stage detail done")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")
@@ -311,6 +404,8 @@ def main():
         "cpu_baseline": cpu,
         "stages": stages,
     }
+    if detail is not None:
+        out["stage_detail"] = detail
     print(json.dumps(out), flush=True)
 
 
