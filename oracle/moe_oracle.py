@@ -205,6 +205,112 @@ def expert_forward(X, w13, w2, act):
     return H @ w2.T, saved
 
 
+# ------------------------------------------------------------- FP8 forward
+# [Recipe] §8.1 and §9.1 list FP8 forward GEMMs with bf16 activations; §6.2
+# stores experts in FP8 and widens them for use. The pages fix neither the
+# FP8 format nor the scale granularity. Reading taken: OCP E4M3 codes, one
+# power-of-two scale per row of each K-contiguous operand (a token row of the
+# GEMM input, an output channel of the weight), chosen as the smallest power
+# of two that brings the row's largest magnitude within E4M3's range.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Value of OCP E4M3 codes: sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN;
+    there are no infinities, so the largest finite magnitude is 1.75 * 2^8."""
+    c = np.asarray(codes).astype(np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sgn * mag
+
+
+def e4m3_encode(v):
+    """Nearest E4M3 code to each value (|v| <= 448), ties to the even
+    mantissa. The quantum is 2^(floor(log2|v|) - 3) in the normal range and
+    2^-9 below 2^-6; |v| / quantum is exact in float64, so rounding it to the
+    nearest integer (half to even) is the whole rounding step."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode: input outside the finite range")
+    _, ex = np.frexp(a)                   # a = mant * 2^ex, mant in [0.5, 1)
+    e = np.maximum(ex - 1, -6)            # binade exponent, subnormals share -6
+    q = np.exp2(e - 3.0)
+    n = np.rint(a / q)                    # round half to even
+    r = n * q                             # rounded magnitude (may reach 2^(e+1))
+    _, ex2 = np.frexp(r)
+    e2 = ex2 - 1
+    normal = r >= 2.0 ** -6
+    field = np.where(normal, e2 + 7, 0)
+    mant = np.where(normal, r / np.exp2(e2) * 8.0 - 8.0, r / 2.0 ** -9)
+    code = (field << 3) | mant.astype(np.int64)
+    code = np.where(r == 0, 0, code)
+    # sign-magnitude: the sign survives rounding to zero (-tiny -> 0x80)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_row_scale_exp(amax):
+    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero row).
+    With amax = m * 2^e0, m in [1, 2), and 448 = 1.75 * 2^8, that is e0 - 8
+    when m <= 1.75 and e0 - 7 otherwise: exact, no division by 448."""
+    amax = np.asarray(amax, dtype=np.float64)
+    mant, ex = np.frexp(amax)             # amax = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(2.0 * mant <= 1.75, ex - 9, ex - 8)
+    return np.where(amax == 0, 0, e).astype(np.int64)
+
+
+def quantize_rows_fp8(X):
+    """Per-row FP8 quantization: codes [n, K] uint8 and scale exponents [n]
+    with X[i] ~= e4m3_decode(codes[i]) * 2^e[i]. Scaling by a power of two is
+    exact, so the only rounding is e4m3_encode's."""
+    X = np.asarray(X, dtype=np.float64)
+    e = fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0))
+    codes = e4m3_encode(X * np.exp2(-e.astype(np.float64))[:, None])
+    return codes, e
+
+
+def dequantize_rows_fp8(codes, e):
+    return e4m3_decode(codes) * np.exp2(np.asarray(e, dtype=np.float64))[:, None]
+
+
+def round_bf16(v):
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    q = np.exp2(np.maximum(ex - 1, -126) - 7.0)
+    return np.sign(v) * np.rint(a / q) * q
+
+
+def expert_forward_fp8(X, w13, w2, act):
+    """expert_forward with both GEMMs on FP8 operands: X and w13 quantized per
+    row, the up-projection taken exactly on their dequantized values; the
+    activation H is kept in bf16 (the stored activation), and that bf16 H and
+    w2 are quantized per row for the down-projection. The saved values for
+    the backward are the pre-activations and H as computed here."""
+    f = w2.shape[1]
+    Xd = dequantize_rows_fp8(*quantize_rows_fp8(X))
+    Wd = dequantize_rows_fp8(*quantize_rows_fp8(w13))
+    pre = Xd @ Wd.T
+    if act == "swiglu":
+        a, b = pre[:, :f], pre[:, f:]
+        H = silu(a) * b
+        saved = dict(a=a, b=b, H=H)
+    elif act == "gelu":
+        a = pre
+        H = gelu(a)
+        saved = dict(a=a, H=H)
+    else:
+        raise ValueError(act)
+    Hd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(H)))
+    W2d = dequantize_rows_fp8(*quantize_rows_fp8(w2))
+    return Hd @ W2d.T, saved
+
+
 def expert_backward(X, w13, w2, saved, dO, act):
     """Backward of expert_forward for upstream dO [n, d].
     Returns (dX [n,d], dw13 (w13's shape), dw2 [d,f], dpre (gradient of the
@@ -225,11 +331,13 @@ def expert_backward(X, w13, w2, saved, dO, act):
     return dX, dw13, dw2, dpre
 
 
-def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None):
+def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None, fp8=False):
     """Grouped GEMM of [Recipe] §4.2: the same result as running every
     expert's GEMMs on its own contiguous rows. Optional shared experts
     ([Recipe] §2.3 / §9.1: an expert every token passes through) read all of
-    x. Returns (O [A,d], Os [T,d] or None, saved)."""
+    x. Returns (O [A,d], Os [T,d] or None, saved). fp8=True runs every
+    expert (shared ones included) through expert_forward_fp8."""
+    fwd = expert_forward_fp8 if fp8 else expert_forward
     E = w13.shape[0]
     A = int(offsets[E])
     d = w2.shape[1]
@@ -237,14 +345,14 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
     saved = []
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        o, s = expert_forward(x_perm[lo:hi], w13[e], w2[e], act)
+        o, s = fwd(x_perm[lo:hi], w13[e], w2[e], act)
         O[lo:hi] = o
         saved.append(s)
     Os, ssaved = None, []
     if sw13 is not None:
         Os = np.zeros((x.shape[0], d))
         for s in range(sw13.shape[0]):
-            o, sv = expert_forward(x, sw13[s], sw2[s], act)
+            o, sv = fwd(x, sw13[s], sw2[s], act)
             Os += o
             ssaved.append(sv)
     return O, Os, dict(routed=saved, shared=ssaved)
@@ -408,7 +516,8 @@ def permute_backward(dx_perm, row_of, dx_shared=None, dx_router=None):
 
 # ------------------------------------------------------------- whole layer
 def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
-                  logit_bias=None, sel_bias=None, sw13=None, sw2=None, gumbel_u=None, tau=None):
+                  logit_bias=None, sel_bias=None, sw13=None, sw2=None, gumbel_u=None, tau=None,
+                  fp8=False):
     """Forward of the layer: router, stats, permute, grouped FFN, combine.
     All arrays float64 (exact values of the fp32/bf16 inputs)."""
     E = w13.shape[0]
@@ -416,7 +525,7 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
     st = aux_stats(r["scores"], r["topk_idx"], E)
     p = permute(r["topk_idx"], E, cap)
     x_perm = x[p["token_of"]]
-    O, Os, saved = grouped_ffn_forward(x_perm, p["offsets"], w13, w2, act, x, sw13, sw2)
+    O, Os, saved = grouped_ffn_forward(x_perm, p["offsets"], w13, w2, act, x, sw13, sw2, fp8)
     Y = combine(O, r["gates"], p["row_of"], Os)
     return dict(router=r, stats=st, perm=p, x_perm=x_perm, O=O, Os=Os, saved=saved, Y=Y)
 

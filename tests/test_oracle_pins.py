@@ -571,3 +571,113 @@ def test_row_comparison_ignores_slot_order_only():
         assert_rows_match(g_idx, np.array([[5, 1], [0, 3]]), o_idx, o_row)
     with pytest.raises(AssertionError):
         assert_rows_match(np.array([[1, 4], [0, 2]]), np.array([[1, 5], [0, 3]]), o_idx, o_row)
+
+
+# ------------------------------------------------------------------ FP8 forward
+def _torch_e4m3_codes(v):
+    import torch
+    return torch.from_numpy(np.asarray(v, dtype=np.float64)).to(torch.float32) \
+        .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_library_on_every_code():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    assert (np.isnan(ref) == np.isnan(got)).all()
+    fin = ~np.isnan(ref)
+    assert (ref[fin] == got[fin]).all()
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9 and got[0x7F] != got[0x7F]
+
+
+def test_e4m3_encode_matches_library_rounding():
+    """Every finite bf16 value within +-448, random fp32 values, and exact
+    ties, against torch's float32 -> float8_e4m3fn cast (round to nearest even)."""
+    u = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    u = u[np.isfinite(u)].astype(np.float64)
+    u = u[np.abs(u) <= 448]
+    rng = np.random.default_rng(5)
+    r = (rng.standard_normal(20000) * np.exp2(rng.integers(-12, 8, 20000))).astype(np.float32)
+    r = r[np.abs(r) <= 448].astype(np.float64)
+    for v in (u, r):
+        assert (O.e4m3_encode(v) == _torch_e4m3_codes(v)).all()
+    # hand ties: halfway values go to the even mantissa
+    assert O.e4m3_encode([1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, 240.0])[:].tolist() == \
+        [0x38, 0x3A, 0x02, 0x00, 0x77]
+    assert O.e4m3_encode([-2.0 ** -11])[0] == 0x80      # sign kept on rounding to zero
+
+
+def test_fp8_row_scale_is_the_smallest_power_of_two():
+    amax = np.array([448.0, 449.0, 224.0, 224.5, 1.0, 1.75, 1.76, 0.0, 3e-5, 6e4])
+    got = O.fp8_row_scale_exp(amax)
+    for a, e in zip(amax, got):
+        if a == 0:
+            assert e == 0
+            continue
+        want = next(x for x in range(-60, 60) if a <= 448.0 * 2.0 ** x)   # brute force
+        assert e == want, (a, e, want)
+
+
+def test_quantize_rows_error_and_range():
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((40, 96)) * np.exp2(rng.integers(-20, 20, 40))[:, None]
+    X = O.round_bf16(X)
+    q, e = O.quantize_rows_fp8(X)
+    D = O.dequantize_rows_fp8(q, e)
+    scaled = np.abs(D) * np.exp2(-e.astype(float))[:, None]
+    assert (scaled.max(axis=1) <= 448).all() and (scaled.max(axis=1) > 224 * 0.9).all()
+    s = np.exp2(e.astype(float))[:, None]
+    normal = np.abs(X) >= 2.0 ** -6 * s
+    err = np.abs(D - X)
+    assert (err[normal] <= 2.0 ** -4 * np.abs(X[normal]) * (1 + 1e-12)).all()
+    assert (err[~normal] <= (2.0 ** -10 * s + 0 * X)[~normal]).all()
+
+
+def test_round_bf16_matches_library():
+    import torch
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(50000) * np.exp2(rng.integers(-30, 30, 50000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert (O.round_bf16(v.astype(np.float64)) == ref).all()
+
+
+def _brute_fp8_rows(M):
+    """Dequantized per-row FP8 by brute force: scale exponent by search, codes
+    by torch's own cast."""
+    out = np.zeros_like(M)
+    for i, row in enumerate(M):
+        a = np.abs(row).max()
+        e = 0 if a == 0 else next(x for x in range(-60, 60) if a <= 448.0 * 2.0 ** x)
+        codes = _torch_e4m3_codes(row / 2.0 ** e)
+        out[i] = O.e4m3_decode(codes) * 2.0 ** e
+    return out
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_expert_forward_fp8_brute_force(act):
+    """The FP8 expert forward against explicit loops over brute-force
+    quantized operands (scale search + library E4M3 cast)."""
+    rng = np.random.default_rng(8)
+    n, d, f = 5, 64, 32
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    P = 2 * f if act == "swiglu" else f
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 8)
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 6)
+    Xd, Wd, W2d = _brute_fp8_rows(X), _brute_fp8_rows(w13), _brute_fp8_rows(w2)
+    pre = np.array([[sum(Xd[t, c] * Wd[j, c] for c in range(d)) for j in range(P)]
+                    for t in range(n)])
+    if act == "swiglu":
+        a, b = pre[:, :f], pre[:, f:]
+        H = a / (1 + np.exp(-a)) * b
+    else:
+        H = O.gelu(pre)
+    Hd = _brute_fp8_rows(O.round_bf16(H))
+    Oref = np.array([[sum(Hd[t, c] * W2d[j, c] for c in range(f)) for j in range(d)]
+                     for t in range(n)])
+    got, sv = O.expert_forward_fp8(X, w13, w2, act)
+    np.testing.assert_allclose(sv["a"], pre[:, :f] if act == "swiglu" else pre, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, Oref, rtol=1e-12, atol=1e-12)
+    # and it stays near the exact forward (quantization error only)
+    exact, _ = O.expert_forward(X, w13, w2, act)
+    assert np.abs(got - exact).max() < 0.15 * np.abs(exact).max()
