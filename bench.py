@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 from moe_inputs import WORKLOADS, as_f64, gen_all  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM % bf16 MFMA peak"
@@ -262,7 +263,8 @@ def cpu_baseline(w, g, tokens):
     cap = O.capacity(ws.T, ws.k, ws.E, ws.cf)
     t0 = time.perf_counter()
     fwd = O.layer_forward(x, f["w_r"], f["w13"], f["w2"], ws.k, ws.score, ws.act, cap,
-                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau)
+                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau,
+                          fp8=ws.fp8)
     O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act, ws.aux_coef,
                      f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau)
     dt = time.perf_counter() - t0
@@ -324,7 +326,7 @@ def main():
         del src, dst
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()
@@ -360,12 +362,16 @@ def main():
         tot, dom, n = max(gk)
         avg_s = tot / n / 1e3
         achieved = flops[dom] / avg_s / 1e12
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        fp8_kernel = w.fp8 and "fwd" in dom
+        peak = (PEAK_FP8_TFLOPS if fp8_kernel else PEAK_BF16_TFLOPS) if w.dtype == "bf16" \
+            else PEAK_F32_TFLOPS
         roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": dom,
                     "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4),
                     "traffic": traffic_for(dom, w.name),
                     "flops_per_launch": flops[dom], "avg_ms": round(tot / n, 4)}
+        if fp8_kernel:
+            roofline["operand_dtype"] = "fp8-e4m3"
         hb = hbm_bytes(w, A)
         for name, b in hb.items():
             if name in stages:
@@ -377,6 +383,14 @@ def main():
                 tf = flops[name] / (stages[name]["avg_ms"] / 1e3) / 1e12
                 stages[name]["TFLOP/s"] = round(tf, 1)
     gemm_tflops = gemm_flops_step * args.steps / (gemm_tot_ms / 1e3) / 1e12 if gemm_tot_ms else None
+    # share of the matrix peak: time the GEMMs would take at their operand
+    # dtype's peak (fp8 forward GEMMs at the fp8 peak) over the time they took
+    mfma_frac = None
+    if gemm_tot_ms and w.dtype == "bf16":
+        ideal_s = sum(flops[name] * n / ((PEAK_FP8_TFLOPS if w.fp8 and "fwd" in name
+                                          else PEAK_BF16_TFLOPS) * 1e12)
+                      for name, tot, n in prof if name in flops)
+        mfma_frac = ideal_s / (gemm_tot_ms / 1e3)
 
     detail = None
     if args.stage_detail:
@@ -394,12 +408,14 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "dtype": ("fp8-e4m3 fwd GEMMs, bf16 bwd" if w.fp8 else "bf16") if w.dtype == "bf16"
+                 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "act": w.act, "score": w.score, "n_shared": w.n_shared,
-                   "capacity": cap, "kept_rows": A, "parallelism": "none (1 GPU)"},
+                   "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8,
+                   "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
-        "gemm_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4) if gemm_tflops and w.dtype == "bf16" else None,
+        "gemm_mfma_frac": round(mfma_frac, 4) if mfma_frac else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -88,7 +88,8 @@ typedef enum {
   MOE_OP_PERMUTE = 2,
   MOE_OP_FFN_FWD = 3,
   MOE_OP_FFN_BWD = 4,
-  MOE_OP_ROUTE_BWD = 5
+  MOE_OP_ROUTE_BWD = 5,
+  MOE_OP_FFN_FWD_FP8 = 6
 } moe_op;
 
 /* ---------------------------------------------------------------- router
@@ -183,6 +184,55 @@ int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t*
                         const void* sw2, void* save_pre, void* save_h, void* save_pre_s,
                         void* save_h_s, void* out, void* out_shared, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* ------------------------------------------------------------ FP8 forward
+ * [Recipe] §8.1 and §9.1 run the forward GEMMs in FP8 with bf16 activations;
+ * §6.2 keeps experts in FP8 storage and widens them for use. Format and
+ * granularity are not given there; this library uses OCP E4M3 codes with one
+ * power-of-two scale per row of each K-contiguous operand.
+ *
+ * moe_quantize_fp8: row i of a bf16 matrix ->
+ *   codes[i][k] = E4M3 nearest (ties to even) of src[i][k] * 2^-scale_exp[i],
+ *   scale_exp[i] = smallest integer e with max_k |src[i][k]| <= 448 * 2^e
+ *   (0 for an all-zero row), so src[i][k] ~= e4m3(codes[i][k]) * 2^scale_exp[i].
+ * The scaling is exact; the codes are a bit-exact function of the input.
+ * Inputs must be finite. No desc: a plain matrix operation.
+ *   src        [rows, K] bf16, row stride ld_src elements (multiple of 8)   in
+ *   valid_rows device int32 or NULL: rows >= *valid_rows are left untouched
+ *              (e.g. offsets + E, the routed row count)                     in
+ *   codes      [rows, K] uint8, row stride ld_codes bytes (multiple of 16)  out
+ *   scale_exp  [rows] int32                                                 out
+ * K must be a positive multiple of 16; rows < 2^31.
+ */
+int moe_quantize_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                     const int32_t* valid_rows, void* codes, int64_t ld_codes, int32_t* scale_exp,
+                     void* stream);
+
+/* moe_grouped_ffn_fwd_fp8: moe_grouped_ffn_fwd with both GEMMs on FP8
+ * operands (moe_quantize_fp8 codes and exponents). The up-projection takes
+ * the quantized rows of x_perm and of w13 (one exponent per weight row), the
+ * pre-activations and H are written in bf16 as in moe_grouped_ffn_fwd (the
+ * backward runs on them, in bf16, against the bf16 weights); the bf16 H is
+ * then quantized per row into the workspace and the down-projection takes it
+ * with the quantized rows of w2. Each output element is
+ * 2^(e_row + e_weight_row) * sum_k e4m3 * e4m3, accumulated in float32.
+ * desc->dtype must be MOE_BF16; d and f multiples of 16.
+ *   xq_perm [T*k, d] uint8, sx_perm [T*k] int32 (rows below offsets[E])   in
+ *   xq [T, d] uint8, sx [T] int32: quantized x for the shared expert       in (or NULL)
+ *   w13q [E, P, d] uint8, s13 [E, P] int32 (P = 2f SwiGLU, f GELU)         in
+ *   w2q [E, d, f] uint8, s2 [E, d] int32                                   in
+ *   sw13q, ss13, sw2q, ss2: the shared expert's, or NULL                   in
+ *   save_pre, save_h, save_pre_s, save_h_s, out, out_shared: as in
+ *     moe_grouped_ffn_fwd (bf16)                                           out
+ *   ws         MOE_OP_FFN_FWD_FP8 bytes (H codes and exponents)            scratch
+ */
+int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int32_t* sx_perm,
+                            const int32_t* offsets, const void* xq, const int32_t* sx,
+                            const void* w13q, const int32_t* s13, const void* w2q,
+                            const int32_t* s2, const void* sw13q, const int32_t* ss13,
+                            const void* sw2q, const int32_t* ss2, void* save_pre, void* save_h,
+                            void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* moe_grouped_ffn_bwd: backward of moe_grouped_ffn_fwd ([VPP]: each device
  * runs forward and backward of its local experts between the exchanges).

@@ -16,19 +16,19 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
- MOE_OP_ROUTE_BWD) = range(6)
+ MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8) = range(7)
 
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route", "moe_aux_stats", "moe_bias_update", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
-    "moe_profile_enable", "moe_profile_read",
+    "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
 )
 
 
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
             "moe_bias_update": [DP, _P, ctypes.c_float, _P, _P],
             "moe_permute": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
             "moe_grouped_ffn_fwd": [DP] + [_P] * 14 + [ctypes.c_size_t, _P],
+            "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                 ctypes.c_int64, _P, _P],
+            "moe_grouped_ffn_fwd_fp8": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
             "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
@@ -198,6 +201,30 @@ def grouped_ffn_fwd(desc, x_perm, offsets, x, w13, w2, sw13, sw2, save_pre, save
     _check("moe_grouped_ffn_fwd", lib().moe_grouped_ffn_fwd(
         ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13), _p(w2), _p(sw13), _p(sw2),
         _p(save_pre), _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
+        _stream(stream)))
+
+
+def quantize_fp8(src, codes, scale_exp, valid_rows=None, stream=None):
+    """Per-row E4M3 quantization of a bf16 tensor [..., K] into codes (uint8,
+    same shape) and scale exponents (int32, shape [...]); valid_rows: optional
+    one-element int32 device tensor bounding the rows quantized."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    if codes.shape != src.shape or scale_exp.numel() != rows:
+        raise ValueError("codes must match src's shape and scale_exp hold one entry per row")
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(src), rows, K, K, _p(valid_rows),
+                                                      _p(codes), K, _p(scale_exp),
+                                                      _stream(stream)))
+
+
+def grouped_ffn_fwd_fp8(desc, xq_perm, sx_perm, offsets, xq, sx, w13q, s13, w2q, s2, sw13q, ss13,
+                        sw2q, ss2, save_pre, save_h, save_pre_s, save_h_s, out, out_shared,
+                        ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_grouped_ffn_fwd_fp8", lib().moe_grouped_ffn_fwd_fp8(
+        ctypes.byref(desc), _p(xq_perm), _p(sx_perm), _p(offsets), _p(xq), _p(sx), _p(w13q),
+        _p(s13), _p(w2q), _p(s2), _p(sw13q), _p(ss13), _p(sw2q), _p(ss2), _p(save_pre),
+        _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
         _stream(stream)))
 
 

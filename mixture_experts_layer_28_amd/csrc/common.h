@@ -133,6 +133,11 @@ struct GemmArgs {
   const float* col_bias;    // EPI_STORE: added per output column, or null
   int64_t max_rows;         // RAG_M: upper bound of sum of M_g (grid sizing)
   int k_splits;             // split-K partitions (fp32 GEMM, RAG_NONE only); 1 = none
+  // FP8 GEMM: power-of-two scale exponents, per A row (indexed like A's rows)
+  // and per weight row (group g at b_sexp + g * b_sexp_gstride)
+  const int32_t* a_sexp;
+  const int32_t* b_sexp;
+  int64_t b_sexp_gstride;
 };
 
 }  // namespace moe

@@ -33,35 +33,17 @@
 namespace moe {
 
 constexpr int kBK = 32;                   // k per stage
-constexpr uint32_t kOOB = 0x80000000u;    // byte offset beyond any buffer extent
 constexpr int kRows = 256;                // tile rows of either operand
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// byte offset of chunk c (0..3) of row r in a K-contiguous [rows][32] tile
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 // byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [32][kRows] tile
 __device__ __forceinline__ int ks_off(int k, int s) {
   return k * (kRows * 2) + ((s ^ ((k & 3) << 1)) << 4);
 }
 
-// raw buffer resource over [base, base + bytes)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (int32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
-// weight row of fused tile row j (gate rows then up rows per wave column); -1 when beyond f
-__device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t fdim) {
-  const int wc = j / WN, w = j - wc * WN, half = WN >> 1;
-  const bool up = w >= half;
-  const int64_t col = n0h + wc * half + (up ? w - half : w);
-  if (col >= fdim) return -1;
-  return up ? fdim + col : col;
-}
 
 // Per-lane DMA source of one operand tile. A wave issues kRows/64 = 4
 // instructions per stage; instruction i fills block blk = wave*4 + i (1 KiB).
@@ -106,13 +88,6 @@ __device__ __forceinline__ void dma_src(DmaSrc& d, int64_t ld, int64_t rows_vali
   }
 }
 
-// four floats -> four bf16 (round to nearest even) in one 8-byte store
-__device__ __forceinline__ void store4_bf16(bf16_t* dst, const float* v) {
-  uint2 w;
-  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  *reinterpret_cast<uint2*>(dst) = w;
-}
 __device__ __forceinline__ void unpack4_bf16(uint2 w, float* v) {
   v[0] = bf2f(w.x & 0xffffu);
   v[1] = bf2f(w.x >> 16);
@@ -120,8 +95,6 @@ __device__ __forceinline__ void unpack4_bf16(uint2 w, float* v) {
   v[3] = bf2f(w.y >> 16);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
   const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

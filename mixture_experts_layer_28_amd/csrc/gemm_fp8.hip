@@ -1,0 +1,316 @@
+// Grouped GEMM on FP8 (OCP E4M3) operands on the gfx950 matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation), for the forward of the
+// expert FFN. Both operands are K-contiguous byte matrices with one
+// power-of-two scale per row (2^a_sexp[m] for the input rows, 2^b_sexp[n]
+// for the weight rows); the epilogue applies them exactly with ldexp, so
+//   C[m][n] = 2^(a_sexp[m] + b_sexp[n]) * sum_k e4m3(A[m][k]) e4m3(B[n][k]).
+//
+// Workgroup: 256 threads = 4 waves in a 2x2 grid; tile 256 x 256; each wave
+// owns 128 x 128 as 4 x 4 MFMA blocks of 32 x 32 held in AGPRs.
+//
+// A stage holds 64 k of both tiles: 2 x 256 rows x 64 bytes = 32 KiB, the
+// same bytes per row as the bf16 GEMM's 32-k stage, so the same swizzled
+// layout and DMA pattern serve (16-byte chunk c of a row = k 16c .. 16c+15).
+// One MFMA consumes a whole stage's k for its block. The matrix core takes
+// from lane l (row l & 31, half h = l >> 5) 32 bytes: k 16h .. 16h+15 in its
+// first 16 bytes and k 32+16h .. 32+16h+15 in the next 16 (measured on
+// gfx950), so a fragment is chunks h and 2+h of its row, the same two
+// conflict-free chunk patterns the bf16 fragments use.
+//
+// Four stages, one barrier per k-step. Entering k-step kt the fragments of
+// stage kt are already in registers (read during k-step kt-1), so after the
+// barrier stage kt is free: its refill with k-step kt+4 is issued during
+// k-step kt, one DMA instruction after every second MFMA, while the
+// fragments of stage kt+1 are read into the other register set.
+#include "gemm_tile.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBK8 = 64;                  // k per stage (bytes per tile row)
+constexpr int kRows8 = 256;               // tile rows of either operand
+
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
+struct Dma8 {
+  uint32_t off[4];
+  int kk[4];
+};
+
+// Per-lane DMA source: instruction i of a wave fills 1 KiB block
+// blk = wave*4 + i = rows blk*16 .. +15; lane l -> row blk*16 + (l >> 2),
+// logical chunk (l & 3) ^ ((l >> 4) & 3) (the kc_off swizzle).
+template <bool FUSED, int WN>
+__device__ __forceinline__ void dma_src8(Dma8& d, int64_t ld, int64_t rows_valid, int64_t r0,
+                                         int64_t fdim, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    int64_t grow;
+    bool ok;
+    if (FUSED) {
+      grow = fused_row(r, WN, r0, fdim);
+      ok = grow >= 0;
+    } else {
+      grow = r0 + r;
+      ok = grow < rows_valid;
+    }
+    d.off[i] = ok ? (uint32_t)(grow * ld + c * 16) : kOOB;
+    d.kk[i] = c * 16;
+  }
+}
+
+__device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
+  v8i32 v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+template <int EPI, int RAG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(GemmArgs p) {
+  constexpr int BM = kRows8, BN = kRows8;
+  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
+  constexpr bool FUSED = EPI == EPI_SWIGLU_FWD;
+  constexpr int BNo = FUSED ? BN / 2 : BN;
+  constexpr int A_B = BM * kBK8, B_B = BN * kBK8;   // bytes per stage of each tile
+  constexpr int ST = A_B + B_B;
+  constexpr int NLD = 8;                            // DMA instructions per wave per stage
+  static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
+  __shared__ __attribute__((aligned(1024))) char st0[ST];
+  __shared__ __attribute__((aligned(1024))) char st1[ST];
+  __shared__ __attribute__((aligned(1024))) char st2[ST];
+  __shared__ __attribute__((aligned(1024))) char st3[ST];
+
+  Tile t;
+  {
+    int* s_tiles = reinterpret_cast<int*>(st3);
+    const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
+    __syncthreads();
+    if (!have) return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const uint8_t* Ab = operand_base<uint8_t>(p.a, t);
+  const uint8_t* Bb = operand_base<uint8_t>(p.b, t);
+  const int64_t b_rows = FUSED ? 2 * p.fdim : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, t.M * p.a.ld);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, b_rows * p.b.ld);
+  Dma8 da, db;
+  dma_src8<false, WN>(da, p.a.ld, t.M, t.m0, p.fdim, wave, lane);
+  dma_src8<FUSED, WN>(db, p.b.ld, FUSED ? p.fdim : p.N, t.n0, p.fdim, wave, lane);
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = (t.K + kBK8 - 1) / kBK8;
+
+  // DMA instruction q (0..7: A blocks then B blocks) of k-step kt into stage s
+  auto dma = [&](int64_t kt, char* s, int q) __attribute__((always_inline)) {
+    const int64_t k0 = kt * kBK8;
+    const bool isA = q < 4;
+    const int i = q & 3;
+    const Dma8& d = isA ? da : db;
+    const bool kin = d.kk[i] < t.K - k0;
+    char* tile = isA ? s : s + A_B;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 4 + i) * 1024), 16,
+                                             kin ? d.off[i] : kOOB, (uint32_t)k0, 0, 0);
+  };
+
+  // fragment of rows base .. base+31: chunks h and 2+h of the lane's row
+  auto frag = [&](const char* tile, int base, int part) __attribute__((always_inline)) -> int4 {
+    return *reinterpret_cast<const int4*>(tile + kc_off(base + (lane & 31), 2 * part + (lane >> 5)));
+  };
+
+  int4 xa[MI][2], xb[NI][2], ya[MI][2], yb[NI][2];
+  // read half `part` of fragment q (0..3: A blocks, 4..7: B blocks) of stage s
+  auto ldfrag = [&](int4 (*fa)[2], int4 (*fb)[2], const char* s, int q, int part)
+      __attribute__((always_inline)) {
+    if (q < MI) fa[q][part] = frag(s, wm0 + q * 32, part);
+    else fb[q - MI][part] = frag(s + A_B, wn0 + (q - MI) * 32, part);
+  };
+  // Transposed accumulation (B fragment first): lane l holds row
+  // wm0+32i+(l&31) and, in acc[i][j][4g..4g+3], columns wn0+32j+8g+4(l>>5)+0..3.
+  // Constant zero scale operands select the unscaled instruction (scale 1).
+  auto mma = [&](int4 (*fa)[2], int4 (*fb)[2], int q) __attribute__((always_inline)) {
+    const int i = q / NI, j = q % NI;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+
+  // k-step kt: fragments of stage kt are in (fa, fb); stage `nxt` holds kt+1;
+  // stage `cur` (kt's) is refilled with k-step kt+4
+  auto kstep = [&](int64_t kt, int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2],
+                   char* cur, const char* nxt) __attribute__((always_inline)) {
+    // loads of kt+1 were followed by those of kt+2 and kt+3
+    wait_vm<2 * NLD>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      mma(fa, fb, q);
+      __builtin_amdgcn_sched_barrier(0);
+      ldfrag(ga, gb, nxt, q >> 1, q & 1);
+      if (q & 1) dma(kt + 4, cur, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(0, st0, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(2, st2, q);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(3, st3, q);
+    wait_vm<3 * NLD>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < MI + NI; ++q) {
+      ldfrag(xa, xb, st0, q, 0);
+      ldfrag(xa, xb, st0, q, 1);
+    }
+    // four k-steps per trip name their stages and register sets statically
+    // (up to three extra k-steps at the end multiply zeros)
+    for (int64_t kt = 0; kt < nk; kt += 4) {
+      kstep(kt, xa, xb, ya, yb, st0, st1);
+      kstep(kt + 1, ya, yb, xa, xb, st1, st2);
+      kstep(kt + 2, xa, xb, ya, yb, st2, st3);
+      kstep(kt + 3, ya, yb, xa, xb, st3, st0);
+    }
+    wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // ---- epilogue: stage each 32-row block row in fp32 (a stage per wave),
+  // read it back row-contiguous, scale by 2^(a_sexp + b_sexp), store bf16.
+  // Slot s of staged row r sits at r*512 + ((s ^ (r & 7)) << 4).
+  char* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+  bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
+  bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
+  if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
+  const int32_t* asx = p.a_sexp + (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M);
+  const int32_t* bsx = p.b_sexp + (int64_t)t.g * p.b_sexp_gstride;
+  const int lr = lane & 31, lh = lane >> 5;
+  static_for<MI>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int j = decltype(Q)::value / 4, g = decltype(Q)::value % 4;
+      const int sl = 8 * j + 2 * g + lh;
+      f32x4 v;
+      v[0] = acc[i][j][4 * g];
+      v[1] = acc[i][j][4 * g + 1];
+      v[2] = acc[i][j][4 * g + 2];
+      v[3] = acc[i][j][4 * g + 3];
+      *reinterpret_cast<f32x4*>(stg + lr * 512 + ((sl ^ (lr & 7)) << 4)) = v;
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    const int64_t mrow0 = t.m0 + wm0 + 32 * i;
+    // lane lr holds the scale exponent of row mrow0 + lr (clamped into range)
+    const int64_t mcl = mrow0 + lr < t.M ? mrow0 + lr : t.M - 1;
+    const int ea_l = asx[mcl];
+    if (EPI == EPI_SWIGLU_FWD) {
+      const int sg = lane & 15, rr = lane >> 4;
+      const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 4 * sg;
+      const int64_t hcl = hc < p.N ? hc : p.N - 4;
+      const int4 eg = *reinterpret_cast<const int4*>(bsx + hcl);
+      const int4 eu = *reinterpret_cast<const int4*>(bsx + p.fdim + hcl);
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        const int r = 4 * q + rr;
+        const int ea = __shfl(ea_l, r, 64);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((sg ^ (r & 7)) << 4));
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((sg + 16) ^ (r & 7)) << 4));
+        const int64_t m = mrow0 + r;
+        if (m >= t.M || hc >= p.N) return;
+        const int egs[4] = {eg.x, eg.y, eg.z, eg.w}, eus[4] = {eu.x, eu.y, eu.z, eu.w};
+        float a[4], b[4], h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = ldexpf(a4[e], ea + egs[e]);
+          b[e] = ldexpf(b4[e], ea + eus[e]);
+          h[e] = silu_f(a[e]) * b[e];
+        }
+        store4_bf16(cb + m * p.ldc + hc, h);
+        store4_bf16(ab + m * p.ldaux + hc, a);
+        store4_bf16(ab + m * p.ldaux + p.fdim + hc, b);
+      });
+    } else {
+      const int64_t n = t.n0 + wn0 + 4 * lr;
+      const bool nok = n < p.N;
+      const int4 eb4 = *reinterpret_cast<const int4*>(bsx + (nok ? n : p.N - 4));
+      const int ebs[4] = {eb4.x, eb4.y, eb4.z, eb4.w};
+      static_for<16>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        const int r = 2 * q + lh;
+        const int ea = __shfl(ea_l, r, 64);
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((lr ^ (r & 7)) << 4));
+        const int64_t m = mrow0 + r;
+        if (m >= t.M || !nok) return;
+        float v[4], o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ldexpf(v4[e], ea + ebs[e]);
+        if (EPI == EPI_STORE) {
+          store4_bf16(cb + m * p.ldc + n, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = gelu_f(v[e]);
+          store4_bf16(cb + m * p.ldc + n, o);
+          store4_bf16(ab + m * p.ldaux + n, v);
+        }
+      });
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+  });
+}
+
+template <int EPI, int RAG>
+hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
+  constexpr int BNo = EPI == EPI_SWIGLU_FWD ? kRows8 / 2 : kRows8;
+  const int64_t nt = (p.N + BNo - 1) / BNo;
+  int64_t tiles;
+  if (RAG == RAG_M)
+    tiles = ((p.max_rows + kRows8 - 1) / kRows8 + p.G) * nt;
+  else
+    tiles = (int64_t)p.G * ((p.M + kRows8 - 1) / kRows8) * nt;
+  const int64_t nb = (tiles + 7) / 8 * 8;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG>), dim3((unsigned)nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// FP8 grouped GEMM, both operands K-contiguous (the forward's layouts).
+// Requires K % 16 == 0, 16-byte aligned rows, N % 4 == 0 (f % 4 for the
+// fused SwiGLU) and 16-byte aligned scale arrays; the caller checks.
+hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
+  if (!p.a_sexp || !p.b_sexp || p.col_bias) return hipErrorInvalidValue;
+#define MOE_CASE(E_, R_) \
+  if (epi == E_ && rag == R_) return launch_fp8<E_, R_>(p, s);
+  MOE_CASE(EPI_SWIGLU_FWD, RAG_M)
+  MOE_CASE(EPI_GELU_FWD, RAG_M)
+  MOE_CASE(EPI_STORE, RAG_M)
+  MOE_CASE(EPI_SWIGLU_FWD, RAG_NONE)
+  MOE_CASE(EPI_GELU_FWD, RAG_NONE)
+  MOE_CASE(EPI_STORE, RAG_NONE)
+#undef MOE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

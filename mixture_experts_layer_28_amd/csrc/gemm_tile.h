@@ -17,6 +17,40 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ------------------------------------------------ direct-to-LDS stage rings
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr uint32_t kOOB = 0x80000000u;    // byte offset beyond any buffer extent
+
+// byte offset of 16-byte chunk c (0..3) of row r in a K-contiguous tile of
+// 64-byte rows (32 bf16 or 64 fp8 per row); conflict-free fragment reads
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// raw buffer resource over [base, base + bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// weight row of fused tile row j (gate rows then up rows per wave column); -1 when beyond f
+__device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t fdim) {
+  const int wc = j / WN, w = j - wc * WN, half = WN >> 1;
+  const bool up = w >= half;
+  const int64_t col = n0h + wc * half + (up ? w - half : w);
+  if (col >= fdim) return -1;
+  return up ? fdim + col : col;
+}
+
+// four floats -> four bf16 (round to nearest even) in one 8-byte store
+__device__ __forceinline__ void store4_bf16(bf16_t* dst, const float* v) {
+  uint2 w;
+  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8). Give
 // each XCD a contiguous range of logical tiles so that the tiles resident on
 // one XCD at a time share A/B panels in that XCD's L2. nb is a multiple of 8.

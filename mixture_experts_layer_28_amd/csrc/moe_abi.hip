@@ -15,6 +15,9 @@
 namespace moe {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
+hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
+hipError_t launch_quant_fp8(const void*, int64_t, int64_t, int64_t, const int32_t*, void*, int64_t,
+                            int32_t*, hipStream_t);
 hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dw(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dx(const GemmArgs& p, hipStream_t s);
@@ -76,7 +79,7 @@ enum KernelId {
   K_FWD_UP, K_FWD_DOWN, K_DGRAD_DOWN, K_DGRAD_UP, K_WGRAD_DOWN, K_WGRAD_UP,
   K_SH_FWD_UP, K_SH_FWD_DOWN, K_SH_DGRAD_DOWN, K_SH_DGRAD_UP, K_SH_WGRAD_DOWN, K_SH_WGRAD_UP,
   K_COMBINE, K_COMBINE_BWD, K_ROUTER_DLOGITS, K_ROUTER_DW, K_ROUTER_DW_REDUCE, K_ROUTER_DX,
-  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_COUNT
+  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_QUANT_FP8, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
   "router_logits", "router_topk", "aux_stats", "permute",
@@ -85,7 +88,7 @@ const char* const kKernelNames[K_COUNT] = {
   "gemm_shared_fwd_up", "gemm_shared_fwd_down", "gemm_shared_dgrad_down", "gemm_shared_dgrad_up",
   "gemm_shared_wgrad_down", "gemm_shared_wgrad_up",
   "combine", "combine_bwd", "router_dlogits", "router_dw", "router_dw_reduce", "router_dx",
-  "unpermute", "fill_zero", "bias_update",
+  "unpermute", "fill_zero", "bias_update", "quant_fp8",
 };
 
 struct ProfRec {
@@ -220,6 +223,12 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       const int S = route_bwd_splits(d);
       return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
     }
+    case MOE_OP_FFN_FWD_FP8: {
+      // FP8 codes and scale exponents of H between the two GEMMs
+      size_t b = align256((size_t)T * d->k * d->f) + align256((size_t)T * d->k * 4);
+      if (d->n_shared) b += align256((size_t)T * d->f) + align256((size_t)T * 4);
+      return b;
+    }
   }
   return 0;
 }
@@ -327,7 +336,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_BWD)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
   *bytes = ws_bytes_for(desc, op);
   return MOE_OK;
@@ -518,6 +527,132 @@ int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t*
     q.max_rows = p.max_rows;
     MOE_TRY(run_gemm(desc, q, true, true, EPI_STORE, rag, s, "ffn fwd down matrix",
                      shared ? K_SH_FWD_DOWN : K_FWD_DOWN));
+  }
+  return MOE_OK;
+}
+
+int moe_quantize_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                     const int32_t* valid_rows, void* codes, int64_t ld_codes, int32_t* scale_exp,
+                     void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || rows >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31) (got %lld)", (long long)rows);
+  if (K < 16 || K % 16)
+    return fail(MOE_ERR_INVALID_ARG, "K must be a positive multiple of 16 (got %lld)", (long long)K);
+  if (ld_src < K || ld_src % 8)
+    return fail(MOE_ERR_INVALID_ARG, "ld_src must be >= K and a multiple of 8 (got %lld)",
+                (long long)ld_src);
+  if (ld_codes < K || ld_codes % 16)
+    return fail(MOE_ERR_INVALID_ARG, "ld_codes must be >= K and a multiple of 16 (got %lld)",
+                (long long)ld_codes);
+  MOE_TRY(need(src, "src"));
+  MOE_TRY(need(codes, "codes"));
+  MOE_TRY(need(scale_exp, "scale_exp"));
+  if (valid_rows && (reinterpret_cast<uintptr_t>(valid_rows) & 3))
+    return fail(MOE_ERR_INVALID_ARG, "valid_rows is not 4-byte aligned");
+  if (rows == 0) return MOE_OK;
+  Scope sc(K_QUANT_FP8, (hipStream_t)stream);
+  return hip_check(launch_quant_fp8(src, rows, K, ld_src, valid_rows, codes, ld_codes, scale_exp,
+                                    (hipStream_t)stream),
+                   "fp8 quantize");
+}
+
+int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int32_t* sx_perm,
+                            const int32_t* offsets, const void* xq, const int32_t* sx,
+                            const void* w13q, const int32_t* s13, const void* w2q,
+                            const int32_t* s2, const void* sw13q, const int32_t* ss13,
+                            const void* sw2q, const int32_t* ss2, void* save_pre, void* save_h,
+                            void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  if (desc->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the FP8 forward writes bf16 activations: desc->dtype must be bf16");
+  if (desc->d % 16 || desc->f % 16)
+    return fail(MOE_ERR_UNSUPPORTED, "the FP8 forward needs d and f multiples of 16");
+  MOE_TRY(need(xq_perm, "xq_perm"));
+  MOE_TRY(need(sx_perm, "sx_perm"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(w13q, "w13q"));
+  MOE_TRY(need(s13, "s13"));
+  MOE_TRY(need(w2q, "w2q"));
+  MOE_TRY(need(s2, "s2"));
+  MOE_TRY(need(save_pre, "save_pre"));
+  MOE_TRY(need(save_h, "save_h"));
+  MOE_TRY(need(out, "out"));
+  if (desc->n_shared) {
+    MOE_TRY(need(xq, "xq"));
+    MOE_TRY(need(sx, "sx"));
+    MOE_TRY(need(sw13q, "sw13q"));
+    MOE_TRY(need(ss13, "ss13"));
+    MOE_TRY(need(sw2q, "sw2q"));
+    MOE_TRY(need(ss2, "ss2"));
+    MOE_TRY(need(save_pre_s, "save_pre_s"));
+    MOE_TRY(need(save_h_s, "save_h_s"));
+    MOE_TRY(need(out_shared, "out_shared"));
+  }
+  MOE_TRY(check_ws(desc, MOE_OP_FFN_FWD_FP8, ws, ws_bytes));
+  if (desc->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
+  const int epi1 = desc->act == MOE_SWIGLU ? EPI_SWIGLU_FWD : EPI_GELU_FWD;
+  char* w = (char*)ws;
+  uint8_t* hq = (uint8_t*)w;
+  int32_t* hs = (int32_t*)(w + align256((size_t)T * desc->k * f));
+  uint8_t* hq_s = (uint8_t*)((char*)hs + align256((size_t)T * desc->k * 4));
+  int32_t* hs_s = desc->n_shared ? (int32_t*)((char*)hq_s + align256((size_t)T * f)) : nullptr;
+  for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
+    const int rag = shared ? RAG_NONE : RAG_M;
+    GemmArgs p = blank();
+    p.a = opnd(shared ? xq : xq_perm, d, 0, 1);
+    p.b = opnd(shared ? sw13q : w13q, d, P * d, 0);
+    p.a_sexp = shared ? sx : sx_perm;
+    p.b_sexp = shared ? ss13 : s13;
+    p.b_sexp_gstride = P;
+    p.c = shared ? save_h_s : save_h;
+    p.ldc = f;
+    p.c_rowidx = 1;
+    p.aux = shared ? save_pre_s : save_pre;
+    p.ldaux = P;
+    p.aux_rowidx = 1;
+    p.offsets = offsets;
+    p.G = shared ? 1 : (int)desc->E;
+    p.M = T;
+    p.N = f;
+    p.K = d;
+    p.fdim = f;
+    p.max_rows = T * desc->k;
+    {
+      Scope sc(shared ? K_SH_FWD_UP : K_FWD_UP, s);
+      MOE_TRY(hip_check(gemm_fp8(p, epi1, rag, s), "fp8 ffn fwd first matrix"));
+    }
+    // H (bf16, kept for the backward) -> FP8 codes for the down-projection;
+    // routed rows beyond offsets[E] are skipped on the device
+    uint8_t* q8 = shared ? hq_s : hq;
+    int32_t* qs = shared ? hs_s : hs;
+    {
+      Scope sc(K_QUANT_FP8, s);
+      MOE_TRY(hip_check(launch_quant_fp8(shared ? save_h_s : save_h, shared ? T : T * desc->k, f, f,
+                                         shared ? nullptr : offsets + desc->E, q8, f, qs, s),
+                        "fp8 quantize H"));
+    }
+    GemmArgs q = blank();
+    q.a = opnd(q8, f, 0, 1);
+    q.b = opnd(shared ? sw2q : w2q, f, d * f, 0);
+    q.a_sexp = qs;
+    q.b_sexp = shared ? ss2 : s2;
+    q.b_sexp_gstride = d;
+    q.c = shared ? out_shared : out;
+    q.ldc = d;
+    q.c_rowidx = 1;
+    q.offsets = offsets;
+    q.G = p.G;
+    q.M = T;
+    q.N = d;
+    q.K = f;
+    q.max_rows = p.max_rows;
+    Scope sc(shared ? K_SH_FWD_DOWN : K_FWD_DOWN, s);
+    MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, rag, s), "fp8 ffn fwd down matrix"));
   }
   return MOE_OK;
 }

@@ -9,10 +9,10 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE, MOE_OP_ROUTE,
-               MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine, combine_bwd, grouped_ffn_bwd,
-               grouped_ffn_fwd, make_desc, permute, permute_bwd, route, route_bwd,
-               workspace_size)
+from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
+               MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine,
+               combine_bwd, grouped_ffn_bwd, grouped_ffn_fwd, grouped_ffn_fwd_fp8, make_desc,
+               permute, permute_bwd, quantize_fp8, route, route_bwd, workspace_size)
 
 
 class MoELayer:
@@ -27,15 +27,24 @@ class MoELayer:
     bias update to sel_bias (in place) from this batch's expert loads;
     gumbel_tau > 0 turns on the noisy gate, whose uniforms [T, E] fp32 the
     caller passes to forward() (inp["gumbel_u"] for step()).
+
+    fp8_fwd runs both forward GEMMs on per-row E4M3 operands: every forward
+    quantizes x_perm (and x for a shared expert) and the current weights,
+    keeps the pre-activations and H in bf16, and the backward runs in bf16
+    as usual.
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
-                 bias_gamma: float = 0.0, gumbel_tau: float = 0.0, device="cuda"):
+                 bias_gamma: float = 0.0, gumbel_tau: float = 0.0, fp8_fwd: bool = False,
+                 device="cuda"):
         self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
         self.bias_gamma = bias_gamma
+        self.fp8_fwd = fp8_fwd
+        if fp8_fwd and dtype != "bf16":
+            raise ValueError("the FP8 forward keeps bf16 activations: dtype must be bf16")
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dt = dt
         P = 2 * f if act == "swiglu" else f
@@ -82,9 +91,18 @@ class MoELayer:
         self.dx_router = z(T, d, dtype=f32)
         self.dw_r = z(E, d, dtype=f32)
         self.dX = z(T, d)
-        wsb = max(workspace_size(self.desc, op) for op in (
-            MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
-            MOE_OP_ROUTE_BWD))
+        if fp8_fwd:
+            u8 = torch.uint8
+            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), z(R, dtype=i32)
+            self.w13q, self.s13 = z(E, P, d, dtype=u8), z(E, P, dtype=i32)
+            self.w2q, self.s2 = z(E, d, f, dtype=u8), z(E, d, dtype=i32)
+            sh = bool(n_shared)
+            self.xq, self.sx = (z(T, d, dtype=u8), z(T, dtype=i32)) if sh else (None, None)
+            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), z(1, P, dtype=i32)) if sh else (None, None)
+            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
+        ops = [MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
+               MOE_OP_ROUTE_BWD] + ([MOE_OP_FFN_FWD_FP8] if fp8_fwd else [])
+        wsb = max(workspace_size(self.desc, op) for op in ops)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------ stages
@@ -97,9 +115,22 @@ class MoELayer:
                   self.aux_out, self.ws)
         permute(D, x, self.topk_idx, self.offsets, self.row_of, self.token_of, self.n_dropped,
                 self.x_perm, self.ws)
-        grouped_ffn_fwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
-                        self.save_h, self.save_pre_s, self.save_h_s, self.out, self.out_shared,
-                        self.ws)
+        if self.fp8_fwd:
+            quantize_fp8(self.x_perm, self.xq_perm, self.sx_perm, valid_rows=self.offsets[self.E:])
+            quantize_fp8(w13, self.w13q, self.s13)
+            quantize_fp8(w2, self.w2q, self.s2)
+            if self.n_shared:
+                quantize_fp8(x, self.xq, self.sx)
+                quantize_fp8(sw13, self.sw13q, self.ss13)
+                quantize_fp8(sw2, self.sw2q, self.ss2)
+            grouped_ffn_fwd_fp8(D, self.xq_perm, self.sx_perm, self.offsets, self.xq, self.sx,
+                                self.w13q, self.s13, self.w2q, self.s2, self.sw13q, self.ss13,
+                                self.sw2q, self.ss2, self.save_pre, self.save_h, self.save_pre_s,
+                                self.save_h_s, self.out, self.out_shared, self.ws)
+        else:
+            grouped_ffn_fwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
+                            self.save_h, self.save_pre_s, self.save_h_s, self.out,
+                            self.out_shared, self.ws)
         combine(D, self.out, self.out_shared, self.gate, self.row_of, self.Y)
         return self.Y
 

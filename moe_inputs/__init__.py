@@ -65,6 +65,7 @@ class Workload:
     z_coef: float = 0.0           # weight of the router z-loss in the backward (softmax only)
     bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
     gumbel_tau: Optional[float] = None   # noisy gate temperature; draws uniforms [T, E]
+    fp8: bool = False             # forward GEMMs on per-row E4M3 operands (bf16 activations)
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -92,6 +93,12 @@ WORKLOADS = {
     # 32 local experts of about 2048 rows each
     "dsv3_ep8_shard_bf16": Workload("dsv3_ep8_shard_bf16", T=8192, d=7168, E=32, k=8, f=2048,
                                     score="sigmoid", n_shared=1, sel_bias=True),
+    # FP8 (E4M3) forward GEMMs, bf16 activations and backward
+    "mixtral_fp8_bf16": Workload("mixtral_fp8_bf16", T=8192, d=4096, E=8, k=2, f=14336, cf=1.25,
+                                 fp8=True),
+    "dsv3_ep8_shard_fp8_bf16": Workload("dsv3_ep8_shard_fp8_bf16", T=8192, d=7168, E=32, k=8,
+                                        f=2048, score="sigmoid", n_shared=1, sel_bias=True,
+                                        fp8=True),
 }
 
 

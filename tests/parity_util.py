@@ -56,7 +56,7 @@ def gpu_layer(w: Workload, g: dict):
     import mixture_experts_layer_28_amd as moe
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -68,7 +68,7 @@ def oracle_layer(w: Workload, g: dict):
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     fwd = O.layer_forward(f["x"], f["w_r"], f["w13"], f["w2"], w.k, w.score, w.act, cap,
                           f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], f["gumbel_u"],
-                          w.gumbel_tau)
+                          w.gumbel_tau, fp8=w.fp8)
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
                            w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau)
     return fwd, bwd, f

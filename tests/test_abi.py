@@ -21,11 +21,11 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -153,7 +153,9 @@ def test_capacity_matches_oracle(T, k, E, cf):
 
 def test_workspace_sizes_cover_the_layer():
     d = moe.make_desc(8192, 4096, 8, 2, 14336, capacity=2560)
-    sizes = [moe.workspace_size(d, op) for op in range(6)]
+    sizes = [moe.workspace_size(d, op) for op in range(7)]
+    # the FP8 forward keeps H's codes and exponents between its two GEMMs
+    assert sizes[moe.MOE_OP_FFN_FWD_FP8] >= 8192 * 2 * 14336 + 8192 * 2 * 4
     # backward needs the [T*k, 2f] activation-gradient buffer
     assert sizes[moe.MOE_OP_FFN_BWD] >= 8192 * 2 * 2 * 14336 * 2
     assert sizes[moe.MOE_OP_ROUTE] >= 8192 * 8 * 4
@@ -204,3 +206,39 @@ def test_binding_signatures_match_header():
         for a in getattr(L, name).argtypes:
             got.append(ct.get(a, "ptr"))  # POINTER(...) types are pointers
         assert got == want, (name, got, want)
+
+
+def test_fp8_quantize_validation():
+    """Bad sizes, strides and pointers fail before any HIP call; rows = 0 is
+    a successful no-op."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ok = dict(src=FAKE, rows=4, K=64, ld_src=64, valid=None, codes=FAKE, ld_q=64, sexp=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.moe_quantize_fp8(P(a["src"]) if a["src"] else None, a["rows"], a["K"], a["ld_src"],
+                                  P(a["valid"]) if a["valid"] else None,
+                                  P(a["codes"]) if a["codes"] else None, a["ld_q"],
+                                  P(a["sexp"]) if a["sexp"] else None, None)
+    for bad in (dict(K=8), dict(K=72), dict(ld_src=32), dict(ld_src=68), dict(ld_q=72),
+                dict(rows=-1), dict(src=0), dict(codes=FAKE + 8), dict(sexp=0),
+                dict(valid=FAKE + 2)):
+        assert call(**bad) == 1, bad
+        assert L.moe_last_error().decode()
+    assert call(rows=0) == 0
+
+
+def test_fp8_forward_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE)] * 19
+
+    def call(d, ws_bytes=1 << 40):
+        return L.moe_grouped_ffn_fwd_fp8(ctypes.byref(d), *ptrs, P(FAKE), ws_bytes, None)
+    # fp32 layers and widths off the 16-grid are unsupported; too little workspace fails
+    assert call(_desc(dtype="f32")) == 2
+    assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
+    assert call(_desc(), ws_bytes=16) == 3
+    assert call(_desc(T=0)) == 0

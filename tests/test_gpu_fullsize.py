@@ -7,6 +7,7 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
   finegrained_bf16  T=16384 d=4096 E=128 k=8 SwiGLU f=1536, aux 0.01, z-loss 1e-3
   dsv3_bf16         T=8192  d=7168 E=256 k=8 sigmoid + selection bias (and its
                     update), one shared expert, SwiGLU f=2048
+  mixtral_fp8_bf16  the Mixtral-like layer with FP8 (E4M3) forward GEMMs
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -103,6 +104,9 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
     dgate_ref = np.zeros((n, k))
     dw13_ref, dw2_ref, dw13_got, dw2_got = [], [], [], []
     sampled_e = set(r["topk_idx"][toks].ravel().tolist())
+    # FP8 forward: per-row quantization, so single rows and weight-row subsets
+    # quantize exactly as in the whole GEMM (the sliced forward's O is unused)
+    efwd = O.expert_forward_fp8 if w.fp8 else O.expert_forward
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
@@ -113,7 +117,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
                 if r["topk_idx"][t, j] != e or pm["row_of"][t, j] < 0:
                     continue
                 row = g_row_of[t, j]
-                o, sv = O.expert_forward(x[t:t + 1], w13e, w2e, w.act)
+                o, sv = efwd(x[t:t + 1], w13e, w2e, w.act)
                 pre = np.concatenate([sv["a"], sv["b"]], 1) if w.act == "swiglu" else sv["a"]
                 dgate_ref[i, j] = float(dy[t] @ o[0])
                 dO = gate[t, j] * dy[t:t + 1]
@@ -134,7 +138,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
             dOe = gate[rows_t, slot][:, None] * dy[rows_t]
             J = np.sort(rng.choice(w.f, size=n_col, replace=False))
             rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
-            _, sv = O.expert_forward(Xe, w13e[rows13], w2e[:, J], w.act)
+            _, sv = efwd(Xe, w13e[rows13], w2e[:, J], w.act)
             _, d13, d2, _ = O.expert_backward(Xe, w13e[rows13], w2e[:, J], sv, dOe, w.act)
             dw13_ref.append(d13)
             dw2_ref.append(d2)
@@ -146,7 +150,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
         # sampled hidden columns of its weight gradients over all tokens
         sw13 = as_f64(g["sw13"][0], dt)
         sw2 = as_f64(g["sw2"][0], dt)
-        os_, svs = O.expert_forward(x[toks], sw13, sw2, w.act)
+        os_, svs = efwd(x[toks], sw13, sw2, w.act)
         dxs, _, _, _ = O.expert_backward(x[toks], sw13, sw2, svs, dy[toks], w.act)
         Y_ref += os_
         dX_ref += dxs
@@ -154,7 +158,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
         assert_close("dX_shared", to_np(L.dx_shared)[toks], dxs, dt, rep)
         J = np.sort(rng.choice(w.f, size=n_col, replace=False))
         rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
-        _, sv = O.expert_forward(x, sw13[rows13], sw2[:, J], w.act)
+        _, sv = efwd(x, sw13[rows13], sw2[:, J], w.act)
         _, d13, d2, _ = O.expert_backward(x, sw13[rows13], sw2[:, J], sv, dy, w.act)
         assert_close("dSW13[sampled]", to_np(L.dsw13[0][torch.as_tensor(rows13, device="cuda")]),
                      d13, dt, rep)
@@ -185,6 +189,6 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
 
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
-                                  "finegrained_bf16", "dsv3_bf16"])
+                                  "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16"])
 def test_fullsize_sampled(name):
     check_sampled(WORKLOADS[name])

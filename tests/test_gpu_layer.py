@@ -25,6 +25,9 @@ REDUCED = {
     # top-1 routing and a 1.5 capacity factor on the skewed load
     "top1_small": WORKLOADS["top1_bf16"].replace(T=1536, d=512, f=768),
     "skewed_cf15_small": WORKLOADS["skewed_cf15_bf16"].replace(T=1024, d=512, f=1024),
+    # FP8 forward GEMMs (routed only; routed + shared with sigmoid scoring)
+    "mixtral_fp8_small": WORKLOADS["mixtral_fp8_bf16"].replace(T=1536, d=512, f=768),
+    "dsv3_fp8_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True),
 }
 
 EDGE = {
@@ -46,6 +49,13 @@ EDGE = {
     # noisy gate through the GEMM-logits router (E > 8), fp32, low temperature
     "noisy_fp32": Workload("noisy32", T=300, d=64, E=40, k=4, f=64, dtype="fp32", gumbel_tau=0.5,
                            aux_coef=0.05, z_coef=0.02),
+    # FP8 forward with ragged T, E, a K tail (d = 144 = 2*64 + 16) and N tails
+    # (f = 208), GELU and a shared expert
+    "ragged_fp8_gelu_shared": Workload("ragged8", T=1000, d=144, E=6, k=3, f=208, act="gelu",
+                                       score="sigmoid", n_shared=1, sel_bias=True, fp8=True),
+    # FP8 forward with every assignment dropped: the routed GEMMs see no rows
+    "fp8_all_dropped_shared": Workload("drop8", T=512, d=256, E=8, k=2, f=256, cf=0.0,
+                                       n_shared=1, fp8=True),
 }
 
 
