@@ -292,10 +292,20 @@ def expert_forward_fp8(X, w13, w2, act):
     activation H is kept in bf16 (the stored activation), and that bf16 H and
     w2 are quantized per row for the down-projection. The saved values for
     the backward are the pre-activations and H as computed here."""
-    f = w2.shape[1]
+    return expert_forward_fp8_wq(X, quantize_weights_fp8(w13), quantize_weights_fp8(w2), act)
+
+
+def quantize_weights_fp8(w):
+    """Dequantized per-row FP8 copy of a weight matrix (rows = output channels)."""
+    return dequantize_rows_fp8(*quantize_rows_fp8(w))
+
+
+def expert_forward_fp8_wq(X, w13d, w2d, act):
+    """expert_forward_fp8 on weights already passed through quantize_weights_fp8
+    (per-row quantization, so any subset of rows quantizes the same way)."""
+    f = w2d.shape[1]
     Xd = dequantize_rows_fp8(*quantize_rows_fp8(X))
-    Wd = dequantize_rows_fp8(*quantize_rows_fp8(w13))
-    pre = Xd @ Wd.T
+    pre = Xd @ w13d.T
     if act == "swiglu":
         a, b = pre[:, :f], pre[:, f:]
         H = silu(a) * b
@@ -307,9 +317,7 @@ def expert_forward_fp8(X, w13, w2, act):
     else:
         raise ValueError(act)
     Hd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(H)))
-    W2d = dequantize_rows_fp8(*quantize_rows_fp8(w2))
-    return Hd @ W2d.T, saved
-
+    return Hd @ w2d.T, saved
 
 def expert_backward(X, w13, w2, saved, dO, act):
     """Backward of expert_forward for upstream dO [n, d].

@@ -105,19 +105,24 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
     dw13_ref, dw2_ref, dw13_got, dw2_got = [], [], [], []
     sampled_e = set(r["topk_idx"][toks].ravel().tolist())
     # FP8 forward: per-row quantization, so single rows and weight-row subsets
-    # quantize exactly as in the whole GEMM (the sliced forward's O is unused)
-    efwd = O.expert_forward_fp8 if w.fp8 else O.expert_forward
+    # quantize exactly as in the whole GEMM; each expert's weights are
+    # quantized once (w13d, w2d) and sliced like the bf16 ones
+    def wq(m):
+        return O.quantize_weights_fp8(m) if w.fp8 else m
+    efwd = O.expert_forward_fp8_wq if w.fp8 else O.expert_forward
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
+        print(f"[step] oracle expert {e}", flush=True)
         w13e = as_f64(g["w13"][e], dt)
         w2e = as_f64(g["w2"][e], dt)
+        w13f, w2f = wq(w13e), wq(w2e)   # the forward's weights (FP8-quantized when w.fp8)
         for i, t in enumerate(toks):
             for j in range(k):
                 if r["topk_idx"][t, j] != e or pm["row_of"][t, j] < 0:
                     continue
                 row = g_row_of[t, j]
-                o, sv = efwd(x[t:t + 1], w13e, w2e, w.act)
+                o, sv = efwd(x[t:t + 1], w13f, w2f, w.act)
                 pre = np.concatenate([sv["a"], sv["b"]], 1) if w.act == "swiglu" else sv["a"]
                 dgate_ref[i, j] = float(dy[t] @ o[0])
                 dO = gate[t, j] * dy[t:t + 1]
@@ -138,19 +143,20 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
             dOe = gate[rows_t, slot][:, None] * dy[rows_t]
             J = np.sort(rng.choice(w.f, size=n_col, replace=False))
             rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
-            _, sv = efwd(Xe, w13e[rows13], w2e[:, J], w.act)
+            _, sv = efwd(Xe, w13f[rows13], w2f[:, J], w.act)
             _, d13, d2, _ = O.expert_backward(Xe, w13e[rows13], w2e[:, J], sv, dOe, w.act)
             dw13_ref.append(d13)
             dw2_ref.append(d2)
             dw13_got.append(to_np(L.dw13[e][torch.as_tensor(rows13, device="cuda")]))
             dw2_got.append(to_np(L.dw2[e][:, torch.as_tensor(J, device="cuda")]))
-        del w13e, w2e
+        del w13e, w2e, w13f, w2f
     if w.n_shared:
         # the shared expert: sampled tokens' outputs and input gradients, and
         # sampled hidden columns of its weight gradients over all tokens
         sw13 = as_f64(g["sw13"][0], dt)
         sw2 = as_f64(g["sw2"][0], dt)
-        os_, svs = efwd(x[toks], sw13, sw2, w.act)
+        sw13f, sw2f = wq(sw13), wq(sw2)
+        os_, svs = efwd(x[toks], sw13f, sw2f, w.act)
         dxs, _, _, _ = O.expert_backward(x[toks], sw13, sw2, svs, dy[toks], w.act)
         Y_ref += os_
         dX_ref += dxs
@@ -158,7 +164,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
         assert_close("dX_shared", to_np(L.dx_shared)[toks], dxs, dt, rep)
         J = np.sort(rng.choice(w.f, size=n_col, replace=False))
         rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
-        _, sv = efwd(x, sw13[rows13], sw2[:, J], w.act)
+        _, sv = efwd(x, sw13f[rows13], sw2f[:, J], w.act)
         _, d13, d2, _ = O.expert_backward(x, sw13[rows13], sw2[:, J], sv, dy, w.act)
         assert_close("dSW13[sampled]", to_np(L.dsw13[0][torch.as_tensor(rows13, device="cuda")]),
                      d13, dt, rep)
