@@ -6,21 +6,26 @@
 // owns a 128 x 128 sub-tile of 32x32 MFMA blocks whose accumulators fill the
 // AGPR file.
 //
-// Operands stream through a ring of five LDS stages, each holding 32 k of
-// both tiles (32 KiB), filled by buffer_load ... lds (global -> LDS with no
-// staging registers). Loads for k-step kt+4 are issued during k-step kt into
-// the stage k-step kt-1 released, one instruction after every fourth MFMA,
-// so the memory queue sees a steady stream instead of a burst per barrier.
-// Per k-step:
-//   slice 0 (k 0..15): 16 MFMAs, slice 1's fragments read in between;
-//   wait for stage kt+1's loads, barrier;
-//   slice 1 (k 16..31): 16 MFMAs, stage kt+1's slice-0 fragments read in
-//   between (they have a whole slice of MFMAs to arrive).
+// Operands stream through two LDS stages of 64 k each (64 KiB: 32 KiB per
+// operand tile), filled by buffer_load ... lds (global -> LDS with no staging
+// registers). A K-contiguous operand row is then 128 bytes of global memory,
+// a whole cache line: measured on gfx950, DMA of 128-byte row pieces feeds a
+// CU about 1.65x faster than 64-byte pieces (the 32-k stages of a deeper ring
+// lost more to that than the ring's depth won).
+// Per k-step (4 slices of 16 k, 16 MFMAs each, with the next slice's
+// fragments read between the MFMAs of the current one):
+//   slice 0: the second half of k-step kt+1's loads into the other stage;
+//   slices 1, 2;
+//   wait for k-step kt+1's loads, barrier: every read of this stage has been
+//   issued and waited for, and the other stage is complete;
+//   slice 3: reads k-step kt+1's slice-0 fragments and issues the first half
+//   of k-step kt+2's loads into this stage.
 //
-// LDS layouts (bank-conflict free for the fragment reads, measured):
-//   K-contiguous operand, [rows][32] bf16: 16-byte chunk c of row r at
-//     r*64 + ((c ^ ((r >> 2) & 3)) << 4).
-//   K-strided operand (the transposed reads of the backward), [32][rows]:
+// LDS layouts (bank-conflict free for the fragment reads):
+//   K-contiguous operand, [rows][64] bf16 (128-byte rows): 16-byte chunk c of
+//     row r at r*128 + ((c ^ ((r >> 1) & 7)) << 4); a 16-lane group reading
+//     one chunk of 16 consecutive rows then covers all 64 banks.
+//   K-strided operand (the transposed reads of the backward), [64][rows]:
 //     16-byte slot s (8 rows) of k-row k at k*rows*2 + ((s ^ ((k & 3) << 1)) << 4);
 //     fragments are built by ds_read_b64_tr_b16, which transposes 4x4
 //     blocks of bf16 across each 16-lane group.
@@ -32,14 +37,17 @@
 
 namespace moe {
 
-constexpr int kBK = 32;                   // k per stage
+constexpr int kBK = 64;                   // k per stage
 constexpr int kRows = 256;                // tile rows of either operand
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [32][kRows] tile
+// byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous tile of
+// 128-byte rows (64 bf16): conflict-free for 16-lane groups reading one chunk
+__device__ __forceinline__ int kc2_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [64][kRows] tile
 __device__ __forceinline__ int ks_off(int k, int s) {
   return k * (kRows * 2) + ((s ^ ((k & 3) << 1)) << 4);
 }
@@ -54,19 +62,25 @@ __device__ __forceinline__ int ks_off(int k, int s) {
 // off[i] is the byte offset at k0 = 0 (kOOB when the rows lie outside the
 // operand); kk[i] is the lane's k inside a stage, for the K-tail test.
 struct DmaSrc {
-  uint32_t off[4];
-  int kk[4];
+  uint32_t off[8];
+  int kk[8];
 };
 
+// Per-lane DMA source of one operand tile: a wave issues 8 instructions per
+// stage; instruction i fills 1 KiB block blk = wave*8 + i.
+//   K-contiguous: block = rows blk*8 .. +7 (128 bytes each), lane l -> row
+//     blk*8 + (l>>3), physical chunk l&7, logical chunk (l&7) ^ ((row>>1)&7).
+//   K-strided: block = k-rows 2*blk, 2*blk+1, lane l -> k-row 2*blk + (l>>5),
+//     logical slot (l&31) ^ ((k&3)<<1), i.e. rows 8*slot .. 8*slot+7.
 template <bool KC, bool FUSED, int WN>
 __device__ __forceinline__ void dma_src(DmaSrc& d, int64_t ld, int64_t rows_valid, int64_t r0,
                                         int64_t fdim, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
     if (KC) {
-      const int r = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((lane >> 4) & 3);
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       int64_t grow;
       bool ok;
       if (FUSED) {
@@ -109,21 +123,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int BNo = FUSED ? BN / 2 : BN;      // output columns per tile
   constexpr int A_EL = BM * kBK, B_EL = BN * kBK;
   constexpr int ST = A_EL + B_EL;               // one stage (bf16 elements)
-  constexpr int NLD = 8;                        // DMA instructions per wave per stage
+  constexpr int NLD = 16;                       // DMA instructions per wave per stage
   static_assert(!FUSED || BKM, "fused SwiGLU needs a K-contiguous weight");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
-  // Five stages, separate objects so that the compiler can tell a stage being
-  // filled by DMA from the stage being read.
+  // Two stages of 64 KiB, separate objects so that the compiler can tell the
+  // stage being filled by DMA from the stage being read.
   __shared__ __attribute__((aligned(1024))) bf16_t st0[ST];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[ST];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[ST];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[ST];
-  __shared__ __attribute__((aligned(1024))) bf16_t st4[ST];
 
   Tile t;
   {
     // the group-tile scan runs before any load and borrows the last stage
-    int* s_tiles = reinterpret_cast<int*>(st4);
+    int* s_tiles = reinterpret_cast<int*>(st1);
     const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
     __syncthreads();
     if (!have) return;
@@ -152,25 +163,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int64_t nk = (t.K + kBK - 1) / kBK;
 
-  // DMA instruction q (0..7: A blocks then B blocks) of k-step kt into stage s
+  // DMA instruction q (0..15: A blocks then B blocks) of k-step kt into stage s
   auto dma = [&](int64_t kt, bf16_t* s, int q) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK;
-    const bool isA = q < 4;
-    const int i = q & 3;
+    const bool isA = q < 8;
+    const int i = q & 7;
     const DmaSrc& d = isA ? da : db;
     const bool kc = isA ? AKM : BKM;
     const int64_t ld = isA ? p.a.ld : p.b.ld;
     const bool kin = d.kk[i] < t.K - k0;
     const uint32_t so = (uint32_t)(kc ? k0 * 2 : k0 * ld * 2);
     bf16_t* tile = isA ? s : s + A_EL;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 4 + i) * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 8 + i) * 512), 16,
                                              kin ? d.off[i] : kOOB, so, 0, 0);
   };
 
-  // fragment of 32 rows (base .. base+31) for k slice sl of a stage tile
+  // fragment of 32 rows (base .. base+31) for k slice sl (0..3) of a stage tile
   auto frag = [&](const bf16_t* tile, bool kc, int base, int sl) __attribute__((always_inline)) -> bf16x8 {
     const char* tb = reinterpret_cast<const char*>(tile);
-    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc_off(base + (lane & 31), sl * 2 + (lane >> 5)));
+    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc2_off(base + (lane & 31), sl * 2 + (lane >> 5)));
     const int g = lane >> 4, i = lane & 15;
     const int row = base + 16 * (g & 1) + 4 * (i & 3);
     const int k = 16 * sl + 8 * (g >> 1) + (i >> 2);
@@ -188,61 +199,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   // Each block is accumulated transposed (B fragment as the MFMA's first
   // operand), so lane l holds row wm0+32i+(l&31) and, in acc[i][j][4g..4g+3],
-  // the four consecutive columns wn0+32j+8g+4(l>>5) .. +3: the epilogue then
-  // writes 8-byte row pieces straight from the accumulators.
+  // the four consecutive columns wn0+32j+8g+4(l>>5) .. +3.
   auto mma = [&](const bf16x8* fa, const bf16x8* fb, int q) __attribute__((always_inline)) {
     const int i = q / NI, j = q % NI;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
-  // one k-step on stage `cur` (slice-0 fragments already in fa0/fb0); the
-  // loads of k-step kt+4 go to stage `fill`
-  auto kstep = [&](int64_t kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
+  // One slice of 16 MFMAs on fragment set (fa, fb), reading the fragments of
+  // slice rsl of stage rs into (ga, gb) between them, and, when dk >= 0, the
+  // DMA instructions dq0 .. dq0+7 of k-step dk into stage ds (one per two MFMAs).
+  auto slice = [&](const bf16x8* fa, const bf16x8* fb, bf16x8* ga, bf16x8* gb, const bf16_t* rs,
+                   int rsl, int64_t dk, bf16_t* ds, int dq0) __attribute__((always_inline)) {
     static_for<NM>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
-      mma(fa0, fb0, q);
+      mma(fa, fb, q);
       __builtin_amdgcn_sched_barrier(0);
-      if (q < MI + NI) ldfrag_q(fa1, fb1, cur, 1, q);
-      if ((q & 3) == 3) dma(kt + 4, fill, q >> 2);
+      if (q < MI + NI) ldfrag_q(ga, gb, rs, rsl, q);
+      if (dk >= 0 && (q & 1)) dma(dk, ds, dq0 + (q >> 1));
       __builtin_amdgcn_sched_barrier(0);
     });
-    // stage kt+1's loads were followed by those of kt+2, kt+3 and half of kt+4
-    wait_vm<2 * NLD + NLD / 2>();
+  };
+
+  // k-step kt on stage cur (its slice-0 fragments already in fa0/fb0); the
+  // first half of k-step kt+1's loads into nxt was issued during the previous
+  // k-step. After slice 2 every read of cur has been issued and waited for,
+  // so the barrier that also publishes nxt frees cur for k-step kt+2.
+  auto kstep = [&](int64_t kt, bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    slice(fa0, fb0, fa1, fb1, cur, 1, kt + 1, nxt, NLD / 2);
+    slice(fa1, fb1, fa0, fb0, cur, 2, -1, nxt, 0);
+    slice(fa0, fb0, fa1, fb1, cur, 3, -1, nxt, 0);
+    wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    static_for<NM>([&](auto Q) __attribute__((always_inline)) {
-      constexpr int q = decltype(Q)::value;
-      mma(fa1, fb1, q);
-      __builtin_amdgcn_sched_barrier(0);
-      if (q < MI + NI) ldfrag_q(fa0, fb0, nxt, 0, q);
-      if ((q & 3) == 3) dma(kt + 4, fill, NLD / 2 + (q >> 2));
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    slice(fa1, fb1, fa0, fb0, nxt, 0, kt + 2, cur, 0);
   };
 
   if (nk > 0) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) dma(0, st0, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(2, st2, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(3, st3, q);
-    wait_vm<3 * NLD>();
+    wait_vm<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, st0, 0, q);
-    // five k-steps per trip name their stages statically (up to four extra
-    // k-steps at the end multiply the zeros their out-of-range loads left)
-    for (int64_t kt = 0; kt < nk; kt += 5) {
-      kstep(kt, st0, st1, st4);
-      kstep(kt + 1, st1, st2, st0);
-      kstep(kt + 2, st2, st3, st1);
-      kstep(kt + 3, st3, st4, st2);
-      kstep(kt + 4, st4, st0, st3);
+#pragma unroll
+    for (int q = 0; q < NLD / 2; ++q) dma(1, st1, q);
+    // two k-steps per trip name their stages statically (one extra k-step at
+    // the end multiplies the zeros its out-of-range loads left)
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+      kstep(kt, st0, st1);
+      kstep(kt + 1, st1, st0);
     }
     // every load (including those past the end) must land before the stages are reused
     wait_vm<0>();
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // back row-contiguous: lane l takes 16-byte slot l&31 of row 2q + (l>>5),
   // so every global access of an instruction covers two whole 256-byte rows.
   // Slot s of row r sits at r*512 + ((s ^ (r & 7)) << 4).
-  char* stg = reinterpret_cast<char*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  char* stg = reinterpret_cast<char*>(st0) + wave * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
