@@ -8,46 +8,45 @@
 // Workgroup: 256 threads = 4 waves in a 2x2 grid; tile 256 x 256; each wave
 // owns 128 x 128 as 4 x 4 MFMA blocks of 32 x 32 held in AGPRs.
 //
-// A stage holds 64 k of both tiles: 2 x 256 rows x 64 bytes = 32 KiB, the
-// same bytes per row as the bf16 GEMM's 32-k stage, so the same swizzled
-// layout and DMA pattern serve (16-byte chunk c of a row = k 16c .. 16c+15).
-// One MFMA consumes a whole stage's k for its block. The matrix core takes
-// from lane l (row l & 31, half h = l >> 5) 32 bytes: k 16h .. 16h+15 in its
-// first 16 bytes and k 32+16h .. 32+16h+15 in the next 16 (measured on
-// gfx950), so a fragment is chunks h and 2+h of its row, the same two
-// conflict-free chunk patterns the bf16 fragments use.
-//
-// Four stages, one barrier per k-step. Entering k-step kt the fragments of
-// stage kt are already in registers (read during k-step kt-1), so after the
-// barrier stage kt is free: its refill with k-step kt+4 is issued during
-// k-step kt, one DMA instruction after every second MFMA, while the
-// fragments of stage kt+1 are read into the other register set.
+// Two LDS stages of 128 k: 2 x 256 rows x 128 bytes = 64 KiB each, so every
+// DMA row piece is a whole 128-byte line (the bf16 GEMM's layout: chunk c of
+// row r at r*128 + ((c ^ ((r >> 1) & 7)) << 4), 16 fp8 per chunk). A k-step
+// is two slices of 64 k, one MFMA per 32 x 32 block each. The matrix core
+// takes from lane l (row l & 31, half h = l >> 5) 32 bytes: k 16h .. 16h+15
+// of its 64-k slice in the first 16 bytes and k 32+16h .. 32+16h+15 in the
+// next 16 (measured on gfx950), so a fragment of slice sl is chunks 4sl+h
+// and 4sl+2+h of its row.
+// Per k-step: slice 0 (slice 1's fragments read between the MFMAs); wait for
+// k-step kt+1, barrier (every read of this stage is done); slice 1 (k-step
+// kt+1's slice-0 fragments read, and all of k-step kt+2's loads issued into
+// this stage, one per MFMA, so they have a whole k-step to land: measured
+// 10-29% faster than splitting them across the two slices).
 #include "gemm_tile.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBK8 = 64;                  // k per stage (bytes per tile row)
+constexpr int kBK8 = 128;                 // k per stage (bytes per tile row)
 constexpr int kRows8 = 256;               // tile rows of either operand
 
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
 struct Dma8 {
-  uint32_t off[4];
-  int kk[4];
+  uint32_t off[8];
+  int kk[8];
 };
 
 // Per-lane DMA source: instruction i of a wave fills 1 KiB block
-// blk = wave*4 + i = rows blk*16 .. +15; lane l -> row blk*16 + (l >> 2),
-// logical chunk (l & 3) ^ ((l >> 4) & 3) (the kc_off swizzle).
+// blk = wave*8 + i = rows blk*8 .. +7 (128 bytes each); lane l -> row
+// blk*8 + (l >> 3), physical chunk l & 7, logical chunk (l & 7) ^ ((row >> 1) & 7).
 template <bool FUSED, int WN>
 __device__ __forceinline__ void dma_src8(Dma8& d, int64_t ld, int64_t rows_valid, int64_t r0,
                                          int64_t fdim, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+  for (int i = 0; i < 8; ++i) {
+    const int r = (wave * 8 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     int64_t grow;
     bool ok;
     if (FUSED) {
@@ -61,6 +60,9 @@ __device__ __forceinline__ void dma_src8(Dma8& d, int64_t ld, int64_t rows_valid
     d.kk[i] = c * 16;
   }
 }
+
+// byte offset of 16-byte chunk c (0..7) of row r in a tile of 128-byte rows
+__device__ __forceinline__ int kc8_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
   v8i32 v;
@@ -77,16 +79,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int BNo = FUSED ? BN / 2 : BN;
   constexpr int A_B = BM * kBK8, B_B = BN * kBK8;   // bytes per stage of each tile
   constexpr int ST = A_B + B_B;
-  constexpr int NLD = 8;                            // DMA instructions per wave per stage
+  constexpr int NLD = 16;                           // DMA instructions per wave per stage
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
   __shared__ __attribute__((aligned(1024))) char st0[ST];
   __shared__ __attribute__((aligned(1024))) char st1[ST];
-  __shared__ __attribute__((aligned(1024))) char st2[ST];
-  __shared__ __attribute__((aligned(1024))) char st3[ST];
 
   Tile t;
   {
-    int* s_tiles = reinterpret_cast<int*>(st3);
+    int* s_tiles = reinterpret_cast<int*>(st1);
     const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
     __syncthreads();
     if (!have) return;
@@ -114,29 +114,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int64_t nk = (t.K + kBK8 - 1) / kBK8;
 
-  // DMA instruction q (0..7: A blocks then B blocks) of k-step kt into stage s
+  // DMA instruction q (0..15: A blocks then B blocks) of k-step kt into stage s
   auto dma = [&](int64_t kt, char* s, int q) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK8;
-    const bool isA = q < 4;
-    const int i = q & 3;
+    const bool isA = q < 8;
+    const int i = q & 7;
     const Dma8& d = isA ? da : db;
     const bool kin = d.kk[i] < t.K - k0;
     char* tile = isA ? s : s + A_B;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 4 + i) * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 8 + i) * 1024), 16,
                                              kin ? d.off[i] : kOOB, (uint32_t)k0, 0, 0);
   };
 
-  // fragment of rows base .. base+31: chunks h and 2+h of the lane's row
-  auto frag = [&](const char* tile, int base, int part) __attribute__((always_inline)) -> int4 {
-    return *reinterpret_cast<const int4*>(tile + kc_off(base + (lane & 31), 2 * part + (lane >> 5)));
+  // half `part` of the fragment of rows base .. base+31 for slice sl
+  auto frag = [&](const char* tile, int base, int sl, int part) __attribute__((always_inline)) -> int4 {
+    return *reinterpret_cast<const int4*>(tile + kc8_off(base + (lane & 31), 4 * sl + 2 * part + (lane >> 5)));
   };
 
   int4 xa[MI][2], xb[NI][2], ya[MI][2], yb[NI][2];
-  // read half `part` of fragment q (0..3: A blocks, 4..7: B blocks) of stage s
-  auto ldfrag = [&](int4 (*fa)[2], int4 (*fb)[2], const char* s, int q, int part)
+  // read half `part` of fragment q (0..3: A blocks, 4..7: B blocks) of slice sl of stage s
+  auto ldfrag = [&](int4 (*fa)[2], int4 (*fb)[2], const char* s, int sl, int q, int part)
       __attribute__((always_inline)) {
-    if (q < MI) fa[q][part] = frag(s, wm0 + q * 32, part);
-    else fb[q - MI][part] = frag(s + A_B, wn0 + (q - MI) * 32, part);
+    if (q < MI) fa[q][part] = frag(s, wm0 + q * 32, sl, part);
+    else fb[q - MI][part] = frag(s + A_B, wn0 + (q - MI) * 32, sl, part);
   };
   // Transposed accumulation (B fragment first): lane l holds row
   // wm0+32i+(l&31) and, in acc[i][j][4g..4g+3], columns wn0+32j+8g+4(l>>5)+0..3.
@@ -147,48 +147,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
   };
 
-  // k-step kt: fragments of stage kt are in (fa, fb); stage `nxt` holds kt+1;
-  // stage `cur` (kt's) is refilled with k-step kt+4
-  auto kstep = [&](int64_t kt, int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2],
-                   char* cur, const char* nxt) __attribute__((always_inline)) {
-    // loads of kt+1 were followed by those of kt+2 and kt+3
-    wait_vm<2 * NLD>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+  // 16 MFMAs on (fa, fb), reading slice rsl of stage rs into (ga, gb) between
+  // them and, when dk >= 0, issuing k-step dk's 16 DMA instructions into ds
+  auto slice = [&](int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2], const char* rs,
+                   int rsl, int64_t dk, char* ds) __attribute__((always_inline)) {
     static_for<NM>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
       mma(fa, fb, q);
       __builtin_amdgcn_sched_barrier(0);
-      ldfrag(ga, gb, nxt, q >> 1, q & 1);
-      if (q & 1) dma(kt + 4, cur, q >> 1);
+      ldfrag(ga, gb, rs, rsl, q >> 1, q & 1);
+      if (dk >= 0) dma(dk, ds, q);
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+
+  auto kstep = [&](int64_t kt, char* cur, char* nxt) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    slice(xa, xb, ya, yb, cur, 1, -1, nxt);
+    wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    slice(ya, yb, xa, xb, nxt, 0, kt + 2, cur);
   };
 
   if (nk > 0) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) dma(0, st0, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(2, st2, q);
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(3, st3, q);
-    wait_vm<3 * NLD>();
+    wait_vm<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < MI + NI; ++q) {
-      ldfrag(xa, xb, st0, q, 0);
-      ldfrag(xa, xb, st0, q, 1);
+      ldfrag(xa, xb, st0, 0, q, 0);
+      ldfrag(xa, xb, st0, 0, q, 1);
     }
-    // four k-steps per trip name their stages and register sets statically
-    // (up to three extra k-steps at the end multiply zeros)
-    for (int64_t kt = 0; kt < nk; kt += 4) {
-      kstep(kt, xa, xb, ya, yb, st0, st1);
-      kstep(kt + 1, ya, yb, xa, xb, st1, st2);
-      kstep(kt + 2, xa, xb, ya, yb, st2, st3);
-      kstep(kt + 3, ya, yb, xa, xb, st3, st0);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
+    // two k-steps per trip name their stages statically (one extra k-step at
+    // the end multiplies zeros)
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+      kstep(kt, st0, st1);
+      kstep(kt + 1, st1, st0);
     }
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- epilogue: stage each 32-row block row in fp32 (a stage per wave),
   // read it back row-contiguous, scale by 2^(a_sexp + b_sexp), store bf16.
   // Slot s of staged row r sits at r*512 + ((s ^ (r & 7)) << 4).
-  char* stg = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+  char* stg = st0 + wave * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
