@@ -268,8 +268,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
   const int lr = lane & 31, lh = lane >> 5;
+  // Backward epilogues read this lane's saved pre-activations (a, and b for
+  // SwiGLU) of each block row: the loads of block row i+1 are issued when
+  // block row i starts, so they overlap its staging, math and stores
+  // (rows/columns clamped into range when out).
+  constexpr bool BWD = EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD;
+  constexpr bool SW = EPI == EPI_SWIGLU_BWD;
+  uint2 pa[2][BWD ? 16 : 1], pb[2][SW ? 16 : 1];
+  auto aux_load = [&](int ii, uint2* da_, uint2* db_) __attribute__((always_inline)) {
+    const int64_t n = t.n0 + wn0 + 4 * lr;
+    const int64_t nc = n < p.N ? n : p.N - 4;
+    static_for<16>([&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      int64_t m = t.m0 + wm0 + 32 * ii + 2 * q + lh;
+      m = m < t.M ? m : t.M - 1;
+      da_[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + nc);
+      if (SW) db_[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + p.fdim + nc);
+    });
+  };
+  if (BWD) aux_load(0, pa[0], pb[0]);
   static_for<MI>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
+    if (BWD && i + 1 < MI) aux_load(i + 1, pa[(i + 1) & 1], pb[(i + 1) & 1]);
     static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
       constexpr int j = decltype(Q)::value / 4, g = decltype(Q)::value % 4;
       const int sl = 8 * j + 2 * g + lh;
@@ -307,23 +327,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         store4_bf16(ab + m * p.ldaux + p.fdim + hc, b);
       });
     } else {
-      constexpr bool BWD = EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD;
-      constexpr bool SW = EPI == EPI_SWIGLU_BWD;
       const int64_t n = t.n0 + wn0 + 4 * lr;
       const bool nok = n < p.N;
-      // backward: this block row's saved pre-activations, all loads issued
-      // before any math (rows/columns clamped into range when out)
-      uint2 ra[BWD ? 16 : 1], rb[SW ? 16 : 1];
-      if (BWD) {
-        const int64_t nc = nok ? n : p.N - 4;
-        static_for<16>([&](auto Q) __attribute__((always_inline)) {
-          constexpr int q = decltype(Q)::value;
-          int64_t m = mrow0 + 2 * q + lh;
-          m = m < t.M ? m : t.M - 1;
-          ra[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + nc);
-          if (SW) rb[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + p.fdim + nc);
-        });
-      }
+      const uint2* ra = pa[i & 1];
+      const uint2* rb = pb[i & 1];
       static_for<16>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
         const int r = 2 * q + lh;
