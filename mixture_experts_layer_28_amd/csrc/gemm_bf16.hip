@@ -102,11 +102,13 @@ __device__ __forceinline__ void dma_src(DmaSrc& d, int64_t ld, int64_t rows_vali
   }
 }
 
-__device__ __forceinline__ void unpack4_bf16(uint2 w, float* v) {
-  v[0] = bf2f(w.x & 0xffffu);
-  v[1] = bf2f(w.x >> 16);
-  v[2] = bf2f(w.y & 0xffffu);
-  v[3] = bf2f(w.y >> 16);
+__device__ __forceinline__ void unpack8_bf16(uint4 w, float* v) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf2f(u[e] & 0xffffu);
+    v[2 * e + 1] = bf2f(u[e] >> 16);
+  }
 }
 
 
@@ -260,30 +262,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- epilogue: per 32-row block row i, the wave stages its 32 x 128 fp32
   // results in a stage of its own (one 16-byte write per (j, g): the four
   // consecutive columns the transposed accumulators hold), then reads them
-  // back row-contiguous: lane l takes 16-byte slot l&31 of row 2q + (l>>5),
-  // so every global access of an instruction covers two whole 256-byte rows.
-  // Slot s of row r sits at r*512 + ((s ^ (r & 7)) << 4).
+  // back row-contiguous, two adjacent 16-byte slots (8 columns) per lane, and
+  // stores 16 bytes of bf16 per lane per output. Slot s of staged row r sits
+  // at r*512 + ((s ^ (r & 7)) << 4); the two rows a 16-lane group reads take
+  // slots of opposite parity, so the readback is conflict-free.
+  // N and every leading dimension are multiples of 8, so an 8-column segment
+  // is wholly inside or wholly outside the output.
   char* stg = reinterpret_cast<char*>(st0) + wave * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
   const int lr = lane & 31, lh = lane >> 5;
+  // plain / GELU / backward epilogues: lane l takes slots 2s, 2s+1 (s = l&15)
+  // of row 4q + (l>>4), q = 0..7
+  const int s8 = lane & 15, rq = lane >> 4;
+  const int64_t n8 = t.n0 + wn0 + 8 * s8;
   // Backward epilogues read this lane's saved pre-activations (a, and b for
   // SwiGLU) of each block row: the loads of block row i+1 are issued when
   // block row i starts, so they overlap its staging, math and stores
   // (rows/columns clamped into range when out).
   constexpr bool BWD = EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD;
   constexpr bool SW = EPI == EPI_SWIGLU_BWD;
-  uint2 pa[2][BWD ? 16 : 1], pb[2][SW ? 16 : 1];
-  auto aux_load = [&](int ii, uint2* da_, uint2* db_) __attribute__((always_inline)) {
-    const int64_t n = t.n0 + wn0 + 4 * lr;
-    const int64_t nc = n < p.N ? n : p.N - 4;
-    static_for<16>([&](auto Q) __attribute__((always_inline)) {
+  uint4 pa[2][BWD ? 8 : 1], pb[2][SW ? 8 : 1];
+  auto aux_load = [&](int ii, uint4* da_, uint4* db_) __attribute__((always_inline)) {
+    const int64_t nc = n8 < p.N ? n8 : p.N - 8;
+    static_for<8>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
-      int64_t m = t.m0 + wm0 + 32 * ii + 2 * q + lh;
+      int64_t m = t.m0 + wm0 + 32 * ii + 4 * q + rq;
       m = m < t.M ? m : t.M - 1;
-      da_[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + nc);
-      if (SW) db_[q] = *reinterpret_cast<const uint2*>(ab + m * p.ldaux + p.fdim + nc);
+      da_[q] = *reinterpret_cast<const uint4*>(ab + m * p.ldaux + nc);
+      if (SW) db_[q] = *reinterpret_cast<const uint4*>(ab + m * p.ldaux + p.fdim + nc);
     });
   };
   if (BWD) aux_load(0, pa[0], pb[0]);
@@ -303,67 +311,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
     const int64_t mrow0 = t.m0 + wm0 + 32 * i;
+    auto ld8 = [&](int r, int slot, float* v) __attribute__((always_inline)) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((slot ^ (r & 7)) << 4));
+      const f32x4 y = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((slot + 1) ^ (r & 7)) << 4));
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+      v[4] = y[0]; v[5] = y[1]; v[6] = y[2]; v[7] = y[3];
+    };
     if (EPI == EPI_SWIGLU_FWD) {
       // slots 0..15 hold gate columns, 16..31 the matching up columns: lane l
-      // takes gate slot l&15 and up slot (l&15)+16 of row 4q + (l>>4)
-      const int sg = lane & 15, rr = lane >> 4;
-      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+      // takes gate slots 2(l&7), +1 and the up slots 16 above them, of row
+      // 8q + (l>>3), q = 0..3
+      const int sg = lane & 7, rr = lane >> 3;
+      const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 8 * sg;
+      static_for<4>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
-        const int r = 4 * q + rr;
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((sg ^ (r & 7)) << 4));
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((sg + 16) ^ (r & 7)) << 4));
+        const int r = 8 * q + rr;
+        float a[8], b[8], h[8];
+        ld8(r, 2 * sg, a);
+        ld8(r, 16 + 2 * sg, b);
         const int64_t m = mrow0 + r;
-        const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 4 * sg;
         if (m >= t.M || hc >= p.N) return;
-        float a[4], b[4], h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = a4[e];
-          b[e] = b4[e];
-          h[e] = silu_f(a[e]) * b[e];
-        }
-        store4_bf16(cb + m * p.ldc + hc, h);
-        store4_bf16(ab + m * p.ldaux + hc, a);
-        store4_bf16(ab + m * p.ldaux + p.fdim + hc, b);
+        for (int e = 0; e < 8; ++e) h[e] = silu_f(a[e]) * b[e];
+        Vec8<bf16_t>::store(cb + m * p.ldc + hc, h);
+        Vec8<bf16_t>::store(ab + m * p.ldaux + hc, a);
+        Vec8<bf16_t>::store(ab + m * p.ldaux + p.fdim + hc, b);
       });
     } else {
-      const int64_t n = t.n0 + wn0 + 4 * lr;
-      const bool nok = n < p.N;
-      const uint2* ra = pa[i & 1];
-      const uint2* rb = pb[i & 1];
-      static_for<16>([&](auto Q) __attribute__((always_inline)) {
+      const bool nok = n8 < p.N;
+      const uint4* ra = pa[i & 1];
+      const uint4* rb = pb[i & 1];
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
-        const int r = 2 * q + lh;
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((lr ^ (r & 7)) << 4));
+        const int r = 4 * q + rq;
+        float v[8], o[8];
+        ld8(r, 2 * s8, v);
         const int64_t m = mrow0 + r;
         if (m >= t.M || !nok) return;
-        float v[4], o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = v4[e];
         if (EPI == EPI_STORE) {
-          store4_bf16(cb + m * p.ldc + n, v);
+          Vec8<bf16_t>::store(cb + m * p.ldc + n8, v);
         } else if (EPI == EPI_GELU_FWD) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = gelu_f(v[e]);
-          store4_bf16(cb + m * p.ldc + n, o);
-          store4_bf16(ab + m * p.ldaux + n, v);
+          for (int e = 0; e < 8; ++e) o[e] = gelu_f(v[e]);
+          Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
+          Vec8<bf16_t>::store(ab + m * p.ldaux + n8, v);
         } else {
-          float a[4];
-          unpack4_bf16(ra[BWD ? q : 0], a);
+          float a[8];
+          unpack8_bf16(ra[BWD ? q : 0], a);
           if (SW) {
-            float b[4], o2[4];
-            unpack4_bf16(rb[SW ? q : 0], b);
+            float b[8], o2[8];
+            unpack8_bf16(rb[SW ? q : 0], b);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 8; ++e) {
               o[e] = v[e] * b[e] * dsilu_f(a[e]);
               o2[e] = v[e] * silu_f(a[e]);
             }
-            store4_bf16(cb + m * p.ldc + n, o);
-            store4_bf16(cb + m * p.ldc + p.fdim + n, o2);
+            Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
+            Vec8<bf16_t>::store(cb + m * p.ldc + p.fdim + n8, o2);
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = v[e] * dgelu_f(a[e]);
-            store4_bf16(cb + m * p.ldc + n, o);
+            for (int e = 0; e < 8; ++e) o[e] = v[e] * dgelu_f(a[e]);
+            Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
           }
         }
       });
