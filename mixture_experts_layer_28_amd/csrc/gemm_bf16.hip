@@ -44,9 +44,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous tile of
-// 128-byte rows (64 bf16): conflict-free for 16-lane groups reading one chunk
-__device__ __forceinline__ int kc2_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 // byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [64][kRows] tile
 __device__ __forceinline__ int ks_off(int k, int s) {
   return k * (kRows * 2) + ((s ^ ((k & 3) << 1)) << 4);
@@ -183,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // fragment of 32 rows (base .. base+31) for k slice sl (0..3) of a stage tile
   auto frag = [&](const bf16_t* tile, bool kc, int base, int sl) __attribute__((always_inline)) -> bf16x8 {
     const char* tb = reinterpret_cast<const char*>(tile);
-    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc2_off(base + (lane & 31), sl * 2 + (lane >> 5)));
+    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc_off(base + (lane & 31), sl * 2 + (lane >> 5)));
     const int g = lane >> 4, i = lane & 15;
     const int row = base + 16 * (g & 1) + 4 * (i & 3);
     const int k = 16 * sl + 8 * (g >> 1) + (i >> 2);

@@ -61,8 +61,6 @@ __device__ __forceinline__ void dma_src8(Dma8& d, int64_t ld, int64_t rows_valid
   }
 }
 
-// byte offset of 16-byte chunk c (0..7) of row r in a tile of 128-byte rows
-__device__ __forceinline__ int kc8_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
   v8i32 v;
@@ -128,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // half `part` of the fragment of rows base .. base+31 for slice sl
   auto frag = [&](const char* tile, int base, int sl, int part) __attribute__((always_inline)) -> int4 {
-    return *reinterpret_cast<const int4*>(tile + kc8_off(base + (lane & 31), 4 * sl + 2 * part + (lane >> 5)));
+    return *reinterpret_cast<const int4*>(tile + kc_off(base + (lane & 31), 4 * sl + 2 * part + (lane >> 5)));
   };
 
   int4 xa[MI][2], xb[NI][2], ya[MI][2], yb[NI][2];
@@ -195,8 +193,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- epilogue: stage each 32-row block row in fp32 (a stage per wave),
-  // read it back row-contiguous, scale by 2^(a_sexp + b_sexp), store bf16.
-  // Slot s of staged row r sits at r*512 + ((s ^ (r & 7)) << 4).
+  // read it back row-contiguous 8 columns per lane, scale by
+  // 2^(a_sexp + b_sexp), store 16 bytes of bf16 per lane per output.
+  // Slot s of staged row r sits at r*512 + ((s ^ (r & 7)) << 4); the two rows
+  // a 16-lane group reads take slots of opposite parity (conflict-free).
   char* stg = st0 + wave * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
@@ -222,54 +222,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // lane lr holds the scale exponent of row mrow0 + lr (clamped into range)
     const int64_t mcl = mrow0 + lr < t.M ? mrow0 + lr : t.M - 1;
     const int ea_l = asx[mcl];
+    // 8 consecutive staged columns (slots slot, slot+1) of row r
+    auto ld8 = [&](int r, int slot, float* v) __attribute__((always_inline)) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((slot ^ (r & 7)) << 4));
+      const f32x4 y = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((slot + 1) ^ (r & 7)) << 4));
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+      v[4] = y[0]; v[5] = y[1]; v[6] = y[2]; v[7] = y[3];
+    };
+    auto ld_exp8 = [&](const int32_t* e, int* out) __attribute__((always_inline)) {
+      const int4 x = *reinterpret_cast<const int4*>(e);
+      const int4 y = *reinterpret_cast<const int4*>(e + 4);
+      out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+      out[4] = y.x; out[5] = y.y; out[6] = y.z; out[7] = y.w;
+    };
     if (EPI == EPI_SWIGLU_FWD) {
-      const int sg = lane & 15, rr = lane >> 4;
-      const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 4 * sg;
-      const int64_t hcl = hc < p.N ? hc : p.N - 4;
-      const int4 eg = *reinterpret_cast<const int4*>(bsx + hcl);
-      const int4 eu = *reinterpret_cast<const int4*>(bsx + p.fdim + hcl);
-      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+      // lane l: gate slots 2(l&7), +1 and the up slots 16 above, of row 8q + (l>>3)
+      const int sg = lane & 7, rr = lane >> 3;
+      const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 8 * sg;
+      const int64_t hcl = hc < p.N ? hc : p.N - 8;
+      int egs[8], eus[8];
+      ld_exp8(bsx + hcl, egs);
+      ld_exp8(bsx + p.fdim + hcl, eus);
+      static_for<4>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
-        const int r = 4 * q + rr;
+        const int r = 8 * q + rr;
         const int ea = __shfl(ea_l, r, 64);
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((sg ^ (r & 7)) << 4));
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + (((sg + 16) ^ (r & 7)) << 4));
+        float a[8], b[8], h[8];
+        ld8(r, 2 * sg, a);
+        ld8(r, 16 + 2 * sg, b);
         const int64_t m = mrow0 + r;
         if (m >= t.M || hc >= p.N) return;
-        const int egs[4] = {eg.x, eg.y, eg.z, eg.w}, eus[4] = {eu.x, eu.y, eu.z, eu.w};
-        float a[4], b[4], h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = ldexpf(a4[e], ea + egs[e]);
-          b[e] = ldexpf(b4[e], ea + eus[e]);
+        for (int e = 0; e < 8; ++e) {
+          a[e] = ldexpf(a[e], ea + egs[e]);
+          b[e] = ldexpf(b[e], ea + eus[e]);
           h[e] = silu_f(a[e]) * b[e];
         }
-        store4_bf16(cb + m * p.ldc + hc, h);
-        store4_bf16(ab + m * p.ldaux + hc, a);
-        store4_bf16(ab + m * p.ldaux + p.fdim + hc, b);
+        Vec8<bf16_t>::store(cb + m * p.ldc + hc, h);
+        Vec8<bf16_t>::store(ab + m * p.ldaux + hc, a);
+        Vec8<bf16_t>::store(ab + m * p.ldaux + p.fdim + hc, b);
       });
     } else {
-      const int64_t n = t.n0 + wn0 + 4 * lr;
+      // lane l: slots 2(l&15), +1 of row 4q + (l>>4)
+      const int s8 = lane & 15, rq = lane >> 4;
+      const int64_t n = t.n0 + wn0 + 8 * s8;
       const bool nok = n < p.N;
-      const int4 eb4 = *reinterpret_cast<const int4*>(bsx + (nok ? n : p.N - 4));
-      const int ebs[4] = {eb4.x, eb4.y, eb4.z, eb4.w};
-      static_for<16>([&](auto Q) __attribute__((always_inline)) {
+      int ebs[8];
+      ld_exp8(bsx + (nok ? n : p.N - 8), ebs);
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
-        const int r = 2 * q + lh;
+        const int r = 4 * q + rq;
         const int ea = __shfl(ea_l, r, 64);
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((lr ^ (r & 7)) << 4));
+        float v[8], o[8];
+        ld8(r, 2 * s8, v);
         const int64_t m = mrow0 + r;
         if (m >= t.M || !nok) return;
-        float v[4], o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = ldexpf(v4[e], ea + ebs[e]);
+        for (int e = 0; e < 8; ++e) v[e] = ldexpf(v[e], ea + ebs[e]);
         if (EPI == EPI_STORE) {
-          store4_bf16(cb + m * p.ldc + n, v);
+          Vec8<bf16_t>::store(cb + m * p.ldc + n, v);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = gelu_f(v[e]);
-          store4_bf16(cb + m * p.ldc + n, o);
-          store4_bf16(ab + m * p.ldaux + n, v);
+          for (int e = 0; e < 8; ++e) o[e] = gelu_f(v[e]);
+          Vec8<bf16_t>::store(cb + m * p.ldc + n, o);
+          Vec8<bf16_t>::store(ab + m * p.ldaux + n, v);
         }
       });
     }

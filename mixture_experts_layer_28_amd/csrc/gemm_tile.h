@@ -21,9 +21,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr uint32_t kOOB = 0x80000000u;    // byte offset beyond any buffer extent
 
-// byte offset of 16-byte chunk c (0..3) of row r in a K-contiguous tile of
-// 64-byte rows (32 bf16 or 64 fp8 per row); conflict-free fragment reads
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous tile of
+// 128-byte rows (64 bf16 or 128 fp8 per row): a 16-lane group reading one
+// chunk of 16 consecutive rows covers all 64 LDS banks
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // raw buffer resource over [base, base + bytes)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -38,14 +39,6 @@ __device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t
   const int64_t col = n0h + wc * half + (up ? w - half : w);
   if (col >= fdim) return -1;
   return up ? fdim + col : col;
-}
-
-// four floats -> four bf16 (round to nearest even) in one 8-byte store
-__device__ __forceinline__ void store4_bf16(bf16_t* dst, const float* v) {
-  uint2 w;
-  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  *reinterpret_cast<uint2*>(dst) = w;
 }
 
 template <int N>
