@@ -6,20 +6,26 @@
 // owns a 128 x 128 sub-tile of 32x32 MFMA blocks whose accumulators fill the
 // AGPR file.
 //
-// Operands stream through two LDS stages of 64 k each (64 KiB: 32 KiB per
-// operand tile), filled by buffer_load ... lds (global -> LDS with no staging
-// registers). A K-contiguous operand row is then 128 bytes of global memory,
-// a whole cache line: measured on gfx950, DMA of 128-byte row pieces feeds a
-// CU about 1.65x faster than 64-byte pieces (the 32-k stages of a deeper ring
-// lost more to that than the ring's depth won).
+// Operands stream through a ring of five 32 KiB LDS buffers, each holding one
+// operand's 64-k tile (the whole 160 KiB of a CU), filled by
+// buffer_load ... lds (global -> LDS with no staging registers). A
+// K-contiguous operand row is 128 bytes of global memory, a whole cache line:
+// measured on gfx950, DMA of 128-byte row pieces feeds a CU about 1.65x
+// faster than 64-byte pieces. Operand X of k-step k lives in buffer
+// (2k + X) mod 5 (A = 0, B = 1), so each tile reuses the buffer of the one
+// five places earlier in the sequence A0 B0 A1 B1 ...; B tiles are loaded one
+// k-step ahead and A tiles two, one DMA instruction per four MFMAs.
 // Per k-step (4 slices of 16 k, 16 MFMAs each, with the next slice's
 // fragments read between the MFMAs of the current one):
-//   slice 0: the second half of k-step kt+1's loads into the other stage;
-//   slices 1, 2;
-//   wait for k-step kt+1's loads, barrier: every read of this stage has been
-//   issued and waited for, and the other stage is complete;
+//   slice 0: the second half of B_{kt+1};
+//   slices 1, 2: A_{kt+2};
+//   wait for A_{kt+1} and B_{kt+1} (A_{kt+2} may stay in flight), barrier:
+//   every read of A_kt and B_kt has been issued and waited for;
 //   slice 3: reads k-step kt+1's slice-0 fragments and issues the first half
-//   of k-step kt+2's loads into this stage.
+//   of B_{kt+2} into A_kt's buffer.
+// Five k-steps per loop trip name their buffers statically; the last
+// nk mod 5 k-steps run after the loop (exits inside the unrolled trip made
+// the register allocator spill).
 //
 // LDS layouts (bank-conflict free for the fragment reads):
 //   K-contiguous operand, [rows][64] bf16 (128-byte rows): 16-byte chunk c of
@@ -125,15 +131,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NLD = 16;                       // DMA instructions per wave per stage
   static_assert(!FUSED || BKM, "fused SwiGLU needs a K-contiguous weight");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
-  // Two stages of 64 KiB, separate objects so that the compiler can tell the
-  // stage being filled by DMA from the stage being read.
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[ST];
-  __shared__ __attribute__((aligned(1024))) bf16_t st1[ST];
+  // Five 32 KiB buffers, each holding one operand's 64-k tile; separate
+  // objects so that the compiler can tell a buffer being filled from one read.
+  __shared__ __attribute__((aligned(1024))) bf16_t h0[A_EL];
+  __shared__ __attribute__((aligned(1024))) bf16_t h1[A_EL];
+  __shared__ __attribute__((aligned(1024))) bf16_t h2[A_EL];
+  __shared__ __attribute__((aligned(1024))) bf16_t h3[A_EL];
+  __shared__ __attribute__((aligned(1024))) bf16_t h4[A_EL];
 
   Tile t;
   {
     // the group-tile scan runs before any load and borrows the last stage
-    int* s_tiles = reinterpret_cast<int*>(st1);
+    int* s_tiles = reinterpret_cast<int*>(h4);
     const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
     __syncthreads();
     if (!have) return;
@@ -162,22 +171,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int64_t nk = (t.K + kBK - 1) / kBK;
 
-  // DMA instruction q (0..15: A blocks then B blocks) of k-step kt into stage s
-  auto dma = [&](int64_t kt, bf16_t* s, int q) __attribute__((always_inline)) {
+  // DMA instruction i (0..7) of operand X (0 = A, 1 = B) of k-step kt into buffer s
+  auto dma = [&](int64_t kt, int X, bf16_t* s, int i) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK;
-    const bool isA = q < 8;
-    const int i = q & 7;
+    const bool isA = X == 0;
     const DmaSrc& d = isA ? da : db;
     const bool kc = isA ? AKM : BKM;
     const int64_t ld = isA ? p.a.ld : p.b.ld;
     const bool kin = d.kk[i] < t.K - k0;
     const uint32_t so = (uint32_t)(kc ? k0 * 2 : k0 * ld * 2);
-    bf16_t* tile = isA ? s : s + A_EL;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 8 + i) * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(s + (wave * 8 + i) * 512), 16,
                                              kin ? d.off[i] : kOOB, so, 0, 0);
   };
 
-  // fragment of 32 rows (base .. base+31) for k slice sl (0..3) of a stage tile
+  // fragment of 32 rows (base .. base+31) for k slice sl (0..3) of an operand tile
   auto frag = [&](const bf16_t* tile, bool kc, int base, int sl) __attribute__((always_inline)) -> bf16x8 {
     const char* tb = reinterpret_cast<const char*>(tile);
     if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc_off(base + (lane & 31), sl * 2 + (lane >> 5)));
@@ -192,65 +199,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   bf16x8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
-  auto ldfrag_q = [&](bf16x8* fa, bf16x8* fb, const bf16_t* s, int sl, int q) __attribute__((always_inline)) {
-    if (q < MI) fa[q] = frag(s, AKM, wm0 + q * 32, sl);
-    else fb[q - MI] = frag(s + A_EL, BKM, wn0 + (q - MI) * 32, sl);
+  auto ldfrag_q = [&](bf16x8* fa, bf16x8* fb, const bf16_t* sa, const bf16_t* sb, int sl, int q)
+      __attribute__((always_inline)) {
+    if (q < MI) fa[q] = frag(sa, AKM, wm0 + q * 32, sl);
+    else fb[q - MI] = frag(sb, BKM, wn0 + (q - MI) * 32, sl);
   };
-  // Each block is accumulated transposed (B fragment as the MFMA's first
-  // operand), so lane l holds row wm0+32i+(l&31) and, in acc[i][j][4g..4g+3],
-  // the four consecutive columns wn0+32j+8g+4(l>>5) .. +3.
   auto mma = [&](const bf16x8* fa, const bf16x8* fb, int q) __attribute__((always_inline)) {
     const int i = q / NI, j = q % NI;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
-  // One slice of 16 MFMAs on fragment set (fa, fb), reading the fragments of
-  // slice rsl of stage rs into (ga, gb) between them, and, when dk >= 0, the
-  // DMA instructions dq0 .. dq0+7 of k-step dk into stage ds (one per two MFMAs).
-  auto slice = [&](const bf16x8* fa, const bf16x8* fb, bf16x8* ga, bf16x8* gb, const bf16_t* rs,
-                   int rsl, int64_t dk, bf16_t* ds, int dq0) __attribute__((always_inline)) {
+  // 16 MFMAs on (fa, fb), reading slice rsl of (rsa, rsb) into (ga, gb)
+  // between them, and DMA instructions i0 .. i0+3 of operand X of k-step dk
+  // into buffer ds (one per four MFMAs)
+  auto slice = [&](const bf16x8* fa, const bf16x8* fb, bf16x8* ga, bf16x8* gb, const bf16_t* rsa,
+                   const bf16_t* rsb, int rsl, int64_t dk, int X, bf16_t* ds, int i0)
+      __attribute__((always_inline)) {
     static_for<NM>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
       mma(fa, fb, q);
       __builtin_amdgcn_sched_barrier(0);
-      if (q < MI + NI) ldfrag_q(ga, gb, rs, rsl, q);
-      if (dk >= 0 && (q & 1)) dma(dk, ds, dq0 + (q >> 1));
+      if (q < MI + NI) ldfrag_q(ga, gb, rsa, rsb, rsl, q);
+      if ((q & 3) == 3) dma(dk, X, ds, i0 + (q >> 2));
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
-  // k-step kt on stage cur (its slice-0 fragments already in fa0/fb0); the
-  // first half of k-step kt+1's loads into nxt was issued during the previous
-  // k-step. After slice 2 every read of cur has been issued and waited for,
-  // so the barrier that also publishes nxt frees cur for k-step kt+2.
-  auto kstep = [&](int64_t kt, bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
+  // Buffer of operand X of k-step k: (2k + X) mod 5, so an operand tile reuses
+  // the buffer of the one five places earlier in the sequence A0 B0 A1 B1 ...
+  // k-step kt (its slice-0 fragments already in fa0/fb0; A_{kt+1} and the
+  // first half of B_{kt+1} in flight since the previous k-step):
+  //   slice 0: second half of B_{kt+1} (into A_{kt-1}'s old buffer);
+  //   slices 1, 2: A_{kt+2} (into B_{kt-1}'s old buffer);
+  //   wait for A_{kt+1}, B_{kt+1} (only A_{kt+2} may stay in flight), barrier:
+  //   every read of A_kt and B_kt is done;
+  //   slice 3: reads k-step kt+1's slice-0 fragments and issues the first half
+  //   of B_{kt+2} into A_kt's buffer.
+  // B tiles have one k-step to land, A tiles two; one DMA per four MFMAs.
+  auto kstep = [&](int64_t kt, bf16_t* a0, bf16_t* b0, bf16_t* a1, bf16_t* b1, bf16_t* a2,
+                   bf16_t* b2) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    slice(fa0, fb0, fa1, fb1, cur, 1, kt + 1, nxt, NLD / 2);
-    slice(fa1, fb1, fa0, fb0, cur, 2, -1, nxt, 0);
-    slice(fa0, fb0, fa1, fb1, cur, 3, -1, nxt, 0);
-    wait_vm<0>();
+    slice(fa0, fb0, fa1, fb1, a0, b0, 1, kt + 1, 1, b1, 4);
+    slice(fa1, fb1, fa0, fb0, a0, b0, 2, kt + 2, 0, a2, 0);
+    slice(fa0, fb0, fa1, fb1, a0, b0, 3, kt + 2, 0, a2, 4);
+    wait_vm<8>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    slice(fa1, fb1, fa0, fb0, nxt, 0, kt + 2, cur, 0);
+    slice(fa1, fb1, fa0, fb0, a1, b1, 0, kt + 2, 1, b2, 0);
   };
 
   if (nk > 0) {
+    // as if just after the barrier of k-step -1: A0, B0, A1 and half of B1
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(0, st0, q);
-    wait_vm<0>();
+    for (int i = 0; i < 8; ++i) dma(0, 0, h0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(0, 1, h1, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(1, 0, h2, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma(1, 1, h3, i);
+    wait_vm<12>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, st0, 0, q);
-#pragma unroll
-    for (int q = 0; q < NLD / 2; ++q) dma(1, st1, q);
-    // two k-steps per trip name their stages statically (one extra k-step at
-    // the end multiplies the zeros its out-of-range loads left)
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-      kstep(kt, st0, st1);
-      kstep(kt + 1, st1, st0);
+    for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, h0, h1, 0, q);
+    // five k-steps per trip name their buffers statically; the trip stops at
+    // the last k-step (loads past the end read zeros and are waited for below)
+    int64_t kt = 0;
+    for (; kt + 5 <= nk; kt += 5) {
+      kstep(kt, h0, h1, h2, h3, h4, h0);
+      kstep(kt + 1, h2, h3, h4, h0, h1, h2);
+      kstep(kt + 2, h4, h0, h1, h2, h3, h4);
+      kstep(kt + 3, h1, h2, h3, h4, h0, h1);
+      kstep(kt + 4, h3, h4, h0, h1, h2, h3);
     }
-    // every load (including those past the end) must land before the stages are reused
+    // the last nk mod 5 k-steps (buffer phase continues from 0)
+    if (kt < nk) kstep(kt, h0, h1, h2, h3, h4, h0);
+    if (kt + 1 < nk) kstep(kt + 1, h2, h3, h4, h0, h1, h2);
+    if (kt + 2 < nk) kstep(kt + 2, h4, h0, h1, h2, h3, h4);
+    if (kt + 3 < nk) kstep(kt + 3, h1, h2, h3, h4, h0, h1);
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -265,7 +292,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // slots of opposite parity, so the readback is conflict-free.
   // N and every leading dimension are multiples of 8, so an 8-column segment
   // is wholly inside or wholly outside the output.
-  char* stg = reinterpret_cast<char*>(st0) + wave * 16384;
+  char* stg = reinterpret_cast<char*>(wave < 2 ? h0 : h1) + (wave & 1) * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
