@@ -8,19 +8,22 @@
 // Workgroup: 256 threads = 4 waves in a 2x2 grid; tile 256 x 256; each wave
 // owns 128 x 128 as 4 x 4 MFMA blocks of 32 x 32 held in AGPRs.
 //
-// Two LDS stages of 128 k: 2 x 256 rows x 128 bytes = 64 KiB each, so every
-// DMA row piece is a whole 128-byte line (the bf16 GEMM's layout: chunk c of
-// row r at r*128 + ((c ^ ((r >> 1) & 7)) << 4), 16 fp8 per chunk). A k-step
-// is two slices of 64 k, one MFMA per 32 x 32 block each. The matrix core
-// takes from lane l (row l & 31, half h = l >> 5) 32 bytes: k 16h .. 16h+15
-// of its 64-k slice in the first 16 bytes and k 32+16h .. 32+16h+15 in the
-// next 16 (measured on gfx950), so a fragment of slice sl is chunks 4sl+h
-// and 4sl+2+h of its row.
-// Per k-step: slice 0 (slice 1's fragments read between the MFMAs); wait for
-// k-step kt+1, barrier (every read of this stage is done); slice 1 (k-step
-// kt+1's slice-0 fragments read, and all of k-step kt+2's loads issued into
-// this stage, one per MFMA, so they have a whole k-step to land: measured
-// 10-29% faster than splitting them across the two slices).
+// LDS is a ring of five 32 KiB buffers, each holding one operand's 128-k
+// tile: 256 rows x 128 bytes, whole 128-byte lines per DMA row piece, in the
+// bf16 GEMM's layout (chunk c of row r at r*128 + ((c ^ ((r >> 1) & 7)) << 4),
+// 16 fp8 per chunk). Operand X of k-step k (A = 0, B = 1) lives in buffer
+// (2k + X) mod 5, reusing the buffer of the tile five places earlier in the
+// sequence A0 B0 A1 B1 .... A k-step is two slices of 64 k, one MFMA per
+// 32 x 32 block each. The matrix core takes from lane l (row l & 31, half
+// h = l >> 5) 32 bytes: k 16h .. 16h+15 of its 64-k slice in the first 16
+// bytes and k 32+16h .. 32+16h+15 in the next 16 (measured on gfx950), so a
+// fragment of slice sl is chunks 4sl+h and 4sl+2+h of its row.
+// Per k-step: slice 0 (slice 1's fragments read between the MFMAs; A_{kt+2}
+// issued into B_{kt-1}'s old buffer); wait for A_{kt+1} and B_{kt+1}
+// (A_{kt+2} may stay in flight), barrier (every read of A_kt and B_kt is
+// done); slice 1 (k-step kt+1's slice-0 fragments read; B_{kt+2} issued into
+// A_kt's buffer). A tiles have three slices to land, B tiles two; one DMA
+// instruction per two MFMAs.
 #include "gemm_tile.h"
 
 namespace moe {
@@ -76,15 +79,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr bool FUSED = EPI == EPI_SWIGLU_FWD;
   constexpr int BNo = FUSED ? BN / 2 : BN;
   constexpr int A_B = BM * kBK8, B_B = BN * kBK8;   // bytes per stage of each tile
-  constexpr int ST = A_B + B_B;
-  constexpr int NLD = 16;                           // DMA instructions per wave per stage
+  static_assert(A_B == B_B, "ring buffers hold either operand");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
-  __shared__ __attribute__((aligned(1024))) char st0[ST];
-  __shared__ __attribute__((aligned(1024))) char st1[ST];
+  __shared__ __attribute__((aligned(1024))) char h0[A_B];
+  __shared__ __attribute__((aligned(1024))) char h1[A_B];
+  __shared__ __attribute__((aligned(1024))) char h2[A_B];
+  __shared__ __attribute__((aligned(1024))) char h3[A_B];
+  __shared__ __attribute__((aligned(1024))) char h4[A_B];
 
   Tile t;
   {
-    int* s_tiles = reinterpret_cast<int*>(st1);
+    int* s_tiles = reinterpret_cast<int*>(h4);
     const bool have = resolve_tile<BM, BNo, RAG>(p, s_tiles, s_tiles + 1028, t);
     __syncthreads();
     if (!have) return;
@@ -112,15 +117,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int64_t nk = (t.K + kBK8 - 1) / kBK8;
 
-  // DMA instruction q (0..15: A blocks then B blocks) of k-step kt into stage s
-  auto dma = [&](int64_t kt, char* s, int q) __attribute__((always_inline)) {
+  // DMA instruction i (0..7) of operand X (0 = A, 1 = B) of k-step kt into buffer s
+  auto dma = [&](int64_t kt, int X, char* s, int i) __attribute__((always_inline)) {
     const int64_t k0 = kt * kBK8;
-    const bool isA = q < 8;
-    const int i = q & 7;
-    const Dma8& d = isA ? da : db;
+    const Dma8& d = X == 0 ? da : db;
     const bool kin = d.kk[i] < t.K - k0;
-    char* tile = isA ? s : s + A_B;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? ra : rb, (lds_void*)(tile + (wave * 8 + i) * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? ra : rb, (lds_void*)(s + (wave * 8 + i) * 1024), 16,
                                              kin ? d.off[i] : kOOB, (uint32_t)k0, 0, 0);
   };
 
@@ -130,11 +132,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   int4 xa[MI][2], xb[NI][2], ya[MI][2], yb[NI][2];
-  // read half `part` of fragment q (0..3: A blocks, 4..7: B blocks) of slice sl of stage s
-  auto ldfrag = [&](int4 (*fa)[2], int4 (*fb)[2], const char* s, int sl, int q, int part)
-      __attribute__((always_inline)) {
-    if (q < MI) fa[q][part] = frag(s, wm0 + q * 32, sl, part);
-    else fb[q - MI][part] = frag(s + A_B, wn0 + (q - MI) * 32, sl, part);
+  // read half `part` of fragment q (0..3: A blocks, 4..7: B blocks) of slice sl of (sa, sb)
+  auto ldfrag = [&](int4 (*fa)[2], int4 (*fb)[2], const char* sa, const char* sb, int sl, int q,
+                    int part) __attribute__((always_inline)) {
+    if (q < MI) fa[q][part] = frag(sa, wm0 + q * 32, sl, part);
+    else fb[q - MI][part] = frag(sb, wn0 + (q - MI) * 32, sl, part);
   };
   // Transposed accumulation (B fragment first): lane l holds row
   // wm0+32i+(l&31) and, in acc[i][j][4g..4g+3], columns wn0+32j+8g+4(l>>5)+0..3.
@@ -145,48 +147,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
   };
 
-  // 16 MFMAs on (fa, fb), reading slice rsl of stage rs into (ga, gb) between
-  // them and, when dk >= 0, issuing k-step dk's 16 DMA instructions into ds
-  auto slice = [&](int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2], const char* rs,
-                   int rsl, int64_t dk, char* ds) __attribute__((always_inline)) {
+  // 16 MFMAs on (fa, fb), reading slice rsl of (rsa, rsb) into (ga, gb)
+  // between them and issuing operand X of k-step dk into ds, one DMA per two
+  auto slice = [&](int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2], const char* rsa,
+                   const char* rsb, int rsl, int64_t dk, int X, char* ds) __attribute__((always_inline)) {
     static_for<NM>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
       mma(fa, fb, q);
       __builtin_amdgcn_sched_barrier(0);
-      ldfrag(ga, gb, rs, rsl, q >> 1, q & 1);
-      if (dk >= 0) dma(dk, ds, q);
+      ldfrag(ga, gb, rsa, rsb, rsl, q >> 1, q & 1);
+      if (q & 1) dma(dk, X, ds, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
-  auto kstep = [&](int64_t kt, char* cur, char* nxt) __attribute__((always_inline)) {
+  auto kstep = [&](int64_t kt, char* a0, char* b0, char* a1, char* b1, char* a2, char* b2)
+      __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    slice(xa, xb, ya, yb, cur, 1, -1, nxt);
-    wait_vm<0>();
+    slice(xa, xb, ya, yb, a0, b0, 1, kt + 2, 0, a2);
+    wait_vm<8>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    slice(ya, yb, xa, xb, nxt, 0, kt + 2, cur);
+    slice(ya, yb, xa, xb, a1, b1, 0, kt + 2, 1, b2);
   };
 
   if (nk > 0) {
+    // as if just before k-step 0: A0, B0 landed, A1 and B1 in flight
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(0, st0, q);
-    wait_vm<0>();
+    for (int i = 0; i < 8; ++i) dma(0, 0, h0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(0, 1, h1, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(1, 0, h2, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(1, 1, h3, i);
+    wait_vm<16>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < MI + NI; ++q) {
-      ldfrag(xa, xb, st0, 0, q, 0);
-      ldfrag(xa, xb, st0, 0, q, 1);
+      ldfrag(xa, xb, h0, h1, 0, q, 0);
+      ldfrag(xa, xb, h0, h1, 0, q, 1);
     }
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) dma(1, st1, q);
-    // two k-steps per trip name their stages statically (one extra k-step at
-    // the end multiplies zeros)
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-      kstep(kt, st0, st1);
-      kstep(kt + 1, st1, st0);
+    // five k-steps per trip name their buffers statically; the last nk mod 5
+    // k-steps run after the loop (loads past the end read zeros)
+    int64_t kt = 0;
+    for (; kt + 5 <= nk; kt += 5) {
+      kstep(kt, h0, h1, h2, h3, h4, h0);
+      kstep(kt + 1, h2, h3, h4, h0, h1, h2);
+      kstep(kt + 2, h4, h0, h1, h2, h3, h4);
+      kstep(kt + 3, h1, h2, h3, h4, h0, h1);
+      kstep(kt + 4, h3, h4, h0, h1, h2, h3);
     }
+    if (kt < nk) kstep(kt, h0, h1, h2, h3, h4, h0);
+    if (kt + 1 < nk) kstep(kt + 1, h2, h3, h4, h0, h1, h2);
+    if (kt + 2 < nk) kstep(kt + 2, h4, h0, h1, h2, h3, h4);
+    if (kt + 3 < nk) kstep(kt + 3, h1, h2, h3, h4, h0, h1);
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -197,7 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // 2^(a_sexp + b_sexp), store 16 bytes of bf16 per lane per output.
   // Slot s of staged row r sits at r*512 + ((s ^ (r & 7)) << 4); the two rows
   // a 16-lane group reads take slots of opposite parity (conflict-free).
-  char* stg = st0 + wave * 16384;
+  char* stg = (wave < 2 ? h0 : h1) + (wave & 1) * 16384;
   bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) + (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
   bf16_t* ab = reinterpret_cast<bf16_t*>(p.aux);
   if (ab) ab += p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride;
