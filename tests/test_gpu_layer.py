@@ -53,6 +53,10 @@ EDGE = {
     # (f = 208), GELU and a shared expert
     "ragged_fp8_gelu_shared": Workload("ragged8", T=1000, d=144, E=6, k=3, f=208, act="gelu",
                                        score="sigmoid", n_shared=1, sel_bias=True, fp8=True),
+    # whole five-k-step ring trips and no tail: d = 320 and f = 640 give the bf16
+    # GEMMs 5 and 10 k-steps of 64 (the FP8 ones 3 and 5 of 128)
+    "ring_whole_trips": Workload("ring5", T=700, d=320, E=4, k=2, f=640, aux_coef=0.02),
+    "ring_whole_trips_fp8": Workload("ring5f8", T=700, d=320, E=4, k=2, f=640, fp8=True),
     # FP8 forward with every assignment dropped: the routed GEMMs see no rows
     "fp8_all_dropped_shared": Workload("drop8", T=512, d=256, E=8, k=2, f=256, cf=0.0,
                                        n_shared=1, fp8=True),
