@@ -43,7 +43,7 @@
 
 namespace moe {
 
-constexpr int kBK = 64;                   // k per stage
+constexpr int kBK = 64;                   // k per operand tile
 constexpr int kRows = 256;                // tile rows of either operand
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -56,21 +56,15 @@ __device__ __forceinline__ int ks_off(int k, int s) {
 }
 
 
-// Per-lane DMA source of one operand tile. A wave issues kRows/64 = 4
-// instructions per stage; instruction i fills block blk = wave*4 + i (1 KiB).
-//   K-contiguous: block = rows blk*16 .. +15, lane l -> row blk*16 + (l>>2),
-//     logical chunk (l&3) ^ ((l>>4)&3); k offset inside the stage = 8*chunk.
-//   K-strided: block = k-rows 2*blk, 2*blk+1, lane l -> k-row 2*blk + (l>>5),
-//     logical slot (l&31) ^ ((k&3)<<1), i.e. rows 8*slot .. 8*slot+7.
-// off[i] is the byte offset at k0 = 0 (kOOB when the rows lie outside the
-// operand); kk[i] is the lane's k inside a stage, for the K-tail test.
 struct DmaSrc {
   uint32_t off[8];
   int kk[8];
 };
 
 // Per-lane DMA source of one operand tile: a wave issues 8 instructions per
-// stage; instruction i fills 1 KiB block blk = wave*8 + i.
+// tile; instruction i fills 1 KiB block blk = wave*8 + i. off[i] is the byte
+// offset at k0 = 0 (kOOB when the rows lie outside the operand); kk[i] is the
+// lane's k inside the tile, for the K-tail test.
 //   K-contiguous: block = rows blk*8 .. +7 (128 bytes each), lane l -> row
 //     blk*8 + (l>>3), physical chunk l&7, logical chunk (l&7) ^ ((row>>1)&7).
 //   K-strided: block = k-rows 2*blk, 2*blk+1, lane l -> k-row 2*blk + (l>>5),
@@ -126,9 +120,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
   constexpr bool FUSED = EPI == EPI_SWIGLU_FWD;
   constexpr int BNo = FUSED ? BN / 2 : BN;      // output columns per tile
-  constexpr int A_EL = BM * kBK, B_EL = BN * kBK;
-  constexpr int ST = A_EL + B_EL;               // one stage (bf16 elements)
-  constexpr int NLD = 16;                       // DMA instructions per wave per stage
+  constexpr int A_EL = BM * kBK, B_EL = BN * kBK;   // elements per operand tile
+  static_assert(A_EL == B_EL, "ring buffers hold either operand");
   static_assert(!FUSED || BKM, "fused SwiGLU needs a K-contiguous weight");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
   // Five 32 KiB buffers, each holding one operand's 64-k tile; separate

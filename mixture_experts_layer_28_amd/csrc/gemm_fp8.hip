@@ -30,7 +30,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBK8 = 128;                 // k per stage (bytes per tile row)
+constexpr int kBK8 = 128;                 // k per operand tile (bytes per tile row)
 constexpr int kRows8 = 256;               // tile rows of either operand
 
 typedef int v8i32 __attribute__((ext_vector_type(8)));
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
   constexpr bool FUSED = EPI == EPI_SWIGLU_FWD;
   constexpr int BNo = FUSED ? BN / 2 : BN;
-  constexpr int A_B = BM * kBK8, B_B = BN * kBK8;   // bytes per stage of each tile
+  constexpr int A_B = BM * kBK8, B_B = BN * kBK8;   // bytes per operand tile
   static_assert(A_B == B_B, "ring buffers hold either operand");
   static_assert(NM == 16 && MI + NI == 8, "schedule assumes 4x4 MFMA blocks per wave");
   __shared__ __attribute__((aligned(1024))) char h0[A_B];
