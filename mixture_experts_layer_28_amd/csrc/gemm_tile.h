@@ -241,65 +241,4 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& p, const Tile& t, 
   }
 }
 
-// Backward-activation epilogue with every side-tensor load issued before
-// any math: the per-lane segment count is a compile-time constant, so all of
-// a lane's loads of a (and b) are in flight together instead of one round
-// trip per segment. Out-of-range segments read a clamped (valid) address and
-// store nothing.
-template <int EPI, int NROWS, int NCOLS, int NTHR>
-__device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& p, const Tile& t,
-                                                 const float* stage, int lds, int64_t m0,
-                                                 int64_t n0, int me) {
-  static_assert(EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD, "backward epilogues only");
-  constexpr int SPR = NCOLS / 8, NSEG = NROWS * SPR, PER = NSEG / NTHR;
-  static_assert(NSEG % NTHR == 0, "segments must split evenly");
-  constexpr bool SW = EPI == EPI_SWIGLU_BWD;
-  bf16_t* cb = reinterpret_cast<bf16_t*>(p.c) +
-               (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride);
-  const bf16_t* ab = reinterpret_cast<const bf16_t*>(p.aux) +
-                     (p.aux_rowidx ? t.r0 * p.ldaux : (int64_t)t.g * p.aux_gstride);
-  // SwiGLU needs a and b: prefetch half a lane's segments at a time
-  constexpr int HP = SW ? PER / 2 : PER;
-#pragma unroll
-  for (int h = 0; h < PER; h += HP) {
-    uint4 ra[HP], rb[SW ? HP : 1];   // packed bf16 until used
-#pragma unroll
-    for (int q = 0; q < HP; ++q) {
-      const int s = me + (h + q) * NTHR;
-      const int rho = s / SPR, c = (s - rho * SPR) << 3;
-      int64_t gm = m0 + rho, gn = n0 + c;
-      gm = gm < t.M ? gm : t.M - 1;
-      gn = gn < p.N ? gn : p.N - 8;
-      ra[q] = *reinterpret_cast<const uint4*>(ab + gm * p.ldaux + gn);
-      if (SW) rb[q] = *reinterpret_cast<const uint4*>(ab + gm * p.ldaux + p.fdim + gn);
-    }
-#pragma unroll
-    for (int q = 0; q < HP; ++q) {
-      const int s = me + (h + q) * NTHR;
-      const int rho = s / SPR, c = (s - rho * SPR) << 3;
-      const int64_t gm = m0 + rho, gn = n0 + c;
-      if (gm >= t.M || gn >= p.N) continue;
-      const float* sv = stage + rho * lds + c;
-      const uint32_t aw[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
-      uint32_t bw[4] = {0, 0, 0, 0};
-      if (SW) { bw[0] = rb[q].x; bw[1] = rb[q].y; bw[2] = rb[q].z; bw[3] = rb[q].w; }
-      float o[8], o2[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = sv[i];
-        const float a = bf2f((i & 1) ? (aw[i >> 1] >> 16) : (aw[i >> 1] & 0xffffu));
-        if (SW) {
-          const float b = bf2f((i & 1) ? (bw[i >> 1] >> 16) : (bw[i >> 1] & 0xffffu));
-          o[i] = v * b * dsilu_f(a);
-          o2[i] = v * silu_f(a);
-        } else {
-          o[i] = v * dgelu_f(a);
-        }
-      }
-      Vec8<bf16_t>::store(cb + gm * p.ldc + gn, o);
-      if (SW) Vec8<bf16_t>::store(cb + gm * p.ldc + p.fdim + gn, o2);
-    }
-  }
-}
-
 }  // namespace moe
