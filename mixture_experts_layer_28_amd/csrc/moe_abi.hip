@@ -40,6 +40,9 @@ hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, con
 hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
+hipError_t launch_router_dw_small(const float*, const void*, bool, int, int, int64_t, float*,
+                                  hipStream_t);
+int router_dw_small_chunks(int T);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 hipError_t launch_router_small(const void*, bool, const float*, const float*, const float*, int,
                                int, int64_t, int, int, int32_t*, float*, float*, float*,
@@ -220,6 +223,7 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return align256((size_t)T * d->k * pre_cols(d) * esize(d)) +
              (d->n_shared ? align256((size_t)T * pre_cols(d) * esize(d)) : 0);
     case MOE_OP_ROUTE_BWD: {
+      if (E <= 8) return align256((size_t)router_dw_small_chunks((int)T) * E * d->d * 4);
       const int S = route_bwd_splits(d);
       return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
     }
@@ -845,6 +849,21 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
                                             z_coef, inv_tau, T, E, k, desc->score, dlogits, s),
                       "router dlogits"));
   }
+  if (E <= 8) {
+    // few experts: one streaming pass over x, 64-token partials folded in order
+    const int S = router_dw_small_chunks(T);
+    {
+      Scope sc(K_ROUTER_DW, s);
+      MOE_TRY(hip_check(launch_router_dw_small(dlogits, x, desc->dtype == MOE_BF16, T, E, desc->d,
+                                               (float*)ws, s),
+                        "router dw"));
+    }
+    {
+      Scope sc(K_ROUTER_DW_REDUCE, s);
+      MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
+                        "router dw reduce"));
+    }
+  } else {
   // dw_r = dl^T x, split over tokens, partials folded in a fixed order
   const int S = route_bwd_splits(desc);
   GemmArgs p = blank();
@@ -865,6 +884,7 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
     Scope sc(K_ROUTER_DW_REDUCE, s);
     MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
                       "router dw reduce"));
+  }
   }
   Scope sc(K_ROUTER_DX, s);
   // dx_router = dl W_r; dl is nonzero only on the chosen experts unless a loss term is dense

@@ -729,13 +729,90 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 // out[i] = sum_s part[s][i], s ascending
+// dW_r = dl^T x for few experts (E <= 8): a streaming reduction over tokens,
+// x read once. Block (bx, chunk) is one wave over 512 columns (8 per lane,
+// one 16-byte load per token); it sums, over the chunk's kRdwTok tokens in
+// ascending order, dl[t][e] * x[t][c .. c+7], with the rows of 8 tokens
+// loaded ahead of their FMAs. The partial [chunk][E][d] is folded by
+// splitk_reduce_kernel in chunk order, so the result is deterministic.
+constexpr int kRdwTok = 64;
+constexpr int kRdwEMax = 8;
+constexpr int kRdwAhead = 8;
+
+template <typename TX>
+__global__ __launch_bounds__(64) void router_dw_small_kernel(const float* __restrict__ dl,
+                                                             const TX* __restrict__ x, int T,
+                                                             int E, int64_t d,
+                                                             float* __restrict__ part) {
+  __shared__ float sdl[kRdwTok * kRdwEMax];
+  const int chunk = blockIdx.y, lane = threadIdx.x;
+  const int t0 = chunk * kRdwTok;
+  const int nt = T - t0 < kRdwTok ? T - t0 : kRdwTok;
+  // weights of the chunk's tokens, zero past its end and for e >= E, so the
+  // loop below has no branches (the loads stay in flight together)
+  for (int i = lane; i < kRdwTok * kRdwEMax; i += 64) {
+    const int tt = i / kRdwEMax, e = i - tt * kRdwEMax;
+    sdl[i] = (tt < nt && e < E) ? dl[(int64_t)(t0 + tt) * E + e] : 0.f;
+  }
+  __syncthreads();
+  const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * 8;
+  if (c >= d) return;
+  float acc[kRdwEMax][8];
+#pragma unroll
+  for (int e = 0; e < kRdwEMax; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[e][j] = 0.f;
+  const TX* xr = x + (int64_t)t0 * d + c;
+  for (int tb = 0; tb < nt; tb += kRdwAhead) {
+    float xv[kRdwAhead][8];
+#pragma unroll
+    for (int u = 0; u < kRdwAhead; ++u) {
+      const int tt = tb + u < nt ? tb + u : nt - 1;   // in range; its weight is 0 past nt
+      Vec8<TX>::load(xr + (int64_t)tt * d, xv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRdwAhead; ++u)
+#pragma unroll
+      for (int e = 0; e < kRdwEMax; ++e) {
+        const float w = sdl[(tb + u) * kRdwEMax + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[e][j] = fmaf(w, xv[u][j], acc[e][j]);
+      }
+  }
+  for (int e = 0; e < E; ++e) Vec8<float>::store(part + ((int64_t)chunk * E + e) * d + c, acc[e]);
+}
+
+hipError_t launch_router_dw_small(const float* dl, const void* x, bool x_bf16, int T, int E,
+                                  int64_t d, float* part, hipStream_t st) {
+  if (E > kRdwEMax || T <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((d + 511) / 512), (unsigned)((T + kRdwTok - 1) / kRdwTok));
+  if (x_bf16)
+    hipLaunchKernelGGL(router_dw_small_kernel<bf16_t>, grid, dim3(64), 0, st, dl,
+                       (const bf16_t*)x, T, E, d, part);
+  else
+    hipLaunchKernelGGL(router_dw_small_kernel<float>, grid, dim3(64), 0, st, dl,
+                       (const float*)x, T, E, d, part);
+  return hipGetLastError();
+}
+
+int router_dw_small_chunks(int T) { return (T + kRdwTok - 1) / kRdwTok; }
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int S, int64_t n,
                                                             float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  // partials summed in index order; loads issued eight at a time
   float acc = 0.f;
-  for (int s = 0; s < S; ++s) acc += part[(int64_t)s * n + i];
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(s + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; s < S; ++s) acc += part[(int64_t)s * n + i];
   out[i] = acc;
 }
 
