@@ -141,17 +141,18 @@ __global__ __launch_bounds__(256) void router_small_kernel(
       const int64_t t = t0 + a < T ? t0 + a : T - 1;
       Vec8<TX>::load(x + t * d + c, xv[a]);
     }
-    static_for<EMAX>([&](auto EI) __attribute__((always_inline)) {
-      constexpr int e = decltype(EI)::value;
-      if (e < E) {
-        float wv[8];
-        Vec8<float>::load(w_r + (int64_t)e * d + c, wv);
+    // every expert row is loaded without a branch (rows e >= E repeat row 0;
+    // their sums are never used), so the loads of an iteration stay in flight
+    // together instead of each waiting behind its own branch
+    float wv[EMAX][8];
 #pragma unroll
-        for (int a = 0; a < TPW; ++a)
+    for (int e = 0; e < EMAX; ++e) Vec8<float>::load(w_r + (int64_t)(e < E ? e : 0) * d + c, wv[e]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[a][e] = fmaf(xv[a][i], wv[i], acc[a][e]);
-      }
-    });
+    for (int e = 0; e < EMAX; ++e)
+#pragma unroll
+      for (int a = 0; a < TPW; ++a)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[a][e] = fmaf(xv[a][i], wv[e][i], acc[a][e]);
   }
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
@@ -234,8 +235,12 @@ hipError_t launch_router_small(const void* x, bool bf16, const float* w_r, const
 }
 
 // ------------------------------------------------------------ aux stats
-// Pass 1: block b sums scores over tokens [256b, 256b+256) per expert
-// (float64, sequential in token order) and counts its assignments.
+// Pass 1: block b covers tokens [256b, 256b+256). Per expert, the scores
+// are summed in float64 by G = 256 / min(E, 256) interleaved token groups
+// (group g takes tokens t0+g, t0+g+G, ...) whose partials are then added in
+// group order; assignments are counted in an LDS histogram and the squared
+// lse values summed by a fixed-shape tree. Every order is fixed, so the
+// result does not change from run to run.
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ topk,
                                                           const float* __restrict__ lse, int T,
@@ -243,24 +248,43 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
                                                           int32_t* __restrict__ pc,
                                                           double* __restrict__ pl) {
   __shared__ int hist[1024];
+  __shared__ double part[256];
+  __shared__ double wl[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int t0 = b * 256, t1 = min(T, t0 + 256);
   for (int i = t0 * k + tid; i < t1 * k; i += 256) atomicAdd(&hist[topk[i]], 1);
-  for (int e = tid; e < E; e += 256) {
+
+  const int W = min(E, 256), G = 256 / W;
+  for (int e0 = 0; e0 < E; e0 += W) {
+    const int e = e0 + tid % W, g = tid / W;
     double z = 0.0;
-    for (int t = t0; t < t1; ++t) z += (double)scores[(int64_t)t * E + e];
-    pz[(int64_t)b * E + e] = z;
+    if (g < G && e < E) {
+#pragma unroll 8
+      for (int t = t0 + g; t < t1; t += G) z += (double)scores[(int64_t)t * E + e];
+    }
+    part[tid] = z;
+    __syncthreads();
+    if (tid < W && e0 + tid < E) {
+      double s = 0.0;
+      for (int j = 0; j < G; ++j) s += part[j * W + tid];
+      pz[(int64_t)b * E + e0 + tid] = s;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int e = tid; e < E; e += 256) pc[(int64_t)b * E + e] = hist[e];
-  if (tid == 0) {
-    double zl = 0.0;
-    if (lse)
-      for (int t = t0; t < t1; ++t) zl += (double)lse[t] * (double)lse[t];
-    pl[b] = zl;
+
+  double zl = 0.0;
+  if (lse && t0 + tid < t1) {
+    const double v = (double)lse[t0 + tid];
+    zl = v * v;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) zl += __shfl_xor(zl, o, 64);
+  if ((tid & 63) == 0) wl[tid >> 6] = zl;
+  __syncthreads();
+  if (tid == 0) pl[b] = ((wl[0] + wl[1]) + wl[2]) + wl[3];
 }
 
 // Pass 2 (one block): fold the partials in block order.
@@ -359,11 +383,22 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ h
   const int tid = threadIdx.x;
   int kept = 0;
   if (tid < E) {
+    // 16 block counts are loaded before any is replaced (clamped, so the
+    // loads need no branch), then the running sum is written back.
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int v = hist[(int64_t)b * E + tid];
-      hist[(int64_t)b * E + tid] = run;
-      run += v;
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int bb = min(b0 + j, nb - 1);
+        const int h = hist[(int64_t)bb * E + tid];
+        v[j] = b0 + j < nb ? h : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nb) hist[(int64_t)(b0 + j) * E + tid] = run;
+        run += v[j];
+      }
     }
     kept = (cap >= 0 && (int64_t)run > cap) ? (int)cap : run;
   }
