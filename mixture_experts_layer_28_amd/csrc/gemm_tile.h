@@ -44,11 +44,18 @@ __device__ __forceinline__ int64_t fused_row(int j, int WN, int64_t n0h, int64_t
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8). Give
-// each XCD a contiguous range of logical tiles so that the tiles resident on
-// one XCD at a time share A/B panels in that XCD's L2. nb is a multiple of 8.
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb) {
-  return (b & 7) * (nb >> 3) + (b >> 3);
+// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8). Of
+// the `valid` logical tiles, XCD x takes the contiguous run
+// [x*valid/8, (x+1)*valid/8): the tiles resident on one XCD at a time share
+// A/B panels in that XCD's L2, and every XCD gets the same number of tiles
+// to within one, however many surplus workgroups the grid holds (a grouped
+// grid is sized for the worst-case tile count). Returns the logical tile of
+// this workgroup, or -1 for none. gridDim.x is a multiple of 8 and at least
+// valid rounded up to one.
+__device__ __forceinline__ int64_t xcd_tile(int64_t valid) {
+  const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int64_t lo = x * valid / 8, hi = (x + 1) * valid / 8;
+  return lo + i < hi ? lo + i : -1;
 }
 
 // Bands of kBandM m-tiles, n-tiles outer inside a band: consecutive logical
@@ -127,11 +134,11 @@ template <int BM, int BNo, int RAG>
 __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, int* s_wsum,
                                              Tile& t) {
   const int64_t nt = (p.N + BNo - 1) / BNo;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
   if (RAG == RAG_M) {
     group_tile_prefix<BM>(p.offsets, p.G, s_tiles, s_wsum);
     const int64_t total = s_tiles[p.G];
-    if (L >= total * nt) return false;
+    const int64_t L = xcd_tile(total * nt);
+    if (L < 0) return false;
     int64_t mt, ntile;
     band_order(L, total, nt, mt, ntile);
     t.g = find_group(s_tiles, p.G, mt);
@@ -144,7 +151,8 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, in
   }
   const int64_t mtg = (p.M + BM - 1) / BM;
   const int64_t per = mtg * nt;
-  if (L >= per * p.G) return false;
+  const int64_t L = xcd_tile(per * p.G);
+  if (L < 0) return false;
   t.g = (int)(L / per);
   int64_t mt, ntile;
   band_order(L - (int64_t)t.g * per, mtg, nt, mt, ntile);
