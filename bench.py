@@ -59,6 +59,19 @@ def gemm_flops(w, A):
     return out
 
 
+def is_fp8_gemm(w, name):
+    """Whether this grouped-GEMM launch runs on E4M3 operands."""
+    return (w.fp8 and "fwd" in name) or (w.fp8_bwd and "dgrad" in name)
+
+
+def dtype_label(w):
+    if w.dtype != "bf16":
+        return "f32"
+    if w.fp8 and w.fp8_bwd:
+        return "fp8-e4m3 fwd and dgrad GEMMs, bf16 wgrad"
+    return "fp8-e4m3 fwd GEMMs, bf16 bwd" if w.fp8 else "bf16"
+
+
 def hbm_bytes(w, A):
     """Algorithmic HBM bytes of the streaming stages (each tensor read or
     written once)."""
@@ -266,7 +279,7 @@ def cpu_baseline(w, g, tokens):
                           f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau,
                           fp8=ws.fp8)
     O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act, ws.aux_coef,
-                     f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau)
+                     f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau, fp8_dgrad=ws.fp8_bwd)
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {tokens} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in "
@@ -326,7 +339,8 @@ def main():
         del src, dst
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
+                     fp8_bwd=w.fp8_bwd)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()
@@ -362,7 +376,7 @@ def main():
         tot, dom, n = max(gk)
         avg_s = tot / n / 1e3
         achieved = flops[dom] / avg_s / 1e12
-        fp8_kernel = w.fp8 and "fwd" in dom
+        fp8_kernel = is_fp8_gemm(w, dom)
         peak = (PEAK_FP8_TFLOPS if fp8_kernel else PEAK_BF16_TFLOPS) if w.dtype == "bf16" \
             else PEAK_F32_TFLOPS
         roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": dom,
@@ -387,7 +401,7 @@ def main():
     # dtype's peak (fp8 forward GEMMs at the fp8 peak) over the time they took
     mfma_frac = None
     if gemm_tot_ms and w.dtype == "bf16":
-        ideal_s = sum(flops[name] * n / ((PEAK_FP8_TFLOPS if w.fp8 and "fwd" in name
+        ideal_s = sum(flops[name] * n / ((PEAK_FP8_TFLOPS if is_fp8_gemm(w, name)
                                           else PEAK_BF16_TFLOPS) * 1e12)
                       for name, tot, n in prof if name in flops)
         mfma_frac = ideal_s / (gemm_tot_ms / 1e3)
@@ -408,11 +422,10 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("fp8-e4m3 fwd GEMMs, bf16 bwd" if w.fp8 else "bf16") if w.dtype == "bf16"
-                 else "f32", "data": "synthetic",
+        "dtype": dtype_label(w), "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "act": w.act, "score": w.score, "n_shared": w.n_shared,
-                   "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8,
+                   "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8, "fp8_dgrad": w.fp8_bwd,
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
         "gemm_mfma_frac": round(mfma_frac, 4) if mfma_frac else None,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -89,7 +89,8 @@ typedef enum {
   MOE_OP_FFN_FWD = 3,
   MOE_OP_FFN_BWD = 4,
   MOE_OP_ROUTE_BWD = 5,
-  MOE_OP_FFN_FWD_FP8 = 6
+  MOE_OP_FFN_FWD_FP8 = 6,
+  MOE_OP_FFN_BWD_FP8 = 7
 } moe_op;
 
 /* ---------------------------------------------------------------- router
@@ -250,6 +251,57 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
                         const void* save_pre_s, const void* save_h_s, const void* dout,
                         const void* dy, void* dx_perm, void* dx_shared, void* dw13, void* dw2,
                         void* dsw13, void* dsw2, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- FP8 backward
+ * [Megatron10x] §5.2 trains in FP8 mixed precision, and [Recipe] §8.1 and
+ * §9.1 list FP8 training with bf16 activations. The pages do not say which
+ * backward GEMMs run in FP8. Reading taken here: the two data-gradient GEMMs
+ * use the forward's per-row scheme, and the weight gradients, which reduce
+ * over tokens, stay in bf16. A data gradient reads a weight along its input
+ * dimension, so the weight enters transposed and is quantized per input
+ * channel.
+ *
+ * moe_quantize_fp8_t: moe_quantize_fp8 applied to the rows of the transposes
+ * of G row-major R x C bf16 matrices. Codes and exponents are a bit-exact
+ * function of the input:
+ *   codes[g][c][r] = E4M3 nearest (ties to even) of src[g][r][c] * 2^-scale_exp[g][c]
+ *   scale_exp[g][c] = smallest e with max_r |src[g][r][c]| <= 448 * 2^e
+ *                     (0 for an all-zero column)
+ * Inputs must be finite. No desc: a plain matrix operation.
+ *   src        [G, R, C] bf16     in
+ *   codes      [G, C, R] uint8    out
+ *   scale_exp  [G, C] int32       out
+ * Constraints: R a multiple of 16 in [16, 2^22]; C a multiple of 8 in [8, 2^31);
+ * 0 <= G <= 65535; every pointer 16-byte aligned.
+ */
+int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                       int32_t* scale_exp, void* stream);
+
+/* moe_grouped_ffn_bwd_fp8: moe_grouped_ffn_bwd with its two data-gradient
+ * GEMMs on FP8 operands. Per group:
+ *   1. the upstream gradient rows are quantized per row;
+ *   2. dH = dO W2 runs against w2q_t, and the activation backward in its
+ *      epilogue writes the pre-activation gradient (dpre) in bf16;
+ *   3. that bf16 dpre is quantized per row;
+ *   4. dX = dpre W13 runs against w13q_t.
+ * Each GEMM output element is 2^(e_row + e_channel) * sum_k e4m3 * e4m3,
+ * accumulated in float32. The weight gradients dW2 = dO^T H and
+ * dW13 = dpre^T X run in bf16 on the bf16 values, as in moe_grouped_ffn_bwd.
+ * desc->dtype must be MOE_BF16; d and f must be multiples of 16.
+ *   w2q_t [E, f, d] uint8, s2_t [E, f] int32    (moe_quantize_fp8_t of w2 [E, d, f])    in
+ *   w13q_t [E, d, P] uint8, s13_t [E, d] int32  (moe_quantize_fp8_t of w13 [E, P, d])   in
+ *   sw2q_t, ss2_t, sw13q_t, ss13_t: the shared expert's, or NULL                       in
+ *   the other arguments are as in moe_grouped_ffn_bwd
+ *   ws  MOE_OP_FFN_BWD_FP8 bytes (dpre, and the FP8 codes and exponents)               scratch
+ */
+int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                            const void* x, const void* w13q_t, const int32_t* s13_t,
+                            const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
+                            const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
+                            const void* save_pre, const void* save_h, const void* save_pre_s,
+                            const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                            void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine: the weighted sum of [Recipe] §2.1/§2.2 (the combine step of

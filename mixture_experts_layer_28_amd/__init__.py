@@ -16,12 +16,12 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
- MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8) = range(7)
+ MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8) = range(8)
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
+    "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8",
 )
 
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                  ctypes.c_int64, _P, _P],
             "moe_grouped_ffn_fwd_fp8": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
+            "moe_quantize_fp8_t": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+            "moe_grouped_ffn_bwd_fp8": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
             "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
@@ -226,6 +229,29 @@ def grouped_ffn_fwd_fp8(desc, xq_perm, sx_perm, offsets, xq, sx, w13q, s13, w2q,
         _p(s13), _p(w2q), _p(s2), _p(sw13q), _p(ss13), _p(sw2q), _p(ss2), _p(save_pre),
         _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
         _stream(stream)))
+
+
+def quantize_fp8_t(src, codes, scale_exp, stream=None):
+    """Per-column E4M3 quantization of bf16 matrices src [..., R, C] into the
+    codes of their transposes ([..., C, R], uint8) and one exponent per
+    column ([..., C], int32)."""
+    R, C = src.shape[-2], src.shape[-1]
+    G = src.numel() // (R * C) if R * C else 0
+    if codes.shape != src.shape[:-2] + (C, R) or scale_exp.shape != src.shape[:-2] + (C,):
+        raise ValueError("codes must be [..., C, R] and scale_exp [..., C] for src [..., R, C]")
+    _check("moe_quantize_fp8_t", lib().moe_quantize_fp8_t(_p(src), G, R, C, _p(codes),
+                                                          _p(scale_exp), _stream(stream)))
+
+
+def grouped_ffn_bwd_fp8(desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t, ss13_t,
+                        sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy, dx_perm,
+                        dx_shared, dw13, dw2, dsw13, dsw2, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_grouped_ffn_bwd_fp8", lib().moe_grouped_ffn_bwd_fp8(
+        ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13q_t), _p(s13_t), _p(w2q_t),
+        _p(s2_t), _p(sw13q_t), _p(ss13_t), _p(sw2q_t), _p(ss2_t), _p(save_pre), _p(save_h),
+        _p(save_pre_s), _p(save_h_s), _p(dout), _p(dy), _p(dx_perm), _p(dx_shared), _p(dw13),
+        _p(dw2), _p(dsw13), _p(dsw2), wp, wn, _stream(stream)))
 
 
 def combine(desc, out, out_shared, gate, row_of, y, stream=None):

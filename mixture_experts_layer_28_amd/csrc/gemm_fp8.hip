@@ -1,6 +1,8 @@
 // Grouped GEMM on FP8 (OCP E4M3) operands on the gfx950 matrix cores
 // (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation), for the forward of the
-// expert FFN. Both operands are K-contiguous byte matrices with one
+// expert FFN and the backward's data gradients (whose weight operand is the
+// transposed weight, quantized per input channel). Both operands are
+// K-contiguous byte matrices with one
 // power-of-two scale per row (2^a_sexp[m] for the input rows, 2^b_sexp[n]
 // for the weight rows); the epilogue applies them exactly with ldexp, so
 //   C[m][n] = 2^(a_sexp[m] + b_sexp[n]) * sum_k e4m3(A[m][k]) e4m3(B[n][k]).
@@ -64,6 +66,15 @@ __device__ __forceinline__ void dma_src8(Dma8& d, int64_t ld, int64_t rows_valid
   }
 }
 
+
+__device__ __forceinline__ void unpack8(uint4 w, float* v) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf2f(u[e] & 0xffffu);
+    v[2 * e + 1] = bf2f(u[e] >> 16);
+  }
+}
 
 __device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
   v8i32 v;
@@ -220,8 +231,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int32_t* asx = p.a_sexp + (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M);
   const int32_t* bsx = p.b_sexp + (int64_t)t.g * p.b_sexp_gstride;
   const int lr = lane & 31, lh = lane >> 5;
+  // Backward epilogues: this lane's saved pre-activations (a, and b for
+  // SwiGLU) of the block row are loaded before its accumulators are staged,
+  // so the loads overlap the staging (rows/columns clamped into range).
+  constexpr bool BWD = EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD;
+  constexpr bool SW = EPI == EPI_SWIGLU_BWD;
   static_for<MI>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
+    uint4 pa8[BWD ? 8 : 1], pb8[SW ? 8 : 1];
+    if (BWD) {
+      const int64_t n = t.n0 + wn0 + 8 * (lane & 15);
+      const int64_t nc = n < p.N ? n : p.N - 8;
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        int64_t m = t.m0 + wm0 + 32 * i + 4 * q + (lane >> 4);
+        m = m < t.M ? m : t.M - 1;
+        pa8[BWD ? q : 0] = *reinterpret_cast<const uint4*>(ab + m * p.ldaux + nc);
+        if (SW) pb8[SW ? q : 0] = *reinterpret_cast<const uint4*>(ab + m * p.ldaux + p.fdim + nc);
+      });
+    }
     static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
       constexpr int j = decltype(Q)::value / 4, g = decltype(Q)::value % 4;
       const int sl = 8 * j + 2 * g + lh;
@@ -297,11 +325,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int e = 0; e < 8; ++e) v[e] = ldexpf(v[e], ea + ebs[e]);
         if (EPI == EPI_STORE) {
           Vec8<bf16_t>::store(cb + m * p.ldc + n, v);
-        } else {
+        } else if (EPI == EPI_GELU_FWD) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = gelu_f(v[e]);
           Vec8<bf16_t>::store(cb + m * p.ldc + n, o);
           Vec8<bf16_t>::store(ab + m * p.ldaux + n, v);
+        } else {
+          // v = dH; C = dpre = [da | db] (SwiGLU) or da (GELU)
+          float a[8];
+          unpack8(pa8[BWD ? q : 0], a);
+          if (SW) {
+            float b[8], o2[8];
+            unpack8(pb8[SW ? q : 0], b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              o[e] = v[e] * b[e] * dsilu_f(a[e]);
+              o2[e] = v[e] * silu_f(a[e]);
+            }
+            Vec8<bf16_t>::store(cb + m * p.ldc + n, o);
+            Vec8<bf16_t>::store(cb + m * p.ldc + p.fdim + n, o2);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = v[e] * dgelu_f(a[e]);
+            Vec8<bf16_t>::store(cb + m * p.ldc + n, o);
+          }
         }
       });
     }
@@ -327,7 +374,8 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
 
 }  // namespace
 
-// FP8 grouped GEMM, both operands K-contiguous (the forward's layouts).
+// FP8 grouped GEMM, both operands K-contiguous (the forward's layouts, and
+// the data gradients against transposed weights).
 // Requires K % 16 == 0, 16-byte aligned rows, N % 4 == 0 (f % 4 for the
 // fused SwiGLU) and 16-byte aligned scale arrays; the caller checks.
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
@@ -337,9 +385,13 @@ hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
   MOE_CASE(EPI_SWIGLU_FWD, RAG_M)
   MOE_CASE(EPI_GELU_FWD, RAG_M)
   MOE_CASE(EPI_STORE, RAG_M)
+  MOE_CASE(EPI_SWIGLU_BWD, RAG_M)
+  MOE_CASE(EPI_GELU_BWD, RAG_M)
   MOE_CASE(EPI_SWIGLU_FWD, RAG_NONE)
   MOE_CASE(EPI_GELU_FWD, RAG_NONE)
   MOE_CASE(EPI_STORE, RAG_NONE)
+  MOE_CASE(EPI_SWIGLU_BWD, RAG_NONE)
+  MOE_CASE(EPI_GELU_BWD, RAG_NONE)
 #undef MOE_CASE
   return hipErrorInvalidValue;
 }

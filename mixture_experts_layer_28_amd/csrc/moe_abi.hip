@@ -16,6 +16,7 @@ namespace moe {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
+hipError_t launch_quant_fp8_t(const void*, int64_t, int64_t, int64_t, void*, int32_t*, hipStream_t);
 hipError_t launch_quant_fp8(const void*, int64_t, int64_t, int64_t, const int32_t*, void*, int64_t,
                             int32_t*, hipStream_t);
 hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
@@ -233,6 +234,13 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       if (d->n_shared) b += align256((size_t)T * d->f) + align256((size_t)T * 4);
       return b;
     }
+    case MOE_OP_FFN_BWD_FP8:
+      // the bf16 backward's pre-activation gradients, then FP8 codes and
+      // exponents of the upstream gradient and of the pre-activation gradient
+      // (routed rows; the shared expert's T rows reuse them afterwards)
+      return ws_bytes_for(d, MOE_OP_FFN_BWD) + align256((size_t)T * d->k * d->d) +
+             align256((size_t)T * d->k * 4) + align256((size_t)T * d->k * pre_cols(d)) +
+             align256((size_t)T * d->k * 4);
   }
   return 0;
 }
@@ -340,7 +348,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FP8)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_BWD_FP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
   *bytes = ws_bytes_for(desc, op);
   return MOE_OK;
@@ -774,6 +782,183 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     w.M = P;
     w.N = d;
     w.K = desc->T;
+    MOE_TRY(run_gemm(desc, w, false, false, EPI_STORE, ragk, s, "ffn wgrad first matrix",
+                     shared ? K_SH_WGRAD_UP : K_WGRAD_UP));
+  }
+  return MOE_OK;
+}
+
+int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                       int32_t* scale_exp, void* stream) {
+  g_err[0] = 0;
+  if (G < 0 || G > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "G must be in [0, 65535] (got %lld)", (long long)G);
+  if (R < 16 || R % 16 || R > (int64_t(1) << 22))
+    return fail(MOE_ERR_INVALID_ARG, "R must be a positive multiple of 16, at most 2^22 (got %lld)",
+                (long long)R);
+  if (C < 8 || C % 8 || C >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "C must be a positive multiple of 8 below 2^31 (got %lld)",
+                (long long)C);
+  MOE_TRY(need(src, "src"));
+  MOE_TRY(need(codes, "codes"));
+  MOE_TRY(need(scale_exp, "scale_exp"));
+  if (G == 0) return MOE_OK;
+  Scope sc(K_QUANT_FP8, (hipStream_t)stream);
+  return hip_check(launch_quant_fp8_t(src, G, R, C, codes, scale_exp, (hipStream_t)stream),
+                   "fp8 transposing quantize");
+}
+
+int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                            const void* x, const void* w13q_t, const int32_t* s13_t,
+                            const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
+                            const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
+                            const void* save_pre, const void* save_h, const void* save_pre_s,
+                            const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                            void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                            void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  if (desc->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the FP8 backward reads bf16 activations: desc->dtype must be bf16");
+  if (desc->d % 16 || desc->f % 16)
+    return fail(MOE_ERR_UNSUPPORTED, "the FP8 backward needs d and f multiples of 16");
+  MOE_TRY(need(x_perm, "x_perm"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(w13q_t, "w13q_t"));
+  MOE_TRY(need(s13_t, "s13_t"));
+  MOE_TRY(need(w2q_t, "w2q_t"));
+  MOE_TRY(need(s2_t, "s2_t"));
+  MOE_TRY(need(save_pre, "save_pre"));
+  MOE_TRY(need(save_h, "save_h"));
+  MOE_TRY(need(dout, "dout"));
+  MOE_TRY(need(dx_perm, "dx_perm"));
+  MOE_TRY(need(dw13, "dw13"));
+  MOE_TRY(need(dw2, "dw2"));
+  if (desc->n_shared) {
+    MOE_TRY(need(x, "x"));
+    MOE_TRY(need(sw13q_t, "sw13q_t"));
+    MOE_TRY(need(ss13_t, "ss13_t"));
+    MOE_TRY(need(sw2q_t, "sw2q_t"));
+    MOE_TRY(need(ss2_t, "ss2_t"));
+    MOE_TRY(need(save_pre_s, "save_pre_s"));
+    MOE_TRY(need(save_h_s, "save_h_s"));
+    MOE_TRY(need(dy, "dy"));
+    MOE_TRY(need(dx_shared, "dx_shared"));
+    MOE_TRY(need(dsw13, "dsw13"));
+    MOE_TRY(need(dsw2, "dsw2"));
+  }
+  MOE_TRY(check_ws(desc, MOE_OP_FFN_BWD_FP8, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
+  if (T == 0) {
+    // no rows: every weight gradient is zero
+    MOE_TRY(hip_check(launch_fill_zero(dw13, (size_t)desc->E * P * d * 2, s), "zero dw13"));
+    MOE_TRY(hip_check(launch_fill_zero(dw2, (size_t)desc->E * d * f * 2, s), "zero dw2"));
+    if (desc->n_shared) {
+      MOE_TRY(hip_check(launch_fill_zero(dsw13, (size_t)P * d * 2, s), "zero dsw13"));
+      MOE_TRY(hip_check(launch_fill_zero(dsw2, (size_t)d * f * 2, s), "zero dsw2"));
+    }
+    return MOE_OK;
+  }
+  // workspace: the bf16 backward's dpre regions, then the FP8 buffers
+  char* wb = (char*)ws;
+  void* dpre_r = wb;
+  void* dpre_s = wb + align256((size_t)T * desc->k * P * 2);
+  char* w8 = wb + ws_bytes_for(desc, MOE_OP_FFN_BWD);
+  uint8_t* gq = (uint8_t*)w8;
+  int32_t* gs = (int32_t*)(w8 + align256((size_t)T * desc->k * d));
+  uint8_t* pq = (uint8_t*)((char*)gs + align256((size_t)T * desc->k * 4));
+  int32_t* ps = (int32_t*)((char*)pq + align256((size_t)T * desc->k * P));
+  const int epi_b = desc->act == MOE_SWIGLU ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
+  for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
+    const int ragm = shared ? RAG_NONE : RAG_M;
+    const int ragk = shared ? RAG_NONE : RAG_K;
+    const int G = shared ? 1 : (int)desc->E;
+    const int64_t rows = shared ? T : T * desc->k;
+    const int32_t* valid = shared ? nullptr : offsets + desc->E;
+    void* dpre = shared ? dpre_s : dpre_r;
+    const void* go = shared ? dy : dout;            // upstream gradient rows
+    const void* xin = shared ? x : x_perm;
+    const void* hs = shared ? save_h_s : save_h;
+    // upstream gradient -> FP8 rows (routed rows beyond offsets[E] skipped)
+    {
+      Scope sc(K_QUANT_FP8, s);
+      MOE_TRY(hip_check(launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s), "fp8 quantize dO"));
+    }
+    // dgrad 1: dH = dO W2 against W2^T in FP8, activation backward in the epilogue
+    GemmArgs p = blank();
+    p.a = opnd(gq, d, 0, 1);
+    p.b = opnd(shared ? sw2q_t : w2q_t, d, f * d, 0);
+    p.a_sexp = gs;
+    p.b_sexp = shared ? ss2_t : s2_t;
+    p.b_sexp_gstride = f;
+    p.c = dpre;
+    p.ldc = P;
+    p.c_rowidx = 1;
+    p.aux = (void*)(shared ? save_pre_s : save_pre);
+    p.ldaux = P;
+    p.aux_rowidx = 1;
+    p.offsets = offsets;
+    p.G = G;
+    p.M = T;
+    p.N = f;
+    p.K = d;
+    p.fdim = f;
+    p.max_rows = T * desc->k;
+    {
+      Scope sc(shared ? K_SH_DGRAD_DOWN : K_DGRAD_DOWN, s);
+      MOE_TRY(hip_check(gemm_fp8(p, epi_b, ragm, s), "fp8 ffn dgrad down matrix"));
+    }
+    // the bf16 pre-activation gradient -> FP8 rows
+    {
+      Scope sc(K_QUANT_FP8, s);
+      MOE_TRY(hip_check(launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s), "fp8 quantize dpre"));
+    }
+    // dgrad 2: dX = dpre W13 against W13^T in FP8
+    GemmArgs q = blank();
+    q.a = opnd(pq, P, 0, 1);
+    q.b = opnd(shared ? sw13q_t : w13q_t, P, d * P, 0);
+    q.a_sexp = ps;
+    q.b_sexp = shared ? ss13_t : s13_t;
+    q.b_sexp_gstride = d;
+    q.c = shared ? dx_shared : dx_perm;
+    q.ldc = d;
+    q.c_rowidx = 1;
+    q.offsets = offsets;
+    q.G = G;
+    q.M = T;
+    q.N = d;
+    q.K = P;
+    q.max_rows = p.max_rows;
+    {
+      Scope sc(shared ? K_SH_DGRAD_UP : K_DGRAD_UP, s);
+      MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, ragm, s), "fp8 ffn dgrad first matrix"));
+    }
+    // weight gradients in bf16, as in moe_grouped_ffn_bwd
+    GemmArgs r = blank();
+    r.a = opnd(go, d, 0, 1);
+    r.b = opnd(hs, f, 0, 1);
+    r.c = shared ? dsw2 : dw2;
+    r.ldc = f;
+    r.c_gstride = d * f;
+    r.offsets = offsets;
+    r.G = G;
+    r.M = d;
+    r.N = f;
+    r.K = T;
+    MOE_TRY(run_gemm(desc, r, false, false, EPI_STORE, ragk, s, "ffn wgrad down matrix",
+                     shared ? K_SH_WGRAD_DOWN : K_WGRAD_DOWN));
+    GemmArgs w = blank();
+    w.a = opnd(dpre, P, 0, 1);
+    w.b = opnd(xin, d, 0, 1);
+    w.c = shared ? dsw13 : dw13;
+    w.ldc = d;
+    w.c_gstride = P * d;
+    w.offsets = offsets;
+    w.G = G;
+    w.M = P;
+    w.N = d;
+    w.K = T;
     MOE_TRY(run_gemm(desc, w, false, false, EPI_STORE, ragk, s, "ffn wgrad first matrix",
                      shared ? K_SH_WGRAD_UP : K_WGRAD_UP));
   }

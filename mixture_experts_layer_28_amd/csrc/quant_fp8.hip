@@ -9,6 +9,10 @@
 // One workgroup of 256 threads per row; each thread keeps up to eight
 // 16-byte chunks of its row in registers between the max pass and the
 // conversion pass (rows up to 16384 wide), longer rows are read twice.
+//
+// The transposing form quantizes each column of a row-major matrix as a row
+// of its transpose (the backward reads the weights along their input
+// dimension): a column-max pass, then a 64 x 64 tiled transpose.
 #include "common.h"
 
 namespace moe {
@@ -90,7 +94,121 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
   for (int64_t c = tid + (int64_t)kQCache * kQThreads; c < nch; c += kQThreads) q[c] = to_e4m3(s[c], e);
 }
 
+// ---- per-column quantization into the transpose
+// src: G row-major R x C bf16 matrices; codes: G row-major C x R (the
+// transposes), so codes row c is src column c quantized like a row above.
+
+constexpr int kTC = 64;                   // columns per workgroup (both passes)
+
+// Pass 1: e[g][c] from max_r |src[g][r][c]|. Thread (rg, cc) covers columns
+// c0 + 8cc .. +7 of rows rg, rg + 32, ...; per-column maxima are bit
+// patterns, folded over the 32 row groups in LDS.
+__global__ __launch_bounds__(256) void col_exp_fp8_kernel(const bf16_t* __restrict__ src, int64_t R,
+                                                          int64_t C, int32_t* __restrict__ sexp) {
+  const int64_t g = blockIdx.y, c0 = (int64_t)blockIdx.x * kTC;
+  const int tid = threadIdx.x, rg = tid >> 3, cc = tid & 7;
+  const int64_t c = c0 + 8 * cc;
+  const bool cok = c < C;   // C % 8 == 0: a chunk is wholly in or out
+  const bf16_t* base = src + g * R * C + (cok ? c : 0);
+  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t r = rg;
+  for (; r + 32 * 7 < R; r += 32 * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(base + (r + 32 * u) * C);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+        m[2 * i] = lo > m[2 * i] ? lo : m[2 * i];
+        m[2 * i + 1] = hi > m[2 * i + 1] ? hi : m[2 * i + 1];
+      }
+    }
+  }
+  for (; r < R; r += 32) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + r * C);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+      m[2 * i] = lo > m[2 * i] ? lo : m[2 * i];
+      m[2 * i + 1] = hi > m[2 * i + 1] ? hi : m[2 * i + 1];
+    }
+  }
+  __shared__ uint32_t sm[32][kTC + 1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sm[rg][8 * cc + i] = m[i];
+  __syncthreads();
+  if (tid < kTC && c0 + tid < C) {
+    uint32_t mm = 0;
+    for (int j = 0; j < 32; ++j) mm = sm[j][tid] > mm ? sm[j][tid] : mm;
+    const float amax = bf2f(mm);
+    int ex = 0;
+    const float mant = frexpf(amax, &ex);
+    sexp[g * C + c0 + tid] = mm == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  }
+}
+
+// Pass 2: a 64 x 64 block of src (rows r0.., columns c0..) through LDS; thread
+// (c, q) writes codes[g][c][r0 + 16q .. +15] as one 16-byte store.
+__global__ __launch_bounds__(256) void transpose_quant_fp8_kernel(const bf16_t* __restrict__ src,
+                                                                  int64_t R, int64_t C,
+                                                                  const int32_t* __restrict__ sexp,
+                                                                  uint8_t* __restrict__ codes) {
+  const int64_t g = blockIdx.z, r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * kTC;
+  const int tid = threadIdx.x;
+  __shared__ uint16_t tile[64][kTC + 2];
+  // load: row tid >> 2, columns 16 (tid & 3) .. +15 (two 16-byte chunks)
+  {
+    const int rr = tid >> 2, cq = (tid & 3) * 16;
+    const int64_t r = r0 + rr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t c = c0 + cq + 8 * h;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + (g * R + r) * C + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tile[rr][cq + 8 * h + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+        tile[rr][cq + 8 * h + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  const int cl = tid >> 2, q = tid & 3;
+  const int64_t c = c0 + cl, r = r0 + 16 * q;
+  if (c >= C || r >= R) return;   // R % 16 == 0: a 16-row piece is wholly in or out
+  const int e = sexp[g * C + c];
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = ldexpf(bf2f(tile[16 * q + 4 * i][cl]), -e);
+    const float b = ldexpf(bf2f(tile[16 * q + 4 * i + 1][cl]), -e);
+    const float cc = ldexpf(bf2f(tile[16 * q + 4 * i + 2][cl]), -e);
+    const float d = ldexpf(bf2f(tile[16 * q + 4 * i + 3][cl]), -e);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, d, w, true);
+    o[i] = (uint32_t)w;
+  }
+  *reinterpret_cast<uint4*>(codes + (g * C + c) * R + r) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 }  // namespace
+
+hipError_t launch_quant_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                              int32_t* sexp, hipStream_t st) {
+  if (G == 0 || R == 0 || C == 0) return hipSuccess;
+  const unsigned nc = (unsigned)((C + kTC - 1) / kTC);
+  hipLaunchKernelGGL(col_exp_fp8_kernel, dim3(nc, (unsigned)G), dim3(256), 0, st,
+                     (const bf16_t*)src, R, C, sexp);
+  hipLaunchKernelGGL(transpose_quant_fp8_kernel, dim3(nc, (unsigned)((R + 63) / 64), (unsigned)G),
+                     dim3(256), 0, st, (const bf16_t*)src, R, C, (const int32_t*)sexp,
+                     (uint8_t*)codes);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                             const int32_t* valid_rows, void* codes, int64_t ld_q, int32_t* sexp,

@@ -299,12 +299,26 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
   __shared__ double red[256];
   const int tid = threadIdx.x;
   double acc = 0.0;
+  // partials are loaded eight blocks at a time (clamped, branch-free) and
+  // added in block order
   for (int e = tid; e < E; e += 256) {
     double zs = 0.0;
     int64_t c = 0;
-    for (int b = 0; b < nb; ++b) {
-      zs += pz[(int64_t)b * E + e];
-      c += pc[(int64_t)b * E + e];
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      double zv[8];
+      int cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t bb = min(b0 + j, nb - 1);
+        zv[j] = pz[bb * E + e];
+        cv[j] = pc[bb * E + e];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (b0 + j < nb) {
+          zs += zv[j];
+          c += cv[j];
+        }
     }
     const double zz = zs / (double)T;
     const double yy = (double)c / ((double)T * (double)k);
@@ -321,7 +335,14 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
   }
   if (tid == 0) {
     double zl = 0.0;
-    for (int b = 0; b < nb; ++b) zl += pl[b];
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      double lv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lv[j] = pl[min(b0 + j, nb - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (b0 + j < nb) zl += lv[j];
+    }
     out3[0] = (float)red[0];
     out3[1] = (float)(red[0] * (double)E);
     out3[2] = (float)(zl / (double)T);

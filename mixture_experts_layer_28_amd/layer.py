@@ -9,10 +9,11 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
+from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
                MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine,
-               combine_bwd, grouped_ffn_bwd, grouped_ffn_fwd, grouped_ffn_fwd_fp8, make_desc,
-               permute, permute_bwd, quantize_fp8, route, route_bwd, workspace_size)
+               combine_bwd, grouped_ffn_bwd, grouped_ffn_bwd_fp8, grouped_ffn_fwd, grouped_ffn_fwd_fp8,
+               make_desc, permute, permute_bwd, quantize_fp8, quantize_fp8_t, route, route_bwd,
+               workspace_size)
 
 
 class MoELayer:
@@ -31,20 +32,23 @@ class MoELayer:
     fp8_fwd runs both forward GEMMs on per-row E4M3 operands: every forward
     quantizes x_perm (and x for a shared expert) and the current weights,
     keeps the pre-activations and H in bf16, and the backward runs in bf16
-    as usual.
+    as usual. fp8_bwd runs the backward's two data-gradient GEMMs on E4M3
+    operands as well: every backward quantizes the current weights per input
+    channel (into their transposes), and the library quantizes the upstream
+    and pre-activation gradients per row; the weight gradients stay bf16.
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
                  bias_gamma: float = 0.0, gumbel_tau: float = 0.0, fp8_fwd: bool = False,
-                 device="cuda"):
+                 fp8_bwd: bool = False, device="cuda"):
         self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
         self.bias_gamma = bias_gamma
-        self.fp8_fwd = fp8_fwd
-        if fp8_fwd and dtype != "bf16":
-            raise ValueError("the FP8 forward keeps bf16 activations: dtype must be bf16")
+        self.fp8_fwd, self.fp8_bwd = fp8_fwd, fp8_bwd
+        if (fp8_fwd or fp8_bwd) and dtype != "bf16":
+            raise ValueError("the FP8 GEMMs keep bf16 activations: dtype must be bf16")
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dt = dt
         P = 2 * f if act == "swiglu" else f
@@ -100,8 +104,16 @@ class MoELayer:
             self.xq, self.sx = (z(T, d, dtype=u8), z(T, dtype=i32)) if sh else (None, None)
             self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), z(1, P, dtype=i32)) if sh else (None, None)
             self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
+        if fp8_bwd:
+            u8 = torch.uint8
+            sh = bool(n_shared)
+            self.w13q_t, self.s13_t = z(E, d, P, dtype=u8), z(E, d, dtype=i32)
+            self.w2q_t, self.s2_t = z(E, f, d, dtype=u8), z(E, f, dtype=i32)
+            self.sw13q_t, self.ss13_t = (z(1, d, P, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
+            self.sw2q_t, self.ss2_t = (z(1, f, d, dtype=u8), z(1, f, dtype=i32)) if sh else (None, None)
         ops = [MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
-               MOE_OP_ROUTE_BWD] + ([MOE_OP_FFN_FWD_FP8] if fp8_fwd else [])
+               MOE_OP_ROUTE_BWD] + ([MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
+              ([MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
         wsb = max(workspace_size(self.desc, op) for op in ops)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
@@ -137,9 +149,22 @@ class MoELayer:
     def backward(self, dy, x, w_r, w13, w2, sw13=None, sw2=None):
         D = self.desc
         combine_bwd(D, dy, self.out, self.gate, self.row_of, self.dgate, self.dout)
-        grouped_ffn_bwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
-                        self.save_h, self.save_pre_s, self.save_h_s, self.dout, dy, self.dx_perm,
-                        self.dx_shared, self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws)
+        if self.fp8_bwd:
+            quantize_fp8_t(w13, self.w13q_t, self.s13_t)
+            quantize_fp8_t(w2, self.w2q_t, self.s2_t)
+            if self.n_shared:
+                quantize_fp8_t(sw13, self.sw13q_t, self.ss13_t)
+                quantize_fp8_t(sw2, self.sw2q_t, self.ss2_t)
+            grouped_ffn_bwd_fp8(D, self.x_perm, self.offsets, x, self.w13q_t, self.s13_t,
+                                self.w2q_t, self.s2_t, self.sw13q_t, self.ss13_t, self.sw2q_t,
+                                self.ss2_t, self.save_pre, self.save_h, self.save_pre_s,
+                                self.save_h_s, self.dout, dy, self.dx_perm, self.dx_shared,
+                                self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws)
+        else:
+            grouped_ffn_bwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
+                            self.save_h, self.save_pre_s, self.save_h_s, self.dout, dy,
+                            self.dx_perm, self.dx_shared, self.dw13, self.dw2, self.dsw13,
+                            self.dsw2, self.ws)
         route_bwd(D, x, w_r, self.scores, self.topk_idx, self.gate, self.dgate, self.y_frac,
                   self.aux_coef, self.lse, self.z_coef, self.dlogits, self.dx_router, self.dw_r,
                   self.ws)

@@ -66,6 +66,7 @@ class Workload:
     bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
     gumbel_tau: Optional[float] = None   # noisy gate temperature; draws uniforms [T, E]
     fp8: bool = False             # forward GEMMs on per-row E4M3 operands (bf16 activations)
+    fp8_bwd: bool = False         # backward data-gradient GEMMs on E4M3 operands as well
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -99,6 +100,12 @@ WORKLOADS = {
     "dsv3_ep8_shard_fp8_bf16": Workload("dsv3_ep8_shard_fp8_bf16", T=8192, d=7168, E=32, k=8,
                                         f=2048, score="sigmoid", n_shared=1, sel_bias=True,
                                         fp8=True),
+    # FP8 forward and FP8 data gradients; weight gradients bf16
+    "mixtral_fp8_dgrad_bf16": Workload("mixtral_fp8_dgrad_bf16", T=8192, d=4096, E=8, k=2,
+                                       f=14336, cf=1.25, fp8=True, fp8_bwd=True),
+    "dsv3_ep8_shard_fp8_dgrad_bf16": Workload("dsv3_ep8_shard_fp8_dgrad_bf16", T=8192, d=7168,
+                                              E=32, k=8, f=2048, score="sigmoid", n_shared=1,
+                                              sel_bias=True, fp8=True, fp8_bwd=True),
 }
 
 

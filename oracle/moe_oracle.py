@@ -12,6 +12,7 @@ Pages cited (titles as printed on them):
   [Balance] "负载均衡策略：MoE训练稳定性保障"
   [ETP]     "ETP专家并行加速MoE模型：ms-swift中稀疏架构的极致优化"
   [VPP]     "MoE模型训练加速10倍？看ms-swift如何通过ETP和VPP实现突破"
+  [Megatron10x] "ms-swift + Megatron：MoE模型加速10倍实测"
 
 Readings taken where the pages are silent, garbled or disagree are listed in
 the repository's design notes; each function names the one it uses.
@@ -339,6 +340,43 @@ def expert_backward(X, w13, w2, saved, dO, act):
     return dX, dw13, dw2, dpre
 
 
+# ------------------------------------------------------------ FP8 backward
+# [Megatron10x] §5.2 trains in FP8 mixed precision and [Recipe] §8.1/§9.1 list
+# FP8 training with bf16 activations; which backward GEMMs run in FP8 is not
+# stated. Reading taken: the two data-gradient GEMMs use the forward's per-row
+# scheme. Their weight operand is the weight read along its input dimension,
+# so it is quantized per row of its transpose (per input channel). The weight
+# gradients, which reduce over tokens, stay on the unquantized values.
+def quantize_weights_fp8_t(w):
+    """Dequantized copy of w^T quantized per row (one scale per input channel
+    of w), shape w.T: the data-gradient GEMMs' weight operand."""
+    return dequantize_rows_fp8(*quantize_rows_fp8(np.asarray(w, dtype=np.float64).T))
+
+
+def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act):
+    """expert_backward with its data-gradient GEMMs on FP8 operands. w2td and
+    w13td come from quantize_weights_fp8_t(w2) and quantize_weights_fp8_t(w13).
+    With bf16 activations, the values that reach a quantizer are the stored
+    bf16 ones: dO, the saved pre-activations a (and b), and dpre.
+      dH   = deq(q(bf16 dO)) @ w2td^T
+      dpre = activation backward of dH on bf16 a (and b)
+      dX   = deq(q(bf16 dpre)) @ w13td^T
+      dW2  = dO^T H,  dW13 = dpre^T X        (unquantized)
+    Returns (dX, dw13, dw2, dpre) as expert_backward does."""
+    H = saved["H"]
+    a = round_bf16(saved["a"])
+    dOd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dO)))
+    dH = dOd @ w2td.T
+    if act == "swiglu":
+        b = round_bf16(saved["b"])
+        dpre = np.concatenate([dH * b * dsilu(a), dH * silu(a)], axis=1)
+    else:
+        dpre = dH * dgelu(a)
+    dpd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dpre)))
+    dX = dpd @ w13td.T
+    return dX, dpre.T @ X, dO.T @ H, dpre
+
+
 def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None, fp8=False):
     """Grouped GEMM of [Recipe] §4.2: the same result as running every
     expert's GEMMs on its own contiguous rows. Optional shared experts
@@ -367,31 +405,42 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
 
 
 def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=None,
-                         sw2=None, dY=None):
+                         sw2=None, dY=None, fp8_dgrad=False):
     """Backward of grouped_ffn_forward: per-expert dgrad and wgrad.
-    The shared expert's upstream gradient is dY itself (gate 1)."""
+    The shared expert's upstream gradient is dY itself (gate 1).
+    fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq)."""
     E = w13.shape[0]
     dX_perm = np.zeros_like(x_perm)
     dw13 = np.zeros_like(w13)
     dw2 = np.zeros_like(w2)
+    dpre_r = np.zeros((x_perm.shape[0], w13.shape[1]))
+
+    def bwd(X, w13e, w2e, sv, g):
+        if fp8_dgrad:
+            return expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),
+                                          quantize_weights_fp8_t(w13e), sv, g, act)
+        return expert_backward(X, w13e, w2e, sv, g, act)
+
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        dx, g13, g2, _ = expert_backward(x_perm[lo:hi], w13[e], w2[e], saved["routed"][e],
-                                         dO[lo:hi], act)
+        dx, g13, g2, dp = bwd(x_perm[lo:hi], w13[e], w2[e], saved["routed"][e], dO[lo:hi])
         dX_perm[lo:hi] = dx
+        dpre_r[lo:hi] = dp
         dw13[e] = g13
         dw2[e] = g2
-    dXs = dsw13 = dsw2 = None
+    dXs = dsw13 = dsw2 = dpre_s = None
     if sw13 is not None:
         dXs = np.zeros_like(x)
         dsw13 = np.zeros_like(sw13)
         dsw2 = np.zeros_like(sw2)
         for s in range(sw13.shape[0]):
-            dx, g13, g2, _ = expert_backward(x, sw13[s], sw2[s], saved["shared"][s], dY, act)
+            dx, g13, g2, dpre_s = bwd(x, sw13[s], sw2[s], saved["shared"][s], dY)
             dXs += dx
             dsw13[s] = g13
             dsw2[s] = g2
-    return dict(dx_perm=dX_perm, dw13=dw13, dw2=dw2, dx_shared=dXs, dsw13=dsw13, dsw2=dsw2)
+    # dpre: gradient of the pre-activations per routed row (and of the last shared expert)
+    return dict(dx_perm=dX_perm, dw13=dw13, dw2=dw2, dx_shared=dXs, dsw13=dsw13, dsw2=dsw2,
+                dpre=dpre_r, dpre_shared=dpre_s)
 
 
 # ----------------------------------------------------------------- combine
@@ -539,13 +588,13 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
 
 
 def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
-                   sw13=None, sw2=None, z_coef=0.0, tau=None):
+                   sw13=None, sw2=None, z_coef=0.0, tau=None, fp8_dgrad=False):
     """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
     router bwd, un-permute."""
     r, p = fwd["router"], fwd["perm"]
     dgate, dO = combine_backward(dY, fwd["O"], r["gates"], p["row_of"])
     g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
-                             sw13, sw2, dY)
+                             sw13, sw2, dY, fp8_dgrad)
     rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
                          aux_coef, fwd["stats"]["y"], z_coef, r["logits"], tau)
     dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])

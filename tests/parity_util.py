@@ -56,7 +56,8 @@ def gpu_layer(w: Workload, g: dict):
     import mixture_experts_layer_28_amd as moe
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
-                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8)
+                     w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
+                     fp8_bwd=w.fp8_bwd)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -70,7 +71,8 @@ def oracle_layer(w: Workload, g: dict):
                           f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], f["gumbel_u"],
                           w.gumbel_tau, fp8=w.fp8)
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
-                           w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau)
+                           w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau,
+                           fp8_dgrad=w.fp8_bwd)
     return fwd, bwd, f
 
 
@@ -87,7 +89,7 @@ class Report:
                          for n, kv in self.lines)
 
 
-def assert_close(name, got, ref, dtype, rep: Report, rel=None, atol=0.0):
+def assert_close(name, got, ref, dtype, rep: Report, rel=None, atol=0.0, max_rel=2e-2, l1_rel=5e-3):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -104,10 +106,10 @@ def assert_close(name, got, ref, dtype, rep: Report, rel=None, atol=0.0):
         r = rel if rel is not None else 1e-5
         assert emax <= r * mx + atol + 1e-30, f"{name}: max|d| {emax:.3e} > {r} * {mx:.3e} + {atol:.1e}"
     else:
-        assert emax <= 2e-2 * mx + atol + 1e-30, \
-            f"{name}: max|d| {emax:.3e} > 2e-2 * {mx:.3e} + {atol:.1e}"
+        assert emax <= max_rel * mx + atol + 1e-30, \
+            f"{name}: max|d| {emax:.3e} > {max_rel} * {mx:.3e} + {atol:.1e}"
         if atol == 0.0 or mx > 1e3 * atol:
-            assert l1 <= 5e-3, f"{name}: mean relative error {l1:.3e} > 5e-3"
+            assert l1 <= l1_rel, f"{name}: mean relative error {l1:.3e} > {l1_rel}"
 
 
 def assert_rows_match(g_idx, g_row_of, o_idx, o_row_of):
@@ -215,7 +217,12 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     # gradients of a row also carry its token's gate: skip rows of flipped tokens
     keep = tok_ok[token_of[g_rows]] if len(g_rows) else np.zeros(0, bool)
     assert_close("dO", to_np(L.dout)[g_rows[keep]], bwd["dO"][o_rows[keep]], dt, rep)
-    assert_close("dX_perm", to_np(L.dx_perm)[g_rows[keep]], bwd["dx_perm"][o_rows[keep]], dt, rep)
+    # outputs computed from a requantized operand (FP8 data gradients) carry
+    # the matrix core's accumulation error amplified by E4M3 rounding: see
+    # check_fp8_dgrad for the exact checks and FP8_DGRAD_TOL for this bound
+    dxt = FP8_DGRAD_TOL if w.fp8_bwd else {}
+    assert_close("dX_perm", to_np(L.dx_perm)[g_rows[keep]], bwd["dx_perm"][o_rows[keep]], dt, rep,
+                 **dxt)
     gw13, gw2 = to_np(L.dw13), to_np(L.dw2)
     assert_close("dW13", gw13[e_ok], bwd["dw13"][e_ok], dt, rep)
     assert_close("dW2", gw2[e_ok], bwd["dw2"][e_ok], dt, rep)
@@ -223,7 +230,7 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     for e in empty:   # an expert without rows has exactly zero gradient
         assert not gw13[e].any() and not gw2[e].any()
     if w.n_shared:
-        assert_close("dX_shared", to_np(L.dx_shared), bwd["dx_shared"], dt, rep)
+        assert_close("dX_shared", to_np(L.dx_shared), bwd["dx_shared"], dt, rep, **dxt)
         assert_close("dSW13", to_np(L.dsw13), bwd["dsw13"], dt, rep)
         assert_close("dSW2", to_np(L.dsw2), bwd["dsw2"], dt, rep)
     # The router gradient can vanish identically (top-1: the one renormalised
@@ -240,8 +247,83 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     if not bad_e:
         assert_close("dW_r", to_np(L.dw_r), bwd["dw_r"], dt, rep,
                      atol=dl_floor * float(np.abs(f["x"]).sum(axis=0).max(initial=0.0)))
-    assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep)
+    assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep, **dxt)
+    if w.fp8_bwd:
+        check_fp8_dgrad(w, L, dev, bwd, rep, g_rows[keep], o_rows[keep], off)
     return len(flips)
+
+
+# FP8 data gradients: dX = deq(q(bf16 dpre)) W13^T. The matrix core's
+# accumulation of the FP8 dH GEMM is good to about 1e-4 of sum|products|
+# (measured); that moves some bf16 dpre values by one bf16 step, and a value
+# near an E4M3 rounding boundary then takes the neighbouring code, one E4M3
+# step (up to 2^-3 relative) away. Applying that perturbation to the oracle
+# itself moves dX by up to 3.1% of max|dX| (mean relative 0.8%) on the
+# DeepSeek-like reduced layer, so GPU-vs-oracle dX is held to 5% / 1.5%;
+# check_fp8_dgrad holds each stage to the bf16 bound separately.
+FP8_DGRAD_TOL = dict(max_rel=5e-2, l1_rel=1.5e-2)
+
+
+def _e4m3_rows_ref(M):
+    """Dequantized per-row E4M3 of M (rows of bf16 values) by an independent
+    route: the scale exponent by a search around log2(amax/448), the codes by
+    torch's float8_e4m3fn cast."""
+    M = np.asarray(M, dtype=np.float64)
+    amax = np.abs(M).max(axis=1, initial=0.0)
+    safe = np.where(amax > 0, amax, 448.0)
+    e = np.floor(np.log2(safe / 448.0)).astype(np.int64) - 1
+    for _ in range(3):                       # smallest e with amax <= 448 * 2^e
+        e = np.where(amax > 448.0 * np.exp2(e.astype(np.float64)), e + 1, e)
+    e = np.where(amax > 0, e, 0)
+    sc = np.exp2(e.astype(np.float64))[:, None]
+    q = torch.from_numpy(M / sc).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64)
+    return q.numpy() * sc
+
+
+def _decode_codes(codes, sexp):
+    """Dequantized rows of device E4M3 codes [n, K] with exponents [n]."""
+    v = codes.cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return v * np.exp2(sexp.cpu().numpy().astype(np.float64))[:, None]
+
+
+def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
+    """The FP8 backward stage by stage: rerun it on the layer's saved tensors
+    into fresh buffers (bitwise identical: deterministic); read its bf16
+    pre-activation gradient dpre from the workspace and compare it with the
+    oracle's; and check dX against the FP8 product of the GPU's own dpre,
+    requantized by _e4m3_rows_ref, with the GPU's transposed weight codes."""
+    import mixture_experts_layer_28_amd as moe
+    dt = w.dtype
+    A = int(off[-1])
+    R, P = w.T * w.k, (2 * w.f if w.act == "swiglu" else w.f)
+    ws = torch.empty_like(L.ws)
+    like = lambda t: torch.empty_like(t) if t is not None else None   # noqa: E731
+    o = {n: like(getattr(L, n)) for n in ("dx_perm", "dx_shared", "dw13", "dw2", "dsw13", "dsw2")}
+    moe.grouped_ffn_bwd_fp8(L.desc, L.x_perm, L.offsets, dev["x"], L.w13q_t, L.s13_t, L.w2q_t,
+                            L.s2_t, L.sw13q_t, L.ss13_t, L.sw2q_t, L.ss2_t, L.save_pre, L.save_h,
+                            L.save_pre_s, L.save_h_s, L.dout, dev["dy"], o["dx_perm"],
+                            o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o["dx_perm"][:A], L.dx_perm[:A]), "FP8 backward is not deterministic"
+    assert torch.equal(o["dw13"], L.dw13) and torch.equal(o["dw2"], L.dw2)
+    dpre = ws[: R * P * 2].view(torch.bfloat16).view(R, P)
+    assert_close("dpre", to_np(dpre)[g_rows], bwd["dpre"][o_rows], dt, rep)
+    w13t = [_decode_codes(L.w13q_t[e], L.s13_t[e]) for e in range(w.E)]   # [d, P] each
+    dp = to_np(dpre)
+    got, ref = [], []
+    for e in range(w.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            ref.append(_e4m3_rows_ref(dp[lo:hi]) @ w13t[e].T)
+            got.append(to_np(L.dx_perm)[lo:hi])
+    if got:
+        assert_close("dX_perm(own dpre)", np.concatenate(got), np.concatenate(ref), dt, rep)
+    if w.n_shared:
+        off_s = (R * P * 2 + 255) // 256 * 256
+        dps = to_np(ws[off_s: off_s + w.T * P * 2].view(torch.bfloat16).view(w.T, P))
+        assert_close("dpre_shared", dps, bwd["dpre_shared"], dt, rep)
+        wst = _decode_codes(L.sw13q_t[0], L.ss13_t[0])
+        assert_close("dX_shared(own dpre)", to_np(L.dx_shared), _e4m3_rows_ref(dps) @ wst.T, dt, rep)
 
 
 def run_and_compare(w: Workload, g=None):

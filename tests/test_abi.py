@@ -21,11 +21,11 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -153,12 +153,15 @@ def test_capacity_matches_oracle(T, k, E, cf):
 
 def test_workspace_sizes_cover_the_layer():
     d = moe.make_desc(8192, 4096, 8, 2, 14336, capacity=2560)
-    sizes = [moe.workspace_size(d, op) for op in range(7)]
+    sizes = [moe.workspace_size(d, op) for op in range(8)]
     # the FP8 forward keeps H's codes and exponents between its two GEMMs
     assert sizes[moe.MOE_OP_FFN_FWD_FP8] >= 8192 * 2 * 14336 + 8192 * 2 * 4
     # backward needs the [T*k, 2f] activation-gradient buffer
     assert sizes[moe.MOE_OP_FFN_BWD] >= 8192 * 2 * 2 * 14336 * 2
     assert sizes[moe.MOE_OP_ROUTE] >= 8192 * 8 * 4
+    # the FP8 backward adds the codes and exponents of dO [T*k, d] and dpre [T*k, 2f]
+    assert sizes[moe.MOE_OP_FFN_BWD_FP8] >= sizes[moe.MOE_OP_FFN_BWD] + 16384 * (4096 + 4) + \
+        16384 * (2 * 14336 + 4)
     with pytest.raises(moe.MoeError):
         moe.workspace_size(d, 99)
 
@@ -242,3 +245,38 @@ def test_fp8_forward_validation():
     assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
     assert call(_desc(), ws_bytes=16) == 3
     assert call(_desc(T=0)) == 0
+
+
+def test_fp8_transposing_quantize_validation():
+    """Bad shapes and pointers fail before any HIP call; G = 0 is a no-op."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ok = dict(src=FAKE, G=2, R=64, C=24, codes=FAKE, sexp=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.moe_quantize_fp8_t(P(a["src"]) if a["src"] else None, a["G"], a["R"], a["C"],
+                                    P(a["codes"]) if a["codes"] else None,
+                                    P(a["sexp"]) if a["sexp"] else None, None)
+    for bad in (dict(R=8), dict(R=72), dict(R=0), dict(C=4), dict(C=12), dict(G=-1),
+                dict(G=70000), dict(src=0), dict(codes=FAKE + 8), dict(sexp=FAKE + 4)):
+        assert call(**bad) == 1, bad
+        assert L.moe_last_error().decode()
+    assert call(G=0) == 0
+
+
+def test_fp8_backward_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE)] * 23
+
+    def call(d, ws_bytes=1 << 40):
+        return L.moe_grouped_ffn_bwd_fp8(ctypes.byref(d), *ptrs, P(FAKE), ws_bytes, None)
+    assert call(_desc(dtype="f32")) == 2
+    assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
+    assert call(_desc(), ws_bytes=16) == 3
+    # a NULL transposed weight is rejected
+    bad = list(ptrs)
+    bad[3] = None
+    assert L.moe_grouped_ffn_bwd_fp8(ctypes.byref(_desc()), *bad, P(FAKE), 1 << 40, None) == 1

@@ -71,3 +71,25 @@ def test_quantize_respects_device_row_bound():
     got_c, got_e = codes.cpu().numpy(), sexp.cpu().numpy()
     assert (got_c[:5] == ref_c[:5]).all() and (got_e[:5] == ref_e[:5]).all()
     assert (got_c[5:] == 0xAB).all() and (got_e[5:] == -12345).all()
+
+
+@pytest.mark.parametrize("G,R,C", [(1, 16, 8), (3, 64, 72), (2, 208, 136), (8, 96, 200),
+                                   (1, 2048, 64), (2, 1040, 24)])
+def test_quantize_transposed_bit_exact(G, R, C):
+    """moe_quantize_fp8_t of [G, R, C] equals the oracle's per-row
+    quantization of the G transposes: partial 64-row and 64-column tiles,
+    the unrolled column-max loop and its tail, special columns."""
+    import mixture_experts_layer_28_amd as moe
+    print(f"[case] quantize transposed G={G} R={R} C={C}", flush=True)
+    # rows of the transposes carry the special patterns, so they become columns
+    bt = _rows(G * C, R, seed=G * 131 + R * 7 + C).reshape(G, C, R)
+    x = _dev_bf16(np.ascontiguousarray(bt.transpose(0, 2, 1)))
+    codes = torch.empty(G, C, R, dtype=torch.uint8, device="cuda")
+    sexp = torch.empty(G, C, dtype=torch.int32, device="cuda")
+    moe.quantize_fp8_t(x, codes, sexp)
+    torch.cuda.synchronize()
+    ref_c, ref_e = O.quantize_rows_fp8(bf16_bits_to_f32(bt.reshape(G * C, R)).astype(np.float64))
+    got_c, got_e = codes.cpu().numpy().reshape(G * C, R), sexp.cpu().numpy().reshape(G * C)
+    assert (got_e == ref_e).all(), np.nonzero(got_e != ref_e)[0][:10]
+    bad = np.argwhere(got_c != ref_c)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"

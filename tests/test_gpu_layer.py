@@ -28,6 +28,10 @@ REDUCED = {
     # FP8 forward GEMMs (routed only; routed + shared with sigmoid scoring)
     "mixtral_fp8_small": WORKLOADS["mixtral_fp8_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True),
+    # FP8 forward and FP8 data gradients (weight gradients bf16)
+    "mixtral_fp8_dgrad_small": WORKLOADS["mixtral_fp8_dgrad_bf16"].replace(T=1536, d=512, f=768),
+    "dsv3_fp8_dgrad_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
+                                                           fp8_bwd=True),
 }
 
 EDGE = {
@@ -60,6 +64,18 @@ EDGE = {
     # FP8 forward with every assignment dropped: the routed GEMMs see no rows
     "fp8_all_dropped_shared": Workload("drop8", T=512, d=256, E=8, k=2, f=256, cf=0.0,
                                        n_shared=1, fp8=True),
+    # FP8 data gradients: ragged sizes with GELU and a shared expert; whole
+    # ring trips (dX: K = 2f = 1280, ten 128-k steps); every assignment
+    # dropped; and FP8 data gradients after a bf16 forward
+    "ragged_fp8_dgrad_gelu_shared": Workload("ragged8d", T=1000, d=144, E=6, k=3, f=208,
+                                             act="gelu", score="sigmoid", n_shared=1,
+                                             sel_bias=True, fp8=True, fp8_bwd=True),
+    "ring_whole_trips_fp8_dgrad": Workload("ring5f8d", T=700, d=320, E=4, k=2, f=640, fp8=True,
+                                           fp8_bwd=True),
+    "fp8_dgrad_all_dropped_shared": Workload("drop8d", T=512, d=256, E=8, k=2, f=256, cf=0.0,
+                                             n_shared=1, fp8=True, fp8_bwd=True),
+    "fp8_dgrad_only": Workload("dg8", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
+                               fp8_bwd=True),
 }
 
 

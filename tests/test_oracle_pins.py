@@ -654,6 +654,84 @@ def _brute_fp8_rows(M):
     return out
 
 
+# ------------------------------------------------------------------ FP8 backward
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_expert_backward_fp8_brute_force(act):
+    """The FP8 expert backward against explicit loops: bf16 dO and W2^T
+    quantized per row by brute force (scale search + library E4M3 cast), the
+    activation backward written out on the bf16 pre-activations, bf16 dpre
+    and W13^T quantized the same way; the weight gradients on the unquantized
+    values."""
+    rng = np.random.default_rng(18)
+    n, d, f = 4, 32, 16
+    P = 2 * f if act == "swiglu" else f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 5)
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 4)
+    _, saved = O.expert_forward(X, w13, w2, act)
+    dO = rng.standard_normal((n, d)) * 0.3
+    dOd = _brute_fp8_rows(O.round_bf16(dO))
+    W2t = _brute_fp8_rows(w2.T.copy())          # [f, d]
+    W13t = _brute_fp8_rows(w13.T.copy())        # [d, P]
+    dH = np.array([[sum(dOd[t, c] * W2t[j, c] for c in range(d)) for j in range(f)]
+                   for t in range(n)])
+    a = O.round_bf16(saved["a"])                 # the stored bf16 pre-activations
+    sg = 1 / (1 + np.exp(-a))
+    if act == "swiglu":
+        b = O.round_bf16(saved["b"])
+        dpre = np.concatenate([dH * b * sg * (1 + a * (1 - sg)), dH * a * sg], axis=1)
+    else:
+        cdf = 0.5 * (1 + sps.erf(a / np.sqrt(2)))
+        dpre = dH * (cdf + a * np.exp(-a * a / 2) / np.sqrt(2 * np.pi))
+    dpd = _brute_fp8_rows(O.round_bf16(dpre))
+    dX = np.array([[sum(dpd[t, p] * W13t[j, p] for p in range(P)) for j in range(d)]
+                   for t in range(n)])
+    gX, g13, g2, gpre = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2),
+                                                 O.quantize_weights_fp8_t(w13), saved, dO, act)
+    np.testing.assert_allclose(gpre, dpre, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gX, dX, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g2, dO.T @ saved["H"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g13, dpre.T @ X, rtol=1e-12, atol=1e-14)
+    # and it stays near the exact backward (quantization error only)
+    ex, _, _, _ = O.expert_backward(X, w13, w2, saved, dO, act)
+    assert np.abs(gX - ex).max() < 0.15 * np.abs(ex).max()
+
+
+def test_expert_backward_fp8_exact_with_per_channel_scales():
+    """When every quantized value is representable, the FP8 backward equals
+    the exact backward bit for bit. Each weight here has one dominant input
+    channel: scaled per input channel (rows of the transpose) every value
+    stays exact, while scaling per output channel would push the small
+    entries into E4M3's subnormal range and round them; the test checks that
+    this wrong axis does change dX, so the pin can catch it."""
+    n, d, f = 6, 16, 8
+    P = 2 * f
+    j0, c0 = 3, 5                                  # dominant input channels of w2, w13
+    small = np.array([1.125, -0.5, 0.75, -1.125, 0.5, -0.75]) * 0.25
+    w2 = np.resize(small, (d, f)).astype(np.float64)
+    w2[:, j0] = 448.0 * 2 ** 6                     # input channel j0 of the down-projection
+    w13 = np.resize(small[::-1], (P, d)).astype(np.float64)
+    w13[:, c0] = -448.0 * 2 ** 5                   # input channel c0 of the up-projection
+    X = np.resize(small, (n, d)) * 4
+    # a = 0: silu = 0, silu' = 1/2; b = 1 except b[:, j0] = 0 (kills the big column of dH)
+    a = np.zeros((n, f))
+    b = np.ones((n, f))
+    b[:, j0] = 0.0
+    saved = dict(a=a, b=b, H=O.silu(a) * b)
+    dO = np.zeros((n, d))
+    for t in range(n):
+        dO[t, (2 * t + 1) % d] = 1.0               # one-hot upstream rows
+    exact = O.expert_backward(X, w13, w2, saved, dO, "swiglu")
+    got = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2), O.quantize_weights_fp8_t(w13),
+                                   saved, dO, "swiglu")
+    for g, e in zip(got, exact):
+        assert np.array_equal(g, e)
+    # the wrong axis (one scale per output channel, i.e. per row of w) loses the small entries
+    wrong = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8(w2).T,
+                                     O.quantize_weights_fp8(w13).T, saved, dO, "swiglu")
+    assert not np.allclose(wrong[0], exact[0], rtol=1e-3, atol=0)
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 def test_expert_forward_fp8_brute_force(act):
     """The FP8 expert forward against explicit loops over brute-force
