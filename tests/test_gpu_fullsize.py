@@ -8,6 +8,7 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
   dsv3_bf16         T=8192  d=7168 E=256 k=8 sigmoid + selection bias (and its
                     update), one shared expert, SwiGLU f=2048
   mixtral_fp8_bf16  the Mixtral-like layer with FP8 (E4M3) forward GEMMs
+  mixtral_fp8_dgrad_bf16  the same with FP8 data-gradient GEMMs as well
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -23,12 +24,16 @@ import torch
 
 import oracle as O
 from moe_inputs import WORKLOADS, as_f64, gen_all
-from parity_util import Report, assert_close, assert_rows_match, bits, gpu_layer, to_np
+from parity_util import (FP8_DGRAD_TOL, Report, assert_close, assert_rows_match, bits, gpu_layer,
+                         to_np)
 
 pytestmark = pytest.mark.gpu
 
 
-def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
+def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
+    """expert_subset: sample only tokens routed entirely to these experts (and
+    weight-gradient columns of them), so that the oracle quantizes only their
+    weights."""
     print(f"[case] full size {w}", flush=True)
     g = gen_all(w)
     L, dev = gpu_layer(w, g)
@@ -89,9 +94,14 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
 
     rng = np.random.default_rng(seed)
     # sampled tokens: routed entirely to unaffected experts and not flipped
-    cand = np.nonzero(tok_ok & e_ok[r["topk_idx"]].all(axis=1))[0]
+    allowed = e_ok.copy()
+    if expert_subset is not None:
+        allowed &= np.isin(np.arange(E), expert_subset)
+    cand = np.nonzero(tok_ok & allowed[r["topk_idx"]].all(axis=1))[0]
+    assert len(cand) > 0, "no token routed entirely to the sampled experts"
     toks = np.sort(rng.choice(cand, size=min(n_tok, len(cand)), replace=False))
-    exps = sorted(set(rng.choice(np.nonzero(e_ok)[0], size=n_exp, replace=False).tolist()))
+    exps = sorted(set(rng.choice(np.nonzero(allowed)[0], size=min(n_exp, int(allowed.sum())),
+                                 replace=False).tolist()))
     gate = r["gates"]
     g_row_of = L.row_of.cpu().numpy()
     g_O, g_H, g_pre = to_np(L.out), to_np(L.save_h), to_np(L.save_pre)
@@ -110,6 +120,17 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
     def wq(m):
         return O.quantize_weights_fp8(m) if w.fp8 else m
     efwd = O.expert_forward_fp8_wq if w.fp8 else O.expert_forward
+    # FP8 data gradients: the weights quantized per input channel (rows of the
+    # transpose), once per expert; any subset of those rows quantizes the same
+    # way, and a token row's dO and dpre are quantized on their own.
+    def ebwd(X, w13e, w2e, w13t, w2t, sv, dO):
+        if w.fp8_bwd:
+            return O.expert_backward_fp8_wq(X, w2t, w13t, sv, dO, w.act)
+        return O.expert_backward(X, w13e, w2e, sv, dO, w.act)
+
+    def wq_t(m):
+        return O.quantize_weights_fp8_t(m) if w.fp8_bwd else None
+    dxt = FP8_DGRAD_TOL if w.fp8_bwd else {}
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
@@ -117,6 +138,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
         w13e = as_f64(g["w13"][e], dt)
         w2e = as_f64(g["w2"][e], dt)
         w13f, w2f = wq(w13e), wq(w2e)   # the forward's weights (FP8-quantized when w.fp8)
+        w13t, w2t = wq_t(w13e), wq_t(w2e)
         for i, t in enumerate(toks):
             for j in range(k):
                 if r["topk_idx"][t, j] != e or pm["row_of"][t, j] < 0:
@@ -126,7 +148,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
                 pre = np.concatenate([sv["a"], sv["b"]], 1) if w.act == "swiglu" else sv["a"]
                 dgate_ref[i, j] = float(dy[t] @ o[0])
                 dO = gate[t, j] * dy[t:t + 1]
-                dxr, _, _, _ = O.expert_backward(x[t:t + 1], w13e, w2e, sv, dO, w.act)
+                dxr, _, _, _ = ebwd(x[t:t + 1], w13e, w2e, w13t, w2t, sv, dO)
                 Y_ref[i] += gate[t, j] * o[0]
                 dX_ref[i] += dxr[0]
                 ref["O"].append(o[0]); got["O"].append(g_O[row])
@@ -144,28 +166,35 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
             J = np.sort(rng.choice(w.f, size=n_col, replace=False))
             rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
             _, sv = efwd(Xe, w13f[rows13], w2f[:, J], w.act)
-            _, d13, d2, _ = O.expert_backward(Xe, w13e[rows13], w2e[:, J], sv, dOe, w.act)
+            # hidden columns J only: dH[:, J] needs rows J of w2's transpose
+            # (dX of this call is not used: it would need all of dpre's row)
+            _, d13, d2, _ = ebwd(Xe, w13e[rows13], w2e[:, J],
+                                 None if w13t is None else w13t[:, rows13],
+                                 None if w2t is None else w2t[J], sv, dOe)
             dw13_ref.append(d13)
             dw2_ref.append(d2)
             dw13_got.append(to_np(L.dw13[e][torch.as_tensor(rows13, device="cuda")]))
             dw2_got.append(to_np(L.dw2[e][:, torch.as_tensor(J, device="cuda")]))
-        del w13e, w2e, w13f, w2f
+        del w13e, w2e, w13f, w2f, w13t, w2t
     if w.n_shared:
         # the shared expert: sampled tokens' outputs and input gradients, and
         # sampled hidden columns of its weight gradients over all tokens
         sw13 = as_f64(g["sw13"][0], dt)
         sw2 = as_f64(g["sw2"][0], dt)
         sw13f, sw2f = wq(sw13), wq(sw2)
+        sw13t, sw2t = wq_t(sw13), wq_t(sw2)
         os_, svs = efwd(x[toks], sw13f, sw2f, w.act)
-        dxs, _, _, _ = O.expert_backward(x[toks], sw13, sw2, svs, dy[toks], w.act)
+        dxs, _, _, _ = ebwd(x[toks], sw13, sw2, sw13t, sw2t, svs, dy[toks])
         Y_ref += os_
         dX_ref += dxs
         assert_close("O_shared", to_np(L.out_shared)[toks], os_, dt, rep)
-        assert_close("dX_shared", to_np(L.dx_shared)[toks], dxs, dt, rep)
+        assert_close("dX_shared", to_np(L.dx_shared)[toks], dxs, dt, rep, **dxt)
         J = np.sort(rng.choice(w.f, size=n_col, replace=False))
         rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
         _, sv = efwd(x, sw13f[rows13], sw2f[:, J], w.act)
-        _, d13, d2, _ = O.expert_backward(x, sw13[rows13], sw2[:, J], sv, dy, w.act)
+        _, d13, d2, _ = ebwd(x, sw13[rows13], sw2[:, J],
+                             None if sw13t is None else sw13t[:, rows13],
+                             None if sw2t is None else sw2t[J], sv, dy)
         assert_close("dSW13[sampled]", to_np(L.dsw13[0][torch.as_tensor(rows13, device="cuda")]),
                      d13, dt, rep)
         assert_close("dSW2[sampled]", to_np(L.dsw2[0][:, torch.as_tensor(J, device="cuda")]), d2,
@@ -173,7 +202,8 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
         del sw13, sw2
     print("[step] sampled oracle done", flush=True)
     for k_ in ref:
-        assert_close(k_, np.array(got[k_]), np.array(ref[k_]), dt, rep)
+        assert_close(k_, np.array(got[k_]), np.array(ref[k_]), dt, rep,
+                     **(dxt if k_ == "dxp" else {}))
     # router backward of the sampled tokens (batch-wide 1/T factors), then Y / dgate / dX rows
     rb = O.router_backward(x[toks], w_r, r["scores"][toks], r["topk_idx"][toks], gate[toks],
                            dgate_ref, w.score, w.aux_coef, st["y"], w.z_coef, r["logits"][toks],
@@ -183,7 +213,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
     assert_close("dgate", to_np(L.dgate)[toks], dgate_ref, dt, rep)
     dl_floor = 2e-6 * float(np.abs(dgate_ref).max(initial=0.0))
     assert_close("dlogits", to_np(L.dlogits)[toks], rb["dlogits"], dt, rep, atol=dl_floor)
-    assert_close("dX", to_np(L.dX)[toks], dX_ref, dt, rep)
+    assert_close("dX", to_np(L.dX)[toks], dX_ref, dt, rep, **dxt)
     if dw13_ref:
         assert_close("dW13[sampled]", np.array(dw13_got), np.array(dw13_ref), dt, rep)
         assert_close("dW2[sampled]", np.array(dw2_got), np.array(dw2_ref), dt, rep)
@@ -195,6 +225,10 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123):
 
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
-                                  "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16"])
+                                  "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16",
+                                  "mixtral_fp8_dgrad_bf16"])
 def test_fullsize_sampled(name):
-    check_sampled(WORKLOADS[name])
+    w = WORKLOADS[name]
+    # the oracle's FP8 backward quantizes each sampled expert's weights both
+    # ways (about 45 s per Mixtral-like expert on the host): two experts
+    check_sampled(w, expert_subset=(2, 5) if w.fp8_bwd else None)
