@@ -409,7 +409,8 @@ static hipError_t launch_one(const GemmArgs& p, hipStream_t s) {
     tiles = ((p.max_rows + kRows - 1) / kRows + p.G) * nt;
   else
     tiles = (int64_t)p.G * ((p.M + kRows - 1) / kRows) * nt;
-  const int64_t nb = (tiles + 7) / 8 * 8;
+  const int64_t nb = RAG == RAG_K ? rag_k_grid(p.G, ((p.M + kRows - 1) / kRows) * nt)
+                                  : (tiles + 7) / 8 * 8;
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI, AKM, BKM, RAG>), dim3((unsigned)nb), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -162,7 +162,8 @@ static hipError_t launch_f32(const GemmArgs& p, hipStream_t s) {
   else
     tiles = (int64_t)p.G * ((p.M + BM - 1) / BM) * nt;
   if (tiles == 0) return hipSuccess;
-  const int64_t nb = (tiles + 7) / 8 * 8;
+  const int64_t nb = RAG == RAG_K ? rag_k_grid(p.G, ((p.M + BM - 1) / BM) * nt)
+                                  : (tiles + 7) / 8 * 8;
   const unsigned ny = (RAG == RAG_NONE && p.k_splits > 1) ? (unsigned)p.k_splits : 1u;
   hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, TC, BM, BN, AKM, BKM, EPI, RAG>),
                      dim3((unsigned)nb, ny), dim3(256), 0, s, p);

@@ -128,6 +128,10 @@ struct Tile {
   int64_t m0, n0;  // tile origin (n0 in output columns; H columns for the fused SwiGLU)
 };
 
+// Workgroups a RAG_K launch needs (see resolve_tile): 8 * G * ceil(per / 8)
+// for per = tiles per group.
+inline int64_t rag_k_grid(int64_t G, int64_t per) { return 8 * G * ((per + 7) / 8); }
+
 // Map this workgroup to a tile; false = no tile (surplus workgroup).
 // BNo: output columns per tile. s_tiles must hold >= G+1 ints, s_wsum 4 ints.
 template <int BM, int BNo, int RAG>
@@ -151,11 +155,27 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, in
   }
   const int64_t mtg = (p.M + BM - 1) / BM;
   const int64_t per = mtg * nt;
-  const int64_t L = xcd_tile(per * p.G);
-  if (L < 0) return false;
-  t.g = (int)(L / per);
+  int64_t Lg;   // tile within its group
+  if (RAG == RAG_K) {
+    // The groups' K (their row counts) differ, so a group's tiles cost
+    // differently from another's. Each group's tiles are split into 8
+    // contiguous runs and XCD x takes run x of every group, in group order:
+    // every XCD does the same share of every group (a contiguous split of
+    // all tiles would give each XCD whole groups). The grid holds
+    // 8 * G * ceil(per / 8) workgroups (rag_k_grid).
+    const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int64_t lo = x * per / 8, n = (x + 1) * per / 8 - lo;
+    if (n == 0 || i >= n * p.G) return false;
+    t.g = (int)(i / n);
+    Lg = lo + i % n;
+  } else {
+    const int64_t L = xcd_tile(per * p.G);
+    if (L < 0) return false;
+    t.g = (int)(L / per);
+    Lg = L - (int64_t)t.g * per;
+  }
   int64_t mt, ntile;
-  band_order(L - (int64_t)t.g * per, mtg, nt, mt, ntile);
+  band_order(Lg, mtg, nt, mt, ntile);
   t.m0 = mt * BM;
   t.n0 = ntile * BNo;
   t.M = p.M;
