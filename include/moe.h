@@ -179,6 +179,9 @@ int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, in
  *   save_pre_s, save_h_s: the same for the shared expert ([T, ...]) out or NULL
  *   out      [T*k, d] dt                                            out (O per row)
  *   out_shared [T, d] dt or NULL                                    out
+ *   ws       MOE_OP_FFN_FWD bytes: bf16 splits the down-projection's last,
+ *            partial round of tiles over K, and keeps its partial sums and
+ *            counters here (fp32: none)                             scratch
  */
 int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                         const void* x, const void* w13, const void* w2, const void* sw13,
@@ -244,6 +247,8 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
  *   dout [T*k, d] dt (from moe_combine_bwd), dy [T, d] dt (shared; may be NULL if n_shared == 0)
  *   dx_perm [T*k, d] dt, dx_shared [T, d] dt or NULL                out
  *   dw13, dw2 (routed weight shapes), dsw13, dsw2 or NULL           out
+ *   ws   MOE_OP_FFN_BWD bytes: dpre, then (bf16) the dX GEMM's split-K
+ *        partials for its last round of tiles                        scratch
  */
 int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                         const void* x, const void* w13, const void* w2, const void* sw13,

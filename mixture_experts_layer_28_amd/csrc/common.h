@@ -138,6 +138,17 @@ struct GemmArgs {
   const int32_t* a_sexp;
   const int32_t* b_sexp;
   int64_t b_sexp_gstride;
+  // bf16 RAG_M plain-store GEMMs: split-K of each XCD's last, partial round of
+  // tiles. tail_ws (null = off) holds tail_counters(cus) zeroed int32 counters,
+  // then the fp32 partial accumulators; tail_cus = CUs per XCD.
+  void* tail_ws;
+  int tail_cus;
 };
+
+// Tail split-K workspace (see GemmArgs::tail_ws) for `cus` CUs per XCD: a
+// counter per possible tail tile (at most cus/2 per XCD), then a 256 KiB
+// partial per split item (at most cus per XCD).
+__host__ __device__ inline size_t tail_counter_bytes(int cus) { return ((size_t)8 * cus * 4 + 255) / 256 * 256; }
+__host__ __device__ inline size_t tail_ws_bytes(int cus) { return tail_counter_bytes(cus) + (size_t)8 * cus * 262144; }
 
 }  // namespace moe

@@ -126,6 +126,11 @@ struct Tile {
   int64_t r0;      // first routed row of the group
   int64_t M, K;    // this group's M and K
   int64_t m0, n0;  // tile origin (n0 in output columns; H columns for the fused SwiGLU)
+  // tail split-K (RAG_M with GemmArgs::tail_ws): this item computes k-steps
+  // [part*ceil(nk/S), ...) of its tile; `slot` indexes the tile's counter
+  // (x*cus + j) and its S partials start at item x*cus + j*S. S = 1: whole tile.
+  int S = 1, part = 0;
+  int64_t slot = 0, item = 0;
 };
 
 // Workgroups a RAG_K launch needs (see resolve_tile): 8 * G * ceil(per / 8)
@@ -141,8 +146,38 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, in
   if (RAG == RAG_M) {
     group_tile_prefix<BM>(p.offsets, p.G, s_tiles, s_wsum);
     const int64_t total = s_tiles[p.G];
-    const int64_t L = xcd_tile(total * nt);
-    if (L < 0) return false;
+    int64_t L;
+    if (p.tail_ws) {
+      // XCD x runs its n tiles (the xcd_tile split) on cus CUs: n / cus whole
+      // rounds, then r = n mod cus tiles. When r <= cus / 2, each of those r
+      // is split into S = min(4, cus / r) parts over K, so the last round
+      // runs r*S shorter items instead of r long ones on an idle XCD.
+      const int64_t V = total * nt;
+      const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, cus = p.tail_cus;
+      const int64_t lo = x * V / 8, n = (x + 1) * V / 8 - lo;
+      const int64_t r = n % cus, full = n - r;
+      if (r > 0 && 2 * r <= cus) {
+        const int64_t S = cus / r < 4 ? cus / r : 4;
+        if (i < full) {
+          L = lo + i;
+        } else if (i < full + r * S) {
+          const int64_t j = (i - full) / S;
+          L = lo + full + j;
+          t.S = (int)S;
+          t.part = (int)((i - full) % S);
+          t.slot = x * cus + j;
+          t.item = x * cus + j * S;
+        } else {
+          return false;
+        }
+      } else {
+        if (i >= n) return false;
+        L = lo + i;
+      }
+    } else {
+      L = xcd_tile(total * nt);
+      if (L < 0) return false;
+    }
     int64_t mt, ntile;
     band_order(L, total, nt, mt, ntile);
     t.g = find_group(s_tiles, p.G, mt);

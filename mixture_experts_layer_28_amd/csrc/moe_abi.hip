@@ -210,6 +210,37 @@ int route_bwd_splits(const moe_desc* d) {
   return (int)s;
 }
 
+// Split-K of the last, partial round of tiles (bf16 plain-store grouped GEMMs)
+// sizes its workspace for at most kTailCusMax CUs per XCD.
+constexpr int kTailCusMax = 32;
+
+// CUs per XCD of the current device for the tail split (0 = off: unknown, or
+// not eight equal XCDs), capped at kTailCusMax. Cached per device.
+int tail_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev] = (n > 0 && n % 8 == 0) ? (n / 8 < kTailCusMax ? n / 8 : kTailCusMax) : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+// Turn on the tail split for GEMM q with workspace region `tw` (counters cleared).
+int enable_tail(GemmArgs& q, void* tw, hipStream_t s) {
+  const int c = tail_cus();
+  if (c <= 0) return MOE_OK;
+  {
+    Scope sc(K_FILL, s);
+    MOE_TRY(hip_check(launch_fill_zero(tw, tail_counter_bytes(c), s), "clear tail counters"));
+  }
+  q.tail_ws = tw;
+  q.tail_cus = c;
+  return MOE_OK;
+}
+
 size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
   switch (op) {
@@ -219,10 +250,11 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return align256(nb * E * 8) + align256(nb * E * 4) + align256(nb * 8);
     }
     case MOE_OP_PERMUTE: return align256((size_t)((T + 63) / 64) * E * 4);
-    case MOE_OP_FFN_FWD: return 0;
+    case MOE_OP_FFN_FWD: return d->dtype == MOE_BF16 ? tail_ws_bytes(kTailCusMax) : 0;
     case MOE_OP_FFN_BWD:
       return align256((size_t)T * d->k * pre_cols(d) * esize(d)) +
-             (d->n_shared ? align256((size_t)T * pre_cols(d) * esize(d)) : 0);
+             (d->n_shared ? align256((size_t)T * pre_cols(d) * esize(d)) : 0) +
+             (d->dtype == MOE_BF16 ? tail_ws_bytes(kTailCusMax) : 0);
     case MOE_OP_ROUTE_BWD: {
       if (E <= 8) return align256((size_t)router_dw_small_chunks((int)T) * E * d->d * 4);
       const int S = route_bwd_splits(d);
@@ -537,6 +569,7 @@ int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t*
     q.N = d;
     q.K = f;
     q.max_rows = p.max_rows;
+    if (!shared && desc->dtype == MOE_BF16) MOE_TRY(enable_tail(q, ws, s));
     MOE_TRY(run_gemm(desc, q, true, true, EPI_STORE, rag, s, "ffn fwd down matrix",
                      shared ? K_SH_FWD_DOWN : K_FWD_DOWN));
   }
@@ -713,6 +746,8 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
   }
   void* dpre_r = ws;
   void* dpre_s = (char*)ws + align256((size_t)desc->T * desc->k * P * esize(desc));
+  // after the dpre regions: the dX GEMM's tail split-K workspace (bf16)
+  char* tail_w = (char*)dpre_s + (desc->n_shared ? align256((size_t)desc->T * P * esize(desc)) : 0);
   const int epi_b = desc->act == MOE_SWIGLU ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
     const int ragm = shared ? RAG_NONE : RAG_M;
@@ -754,6 +789,7 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
     q.N = d;
     q.K = P;
     q.max_rows = p.max_rows;
+    if (!shared && desc->dtype == MOE_BF16) MOE_TRY(enable_tail(q, tail_w, s));
     MOE_TRY(run_gemm(desc, q, true, false, EPI_STORE, ragm, s, "ffn dgrad first matrix",
                      shared ? K_SH_DGRAD_UP : K_DGRAD_UP));
     // wgrad 2: dW2 = dO^T H (reduce over the expert's rows)
