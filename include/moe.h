@@ -228,7 +228,8 @@ int moe_quantize_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
  *   sw13q, ss13, sw2q, ss2: the shared expert's, or NULL                   in
  *   save_pre, save_h, save_pre_s, save_h_s, out, out_shared: as in
  *     moe_grouped_ffn_fwd (bf16)                                           out
- *   ws         MOE_OP_FFN_FWD_FP8 bytes (H codes and exponents)            scratch
+ *   ws         MOE_OP_FFN_FWD_FP8 bytes (H codes and exponents, then the
+ *              down-projection's split-K partials for its last round)  scratch
  */
 int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int32_t* sx_perm,
                             const int32_t* offsets, const void* xq, const int32_t* sx,
@@ -297,7 +298,8 @@ int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* c
  *   w13q_t [E, d, P] uint8, s13_t [E, d] int32  (moe_quantize_fp8_t of w13 [E, P, d])   in
  *   sw2q_t, ss2_t, sw13q_t, ss13_t: the shared expert's, or NULL                       in
  *   the other arguments are as in moe_grouped_ffn_bwd
- *   ws  MOE_OP_FFN_BWD_FP8 bytes (dpre, and the FP8 codes and exponents)               scratch
+ *   ws  MOE_OP_FFN_BWD_FP8 bytes (moe_grouped_ffn_bwd's layout: dpre and the dX GEMM's
+ *       split-K partials; then the FP8 codes and exponents)                            scratch
  */
 int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                             const void* x, const void* w13q_t, const int32_t* s13_t,

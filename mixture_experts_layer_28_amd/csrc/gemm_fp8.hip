@@ -126,11 +126,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int64_t nk = (t.K + kBK8 - 1) / kBK8;
+  // k-steps of this tile; a tail split-K item takes its part of them
+  constexpr bool TAIL = EPI == EPI_STORE && RAG == RAG_M;
+  int64_t nk = (t.K + kBK8 - 1) / kBK8;
+  int64_t kbase = 0;
+  if (TAIL && t.S > 1) {
+    const int64_t per = (nk + t.S - 1) / t.S;
+    kbase = per * t.part;
+    nk = kbase >= nk ? 0 : (nk - kbase < per ? nk - kbase : per);
+  }
 
   // DMA instruction i (0..7) of operand X (0 = A, 1 = B) of k-step kt into buffer s
   auto dma = [&](int64_t kt, int X, char* s, int i) __attribute__((always_inline)) {
-    const int64_t k0 = kt * kBK8;
+    const int64_t k0 = (kbase + kt) * kBK8;
     const Dma8& d = X == 0 ? da : db;
     const bool kin = d.kk[i] < t.K - k0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? ra : rb, (lds_void*)(s + (wave * 8 + i) * 1024), 16,
@@ -217,6 +225,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
+  }
+
+  if constexpr (TAIL) {
+    if (t.S > 1) {
+      // Tail split-K, as in the bf16 GEMM: store this item's fp32
+      // accumulators ([register][thread]), count the tile's arrived items;
+      // the last adds the S partials in part order and stores the tile (the
+      // per-row exponents apply to the sum as to a whole tile's accumulators).
+      char* tw = reinterpret_cast<char*>(p.tail_ws);
+      float* parts = reinterpret_cast<float*>(tw + tail_counter_bytes(p.tail_cus));
+      float* mine = parts + (t.item + t.part) * 65536;
+      static_for<MI * NI>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(q * 16 + r) * 256 + tid] = acc[q / NI][q % NI][r];
+      });
+      __threadfence();
+      __syncthreads();
+      int* last = reinterpret_cast<int*>(h4);   // the ring is idle now; stages use h0, h1
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(reinterpret_cast<int*>(tw) + t.slot, 1,
+                                               __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *last = old == t.S - 1;
+      }
+      __syncthreads();
+      if (!*last) return;
+      __threadfence();
+      const float* all = parts + t.item * 65536;
+      const int S = t.S;
+      static_for<MI * NI>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        float w[4][16];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            w[sp][r] = all[(int64_t)(sp < S ? sp : S - 1) * 65536 + (q * 16 + r) * 256 + tid];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = w[0][r];
+          v += S > 1 ? w[1][r] : 0.f;
+          v += S > 2 ? w[2][r] : 0.f;
+          v += S > 3 ? w[3][r] : 0.f;
+          acc[q / NI][q % NI][r] = v;
+        }
+      });
+    }
   }
 
   // ---- epilogue: stage each 32-row block row in fp32 (a stage per wave),
@@ -366,7 +421,9 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
     tiles = ((p.max_rows + kRows8 - 1) / kRows8 + p.G) * nt;
   else
     tiles = (int64_t)p.G * ((p.M + kRows8 - 1) / kRows8) * nt;
-  const int64_t nb = (tiles + 7) / 8 * 8;
+  int64_t nb = (tiles + 7) / 8 * 8;
+  // tail split-K: up to tail_cus more items per XCD
+  if (RAG == RAG_M && EPI == EPI_STORE && p.tail_ws) nb += 8 * (int64_t)p.tail_cus;
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG>), dim3((unsigned)nb), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -261,10 +261,11 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
     }
     case MOE_OP_FFN_FWD_FP8: {
-      // FP8 codes and scale exponents of H between the two GEMMs
+      // FP8 codes and scale exponents of H between the two GEMMs, then the
+      // down-projection's split-K tail
       size_t b = align256((size_t)T * d->k * d->f) + align256((size_t)T * d->k * 4);
       if (d->n_shared) b += align256((size_t)T * d->f) + align256((size_t)T * 4);
-      return b;
+      return b + tail_ws_bytes(kTailCusMax);
     }
     case MOE_OP_FFN_BWD_FP8:
       // the bf16 backward's pre-activation gradients, then FP8 codes and
@@ -646,6 +647,7 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
   int32_t* hs = (int32_t*)(w + align256((size_t)T * desc->k * f));
   uint8_t* hq_s = (uint8_t*)((char*)hs + align256((size_t)T * desc->k * 4));
   int32_t* hs_s = desc->n_shared ? (int32_t*)((char*)hq_s + align256((size_t)T * f)) : nullptr;
+  char* tail_w = w + ws_bytes_for(desc, MOE_OP_FFN_FWD_FP8) - tail_ws_bytes(kTailCusMax);
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
     const int rag = shared ? RAG_NONE : RAG_M;
     GemmArgs p = blank();
@@ -696,6 +698,7 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
     q.N = d;
     q.K = f;
     q.max_rows = p.max_rows;
+    if (!shared) MOE_TRY(enable_tail(q, tail_w, s));
     Scope sc(shared ? K_SH_FWD_DOWN : K_FWD_DOWN, s);
     MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, rag, s), "fp8 ffn fwd down matrix"));
   }
@@ -900,6 +903,8 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
   char* wb = (char*)ws;
   void* dpre_r = wb;
   void* dpre_s = wb + align256((size_t)T * desc->k * P * 2);
+  // the bf16 backward's layout: after the dpre regions, the dX GEMM's split-K tail
+  char* tail_w = (char*)dpre_s + (desc->n_shared ? align256((size_t)T * P * 2) : 0);
   char* w8 = wb + ws_bytes_for(desc, MOE_OP_FFN_BWD);
   uint8_t* gq = (uint8_t*)w8;
   int32_t* gs = (int32_t*)(w8 + align256((size_t)T * desc->k * d));
@@ -966,6 +971,7 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
     q.N = d;
     q.K = P;
     q.max_rows = p.max_rows;
+    if (!shared) MOE_TRY(enable_tail(q, tail_w, s));
     {
       Scope sc(shared ? K_SH_DGRAD_UP : K_DGRAD_UP, s);
       MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, ragm, s), "fp8 ffn dgrad first matrix"));
