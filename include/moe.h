@@ -283,6 +283,25 @@ int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t*
 int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
                        int32_t* scale_exp, void* stream);
 
+/* moe_quantize_fp8_both: moe_quantize_fp8 of the rows of G row-major R x C
+ * bf16 matrices and moe_quantize_fp8_t of their columns, with the same codes
+ * and exponents as the two separate calls. It takes two reads of src instead
+ * of three: the row pass also keeps per-column maxima (a partial per 64 rows,
+ * in ws), then the transposes are written with the column exponents. It is
+ * for a layer whose forward and data gradients both run in FP8: the forward
+ * quantizes each weight this way, and the backward uses the transposed codes.
+ *   src          [G, R, C] bf16                          in
+ *   codes        [G, R, C] uint8, scale_exp [G, R] int32  out (rows)
+ *   codes_t      [G, C, R] uint8, scale_exp_t [G, C] int32 out (columns)
+ *   ws           G * ceil(R / 64) * C * 2 bytes, rounded up to a multiple of
+ *                256, 256-byte aligned                    scratch
+ * Constraints: R a multiple of 16 in [16, 2^22]; C a multiple of 16 in
+ * [16, 32768]; 0 <= G <= 65535; src, codes and exponent pointers 16-byte aligned.
+ */
+int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                          int32_t* scale_exp, void* codes_t, int32_t* scale_exp_t, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* moe_grouped_ffn_bwd_fp8: moe_grouped_ffn_bwd with its two data-gradient
  * GEMMs on FP8 operands. Per group:
  *   1. the upstream gradient rows are quantized per row;

@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
-    "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8",
+    "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8", "moe_quantize_fp8_both",
 )
 
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int64, _P, _P],
             "moe_grouped_ffn_fwd_fp8": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
             "moe_quantize_fp8_t": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
+            "moe_quantize_fp8_both": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P,
+                                      _P, ctypes.c_size_t, _P],
             "moe_grouped_ffn_bwd_fp8": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
@@ -241,6 +243,31 @@ def quantize_fp8_t(src, codes, scale_exp, stream=None):
         raise ValueError("codes must be [..., C, R] and scale_exp [..., C] for src [..., R, C]")
     _check("moe_quantize_fp8_t", lib().moe_quantize_fp8_t(_p(src), G, R, C, _p(codes),
                                                           _p(scale_exp), _stream(stream)))
+
+
+def quantize_fp8_both_ws(src_shape) -> int:
+    """Workspace bytes of quantize_fp8_both for a bf16 tensor of shape [..., R, C]."""
+    R, C = src_shape[-2], src_shape[-1]
+    G = 1
+    for n in src_shape[:-2]:
+        G *= n
+    return (G * ((R + 63) // 64) * C * 2 + 255) // 256 * 256
+
+
+def quantize_fp8_both(src, codes, scale_exp, codes_t, scale_exp_t, ws, stream=None):
+    """Rows and columns of bf16 matrices src [..., R, C] in one call (two reads
+    of src): codes [..., R, C] with scale_exp [..., R], and the transposes'
+    codes_t [..., C, R] with scale_exp_t [..., C]; ws: quantize_fp8_both_ws bytes."""
+    R, C = src.shape[-2], src.shape[-1]
+    G = src.numel() // (R * C) if R * C else 0
+    lead = src.shape[:-2]
+    if codes.shape != src.shape or scale_exp.shape != lead + (R,) or \
+            codes_t.shape != lead + (C, R) or scale_exp_t.shape != lead + (C,):
+        raise ValueError("codes [..., R, C], scale_exp [..., R], codes_t [..., C, R], scale_exp_t [..., C]")
+    wp, wn = _ws(ws)
+    _check("moe_quantize_fp8_both", lib().moe_quantize_fp8_both(
+        _p(src), G, R, C, _p(codes), _p(scale_exp), _p(codes_t), _p(scale_exp_t), wp, wn,
+        _stream(stream)))
 
 
 def grouped_ffn_bwd_fp8(desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t, ss13_t,

@@ -17,6 +17,9 @@ hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hi
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
 hipError_t launch_quant_fp8_t(const void*, int64_t, int64_t, int64_t, void*, int32_t*, hipStream_t);
+hipError_t launch_quant_fp8_both(const void*, int64_t, int64_t, int64_t, void*, int32_t*, void*,
+                                 int32_t*, void*, hipStream_t);
+size_t quant_fp8_both_ws(int64_t, int64_t, int64_t);
 hipError_t launch_quant_fp8(const void*, int64_t, int64_t, int64_t, const int32_t*, void*, int64_t,
                             int32_t*, hipStream_t);
 hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
@@ -845,6 +848,35 @@ int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* c
   Scope sc(K_QUANT_FP8, (hipStream_t)stream);
   return hip_check(launch_quant_fp8_t(src, G, R, C, codes, scale_exp, (hipStream_t)stream),
                    "fp8 transposing quantize");
+}
+
+int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                          int32_t* scale_exp, void* codes_t, int32_t* scale_exp_t, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (G < 0 || G > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "G must be in [0, 65535] (got %lld)", (long long)G);
+  if (R < 16 || R % 16 || R > (int64_t(1) << 22))
+    return fail(MOE_ERR_INVALID_ARG, "R must be a positive multiple of 16, at most 2^22 (got %lld)",
+                (long long)R);
+  if (C < 16 || C % 16 || C > 32768)
+    return fail(MOE_ERR_INVALID_ARG, "C must be a positive multiple of 16, at most 32768 (got %lld)",
+                (long long)C);
+  MOE_TRY(need(src, "src"));
+  MOE_TRY(need(codes, "codes"));
+  MOE_TRY(need(scale_exp, "scale_exp"));
+  MOE_TRY(need(codes_t, "codes_t"));
+  MOE_TRY(need(scale_exp_t, "scale_exp_t"));
+  if (G == 0) return MOE_OK;
+  const size_t need_ws = quant_fp8_both_ws(G, R, C);
+  if (!ws || ws_bytes < need_ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_ws, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(MOE_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  Scope sc(K_QUANT_FP8, (hipStream_t)stream);
+  return hip_check(launch_quant_fp8_both(src, G, R, C, codes, scale_exp, codes_t, scale_exp_t, ws,
+                                         (hipStream_t)stream),
+                   "fp8 quantize both orientations");
 }
 
 int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,

@@ -196,7 +196,159 @@ __global__ __launch_bounds__(256) void transpose_quant_fp8_kernel(const bf16_t* 
   *reinterpret_cast<uint4*>(codes + (g * C + c) * R + r) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// ---- both orientations with two reads of the source: rows and column
+// maxima in one pass, then the transpose with the column exponents.
+
+constexpr int kBR = 64;   // rows per workgroup of the fused pass
+
+__device__ __forceinline__ uint32_t max_pairs(uint32_t a, uint32_t w) {
+  // lanes (lo, hi) of two packed 15-bit magnitude pairs
+  const uint32_t lo = (a & 0xffffu) > (w & 0x7fffu) ? (a & 0xffffu) : (w & 0x7fffu);
+  const uint32_t hi = (a >> 16) > ((w >> 16) & 0x7fffu) ? (a >> 16) : ((w >> 16) & 0x7fffu);
+  return lo | (hi << 16);
+}
+
+// Workgroup (b, g) quantizes rows 64b .. 64b+63 of src[g] as
+// quant_rows_fp8_kernel does, RB rows at a time (TPR = 256 / RB threads per
+// row, up to 16 chunks of 8 columns each), and keeps each column's running
+// maximum |value|; the RB row slots' maxima are folded in LDS and written as
+// partial[g][b][c] (bf16 magnitude bit patterns). C <= 4096 * 8 / RB.
+template <int RB>
+__global__ __launch_bounds__(256) void rows_colmax_fp8_kernel(const bf16_t* __restrict__ src,
+                                                              int64_t R, int64_t C,
+                                                              uint8_t* __restrict__ codes,
+                                                              int32_t* __restrict__ sexp,
+                                                              uint16_t* __restrict__ partial) {
+  constexpr int TPR = 256 / RB, NCH = 16;
+  const int64_t g = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
+  const int tid = threadIdx.x, slot = tid / TPR, t = tid % TPR, wave = tid >> 6;
+  const int64_t nch = C / 8;
+  __shared__ uint32_t wred[4];
+  __shared__ uint16_t scm[32768];
+  uint32_t cm[NCH][4];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cm[u][i] = 0;
+  for (int grp = 0; grp < kBR / RB; ++grp) {
+    const int64_t row = b * kBR + grp * RB + slot;
+    const bool rok = row < R;
+    const uint4* s = reinterpret_cast<const uint4*>(src + (g * R + (rok ? row : 0)) * C);
+    uint4 cache[NCH];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int64_t c = t + (int64_t)u * TPR;
+      cache[u] = (rok && c < nch) ? s[c] : make_uint4(0, 0, 0, 0);
+      m = absmax8(cache[u], m);
+    }
+    // the row's maximum over its TPR threads
+#pragma unroll
+    for (int o = (TPR < 64 ? TPR : 64) / 2; o > 0; o >>= 1) {
+      const uint32_t x = __shfl_xor(m, o, 64);
+      m = x > m ? x : m;
+    }
+    if constexpr (TPR > 64) {
+      if ((tid & 63) == 0) wred[wave] = m;
+      __syncthreads();
+      m = 0;
+#pragma unroll
+      for (int w = 0; w < TPR / 64; ++w) {
+        const uint32_t x = wred[slot * (TPR / 64) + w];
+        m = x > m ? x : m;
+      }
+      __syncthreads();
+    }
+    const float amax = bf2f(m);
+    int ex = 0;
+    const float mant = frexpf(amax, &ex);
+    const int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+    if (rok && t == 0) sexp[g * R + row] = e;
+    uint2* q = reinterpret_cast<uint2*>(codes + (g * R + row) * C);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int64_t c = t + (int64_t)u * TPR;
+      if (rok && c < nch) q[c] = to_e4m3(cache[u], e);
+      cm[u][0] = max_pairs(cm[u][0], cache[u].x);
+      cm[u][1] = max_pairs(cm[u][1], cache[u].y);
+      cm[u][2] = max_pairs(cm[u][2], cache[u].z);
+      cm[u][3] = max_pairs(cm[u][3], cache[u].w);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int64_t c = t + (int64_t)u * TPR;
+    if (c < nch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        scm[slot * C + c * 8 + 2 * i] = (uint16_t)(cm[u][i] & 0xffffu);
+        scm[slot * C + c * 8 + 2 * i + 1] = (uint16_t)(cm[u][i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  for (int64_t col = tid; col < C; col += 256) {
+    uint16_t mx = 0;
+#pragma unroll
+    for (int sl = 0; sl < RB; ++sl) mx = scm[sl * C + col] > mx ? scm[sl * C + col] : mx;
+    partial[(g * nb + b) * C + col] = mx;
+  }
+}
+
+// e[g][c] from the nb partial maxima of column c (eight loaded at a time).
+__global__ __launch_bounds__(256) void colmax_reduce_fp8_kernel(const uint16_t* __restrict__ partial,
+                                                                int64_t nb, int64_t C,
+                                                                int32_t* __restrict__ sexp) {
+  const int64_t g = blockIdx.y, col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  const uint16_t* p = partial + g * nb * C + col;
+  uint32_t mm = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[(b0 + j < nb ? b0 + j : nb - 1) * C];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm = v[j] > mm ? v[j] : mm;
+  }
+  const float amax = bf2f(mm);
+  int ex = 0;
+  const float mant = frexpf(amax, &ex);
+  sexp[g * C + col] = mm == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+}
+
 }  // namespace
+
+size_t quant_fp8_both_ws(int64_t G, int64_t R, int64_t C) {
+  return ((size_t)G * ((R + kBR - 1) / kBR) * C * 2 + 255) / 256 * 256;
+}
+
+// Rows [G*R, C] and transposes [G, C, R] of G row-major R x C matrices; ws
+// holds quant_fp8_both_ws bytes of partial column maxima. C % 16 == 0,
+// C <= 32768, R % 16 == 0.
+hipError_t launch_quant_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                                 int32_t* sexp, void* codes_t, int32_t* sexp_t, void* ws,
+                                 hipStream_t st) {
+  if (G == 0 || R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((R + kBR - 1) / kBR), (unsigned)G);
+  const bf16_t* x = (const bf16_t*)src;
+  uint16_t* part = (uint16_t*)ws;
+  if (C <= 4096)
+    hipLaunchKernelGGL(rows_colmax_fp8_kernel<8>, grid, dim3(256), 0, st, x, R, C, (uint8_t*)codes, sexp, part);
+  else if (C <= 8192)
+    hipLaunchKernelGGL(rows_colmax_fp8_kernel<4>, grid, dim3(256), 0, st, x, R, C, (uint8_t*)codes, sexp, part);
+  else if (C <= 16384)
+    hipLaunchKernelGGL(rows_colmax_fp8_kernel<2>, grid, dim3(256), 0, st, x, R, C, (uint8_t*)codes, sexp, part);
+  else if (C <= 32768)
+    hipLaunchKernelGGL(rows_colmax_fp8_kernel<1>, grid, dim3(256), 0, st, x, R, C, (uint8_t*)codes, sexp, part);
+  else
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(colmax_reduce_fp8_kernel, dim3((unsigned)((C + 255) / 256), (unsigned)G),
+                     dim3(256), 0, st, (const uint16_t*)part, (int64_t)grid.x, C, sexp_t);
+  const unsigned nc = (unsigned)((C + kTC - 1) / kTC);
+  hipLaunchKernelGGL(transpose_quant_fp8_kernel, dim3(nc, (unsigned)((R + 63) / 64), (unsigned)G),
+                     dim3(256), 0, st, x, R, C, (const int32_t*)sexp_t, (uint8_t*)codes_t);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
                               int32_t* sexp, hipStream_t st) {

@@ -12,8 +12,8 @@ import torch
 from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
                MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine,
                combine_bwd, grouped_ffn_bwd, grouped_ffn_bwd_fp8, grouped_ffn_fwd, grouped_ffn_fwd_fp8,
-               make_desc, permute, permute_bwd, quantize_fp8, quantize_fp8_t, route, route_bwd,
-               workspace_size)
+               make_desc, permute, permute_bwd, quantize_fp8, quantize_fp8_both,
+               quantize_fp8_both_ws, quantize_fp8_t, route, route_bwd, workspace_size)
 
 
 class MoELayer:
@@ -33,9 +33,12 @@ class MoELayer:
     quantizes x_perm (and x for a shared expert) and the current weights,
     keeps the pre-activations and H in bf16, and the backward runs in bf16
     as usual. fp8_bwd runs the backward's two data-gradient GEMMs on E4M3
-    operands as well: every backward quantizes the current weights per input
-    channel (into their transposes), and the library quantizes the upstream
-    and pre-activation gradients per row; the weight gradients stay bf16.
+    operands as well: the weights are quantized per input channel (into their
+    transposes) - by the forward in the same pass as its row quantization
+    when both are FP8, else by the backward - and the library quantizes the
+    upstream and pre-activation gradients per row; the weight gradients stay
+    bf16. The transposed codes a forward made serve the next backward on the
+    same weight tensors (weights do not change between the two).
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
@@ -115,6 +118,9 @@ class MoELayer:
                MOE_OP_ROUTE_BWD] + ([MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
               ([MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
         wsb = max(workspace_size(self.desc, op) for op in ops)
+        if fp8_fwd and fp8_bwd:   # both weight orientations from the forward's one pass
+            wsb = max(wsb, quantize_fp8_both_ws((E, P, d)), quantize_fp8_both_ws((E, d, f)))
+        self._wt_from = None      # weights whose transposed codes the forward made
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------ stages
@@ -129,12 +135,22 @@ class MoELayer:
                 self.x_perm, self.ws)
         if self.fp8_fwd:
             quantize_fp8(self.x_perm, self.xq_perm, self.sx_perm, valid_rows=self.offsets[self.E:])
-            quantize_fp8(w13, self.w13q, self.s13)
-            quantize_fp8(w2, self.w2q, self.s2)
+            if self.fp8_bwd:
+                # rows for the forward and columns (transposes) for the backward in one pass
+                quantize_fp8_both(w13, self.w13q, self.s13, self.w13q_t, self.s13_t, self.ws)
+                quantize_fp8_both(w2, self.w2q, self.s2, self.w2q_t, self.s2_t, self.ws)
+                self._wt_from = (w13.data_ptr(), w2.data_ptr())
+            else:
+                quantize_fp8(w13, self.w13q, self.s13)
+                quantize_fp8(w2, self.w2q, self.s2)
             if self.n_shared:
                 quantize_fp8(x, self.xq, self.sx)
-                quantize_fp8(sw13, self.sw13q, self.ss13)
-                quantize_fp8(sw2, self.sw2q, self.ss2)
+                if self.fp8_bwd:
+                    quantize_fp8_both(sw13, self.sw13q, self.ss13, self.sw13q_t, self.ss13_t, self.ws)
+                    quantize_fp8_both(sw2, self.sw2q, self.ss2, self.sw2q_t, self.ss2_t, self.ws)
+                else:
+                    quantize_fp8(sw13, self.sw13q, self.ss13)
+                    quantize_fp8(sw2, self.sw2q, self.ss2)
             grouped_ffn_fwd_fp8(D, self.xq_perm, self.sx_perm, self.offsets, self.xq, self.sx,
                                 self.w13q, self.s13, self.w2q, self.s2, self.sw13q, self.ss13,
                                 self.sw2q, self.ss2, self.save_pre, self.save_h, self.save_pre_s,
@@ -150,11 +166,15 @@ class MoELayer:
         D = self.desc
         combine_bwd(D, dy, self.out, self.gate, self.row_of, self.dgate, self.dout)
         if self.fp8_bwd:
-            quantize_fp8_t(w13, self.w13q_t, self.s13_t)
-            quantize_fp8_t(w2, self.w2q_t, self.s2_t)
-            if self.n_shared:
-                quantize_fp8_t(sw13, self.sw13q_t, self.ss13_t)
-                quantize_fp8_t(sw2, self.sw2q_t, self.ss2_t)
+            # the forward already made the transposed codes of these weights
+            # (FP8 forward); otherwise quantize them here
+            if self._wt_from != (w13.data_ptr(), w2.data_ptr()):
+                quantize_fp8_t(w13, self.w13q_t, self.s13_t)
+                quantize_fp8_t(w2, self.w2q_t, self.s2_t)
+                if self.n_shared:
+                    quantize_fp8_t(sw13, self.sw13q_t, self.ss13_t)
+                    quantize_fp8_t(sw2, self.sw2q_t, self.ss2_t)
+            self._wt_from = None
             grouped_ffn_bwd_fp8(D, self.x_perm, self.offsets, x, self.w13q_t, self.s13_t,
                                 self.w2q_t, self.s2_t, self.sw13q_t, self.ss13_t, self.sw2q_t,
                                 self.ss2_t, self.save_pre, self.save_h, self.save_pre_s,

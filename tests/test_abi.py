@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -280,3 +280,25 @@ def test_fp8_backward_validation():
     bad = list(ptrs)
     bad[3] = None
     assert L.moe_grouped_ffn_bwd_fp8(ctypes.byref(_desc()), *bad, P(FAKE), 1 << 40, None) == 1
+
+
+def test_fp8_quantize_both_validation():
+    """Bad shapes, pointers and workspace fail before any HIP call."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ok = dict(src=FAKE, G=2, R=64, C=48, codes=FAKE, sexp=FAKE, codes_t=FAKE, sexp_t=FAKE,
+              ws=FAKE, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        ptr = lambda v: P(v) if v else None   # noqa: E731
+        return L.moe_quantize_fp8_both(ptr(a["src"]), a["G"], a["R"], a["C"], ptr(a["codes"]),
+                                       ptr(a["sexp"]), ptr(a["codes_t"]), ptr(a["sexp_t"]),
+                                       ptr(a["ws"]), a["ws_bytes"], None)
+    for bad in (dict(R=8), dict(R=72), dict(C=8), dict(C=40), dict(C=32784), dict(G=-1),
+                dict(codes_t=0), dict(sexp_t=FAKE + 4), dict(ws=FAKE + 16)):
+        assert call(**bad) == 1, bad
+    # 2 * ceil(64 / 64) * 48 * 2 = 192 bytes -> 256 needed
+    assert call(ws_bytes=255) == 3 and call(ws=0) == 3
+    assert call(G=0) == 0

@@ -93,3 +93,34 @@ def test_quantize_transposed_bit_exact(G, R, C):
     assert (got_e == ref_e).all(), np.nonzero(got_e != ref_e)[0][:10]
     bad = np.argwhere(got_c != ref_c)
     assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("G,R,C", [(1, 16, 16), (2, 80, 48), (3, 208, 208), (2, 64, 4096),
+                                   (1, 96, 6160), (1, 96, 14336), (1, 48, 20000)])
+def test_quantize_both_bit_exact(G, R, C):
+    """moe_quantize_fp8_both: the row codes equal the oracle's per-row
+    quantization of each matrix, and the transposed codes its per-row
+    quantization of the transposes (every rows-per-pass variant, partial
+    64-row blocks, special rows and columns)."""
+    import mixture_experts_layer_28_amd as moe
+    print(f"[case] quantize both G={G} R={R} C={C}", flush=True)
+    rows = _rows(G * R, C, seed=G * 17 + R * 3 + C).reshape(G, R, C)
+    # special patterns in columns too: overwrite a few columns with a transposed block
+    colsp = _rows(min(C, 7), R, seed=C + 1).T
+    rows[0, :, : colsp.shape[1]] = colsp
+    x = _dev_bf16(np.ascontiguousarray(rows))
+    codes = torch.empty(G, R, C, dtype=torch.uint8, device="cuda")
+    sexp = torch.empty(G, R, dtype=torch.int32, device="cuda")
+    codes_t = torch.empty(G, C, R, dtype=torch.uint8, device="cuda")
+    sexp_t = torch.empty(G, C, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.quantize_fp8_both_ws((G, R, C)), dtype=torch.uint8, device="cuda")
+    moe.quantize_fp8_both(x, codes, sexp, codes_t, sexp_t, ws)
+    torch.cuda.synchronize()
+    f = bf16_bits_to_f32(rows).astype(np.float64)
+    rc, re_ = O.quantize_rows_fp8(f.reshape(G * R, C))
+    tc, te = O.quantize_rows_fp8(np.ascontiguousarray(f.transpose(0, 2, 1)).reshape(G * C, R))
+    assert (sexp.cpu().numpy().reshape(-1) == re_).all()
+    assert (codes.cpu().numpy().reshape(G * R, C) == rc).all()
+    assert (sexp_t.cpu().numpy().reshape(-1) == te).all()
+    bad = np.argwhere(codes_t.cpu().numpy().reshape(G * C, R) != tc)
+    assert bad.size == 0, f"{len(bad)} transposed codes differ, first {bad[:5].tolist()}"
