@@ -115,7 +115,8 @@ typedef enum {
  *   gate       [T, k] float                  out
  *   scores     [T, E] float                  out
  *   lse        [T] float or NULL             out (log sum_e exp(l_te), for the z-loss)
- *   ws         MOE_OP_ROUTE bytes            scratch
+ *   ws         MOE_OP_ROUTE bytes            scratch (E > 8: the logits, and when
+ *              few tiles cover T x E the split-K partials of x W_r^T)
  */
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
               const float* sel_bias, const float* gumbel_u, int32_t* topk_idx, float* gate,

@@ -86,7 +86,7 @@ enum KernelId {
   K_FWD_UP, K_FWD_DOWN, K_DGRAD_DOWN, K_DGRAD_UP, K_WGRAD_DOWN, K_WGRAD_UP,
   K_SH_FWD_UP, K_SH_FWD_DOWN, K_SH_DGRAD_DOWN, K_SH_DGRAD_UP, K_SH_WGRAD_DOWN, K_SH_WGRAD_UP,
   K_COMBINE, K_COMBINE_BWD, K_ROUTER_DLOGITS, K_ROUTER_DW, K_ROUTER_DW_REDUCE, K_ROUTER_DX,
-  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_QUANT_FP8, K_COUNT
+  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_QUANT_FP8, K_ROUTER_LOGITS_REDUCE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
   "router_logits", "router_topk", "aux_stats", "permute",
@@ -95,7 +95,7 @@ const char* const kKernelNames[K_COUNT] = {
   "gemm_shared_fwd_up", "gemm_shared_fwd_down", "gemm_shared_dgrad_down", "gemm_shared_dgrad_up",
   "gemm_shared_wgrad_down", "gemm_shared_wgrad_up",
   "combine", "combine_bwd", "router_dlogits", "router_dw", "router_dw_reduce", "router_dx",
-  "unpermute", "fill_zero", "bias_update", "quant_fp8",
+  "unpermute", "fill_zero", "bias_update", "quant_fp8", "router_logits_reduce",
 };
 
 struct ProfRec {
@@ -204,6 +204,19 @@ size_t esize(const moe_desc* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 int64_t pre_cols(const moe_desc* d) { return d->act == MOE_SWIGLU ? 2 * d->f : d->f; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Split-K of the router logits (E > 8): enough partitions to give about 512
+// workgroups when few 64 x 64 tiles cover T x E, each at least 256 deep.
+int route_fwd_splits(const moe_desc* d) {
+  if (d->E <= 8) return 1;
+  const int64_t tiles = ((d->T + 63) / 64) * ((d->E + 63) / 64);
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t smax = d->d / 256 > 1 ? d->d / 256 : 1;
+  if (s > smax) s = smax;
+  if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 int route_bwd_splits(const moe_desc* d) {
   const int64_t tiles = ((d->E + 63) / 64) * ((d->d + 63) / 64);
   int64_t s = (512 + tiles - 1) / tiles;
@@ -247,7 +260,10 @@ int enable_tail(GemmArgs& q, void* tw, hipStream_t s) {
 size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
   switch (op) {
-    case MOE_OP_ROUTE: return align256((size_t)T * E * 4);
+    case MOE_OP_ROUTE: {
+      const int S = route_fwd_splits(d);
+      return align256((size_t)T * E * 4) + (S > 1 ? (size_t)S * T * E * 4 : 0);
+    }
     case MOE_OP_AUX_STATS: {
       const size_t nb = (size_t)(T + 255) / 256;
       return align256(nb * E * 8) + align256(nb * E * 4) + align256(nb * 8);
@@ -431,20 +447,30 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
                                          desc->gumbel_tau, s),
                      "router (fused)");
   }
+  // logits = x W_r^T (+ logit_bias); with split-K the partitions land after
+  // the logits (partition 0 carries the bias) and are folded in order
   float* logits = (float*)ws;
+  const int S = route_fwd_splits(desc);
+  float* part = (float*)((char*)ws + align256((size_t)desc->T * desc->E * 4));
   GemmArgs p = blank();
   p.a = opnd(x, desc->d, 0, 1);
   p.b = opnd(w_r, desc->d, 0, 0);
-  p.c = logits;
+  p.c = S > 1 ? part : logits;
   p.ldc = desc->E;
   p.G = 1;
   p.M = desc->T;
   p.N = desc->E;
   p.K = desc->d;
   p.col_bias = logit_bias;
+  p.k_splits = S;
   {
     Scope sc(K_ROUTER_LOGITS, s);
     MOE_TRY(hip_check(gemm_router_logits(p, desc->dtype == MOE_BF16, s), "router logits"));
+  }
+  if (S > 1) {
+    Scope sc(K_ROUTER_LOGITS_REDUCE, s);
+    MOE_TRY(hip_check(launch_splitk_reduce(part, S, desc->T * desc->E, logits, s),
+                      "router logits reduce"));
   }
   Scope sc(K_ROUTER_TOPK, s);
   return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,

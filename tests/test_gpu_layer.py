@@ -53,6 +53,14 @@ EDGE = {
     # noisy gate through the GEMM-logits router (E > 8), fp32, low temperature
     "noisy_fp32": Workload("noisy32", T=300, d=64, E=40, k=4, f=64, dtype="fp32", gumbel_tau=0.5,
                            aux_coef=0.05, z_coef=0.02),
+    # router logits split over K (few T x E tiles, d >= 512) with a logit bias in
+    # partition 0, E = 40 (an N tail of the 64-wide tile), dense dl from the
+    # aux and z losses; then float32 with d = 1032 (a K tail of 8 in the last
+    # partition) and E = 20 (dl's rows not 8-aligned: dW_r and dx on the ALU)
+    "router_splitk_bias": Workload("rsplit", T=777, d=1024, E=40, k=4, f=64,
+                                   logit_bias={3: 1.5, 17: -2.0}, aux_coef=0.02, z_coef=0.01),
+    "router_splitk_ktail_fp32": Workload("rsplit32", T=515, d=1032, E=20, k=2, f=48,
+                                         dtype="fp32", logit_bias={0: 1.0}, aux_coef=0.05),
     # FP8 forward with ragged T, E, a K tail (d = 144 = 2*64 + 16) and N tails
     # (f = 208), GELU and a shared expert
     "ragged_fp8_gelu_shared": Workload("ragged8", T=1000, d=144, E=6, k=3, f=208, act="gelu",
