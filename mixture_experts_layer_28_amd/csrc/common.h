@@ -14,17 +14,22 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> bfloat16, round to nearest even (NaN kept quiet)
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> a packed bfloat16 pair (lo in bits 0-15), round to nearest
+// even, NaN stays NaN: gfx950's v_cvt_pk_bf16_f32, one instruction per pair.
+// On every non-NaN float32 input it gives the same bits as integer
+// round-to-nearest-even (u + 0x7fff + ((u >> 16) & 1)) >> 16 (checked over
+// all 2^32 inputs on the device); an integer version compiles to a
+// branch per element for the NaN case.
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
-}
+// float -> bfloat16 bits, same rounding
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf2(f, 0.0f) & 0xffffu; }
 
 // 8 consecutive elements <-> 8 floats, for either storage type
 template <typename T> struct Vec8;
