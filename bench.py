@@ -150,16 +150,17 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     f_scale = CALIB_BYTES / (fc[-1] * 1024.0)
     w_scale = CALIB_BYTES / (wc[-1] * 1024.0)
     out = {"workload": workload, "source_sha": gemm_source_hash(),
-           "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch), two separate rocprofv3 --pmc runs",
+           "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch), two separate rocprofv3 --pmc runs; "
+                       "$R = repository root, $OUT = a directory for the counter output",
            "commands": [
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o f "
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_fetch -o f "
                "--output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
                "--no-profile --calibrate-copy",
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o w "
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_write -o w "
                "--output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
                "--no-profile --calibrate-copy",
-               "python bench.py --summarize-pmc $R/gpurun_out/pmc_fetch/f_counter_collection.csv "
-               "$R/gpurun_out/pmc_write/w_counter_collection.csv"],
+               "python bench.py --summarize-pmc $OUT/pmc_fetch/f_counter_collection.csv "
+               "$OUT/pmc_write/w_counter_collection.csv"],
            "calibration": {"bytes": CALIB_BYTES, "fetch_kib": fc[-1], "write_kib": wc[-1],
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": {}}
