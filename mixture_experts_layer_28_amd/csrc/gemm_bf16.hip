@@ -369,6 +369,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
   };
   if (BWD) aux_load(0, pa[0], pb[0]);
+  if (EPI == EPI_STORE) {
+    // plain store: the output is bf16, so the block row is staged as bf16
+    // (half the LDS traffic of float32 staging, same bits). Row r of the
+    // block row is 256 bytes at r*256; its 16-byte slot s (columns 8s..8s+7)
+    // sits at ((s ^ (r & 15)) << 4), so the 32 rows a (j, g) write touches
+    // spread over all banks and a 16-lane group's row readback is a
+    // permutation of one row. Lane (lr, lh) holds columns 32j + 8g + 4lh .. +3:
+    // slot 4j + g, 8-byte half lh.
+    static_for<MI>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int j = decltype(Q)::value / 4, g = decltype(Q)::value % 4;
+        uint2 w;
+        w.x = pack_bf2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+        w.y = pack_bf2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(stg + lr * 256 + (((4 * j + g) ^ (lr & 15)) << 4) + 8 * lh) = w;
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      const int64_t mrow0 = t.m0 + wm0 + 32 * i;
+      const bool nok = n8 < p.N;
+      static_for<8>([&](auto Q) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        const int r = 4 * q + rq;
+        const uint4 u = *reinterpret_cast<const uint4*>(stg + r * 256 + ((s8 ^ (r & 15)) << 4));
+        const int64_t m = mrow0 + r;
+        if (m < t.M && nok) *reinterpret_cast<uint4*>(cb + m * p.ldc + n8) = u;
+      });
+      // the next block row overwrites the stage: finish this one's reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+    });
+    return;
+  }
   static_for<MI>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
     if (BWD && i + 1 < MI) aux_load(i + 1, pa[(i + 1) & 1], pb[(i + 1) & 1]);
