@@ -208,12 +208,33 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
         pre_ref, h_ref = np.zeros((0, P)), np.zeros((0, w.f))
     assert_close("pre(a|b)", to_np(L.save_pre)[g_rows], pre_ref[o_rows], dt, rep)
     assert_close("H", to_np(L.save_h)[g_rows], h_ref[o_rows], dt, rep)
-    assert_close("O", to_np(L.out)[g_rows], fwd["O"][o_rows], dt, rep)
+    # FP8 forward: H is quantized from its stored bf16 value on both sides, and
+    # the two sides' bf16 H can differ in the last bit (float32 vs float64
+    # evaluation); a value on an E4M3 rounding boundary then takes the
+    # neighbouring code, one E4M3 step (up to 2^-3 of the element) away. The
+    # down-projection is therefore checked to the bf16 bound against the
+    # oracle's own FP8 down-projection of the GPU's H, and end to end against
+    # a bound for such steps: one step in one of the f terms of a row moves it
+    # by up to about 2 * 2^-3 / sqrt(f) of max|O|.
+    o_tol = {}
+    if w.fp8:
+        check_fp8_down_own_h(w, L, f, off, rep)
+        o_tol = dict(max_rel=max(2e-2, 0.25 / np.sqrt(w.f)))
+    assert_close("O", to_np(L.out)[g_rows], fwd["O"][o_rows], dt, rep, **o_tol)
     if w.n_shared:
-        assert_close("O_shared", to_np(L.out_shared), fwd["Os"], dt, rep)
-    assert_close("Y", to_np(L.Y)[tok_ok], fwd["Y"][tok_ok], dt, rep)
+        assert_close("O_shared", to_np(L.out_shared), fwd["Os"], dt, rep, **o_tol)
+    assert_close("Y", to_np(L.Y)[tok_ok], fwd["Y"][tok_ok], dt, rep, **o_tol)
     # ---- backward
-    assert_close("dgate", to_np(L.dgate)[tok_ok], bwd["dgate"][tok_ok], dt, rep)
+    if w.fp8:
+        # dgate = <dY, O> of the GPU's own O, to the bf16 bound; downstream of O
+        # (dgate, the router gradients, dX through dx_router) the end-to-end
+        # comparison takes O's bound
+        rowg = L.row_of.cpu().numpy().astype(np.int64)
+        Og = to_np(L.out)
+        own = np.einsum("tc,tjc->tj", f["dy"], Og[np.maximum(rowg, 0)])
+        own = np.where(rowg >= 0, own, 0.0)
+        assert_close("dgate(own O)", to_np(L.dgate), own, dt, rep)
+    assert_close("dgate", to_np(L.dgate)[tok_ok], bwd["dgate"][tok_ok], dt, rep, **o_tol)
     # gradients of a row also carry its token's gate: skip rows of flipped tokens
     keep = tok_ok[token_of[g_rows]] if len(g_rows) else np.zeros(0, bool)
     assert_close("dO", to_np(L.dout)[g_rows[keep]], bwd["dO"][o_rows[keep]], dt, rep)
@@ -238,7 +259,7 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     # GPU; an absolute floor scaled by the formula's inputs covers that case.
     dl_floor = 2e-6 * float(np.abs(bwd["dgate"]).max(initial=0.0))
     assert_close("dlogits", to_np(L.dlogits)[tok_ok], bwd["dlogits"][tok_ok], dt, rep,
-                 atol=dl_floor)
+                 atol=dl_floor, **o_tol)
     # router weight gradient: against the oracle, and exactly dl^T x of the
     # GPU's own dl (a property of the definition that holds at any size)
     gdl = to_np(L.dlogits)
@@ -246,8 +267,11 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     assert_close("dx_router(own dl)", to_np(L.dx_router), gdl @ f["w_r"], dt, rep, rel=2e-5)
     if not bad_e:
         assert_close("dW_r", to_np(L.dw_r), bwd["dw_r"], dt, rep,
-                     atol=dl_floor * float(np.abs(f["x"]).sum(axis=0).max(initial=0.0)))
-    assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep, **dxt)
+                     atol=dl_floor * float(np.abs(f["x"]).sum(axis=0).max(initial=0.0)), **o_tol)
+    dxo = dict(dxt)
+    if o_tol:
+        dxo["max_rel"] = max(dxo.get("max_rel", 2e-2), o_tol["max_rel"])
+    assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep, **dxo)
     if w.fp8_bwd:
         check_fp8_dgrad(w, L, dev, bwd, rep, g_rows[keep], o_rows[keep], off)
     return len(flips)
@@ -324,6 +348,26 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
         assert_close("dpre_shared", dps, bwd["dpre_shared"], dt, rep)
         wst = _decode_codes(L.sw13q_t[0], L.ss13_t[0])
         assert_close("dX_shared(own dpre)", to_np(L.dx_shared), _e4m3_rows_ref(dps) @ wst.T, dt, rep)
+
+
+def check_fp8_down_own_h(w, L, f, off, rep):
+    """FP8 down-projection of the GPU's own bf16 H (routed experts, and the
+    shared expert on all tokens), recomputed by the oracle: per-row E4M3 codes
+    of H against the per-row quantized W2, held to the bf16 bound."""
+    Hg = to_np(L.save_h).astype(np.float64)
+    Og = to_np(L.out).astype(np.float64)
+    w2 = f["w2"]
+    for e in range(w.E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        own = O.dequantize_rows_fp8(*O.quantize_rows_fp8(Hg[r0:r1])) @ O.quantize_weights_fp8(w2[e]).T
+        assert_close(f"O(own H) e{e}", Og[r0:r1], own, "bf16", rep)
+    if w.n_shared:
+        hs = to_np(L.save_h_s).astype(np.float64)
+        sw2 = f["sw2"][0]
+        own = O.dequantize_rows_fp8(*O.quantize_rows_fp8(hs)) @ O.quantize_weights_fp8(sw2).T
+        assert_close("O_shared(own H)", to_np(L.out_shared).astype(np.float64), own, "bf16", rep)
 
 
 def run_and_compare(w: Workload, g=None):
