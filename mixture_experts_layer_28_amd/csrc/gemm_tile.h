@@ -72,7 +72,7 @@ __device__ __forceinline__ void band_order(int64_t L, int64_t mt_total, int64_t 
 }
 
 // Exclusive prefix over groups of ceil(M_g / BM) (M_g from offsets), written
-// to s_tiles[0..G] (s_tiles[G] = total). 256 threads, G <= 1024.
+// to s_tiles[0..G] (s_tiles[G] = total; G + 1 ints). 256 threads, G <= 1024.
 template <int BM>
 __device__ __forceinline__ void group_tile_prefix(const int32_t* __restrict__ off, int G,
                                                   int* s_tiles, int* s_wsum) {
@@ -104,9 +104,12 @@ __device__ __forceinline__ void group_tile_prefix(const int32_t* __restrict__ of
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int gi = tid * 4 + i;
-    if (gi <= G) s_tiles[gi] = ex;
+    if (gi < G) s_tiles[gi] = ex;
     ex += cnt[i];
   }
+  // the total: the last thread's inclusive sum covers all 1024 slots (slots
+  // past G count zero), so this also holds for G == 1024
+  if (tid == 255) s_tiles[G] = base + incl;
   __syncthreads();
 }
 

@@ -19,7 +19,8 @@ Workloads (the five layer shapes benchmarked and parity-tested):
   tiny_fp32        T=256  d=128  E=8   k=2 softmax, SwiGLU f=256, fp32
   mixtral_bf16     T=8192 d=4096 E=8   k=2 softmax, SwiGLU f=14336, cf 1.25
   skewed_bf16      T=4096 d=4096 E=8   k=2 softmax + logit bias +2 on experts
-                   0 and 3, GELU two-matrix f=16384, cf 1.0 or none
+                   0 and 3 and -0.75 on experts 5 and 6 (SKEW_BIAS), GELU
+                   two-matrix f=16384, cf 1.0 or none
   finegrained_bf16 T=16384 d=4096 E=128 k=8 softmax, SwiGLU f=1536, aux stats
                    with coefficient 0.01
   dsv3_bf16        T=8192 d=7168 E=256 k=8 sigmoid + selection bias, one shared
@@ -73,13 +74,20 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
+# The skewed load: +2.0 on the logits of experts 0 and 3 (so they take about
+# two thirds of the assignments), and -0.75 on experts 5 and 6 (so they take
+# under 3% each). The +2.0 shift alone leaves 5 and 6 at about 6%, like the
+# other unbiased experts; the cold-expert shift is chosen so the two targets
+# hold together on the seeded draws (0 and 3: 70.4%, 5: 2.4%, 6: 2.6%).
+SKEW_BIAS = {0: 2.0, 3: 2.0, 5: -0.75, 6: -0.75}
+
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", T=256, d=128, E=8, k=2, f=256, dtype="fp32"),
     "mixtral_bf16": Workload("mixtral_bf16", T=8192, d=4096, E=8, k=2, f=14336, cf=1.25),
     "skewed_bf16": Workload("skewed_bf16", T=4096, d=4096, E=8, k=2, f=16384, act="gelu",
-                            cf=1.0, logit_bias={0: 2.0, 3: 2.0}),
+                            cf=1.0, logit_bias=SKEW_BIAS),
     "skewed_nocap_bf16": Workload("skewed_nocap_bf16", T=4096, d=4096, E=8, k=2, f=16384,
-                                  act="gelu", cf=None, logit_bias={0: 2.0, 3: 2.0}),
+                                  act="gelu", cf=None, logit_bias=SKEW_BIAS),
     "finegrained_bf16": Workload("finegrained_bf16", T=16384, d=4096, E=128, k=8, f=1536,
                                  aux_coef=0.01, z_coef=1e-3),
     "dsv3_bf16": Workload("dsv3_bf16", T=8192, d=7168, E=256, k=8, f=2048, score="sigmoid",
@@ -89,7 +97,7 @@ WORKLOADS = {
                                    cf=1.25, gumbel_tau=1.0, aux_coef=0.01, z_coef=1e-3),
     "top1_bf16": Workload("top1_bf16", T=8192, d=4096, E=8, k=1, f=14336, cf=1.25),
     "skewed_cf15_bf16": Workload("skewed_cf15_bf16", T=4096, d=4096, E=8, k=2, f=16384,
-                                 act="gelu", cf=1.5, logit_bias={0: 2.0, 3: 2.0}),
+                                 act="gelu", cf=1.5, logit_bias=SKEW_BIAS),
     # one GPU's share of the DeepSeek-like layer under 8-way expert parallelism:
     # 32 local experts of about 2048 rows each
     "dsv3_ep8_shard_bf16": Workload("dsv3_ep8_shard_bf16", T=8192, d=7168, E=32, k=8, f=2048,

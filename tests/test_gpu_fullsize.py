@@ -104,8 +104,9 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
                                  replace=False).tolist()))
     gate = r["gates"]
     g_row_of = L.row_of.cpu().numpy()
-    g_O, g_H, g_pre = to_np(L.out), to_np(L.save_h), to_np(L.save_pre)
-    g_dO, g_dxp = to_np(L.dout), to_np(L.dx_perm)
+    # routed buffers hold T*k rows; only the first A are written
+    g_O, g_H, g_pre = to_np(L.out[:A]), to_np(L.save_h[:A]), to_np(L.save_pre[:A])
+    g_dO, g_dxp = to_np(L.dout[:A]), to_np(L.dx_perm[:A])
     ref = {k_: [] for k_ in ("O", "H", "pre", "dO", "dxp")}
     got = {k_: [] for k_ in ref}
     n = len(toks)
@@ -219,6 +220,19 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
         assert_close("dW2[sampled]", np.array(dw2_got), np.array(dw2_ref), dt, rep)
     gdl = to_np(L.dlogits)
     assert_close("dW_r(own dl)", to_np(L.dw_r), gdl.T @ x, dt, rep, rel=2e-5)
+    # the whole router backward against the oracle's, on every token, given
+    # the GPU's own dgate (its forward inputs are the oracle's routing: tokens
+    # with a near-tie flip are left out of dlogits, and the oracle's dW_r
+    # then runs on the same token set as the GPU's own dl)
+    if not bad_e:
+        g_dgate = to_np(L.dgate)
+        rb_all = O.router_backward(x, w_r, r["scores"], r["topk_idx"], gate, g_dgate, w.score,
+                                   w.aux_coef, st["y"], w.z_coef, r["logits"])
+        floor_all = 2e-6 * float(np.abs(g_dgate).max(initial=0.0))
+        assert_close("dlogits(own dgate, all tokens)", gdl, rb_all["dlogits"], dt, rep,
+                     atol=floor_all)
+        assert_close("dW_r(own dgate)", to_np(L.dw_r), rb_all["dw_r"], dt, rep,
+                     atol=floor_all * float(np.abs(x).sum(axis=0).max(initial=0.0)))
     print(rep, flush=True)
     del L, dev
     torch.cuda.empty_cache()

@@ -50,6 +50,9 @@ EDGE = {
     "single_expert": Workload("single", T=300, d=128, E=1, k=1, f=384),
     # E at the router's 1024-expert limit region and k at 16
     "wide_router": Workload("wide", T=256, d=64, E=320, k=16, f=64, aux_coef=0.02, z_coef=0.01),
+    # the library's limit of 1024 experts: the grouped GEMMs' group prefix
+    # covers all 1024 groups (most hold 0-4 rows), router and statistics at E = 1024
+    "max_experts": Workload("e1024", T=640, d=64, E=1024, k=4, f=64, aux_coef=0.01),
     # noisy gate through the GEMM-logits router (E > 8), fp32, low temperature
     "noisy_fp32": Workload("noisy32", T=300, d=64, E=40, k=4, f=64, dtype="fp32", gumbel_tau=0.5,
                            aux_coef=0.05, z_coef=0.02),

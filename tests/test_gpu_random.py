@@ -34,7 +34,9 @@ def _draw(i):
                     fp8=fp8, fp8_bwd=fp8 and rng.random() < 0.6, seed=i)
 
 
-@pytest.mark.parametrize("i", range(24))
+# 0-23: the sweep; 45: an FP8 forward case with f = 16 where E4M3 boundary
+# steps of H moved O by 4.3% (the case behind the FP8 forward's end-to-end bound)
+@pytest.mark.parametrize("i", list(range(24)) + [45])
 def test_random_layer_parity(i):
     w = _draw(i)
     print(f"[case] random {i} {w}", flush=True)

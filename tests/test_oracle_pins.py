@@ -200,6 +200,16 @@ def test_golden_capacity_worked_example():
     assert O.capacity(T, k, E, None) is None
 
 
+def test_capacity_rounds_up_a_fractional_limit():
+    """The worked example's limit is an integer; where cf T k / E is not,
+    the reading taken rounds up (a limit of 2.5 tokens keeps 3), so the
+    limit is never below cf times the mean load."""
+    assert O.capacity(10, 1, 4, 1.0) == 3            # 2.5
+    assert O.capacity(3, 2, 4, 1.25) == 2            # 1.875
+    assert O.capacity(8, 2, 8, 1.0) == 2             # exactly 2: no rounding
+    assert O.capacity(7, 1, 3, 0.0) == 0
+
+
 def test_capacity_keeps_first_tokens_when_all_go_to_one_expert():
     T, E, k, cap = 50, 4, 1, 7
     idx = np.full((T, k), 2)
