@@ -1,16 +1,19 @@
 """Benchmark one MoE layer step (forward + backward, every stage of the hot
 path) on one MI355X, and print one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_bf16]
 
 A step = router, load-balance stats, permute, grouped FFN forward, combine,
 combine backward, grouped FFN backward, router backward, un-permute, over
-one batch of seeded synthetic inputs already resident in HBM. W untimed
-steps, then K steps between two synchronisations. Per-kernel durations come
-from the library's timing events (recorded on the launch stream) over the
-same timed steps; the roofline object is for the dominant kernel. The CPU
-oracle is timed on a bounded token sample of the same workload on the host
-cores (rank 0, one GPU).
+one batch of seeded synthetic inputs already resident in HBM. The default
+workload is the largest configuration, the DeepSeek-like layer (dsv3_bf16).
+W untimed steps, then K timed steps between two synchronisations (the
+headline; one event between consecutive steps gives the median step). A
+second, profiled pass of K steps records the library's timing events
+around every kernel launch (on the launch stream) for the per-kernel times
+and the roofline object of the dominant kernel. The CPU oracle is timed on a
+bounded token sample of the same workload on the host cores (rank 0, one
+GPU), streaming the experts' weights one at a time.
 """
 from __future__ import annotations
 
@@ -56,6 +59,57 @@ def gemm_flops(w, A):
             "gemm_shared_dgrad_down": 2 * T * d * f, "gemm_shared_dgrad_up": 2 * T * P * d,
             "gemm_shared_wgrad_down": 2 * T * d * f, "gemm_shared_wgrad_up": 2 * T * P * d,
         })
+    return out
+
+
+def gemm_bytes(w, A):
+    """Algorithmic HBM bytes of each grouped-GEMM launch: every operand read
+    once and every output written once (all E experts' weights, and their
+    gradients, whatever their row counts)."""
+    s = 2 if w.dtype == "bf16" else 4
+    P = 2 * w.f if w.act == "swiglu" else w.f
+    d, f, E = w.d, w.f, w.E
+
+    def roles(R, G):
+        return {
+            "fwd_up": (R * d + G * P * d + R * f + R * P) * s,
+            "fwd_down": (R * f + G * d * f + R * d) * s,
+            "dgrad_down": (R * d + G * d * f + R * P + R * P) * s,
+            "dgrad_up": (R * P + G * P * d + R * d) * s,
+            "wgrad_down": (R * d + R * f + G * d * f) * s,
+            "wgrad_up": (R * P + R * d + G * P * d) * s,
+        }
+    out = {"gemm_" + k: v for k, v in roles(A, E).items()}
+    if w.n_shared:
+        out.update({"gemm_shared_" + k: v for k, v in roles(w.T, 1).items()})
+    return out
+
+
+def gemm_roofline(w, name, flops, nbytes, avg_ms):
+    """Roofline of one grouped-GEMM launch: the matrix-core time (flops at the
+    operand dtype's peak) and the HBM time (algorithmic bytes at 8 TB/s); the
+    larger one binds. frac = achieved / peak of the binding roofline;
+    mfma_frac and hbm_frac are each ideal time over the measured time, and
+    attainable_frac = max of the two."""
+    fp8_kernel = is_fp8_gemm(w, name)
+    peak_f = (PEAK_FP8_TFLOPS if fp8_kernel else PEAK_BF16_TFLOPS) if w.dtype == "bf16" \
+        else PEAK_F32_TFLOPS
+    t = avg_ms / 1e3
+    t_mfma = flops / (peak_f * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
+        out = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+               "unit": "GB/s", "frac": round(t_hbm / t, 4)}
+    else:
+        out = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+               "achieved": round(flops / t / 1e12, 1), "peak": peak_f, "unit": "TFLOP/s",
+               "frac": round(t_mfma / t, 4)}
+    out.update({"kernel": name, "avg_ms": round(avg_ms, 4), "flops_per_launch": flops,
+                "bytes_per_launch": nbytes, "tflops": round(flops / t / 1e12, 1),
+                "mfma_frac": round(t_mfma / t, 4), "hbm_frac": round(t_hbm / t, 4),
+                "attainable_frac": round(max(t_mfma, t_hbm) / t, 4)})
+    if fp8_kernel:
+        out["operand_dtype"] = "fp8-e4m3"
     return out
 
 
@@ -198,7 +252,7 @@ def gpu_clock_info():
 
 def stage_detail(layer, inp, moe, w, A, iters=20):
     """Median time of each streaming stage as one C-ABI call, with and without a
-    512 MiB write before every timed call (that write evicts the 256 MB MALL, so
+    512 MiB read before every timed call (that read evicts the 256 MB MALL, so
     the flushed figure reads its inputs from HBM), and a per-expert loop of
     torch's own GEMM (hipBLASLt) on the two forward shapes, as context."""
     import torch
@@ -215,14 +269,17 @@ def stage_detail(layer, inp, moe, w, A, iters=20):
         "unpermute": lambda: moe.permute_bwd(D, layer.dx_perm, layer.row_of, layer.dx_shared,
                                              layer.dx_router, layer.dX),
     }
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # the flush reads 512 MiB (twice the MALL) and writes 4 bytes: no dirty
+    # lines of its own can be written back inside the timed call
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def median_ms(fn, flushed):
         ts = []
         for i in range(iters + 2):
             if flushed:
-                flush.fill_(i & 0xFF)
+                flush.max()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -261,30 +318,115 @@ def stage_detail(layer, inp, moe, w, A, iters=20):
             "gpu_clocks": gpu_clock_info()}
 
 
+# token sample of the CPU oracle per workload (about 10-30 s of float64 work
+# on a 16-core host); other workloads use DEFAULT_CPU_TOKENS
+CPU_TOKENS = {"dsv3_bf16": 4096, "finegrained_bf16": 2048, "mixtral_bf16": 4096}
+DEFAULT_CPU_TOKENS = 2048
+
+
 def cpu_baseline(w, g, tokens):
     """The oracle, as it stands, on the first `tokens` tokens of the workload
-    (same weights; capacity recomputed for the sample)."""
+    (same weights; capacity recomputed for the sample), fwd+bwd in float64.
+
+    The experts are streamed: each expert's bf16 weights are widened to
+    float64 just before its rows run (untimed) and dropped after, so the
+    host never holds every expert in float64 (about 90 GB for the
+    DeepSeek-like layer). Per expert the oracle's own functions run on that
+    expert's rows: expert_forward, combine_backward of those rows (their dO
+    depends only on gates and dY) and expert_backward. Router, statistics,
+    permutation, combine, router backward and un-permute run once on the
+    whole sample. Only the oracle calls are timed."""
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        blas = None
+    clock = [0.0]
+    streamed_oracle_step(w, g, tokens, clock)
+    dt_s = clock[0]
+    return {"value": tokens / dt_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "blas_threads": blas,
+            "sample": f"first {tokens} of {w.T} tokens (capacity recomputed for the sample), "
+                      f"all {w.E} experts' weights streamed one expert at a time, fwd+bwd in "
+                      f"float64 NumPy: {dt_s:.1f} s of oracle calls; bf16->float64 widening "
+                      f"untimed"}
+
+
+def streamed_oracle_step(w, g, tokens, clock):
+    """One fwd+bwd of the oracle on the first `tokens` tokens, one expert's
+    weights in float64 at a time (see cpu_baseline). Adds the seconds spent in
+    oracle calls to clock[0]. Returns Y, dX, dgate, dw_r and, per expert, the
+    sums of dW13 and dW2 (the weight gradients themselves are dropped with the
+    expert's weights)."""
+    import oracle as O
     ws = w.replace(T=tokens)
-    f = {n: (as_f64(v, w.dtype) if v is not None else None) for n, v in g.items()}
-    x, dy = f["x"][:tokens], f["dy"][:tokens]
-    gu = f["gumbel_u"][:tokens] if f["gumbel_u"] is not None else None
+    dt = w.dtype
+    cv = lambda a: as_f64(a, dt) if a is not None else None   # noqa: E731
+    x, dy = cv(g["x"][:tokens]), cv(g["dy"][:tokens])
+    w_r = g["w_r"].astype(np.float64)
+    lb = g["logit_bias"].astype(np.float64) if g["logit_bias"] is not None else None
+    sb = g["sel_bias"].astype(np.float64) if g["sel_bias"] is not None else None
+    gu = g["gumbel_u"][:tokens].astype(np.float64) if g["gumbel_u"] is not None else None
     cap = O.capacity(ws.T, ws.k, ws.E, ws.cf)
-    t0 = time.perf_counter()
-    fwd = O.layer_forward(x, f["w_r"], f["w13"], f["w2"], ws.k, ws.score, ws.act, cap,
-                          f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau,
-                          fp8=ws.fp8)
-    O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act, ws.aux_coef,
-                     f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau, fp8_dgrad=ws.fp8_bwd)
-    dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {tokens} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in "
-                      f"float64 NumPy ({dt:.1f} s; bf16->float64 input conversion untimed)"}
+
+    def timed(fn, *a):
+        t0 = time.perf_counter()
+        out = fn(*a)
+        clock[0] += time.perf_counter() - t0
+        return out
+
+    def fwd_e(X, w13e, w2e):
+        if ws.fp8:
+            return O.expert_forward_fp8(X, w13e, w2e, ws.act)
+        return O.expert_forward(X, w13e, w2e, ws.act)
+
+    def bwd_e(X, w13e, w2e, sv, dO):
+        if ws.fp8_bwd:
+            return O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2e),
+                                            O.quantize_weights_fp8_t(w13e), sv, dO, ws.act)
+        return O.expert_backward(X, w13e, w2e, sv, dO, ws.act)
+
+    r = timed(O.router_forward, x, w_r, ws.k, ws.score, lb, sb, gu, ws.gumbel_tau)
+    st = timed(O.aux_stats, r["scores"], r["topk_idx"], ws.E)
+    pm = timed(O.permute, r["topk_idx"], ws.E, cap)
+    off, tok = pm["offsets"], pm["token_of"]
+    A = int(off[-1])
+    x_perm = timed(lambda: x[tok])
+    Orows = np.zeros((A, ws.d))
+    dX_perm = np.zeros((A, ws.d))
+    dgate = np.zeros((ws.T, ws.k))
+    slot_of = np.zeros(A, dtype=np.int64)
+    kept = np.nonzero(pm["row_of"] >= 0)
+    slot_of[pm["row_of"][kept]] = kept[1]
+    gsum = np.zeros((ws.E, 2))
+    for e in range(ws.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        w13e, w2e = cv(g["w13"][e]), cv(g["w2"][e])           # untimed widening
+        te, je = tok[lo:hi], slot_of[lo:hi]
+        o, sv = timed(fwd_e, x_perm[lo:hi], w13e, w2e)
+        Orows[lo:hi] = o
+        dg_e, dO_e = timed(O.combine_backward, dy[te], o, r["gates"][te, je][:, None],
+                           np.arange(hi - lo)[:, None])
+        dgate[te, je] = dg_e[:, 0]
+        dxe, g13, g2, _ = timed(bwd_e, x_perm[lo:hi], w13e, w2e, sv, dO_e)
+        dX_perm[lo:hi] = dxe
+        gsum[e] = g13.sum(), g2.sum()
+        del w13e, w2e, g13, g2
+    Os = dXs = None
+    if ws.n_shared:
+        sw13, sw2 = cv(g["sw13"][0]), cv(g["sw2"][0])
+        Os, svs = timed(fwd_e, x, sw13, sw2)
+        dXs, _, _, _ = timed(bwd_e, x, sw13, sw2, svs, dy)
+        del sw13, sw2
+    Y = timed(O.combine, Orows, r["gates"], pm["row_of"], Os)
+    rb = timed(O.router_backward, x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, ws.score,
+               ws.aux_coef, st["y"], ws.z_coef, r["logits"], ws.gumbel_tau)
+    dX = timed(O.permute_backward, dX_perm, pm["row_of"], dXs, rb["dx_router"])
+    return dict(Y=Y, dX=dX, dgate=dgate, dw_r=rb["dw_r"], dw_sums=gsum)
 
 
 def main():
@@ -292,11 +434,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixtral_bf16", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--workload", default="dsv3_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="token sample of the CPU oracle (default: per workload, CPU_TOKENS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
-                    help="time without per-kernel events (roofline object omitted)")
+                    help="skip the profiled pass (no per-kernel times, roofline object omitted)")
     ap.add_argument("--stage-detail", action="store_true",
                     help="also time each streaming stage alone, MALL-flushed and not, "
                          "torch's per-expert GEMM as context, and record GPU clocks")
@@ -348,24 +491,42 @@ def main():
     log("[bench] warmup done")
 
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if not args.no_profile:
-        moe.profile_enable(True)
+    # timed pass (the headline): K steps between two synchronisations, with
+    # one timing event between consecutive steps and none inside a step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         layer.step(inp)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    prof = moe.profile_read() if not args.no_profile else []
-    moe.profile_enable(False)
-    ms = ev0.elapsed_time(ev1)
+    ms = evs[0].elapsed_time(evs[-1])
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     ms_step = ms / args.steps
     value = w.T * args.steps / (ms / 1e3)
     A = int(layer.offsets[-1].item())
-    log(f"[bench] {ms_step:.3f} ms/step, {value:.0f} tokens/s, kept rows {A}")
+    log(f"[bench] {ms_step:.3f} ms/step (median {np.median(step_ms):.3f}), {value:.0f} tokens/s, "
+        f"kept rows {A}")
+
+    # profiled pass: the same K steps again with the library's timing events
+    # around every kernel launch (per-kernel times, roofline)
+    prof, prof_ms_step = [], None
+    if not args.no_profile:
+        moe.profile_enable(True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            layer.step(inp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prof = moe.profile_read()
+        moe.profile_enable(False)
+        prof_ms_step = e0.elapsed_time(e1) / args.steps
+        log(f"[bench] profiled pass: {prof_ms_step:.3f} ms/step")
 
     flops = gemm_flops(w, A)
+    gbytes = gemm_bytes(w, A)
     stages = {}
     for name, tot, n in prof:
         stages[name] = {"avg_ms": round(tot / n, 4), "launches": n}
@@ -375,18 +536,8 @@ def main():
     if prof:
         gk = [(tot, name, n) for name, tot, n in prof if name in flops]
         tot, dom, n = max(gk)
-        avg_s = tot / n / 1e3
-        achieved = flops[dom] / avg_s / 1e12
-        fp8_kernel = is_fp8_gemm(w, dom)
-        peak = (PEAK_FP8_TFLOPS if fp8_kernel else PEAK_BF16_TFLOPS) if w.dtype == "bf16" \
-            else PEAK_F32_TFLOPS
-        roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": dom,
-                    "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4),
-                    "traffic": traffic_for(dom, w.name),
-                    "flops_per_launch": flops[dom], "avg_ms": round(tot / n, 4)}
-        if fp8_kernel:
-            roofline["operand_dtype"] = "fp8-e4m3"
+        roofline = gemm_roofline(w, dom, flops[dom], gbytes[dom], tot / n)
+        roofline["traffic"] = traffic_for(dom, w.name)
         hb = hbm_bytes(w, A)
         for name, b in hb.items():
             if name in stages:
@@ -395,8 +546,10 @@ def main():
                 stages[name]["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 3)
         for name in flops:
             if name in stages:
-                tf = flops[name] / (stages[name]["avg_ms"] / 1e3) / 1e12
-                stages[name]["TFLOP/s"] = round(tf, 1)
+                r = gemm_roofline(w, name, flops[name], gbytes[name], stages[name]["avg_ms"])
+                stages[name]["TFLOP/s"] = round(flops[name] / (stages[name]["avg_ms"] / 1e3) / 1e12, 1)
+                stages[name]["mfma_frac"] = r["mfma_frac"]
+                stages[name]["attainable_frac"] = r["attainable_frac"]
     gemm_tflops = gemm_flops_step * args.steps / (gemm_tot_ms / 1e3) / 1e12 if gemm_tot_ms else None
     # share of the matrix peak: time the GEMMs would take at their operand
     # dtype's peak (fp8 forward GEMMs at the fp8 peak) over the time they took
@@ -415,13 +568,17 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(w, g, args.cpu_tokens)
+        ntok = args.cpu_tokens or CPU_TOKENS.get(w.name, DEFAULT_CPU_TOKENS)
+        ntok = min(ntok, w.T)
+        log(f"[bench] timing the CPU oracle on {ntok} tokens")
+        cpu = cpu_baseline(w, g, ntok)
         log(f"[bench] oracle: {cpu['value']:.2f} tokens/s")
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "median_ms_per_step": round(float(np.median(step_ms)), 4),
+        "profiled_ms_per_step": round(prof_ms_step, 4) if prof_ms_step else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype_label(w), "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,

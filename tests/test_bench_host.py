@@ -56,3 +56,52 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_streamed_cpu_baseline_equals_the_oracle_layer():
+    """The CPU baseline streams the experts' weights one at a time; it must
+    compute the same fwd+bwd as the oracle's whole-layer functions."""
+    import numpy as np
+    import oracle as O
+    from moe_inputs import as_f64, gen_all
+    for name, kw in (("dsv3_bf16", dict(T=64, d=32, f=16, E=12)),
+                     ("mixtral_noisy_bf16", dict(T=48, d=32, f=24)),
+                     ("skewed_bf16", dict(T=40, d=16, f=32))):
+        w = WORKLOADS[name].replace(**kw)
+        g = gen_all(w)
+        clock = [0.0]
+        got = bench.streamed_oracle_step(w, g, 32, clock)
+        assert clock[0] > 0
+        ws = w.replace(T=32)
+        f = {n: (as_f64(v, w.dtype) if v is not None else None) for n, v in g.items()}
+        x, dy = f["x"][:32], f["dy"][:32]
+        gu = f["gumbel_u"][:32] if f["gumbel_u"] is not None else None
+        cap = O.capacity(32, ws.k, ws.E, ws.cf)
+        fwd = O.layer_forward(x, f["w_r"], f["w13"], f["w2"], ws.k, ws.score, ws.act, cap,
+                              f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], gu, ws.gumbel_tau)
+        bwd = O.layer_backward(fwd, x, f["w_r"], f["w13"], f["w2"], dy, ws.score, ws.act,
+                               ws.aux_coef, f["sw13"], f["sw2"], ws.z_coef, ws.gumbel_tau)
+        np.testing.assert_allclose(got["Y"], fwd["Y"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dX"], bwd["dX"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dgate"], bwd["dgate"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dw_r"], bwd["dw_r"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dw_sums"][:, 0], bwd["dw13"].sum(axis=(1, 2)), atol=1e-9)
+        np.testing.assert_allclose(got["dw_sums"][:, 1], bwd["dw2"].sum(axis=(1, 2)), atol=1e-9)
+
+
+def test_gemm_roofline_picks_the_binding_bound():
+    # DeepSeek-like weight gradient of the first matrix: 15 GB of bf16 dW13
+    # written against 3.85 TFLOP, so HBM binds; the Mixtral-like dX GEMM is
+    # matrix-core bound
+    s = WORKLOADS["dsv3_bf16"]
+    A = 65536
+    fl, by = bench.gemm_flops(s, A), bench.gemm_bytes(s, A)
+    assert by["gemm_wgrad_up"] == (A * 2 * s.f + A * s.d + s.E * 2 * s.f * s.d) * 2
+    r = bench.gemm_roofline(s, "gemm_wgrad_up", fl["gemm_wgrad_up"], by["gemm_wgrad_up"], 4.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["frac"] - by["gemm_wgrad_up"] / 8e12 / 4e-3) < 1e-4
+    assert r["attainable_frac"] == r["hbm_frac"] > r["mfma_frac"]
+    m = WORKLOADS["mixtral_bf16"]
+    fl, by = bench.gemm_flops(m, 16384), bench.gemm_bytes(m, 16384)
+    r = bench.gemm_roofline(m, "gemm_dgrad_up", fl["gemm_dgrad_up"], by["gemm_dgrad_up"], 3.3)
+    assert r["bound"] == "mfma" and abs(r["frac"] - fl["gemm_dgrad_up"] / 2.5e15 / 3.3e-3) < 1e-4
