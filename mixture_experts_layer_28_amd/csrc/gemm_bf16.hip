@@ -49,6 +49,7 @@ constexpr int kRows = 256;                // tile rows of either operand
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 // byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [64][kRows] tile
 __device__ __forceinline__ int ks_off(int k, int s) {
@@ -144,12 +145,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const bf16_t* Ab = operand_base<bf16_t>(p.a, t);
-  const bf16_t* Bb = operand_base<bf16_t>(p.b, t);
   // buffer extents: K-contiguous operands span rows x ld, K-strided span K x ld
   const int64_t b_rows = FUSED ? 2 * p.fdim : p.N;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, (AKM ? t.M : t.K) * p.a.ld * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, (BKM ? b_rows : t.K) * p.b.ld * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(operand_base<bf16_t>(p.a, t), (AKM ? t.M : t.K) * p.a.ld * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(operand_base<bf16_t>(p.b, t), (BKM ? b_rows : t.K) * p.b.ld * 2);
   DmaSrc da, db;
   dma_src<AKM, false, WN>(da, p.a.ld, t.M, t.m0, p.fdim, wave, lane);
   dma_src<BKM, FUSED, WN>(db, p.b.ld, FUSED ? p.fdim : p.N, t.n0, p.fdim, wave, lane);
@@ -185,25 +184,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                              kin ? d.off[i] : kOOB, so, 0, 0);
   };
 
-  // fragment of 32 rows (base .. base+31) for k slice sl (0..3) of an operand tile
-  auto frag = [&](const bf16_t* tile, bool kc, int base, int sl) __attribute__((always_inline)) -> bf16x8 {
-    const char* tb = reinterpret_cast<const char*>(tile);
-    if (kc) return *reinterpret_cast<const bf16x8*>(tb + kc_off(base + (lane & 31), sl * 2 + (lane >> 5)));
+  // K-strided fragments (ds_read_b64_tr_b16). Block qq of a wave's rows
+  // (rows w0 + 32qq .. +31, w0 = wm0 or wn0) for k slice sl: lane (g, i) =
+  // (lane >> 4, lane & 15) reads row w0 + 32qq + 16(g & 1) + 4(i & 3) at k-rows
+  // k and k + 4, k = 16sl + 8(g >> 1) + (i >> 2). In the [64][256] layout
+  // (ks_off) that byte offset splits into a lane part, which depends on qq only
+  // through its parity, and a compile-time part:
+  //   ks_off(k, row >> 3) + 2(row & 7) = tlo[qq & 1] + 8192 sl + 64 (qq & ~1)
+  //   (+ 2048 for k + 4), with
+  //   tlo[par] = 512 kl + 2 w0 + 64 (par ^ xb) + 16 (y ^ (x & 3)) + 2 (rl & 7),
+  // kl = 8(g >> 1) + (i >> 2), rl = 16(g & 1) + 4(i & 3), x = (kl & 3) << 1,
+  // y = rl >> 3, xb = x >> 2. So every read is one of two lane offsets per
+  // operand plus an immediate, instead of an address register per read.
+  auto tr_lane_off = [&](int w0, int par) __attribute__((always_inline)) -> int {
     const int g = lane >> 4, i = lane & 15;
-    const int row = base + 16 * (g & 1) + 4 * (i & 3);
-    const int k = 16 * sl + 8 * (g >> 1) + (i >> 2);
-    const int b0 = ks_off(k, row >> 3) + (row & 7) * 2;
-    const int b1 = ks_off(k + 4, row >> 3) + (row & 7) * 2;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tb + b0));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tb + b1));
+    const int rl = 16 * (g & 1) + 4 * (i & 3), kl = 8 * (g >> 1) + (i >> 2);
+    const int x = (kl & 3) << 1, y = rl >> 3, xb = x >> 2;
+    return 512 * kl + 2 * w0 + 64 * (par ^ xb) + 16 * (y ^ (x & 3)) + 2 * (rl & 7);
+  };
+  const int tlo_a[2] = {tr_lane_off(wm0, 0), tr_lane_off(wm0, 1)};
+  const int tlo_b[2] = {tr_lane_off(wn0, 0), tr_lane_off(wn0, 1)};
+
+  // fragment of block qq (rows w0 + 32qq .. +31) for k slice sl (0..3) of an operand tile
+  auto frag = [&](const bf16_t* tile, bool kc, bool isA, int qq, int sl) __attribute__((always_inline)) -> bf16x8 {
+    const char* tb = reinterpret_cast<const char*>(tile);
+    if (kc)
+      return *reinterpret_cast<const bf16x8*>(
+          tb + kc_off((isA ? wm0 : wn0) + qq * 32 + (lane & 31), sl * 2 + (lane >> 5)));
+    const char* lb = tb + (isA ? tlo_a[qq & 1] : tlo_b[qq & 1]) + 8192 * sl + 64 * (qq & ~1);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)lb);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + 2048));
     return join(lo, hi);
   };
 
   bf16x8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
   auto ldfrag_q = [&](bf16x8* fa, bf16x8* fb, const bf16_t* sa, const bf16_t* sb, int sl, int q)
       __attribute__((always_inline)) {
-    if (q < MI) fa[q] = frag(sa, AKM, wm0 + q * 32, sl);
-    else fb[q - MI] = frag(sb, BKM, wn0 + (q - MI) * 32, sl);
+    if (q < MI) fa[q] = frag(sa, AKM, true, q, sl);
+    else fb[q - MI] = frag(sb, BKM, false, q - MI, sl);
   };
   auto mma = [&](const bf16x8* fa, const bf16x8* fb, int q) __attribute__((always_inline)) {
     const int i = q / NI, j = q % NI;
@@ -250,8 +268,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     slice(fa1, fb1, fa0, fb0, a1, b1, 0, kt + 2, 1, b2, 0);
   };
 
-  if (nk > 0) {
-    // as if just after the barrier of k-step -1: A0, B0, A1 and half of B1
+  // as if just after the barrier of k-step -1: A0, B0, A1 and half of B1
+  // (28 DMA instructions per wave)
+  auto prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma(0, 0, h0, i);
 #pragma unroll
@@ -260,8 +279,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < 8; ++i) dma(1, 0, h2, i);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma(1, 1, h3, i);
-    wait_vm<12>();
-    __builtin_amdgcn_s_barrier();
+  };
+  // the k-steps of the tile, A0 and B0 landed and visible to every wave
+  auto mainloop = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < MI + NI; ++q) ldfrag_q(fa0, fb0, h0, h1, 0, q);
     // five k-steps per trip name their buffers statically; the trip stops at
@@ -279,6 +299,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (kt + 1 < nk) kstep(kt + 1, h2, h3, h4, h0, h1, h2);
     if (kt + 2 < nk) kstep(kt + 2, h4, h0, h1, h2, h3, h4);
     if (kt + 3 < nk) kstep(kt + 3, h1, h2, h3, h4, h0, h1);
+  };
+
+
+  if (nk > 0) {
+    prologue();
+    wait_vm<12>();
+    __builtin_amdgcn_s_barrier();
+    mainloop();
     wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -397,9 +425,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int64_t m = mrow0 + r;
         if (m < t.M && nok) *reinterpret_cast<uint4*>(cb + m * p.ldc + n8) = u;
       });
-      // the next block row overwrites the stage: finish this one's reads
+      // the next block row overwrites the stage: finish this one's reads;
+      // and keep its accumulator reads and conversions here (hoisted ahead,
+      // they would hold all 128 packed registers at once)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     });
     return;
   }

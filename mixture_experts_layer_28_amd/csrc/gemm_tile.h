@@ -140,6 +140,38 @@ struct Tile {
 // for per = tiles per group.
 inline int64_t rag_k_grid(int64_t G, int64_t per) { return 8 * G * ((per + 7) / 8); }
 
+// Tile `i` of XCD x in a RAG_K launch. The groups' K (their row counts)
+// differ, so a group's tiles cost differently from another's. Each group's
+// tiles are split into 8 contiguous runs and XCD x takes run x of every
+// group, in group order: every XCD does the same share of every group (a
+// contiguous split of all tiles would give each XCD whole groups). XCD x
+// holds n * G tiles, n = its run length; false when i is past them.
+// 32-bit arithmetic: a weight's tile count and an XCD's tile list stay far
+// below 2^31 (one expert's weight is under 2 GiB, at most 1024 experts).
+template <int BM, int BNo>
+__device__ __forceinline__ bool rag_k_tile(const GemmArgs& p, uint32_t x, uint32_t i, Tile& t) {
+  const uint32_t nt = (uint32_t)((p.N + BNo - 1) / BNo);
+  const uint32_t mtg = (uint32_t)((p.M + BM - 1) / BM);
+  const uint32_t per = mtg * nt;
+  const uint32_t lo = x * per / 8, n = (x + 1) * per / 8 - lo;
+  if (n == 0 || i >= n * (uint32_t)p.G) return false;
+  const uint32_t g = i / n, L = lo + (i - g * n);
+  // band_order in 32 bits
+  const uint32_t band = L / (kBandM * nt);
+  const uint32_t within = L - band * kBandM * nt;
+  const uint32_t rem = mtg - band * kBandM;
+  const uint32_t h = rem < (uint32_t)kBandM ? rem : (uint32_t)kBandM;
+  const uint32_t ntile = within / h;
+  const uint32_t mt = band * kBandM + (within - ntile * h);
+  t.g = (int)g;
+  t.m0 = (int64_t)mt * BM;
+  t.n0 = (int64_t)ntile * BNo;
+  t.M = p.M;
+  t.r0 = p.offsets[g];
+  t.K = p.offsets[g + 1] - t.r0;
+  return true;
+}
+
 // Map this workgroup to a tile; false = no tile (surplus workgroup).
 // BNo: output columns per tile. s_tiles must hold >= G+1 ints, s_wsum 4 ints.
 template <int BM, int BNo, int RAG>
@@ -191,39 +223,21 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, in
     t.n0 = ntile * BNo;
     return true;
   }
+  // RAG_K: the grid holds 8 * G * ceil(per / 8) workgroups (rag_k_grid);
+  // workgroup i of XCD x takes that XCD's tile i
+  if (RAG == RAG_K) return rag_k_tile<BM, BNo>(p, blockIdx.x & 7, blockIdx.x >> 3, t);
   const int64_t mtg = (p.M + BM - 1) / BM;
   const int64_t per = mtg * nt;
-  int64_t Lg;   // tile within its group
-  if (RAG == RAG_K) {
-    // The groups' K (their row counts) differ, so a group's tiles cost
-    // differently from another's. Each group's tiles are split into 8
-    // contiguous runs and XCD x takes run x of every group, in group order:
-    // every XCD does the same share of every group (a contiguous split of
-    // all tiles would give each XCD whole groups). The grid holds
-    // 8 * G * ceil(per / 8) workgroups (rag_k_grid).
-    const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3;
-    const int64_t lo = x * per / 8, n = (x + 1) * per / 8 - lo;
-    if (n == 0 || i >= n * p.G) return false;
-    t.g = (int)(i / n);
-    Lg = lo + i % n;
-  } else {
-    const int64_t L = xcd_tile(per * p.G);
-    if (L < 0) return false;
-    t.g = (int)(L / per);
-    Lg = L - (int64_t)t.g * per;
-  }
+  const int64_t L = xcd_tile(per * p.G);
+  if (L < 0) return false;
+  t.g = (int)(L / per);
   int64_t mt, ntile;
-  band_order(Lg, mtg, nt, mt, ntile);
+  band_order(L - (int64_t)t.g * per, mtg, nt, mt, ntile);
   t.m0 = mt * BM;
   t.n0 = ntile * BNo;
   t.M = p.M;
-  if (RAG == RAG_K) {
-    t.r0 = p.offsets[t.g];
-    t.K = p.offsets[t.g + 1] - t.r0;
-  } else {
-    t.r0 = (int64_t)t.g * p.M;
-    t.K = p.K;
-  }
+  t.r0 = (int64_t)t.g * p.M;
+  t.K = p.K;
   return true;
 }
 

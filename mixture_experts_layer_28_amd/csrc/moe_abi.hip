@@ -47,6 +47,7 @@ hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t)
 hipError_t launch_router_dw_small(const float*, const void*, bool, int, int, int64_t, float*,
                                   hipStream_t);
 int router_dw_small_chunks(int T);
+size_t perm_ws_bytes(int T, int E);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 hipError_t launch_router_small(const void*, bool, const float*, const float*, const float*, int,
                                int, int64_t, int, int, int32_t*, float*, float*, float*,
@@ -268,7 +269,7 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       const size_t nb = (size_t)(T + 255) / 256;
       return align256(nb * E * 8) + align256(nb * E * 4) + align256(nb * 8);
     }
-    case MOE_OP_PERMUTE: return align256((size_t)((T + 63) / 64) * E * 4);
+    case MOE_OP_PERMUTE: return align256(perm_ws_bytes((int)T, (int)E));
     case MOE_OP_FFN_FWD: return d->dtype == MOE_BF16 ? tail_ws_bytes(kTailCusMax) : 0;
     case MOE_OP_FFN_BWD:
       return align256((size_t)T * d->k * pre_cols(d) * esize(d)) +

@@ -5,6 +5,8 @@
 
 namespace moe {
 
+typedef uint32_t v4u32_ __attribute__((ext_vector_type(4)));
+
 // --------------------------------------------------------------- router
 // One wave per token. Experts e = lane + 64*i live in registers (EPL per lane).
 // Softmax is max-subtracted; top-k is k rounds of a wave arg-max on the
@@ -379,50 +381,68 @@ hipError_t launch_bias_update(const int32_t* counts, int E, int64_t Tk, float ga
 }
 
 // -------------------------------------------------------------- permute
-// 64-token blocks. (1) per-block histogram; (2) per expert, exclusive scan
-// over blocks (in place) and capacity-clipped exclusive scan over experts;
-// (3) per block, rank of each assignment among earlier tokens of the block
-// routed to the same expert (wave ballot), giving its row.
-__global__ __launch_bounds__(64) void perm_hist_kernel(const int32_t* __restrict__ topk, int T,
-                                                       int E, int k, int32_t* __restrict__ hist) {
-  __shared__ int h[1024];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) h[e] = 0;
-  __syncthreads();
-  const int t = b * 64 + lane;
-  if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&h[topk[(int64_t)t * k + j]], 1);
-  __syncthreads();
-  for (int e = lane; e < E; e += 64) hist[(int64_t)b * E + e] = h[e];
-}
+// Two launches; the row of every kept assignment is fixed by expert and
+// token order, never by thread timing.
+// (1) perm_count_kernel, one 1024-thread workgroup: the histogram of the
+//     assignments per (block b of bt tokens, expert e) in LDS; per expert,
+//     the exclusive prefix of its column over blocks (base[b][e] = tokens
+//     before block b routed to e) and its total; totals clipped to the
+//     capacity; the exclusive scan of the clipped totals over experts
+//     (offsets). base goes to the workspace.
+// (2) perm_gather_kernel (below), one wave per token: the rank of each of the
+//     token's slots among its expert's assignments is base[b][e] plus the
+//     number of earlier tokens of the block routed to e (wave ballots); the
+//     slot is kept when the rank is below the capacity, at row
+//     offsets[e] + rank; then x[t] is copied to its kept rows.
+// bt is the smallest power-of-two multiple of 64 with ceil(T / bt) * E <=
+// kPermCells, so the histogram always fits the workgroup's LDS.
+constexpr int kPermCells = 32768;   // 128 KiB of int counts
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ hist, int nb, int T,
-                                                         int E, int k, int64_t cap,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ n_dropped) {
+__global__ __launch_bounds__(1024) void perm_count_kernel(const int32_t* __restrict__ topk, int T,
+                                                          int E, int k, int bt, int64_t cap,
+                                                          int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ n_dropped) {
+  __shared__ int h[kPermCells];
+  __shared__ int tot[1024];
   __shared__ int sc[1024];
   const int tid = threadIdx.x;
+  const int nb = (T + bt - 1) / bt;
+  const int cells = nb * E;
+  for (int c = tid; c < cells; c += 1024) h[c] = 0;
+  __syncthreads();
+  for (int t = tid; t < T; t += 1024) {
+    const int row = (t / bt) * E;
+    for (int j = 0; j < k; ++j) atomicAdd(&h[row + topk[(int64_t)t * k + j]], 1);
+  }
+  __syncthreads();
+  // column prefixes: P threads per expert, each over a chunk of ch blocks
+  const int P = 1024 / E;
+  const int e = tid / P, part = tid - e * P;
+  const int ch = (nb + P - 1) / P;
+  const int b0 = part * ch, b1 = min(nb, b0 + ch);
+  int s = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) s += h[b * E + e];
+  tot[tid] = s;
+  __syncthreads();
+  if (e < E) {
+    int run = 0;
+    for (int q = 0; q < part; ++q) run += tot[e * P + q];
+    for (int b = b0; b < b1; ++b) {
+      const int v = h[b * E + e];
+      h[b * E + e] = run;
+      run += v;
+    }
+    if (part == P - 1) sc[e] = run;   // the expert's total, before the capacity
+  }
+  __syncthreads();
   int kept = 0;
   if (tid < E) {
-    // 16 block counts are loaded before any is replaced (clamped, so the
-    // loads need no branch), then the running sum is written back.
-    int run = 0;
-    for (int b0 = 0; b0 < nb; b0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int bb = min(b0 + j, nb - 1);
-        const int h = hist[(int64_t)bb * E + tid];
-        v[j] = b0 + j < nb ? h : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (b0 + j < nb) hist[(int64_t)(b0 + j) * E + tid] = run;
-        run += v[j];
-      }
-    }
-    kept = (cap >= 0 && (int64_t)run > cap) ? (int)cap : run;
+    const int n = sc[tid];
+    kept = (cap >= 0 && (int64_t)n > cap) ? (int)cap : n;
   }
+  __syncthreads();
   sc[tid] = kept;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -434,142 +454,264 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ h
   if (tid < E) offsets[tid + 1] = sc[tid];
   if (tid == 0) {
     offsets[0] = 0;
-    n_dropped[0] = T * k - sc[E - 1];
+    n_dropped[0] = (int)((int64_t)T * k - sc[E - 1]);
+  }
+  for (int c = tid; c < cells; c += 1024) base[c] = h[c];
+}
+
+int perm_block_tokens(int T, int E) {
+  int bt = 64;
+  while ((int64_t)((T + bt - 1) / bt) * E > kPermCells) bt *= 2;
+  return bt;
+}
+
+size_t perm_ws_bytes(int T, int E) {
+  const int bt = perm_block_tokens(T, E);
+  return (size_t)((T + bt - 1) / bt) * E * 4;
+}
+
+// ------------------------------------------------- routed-row streaming
+// The permute gather, combine, combine backward and un-permute move rows of
+// d elements between token-indexed tensors [T, d] and routed-row tensors
+// [T*k, d]. One wave per token (4 tokens per 256-thread workgroup); lane l
+// takes 8-element chunks l, l + 64, ... of the row, so each wave instruction
+// moves 1 KiB (bf16) of one row. Routed rows go through buffer instructions
+// over the whole routed tensor: a dropped slot (row_of = -1) gets an offset
+// past the buffer's extent, so its loads return zeros and its stores are
+// dropped without touching memory, and every slot's load is issued before
+// any of them is used (no branch between a load and the next).
+// (check_desc bounds T*k*d*sizeof(T) below 2^31, so byte offsets fit 32 bits.)
+template <typename T> struct Rows;
+template <> struct Rows<bf16_t> {
+  typedef uint4 Packed;
+  static __device__ __forceinline__ Packed load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, Packed v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_, v), r, off, 0, 0);
+  }
+  static __device__ __forceinline__ Packed gload(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ void gstore(bf16_t* p, Packed v) { *reinterpret_cast<uint4*>(p) = v; }
+  static __device__ __forceinline__ void unpack(Packed u, float* v) {
+    v[0] = bf2f(u.x & 0xffff); v[1] = bf2f(u.x >> 16);
+    v[2] = bf2f(u.y & 0xffff); v[3] = bf2f(u.y >> 16);
+    v[4] = bf2f(u.z & 0xffff); v[5] = bf2f(u.z >> 16);
+    v[6] = bf2f(u.w & 0xffff); v[7] = bf2f(u.w >> 16);
+  }
+  static __device__ __forceinline__ Packed pack(const float* v) {
+    Packed u;
+    u.x = pack_bf2(v[0], v[1]); u.y = pack_bf2(v[2], v[3]);
+    u.z = pack_bf2(v[4], v[5]); u.w = pack_bf2(v[6], v[7]);
+    return u;
+  }
+};
+template <> struct Rows<float> {
+  struct Packed { uint4 a, b; };
+  static __device__ __forceinline__ Packed load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Packed p;
+    p.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    p.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off == kOOB ? kOOB : off + 16, 0, 0));
+    return p;
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, Packed v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_, v.a), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_, v.b), r, off == kOOB ? kOOB : off + 16, 0, 0);
+  }
+  static __device__ __forceinline__ Packed gload(const float* p) {
+    Packed v;
+    v.a = reinterpret_cast<const uint4*>(p)[0];
+    v.b = reinterpret_cast<const uint4*>(p)[1];
+    return v;
+  }
+  static __device__ __forceinline__ void gstore(float* p, Packed v) {
+    reinterpret_cast<uint4*>(p)[0] = v.a;
+    reinterpret_cast<uint4*>(p)[1] = v.b;
+  }
+  static __device__ __forceinline__ void unpack(Packed u, float* v) {
+    v[0] = __uint_as_float(u.a.x); v[1] = __uint_as_float(u.a.y);
+    v[2] = __uint_as_float(u.a.z); v[3] = __uint_as_float(u.a.w);
+    v[4] = __uint_as_float(u.b.x); v[5] = __uint_as_float(u.b.y);
+    v[6] = __uint_as_float(u.b.z); v[7] = __uint_as_float(u.b.w);
+  }
+  static __device__ __forceinline__ Packed pack(const float* v) {
+    Packed u;
+    u.a = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    u.b = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
+    return u;
+  }
+};
+
+// byte offset of a token's slot rows (kOOB for a dropped slot or j >= k);
+// row_of values are uniform across the wave (scalar loads)
+template <typename T, int KM>
+__device__ __forceinline__ void slot_rows(const int32_t* __restrict__ row_of, int64_t t, int k,
+                                          int64_t d, uint32_t* rb) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int r = j < k ? row_of[t * k + j] : -1;
+    rb[j] = r >= 0 ? (uint32_t)((int64_t)r * d * sizeof(T)) : kOOB;
   }
 }
 
-__global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ topk, int T,
-                                                       int E, int k, int64_t cap,
-                                                       const int32_t* __restrict__ base,
-                                                       const int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ row_of,
-                                                       int32_t* __restrict__ token_of) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int t = b * 64 + lane;
-  int mine[16];
+// Ranks and rows of token t's slots (see perm_count_kernel), then
+// x_perm[row] = x[t] for every kept slot.
+template <typename T, int KM>
+__global__ __launch_bounds__(256) void perm_gather_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ topk, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int ntok, int k, int E, int bt, int64_t cap, int64_t d,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of, T* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  int ex[KM], cnt[KM];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) mine[j] = (t < T && j < k) ? topk[(int64_t)t * k + j] : -1;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = 0; e < E; ++e) {
-    int slot = -1;
+  for (int j = 0; j < KM; ++j) {
+    ex[j] = j < k ? topk[t * k + j] : -1;
+    cnt[j] = 0;
+  }
+  // earlier tokens of this token's block routed to each of its experts
+  const int64_t t0 = (t / bt) * bt;
+  for (int64_t s0 = t0; s0 < t; s0 += 64) {
+    const int64_t tt = s0 + lane;
+    const bool valid = tt < t;
+    int me[KM];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (mine[j] == e) slot = j;
-    const uint64_t m = __ballot(slot >= 0);
-    if (m == 0) continue;
-    if (slot >= 0) {
-      const int64_t rank = (int64_t)base[(int64_t)b * E + e] + __popcll(m & lt);
-      if (cap < 0 || rank < cap) {
-        const int row = offsets[e] + (int)rank;
-        row_of[(int64_t)t * k + slot] = row;
-        token_of[row] = t;
-      } else {
-        row_of[(int64_t)t * k + slot] = -1;
-      }
+    for (int jj = 0; jj < KM; ++jj) me[jj] = (valid && jj < k) ? topk[tt * k + jj] : -2;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      bool m = false;
+#pragma unroll
+      for (int jj = 0; jj < KM; ++jj) m = m || me[jj] == ex[j];
+      cnt[j] += __popcll(__ballot(m && j < k));
     }
   }
-}
-
-// One block per token: read x[t] once, write it to each kept row.
-template <typename T>
-__global__ __launch_bounds__(256) void perm_gather_kernel(const T* __restrict__ x,
-                                                          const int32_t* __restrict__ row_of,
-                                                          int k, int64_t d,
-                                                          T* __restrict__ x_perm) {
-  const int64_t t = blockIdx.x;
-  int rows[16];
+  uint32_t rb[KM];
+  int myrow = -1;
+  const int32_t* brow = base + (t / bt) * E;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) rows[j] = j < k ? row_of[t * k + j] : -1;
-  constexpr int EL = 16 / sizeof(T);
-  const int64_t nch = d / EL;
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
-  for (int64_t c = threadIdx.x; c < nch; c += 256) {
-    const uint4 v = src[c];
+  for (int j = 0; j < KM; ++j) {
+    int row = -1;
+    if (j < k) {
+      const int64_t rank = (int64_t)brow[ex[j]] + cnt[j];
+      if (cap < 0 || rank < cap) row = offsets[ex[j]] + (int)rank;
+    }
+    rb[j] = row >= 0 ? (uint32_t)((int64_t)row * d * sizeof(T)) : kOOB;
+    if (lane == j) myrow = row;
+  }
+  if (lane < k) {
+    row_of[t * k + lane] = myrow;
+    if (myrow >= 0) token_of[myrow] = (int32_t)t;
+  }
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(x_perm, (int64_t)ntok * k * d * sizeof(T));
+  const T* xr = x + t * d;
+  for (int64_t c = lane; c < d / 8; c += 64) {
+    const typename Rows<T>::Packed v = Rows<T>::gload(xr + c * 8);
+    const uint32_t co = (uint32_t)(c * 8 * sizeof(T));
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (rows[j] >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)rows[j] * d)[c] = v;
+    for (int j = 0; j < KM; ++j) Rows<T>::store(rp, rb[j] == kOOB ? kOOB : rb[j] + co, v);
   }
 }
 
 hipError_t launch_permute(const void* x, bool bf16, const int32_t* topk, int T, int E, int k,
-                          int64_t d, int64_t cap, int32_t* hist, int32_t* offsets,
+                          int64_t d, int64_t cap, int32_t* base, int32_t* offsets,
                           int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* x_perm,
                           hipStream_t st) {
-  const int nb = (T + 63) / 64;
-  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(64), 0, st, topk, T, E, k, hist);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nb, T, E, k, cap, offsets, n_dropped);
-  hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(64), 0, st, topk, T, E, k, cap, hist, offsets, row_of, token_of);
-  if (bf16)
-    hipLaunchKernelGGL(perm_gather_kernel<bf16_t>, dim3(T), dim3(256), 0, st,
-                       (const bf16_t*)x, row_of, k, d, (bf16_t*)x_perm);
-  else
-    hipLaunchKernelGGL(perm_gather_kernel<float>, dim3(T), dim3(256), 0, st,
-                       (const float*)x, row_of, k, d, (float*)x_perm);
+  const int bt = perm_block_tokens(T, E);
+  hipLaunchKernelGGL(perm_count_kernel, dim3(1), dim3(1024), 0, st, topk, T, E, k, bt, cap, base,
+                     offsets, n_dropped);
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_GATHER(TY, KM)                                                                     \
+  hipLaunchKernelGGL((perm_gather_kernel<TY, KM>), grid, block, 0, st, (const TY*)x, topk, base, \
+                     offsets, T, k, E, bt, cap, d, row_of, token_of, (TY*)x_perm)
+  if (bf16) {
+    if (k <= 2) MOE_GATHER(bf16_t, 2);
+    else if (k <= 8) MOE_GATHER(bf16_t, 8);
+    else MOE_GATHER(bf16_t, 16);
+  } else {
+    if (k <= 2) MOE_GATHER(float, 2);
+    else if (k <= 8) MOE_GATHER(float, 8);
+    else MOE_GATHER(float, 16);
+  }
+#undef MOE_GATHER
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------- combine
-// y[t] = out_shared[t] + sum_j gate[t,j] * out[row_of[t,j]] (slot order).
-template <typename T>
+// y[t] = out_shared[t] + sum_j gate[t,j] * out[row_of[t,j]] (slot order,
+// float32, one rounding); a dropped slot adds nothing.
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
                                                       const T* __restrict__ out_shared,
                                                       const float* __restrict__ gate,
-                                                      const int32_t* __restrict__ row_of, int k,
-                                                      int64_t d, T* __restrict__ y) {
-  const int64_t t = blockIdx.x;
-  int rows[16];
-  float g[16];
+                                                      const int32_t* __restrict__ row_of, int ntok,
+                                                      int k, int64_t d, T* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (int64_t)ntok * k * d * sizeof(T));
+  uint32_t rb[KM];
+  float g[KM];
+  slot_rows<T, KM>(row_of, t, k, d, rb);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    rows[j] = j < k ? row_of[t * k + j] : -1;
-    g[j] = j < k ? gate[t * k + j] : 0.f;
-  }
-  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
+  for (int j = 0; j < KM; ++j) g[j] = j < k ? gate[t * k + j] : 0.f;
+  for (int64_t c = lane; c < d / 8; c += 64) {
+    const uint32_t co = (uint32_t)(c * 8 * sizeof(T));
+    typename Rows<T>::Packed pv[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) pv[j] = Rows<T>::load(ro, rb[j] == kOOB ? kOOB : rb[j] + co);
     float acc[8], v[8];
     if (out_shared) {
-      Vec8<T>::load(out_shared + t * d + c, acc);
+      Rows<T>::unpack(Rows<T>::gload(out_shared + t * d + c * 8), acc);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (rows[j] < 0) continue;
-      Vec8<T>::load(out + (int64_t)rows[j] * d + c, v);
+    for (int j = 0; j < KM; ++j) {
+      Rows<T>::unpack(pv[j], v);
+      const bool kept = rb[j] != kOOB;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = kept ? fmaf(g[j], v[i], acc[i]) : acc[i];
     }
-    Vec8<T>::store(y + t * d + c, acc);
+    Rows<T>::gstore(y + t * d + c * 8, Rows<T>::pack(acc));
   }
 }
 
-// dgate[t,j] = <dy[t], out[row]>, dout[row] = gate * dy[t]; one block per token.
-template <typename T>
+// dgate[t,j] = <dy[t], out[row]>, dout[row] = gate * dy[t]. Each lane keeps
+// one partial per slot (chunks in ascending order, an fma chain inside a
+// chunk); the wave's partials are then summed by a fixed butterfly.
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ out,
                                                           const float* __restrict__ gate,
                                                           const int32_t* __restrict__ row_of,
-                                                          int k, int64_t d,
+                                                          int ntok, int k, int64_t d,
                                                           float* __restrict__ dgate,
                                                           T* __restrict__ dout) {
-  __shared__ float red[4][16];
-  const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int rows[16];
-  float g[16], part[16];
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int64_t bytes = (int64_t)ntok * k * d * sizeof(T);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout, bytes);
+  uint32_t rb[KM];
+  float g[KM], part[KM];
+  slot_rows<T, KM>(row_of, t, k, d, rb);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    rows[j] = j < k ? row_of[t * k + j] : -1;
+  for (int j = 0; j < KM; ++j) {
     g[j] = j < k ? gate[t * k + j] : 0.f;
     part[j] = 0.f;
   }
-  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    float vy[8], vo[8], w[8];
-    Vec8<T>::load(dy + t * d + c, vy);
+  for (int64_t c = lane; c < d / 8; c += 64) {
+    const uint32_t co = (uint32_t)(c * 8 * sizeof(T));
+    typename Rows<T>::Packed pv[KM];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (rows[j] < 0) continue;
-      Vec8<T>::load(out + (int64_t)rows[j] * d + c, vo);
+    for (int j = 0; j < KM; ++j) pv[j] = Rows<T>::load(ro, rb[j] == kOOB ? kOOB : rb[j] + co);
+    float vy[8], vo[8], w[8];
+    Rows<T>::unpack(Rows<T>::gload(dy + t * d + c * 8), vy);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      Rows<T>::unpack(pv[j], vo);
       float p = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -577,92 +719,107 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
         w[i] = g[j] * vy[i];
       }
       part[j] += p;
-      Vec8<T>::store(dout + (int64_t)rows[j] * d + c, w);
+      Rows<T>::store(rd, rb[j] == kOOB ? kOOB : rb[j] + co, Rows<T>::pack(w));
     }
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j >= k) break;
-    const float s = wave_sum(part[j]);
-    if (lane == 0) red[wave][j] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x < k) {
-    const int j = threadIdx.x;
-    dgate[t * k + j] = rows[j] < 0 ? 0.f : ((red[0][j] + red[1][j]) + (red[2][j] + red[3][j]));
+    const float sj = wave_sum(part[j]);
+    if (lane == 0) dgate[t * k + j] = rb[j] == kOOB ? 0.f : sj;
   }
 }
 
 // dx[t] = dx_shared[t] + sum_j dx_perm[row_of[t,j]] + dx_router[t]; one rounding.
-template <typename T>
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void unpermute_kernel(const T* __restrict__ dx_perm,
                                                         const int32_t* __restrict__ row_of,
                                                         const T* __restrict__ dx_shared,
                                                         const float* __restrict__ dx_router,
-                                                        int k, int64_t d, T* __restrict__ dx) {
-  const int64_t t = blockIdx.x;
-  int rows[16];
+                                                        int ntok, int k, int64_t d,
+                                                        T* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(dx_perm, (int64_t)ntok * k * d * sizeof(T));
+  uint32_t rb[KM];
+  slot_rows<T, KM>(row_of, t, k, d, rb);
+  for (int64_t c = lane; c < d / 8; c += 64) {
+    const uint32_t co = (uint32_t)(c * 8 * sizeof(T));
+    typename Rows<T>::Packed pv[KM];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) rows[j] = j < k ? row_of[t * k + j] : -1;
-  for (int64_t c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    for (int j = 0; j < KM; ++j) pv[j] = Rows<T>::load(rp, rb[j] == kOOB ? kOOB : rb[j] + co);
     float acc[8], v[8];
     if (dx_shared) {
-      Vec8<T>::load(dx_shared + t * d + c, acc);
+      Rows<T>::unpack(Rows<T>::gload(dx_shared + t * d + c * 8), acc);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (rows[j] < 0) continue;
-      Vec8<T>::load(dx_perm + (int64_t)rows[j] * d + c, v);
+    for (int j = 0; j < KM; ++j) {
+      Rows<T>::unpack(pv[j], v);
+      const bool kept = rb[j] != kOOB;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int i = 0; i < 8; ++i) acc[i] = kept ? acc[i] + v[i] : acc[i];
     }
     if (dx_router) {
-      Vec8<float>::load(dx_router + t * d + c, v);
+      Vec8<float>::load(dx_router + t * d + c * 8, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
-    Vec8<T>::store(dx + t * d + c, acc);
+    Rows<T>::gstore(dx + t * d + c * 8, Rows<T>::pack(acc));
   }
 }
 
+// the smallest slot count instantiated that holds k (k <= 16)
+#define MOE_BY_K(MAC, TY)            \
+  do {                               \
+    if (k <= 1) MAC(TY, 1);          \
+    else if (k <= 2) MAC(TY, 2);     \
+    else if (k <= 4) MAC(TY, 4);     \
+    else if (k <= 8) MAC(TY, 8);     \
+    else MAC(TY, 16);                \
+  } while (0)
+
 hipError_t launch_combine(const void* out, const void* out_shared, bool bf16, const float* gate,
                           const int32_t* row_of, int T, int k, int64_t d, void* y, hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)out,
-                       (const bf16_t*)out_shared, gate, row_of, k, d, (bf16_t*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)out,
-                       (const float*)out_shared, gate, row_of, k, d, (float*)y);
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_COMB(TY, KM)                                                                        \
+  hipLaunchKernelGGL((combine_kernel<TY, KM>), grid, block, 0, st, (const TY*)out,             \
+                     (const TY*)out_shared, gate, row_of, T, k, d, (TY*)y)
+  if (bf16) MOE_BY_K(MOE_COMB, bf16_t);
+  else MOE_BY_K(MOE_COMB, float);
+#undef MOE_COMB
   return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const void* dy, const void* out, bool bf16, const float* gate,
                               const int32_t* row_of, int T, int k, int64_t d, float* dgate,
                               void* dout, hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)dy,
-                       (const bf16_t*)out, gate, row_of, k, d, dgate, (bf16_t*)dout);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)dy,
-                       (const float*)out, gate, row_of, k, d, dgate, (float*)dout);
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_CBWD(TY, KM)                                                                        \
+  hipLaunchKernelGGL((combine_bwd_kernel<TY, KM>), grid, block, 0, st, (const TY*)dy,          \
+                     (const TY*)out, gate, row_of, T, k, d, dgate, (TY*)dout)
+  if (bf16) MOE_BY_K(MOE_CBWD, bf16_t);
+  else MOE_BY_K(MOE_CBWD, float);
+#undef MOE_CBWD
   return hipGetLastError();
 }
 
 hipError_t launch_unpermute(const void* dx_perm, const int32_t* row_of, const void* dx_shared,
                             const float* dx_router, bool bf16, int T, int k, int64_t d, void* dx,
                             hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(unpermute_kernel<bf16_t>, dim3(T), dim3(256), 0, st,
-                       (const bf16_t*)dx_perm, row_of, (const bf16_t*)dx_shared, dx_router, k, d,
-                       (bf16_t*)dx);
-  else
-    hipLaunchKernelGGL(unpermute_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)dx_perm,
-                       row_of, (const float*)dx_shared, dx_router, k, d, (float*)dx);
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_UNP(TY, KM)                                                                         \
+  hipLaunchKernelGGL((unpermute_kernel<TY, KM>), grid, block, 0, st, (const TY*)dx_perm,       \
+                     row_of, (const TY*)dx_shared, dx_router, T, k, d, (TY*)dx)
+  if (bf16) MOE_BY_K(MOE_UNP, bf16_t);
+  else MOE_BY_K(MOE_UNP, float);
+#undef MOE_UNP
   return hipGetLastError();
 }
+#undef MOE_BY_K
 
 // ------------------------------------------------------- router backward
 // One wave per token: dlogits[t, :] from the renormalised-gate gradient and

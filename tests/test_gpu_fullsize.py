@@ -221,12 +221,12 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     gdl = to_np(L.dlogits)
     assert_close("dW_r(own dl)", to_np(L.dw_r), gdl.T @ x, dt, rep, rel=2e-5)
     # the whole router backward against the oracle's, on every token, given
-    # the GPU's own dgate (its forward inputs are the oracle's routing: tokens
-    # with a near-tie flip are left out of dlogits, and the oracle's dW_r
-    # then runs on the same token set as the GPU's own dl)
+    # the GPU's own routing and dgate (the GPU may list a token's two
+    # near-tied experts in the other slot order; its dgate follows its own
+    # order), with the oracle's scores and logits
     if not bad_e:
         g_dgate = to_np(L.dgate)
-        rb_all = O.router_backward(x, w_r, r["scores"], r["topk_idx"], gate, g_dgate, w.score,
+        rb_all = O.router_backward(x, w_r, r["scores"], g_idx, to_np(L.gate), g_dgate, w.score,
                                    w.aux_coef, st["y"], w.z_coef, r["logits"])
         floor_all = 2e-6 * float(np.abs(g_dgate).max(initial=0.0))
         assert_close("dlogits(own dgate, all tokens)", gdl, rb_all["dlogits"], dt, rep,
