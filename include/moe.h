@@ -15,7 +15,8 @@
  *   row-major and densely packed with the shape given below. The caller
  *   allocates and frees every buffer; the library never allocates, frees or
  *   keeps a pointer after a call returns. Scratch memory comes from the
- *   caller's workspace `ws` of at least moe_workspace_size(desc, op) bytes.
+ *   caller's workspace `ws` of at least moe_workspace_size(desc, op) bytes
+ *   (moe_permute_noalloc alone uses a library-owned device array instead).
  * Dtypes. "dt" means the layer dtype desc->dtype (MOE_F32: float, MOE_BF16:
  *   bfloat16 bit patterns). Router weight, biases, scores, gates, dgate,
  *   statistics, logits and their gradients are always float32. Indices,
@@ -164,6 +165,21 @@ int moe_bias_update(const moe_desc* desc, const int32_t* counts, float gamma, fl
 int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, int32_t* offsets,
                 int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* x_perm, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* moe_permute_noalloc: moe_permute with no workspace argument, for callers
+ * that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * moe_permute (bit-identical outputs); the permute's scratch (its per-block
+ * base counts, at most 128 KiB) lives in a library-owned device array, one
+ * per GPU, held until the process ends. It allocates nothing: the array's
+ * address is looked up once per device on the first call there.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (other streams or threads) race and must be serialised by the
+ * caller. A size that would need more scratch returns MOE_ERR_UNSUPPORTED
+ * (the permute chooses its token blocks so that it never does). */
+int moe_permute_noalloc(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                        int32_t* offsets, int32_t* row_of, int32_t* token_of, int32_t* n_dropped,
+                        void* x_perm, void* stream);
 
 /* ------------------------------------------------------------ grouped FFN
  * moe_grouped_ffn_fwd: the grouped GEMM of [Recipe] §4.2 - every expert's FFN

@@ -30,6 +30,7 @@ EXPORTS = (
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
     "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8", "moe_quantize_fp8_both",
+    "moe_permute_noalloc",
 )
 
 
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "moe_aux_stats": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
             "moe_bias_update": [DP, _P, ctypes.c_float, _P, _P],
             "moe_permute": [DP] + [_P] * 8 + [ctypes.c_size_t, _P],
+            "moe_permute_noalloc": [DP] + [_P] * 8,
             "moe_grouped_ffn_fwd": [DP] + [_P] * 14 + [ctypes.c_size_t, _P],
             "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                  ctypes.c_int64, _P, _P],
@@ -198,6 +200,13 @@ def permute(desc, x, topk_idx, offsets, row_of, token_of, n_dropped, x_perm, ws=
     _check("moe_permute", lib().moe_permute(ctypes.byref(desc), _p(x), _p(topk_idx), _p(offsets),
                                             _p(row_of), _p(token_of), _p(n_dropped), _p(x_perm),
                                             wp, wn, _stream(stream)))
+
+
+def permute_noalloc(desc, x, topk_idx, offsets, row_of, token_of, n_dropped, x_perm, stream=None):
+    """moe_permute without a workspace (the library's own device scratch)."""
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        ctypes.byref(desc), _p(x), _p(topk_idx), _p(offsets), _p(row_of), _p(token_of),
+        _p(n_dropped), _p(x_perm), _stream(stream)))
 
 
 def grouped_ffn_fwd(desc, x_perm, offsets, x, w13, w2, sw13, sw2, save_pre, save_h, save_pre_s,

@@ -332,6 +332,38 @@ int run_gemm(const moe_desc* d, const GemmArgs& p, bool akm, bool bkm, int epi, 
   return hip_check(e, what);
 }
 
+// ------------------------------------------------ library-owned scratch
+// moe_permute_noalloc keeps the permute's per-block base counts in this
+// array instead of a caller workspace. One copy per GPU (each device holds
+// its own at its own address); host code never passes the symbol itself to
+// a kernel, only the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+constexpr size_t kScratchBytes = 131072;   // the permute's largest histogram (32768 ints)
+static __device__ __align__(256) int32_t scratch[kScratchBytes / 4];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// device address of `scratch` on the current device (nullptr + error text on failure)
+void* scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(MOE_ERR_HIP, "scratch: no current device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(MOE_ERR_HIP, "scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,6 +571,33 @@ int moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx, in
                                   (int32_t*)ws, offsets, row_of, token_of, n_dropped, x_perm,
                                   (hipStream_t)stream),
                    "permute");
+}
+
+int moe_permute_noalloc(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                        int32_t* offsets, int32_t* row_of, int32_t* token_of, int32_t* n_dropped,
+                        void* x_perm, void* stream) {
+  g_err[0] = 0;
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(offsets, "offsets"));
+  MOE_TRY(need(row_of, "row_of"));
+  MOE_TRY(need(token_of, "token_of"));
+  MOE_TRY(need(n_dropped, "n_dropped"));
+  MOE_TRY(need(x_perm, "x_perm"));
+  const size_t want = ws_bytes_for(desc, MOE_OP_PERMUTE);
+  if (want > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "permute needs %zu bytes of scratch, the library holds %zu",
+                want, kScratchBytes);
+  if (desc->T == 0) return MOE_OK;
+  void* base = scratch_for_current_device();
+  if (!base) return MOE_ERR_HIP;
+  Scope sc(K_PERMUTE, (hipStream_t)stream);
+  return hip_check(launch_permute(x, desc->dtype == MOE_BF16, topk_idx, (int)desc->T,
+                                  (int)desc->E, (int)desc->k, desc->d, desc->capacity,
+                                  (int32_t*)base, offsets, row_of, token_of, n_dropped, x_perm,
+                                  (hipStream_t)stream),
+                   "permute (library scratch)");
 }
 
 int moe_grouped_ffn_fwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,

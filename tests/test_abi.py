@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 23
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +209,25 @@ def test_binding_signatures_match_header():
         for a in getattr(L, name).argtypes:
             got.append(ct.get(a, "ptr"))  # POINTER(...) types are pointers
         assert got == want, (name, got, want)
+
+
+def test_permute_noalloc_validation():
+    """The workspace-free permute checks its arguments as moe_permute does,
+    before any HIP call (fake pointers are never touched); T = 0 is a no-op."""
+    L = moe.lib()
+    D = _desc()
+    args = [FAKE] * 7
+    for i in range(7):
+        bad = list(args)
+        bad[i] = None
+        st = L.moe_permute_noalloc(ctypes.byref(D), *bad, None)
+        assert st == 1, (i, st)                       # MOE_ERR_INVALID_ARG
+        bad[i] = FAKE + 4
+        assert L.moe_permute_noalloc(ctypes.byref(D), *bad, None) == 1
+    Z = _desc(T=0)
+    assert L.moe_permute_noalloc(ctypes.byref(Z), *args, None) == 0
+    B = _desc(E=0)
+    assert L.moe_permute_noalloc(ctypes.byref(B), *args, None) == 1
 
 
 def test_fp8_quantize_validation():
