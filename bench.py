@@ -148,10 +148,14 @@ def gemm_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
 def traffic_for(kernel, workload):
-    """Measured HBM bytes per launch from the committed counter summary, if it
-    was taken on the current GEMM sources; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    """Measured HBM bytes per launch from the committed counter summary of this
+    workload, if it was taken on the current GEMM sources; else None."""
+    path = traffic_path(workload)
     try:
         with open(path) as fh:
             tr = json.load(fh)
@@ -175,12 +179,26 @@ def gemm_roles(w):
 
 CALIB_BYTES = 1 << 30   # plain device copy used to scale the HBM byte counters
 
+# streaming stages: the kernels each one launches (function names as the
+# profiler prints them) and its algorithmic bytes (hbm_bytes)
+STREAM_KERNELS = {"permute": ("perm_count_kernel", "perm_gather_kernel"),
+                  "combine": ("combine_kernel",), "combine_bwd": ("combine_bwd_kernel",),
+                  "unpermute": ("unpermute_kernel",)}
 
-def summarize_pmc(fetch_csv, write_csv, workload):
-    """HBM bytes per launch of each grouped-GEMM role from two rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
-    counter reads for the calibration copy of CALIB_BYTES (read once, written
-    once). Writes profiles/gemm_traffic.json."""
+
+def kernel_base_name(name):
+    """'void moe::combine_kernel<unsigned short, 8>(...)' -> 'combine_kernel'."""
+    head = name.split("(")[0].split("<")[0].strip()
+    return head.split("::")[-1].split()[-1]
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, stats_csv=None):
+    """HBM bytes per launch of each grouped-GEMM role and streaming stage from
+    two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
+    scaled by what the same counter reads for the calibration copy of
+    CALIB_BYTES (read once, written once). With a rocprofv3 --stats kernel
+    summary, the streaming stages also get their counted bytes over their
+    average duration (GB/s). Writes profiles/traffic_<workload>.json."""
     import csv
     w = WORKLOADS[workload]
     roles = gemm_roles(w)
@@ -195,10 +213,15 @@ def summarize_pmc(fetch_csv, write_csv, workload):
         per_role = {}
         for i, v in enumerate(gem):
             per_role.setdefault(roles[i % len(roles)], []).append(v)
-        return calib, per_role
+        per_kernel = {}
+        for r in rows:
+            per_kernel.setdefault(kernel_base_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return calib, per_role, per_kernel
 
-    fc, fr = load(fetch_csv, "FETCH_SIZE")
-    wc, wr = load(write_csv, "WRITE_SIZE")
+    # kept rows: every assignment without a capacity limit (else data-dependent)
+    A = w.T * w.k if w.cf is None else None
+    fc, fr, fk_all = load(fetch_csv, "FETCH_SIZE")
+    wc, wr, wk_all = load(write_csv, "WRITE_SIZE")
     if not fc or not wc:
         raise SystemExit("calibration copy not found in the counter files")
     f_scale = CALIB_BYTES / (fc[-1] * 1024.0)
@@ -208,13 +231,17 @@ def summarize_pmc(fetch_csv, write_csv, workload):
                        "$R = repository root, $OUT = a directory for the counter output",
            "commands": [
                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_fetch -o f "
-               "--output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-               "--no-profile --calibrate-copy",
+               f"--output-format csv -- python3 $R/bench.py --workload {workload} --steps 2 --warmup 1 "
+               "--no-cpu-baseline --no-profile --calibrate-copy",
                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_write -o w "
-               "--output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-               "--no-profile --calibrate-copy",
-               "python bench.py --summarize-pmc $OUT/pmc_fetch/f_counter_collection.csv "
-               "$OUT/pmc_write/w_counter_collection.csv"],
+               f"--output-format csv -- python3 $R/bench.py --workload {workload} --steps 2 --warmup 1 "
+               "--no-cpu-baseline --no-profile --calibrate-copy",
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/trace -o t "
+               f"--output-format csv -- python3 $R/bench.py --workload {workload} --steps 5 --warmup 2 "
+               "--no-cpu-baseline --no-profile",
+               f"python bench.py --workload {workload} --summarize-pmc "
+               "$OUT/pmc_fetch/f_counter_collection.csv $OUT/pmc_write/w_counter_collection.csv "
+               "$OUT/trace/t_kernel_stats.csv"],
            "calibration": {"bytes": CALIB_BYTES, "fetch_kib": fc[-1], "write_kib": wc[-1],
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": {}}
@@ -225,7 +252,28 @@ def summarize_pmc(fetch_csv, write_csv, workload):
         wk = sum(wr[role]) / len(wr[role])
         out["kernels"][role] = {"fetch_kib": fk, "write_kib": wk,
                                 "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale)}
-    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+        if A is not None:
+            out["kernels"][role]["algorithmic_bytes"] = gemm_bytes(w, A)[role]
+    stats = {}
+    if stats_csv:
+        for r in csv.DictReader(open(stats_csv)):
+            stats.setdefault(kernel_base_name(r["Name"]), []).append(float(r["AverageNs"]))
+    out["streaming"] = {}
+    for stage, kernels in STREAM_KERNELS.items():
+        if not all(k in fk_all and k in wk_all for k in kernels):
+            continue
+        byt = sum(sum(fk_all[k]) / len(fk_all[k]) * 1024 * f_scale
+                  + sum(wk_all[k]) / len(wk_all[k]) * 1024 * w_scale for k in kernels)
+        rec = {"kernels": list(kernels), "bytes_per_launch": int(byt)}
+        if A is not None:
+            rec["algorithmic_bytes"] = hbm_bytes(w, A)[stage]
+        if all(k in stats for k in kernels):
+            ns = sum(sum(stats[k]) / len(stats[k]) for k in kernels)
+            rec["avg_us"] = round(ns / 1e3, 2)
+            rec["counted_GB/s"] = round(byt / ns, 1)
+            rec["counted_hbm_frac"] = round(byt / ns / PEAK_HBM_GBS, 3)
+        out["streaming"][stage] = rec
+    path = traffic_path(workload)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -445,11 +493,15 @@ def main():
                          "torch's per-expert GEMM as context, and record GPU clocks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (counter calibration)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/gemm_traffic.json from two counter runs and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="FETCH_CSV WRITE_CSV [KERNEL_STATS_CSV]: write "
+                         "profiles/traffic_<workload>.json from two counter runs and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        if len(args.summarize_pmc) not in (2, 3):
+            ap.error("--summarize-pmc takes FETCH_CSV WRITE_CSV [KERNEL_STATS_CSV]")
+        pm = args.summarize_pmc
+        summarize_pmc(pm[0], pm[1], args.workload, pm[2] if len(pm) == 3 else None)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

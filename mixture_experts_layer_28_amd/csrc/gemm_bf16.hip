@@ -51,6 +51,16 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
+// 8 floats -> 8 bf16 at p (16-byte aligned), one nontemporal 16-byte store.
+// Every epilogue output (H, the saved pre-activations, dpre, C) is written
+// once and not read again by the launch, so it streams past the caches.
+__device__ __forceinline__ void store8_nt(bf16_t* p, const float* v) {
+  v4u32 u;
+  u[0] = pack_bf2(v[0], v[1]); u[1] = pack_bf2(v[2], v[3]);
+  u[2] = pack_bf2(v[4], v[5]); u[3] = pack_bf2(v[6], v[7]);
+  __builtin_nontemporal_store(u, reinterpret_cast<v4u32*>(p));
+}
+
 // byte offset of slot s (rows 8s..8s+7) of k-row k in a K-strided [64][kRows] tile
 __device__ __forceinline__ int ks_off(int k, int s) {
   return k * (kRows * 2) + ((s ^ ((k & 3) << 1)) << 4);
@@ -404,7 +414,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // sits at ((s ^ (r & 15)) << 4), so the 32 rows a (j, g) write touches
     // spread over all banks and a 16-lane group's row readback is a
     // permutation of one row. Lane (lr, lh) holds columns 32j + 8g + 4lh .. +3:
-    // slot 4j + g, 8-byte half lh.
+    // slot 4j + g, 8-byte half lh. The output is written once and not read
+    // again by this launch, so its stores are nontemporal (streamed past the
+    // caches): a weight gradient with K = 256 spends about 2.6 us of a 15 us
+    // tile issuing its 128 KiB of stores, and nontemporal ones take 1 us off.
     static_for<MI>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       static_for<NI * 4>([&](auto Q) __attribute__((always_inline)) {
@@ -423,7 +436,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int r = 4 * q + rq;
         const uint4 u = *reinterpret_cast<const uint4*>(stg + r * 256 + ((s8 ^ (r & 15)) << 4));
         const int64_t m = mrow0 + r;
-        if (m < t.M && nok) *reinterpret_cast<uint4*>(cb + m * p.ldc + n8) = u;
+        if (m < t.M && nok)
+          __builtin_nontemporal_store(__builtin_bit_cast(v4u32, u), reinterpret_cast<v4u32*>(cb + m * p.ldc + n8));
       });
       // the next block row overwrites the stage: finish this one's reads;
       // and keep its accumulator reads and conversions here (hoisted ahead,
@@ -472,9 +486,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (m >= t.M || hc >= p.N) return;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = silu_f(a[e]) * b[e];
-        Vec8<bf16_t>::store(cb + m * p.ldc + hc, h);
-        Vec8<bf16_t>::store(ab + m * p.ldaux + hc, a);
-        Vec8<bf16_t>::store(ab + m * p.ldaux + p.fdim + hc, b);
+        store8_nt(cb + m * p.ldc + hc, h);
+        store8_nt(ab + m * p.ldaux + hc, a);
+        store8_nt(ab + m * p.ldaux + p.fdim + hc, b);
       });
     } else {
       const bool nok = n8 < p.N;
@@ -488,12 +502,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int64_t m = mrow0 + r;
         if (m >= t.M || !nok) return;
         if (EPI == EPI_STORE) {
-          Vec8<bf16_t>::store(cb + m * p.ldc + n8, v);
+          store8_nt(cb + m * p.ldc + n8, v);
         } else if (EPI == EPI_GELU_FWD) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = gelu_f(v[e]);
-          Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
-          Vec8<bf16_t>::store(ab + m * p.ldaux + n8, v);
+          store8_nt(cb + m * p.ldc + n8, o);
+          store8_nt(ab + m * p.ldaux + n8, v);
         } else {
           float a[8];
           unpack8_bf16(ra[BWD ? q : 0], a);
@@ -505,12 +519,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
               o[e] = v[e] * b[e] * dsilu_f(a[e]);
               o2[e] = v[e] * silu_f(a[e]);
             }
-            Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
-            Vec8<bf16_t>::store(cb + m * p.ldc + p.fdim + n8, o2);
+            store8_nt(cb + m * p.ldc + n8, o);
+            store8_nt(cb + m * p.ldc + p.fdim + n8, o2);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = v[e] * dgelu_f(a[e]);
-            Vec8<bf16_t>::store(cb + m * p.ldc + n8, o);
+            store8_nt(cb + m * p.ldc + n8, o);
           }
         }
       });

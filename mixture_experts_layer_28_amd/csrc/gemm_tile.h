@@ -71,6 +71,27 @@ __device__ __forceinline__ void band_order(int64_t L, int64_t mt_total, int64_t 
   ntile = within / h;
 }
 
+// RAG_M tile order: logical tile L lies in group g when
+// s_tiles[g] * nt <= L < s_tiles[g+1] * nt, so a group's tiles are
+// contiguous and never share a band with another group's. Inside the group,
+// local tile u runs band_order over its mtg m-tiles, with the whole group as
+// one band when mtg <= kGroupBandMax. Experts with few rows (one or two
+// m-tiles) then run all their n-tiles side by side: each weight panel is
+// streamed once for both m-tiles and each A panel once for all n-tiles. In
+// bands that straddled groups, the tiles resident on an XCD at once read a
+// different expert's weight panel per m-tile and re-read the A panels every
+// few n-tiles (1.5x the algorithmic HBM traffic on the DeepSeek-like layer).
+constexpr int kGroupBandMax = 12;
+__device__ __forceinline__ void group_band_order(int64_t u, int64_t mtg, int64_t nt, int64_t& mt,
+                                                 int64_t& ntile) {
+  if (mtg <= kGroupBandMax) {
+    ntile = u / mtg;
+    mt = u - ntile * mtg;
+  } else {
+    band_order(u, mtg, nt, mt, ntile);
+  }
+}
+
 // Exclusive prefix over groups of ceil(M_g / BM) (M_g from offsets), written
 // to s_tiles[0..G] (s_tiles[G] = total; G + 1 ints). 256 threads, G <= 1024.
 template <int BM>
@@ -213,13 +234,14 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int* s_tiles, in
       L = xcd_tile(total * nt);
       if (L < 0) return false;
     }
+    t.g = find_group(s_tiles, p.G, L / nt);
     int64_t mt, ntile;
-    band_order(L, total, nt, mt, ntile);
-    t.g = find_group(s_tiles, p.G, mt);
+    const int64_t first = s_tiles[t.g];
+    group_band_order(L - first * nt, s_tiles[t.g + 1] - first, nt, mt, ntile);
     t.r0 = p.offsets[t.g];
     t.M = p.offsets[t.g + 1] - t.r0;
     t.K = p.K;
-    t.m0 = (mt - s_tiles[t.g]) * BM;
+    t.m0 = mt * BM;
     t.n0 = ntile * BNo;
     return true;
   }

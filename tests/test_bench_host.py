@@ -42,7 +42,7 @@ def test_fp8_launch_classification_and_labels():
 
 
 def test_traffic_is_used_only_for_the_sources_and_workload_it_was_taken_on(monkeypatch):
-    with open(os.path.join(ROOT, "profiles", "gemm_traffic.json")) as fh:
+    with open(bench.traffic_path("mixtral_bf16")) as fh:
         tr = json.load(fh)
     kernel = next(iter(tr["kernels"]))
     monkeypatch.setattr(bench, "gemm_source_hash", lambda: tr["source_sha"])

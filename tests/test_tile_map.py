@@ -1,13 +1,16 @@
 """CPU model of the grouped GEMMs' workgroup -> tile mapping.
 
 The kernels map blockIdx.x to a tile with integer arithmetic only
-(csrc/gemm_tile.h: group_tile_prefix, xcd_tile, band_order, resolve_tile and
-the launch grids in csrc/gemm_bf16.hip). This file restates that arithmetic
+(csrc/gemm_tile.h: group_tile_prefix, xcd_tile, band_order, group_band_order,
+resolve_tile and the launch grids in csrc/gemm_bf16.hip). This file restates that arithmetic
 in Python and checks, over many group layouts and CU counts, what the
 kernels rely on:
 
 * every tile of every group is computed exactly once, and surplus
   workgroups find no tile;
+* a RAG_M group's tiles are contiguous in the tile order, and a group of at
+  most 12 m-tiles is one band: its n-tiles advance together over all its
+  m-tiles;
 * with the split-K of each XCD's last, partial round of tiles, every split
   tile gets exactly its S parts, each once; its counter slot and its partial
   sums stay inside the workspace and no two tiles share them; the parts'
@@ -23,6 +26,7 @@ import pytest
 
 TAIL_CUS_MAX = 32          # the library sizes the split-K workspace for 32 CUs per XCD
 BAND_M = 8                 # m-tiles per band
+GROUP_BAND_MAX = 12        # a RAG_M group of at most this many m-tiles is one band
 
 
 def cdiv(a, b):
@@ -67,6 +71,12 @@ def band_order(L, mt_total, nt):
     return band * BAND_M + within % h, within // h
 
 
+def group_band_order(u, mtg, nt):
+    if mtg <= GROUP_BAND_MAX:
+        return u % mtg, u // mtg
+    return band_order(u, mtg, nt)
+
+
 def find_group(s_tiles, G, mt):
     lo, hi = 0, G - 1
     while lo < hi:
@@ -78,8 +88,9 @@ def find_group(s_tiles, G, mt):
     return lo
 
 
-def resolve_rag_m(bid, offsets, BM, BNo, N, tail_cus, s_tiles):
-    """One workgroup of a RAG_M launch: (g, m0, n0, S, part, slot, item) or None.
+def resolve_rag_m(bid, offsets, BM, BNo, N, tail_cus, s_tiles, with_L=False):
+    """One workgroup of a RAG_M launch: (g, m0, n0, S, part, slot, item) or None
+    (with_L: also the logical tile index).
     s_tiles: group_tile_prefix of the offsets (every workgroup computes the
     same prefix, so the model computes it once per launch)."""
     G = len(offsets) - 1
@@ -112,9 +123,11 @@ def resolve_rag_m(bid, offsets, BM, BNo, N, tail_cus, s_tiles):
         L = xcd_tile(bid, total * nt)
         if L < 0:
             return None
-    mt, ntile = band_order(L, total, nt)
-    g = find_group(s_tiles, G, mt)
-    return g, (mt - s_tiles[g]) * BM, ntile * BNo, S, part, slot, item
+    g = find_group(s_tiles, G, L // nt)
+    first = s_tiles[g]
+    mt, ntile = group_band_order(L - first * nt, s_tiles[g + 1] - first, nt)
+    r = (g, mt * BM, ntile * BNo, S, part, slot, item)
+    return r + (L,) if with_L else r
 
 
 def grid_rag_m(max_rows, G, BM, BNo, N, tail_cus):
@@ -252,3 +265,31 @@ def test_group_prefix_total_up_to_1024_groups(G):
     for c in counts:
         want.append(want[-1] + cdiv(c, 256))
     assert s == want
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rag_m_groups_are_contiguous_and_small_groups_one_band(seed):
+    rng = random.Random(seed)
+    G, BM, BNo, N = rng.choice([(9, 256, 256, 1024), (40, 256, 128, 2048), (256, 256, 256, 7168)])
+    counts = [rng.choice([0, rng.randrange(1, 600), rng.randrange(2000, 3300)]) for _ in range(G)]
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    s_tiles = group_tile_prefix(counts, BM)
+    nt = cdiv(N, BNo)
+    order = {}
+    for bid in range(grid_rag_m(offsets[-1], G, BM, BNo, N, 0)):
+        r = resolve_rag_m(bid, offsets, BM, BNo, N, 0, s_tiles, with_L=True)
+        if r is not None:
+            order[r[-1]] = r[:3]
+    assert sorted(order) == list(range(s_tiles[G] * nt))
+    for g in range(G):
+        Ls = sorted(L for L, t in order.items() if t[0] == g)
+        mtg = cdiv(counts[g], BM)
+        assert len(Ls) == mtg * nt
+        if Ls:
+            assert Ls == list(range(Ls[0], Ls[0] + len(Ls)))
+        if 0 < mtg <= GROUP_BAND_MAX:
+            # consecutive tiles: all m-tiles of n-tile 0, then of n-tile 1, ...
+            seq = [order[L][1:] for L in Ls]
+            assert seq == [(m * BM, n * BNo) for n in range(nt) for m in range(mtg)]
