@@ -215,11 +215,11 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     # down-projection is therefore checked to the bf16 bound against the
     # oracle's own FP8 down-projection of the GPU's H, and end to end against
     # a bound for such steps: one step in one of the f terms of a row moves it
-    # by up to about 2 * 2^-3 / sqrt(f) of max|O|.
+    # by up to about 0.5 / sqrt(f) of max|O| (fp8_fwd_tol).
     o_tol = {}
     if w.fp8:
         check_fp8_down_own_h(w, L, f, off, rep)
-        o_tol = dict(max_rel=max(2e-2, 0.25 / np.sqrt(w.f)))
+        o_tol = fp8_fwd_tol(w.f)
     assert_close("O", to_np(L.out[:A])[g_rows], fwd["O"][o_rows], dt, rep, **o_tol)
     if w.n_shared:
         assert_close("O_shared", to_np(L.out_shared), fwd["Os"], dt, rep, **o_tol)
@@ -242,8 +242,8 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     assert_close("dO", to_np(L.dout[:A])[g_rows[keep]], bwd["dO"][o_rows[keep]], dt, rep)
     # outputs computed from a requantized operand (FP8 data gradients) carry
     # the matrix core's accumulation error amplified by E4M3 rounding: see
-    # check_fp8_dgrad for the exact checks and FP8_DGRAD_TOL for this bound
-    dxt = FP8_DGRAD_TOL if w.fp8_bwd else {}
+    # check_fp8_dgrad for the exact checks and fp8_dgrad_tol for this bound
+    dxt = fp8_dgrad_tol(w.f) if w.fp8_bwd else {}
     assert_close("dX_perm", to_np(L.dx_perm[:A])[g_rows[keep]], bwd["dx_perm"][o_rows[keep]], dt, rep,
                  **dxt)
     gw13, gw2 = to_np(L.dw13), to_np(L.dw2)
@@ -279,15 +279,21 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     return len(flips)
 
 
-# FP8 data gradients: dX = deq(q(bf16 dpre)) W13^T. The matrix core's
-# accumulation of the FP8 dH GEMM is good to about 1e-4 of sum|products|
-# (measured); that moves some bf16 dpre values by one bf16 step, and a value
-# near an E4M3 rounding boundary then takes the neighbouring code, one E4M3
-# step (up to 2^-3 relative) away. Applying that perturbation to the oracle
-# itself moves dX by up to 3.1% of max|dX| (mean relative 0.8%) on the
-# DeepSeek-like reduced layer, so GPU-vs-oracle dX is held to 5% / 1.5%;
-# check_fp8_dgrad holds each stage to the bf16 bound separately.
-FP8_DGRAD_TOL = dict(max_rel=5e-2, l1_rel=1.5e-2)
+# FP8 bounds where each side quantizes a bf16 tensor it computed itself (H in
+# the forward, dpre in the data gradients). float32 on the device against
+# float64 in the oracle moves some bf16 values by one bf16 step, and a value
+# at an E4M3 rounding boundary then takes the neighbouring code, one E4M3 step
+# (2^-4 to 2^-3 of the element) away. One such code moves an output element
+# by up to about 0.42 / sqrt(f) of the tensor's max (derived, and measured on
+# an emulation of the device arithmetic, in tests/test_fp8_tolerance.py).
+# The exact stage checks (check_fp8_down_own_h, check_fp8_dgrad) hold each
+# FP8 product of the GPU's own bf16 operand to the bf16 bound.
+def fp8_fwd_tol(f):
+    return dict(max_rel=max(2e-2, 0.5 / np.sqrt(f)))
+
+
+def fp8_dgrad_tol(f):
+    return dict(max_rel=max(5e-2, 0.5 / np.sqrt(f)), l1_rel=1.5e-2)
 
 
 def _e4m3_rows_ref(M):

@@ -24,7 +24,7 @@ import torch
 
 import oracle as O
 from moe_inputs import WORKLOADS, as_f64, gen_all
-from parity_util import (FP8_DGRAD_TOL, Report, assert_close, assert_rows_match, bits, gpu_layer,
+from parity_util import (Report, assert_close, assert_rows_match, bits, fp8_dgrad_tol, gpu_layer,
                          to_np)
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
 
     def wq_t(m):
         return O.quantize_weights_fp8_t(m) if w.fp8_bwd else None
-    dxt = FP8_DGRAD_TOL if w.fp8_bwd else {}
+    dxt = fp8_dgrad_tol(w.f) if w.fp8_bwd else {}
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
