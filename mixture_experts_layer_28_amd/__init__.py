@@ -54,13 +54,15 @@ _P = ctypes.c_void_p
 
 
 def lib() -> ctypes.CDLL:
-    """Load libmoe.so (once). Raises if it is not built."""
+    """Load libmoe.so (once; MOE_LIBRARY names another build of it, such as
+    the host-sanitized one). Raises if it is not built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = os.environ.get("MOE_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m mixture_experts_layer_28_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         DP = ctypes.POINTER(MoeDesc)
         sig = {
             "moe_route": [DP] + [_P] * 10 + [ctypes.c_size_t, _P],
