@@ -340,6 +340,80 @@ def expert_backward(X, w13, w2, saved, dO, act):
     return dX, dw13, dw2, dpre
 
 
+# ----------------------------------------------- FP8 forward, block scales
+# Finer scales for the same FP8 forward. [Recipe] §8.1/§9.1 (FP8 GEMMs, bf16
+# activations) fix no granularity; the ranked follow-on asks for per-tile
+# scales. Reading taken: every K-contiguous operand row is cut into blocks of
+# FP8_BLOCK consecutive elements along K (the last block may be partial), and
+# each block gets its own power-of-two scale, chosen by the per-row rule on the
+# block's own maximum, then clipped to the 8-bit exponent scale's range
+# [-127, 127] (a block whose maximum is below 448 * 2^-127 keeps 2^-127, and
+# its elements round to E4M3 subnormals or zero). One scale per 32 elements
+# along K is what gfx950's block-scaled matrix instruction applies.
+FP8_BLOCK = 32
+FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -127, 127
+
+
+def quantize_blocks_fp8(X, block=FP8_BLOCK):
+    """Per-block FP8 quantization of the rows of X [n, K]: codes [n, K] uint8
+    and scale exponents [n, ceil(K / block)] with
+    X[i, k] ~= e4m3_decode(codes[i, k]) * 2^e[i, k // block]."""
+    X = np.asarray(X, dtype=np.float64)
+    n, K = X.shape
+    nb = -(-K // block)
+    e = np.zeros((n, nb), dtype=np.int64)
+    codes = np.zeros((n, K), dtype=np.uint8)
+    for j in range(nb):
+        blk = X[:, j * block:(j + 1) * block]
+        ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0)),
+                     FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX)
+        e[:, j] = ej
+        codes[:, j * block:(j + 1) * block] = e4m3_encode(blk * np.exp2(-ej.astype(np.float64))[:, None])
+    return codes, e
+
+
+def dequantize_blocks_fp8(codes, e, block=FP8_BLOCK):
+    e = np.asarray(e, dtype=np.float64)
+    K = codes.shape[1]
+    return e4m3_decode(codes) * np.repeat(np.exp2(e), block, axis=1)[:, :K]
+
+
+def quantize_weights_fp8_block(w):
+    """Dequantized block-scaled FP8 copy of a weight (rows = output channels,
+    blocks along the input dimension)."""
+    return dequantize_blocks_fp8(*quantize_blocks_fp8(w))
+
+
+def expert_forward_fp8_block(X, w13, w2, act):
+    """expert_forward_fp8 with block scales: X and w13 quantized per block of
+    their rows, the up-projection taken exactly on the dequantized values; H
+    kept in bf16, then that bf16 H and w2 quantized per block for the
+    down-projection."""
+    return expert_forward_fp8_block_wq(X, quantize_weights_fp8_block(w13),
+                                       quantize_weights_fp8_block(w2), act)
+
+
+def expert_forward_fp8_block_wq(X, w13d, w2d, act):
+    """expert_forward_fp8_block on weights already passed through
+    quantize_weights_fp8_block (rows quantize independently, so any subset of
+    weight rows quantizes the same way)."""
+    f = w2d.shape[1]
+    Xd = dequantize_blocks_fp8(*quantize_blocks_fp8(X))
+    pre = Xd @ w13d.T
+    if act == "swiglu":
+        a, b = pre[:, :f], pre[:, f:]
+        H = silu(a) * b
+        saved = dict(a=a, b=b, H=H)
+    elif act == "gelu":
+        a = pre
+        H = gelu(a)
+        saved = dict(a=a, H=H)
+    else:
+        raise ValueError(act)
+    Hd = dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(H)))
+    return Hd @ w2d.T, saved
+
+
 # ------------------------------------------------------------ FP8 backward
 # [Megatron10x] §5.2 trains in FP8 mixed precision and [Recipe] §8.1/§9.1 list
 # FP8 training with bf16 activations; which backward GEMMs run in FP8 is not
@@ -382,8 +456,9 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
     expert's GEMMs on its own contiguous rows. Optional shared experts
     ([Recipe] §2.3 / §9.1: an expert every token passes through) read all of
     x. Returns (O [A,d], Os [T,d] or None, saved). fp8=True runs every
-    expert (shared ones included) through expert_forward_fp8."""
-    fwd = expert_forward_fp8 if fp8 else expert_forward
+    expert (shared ones included) through expert_forward_fp8 (per-row
+    scales), fp8="block" through expert_forward_fp8_block."""
+    fwd = expert_forward_fp8_block if fp8 == "block" else (expert_forward_fp8 if fp8 else expert_forward)
     E = w13.shape[0]
     A = int(offsets[E])
     d = w2.shape[1]

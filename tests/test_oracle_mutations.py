@@ -145,6 +145,15 @@ MUTANTS = [
      "Hd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(H)))",
      "Hd = dequantize_rows_fp8(*quantize_rows_fp8(H))",
      [(P.test_expert_forward_fp8_brute_force, "swiglu")]),
+    ("FP8 block scales: one scale per row instead of per block",
+     "ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0)),",
+     "ej = np.clip(fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0)),",
+     [(P.test_fp8_blocks_keep_small_blocks_that_a_row_scale_loses,),
+      (P.test_fp8_blocks_brute_force_and_partial_last_block,)]),
+    ("FP8 block exponent not clipped to the scale range",
+     "FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -127, 127",
+     "FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -1000, 1000",
+     [(P.test_fp8_block_exponent_is_clipped_to_the_scale_range,)]),
 ]
 
 

@@ -769,3 +769,89 @@ def test_expert_forward_fp8_brute_force(act):
     # and it stays near the exact forward (quantization error only)
     exact, _ = O.expert_forward(X, w13, w2, act)
     assert np.abs(got - exact).max() < 0.15 * np.abs(exact).max()
+
+
+# ------------------------------------------------------- FP8 block scales
+def _brute_fp8_blocks(M, block=32):
+    """Dequantized block-scaled FP8 by brute force: per block of `block`
+    elements along a row, the exponent by search (clipped to [-127, 127]),
+    codes by torch's own cast."""
+    out = np.zeros_like(M)
+    for i, row in enumerate(M):
+        for j0 in range(0, row.size, block):
+            blk = row[j0:j0 + block]
+            a = np.abs(blk).max()
+            e = 0 if a == 0 else next(x for x in range(-200, 200) if a <= 448.0 * 2.0 ** x)
+            e = min(max(e, -127), 127)
+            out[i, j0:j0 + block] = O.e4m3_decode(_torch_e4m3_codes(blk / 2.0 ** e)) * 2.0 ** e
+    return out
+
+
+def test_fp8_blocks_reduce_to_rows_for_one_block():
+    """A row of at most one block quantizes exactly as the per-row scheme."""
+    rng = np.random.default_rng(40)
+    for K in (1, 16, 32):
+        X = O.round_bf16(rng.standard_normal((20, K)) * np.exp2(rng.integers(-30, 30, 20))[:, None])
+        qb, eb = O.quantize_blocks_fp8(X)
+        qr, er = O.quantize_rows_fp8(X)
+        assert (qb == qr).all() and (eb[:, 0] == er).all() and eb.shape == (20, 1)
+
+
+def test_fp8_blocks_brute_force_and_partial_last_block():
+    rng = np.random.default_rng(41)
+    for K in (64, 96, 100, 208):
+        X = O.round_bf16(rng.standard_normal((9, K)) * np.exp2(rng.integers(-12, 12, (9, 1))))
+        X[:, :32] *= 1e3                          # blocks of different magnitude
+        q, e = O.quantize_blocks_fp8(X)
+        assert e.shape == (9, -(-K // 32))
+        np.testing.assert_array_equal(O.dequantize_blocks_fp8(q, e), _brute_fp8_blocks(X))
+
+
+def test_fp8_blocks_keep_small_blocks_that_a_row_scale_loses():
+    """Each block takes its own scale: a block 2^20 below its row's largest
+    block keeps E4M3 precision (error at most 2^-4 of each element), while one
+    scale for the whole row rounds it to zero or subnormals."""
+    rng = np.random.default_rng(42)
+    big = 1.0 + rng.random(32)
+    small = (1.0 + rng.random(32)) * 2.0 ** -20
+    X = O.round_bf16(np.concatenate([big, small])[None, :])
+    D = O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(X))
+    assert (np.abs(D - X) <= 2.0 ** -4 * np.abs(X) * (1 + 1e-12)).all()
+    R = O.dequantize_rows_fp8(*O.quantize_rows_fp8(X))
+    assert np.abs(R[0, 32:] - X[0, 32:]).max() > 0.5 * np.abs(X[0, 32:]).max()
+
+
+def test_fp8_block_exponent_is_clipped_to_the_scale_range():
+    X = np.zeros((3, 64))
+    X[0, :32] = 2.0 ** -140                      # wants 2^-148: clipped to 2^-127
+    X[1, 32:] = 1.0                              # block 0 all zero: exponent 0
+    X[2, :] = 1.5 * 2.0 ** 100
+    q, e = O.quantize_blocks_fp8(X)
+    assert e.tolist() == [[-127, 0], [0, -8], [92, 92]]      # 1.5 * 2^100 <= 1.75 * 2^8 * 2^92
+    assert (O.e4m3_decode(q[0, :32]) == 0).all()  # 2^-13 of the smallest subnormal step: zero
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_expert_forward_fp8_block_brute_force(act):
+    """The block-scaled FP8 expert forward against explicit loops over
+    operands quantized by brute force (scale search per block + library E4M3
+    cast), with K = 40 and 24: a partial last block in both GEMMs."""
+    rng = np.random.default_rng(43)
+    n, d, f = 5, 40, 24
+    P = 2 * f if act == "swiglu" else f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    X[:, 32:] *= 2.0 ** -9                       # the partial block far below the first
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 6)
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 5)
+    Xd, W13d, W2d = _brute_fp8_blocks(X), _brute_fp8_blocks(w13), _brute_fp8_blocks(w2)
+    pre = np.array([[sum(Xd[t, c] * W13d[j, c] for c in range(d)) for j in range(P)] for t in range(n)])
+    if act == "swiglu":
+        a, b = pre[:, :f], pre[:, f:]
+        H = a / (1 + np.exp(-a)) * b
+    else:
+        H = 0.5 * pre * (1 + sps.erf(pre / np.sqrt(2)))
+    Hd = _brute_fp8_blocks(O.round_bf16(H))
+    out = np.array([[sum(Hd[t, j] * W2d[c, j] for j in range(f)) for c in range(d)] for t in range(n)])
+    got, saved = O.expert_forward_fp8_block(X, w13, w2, act)
+    np.testing.assert_allclose(got, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(saved["H"], H, rtol=1e-11, atol=1e-13)
