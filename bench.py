@@ -121,9 +121,10 @@ def is_fp8_gemm(w, name):
 def dtype_label(w):
     if w.dtype != "bf16":
         return "f32"
+    blk = " (1x32 block scales)" if w.fp8_scale == "block" else ""
     if w.fp8 and w.fp8_bwd:
-        return "fp8-e4m3 fwd and dgrad GEMMs, bf16 wgrad"
-    return "fp8-e4m3 fwd GEMMs, bf16 bwd" if w.fp8 else "bf16"
+        return f"fp8-e4m3 fwd{blk} and dgrad GEMMs, bf16 wgrad"
+    return f"fp8-e4m3 fwd GEMMs{blk}, bf16 bwd" if w.fp8 else "bf16"
 
 
 def hbm_bytes(w, A):
@@ -426,6 +427,8 @@ def streamed_oracle_step(w, g, tokens, clock):
         return out
 
     def fwd_e(X, w13e, w2e):
+        if ws.fp8 and ws.fp8_scale == "block":
+            return O.expert_forward_fp8_block(X, w13e, w2e, ws.act)
         if ws.fp8:
             return O.expert_forward_fp8(X, w13e, w2e, ws.act)
         return O.expert_forward(X, w13e, w2e, ws.act)
@@ -536,7 +539,7 @@ def main():
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
-                     fp8_bwd=w.fp8_bwd)
+                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()
@@ -636,6 +639,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "act": w.act, "score": w.score, "n_shared": w.n_shared,
                    "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8, "fp8_dgrad": w.fp8_bwd,
+                   "fp8_scale": w.fp8_scale if w.fp8 else None,
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
         "gemm_mfma_frac": round(mfma_frac, 4) if mfma_frac else None,

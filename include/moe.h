@@ -91,7 +91,8 @@ typedef enum {
   MOE_OP_FFN_BWD = 4,
   MOE_OP_ROUTE_BWD = 5,
   MOE_OP_FFN_FWD_FP8 = 6,
-  MOE_OP_FFN_BWD_FP8 = 7
+  MOE_OP_FFN_BWD_FP8 = 7,
+  MOE_OP_FFN_FWD_FP8B = 8
 } moe_op;
 
 /* ---------------------------------------------------------------- router
@@ -255,6 +256,59 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
                             const void* sw2q, const int32_t* ss2, void* save_pre, void* save_h,
                             void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* Block scales. [Recipe] §8.1 and §9.1 leave the FP8 scaling granularity
+ * open; the second FP8 mode reads it as one power-of-two scale per block of
+ * 32 consecutive elements along K of each operand row (the finest granularity
+ * the gfx950 block-scaled matrix instructions take), with the per-row rule of
+ * moe_quantize_fp8 applied to each block and the exponent clipped to
+ * [-127, 127].
+ *
+ * moe_quantize_fp8_blocks: row i, block b = k / 32 of a bf16 matrix ->
+ *   e[i][b] = clip(smallest integer e with max over the block |src| <= 448 * 2^e,
+ *                  -127, 127) (0 for an all-zero block),
+ *   codes[i][k] = E4M3 nearest (ties to even) of src[i][k] * 2^-e[i][k/32],
+ *   scales[i * SB + b] = e[i][b] + 127 (one byte, the e8m0 encoding),
+ *   SB = 4 * ceil(K / 128) bytes per row; bytes for blocks at or past K
+ *   (the padding to a 128-element step) hold 127 (a scale of 1).
+ * A last block shorter than 32 (K % 32 == 16) takes its max over what is
+ * there. The codes and bytes are a bit-exact function of the input; inputs
+ * must be finite. No desc: a plain matrix operation.
+ *   src        [rows, K] bf16, row stride ld_src elements (multiple of 8)   in
+ *   valid_rows device int32 or NULL: rows >= *valid_rows are left untouched in
+ *   codes      [rows, K] uint8, row stride ld_codes bytes (multiple of 16)  out
+ *   scales     [rows, SB] uint8, contiguous                                 out
+ * K must be a positive multiple of 16; rows < 2^31.
+ */
+int moe_quantize_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                            const int32_t* valid_rows, void* codes, int64_t ld_codes,
+                            uint8_t* scales, void* stream);
+
+/* moe_grouped_ffn_fwd_fp8b: moe_grouped_ffn_fwd_fp8 with block scales
+ * (moe_quantize_fp8_blocks codes and bytes) in place of per-row exponents.
+ * Each output element is sum over blocks b of
+ * 2^(e_row[b] + e_weight_row[b]) * sum_{k in b} e4m3 * e4m3, accumulated in
+ * float32 (the block-scaled MFMA applies both scales to each 32-k product).
+ * H is quantized with block scales into the workspace between the GEMMs.
+ * desc->dtype must be MOE_BF16; d and f multiples of 16.
+ *   xq_perm [T*k, d] uint8, bx_perm [T*k, SB(d)] uint8                    in
+ *   xq [T, d] uint8, bx [T, SB(d)] uint8: the shared expert's x           in (or NULL)
+ *   w13q [E, P, d] uint8, b13 [E, P, SB(d)] uint8                         in
+ *   w2q [E, d, f] uint8, b2 [E, d, SB(f)] uint8                           in
+ *   sw13q, sb13, sw2q, sb2: the shared expert's, or NULL                  in
+ *   save_pre, save_h, save_pre_s, save_h_s, out, out_shared: as in
+ *     moe_grouped_ffn_fwd (bf16)                                          out
+ *   ws         MOE_OP_FFN_FWD_FP8B bytes (H codes and block scales, then
+ *              the down-projection's split-K partials)                 scratch
+ * SB(K) = 4 * ceil(K / 128).
+ */
+int moe_grouped_ffn_fwd_fp8b(const moe_desc* desc, const void* xq_perm, const uint8_t* bx_perm,
+                             const int32_t* offsets, const void* xq, const uint8_t* bx,
+                             const void* w13q, const uint8_t* b13, const void* w2q,
+                             const uint8_t* b2, const void* sw13q, const uint8_t* sb13,
+                             const void* sw2q, const uint8_t* sb2, void* save_pre, void* save_h,
+                             void* save_pre_s, void* save_h_s, void* out, void* out_shared,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* moe_grouped_ffn_bwd: backward of moe_grouped_ffn_fwd ([VPP]: each device
  * runs forward and backward of its local experts between the exchanges).

@@ -21,7 +21,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
- MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8) = range(8)
+ MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD_FP8B) = range(9)
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -30,7 +30,7 @@ EXPORTS = (
     "moe_workspace_size", "moe_capacity", "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
     "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8", "moe_quantize_fp8_both",
-    "moe_permute_noalloc",
+    "moe_permute_noalloc", "moe_quantize_fp8_blocks", "moe_grouped_ffn_fwd_fp8b",
 )
 
 
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                  ctypes.c_int64, _P, _P],
             "moe_grouped_ffn_fwd_fp8": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
+            "moe_quantize_fp8_blocks": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                        ctypes.c_int64, _P, _P],
+            "moe_grouped_ffn_fwd_fp8b": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
             "moe_quantize_fp8_t": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P],
             "moe_quantize_fp8_both": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P],
@@ -240,6 +243,34 @@ def grouped_ffn_fwd_fp8(desc, xq_perm, sx_perm, offsets, xq, sx, w13q, s13, w2q,
     _check("moe_grouped_ffn_fwd_fp8", lib().moe_grouped_ffn_fwd_fp8(
         ctypes.byref(desc), _p(xq_perm), _p(sx_perm), _p(offsets), _p(xq), _p(sx), _p(w13q),
         _p(s13), _p(w2q), _p(s2), _p(sw13q), _p(ss13), _p(sw2q), _p(ss2), _p(save_pre),
+        _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
+        _stream(stream)))
+
+
+def fp8_block_bytes(K: int) -> int:
+    """Bytes of block scales per row of K elements: one byte per 32 elements,
+    padded to a 32-bit word per 128."""
+    return 4 * ((K + 127) // 128)
+
+
+def quantize_fp8_blocks(src, codes, scales, valid_rows=None, stream=None):
+    """Block-scaled E4M3 quantization of a bf16 tensor [..., K] into codes
+    (uint8, same shape) and e8m0 scale bytes (uint8, [..., fp8_block_bytes(K)])."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    if codes.shape != src.shape or scales.numel() != rows * fp8_block_bytes(K):
+        raise ValueError("codes must match src's shape and scales hold fp8_block_bytes(K) per row")
+    _check("moe_quantize_fp8_blocks", lib().moe_quantize_fp8_blocks(
+        _p(src), rows, K, K, _p(valid_rows), _p(codes), K, _p(scales), _stream(stream)))
+
+
+def grouped_ffn_fwd_fp8b(desc, xq_perm, bx_perm, offsets, xq, bx, w13q, b13, w2q, b2, sw13q, sb13,
+                         sw2q, sb2, save_pre, save_h, save_pre_s, save_h_s, out, out_shared,
+                         ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_grouped_ffn_fwd_fp8b", lib().moe_grouped_ffn_fwd_fp8b(
+        ctypes.byref(desc), _p(xq_perm), _p(bx_perm), _p(offsets), _p(xq), _p(bx), _p(w13q),
+        _p(b13), _p(w2q), _p(b2), _p(sw13q), _p(sb13), _p(sw2q), _p(sb2), _p(save_pre),
         _p(save_h), _p(save_pre_s), _p(save_h_s), _p(out), _p(out_shared), wp, wn,
         _stream(stream)))
 

@@ -161,10 +161,14 @@ struct GemmArgs {
   int64_t max_rows;         // RAG_M: upper bound of sum of M_g (grid sizing)
   int k_splits;             // split-K partitions (fp32 GEMM, RAG_NONE only); 1 = none
   // FP8 GEMM: power-of-two scale exponents, per A row (indexed like A's rows)
-  // and per weight row (group g at b_sexp + g * b_sexp_gstride)
+  // and per weight row (group g at b_sexp + g * b_sexp_gstride). With
+  // blk_scales, both point at block scales instead: per row, one 8-bit
+  // exponent byte (e + 127) per 32 elements along K, 4 * ceil(K / 128) bytes
+  // per row (one 32-bit word per 128-k step), and b_sexp_gstride counts words.
   const int32_t* a_sexp;
   const int32_t* b_sexp;
   int64_t b_sexp_gstride;
+  int blk_scales;
   // bf16 RAG_M plain-store GEMMs: split-K of each XCD's last, partial round of
   // tiles. tail_ws (null = off) holds tail_counters(cus) zeroed int32 counters,
   // then the fp32 partial accumulators; tail_cus = CUs per XCD.

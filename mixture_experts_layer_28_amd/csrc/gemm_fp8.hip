@@ -26,6 +26,16 @@
 // done); slice 1 (k-step kt+1's slice-0 fragments read; B_{kt+2} issued into
 // A_kt's buffer). A tiles have three slices to land, B tiles two; one DMA
 // instruction per two MFMAs.
+//
+// Block scales (BLK, GemmArgs::blk_scales): instead of one exponent per row,
+// one 8-bit exponent (e8m0: e + 127) per 32 elements along K of every row of
+// either operand, applied inside the matrix instruction by its block-scaled
+// form (v_mfma_scale_f32_32x32x64_f8f6f4): lane l supplies the exponent of
+// row l & 31 for the 32-k block l >> 5 of its 64-k slice. A row's 4 bytes of
+// a 128-k step form one 32-bit word; each lane loads its rows' words for the
+// next k-step with the current one's DMAs and shifts them right by 8 (l >> 5),
+// so byte 2 sl holds its block of slice sl. The epilogue then applies no
+// exponent.
 #include "gemm_tile.h"
 
 namespace moe {
@@ -83,7 +93,7 @@ __device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
   return v;
 }
 
-template <int EPI, int RAG>
+template <int EPI, int RAG, bool BLK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(GemmArgs p) {
   constexpr int BM = kRows8, BN = kRows8;
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
@@ -118,6 +128,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   dma_src8<false, WN>(da, p.a.ld, t.M, t.m0, p.fdim, wave, lane);
   dma_src8<FUSED, WN>(db, p.b.ld, FUSED ? p.fdim : p.N, t.n0, p.fdim, wave, lane);
 
+  // block scales: the 32-bit word offset of each of this lane's rows (rows
+  // outside are clamped into range: they read zero codes, so any exponent
+  // does); KW words per row
+  const int64_t KW = (t.K + kBK8 - 1) / kBK8;
+  const uint32_t* swa = reinterpret_cast<const uint32_t*>(p.a_sexp) +
+                        (BLK ? (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M) * KW : 0);
+  const uint32_t* swb = reinterpret_cast<const uint32_t*>(p.b_sexp) + (BLK ? (int64_t)t.g * p.b_sexp_gstride : 0);
+  uint32_t sa_off[BLK ? MI : 1], sb_off[BLK ? NI : 1];
+  uint32_t sa_nxt[BLK ? MI : 1], sb_nxt[BLK ? NI : 1], sa_cur[BLK ? MI : 1], sb_cur[BLK ? NI : 1];
+  if constexpr (BLK) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int64_t m = t.m0 + wm0 + 32 * i + (lane & 31);
+      sa_off[i] = (uint32_t)((m < t.M ? m : t.M - 1) * KW);
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = wn0 + 32 * j + (lane & 31);
+      int64_t n;
+      if (FUSED) n = fused_row(r, WN, t.n0, p.fdim);
+      else n = t.n0 + r < p.N ? t.n0 + r : -1;
+      sb_off[j] = (uint32_t)((n < 0 ? 0 : n) * KW);
+    }
+  }
+
   f32x16 acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -135,6 +170,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     kbase = per * t.part;
     nk = kbase >= nk ? 0 : (nk - kbase < per ? nk - kbase : per);
   }
+  // BLK: words of k-step kt into the nxt registers (k-steps past the end
+  // read the last word: their codes are zero); nxt -> cur, shifted
+  auto load_scales = [&](int64_t kt) __attribute__((always_inline)) {
+    if constexpr (BLK) {
+      const int64_t kg0 = kbase + kt;
+      const uint32_t kg = (uint32_t)(kg0 < KW ? kg0 : KW - 1);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sa_nxt[i] = swa[sa_off[i] + kg];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) sb_nxt[j] = swb[sb_off[j] + kg];
+    }
+  };
+  auto take_scales = [&]() __attribute__((always_inline)) {
+    if constexpr (BLK) {
+      const int sh = 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sa_cur[i] = sa_nxt[i] >> sh;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) sb_cur[j] = sb_nxt[j] >> sh;
+    }
+  };
 
   // DMA instruction i (0..7) of operand X (0 = A, 1 = B) of k-step kt into buffer s
   auto dma = [&](int64_t kt, int X, char* s, int i) __attribute__((always_inline)) {
@@ -160,19 +216,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Transposed accumulation (B fragment first): lane l holds row
   // wm0+32i+(l&31) and, in acc[i][j][4g..4g+3], columns wn0+32j+8g+4(l>>5)+0..3.
   // Constant zero scale operands select the unscaled instruction (scale 1).
-  auto mma = [&](int4 (*fa)[2], int4 (*fb)[2], int q) __attribute__((always_inline)) {
+  // BLK: the first operand (B rows) takes sb_cur[j], the second (A rows)
+  // sa_cur[i]; byte 2 sl of the shifted word is the lane's 32-k block of
+  // slice sl
+  auto mma = [&](int4 (*fa)[2], int4 (*fb)[2], int q, auto SL) __attribute__((always_inline)) {
     const int i = q / NI, j = q % NI;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
+    if constexpr (BLK) {
+      constexpr int os = 2 * decltype(SL)::value;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, os, (int)sb_cur[j], os,
+          (int)sa_cur[i]);
+    } else {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
   };
 
   // 16 MFMAs on (fa, fb), reading slice rsl of (rsa, rsb) into (ga, gb)
   // between them and issuing operand X of k-step dk into ds, one DMA per two
   auto slice = [&](int4 (*fa)[2], int4 (*fb)[2], int4 (*ga)[2], int4 (*gb)[2], const char* rsa,
-                   const char* rsb, int rsl, int64_t dk, int X, char* ds) __attribute__((always_inline)) {
+                   const char* rsb, int rsl, int64_t dk, int X, char* ds, auto SL) __attribute__((always_inline)) {
     static_for<NM>([&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
-      mma(fa, fb, q);
+      mma(fa, fb, q, SL);
       __builtin_amdgcn_sched_barrier(0);
       ldfrag(ga, gb, rsa, rsb, rsl, q >> 1, q & 1);
       if (q & 1) dma(dk, X, ds, q >> 1);
@@ -180,19 +246,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
   };
 
+  // BLK: k-step kt's scale words (loaded during k-step kt-1) become the
+  // current ones, and k-step kt+1's are loaded before this k-step's DMAs, so
+  // the wait below (only A_{kt+2} in flight) also covers them
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   auto kstep = [&](int64_t kt, char* a0, char* b0, char* a1, char* b1, char* a2, char* b2)
       __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    slice(xa, xb, ya, yb, a0, b0, 1, kt + 2, 0, a2);
+    take_scales();
+    load_scales(kt + 1);
+    slice(xa, xb, ya, yb, a0, b0, 1, kt + 2, 0, a2, S0{});
     wait_vm<8>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    slice(ya, yb, xa, xb, a1, b1, 0, kt + 2, 1, b2);
+    slice(ya, yb, xa, xb, a1, b1, 0, kt + 2, 1, b2, S1{});
   };
 
   if (nk > 0) {
-    // as if just before k-step 0: A0, B0 landed, A1 and B1 in flight
+    // as if just before k-step 0: A0, B0 (and k-step 0's scale words) landed,
+    // A1 and B1 in flight
+    load_scales(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma(0, 0, h0, i);
 #pragma unroll
@@ -320,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t mrow0 = t.m0 + wm0 + 32 * i;
     // lane lr holds the scale exponent of row mrow0 + lr (clamped into range)
     const int64_t mcl = mrow0 + lr < t.M ? mrow0 + lr : t.M - 1;
-    const int ea_l = asx[mcl];
+    const int ea_l = BLK ? 0 : asx[mcl];
     // 8 consecutive staged columns (slots slot, slot+1) of row r
     auto ld8 = [&](int r, int slot, float* v) __attribute__((always_inline)) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * 512 + ((slot ^ (r & 7)) << 4));
@@ -339,9 +414,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int sg = lane & 7, rr = lane >> 3;
       const int64_t hc = t.n0 + (wave & 1) * (WN / 2) + 8 * sg;
       const int64_t hcl = hc < p.N ? hc : p.N - 8;
-      int egs[8], eus[8];
-      ld_exp8(bsx + hcl, egs);
-      ld_exp8(bsx + p.fdim + hcl, eus);
+      int egs[8] = {0, 0, 0, 0, 0, 0, 0, 0}, eus[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (!BLK) {
+        ld_exp8(bsx + hcl, egs);
+        ld_exp8(bsx + p.fdim + hcl, eus);
+      }
       static_for<4>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
         const int r = 8 * q + rr;
@@ -366,8 +443,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int s8 = lane & 15, rq = lane >> 4;
       const int64_t n = t.n0 + wn0 + 8 * s8;
       const bool nok = n < p.N;
-      int ebs[8];
-      ld_exp8(bsx + (nok ? n : p.N - 8), ebs);
+      int ebs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (!BLK) ld_exp8(bsx + (nok ? n : p.N - 8), ebs);
       static_for<8>([&](auto Q) __attribute__((always_inline)) {
         constexpr int q = decltype(Q)::value;
         const int r = 4 * q + rq;
@@ -412,7 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   });
 }
 
-template <int EPI, int RAG>
+template <int EPI, int RAG, bool BLK>
 hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
   constexpr int BNo = EPI == EPI_SWIGLU_FWD ? kRows8 / 2 : kRows8;
   const int64_t nt = (p.N + BNo - 1) / BNo;
@@ -425,7 +502,7 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
   // tail split-K: up to tail_cus more items per XCD
   if (RAG == RAG_M && EPI == EPI_STORE && p.tail_ws) nb += 8 * (int64_t)p.tail_cus;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG>), dim3((unsigned)nb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG, BLK>), dim3((unsigned)nb), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -438,7 +515,19 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
   if (!p.a_sexp || !p.b_sexp || p.col_bias) return hipErrorInvalidValue;
 #define MOE_CASE(E_, R_) \
-  if (epi == E_ && rag == R_) return launch_fp8<E_, R_>(p, s);
+  if (epi == E_ && rag == R_) return launch_fp8<E_, R_, false>(p, s);
+#define MOE_CASE_BLK(E_, R_) \
+  if (epi == E_ && rag == R_) return launch_fp8<E_, R_, true>(p, s);
+  if (p.blk_scales) {
+    // block scales: the forward GEMMs
+    MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_M)
+    MOE_CASE_BLK(EPI_GELU_FWD, RAG_M)
+    MOE_CASE_BLK(EPI_STORE, RAG_M)
+    MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_NONE)
+    MOE_CASE_BLK(EPI_GELU_FWD, RAG_NONE)
+    MOE_CASE_BLK(EPI_STORE, RAG_NONE)
+    return hipErrorInvalidValue;
+  }
   MOE_CASE(EPI_SWIGLU_FWD, RAG_M)
   MOE_CASE(EPI_GELU_FWD, RAG_M)
   MOE_CASE(EPI_STORE, RAG_M)
@@ -450,6 +539,7 @@ hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
   MOE_CASE(EPI_SWIGLU_BWD, RAG_NONE)
   MOE_CASE(EPI_GELU_BWD, RAG_NONE)
 #undef MOE_CASE
+#undef MOE_CASE_BLK
   return hipErrorInvalidValue;
 }
 

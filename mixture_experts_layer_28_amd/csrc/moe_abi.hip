@@ -14,6 +14,9 @@
 
 namespace moe {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
+hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                                   const int32_t* valid_rows, void* codes, int64_t ld_q,
+                                   uint8_t* scales, hipStream_t st);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
 hipError_t launch_quant_fp8_t(const void*, int64_t, int64_t, int64_t, void*, int32_t*, hipStream_t);
@@ -258,6 +261,10 @@ int enable_tail(GemmArgs& q, void* tw, hipStream_t s) {
   return MOE_OK;
 }
 
+// bytes of block scales per row of K elements: one byte per 32, padded to a
+// 32-bit word per 128
+size_t blk_scale_bytes(int64_t K) { return (size_t)4 * ((K + 127) / 128); }
+
 size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
   switch (op) {
@@ -294,6 +301,14 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return ws_bytes_for(d, MOE_OP_FFN_BWD) + align256((size_t)T * d->k * d->d) +
              align256((size_t)T * d->k * 4) + align256((size_t)T * d->k * pre_cols(d)) +
              align256((size_t)T * d->k * 4);
+    case MOE_OP_FFN_FWD_FP8B: {
+      // FP8 codes and block scales of H between the two GEMMs, then the
+      // down-projection's split-K tail
+      const size_t sb = blk_scale_bytes(d->f);
+      size_t b = align256((size_t)T * d->k * d->f) + align256((size_t)T * d->k * sb);
+      if (d->n_shared) b += align256((size_t)T * d->f) + align256((size_t)T * sb);
+      return b + tail_ws_bytes(kTailCusMax);
+    }
   }
   return 0;
 }
@@ -433,7 +448,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_BWD_FP8)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FP8B)
     return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
   *bytes = ws_bytes_for(desc, op);
   return MOE_OK;
@@ -692,13 +707,18 @@ int moe_quantize_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                    "fp8 quantize");
 }
 
-int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int32_t* sx_perm,
-                            const int32_t* offsets, const void* xq, const int32_t* sx,
-                            const void* w13q, const int32_t* s13, const void* w2q,
-                            const int32_t* s2, const void* sw13q, const int32_t* ss13,
-                            const void* sw2q, const int32_t* ss2, void* save_pre, void* save_h,
-                            void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
-                            size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The FP8 forward with per-row exponents (blk = false: int32 per row) or
+// block scales (blk = true: bytes, blk_scale_bytes(K) per row).
+int ffn_fwd_fp8_impl(bool blk, const moe_desc* desc, const void* xq_perm, const void* sx_perm,
+                     const int32_t* offsets, const void* xq, const void* sx, const void* w13q,
+                     const void* s13, const void* w2q, const void* s2, const void* sw13q,
+                     const void* ss13, const void* sw2q, const void* ss2, void* save_pre,
+                     void* save_h, void* save_pre_s, void* save_h_s, void* out, void* out_shared,
+                     void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (desc->dtype != MOE_BF16)
@@ -726,25 +746,31 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
     MOE_TRY(need(save_h_s, "save_h_s"));
     MOE_TRY(need(out_shared, "out_shared"));
   }
-  MOE_TRY(check_ws(desc, MOE_OP_FFN_FWD_FP8, ws, ws_bytes));
+  const int op = blk ? MOE_OP_FFN_FWD_FP8B : MOE_OP_FFN_FWD_FP8;
+  MOE_TRY(check_ws(desc, op, ws, ws_bytes));
   if (desc->T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
   const int epi1 = desc->act == MOE_SWIGLU ? EPI_SWIGLU_FWD : EPI_GELU_FWD;
+  // H codes and its scales (4 bytes per row, or blk_scale_bytes(f)) between
+  // the GEMMs; scale row strides in 32-bit words for the block scales
+  const size_t hsb = blk ? blk_scale_bytes(f) : 4;
+  const int64_t kwd = (d + 127) / 128, kwf = (f + 127) / 128;
   char* w = (char*)ws;
   uint8_t* hq = (uint8_t*)w;
-  int32_t* hs = (int32_t*)(w + align256((size_t)T * desc->k * f));
-  uint8_t* hq_s = (uint8_t*)((char*)hs + align256((size_t)T * desc->k * 4));
-  int32_t* hs_s = desc->n_shared ? (int32_t*)((char*)hq_s + align256((size_t)T * f)) : nullptr;
-  char* tail_w = w + ws_bytes_for(desc, MOE_OP_FFN_FWD_FP8) - tail_ws_bytes(kTailCusMax);
+  void* hs = w + align256((size_t)T * desc->k * f);
+  uint8_t* hq_s = (uint8_t*)((char*)hs + align256((size_t)T * desc->k * hsb));
+  void* hs_s = desc->n_shared ? (void*)((char*)hq_s + align256((size_t)T * f)) : nullptr;
+  char* tail_w = w + ws_bytes_for(desc, op) - tail_ws_bytes(kTailCusMax);
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
     const int rag = shared ? RAG_NONE : RAG_M;
     GemmArgs p = blank();
     p.a = opnd(shared ? xq : xq_perm, d, 0, 1);
     p.b = opnd(shared ? sw13q : w13q, d, P * d, 0);
-    p.a_sexp = shared ? sx : sx_perm;
-    p.b_sexp = shared ? ss13 : s13;
-    p.b_sexp_gstride = P;
+    p.a_sexp = (const int32_t*)(shared ? sx : sx_perm);
+    p.b_sexp = (const int32_t*)(shared ? ss13 : s13);
+    p.b_sexp_gstride = blk ? P * kwd : P;
+    p.blk_scales = blk;
     p.c = shared ? save_h_s : save_h;
     p.ldc = f;
     p.c_rowidx = 1;
@@ -765,19 +791,23 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
     // H (bf16, kept for the backward) -> FP8 codes for the down-projection;
     // routed rows beyond offsets[E] are skipped on the device
     uint8_t* q8 = shared ? hq_s : hq;
-    int32_t* qs = shared ? hs_s : hs;
+    void* qs = shared ? hs_s : hs;
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(launch_quant_fp8(shared ? save_h_s : save_h, shared ? T : T * desc->k, f, f,
-                                         shared ? nullptr : offsets + desc->E, q8, f, qs, s),
+      const void* hsrc = shared ? save_h_s : save_h;
+      const int64_t hrows = shared ? T : T * desc->k;
+      const int32_t* hvalid = shared ? nullptr : offsets + desc->E;
+      MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(hsrc, hrows, f, f, hvalid, q8, f, (uint8_t*)qs, s)
+                            : launch_quant_fp8(hsrc, hrows, f, f, hvalid, q8, f, (int32_t*)qs, s),
                         "fp8 quantize H"));
     }
     GemmArgs q = blank();
     q.a = opnd(q8, f, 0, 1);
     q.b = opnd(shared ? sw2q : w2q, f, d * f, 0);
-    q.a_sexp = qs;
-    q.b_sexp = shared ? ss2 : s2;
-    q.b_sexp_gstride = d;
+    q.a_sexp = (const int32_t*)qs;
+    q.b_sexp = (const int32_t*)(shared ? ss2 : s2);
+    q.b_sexp_gstride = blk ? d * kwf : d;
+    q.blk_scales = blk;
     q.c = shared ? out_shared : out;
     q.ldc = d;
     q.c_rowidx = 1;
@@ -792,6 +822,60 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
     MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, rag, s), "fp8 ffn fwd down matrix"));
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int32_t* sx_perm,
+                            const int32_t* offsets, const void* xq, const int32_t* sx,
+                            const void* w13q, const int32_t* s13, const void* w2q,
+                            const int32_t* s2, const void* sw13q, const int32_t* ss13,
+                            const void* sw2q, const int32_t* ss2, void* save_pre, void* save_h,
+                            void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return ffn_fwd_fp8_impl(false, desc, xq_perm, sx_perm, offsets, xq, sx, w13q, s13, w2q, s2, sw13q,
+                          ss13, sw2q, ss2, save_pre, save_h, save_pre_s, save_h_s, out, out_shared, ws,
+                          ws_bytes, stream);
+}
+
+int moe_grouped_ffn_fwd_fp8b(const moe_desc* desc, const void* xq_perm, const uint8_t* bx_perm,
+                             const int32_t* offsets, const void* xq, const uint8_t* bx,
+                             const void* w13q, const uint8_t* b13, const void* w2q,
+                             const uint8_t* b2, const void* sw13q, const uint8_t* sb13,
+                             const void* sw2q, const uint8_t* sb2, void* save_pre, void* save_h,
+                             void* save_pre_s, void* save_h_s, void* out, void* out_shared, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return ffn_fwd_fp8_impl(true, desc, xq_perm, bx_perm, offsets, xq, bx, w13q, b13, w2q, b2, sw13q,
+                          sb13, sw2q, sb2, save_pre, save_h, save_pre_s, save_h_s, out, out_shared,
+                          ws, ws_bytes, stream);
+}
+
+int moe_quantize_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                            const int32_t* valid_rows, void* codes, int64_t ld_codes,
+                            uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || rows >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31) (got %lld)", (long long)rows);
+  if (K < 16 || K % 16)
+    return fail(MOE_ERR_INVALID_ARG, "K must be a positive multiple of 16 (got %lld)", (long long)K);
+  if (ld_src < K || ld_src % 8)
+    return fail(MOE_ERR_INVALID_ARG, "ld_src must be >= K and a multiple of 8 (got %lld)",
+                (long long)ld_src);
+  if (ld_codes < K || ld_codes % 16)
+    return fail(MOE_ERR_INVALID_ARG, "ld_codes must be >= K and a multiple of 16 (got %lld)",
+                (long long)ld_codes);
+  MOE_TRY(need(src, "src"));
+  MOE_TRY(need(codes, "codes"));
+  MOE_TRY(need(scales, "scales"));
+  if (valid_rows && (reinterpret_cast<uintptr_t>(valid_rows) & 3))
+    return fail(MOE_ERR_INVALID_ARG, "valid_rows is not 4-byte aligned");
+  if (rows == 0) return MOE_OK;
+  Scope sc(K_QUANT_FP8, (hipStream_t)stream);
+  return hip_check(launch_quant_fp8_blocks(src, rows, K, ld_src, valid_rows, codes, ld_codes, scales,
+                                           (hipStream_t)stream),
+                   "fp8 quantize blocks");
 }
 
 int moe_grouped_ffn_bwd(const moe_desc* desc, const void* x_perm, const int32_t* offsets,

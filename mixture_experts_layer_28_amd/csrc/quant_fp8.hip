@@ -94,6 +94,38 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
   for (int64_t c = tid + (int64_t)kQCache * kQThreads; c < nch; c += kQThreads) q[c] = to_e4m3(s[c], e);
 }
 
+// ---- block scales: one exponent per 32 elements along K
+// Row r, block b (elements 32b .. 32b+31, the last one partial when K is not
+// a multiple of 32): e = the per-row rule on the block's maximum, clipped to
+// [-127, 127]; codes as above; the exponent is stored as the byte e + 127 at
+// scales[r * sld + b], sld = 4 * ceil(K / 128) (a 32-bit word per 128 k,
+// padding blocks past K hold 127). One thread per 8 elements (a 16-byte
+// chunk); the four threads of a block agree on its maximum through two
+// lane swaps. Grid: x = rows, y = chunks of 256 threads over sld * 4 chunks.
+__global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
+    const bf16_t* __restrict__ src, int64_t K, int64_t ld_src, const int32_t* __restrict__ valid_rows,
+    uint8_t* __restrict__ codes, int64_t ld_q, uint8_t* __restrict__ scales, int64_t sld) {
+  const int64_t row = blockIdx.x;
+  if (valid_rows && row >= (int64_t)*valid_rows) return;
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;   // chunk of 8 elements
+  if (c >= sld * 4) return;   // a whole group of four threads is in or out
+  const int64_t nch = K / 8;
+  const uint4 v = c < nch ? *reinterpret_cast<const uint4*>(src + row * ld_src + 8 * c) : make_uint4(0, 0, 0, 0);
+  uint32_t m = absmax8(v, 0);
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    const uint32_t t = __shfl_xor(m, o, 64);
+    m = t > m ? t : m;
+  }
+  const float amax = bf2f(m);
+  int ex = 0;
+  const float mant = frexpf(amax, &ex);
+  int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  if (c < nch) *reinterpret_cast<uint2*>(codes + row * ld_q + 8 * c) = to_e4m3(v, e);
+  if ((c & 3) == 0) scales[row * sld + c / 4] = (uint8_t)(e + 127);
+}
+
 // ---- per-column quantization into the transpose
 // src: G row-major R x C bf16 matrices; codes: G row-major C x R (the
 // transposes), so codes row c is src column c quantized like a row above.
@@ -368,6 +400,19 @@ hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(kQThreads), 0, st,
                      (const bf16_t*)src, K, ld_src, valid_rows, (uint8_t*)codes, ld_q, sexp);
+  return hipGetLastError();
+}
+
+// Block-scaled rows: codes [rows, K] (row stride ld_q) and scales
+// [rows, 4 * ceil(K / 128)] bytes. K % 8 == 0, 16-byte aligned source rows.
+hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
+                                   const int32_t* valid_rows, void* codes, int64_t ld_q,
+                                   uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || K == 0) return hipSuccess;
+  const int64_t sld = 4 * ((K + 127) / 128);
+  const dim3 grid((unsigned)rows, (unsigned)((sld * 4 + 255) / 256));
+  hipLaunchKernelGGL(quant_blocks_fp8_kernel, grid, dim3(256), 0, st, (const bf16_t*)src, K, ld_src,
+                     valid_rows, (uint8_t*)codes, ld_q, scales, sld);
   return hipGetLastError();
 }
 

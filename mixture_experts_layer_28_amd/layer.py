@@ -10,9 +10,10 @@ from typing import Optional
 import torch
 
 from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
-               MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine,
-               combine_bwd, grouped_ffn_bwd, grouped_ffn_bwd_fp8, grouped_ffn_fwd, grouped_ffn_fwd_fp8,
-               make_desc, permute, permute_bwd, quantize_fp8, quantize_fp8_both,
+               MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats,
+               bias_update, combine, combine_bwd, fp8_block_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8,
+               grouped_ffn_fwd, grouped_ffn_fwd_fp8, grouped_ffn_fwd_fp8b, make_desc, permute,
+               permute_bwd, quantize_fp8, quantize_fp8_blocks, quantize_fp8_both,
                quantize_fp8_both_ws, quantize_fp8_t, route, route_bwd, workspace_size)
 
 
@@ -39,12 +40,18 @@ class MoELayer:
     upstream and pre-activation gradients per row; the weight gradients stay
     bf16. The transposed codes a forward made serve the next backward on the
     same weight tensors (weights do not change between the two).
+
+    fp8_scale picks the forward's scaling: "row" (one power-of-two scale per
+    operand row) or "block" (one per 32 elements along K of each row, e8m0
+    bytes, on the block-scaled matrix instructions). The backward's FP8 GEMMs
+    keep per-row scales either way; with "block" the backward quantizes the
+    weight transposes itself.
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
                  bias_gamma: float = 0.0, gumbel_tau: float = 0.0, fp8_fwd: bool = False,
-                 fp8_bwd: bool = False, device="cuda"):
+                 fp8_bwd: bool = False, fp8_scale: str = "row", device="cuda"):
         self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
@@ -52,6 +59,9 @@ class MoELayer:
         self.fp8_fwd, self.fp8_bwd = fp8_fwd, fp8_bwd
         if (fp8_fwd or fp8_bwd) and dtype != "bf16":
             raise ValueError("the FP8 GEMMs keep bf16 activations: dtype must be bf16")
+        if fp8_scale not in ("row", "block"):
+            raise ValueError(f"fp8_scale must be 'row' or 'block' (got {fp8_scale!r})")
+        self.fp8_block = fp8_fwd and fp8_scale == "block"
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dt = dt
         P = 2 * f if act == "swiglu" else f
@@ -100,13 +110,19 @@ class MoELayer:
         self.dX = z(T, d)
         if fp8_fwd:
             u8 = torch.uint8
-            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), z(R, dtype=i32)
-            self.w13q, self.s13 = z(E, P, d, dtype=u8), z(E, P, dtype=i32)
-            self.w2q, self.s2 = z(E, d, f, dtype=u8), z(E, d, dtype=i32)
+            # per-row exponents (int32), or block-scale bytes per row
+            if self.fp8_block:
+                sd, sf = (fp8_block_bytes(d),), (fp8_block_bytes(f),)
+                st = u8
+            else:
+                sd, sf, st = (), (), i32
+            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), z(R, *sd, dtype=st)
+            self.w13q, self.s13 = z(E, P, d, dtype=u8), z(E, P, *sd, dtype=st)
+            self.w2q, self.s2 = z(E, d, f, dtype=u8), z(E, d, *sf, dtype=st)
             sh = bool(n_shared)
-            self.xq, self.sx = (z(T, d, dtype=u8), z(T, dtype=i32)) if sh else (None, None)
-            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), z(1, P, dtype=i32)) if sh else (None, None)
-            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
+            self.xq, self.sx = (z(T, d, dtype=u8), z(T, *sd, dtype=st)) if sh else (None, None)
+            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), z(1, P, *sd, dtype=st)) if sh else (None, None)
+            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), z(1, d, *sf, dtype=st)) if sh else (None, None)
         if fp8_bwd:
             u8 = torch.uint8
             sh = bool(n_shared)
@@ -115,7 +131,8 @@ class MoELayer:
             self.sw13q_t, self.ss13_t = (z(1, d, P, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
             self.sw2q_t, self.ss2_t = (z(1, f, d, dtype=u8), z(1, f, dtype=i32)) if sh else (None, None)
         ops = [MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
-               MOE_OP_ROUTE_BWD] + ([MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
+               MOE_OP_ROUTE_BWD] + \
+              ([MOE_OP_FFN_FWD_FP8B if self.fp8_block else MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
               ([MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
         wsb = max(workspace_size(self.desc, op) for op in ops)
         if fp8_fwd and fp8_bwd:   # both weight orientations from the forward's one pass
@@ -133,7 +150,20 @@ class MoELayer:
                   self.aux_out, self.ws)
         permute(D, x, self.topk_idx, self.offsets, self.row_of, self.token_of, self.n_dropped,
                 self.x_perm, self.ws)
-        if self.fp8_fwd:
+        if self.fp8_block:
+            quantize_fp8_blocks(self.x_perm, self.xq_perm, self.sx_perm,
+                                valid_rows=self.offsets[self.E:])
+            quantize_fp8_blocks(w13, self.w13q, self.s13)
+            quantize_fp8_blocks(w2, self.w2q, self.s2)
+            if self.n_shared:
+                quantize_fp8_blocks(x, self.xq, self.sx)
+                quantize_fp8_blocks(sw13, self.sw13q, self.ss13)
+                quantize_fp8_blocks(sw2, self.sw2q, self.ss2)
+            grouped_ffn_fwd_fp8b(D, self.xq_perm, self.sx_perm, self.offsets, self.xq, self.sx,
+                                 self.w13q, self.s13, self.w2q, self.s2, self.sw13q, self.ss13,
+                                 self.sw2q, self.ss2, self.save_pre, self.save_h, self.save_pre_s,
+                                 self.save_h_s, self.out, self.out_shared, self.ws)
+        elif self.fp8_fwd:
             quantize_fp8(self.x_perm, self.xq_perm, self.sx_perm, valid_rows=self.offsets[self.E:])
             if self.fp8_bwd:
                 # rows for the forward and columns (transposes) for the backward in one pass

@@ -32,6 +32,8 @@ Routing variants and the per-GPU shard:
   skewed_cf15_bf16    the skewed GELU layer with capacity factor 1.5
   dsv3_ep8_shard_bf16 the DeepSeek-like layer's local share under 8-way expert
                       parallelism: 32 experts, about 2048 rows each
+FP8 variants (*_fp8_*: per-row scales, *_fp8b_*: one scale per 32 elements
+along K) of the Mixtral-like layer and of that shard.
 """
 from __future__ import annotations
 
@@ -66,7 +68,8 @@ class Workload:
     z_coef: float = 0.0           # weight of the router z-loss in the backward (softmax only)
     bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
     gumbel_tau: Optional[float] = None   # noisy gate temperature; draws uniforms [T, E]
-    fp8: bool = False             # forward GEMMs on per-row E4M3 operands (bf16 activations)
+    fp8: bool = False             # forward GEMMs on E4M3 operands (bf16 activations)
+    fp8_scale: str = "row"        # the forward's FP8 scales: "row" or "block" (32 along K)
     fp8_bwd: bool = False         # backward data-gradient GEMMs on E4M3 operands as well
     seed: int = 0
 
@@ -108,6 +111,12 @@ WORKLOADS = {
     "dsv3_ep8_shard_fp8_bf16": Workload("dsv3_ep8_shard_fp8_bf16", T=8192, d=7168, E=32, k=8,
                                         f=2048, score="sigmoid", n_shared=1, sel_bias=True,
                                         fp8=True),
+    # FP8 forward with one scale per 32 elements along K (block-scaled MFMA)
+    "mixtral_fp8b_bf16": Workload("mixtral_fp8b_bf16", T=8192, d=4096, E=8, k=2, f=14336,
+                                  cf=1.25, fp8=True, fp8_scale="block"),
+    "dsv3_ep8_shard_fp8b_bf16": Workload("dsv3_ep8_shard_fp8b_bf16", T=8192, d=7168, E=32, k=8,
+                                         f=2048, score="sigmoid", n_shared=1, sel_bias=True,
+                                         fp8=True, fp8_scale="block"),
     # FP8 forward and FP8 data gradients; weight gradients bf16
     "mixtral_fp8_dgrad_bf16": Workload("mixtral_fp8_dgrad_bf16", T=8192, d=4096, E=8, k=2,
                                        f=14336, cf=1.25, fp8=True, fp8_bwd=True),

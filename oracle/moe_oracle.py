@@ -342,8 +342,8 @@ def expert_backward(X, w13, w2, saved, dO, act):
 
 # ----------------------------------------------- FP8 forward, block scales
 # Finer scales for the same FP8 forward. [Recipe] §8.1/§9.1 (FP8 GEMMs, bf16
-# activations) fix no granularity; the ranked follow-on asks for per-tile
-# scales. Reading taken: every K-contiguous operand row is cut into blocks of
+# activations) fix no granularity; one scale per row loses the small blocks of
+# a row whose parts differ by many binades. Reading taken: every K-contiguous operand row is cut into blocks of
 # FP8_BLOCK consecutive elements along K (the last block may be partial), and
 # each block gets its own power-of-two scale, chosen by the per-row rule on the
 # block's own maximum, then clipped to the 8-bit exponent scale's range

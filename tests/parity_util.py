@@ -52,12 +52,20 @@ def bits(t):
 
 
 # -------------------------------------------------------------- runners
+def oracle_fp8(w: Workload):
+    """The oracle's fp8 argument for a workload: False, True (per-row scales)
+    or "block"."""
+    if not w.fp8:
+        return False
+    return "block" if w.fp8_scale == "block" else True
+
+
 def gpu_layer(w: Workload, g: dict):
     import mixture_experts_layer_28_amd as moe
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
-                     fp8_bwd=w.fp8_bwd)
+                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -69,7 +77,7 @@ def oracle_layer(w: Workload, g: dict):
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     fwd = O.layer_forward(f["x"], f["w_r"], f["w13"], f["w2"], w.k, w.score, w.act, cap,
                           f["logit_bias"], f["sel_bias"], f["sw13"], f["sw2"], f["gumbel_u"],
-                          w.gumbel_tau, fp8=w.fp8)
+                          w.gumbel_tau, fp8=oracle_fp8(w))
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
                            w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau,
                            fp8_dgrad=w.fp8_bwd)
@@ -360,8 +368,15 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
 
 def check_fp8_down_own_h(w, L, f, off, rep):
     """FP8 down-projection of the GPU's own bf16 H (routed experts, and the
-    shared expert on all tokens), recomputed by the oracle: per-row E4M3 codes
-    of H against the per-row quantized W2, held to the bf16 bound."""
+    shared expert on all tokens), recomputed by the oracle: E4M3 codes of H
+    against the quantized W2 (per row, or per 32-element block with
+    fp8_scale "block"), held to the bf16 bound."""
+    if w.fp8_scale == "block":
+        qa = lambda m: O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m))   # noqa: E731
+        qw = O.quantize_weights_fp8_block
+    else:
+        qa = lambda m: O.dequantize_rows_fp8(*O.quantize_rows_fp8(m))   # noqa: E731
+        qw = O.quantize_weights_fp8
     A = int(off[-1])
     Hg = to_np(L.save_h[:A]).astype(np.float64)
     Og = to_np(L.out[:A]).astype(np.float64)
@@ -370,12 +385,12 @@ def check_fp8_down_own_h(w, L, f, off, rep):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
             continue
-        own = O.dequantize_rows_fp8(*O.quantize_rows_fp8(Hg[r0:r1])) @ O.quantize_weights_fp8(w2[e]).T
+        own = qa(Hg[r0:r1]) @ qw(w2[e]).T
         assert_close(f"O(own H) e{e}", Og[r0:r1], own, "bf16", rep)
     if w.n_shared:
         hs = to_np(L.save_h_s).astype(np.float64)
         sw2 = f["sw2"][0]
-        own = O.dequantize_rows_fp8(*O.quantize_rows_fp8(hs)) @ O.quantize_weights_fp8(sw2).T
+        own = qa(hs) @ qw(sw2).T
         assert_close("O_shared(own H)", to_np(L.out_shared).astype(np.float64), own, "bf16", rep)
 
 

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 25
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -264,6 +264,53 @@ def test_fp8_forward_validation():
     assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
     assert call(_desc(), ws_bytes=16) == 3
     assert call(_desc(T=0)) == 0
+
+
+def test_fp8_block_quantize_validation():
+    """Bad sizes, strides and pointers fail before any HIP call; rows = 0 is
+    a successful no-op."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ok = dict(src=FAKE, rows=4, K=80, ld_src=80, valid=None, codes=FAKE, ld_q=80, sc=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        ptr = lambda v: P(v) if v else None   # noqa: E731
+        return L.moe_quantize_fp8_blocks(ptr(a["src"]), a["rows"], a["K"], a["ld_src"],
+                                         ptr(a["valid"]), ptr(a["codes"]), a["ld_q"], ptr(a["sc"]),
+                                         None)
+    for bad in (dict(K=8), dict(K=72), dict(ld_src=64), dict(ld_src=84), dict(ld_q=88),
+                dict(rows=-1), dict(rows=1 << 31), dict(src=0), dict(codes=FAKE + 8),
+                dict(sc=0), dict(sc=FAKE + 4), dict(valid=FAKE + 2)):
+        assert call(**bad) == 1, bad
+        assert L.moe_last_error().decode()
+    assert call(rows=0) == 0
+
+
+def test_fp8_block_forward_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE)] * 19
+
+    def call(d, ws_bytes=1 << 40, p=ptrs):
+        return L.moe_grouped_ffn_fwd_fp8b(ctypes.byref(d), *p, P(FAKE), ws_bytes, None)
+    assert call(_desc(dtype="f32")) == 2
+    assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
+    assert call(_desc(T=0)) == 0
+    # the workspace holds H's codes and block scales (4 bytes per 128 of f)
+    d = _desc(T=64, k=2, f=256)
+    need = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_FWD_FP8B, ctypes.byref(need)) == 0
+    row = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_FWD_FP8, ctypes.byref(row)) == 0
+    assert need.value - row.value == 256 * ((128 * 8 + 255) // 256) - 256 * ((128 * 4 + 255) // 256)
+    assert call(d, ws_bytes=need.value - 1) == 3
+    # a NULL or misaligned block-scale array is rejected
+    for bad_v in (None, P(FAKE + 4)):
+        bad = list(ptrs)
+        bad[1] = bad_v
+        assert call(_desc(), p=bad) == 1
 
 
 def test_fp8_transposing_quantize_validation():

@@ -39,6 +39,8 @@ def test_fp8_launch_classification_and_labels():
     assert bench.dtype_label(f8) == "fp8-e4m3 fwd GEMMs, bf16 bwd"
     assert bench.dtype_label(f8d) == "fp8-e4m3 fwd and dgrad GEMMs, bf16 wgrad"
     assert bench.dtype_label(WORKLOADS["tiny_fp32"]) == "f32"
+    assert bench.dtype_label(WORKLOADS["mixtral_fp8b_bf16"]) == \
+        "fp8-e4m3 fwd GEMMs (1x32 block scales), bf16 bwd"
 
 
 def test_traffic_is_used_only_for_the_sources_and_workload_it_was_taken_on(monkeypatch):
@@ -47,6 +49,10 @@ def test_traffic_is_used_only_for_the_sources_and_workload_it_was_taken_on(monke
     kernel = next(iter(tr["kernels"]))
     monkeypatch.setattr(bench, "gemm_source_hash", lambda: tr["source_sha"])
     assert bench.traffic_for(kernel, tr["workload"]) == int(tr["kernels"][kernel]["bytes_per_launch"])
+    # no summary for this workload; a summary taken on another workload
+    assert bench.traffic_for(kernel, "top1_bf16") is None
+    monkeypatch.setattr(bench, "traffic_path", lambda w: os.path.join(ROOT, "profiles",
+                                                                       "traffic_mixtral_bf16.json"))
     assert bench.traffic_for(kernel, "finegrained_bf16") is None
     monkeypatch.setattr(bench, "gemm_source_hash", lambda: "0" * 16)
     assert bench.traffic_for(kernel, tr["workload"]) is None

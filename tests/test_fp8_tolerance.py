@@ -79,18 +79,28 @@ def _rel(got, ref):
     return err.max() / np.abs(ref).max(), err.sum() / np.abs(ref).sum()
 
 
-def forward_gap(rng, E, n, d, f):
+def _q_rows(m):
+    return O.dequantize_rows_fp8(*O.quantize_rows_fp8(m))
+
+
+def _q_blocks(m):
+    return O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m))
+
+
+def forward_gap(rng, E, n, d, f, block=False):
     """max and L1 relative gap of the routed O (E experts of n rows) between
-    the device emulation and the oracle's FP8 forward."""
+    the device emulation and the oracle's FP8 forward (per-row scales, or
+    one scale per 32 elements along K with block=True)."""
+    q, qw = (_q_blocks, O.quantize_weights_fp8_block) if block else (_q_rows, O.quantize_weights_fp8)
+    efwd = O.expert_forward_fp8_block_wq if block else O.expert_forward_fp8_wq
     got, ref = [], []
     for _ in range(E):
         X, w13, w2 = _draw(rng, n, d, f)
-        w13d, w2d = O.quantize_weights_fp8(w13), O.quantize_weights_fp8(w2)
-        r, _ = O.expert_forward_fp8_wq(X, w13d, w2d, "swiglu")
-        Xd = O.dequantize_rows_fp8(*O.quantize_rows_fp8(X))
-        pre = _device_matmul(Xd, w13d, rng).astype(np.float32)
+        w13d, w2d = qw(w13), qw(w2)
+        r, _ = efwd(X, w13d, w2d, "swiglu")
+        pre = _device_matmul(q(X), w13d, rng).astype(np.float32)
         H = _bf16(_silu32(pre[:, :f]) * pre[:, f:])
-        got.append(O.dequantize_rows_fp8(*O.quantize_rows_fp8(H)) @ w2d.T)
+        got.append(q(H) @ w2d.T)
         ref.append(r)
     return _rel(np.concatenate(got), np.concatenate(ref))
 
@@ -124,12 +134,16 @@ SHAPES = [(32, 32, 512, 256), (8, 64, 256, 512), (16, 64, 256, 64), (8, 128, 128
 SEEDS = 3
 
 
-@pytest.mark.parametrize("kind", ["forward", "dgrad"])
+@pytest.mark.parametrize("kind", ["forward", "forward_block", "dgrad"])
 def test_fp8_bounds_cover_the_emulated_device(kind):
-    gap = forward_gap if kind == "forward" else dgrad_gap
+    """The block-scaled forward is held to the per-row forward's bound: a
+    flipped code is one E4M3 step of its element whatever the scale's
+    granularity, so the same reasoning gives the same bound."""
+    gap = {"forward": forward_gap, "dgrad": dgrad_gap,
+           "forward_block": lambda *a: forward_gap(*a, block=True)}[kind]
     ratios = []
     for E, n, d, f in SHAPES:
-        tol = fp8_fwd_tol(f) if kind == "forward" else fp8_dgrad_tol(f)
+        tol = fp8_dgrad_tol(f) if kind == "dgrad" else fp8_fwd_tol(f)
         l1_bound = tol.get("l1_rel", 5e-3)
         for s in range(SEEDS):
             mx, l1 = gap(np.random.default_rng(1000 + s), E, n, d, f)
@@ -138,3 +152,30 @@ def test_fp8_bounds_cover_the_emulated_device(kind):
             ratios.append(mx / tol["max_rel"])
     # the bound is tight where flips weigh most, not loose by orders of magnitude
     assert max(ratios) > 0.3, ratios
+
+
+def test_block_scaled_inputs_tell_block_from_row_scales():
+    """The GPU test on block-varied inputs (x's 32-column blocks scaled by 2^s,
+    s in [-10, 10], w13's input columns by 2^-s, w2's blocks by 2^r, r in
+    [-4, 4]) separates a correct block-scaled forward from a per-row one and
+    from block scales applied one block off: both land well outside the FP8
+    forward bound."""
+    rng = np.random.default_rng(7)
+    n, d, f = 64, 384, 512
+    X, w13, w2 = _draw(rng, n, d, f)
+    col = lambda s: np.repeat(s, 32)   # noqa: E731
+    sx = col(np.exp2(rng.integers(-10, 11, d // 32)))
+    X, w13 = X * sx, w13 / sx
+    w2 = w2 * col(np.exp2(rng.integers(-4, 5, f // 32)))
+    ref, _ = O.expert_forward_fp8_block(X, w13, w2, "swiglu")
+    row, _ = O.expert_forward_fp8(X, w13, w2, "swiglu")
+
+    def shifted(m):   # each block decoded with its right neighbour's scale
+        c, e = O.quantize_blocks_fp8(m)
+        return O.dequantize_blocks_fp8(c, np.roll(e, -1, axis=1))
+    pre = shifted(X) @ shifted(w13).T
+    H = O.round_bf16(O.silu(pre[:, :f]) * pre[:, f:])
+    off = shifted(H) @ shifted(w2).T
+    tol = fp8_fwd_tol(f)["max_rel"]
+    assert _rel(row, ref)[0] > 3 * tol
+    assert _rel(off, ref)[0] > 3 * tol

@@ -124,3 +124,68 @@ def test_quantize_both_bit_exact(G, R, C):
     assert (sexp_t.cpu().numpy().reshape(-1) == te).all()
     bad = np.argwhere(codes_t.cpu().numpy().reshape(G * C, R) != tc)
     assert bad.size == 0, f"{len(bad)} transposed codes differ, first {bad[:5].tolist()}"
+
+
+# ------------------------------------------------------------ block scales
+def _block_rows(rows, K, seed):
+    """_rows with every 32-element block scaled by its own power of two in
+    2^-40 .. 2^40, some blocks zeroed and some pushed below the scale range
+    (block maxima under 448 * 2^-127 clip the exponent at -127)."""
+    bits = _rows(rows, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    f = bf16_bits_to_f32(bits)
+    nb = -(-K // 32)
+    sh = rng.integers(-40, 41, (rows, nb)).astype(np.float32)
+    g = np.repeat(np.exp2(sh), 32, axis=1)[:, :K]
+    with np.errstate(over="ignore"):
+        fg = f * g
+    keep = np.isfinite(fg) & (np.abs(fg) < 3e38)
+    f = np.where(keep, fg, f)   # powers of two: exact unless over- or underflow
+    if rows > 8 and nb > 1:
+        f[8, 32:64] = 0.0                                           # one zero block
+        f[8, :32] = rng.standard_normal(min(32, K)).astype(np.float32) * 2.0 ** -124
+    return to_bf16_bits(f)
+
+
+@pytest.mark.parametrize("rows,K", [(9, 16), (11, 48), (12, 208), (10, 4096), (5, 14336),
+                                    (9, 2064), (3, 16400)])
+def test_quantize_blocks_bit_exact(rows, K):
+    """moe_quantize_fp8_blocks equals the oracle's per-block quantization:
+    codes, one e8m0 byte per 32-element block (a partial last block when
+    K % 32 == 16, clipped exponents) and 127 in the padding bytes up to a
+    whole 32-bit word per 128 elements."""
+    import mixture_experts_layer_28_amd as moe
+    print(f"[case] quantize blocks rows={rows} K={K}", flush=True)
+    bits = _block_rows(rows, K, seed=rows * 5 + K)
+    x = _dev_bf16(bits)
+    SB = moe.fp8_block_bytes(K)
+    codes = torch.empty(rows, K, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, SB), 0xEE, dtype=torch.uint8, device="cuda")
+    moe.quantize_fp8_blocks(x, codes, scales)
+    torch.cuda.synchronize()
+    ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
+    nb = ref_e.shape[1]
+    got_s = scales.cpu().numpy().astype(np.int64)
+    assert (got_s[:, :nb] == ref_e + 127).all(), np.argwhere(got_s[:, :nb] != ref_e + 127)[:5]
+    assert (got_s[:, nb:] == 127).all()
+    bad = np.argwhere(codes.cpu().numpy() != ref_c)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+    if rows > 8 and K > 64:
+        assert ref_e[8, 0] == -127 and ref_e[8, 1] == 0   # the clipped and the zero block
+
+
+def test_quantize_blocks_respects_device_row_bound():
+    import mixture_experts_layer_28_amd as moe
+    rows, K = 9, 80
+    bits = _block_rows(rows, K, seed=4)
+    x = _dev_bf16(bits)
+    SB = moe.fp8_block_bytes(K)
+    codes = torch.full((rows, K), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, SB), 0xCD, dtype=torch.uint8, device="cuda")
+    valid = torch.tensor([6], dtype=torch.int32, device="cuda")
+    moe.quantize_fp8_blocks(x, codes, scales, valid_rows=valid)
+    torch.cuda.synchronize()
+    ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy().astype(np.int64)
+    assert (got_c[:6] == ref_c[:6]).all() and (got_s[:6, :3] == ref_e[:6] + 127).all()
+    assert (got_c[6:] == 0xAB).all() and (got_s[6:] == 0xCD).all()

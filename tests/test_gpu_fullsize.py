@@ -9,6 +9,8 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
                     update), one shared expert, SwiGLU f=2048
   mixtral_fp8_bf16  the Mixtral-like layer with FP8 (E4M3) forward GEMMs
   mixtral_fp8_dgrad_bf16  the same with FP8 data-gradient GEMMs as well
+  mixtral_fp8b_bf16 the Mixtral-like layer with block-scaled FP8 forward GEMMs
+                    (one scale per 32 elements along K)
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -118,9 +120,15 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     # FP8 forward: per-row quantization, so single rows and weight-row subsets
     # quantize exactly as in the whole GEMM; each expert's weights are
     # quantized once (w13d, w2d) and sliced like the bf16 ones
+    # (block scales: the same holds, blocks run along a row)
+    blk = w.fp8 and w.fp8_scale == "block"
+
     def wq(m):
-        return O.quantize_weights_fp8(m) if w.fp8 else m
-    efwd = O.expert_forward_fp8_wq if w.fp8 else O.expert_forward
+        if not w.fp8:
+            return m
+        return O.quantize_weights_fp8_block(m) if blk else O.quantize_weights_fp8(m)
+    efwd = (O.expert_forward_fp8_block_wq if blk else O.expert_forward_fp8_wq) if w.fp8 \
+        else O.expert_forward
     # FP8 data gradients: the weights quantized per input channel (rows of the
     # transpose), once per expert; any subset of those rows quantizes the same
     # way, and a token row's dO and dpre are quantized on their own.
@@ -240,9 +248,11 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
                                   "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16",
-                                  "mixtral_fp8_dgrad_bf16"])
+                                  "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16"])
 def test_fullsize_sampled(name):
     w = WORKLOADS[name]
     # the oracle's FP8 backward quantizes each sampled expert's weights both
-    # ways (about 45 s per Mixtral-like expert on the host): two experts
-    check_sampled(w, expert_subset=(2, 5) if w.fp8_bwd else None)
+    # ways (about 45 s per Mixtral-like expert on the host), and its block
+    # quantizer walks the weights block by block: two experts
+    slow = w.fp8_bwd or w.fp8_scale == "block"
+    check_sampled(w, expert_subset=(2, 5) if slow else None)

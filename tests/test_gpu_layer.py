@@ -28,6 +28,10 @@ REDUCED = {
     # FP8 forward GEMMs (routed only; routed + shared with sigmoid scoring)
     "mixtral_fp8_small": WORKLOADS["mixtral_fp8_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True),
+    # FP8 forward GEMMs with one scale per 32 elements along K
+    "mixtral_fp8b_small": WORKLOADS["mixtral_fp8b_bf16"].replace(T=1536, d=512, f=768),
+    "dsv3_fp8b_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
+                                                      fp8_scale="block"),
     # FP8 forward and FP8 data gradients (weight gradients bf16)
     "mixtral_fp8_dgrad_small": WORKLOADS["mixtral_fp8_dgrad_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_dgrad_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
@@ -87,6 +91,18 @@ EDGE = {
                                              n_shared=1, fp8=True, fp8_bwd=True),
     "fp8_dgrad_only": Workload("dg8", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
                                fp8_bwd=True),
+    # block-scaled FP8 forward: K tails with a partial last block and padding
+    # bytes (d = 144: blocks 0-4, the last of 16; f = 208: blocks 0-6, the last
+    # of 16), whole ring trips, no routed rows, and FP8 data gradients after it
+    "ragged_fp8b_gelu_shared": Workload("ragged8b", T=1000, d=144, E=6, k=3, f=208, act="gelu",
+                                        score="sigmoid", n_shared=1, sel_bias=True, fp8=True,
+                                        fp8_scale="block"),
+    "ring_whole_trips_fp8b": Workload("ring5f8b", T=700, d=320, E=4, k=2, f=640, fp8=True,
+                                      fp8_scale="block"),
+    "fp8b_all_dropped_shared": Workload("drop8b", T=512, d=256, E=8, k=2, f=256, cf=0.0,
+                                        n_shared=1, fp8=True, fp8_scale="block"),
+    "fp8b_fwd_fp8_dgrad": Workload("f8bd", T=600, d=256, E=4, k=2, f=384, fp8=True,
+                                   fp8_bwd=True, fp8_scale="block"),
 }
 
 
@@ -111,6 +127,30 @@ def test_layer_edge_cases(name):
         off = L.offsets.cpu().numpy()
         assert list(np.diff(off)) == [0, 0, 175, 0]
         assert (L.token_of[:175].cpu().numpy() == np.arange(175)).all()
+
+
+def test_fp8_block_scales_follow_the_blocks():
+    """Inputs whose 32-column blocks span many binades: x's blocks scaled by
+    2^s_b, s_b in [-10, 10], with the matching input columns of w13 and of
+    the router weight scaled by 2^-s_b (products and router logits are
+    unchanged), and w2's blocks by 2^r_b, r_b in [-4, 4]. Each block's scale
+    then differs from its neighbours', so a scale applied to the wrong block,
+    or one scale per row, misses the oracle's block-scaled result by far more
+    than the FP8 bound (test_fp8_tolerance.py shows both on the CPU)."""
+    from moe_inputs import bf16_bits_to_f32, to_bf16_bits
+    w = WORKLOADS["mixtral_fp8b_bf16"].replace(T=768, d=384, f=512, seed=5)
+    print(f"[case] fp8 block scales {w}", flush=True)
+    g = gen_all(w)
+    rng = np.random.default_rng(11)
+    sx = np.exp2(rng.integers(-10, 11, w.d // 32)).astype(np.float32)
+    sw = np.exp2(rng.integers(-4, 5, w.f // 32)).astype(np.float32)
+    col = lambda s: np.repeat(s, 32)   # noqa: E731
+    g["x"] = to_bf16_bits(bf16_bits_to_f32(g["x"]) * col(sx))
+    g["w13"] = to_bf16_bits(bf16_bits_to_f32(g["w13"]) / col(sx))
+    g["w_r"] = (g["w_r"] / col(sx)).astype(np.float32)
+    g["w2"] = to_bf16_bits(bf16_bits_to_f32(g["w2"]) * col(sw))
+    rep, flips, L, dev = run_and_compare(w, g)
+    print(rep, flush=True)
 
 
 # finegrained_small: many small groups; mixtral_small: every tile of the
