@@ -268,39 +268,49 @@ int moe_grouped_ffn_fwd_fp8(const moe_desc* desc, const void* xq_perm, const int
  *   e[i][b] = clip(smallest integer e with max over the block |src| <= 448 * 2^e,
  *                  -127, 127) (0 for an all-zero block),
  *   codes[i][k] = E4M3 nearest (ties to even) of src[i][k] * 2^-e[i][k/32],
- *   scales[i * SB + b] = e[i][b] + 127 (one byte, the e8m0 encoding),
- *   SB = 4 * ceil(K / 128) bytes per row; bytes for blocks at or past K
- *   (the padding to a 128-element step) hold 127 (a scale of 1).
+ *   and the byte e[i][b] + 127 (the e8m0 encoding) in the scales.
+ * Scale layout: the bytes of blocks 4w .. 4w+3 of row i form 32-bit word w
+ * (low byte first; w < KW = ceil(K / 128); bytes of blocks at or past K
+ * hold 127, a scale of 1), and the words are 32-row interleaved: word w of
+ * row i is word (i / 32 * KW + w) * 32 + i % 32 of the array, so one 128-k
+ * step of 32 consecutive rows is one 128-byte line. The array holds
+ * MOE_FP8_BLOCK_SCALE_BYTES(rows, K) = 128 * KW * ceil(rows / 32) bytes; the
+ * words of the padding rows of the last group of 32 are left untouched.
  * A last block shorter than 32 (K % 32 == 16) takes its max over what is
  * there. The codes and bytes are a bit-exact function of the input; inputs
  * must be finite. No desc: a plain matrix operation.
  *   src        [rows, K] bf16, row stride ld_src elements (multiple of 8)   in
  *   valid_rows device int32 or NULL: rows >= *valid_rows are left untouched in
  *   codes      [rows, K] uint8, row stride ld_codes bytes (multiple of 16)  out
- *   scales     [rows, SB] uint8, contiguous                                 out
- * K must be a positive multiple of 16; rows < 2^31.
+ *   scales     MOE_FP8_BLOCK_SCALE_BYTES(rows, K) bytes, layout above       out
+ * K must be a positive multiple of 16; rows < 2^31; the scale array must
+ * stay under 2^31 words.
  */
+#define MOE_FP8_BLOCK_SCALE_BYTES(rows, K) \
+  ((size_t)128 * (size_t)(((K) + 127) / 128) * (size_t)(((rows) + 31) / 32))
 int moe_quantize_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                             const int32_t* valid_rows, void* codes, int64_t ld_codes,
                             uint8_t* scales, void* stream);
 
 /* moe_grouped_ffn_fwd_fp8b: moe_grouped_ffn_fwd_fp8 with block scales
- * (moe_quantize_fp8_blocks codes and bytes) in place of per-row exponents.
- * Each output element is sum over blocks b of
+ * (moe_quantize_fp8_blocks codes and scale arrays) in place of per-row
+ * exponents. Each output element is the sum over blocks b of
  * 2^(e_row[b] + e_weight_row[b]) * sum_{k in b} e4m3 * e4m3, accumulated in
  * float32 (the block-scaled MFMA applies both scales to each 32-k product).
  * H is quantized with block scales into the workspace between the GEMMs.
- * desc->dtype must be MOE_BF16; d and f multiples of 16.
- *   xq_perm [T*k, d] uint8, bx_perm [T*k, SB(d)] uint8                    in
- *   xq [T, d] uint8, bx [T, SB(d)] uint8: the shared expert's x           in (or NULL)
- *   w13q [E, P, d] uint8, b13 [E, P, SB(d)] uint8                         in
- *   w2q [E, d, f] uint8, b2 [E, d, SB(f)] uint8                           in
- *   sw13q, sb13, sw2q, sb2: the shared expert's, or NULL                  in
+ * Weight scale arrays are those of the [E * rows, K] matrix (expert e's row
+ * n is matrix row e * rows + n). desc->dtype must be MOE_BF16; d and f
+ * multiples of 16. SB(r, K) = MOE_FP8_BLOCK_SCALE_BYTES(r, K).
+ *   xq_perm [T*k, d] uint8, bx_perm SB(T*k, d) bytes                      in
+ *   xq [T, d] uint8, bx SB(T, d) bytes: the shared expert's x             in (or NULL)
+ *   w13q [E, P, d] uint8, b13 SB(E*P, d) bytes                            in
+ *   w2q [E, d, f] uint8, b2 SB(E*d, f) bytes                              in
+ *   sw13q, sb13 (SB(P, d)), sw2q, sb2 (SB(d, f)): the shared expert's,
+ *     or NULL                                                             in
  *   save_pre, save_h, save_pre_s, save_h_s, out, out_shared: as in
  *     moe_grouped_ffn_fwd (bf16)                                          out
  *   ws         MOE_OP_FFN_FWD_FP8B bytes (H codes and block scales, then
  *              the down-projection's split-K partials)                 scratch
- * SB(K) = 4 * ceil(K / 128).
  */
 int moe_grouped_ffn_fwd_fp8b(const moe_desc* desc, const void* xq_perm, const uint8_t* bx_perm,
                              const int32_t* offsets, const void* xq, const uint8_t* bx,

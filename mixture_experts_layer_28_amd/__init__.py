@@ -247,19 +247,21 @@ def grouped_ffn_fwd_fp8(desc, xq_perm, sx_perm, offsets, xq, sx, w13q, s13, w2q,
         _stream(stream)))
 
 
-def fp8_block_bytes(K: int) -> int:
-    """Bytes of block scales per row of K elements: one byte per 32 elements,
-    padded to a 32-bit word per 128."""
-    return 4 * ((K + 127) // 128)
+def fp8_block_scale_bytes(rows: int, K: int) -> int:
+    """Bytes of the block scales of a rows x K matrix: one byte per 32
+    elements, four to a 32-bit word per 128, words 32-row interleaved (word w
+    of row r at word (r // 32 * ceil(K / 128) + w) * 32 + r % 32)."""
+    return 128 * ((K + 127) // 128) * ((rows + 31) // 32)
 
 
 def quantize_fp8_blocks(src, codes, scales, valid_rows=None, stream=None):
-    """Block-scaled E4M3 quantization of a bf16 tensor [..., K] into codes
-    (uint8, same shape) and e8m0 scale bytes (uint8, [..., fp8_block_bytes(K)])."""
+    """Block-scaled E4M3 quantization of a bf16 tensor [..., K] (its rows)
+    into codes (uint8, same shape) and e8m0 scale bytes (a uint8 tensor of
+    fp8_block_scale_bytes(rows, K) elements, interleaved as described there)."""
     K = src.shape[-1]
     rows = src.numel() // K if K else 0
-    if codes.shape != src.shape or scales.numel() != rows * fp8_block_bytes(K):
-        raise ValueError("codes must match src's shape and scales hold fp8_block_bytes(K) per row")
+    if codes.shape != src.shape or scales.numel() != fp8_block_scale_bytes(rows, K):
+        raise ValueError("codes must match src's shape and scales hold fp8_block_scale_bytes(rows, K)")
     _check("moe_quantize_fp8_blocks", lib().moe_quantize_fp8_blocks(
         _p(src), rows, K, K, _p(valid_rows), _p(codes), K, _p(scales), _stream(stream)))
 

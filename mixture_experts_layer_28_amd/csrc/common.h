@@ -162,9 +162,11 @@ struct GemmArgs {
   int k_splits;             // split-K partitions (fp32 GEMM, RAG_NONE only); 1 = none
   // FP8 GEMM: power-of-two scale exponents, per A row (indexed like A's rows)
   // and per weight row (group g at b_sexp + g * b_sexp_gstride). With
-  // blk_scales, both point at block scales instead: per row, one 8-bit
-  // exponent byte (e + 127) per 32 elements along K, 4 * ceil(K / 128) bytes
-  // per row (one 32-bit word per 128-k step), and b_sexp_gstride counts words.
+  // blk_scales, both point at block scales instead: one 8-bit exponent byte
+  // (e + 127) per 32 elements along K, four to a 32-bit word per 128-k step,
+  // words 32-row interleaved (word w of matrix row r at (r / 32 * ceil(K /
+  // 128) + w) * 32 + r % 32); A's rows are indexed like A's, group g's weight
+  // rows start at matrix row g * b_sexp_gstride.
   const int32_t* a_sexp;
   const int32_t* b_sexp;
   int64_t b_sexp_gstride;

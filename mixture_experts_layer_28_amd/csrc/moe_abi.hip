@@ -261,9 +261,17 @@ int enable_tail(GemmArgs& q, void* tw, hipStream_t s) {
   return MOE_OK;
 }
 
-// bytes of block scales per row of K elements: one byte per 32, padded to a
-// 32-bit word per 128
-size_t blk_scale_bytes(int64_t K) { return (size_t)4 * ((K + 127) / 128); }
+// bytes of the block scales of a rows x K matrix: one byte per 32 elements,
+// four to a 32-bit word per 128, words 32-row interleaved (rows padded to a
+// multiple of 32)
+size_t blk_scale_bytes(int64_t rows, int64_t K) {
+  return (size_t)128 * ((K + 127) / 128) * ((rows + 31) / 32);
+}
+
+// the GEMM addresses block-scale words with 32-bit offsets
+bool blk_scale_words_fit(int64_t rows, int64_t K) {
+  return blk_scale_bytes(rows, K) / 4 < ((size_t)1 << 31);
+}
 
 size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
@@ -304,9 +312,8 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
     case MOE_OP_FFN_FWD_FP8B: {
       // FP8 codes and block scales of H between the two GEMMs, then the
       // down-projection's split-K tail
-      const size_t sb = blk_scale_bytes(d->f);
-      size_t b = align256((size_t)T * d->k * d->f) + align256((size_t)T * d->k * sb);
-      if (d->n_shared) b += align256((size_t)T * d->f) + align256((size_t)T * sb);
+      size_t b = align256((size_t)T * d->k * d->f) + align256(blk_scale_bytes(T * d->k, d->f));
+      if (d->n_shared) b += align256((size_t)T * d->f) + align256(blk_scale_bytes(T, d->f));
       return b + tail_ws_bytes(kTailCusMax);
     }
   }
@@ -752,14 +759,19 @@ int ffn_fwd_fp8_impl(bool blk, const moe_desc* desc, const void* xq_perm, const 
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
   const int epi1 = desc->act == MOE_SWIGLU ? EPI_SWIGLU_FWD : EPI_GELU_FWD;
-  // H codes and its scales (4 bytes per row, or blk_scale_bytes(f)) between
-  // the GEMMs; scale row strides in 32-bit words for the block scales
-  const size_t hsb = blk ? blk_scale_bytes(f) : 4;
-  const int64_t kwd = (d + 127) / 128, kwf = (f + 127) / 128;
+  if (blk) {
+    const int64_t R = T * desc->k;
+    if (!blk_scale_words_fit(R, d) || !blk_scale_words_fit(R, f) ||
+        !blk_scale_words_fit(desc->E * P, d) || !blk_scale_words_fit(desc->E * d, f))
+      return fail(MOE_ERR_UNSUPPORTED, "block scales of this layer exceed 2^31 words");
+  }
+  // H codes and its scales (an int32 per row, or the block scales) between
+  // the GEMMs
   char* w = (char*)ws;
   uint8_t* hq = (uint8_t*)w;
   void* hs = w + align256((size_t)T * desc->k * f);
-  uint8_t* hq_s = (uint8_t*)((char*)hs + align256((size_t)T * desc->k * hsb));
+  uint8_t* hq_s = (uint8_t*)((char*)hs + align256(blk ? blk_scale_bytes(T * desc->k, f)
+                                                      : (size_t)T * desc->k * 4));
   void* hs_s = desc->n_shared ? (void*)((char*)hq_s + align256((size_t)T * f)) : nullptr;
   char* tail_w = w + ws_bytes_for(desc, op) - tail_ws_bytes(kTailCusMax);
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
@@ -769,7 +781,7 @@ int ffn_fwd_fp8_impl(bool blk, const moe_desc* desc, const void* xq_perm, const 
     p.b = opnd(shared ? sw13q : w13q, d, P * d, 0);
     p.a_sexp = (const int32_t*)(shared ? sx : sx_perm);
     p.b_sexp = (const int32_t*)(shared ? ss13 : s13);
-    p.b_sexp_gstride = blk ? P * kwd : P;
+    p.b_sexp_gstride = P;
     p.blk_scales = blk;
     p.c = shared ? save_h_s : save_h;
     p.ldc = f;
@@ -806,7 +818,7 @@ int ffn_fwd_fp8_impl(bool blk, const moe_desc* desc, const void* xq_perm, const 
     q.b = opnd(shared ? sw2q : w2q, f, d * f, 0);
     q.a_sexp = (const int32_t*)qs;
     q.b_sexp = (const int32_t*)(shared ? ss2 : s2);
-    q.b_sexp_gstride = blk ? d * kwf : d;
+    q.b_sexp_gstride = d;
     q.blk_scales = blk;
     q.c = shared ? out_shared : out;
     q.ldc = d;
@@ -871,6 +883,9 @@ int moe_quantize_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld
   MOE_TRY(need(scales, "scales"));
   if (valid_rows && (reinterpret_cast<uintptr_t>(valid_rows) & 3))
     return fail(MOE_ERR_INVALID_ARG, "valid_rows is not 4-byte aligned");
+  if (!blk_scale_words_fit(rows, K))
+    return fail(MOE_ERR_INVALID_ARG, "block scales of %lld x %lld exceed 2^31 words", (long long)rows,
+                (long long)K);
   if (rows == 0) return MOE_OK;
   Scope sc(K_QUANT_FP8, (hipStream_t)stream);
   return hip_check(launch_quant_fp8_blocks(src, rows, K, ld_src, valid_rows, codes, ld_codes, scales,

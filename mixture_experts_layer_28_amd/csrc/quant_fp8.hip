@@ -97,18 +97,21 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
 // ---- block scales: one exponent per 32 elements along K
 // Row r, block b (elements 32b .. 32b+31, the last one partial when K is not
 // a multiple of 32): e = the per-row rule on the block's maximum, clipped to
-// [-127, 127]; codes as above; the exponent is stored as the byte e + 127 at
-// scales[r * sld + b], sld = 4 * ceil(K / 128) (a 32-bit word per 128 k,
-// padding blocks past K hold 127). One thread per 8 elements (a 16-byte
-// chunk); the four threads of a block agree on its maximum through two
-// lane swaps. Grid: x = rows, y = chunks of 256 threads over sld * 4 chunks.
+// [-127, 127]; codes as above; the exponent is stored as the byte e + 127.
+// Layout (32-row interleaved): the four bytes of blocks 4w .. 4w+3 of a row
+// form 32-bit word w (w < KW = ceil(K / 128); blocks past K hold 127), and
+// word w of rows 32g .. 32g+31 sits at words (g * KW + w) * 32 + (r & 31), so
+// the GEMM reads one k-step's words of 32 consecutive rows as one 128-byte
+// line. One thread per 8 elements (a 16-byte chunk); the four threads of a
+// block agree on its maximum through two lane swaps. Grid: x = rows,
+// y = chunks of 256 threads over 16 * KW chunks per row.
 __global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t K, int64_t ld_src, const int32_t* __restrict__ valid_rows,
-    uint8_t* __restrict__ codes, int64_t ld_q, uint8_t* __restrict__ scales, int64_t sld) {
+    uint8_t* __restrict__ codes, int64_t ld_q, uint8_t* __restrict__ scales, int64_t KW) {
   const int64_t row = blockIdx.x;
   if (valid_rows && row >= (int64_t)*valid_rows) return;
   const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;   // chunk of 8 elements
-  if (c >= sld * 4) return;   // a whole group of four threads is in or out
+  if (c >= KW * 16) return;   // a whole group of four threads is in or out
   const int64_t nch = K / 8;
   const uint4 v = c < nch ? *reinterpret_cast<const uint4*>(src + row * ld_src + 8 * c) : make_uint4(0, 0, 0, 0);
   uint32_t m = absmax8(v, 0);
@@ -123,7 +126,10 @@ __global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
   int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
   e = e < -127 ? -127 : (e > 127 ? 127 : e);
   if (c < nch) *reinterpret_cast<uint2*>(codes + row * ld_q + 8 * c) = to_e4m3(v, e);
-  if ((c & 3) == 0) scales[row * sld + c / 4] = (uint8_t)(e + 127);
+  if ((c & 3) == 0) {
+    const int64_t b = c >> 2;   // block
+    scales[(((row >> 5) * KW + (b >> 2)) * 32 + (row & 31)) * 4 + (b & 3)] = (uint8_t)(e + 127);
+  }
 }
 
 // ---- per-column quantization into the transpose
@@ -403,16 +409,17 @@ hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld
   return hipGetLastError();
 }
 
-// Block-scaled rows: codes [rows, K] (row stride ld_q) and scales
-// [rows, 4 * ceil(K / 128)] bytes. K % 8 == 0, 16-byte aligned source rows.
+// Block-scaled rows: codes [rows, K] (row stride ld_q) and 32-row
+// interleaved scale words (ceil(rows / 32) * 32 * ceil(K / 128) words).
+// K % 8 == 0, 16-byte aligned source rows.
 hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                                    const int32_t* valid_rows, void* codes, int64_t ld_q,
                                    uint8_t* scales, hipStream_t st) {
   if (rows == 0 || K == 0) return hipSuccess;
-  const int64_t sld = 4 * ((K + 127) / 128);
-  const dim3 grid((unsigned)rows, (unsigned)((sld * 4 + 255) / 256));
+  const int64_t KW = (K + 127) / 128;
+  const dim3 grid((unsigned)rows, (unsigned)((KW * 16 + 255) / 256));
   hipLaunchKernelGGL(quant_blocks_fp8_kernel, grid, dim3(256), 0, st, (const bf16_t*)src, K, ld_src,
-                     valid_rows, (uint8_t*)codes, ld_q, scales, sld);
+                     valid_rows, (uint8_t*)codes, ld_q, scales, KW);
   return hipGetLastError();
 }
 

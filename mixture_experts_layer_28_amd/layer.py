@@ -11,7 +11,7 @@ import torch
 
 from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
                MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats,
-               bias_update, combine, combine_bwd, fp8_block_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8,
+               bias_update, combine, combine_bwd, fp8_block_scale_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8,
                grouped_ffn_fwd, grouped_ffn_fwd_fp8, grouped_ffn_fwd_fp8b, make_desc, permute,
                permute_bwd, quantize_fp8, quantize_fp8_blocks, quantize_fp8_both,
                quantize_fp8_both_ws, quantize_fp8_t, route, route_bwd, workspace_size)
@@ -110,19 +110,21 @@ class MoELayer:
         self.dX = z(T, d)
         if fp8_fwd:
             u8 = torch.uint8
-            # per-row exponents (int32), or block-scale bytes per row
+            # per-row exponents (int32), or the block-scale array of the
+            # [rows, K] matrix (bytes)
             if self.fp8_block:
-                sd, sf = (fp8_block_bytes(d),), (fp8_block_bytes(f),)
-                st = u8
+                def sc(rows, K):
+                    return z(fp8_block_scale_bytes(rows, K), dtype=u8)
             else:
-                sd, sf, st = (), (), i32
-            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), z(R, *sd, dtype=st)
-            self.w13q, self.s13 = z(E, P, d, dtype=u8), z(E, P, *sd, dtype=st)
-            self.w2q, self.s2 = z(E, d, f, dtype=u8), z(E, d, *sf, dtype=st)
+                def sc(rows, K):
+                    return z(rows, dtype=i32)
+            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), sc(R, d)
+            self.w13q, self.s13 = z(E, P, d, dtype=u8), sc(E * P, d)
+            self.w2q, self.s2 = z(E, d, f, dtype=u8), sc(E * d, f)
             sh = bool(n_shared)
-            self.xq, self.sx = (z(T, d, dtype=u8), z(T, *sd, dtype=st)) if sh else (None, None)
-            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), z(1, P, *sd, dtype=st)) if sh else (None, None)
-            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), z(1, d, *sf, dtype=st)) if sh else (None, None)
+            self.xq, self.sx = (z(T, d, dtype=u8), sc(T, d)) if sh else (None, None)
+            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), sc(P, d)) if sh else (None, None)
+            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), sc(d, f)) if sh else (None, None)
         if fp8_bwd:
             u8 = torch.uint8
             sh = bool(n_shared)

@@ -282,7 +282,9 @@ def test_fp8_block_quantize_validation():
                                          None)
     for bad in (dict(K=8), dict(K=72), dict(ld_src=64), dict(ld_src=84), dict(ld_q=88),
                 dict(rows=-1), dict(rows=1 << 31), dict(src=0), dict(codes=FAKE + 8),
-                dict(sc=0), dict(sc=FAKE + 4), dict(valid=FAKE + 2)):
+                dict(sc=0), dict(sc=FAKE + 4), dict(valid=FAKE + 2),
+                # 2^30 rows x 2 words: the scale array would reach 2^31 words
+                dict(rows=1 << 30, K=256, ld_src=256, ld_q=256)):
         assert call(**bad) == 1, bad
         assert L.moe_last_error().decode()
     assert call(rows=0) == 0
@@ -298,13 +300,14 @@ def test_fp8_block_forward_validation():
     assert call(_desc(dtype="f32")) == 2
     assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
     assert call(_desc(T=0)) == 0
-    # the workspace holds H's codes and block scales (4 bytes per 128 of f)
+    # the workspace holds H's codes and block scales (128 bytes per 128 of f
+    # and 32 rows: 4 groups of 32 rows x 2 words here)
     d = _desc(T=64, k=2, f=256)
     need = ctypes.c_size_t()
     assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_FWD_FP8B, ctypes.byref(need)) == 0
     row = ctypes.c_size_t()
     assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_FWD_FP8, ctypes.byref(row)) == 0
-    assert need.value - row.value == 256 * ((128 * 8 + 255) // 256) - 256 * ((128 * 4 + 255) // 256)
+    assert need.value - row.value == 128 * 2 * 4 - 128 * 4
     assert call(d, ws_bytes=need.value - 1) == 3
     # a NULL or misaligned block-scale array is rejected
     for bad_v in (None, P(FAKE + 4)):

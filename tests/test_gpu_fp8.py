@@ -147,8 +147,20 @@ def _block_rows(rows, K, seed):
     return to_bf16_bits(f)
 
 
+def _block_bytes(buf, rows, K):
+    """[rows, 4 * ceil(K / 128)] bytes (row, block) out of the 32-row
+    interleaved scale array: word w of row r is word (r // 32 * KW + w) * 32
+    + r % 32, its byte j the scale of block 4w + j."""
+    KW = -(-K // 128)
+    words = np.asarray(buf, dtype=np.uint8).view("<u4")
+    r = np.arange(rows)[:, None]
+    w = np.arange(KW)[None, :]
+    sel = words[(r // 32 * KW + w) * 32 + r % 32]                      # [rows, KW]
+    return ((sel[:, :, None] >> (8 * np.arange(4, dtype=np.uint32))) & 0xFF).reshape(rows, 4 * KW)
+
+
 @pytest.mark.parametrize("rows,K", [(9, 16), (11, 48), (12, 208), (10, 4096), (5, 14336),
-                                    (9, 2064), (3, 16400)])
+                                    (9, 2064), (3, 16400), (70, 272)])
 def test_quantize_blocks_bit_exact(rows, K):
     """moe_quantize_fp8_blocks equals the oracle's per-block quantization:
     codes, one e8m0 byte per 32-element block (a partial last block when
@@ -158,16 +170,23 @@ def test_quantize_blocks_bit_exact(rows, K):
     print(f"[case] quantize blocks rows={rows} K={K}", flush=True)
     bits = _block_rows(rows, K, seed=rows * 5 + K)
     x = _dev_bf16(bits)
-    SB = moe.fp8_block_bytes(K)
+    SB = moe.fp8_block_scale_bytes(rows, K)
+    assert SB == 128 * (-(-K // 128)) * (-(-rows // 32))
     codes = torch.empty(rows, K, dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows, SB), 0xEE, dtype=torch.uint8, device="cuda")
+    scales = torch.full((SB,), 0xEE, dtype=torch.uint8, device="cuda")
     moe.quantize_fp8_blocks(x, codes, scales)
     torch.cuda.synchronize()
     ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
     nb = ref_e.shape[1]
-    got_s = scales.cpu().numpy().astype(np.int64)
+    raw = scales.cpu().numpy()
+    got_s = _block_bytes(raw, rows, K).astype(np.int64)
     assert (got_s[:, :nb] == ref_e + 127).all(), np.argwhere(got_s[:, :nb] != ref_e + 127)[:5]
     assert (got_s[:, nb:] == 127).all()
+    # the padding rows of the last group of 32 are not written
+    KW = -(-K // 128)
+    words = raw.view("<u4").reshape(-1, KW, 32)
+    pad = words[-1, :, rows % 32:] if rows % 32 else words[:0]
+    assert (pad == 0xEEEEEEEE).all()
     bad = np.argwhere(codes.cpu().numpy() != ref_c)
     assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
     if rows > 8 and K > 64:
@@ -179,13 +198,13 @@ def test_quantize_blocks_respects_device_row_bound():
     rows, K = 9, 80
     bits = _block_rows(rows, K, seed=4)
     x = _dev_bf16(bits)
-    SB = moe.fp8_block_bytes(K)
+    SB = moe.fp8_block_scale_bytes(rows, K)
     codes = torch.full((rows, K), 0xAB, dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows, SB), 0xCD, dtype=torch.uint8, device="cuda")
+    scales = torch.full((SB,), 0xCD, dtype=torch.uint8, device="cuda")
     valid = torch.tensor([6], dtype=torch.int32, device="cuda")
     moe.quantize_fp8_blocks(x, codes, scales, valid_rows=valid)
     torch.cuda.synchronize()
     ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
-    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy().astype(np.int64)
+    got_c, got_s = codes.cpu().numpy(), _block_bytes(scales.cpu().numpy(), rows, K).astype(np.int64)
     assert (got_c[:6] == ref_c[:6]).all() and (got_s[:6, :3] == ref_e[:6] + 127).all()
     assert (got_c[6:] == 0xAB).all() and (got_s[6:] == 0xCD).all()
