@@ -451,6 +451,26 @@ def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act):
     return dX, dpre.T @ X, dO.T @ H, dpre
 
 
+# ------------------------------------------------ FP8 weight gradients
+# [Megatron10x] §5.2 trains in FP8 mixed precision; the weight-gradient GEMMs
+# reduce over an expert's tokens, so their operands are read along the token
+# axis. Reading taken: both operands of dW2 = dO^T H and dW13 = dpre^T X are
+# quantized per column with one power-of-two scale per block of 32 consecutive
+# tokens of the expert (blocks start at the expert's first row; the last one
+# may be partial), by the block rule of quantize_blocks_fp8 applied to the
+# transposed operands; the values quantized are the stored bf16 ones.
+def expert_wgrad_fp8(X, H, dO, dpre):
+    """(dW13, dW2) of one expert with FP8 block-scaled operands along the
+    token axis: X [n, d], H [n, f], dO [n, d], dpre [n, 2f|f].
+      dW2  = deq(qb(bf16 dO ^T)) @ deq(qb(bf16 H ^T))^T
+      dW13 = deq(qb(bf16 dpre ^T)) @ deq(qb(X ^T))^T
+    qb: quantize_blocks_fp8 of each row of the transposed operand (a column of
+    the token-major one), blocks of 32 tokens."""
+    def qt(m):
+        return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))
+    return qt(dpre) @ qt(X).T, qt(dO) @ qt(H).T
+
+
 def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None, fp8=False):
     """Grouped GEMM of [Recipe] §4.2: the same result as running every
     expert's GEMMs on its own contiguous rows. Optional shared experts
@@ -480,10 +500,12 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
 
 
 def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=None,
-                         sw2=None, dY=None, fp8_dgrad=False):
+                         sw2=None, dY=None, fp8_dgrad=False, fp8_wgrad=False):
     """Backward of grouped_ffn_forward: per-expert dgrad and wgrad.
     The shared expert's upstream gradient is dY itself (gate 1).
-    fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq)."""
+    fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq).
+    fp8_wgrad: the weight gradients on FP8 operands (expert_wgrad_fp8, on
+    the expert's own dpre)."""
     E = w13.shape[0]
     dX_perm = np.zeros_like(x_perm)
     dw13 = np.zeros_like(w13)
@@ -492,9 +514,15 @@ def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=
 
     def bwd(X, w13e, w2e, sv, g):
         if fp8_dgrad:
-            return expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),
-                                          quantize_weights_fp8_t(w13e), sv, g, act)
-        return expert_backward(X, w13e, w2e, sv, g, act)
+            out = expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),
+                                         quantize_weights_fp8_t(w13e), sv, g, act)
+        else:
+            out = expert_backward(X, w13e, w2e, sv, g, act)
+        if fp8_wgrad:
+            dx, _, _, dp = out
+            g13, g2 = expert_wgrad_fp8(X, sv["H"], g, dp)
+            out = (dx, g13, g2, dp)
+        return out
 
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -663,13 +691,13 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
 
 
 def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
-                   sw13=None, sw2=None, z_coef=0.0, tau=None, fp8_dgrad=False):
+                   sw13=None, sw2=None, z_coef=0.0, tau=None, fp8_dgrad=False, fp8_wgrad=False):
     """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
     router bwd, un-permute."""
     r, p = fwd["router"], fwd["perm"]
     dgate, dO = combine_backward(dY, fwd["O"], r["gates"], p["row_of"])
     g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
-                             sw13, sw2, dY, fp8_dgrad)
+                             sw13, sw2, dY, fp8_dgrad, fp8_wgrad)
     rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
                          aux_coef, fwd["stats"]["y"], z_coef, r["logits"], tau)
     dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])

@@ -154,6 +154,14 @@ MUTANTS = [
      "FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -127, 127",
      "FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -1000, 1000",
      [(P.test_fp8_block_exponent_is_clipped_to_the_scale_range,)]),
+    ("FP8 weight gradients: blocks along each token row instead of along the token axis",
+     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))",
+     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)))).T",
+     [(P.test_expert_wgrad_fp8_brute_force,), (P.test_fp8_wgrad_exact_on_block_exact_columns,)]),
+    ("FP8 weight gradients quantize dpre without its bf16 rounding",
+     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))",
+     "return dequantize_blocks_fp8(*quantize_blocks_fp8(np.asarray(m, dtype=np.float64).T))",
+     [(P.test_expert_wgrad_fp8_brute_force,)]),
 ]
 
 

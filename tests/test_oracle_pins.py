@@ -855,3 +855,83 @@ def test_expert_forward_fp8_block_brute_force(act):
     got, saved = O.expert_forward_fp8_block(X, w13, w2, act)
     np.testing.assert_allclose(got, out, rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(saved["H"], H, rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------------ FP8 weight gradients
+def test_expert_wgrad_fp8_brute_force():
+    """FP8 weight gradients against explicit loops: every column of dO, H,
+    dpre and X quantized by brute force over blocks of 32 tokens (40 tokens:
+    one whole block and a partial one, with the partial block far smaller),
+    after bf16 rounding of the values as stored (dpre here arrives in float64
+    and must be rounded first)."""
+    rng = np.random.default_rng(47)
+    n, d, f = 40, 6, 5
+    P = 2 * f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    H = O.round_bf16(rng.standard_normal((n, f)))
+    dO = O.round_bf16(rng.standard_normal((n, d)))
+    dpre = rng.standard_normal((n, P))                   # not bf16: the function rounds it
+    for m in (X, H, dO, dpre):
+        m[32:] *= 2.0 ** -9
+    Xd, Hd, dOd = (_brute_fp8_blocks(m.T).T for m in (X, H, dO))
+    dpd = _brute_fp8_blocks(O.round_bf16(dpre).T).T
+    dw2 = np.array([[sum(dOd[t, c] * Hd[t, j] for t in range(n)) for j in range(f)] for c in range(d)])
+    dw13 = np.array([[sum(dpd[t, r] * Xd[t, c] for t in range(n)) for c in range(d)] for r in range(P)])
+    g13, g2 = O.expert_wgrad_fp8(X, H, dO, dpre)
+    np.testing.assert_allclose(g2, dw2, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(g13, dw13, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_wgrad_exact_on_block_exact_columns():
+    """Columns whose 32-token blocks are E4M3 values times a power of two of
+    their own (one element of each block in (224, 448] times it, so the
+    block's scale is that power): the FP8 weight gradients equal the exact
+    ones bit for bit. A scale per token row (the plausible mistake) cannot hold
+    these columns, whose powers differ by up to 2^16 within a row."""
+    rng = np.random.default_rng(48)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_decode(codes)
+    mant = vals[(vals >= 1.0) & (vals <= 448.0)]
+    top = mant[mant > 224.0]
+    n, d, f = 72, 4, 3
+
+    def block_exact(cols):
+        m = rng.choice(mant, size=(n, cols))
+        for b0 in range(0, n, 32):
+            r = rng.integers(b0, min(b0 + 32, n), cols)
+            m[r, np.arange(cols)] = rng.choice(top, cols)
+            m[b0:b0 + 32] *= np.exp2(rng.integers(-8, 9, cols))
+        return m * rng.choice([-1.0, 1.0], size=(n, cols))
+    X, H, dO, dpre = block_exact(d), block_exact(f), block_exact(d), block_exact(2 * f)
+    g13, g2 = O.expert_wgrad_fp8(X, H, dO, dpre)
+    assert (g2 == dO.T @ H).all() and (g13 == dpre.T @ X).all()
+    rows = O.dequantize_rows_fp8(*O.quantize_rows_fp8(dO))
+    assert (rows != dO).any()
+
+
+def test_grouped_backward_fp8_wgrad_is_per_expert():
+    """With fp8_wgrad, each expert's weight gradients come from its own rows
+    alone (token blocks restart at its first row): an expert of 40 tiny rows
+    next to one of huge rows keeps the gradients of its own blocks, and the
+    data gradients are untouched."""
+    rng = np.random.default_rng(49)
+    d, f, E = 8, 6, 2
+    n0, n1 = 40, 24
+    x_perm = O.round_bf16(rng.standard_normal((n0 + n1, d)))
+    x_perm[:n0] *= 2.0 ** -20
+    offsets = np.array([0, n0, n0 + n1])
+    w13 = rng.standard_normal((E, 2 * f, d)) / 3
+    w2 = rng.standard_normal((E, d, f)) / 3
+    _, _, saved = O.grouped_ffn_forward(x_perm, offsets, w13, w2, "swiglu")
+    dO = O.round_bf16(rng.standard_normal((n0 + n1, d)))
+    ref = O.grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, "swiglu")
+    got = O.grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, "swiglu", fp8_wgrad=True)
+    np.testing.assert_array_equal(got["dx_perm"], ref["dx_perm"])
+    for e, (lo, hi) in enumerate(((0, n0), (n0, n0 + n1))):
+        g13, g2 = O.expert_wgrad_fp8(x_perm[lo:hi], saved["routed"][e]["H"], dO[lo:hi],
+                                     ref["dpre"][lo:hi])
+        np.testing.assert_array_equal(got["dw13"][e], g13)
+        np.testing.assert_array_equal(got["dw2"][e], g2)
+        # FP8 error of a sum over the expert's rows, relative to its own scale
+        err = np.abs(got["dw13"][e] - ref["dw13"][e]).max() / np.abs(ref["dw13"][e]).max()
+        assert err < 0.1, (e, err)
