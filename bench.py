@@ -115,13 +115,16 @@ def gemm_roofline(w, name, flops, nbytes, avg_ms):
 
 def is_fp8_gemm(w, name):
     """Whether this grouped-GEMM launch runs on E4M3 operands."""
-    return (w.fp8 and "fwd" in name) or (w.fp8_bwd and "dgrad" in name)
+    return ((w.fp8 and "fwd" in name) or (w.fp8_bwd and "dgrad" in name)
+            or (w.fp8_wgrad and "wgrad" in name))
 
 
 def dtype_label(w):
     if w.dtype != "bf16":
         return "f32"
     blk = " (1x32 block scales)" if w.fp8_scale == "block" else ""
+    if w.fp8 and w.fp8_wgrad:
+        return f"fp8-e4m3 fwd{blk}, dgrad and wgrad GEMMs (wgrad: 32-token block scales)"
     if w.fp8 and w.fp8_bwd:
         return f"fp8-e4m3 fwd{blk} and dgrad GEMMs, bf16 wgrad"
     return f"fp8-e4m3 fwd GEMMs{blk}, bf16 bwd" if w.fp8 else "bf16"
@@ -435,9 +438,14 @@ def streamed_oracle_step(w, g, tokens, clock):
 
     def bwd_e(X, w13e, w2e, sv, dO):
         if ws.fp8_bwd:
-            return O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2e),
-                                            O.quantize_weights_fp8_t(w13e), sv, dO, ws.act)
-        return O.expert_backward(X, w13e, w2e, sv, dO, ws.act)
+            out = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2e),
+                                           O.quantize_weights_fp8_t(w13e), sv, dO, ws.act)
+        else:
+            out = O.expert_backward(X, w13e, w2e, sv, dO, ws.act)
+        if ws.fp8_wgrad:
+            g13, g2 = O.expert_wgrad_fp8(X, sv["H"], dO, out[3])
+            out = (out[0], g13, g2, out[3])
+        return out
 
     r = timed(O.router_forward, x, w_r, ws.k, ws.score, lb, sb, gu, ws.gumbel_tau)
     st = timed(O.aux_stats, r["scores"], r["topk_idx"], ws.E)
@@ -539,7 +547,7 @@ def main():
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     layer = MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
-                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale)
+                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale, fp8_wgrad=w.fp8_wgrad)
     for _ in range(args.warmup):
         layer.step(inp)
     torch.cuda.synchronize()
@@ -638,7 +646,7 @@ def main():
         "dtype": dtype_label(w), "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "act": w.act, "score": w.score, "n_shared": w.n_shared,
-                   "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8, "fp8_dgrad": w.fp8_bwd,
+                   "capacity": cap, "kept_rows": A, "fp8_fwd": w.fp8, "fp8_dgrad": w.fp8_bwd, "fp8_wgrad": w.fp8_wgrad,
                    "fp8_scale": w.fp8_scale if w.fp8 else None,
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 1) if gemm_tflops else None,

@@ -92,7 +92,8 @@ typedef enum {
   MOE_OP_ROUTE_BWD = 5,
   MOE_OP_FFN_FWD_FP8 = 6,
   MOE_OP_FFN_BWD_FP8 = 7,
-  MOE_OP_FFN_FWD_FP8B = 8
+  MOE_OP_FFN_FWD_FP8B = 8,
+  MOE_OP_FFN_BWD_FP8W = 9
 } moe_op;
 
 /* ---------------------------------------------------------------- router
@@ -409,6 +410,31 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* moe_grouped_ffn_bwd_fp8w: moe_grouped_ffn_bwd_fp8 with the weight
+ * gradients on FP8 operands as well. [Megatron10x] §5.2 trains in FP8 mixed
+ * precision without naming the GEMMs; the reading taken here quantizes the
+ * operands of dW2 = dO^T H and dW13 = dpre^T X (the stored bf16 values) per
+ * column, with one power-of-two scale per block of 32 consecutive tokens of
+ * each expert (blocks start at the expert's first row, the last may be
+ * partial; the rule of moe_quantize_fp8_blocks along the token axis). The
+ * library writes each operand's transpose in FP8 into the workspace, each
+ * expert's tokens starting on a 128-token step, and runs the block-scaled
+ * GEMM over them: each output element is the sum over token blocks of
+ * 2^(e_a + e_b) * sum e4m3 * e4m3, accumulated in float32, stored in bf16.
+ * Arguments as in moe_grouped_ffn_bwd_fp8.
+ *   ws  MOE_OP_FFN_BWD_FP8W bytes (moe_grouped_ffn_bwd_fp8's layout, then
+ *       the token-axis codes and scales of the weight gradients' operands:
+ *       about (max(d, 2f|f) + max(f, d)) * (T*k + 128 E) bytes)            scratch
+ */
+int moe_grouped_ffn_bwd_fp8w(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w13q_t, const int32_t* s13_t,
+                             const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
+                             const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
+                             const void* save_pre, const void* save_h, const void* save_pre_s,
+                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine: the weighted sum of [Recipe] §2.1/§2.2 (the combine step of

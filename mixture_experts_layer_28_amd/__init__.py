@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
- MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD_FP8B) = range(9)
+ MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD_FP8B,
+ MOE_OP_FFN_BWD_FP8W) = range(10)
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -31,6 +32,7 @@ EXPORTS = (
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
     "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8", "moe_quantize_fp8_both",
     "moe_permute_noalloc", "moe_quantize_fp8_blocks", "moe_grouped_ffn_fwd_fp8b",
+    "moe_grouped_ffn_bwd_fp8w",
 )
 
 
@@ -81,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8_both": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P],
             "moe_grouped_ffn_bwd_fp8": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
+            "moe_grouped_ffn_bwd_fp8w": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
             "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
@@ -316,9 +319,13 @@ def quantize_fp8_both(src, codes, scale_exp, codes_t, scale_exp_t, ws, stream=No
 
 def grouped_ffn_bwd_fp8(desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t, ss13_t,
                         sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy, dx_perm,
-                        dx_shared, dw13, dw2, dsw13, dsw2, ws=None, stream=None):
+                        dx_shared, dw13, dw2, dsw13, dsw2, ws=None, stream=None, fp8_wgrad=False):
+    """The FP8 backward (data gradients on FP8 operands); fp8_wgrad runs the
+    weight gradients on token-axis block-scaled FP8 operands as well
+    (moe_grouped_ffn_bwd_fp8w, workspace MOE_OP_FFN_BWD_FP8W)."""
     wp, wn = _ws(ws)
-    _check("moe_grouped_ffn_bwd_fp8", lib().moe_grouped_ffn_bwd_fp8(
+    name = "moe_grouped_ffn_bwd_fp8w" if fp8_wgrad else "moe_grouped_ffn_bwd_fp8"
+    _check(name, getattr(lib(), name)(
         ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13q_t), _p(s13_t), _p(w2q_t),
         _p(s2_t), _p(sw13q_t), _p(ss13_t), _p(sw2q_t), _p(ss2_t), _p(save_pre), _p(save_h),
         _p(save_pre_s), _p(save_h_s), _p(dout), _p(dy), _p(dx_perm), _p(dx_shared), _p(dw13),

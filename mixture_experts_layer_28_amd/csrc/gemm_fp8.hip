@@ -136,11 +136,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // this lane's rows, by matrix row (A: the group's first row + m; B: group
   // g's b_sexp_gstride rows + n). Rows outside are clamped into range: they
   // read zero codes, so any exponent does.
+  // RAG_K (weight gradients): both operands are token-axis transposes
+  // ([rows, Rp] codes, Rp = the row stride) in which group g's tokens start
+  // at k = kpos = 128 * (ceil(r0 / 128) + g); their scale rows hold Rp / 128
+  // words and the group's words start at kpos / 128.
   const int64_t KW = (t.K + kBK8 - 1) / kBK8;
+  const int64_t kpos = RAG == RAG_K ? kBK8 * ((t.r0 + kBK8 - 1) / kBK8 + t.g) : 0;
+  const int64_t KWrow = RAG == RAG_K ? p.a.ld / kBK8 : KW;
   const uint32_t* swa = reinterpret_cast<const uint32_t*>(p.a_sexp);
   const uint32_t* swb = reinterpret_cast<const uint32_t*>(p.b_sexp);
   auto word0 = [&](int64_t r) __attribute__((always_inline)) {
-    return (uint32_t)(((r >> 5) * KW) * 32 + (r & 31));
+    return (uint32_t)(((r >> 5) * KWrow) * 32 + (r & 31));
   };
   uint32_t sa_off[BLK ? MI : 1], sb_off[BLK ? NI : 1];
   uint32_t sa_nxt[BLK ? MI : 1], sb_nxt[BLK ? NI : 1], sa_cur[BLK ? MI : 1], sb_cur[BLK ? NI : 1];
@@ -148,7 +154,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t m = t.m0 + wm0 + 32 * i + (lane & 31);
-      sa_off[i] = word0((p.a.rowidx ? t.r0 : (int64_t)t.g * p.M) + (m < t.M ? m : t.M - 1));
+      const int64_t arow0 = RAG == RAG_K ? 0 : (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M);
+      sa_off[i] = word0(arow0 + (m < t.M ? m : t.M - 1));
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto load_scales = [&](int64_t kt) __attribute__((always_inline)) {
     if constexpr (BLK) {
       const int64_t kg0 = kbase + kt;
-      const uint32_t kg = 32 * (uint32_t)(kg0 < KW ? kg0 : KW - 1);
+      const uint32_t kg = 32 * (uint32_t)(kpos / kBK8 + (kg0 < KW ? kg0 : KW - 1));
 #pragma unroll
       for (int i = 0; i < MI; ++i) sa_nxt[i] = swa[sa_off[i] + kg];
 #pragma unroll
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const Dma8& d = X == 0 ? da : db;
     const bool kin = d.kk[i] < t.K - k0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? ra : rb, (lds_void*)(s + (wave * 8 + i) * 1024), 16,
-                                             kin ? d.off[i] : kOOB, (uint32_t)k0, 0, 0);
+                                             kin ? d.off[i] : kOOB, (uint32_t)(kpos + k0), 0, 0);
   };
 
   // half `part` of the fragment of rows base .. base+31 for slice sl
@@ -506,6 +513,7 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
   else
     tiles = (int64_t)p.G * ((p.M + kRows8 - 1) / kRows8) * nt;
   int64_t nb = (tiles + 7) / 8 * 8;
+  if (RAG == RAG_K) nb = rag_k_grid(p.G, ((p.M + kRows8 - 1) / kRows8) * nt);
   // tail split-K: up to tail_cus more items per XCD
   if (RAG == RAG_M && EPI == EPI_STORE && p.tail_ws) nb += 8 * (int64_t)p.tail_cus;
   if (tiles == 0) return hipSuccess;
@@ -516,9 +524,14 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
 }  // namespace
 
 // FP8 grouped GEMM, both operands K-contiguous (the forward's layouts, and
-// the data gradients against transposed weights).
-// Requires K % 16 == 0, 16-byte aligned rows, N % 4 == 0 (f % 4 for the
-// fused SwiGLU) and 16-byte aligned scale arrays; the caller checks.
+// the data gradients against transposed weights). With block scales also
+// RAG_K: the weight gradients, both operands token-axis transposes with each
+// group's tokens from k = 128 * (ceil(offsets[g] / 128) + g) (groups may hold
+// any number of rows; the codes past a group's rows within its last k-step
+// must be zero).
+// Requires K % 16 == 0 (RAG_M, RAG_NONE), 16-byte aligned rows, N % 4 == 0
+// (f % 4 for the fused SwiGLU) and 16-byte aligned scale arrays; the caller
+// checks.
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
   if (!p.a_sexp || !p.b_sexp || p.col_bias) return hipErrorInvalidValue;
 #define MOE_CASE(E_, R_) \
@@ -533,6 +546,8 @@ hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
     MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_NONE)
     MOE_CASE_BLK(EPI_GELU_FWD, RAG_NONE)
     MOE_CASE_BLK(EPI_STORE, RAG_NONE)
+    // and the weight gradients on token-axis transposes
+    MOE_CASE_BLK(EPI_STORE, RAG_K)
     return hipErrorInvalidValue;
   }
   MOE_CASE(EPI_SWIGLU_FWD, RAG_M)

@@ -12,11 +12,16 @@
 #include "../../include/moe.h"
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                                    const int32_t* valid_rows, void* codes, int64_t ld_q,
                                    uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
+                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st);
+hipError_t launch_set_bounds(int32_t* bounds, int32_t lo, int32_t hi, hipStream_t st);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
 hipError_t launch_quant_fp8_t(const void*, int64_t, int64_t, int64_t, void*, int32_t*, hipStream_t);
@@ -268,6 +273,10 @@ size_t blk_scale_bytes(int64_t rows, int64_t K) {
   return (size_t)128 * ((K + 127) / 128) * ((rows + 31) / 32);
 }
 
+// padded token axis of the FP8 weight gradients' transposed operands: each
+// of the E groups starts on a 128-token k-step
+int64_t wgrad_rp(const moe_desc* d) { return 128 * ((d->T * d->k + 127) / 128 + d->E); }
+
 // the GEMM addresses block-scale words with 32-bit offsets
 bool blk_scale_words_fit(int64_t rows, int64_t K) {
   return blk_scale_bytes(rows, K) / 4 < ((size_t)1 << 31);
@@ -309,6 +318,17 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return ws_bytes_for(d, MOE_OP_FFN_BWD) + align256((size_t)T * d->k * d->d) +
              align256((size_t)T * d->k * 4) + align256((size_t)T * d->k * pre_cols(d)) +
              align256((size_t)T * d->k * 4);
+    case MOE_OP_FFN_BWD_FP8W: {
+      // the FP8 backward's buffers, then the token-axis codes and block
+      // scales of the weight gradients' two operands (largest of the two
+      // GEMMs; the shared expert's fit in the routed ones), the k-step table
+      // and two ints of bounds
+      const int64_t Rp = wgrad_rp(d), P = pre_cols(d);
+      const int64_t ma = std::max(d->d, P), mb = std::max(d->f, d->d);
+      return ws_bytes_for(d, MOE_OP_FFN_BWD_FP8) + align256((size_t)ma * Rp) +
+             align256(blk_scale_bytes(ma, Rp)) + align256((size_t)mb * Rp) +
+             align256(blk_scale_bytes(mb, Rp)) + align256((size_t)(Rp / 128) * 4) + 256;
+    }
     case MOE_OP_FFN_FWD_FP8B: {
       // FP8 codes and block scales of H between the two GEMMs, then the
       // down-projection's split-K tail
@@ -455,7 +475,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FP8B)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_BWD_FP8W)
     return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
   *bytes = ws_bytes_for(desc, op);
   return MOE_OK;
@@ -1064,14 +1084,19 @@ int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void
                    "fp8 quantize both orientations");
 }
 
-int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
-                            const void* x, const void* w13q_t, const int32_t* s13_t,
-                            const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
-                            const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
-                            const void* save_pre, const void* save_h, const void* save_pre_s,
-                            const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
-                            void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
-                            void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The FP8 backward: data gradients on per-row FP8 operands, weight gradients
+// in bf16 (fp8w = false) or on token-axis block-scaled FP8 operands.
+int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                     const void* x, const void* w13q_t, const int32_t* s13_t, const void* w2q_t,
+                     const int32_t* s2_t, const void* sw13q_t, const int32_t* ss13_t,
+                     const void* sw2q_t, const int32_t* ss2_t, const void* save_pre,
+                     const void* save_h, const void* save_pre_s, const void* save_h_s,
+                     const void* dout, const void* dy, void* dx_perm, void* dx_shared, void* dw13,
+                     void* dw2, void* dsw13, void* dsw2, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (desc->dtype != MOE_BF16)
@@ -1103,9 +1128,13 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
     MOE_TRY(need(dsw13, "dsw13"));
     MOE_TRY(need(dsw2, "dsw2"));
   }
-  MOE_TRY(check_ws(desc, MOE_OP_FFN_BWD_FP8, ws, ws_bytes));
+  MOE_TRY(check_ws(desc, fp8w ? MOE_OP_FFN_BWD_FP8W : MOE_OP_FFN_BWD_FP8, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
+  const int64_t Rp = wgrad_rp(desc);
+  if (fp8w && (std::max(d, P) * Rp >= (int64_t(1) << 31) || std::max(f, d) * Rp >= (int64_t(1) << 31) ||
+               !blk_scale_words_fit(std::max(d, P), Rp) || !blk_scale_words_fit(std::max(f, d), Rp)))
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients: the token-axis codes exceed 2^31 bytes");
   if (T == 0) {
     // no rows: every weight gradient is zero
     MOE_TRY(hip_check(launch_fill_zero(dw13, (size_t)desc->E * P * d * 2, s), "zero dw13"));
@@ -1127,6 +1156,15 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
   int32_t* gs = (int32_t*)(w8 + align256((size_t)T * desc->k * d));
   uint8_t* pq = (uint8_t*)((char*)gs + align256((size_t)T * desc->k * 4));
   int32_t* ps = (int32_t*)((char*)pq + align256((size_t)T * desc->k * P));
+  // FP8 weight gradients: token-axis codes and scales of the two operands,
+  // the k-step -> group table and the shared expert's one-group bounds
+  char* w9 = w8 + (ws_bytes_for(desc, MOE_OP_FFN_BWD_FP8) - ws_bytes_for(desc, MOE_OP_FFN_BWD));
+  uint8_t* qa = (uint8_t*)w9;
+  uint8_t* qa_s = qa + align256((size_t)std::max(d, P) * Rp);
+  uint8_t* qb = qa_s + align256(blk_scale_bytes(std::max(d, P), Rp));
+  uint8_t* qb_s = qb + align256((size_t)std::max(f, d) * Rp);
+  int32_t* ktab = (int32_t*)(qb_s + align256(blk_scale_bytes(std::max(f, d), Rp)));
+  int32_t* bounds = (int32_t*)((char*)ktab + align256((size_t)(Rp / 128) * 4));
   const int epi_b = desc->act == MOE_SWIGLU ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
     const int ragm = shared ? RAG_NONE : RAG_M;
@@ -1193,6 +1231,47 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
       Scope sc(shared ? K_SH_DGRAD_UP : K_DGRAD_UP, s);
       MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, ragm, s), "fp8 ffn dgrad first matrix"));
     }
+    if (fp8w) {
+      // weight gradients on token-axis FP8 operands (block scales per 32 of
+      // each expert's tokens): dW2 = dO^T H, then dW13 = dpre^T X
+      const int32_t* off = offsets;
+      if (shared) {
+        MOE_TRY(hip_check(launch_set_bounds(bounds, 0, (int32_t)T, s), "shared bounds"));
+        off = bounds;
+      }
+      const int64_t R = shared ? T : T * desc->k;
+      const int64_t rp = 128 * ((R + 127) / 128 + G);
+      auto quant_t = [&](const void* src, int64_t C, uint8_t* codes, uint8_t* sc) {
+        Scope q(K_QUANT_FP8, s);
+        return hip_check(launch_quant_fp8_tblocks(src, R, C, off, G, ktab, codes, sc, s),
+                         "fp8 token-axis quantize");
+      };
+      for (int which = 0; which < 2; ++which) {
+        const bool down = which == 0;
+        const int64_t M = down ? d : P, N = down ? f : d;
+        MOE_TRY(quant_t(down ? go : dpre, M, qa, qa_s));
+        MOE_TRY(quant_t(down ? hs : xin, N, qb, qb_s));
+        GemmArgs r = blank();
+        r.a = opnd(qa, rp, 0, 0);
+        r.b = opnd(qb, rp, 0, 0);
+        r.a_sexp = (const int32_t*)qa_s;
+        r.b_sexp = (const int32_t*)qb_s;
+        r.b_sexp_gstride = 0;
+        r.blk_scales = 1;
+        r.c = down ? (shared ? dsw2 : dw2) : (shared ? dsw13 : dw13);
+        r.ldc = N;
+        r.c_gstride = M * N;
+        r.offsets = off;
+        r.G = G;
+        r.M = M;
+        r.N = N;
+        r.K = R;
+        Scope sc(down ? (shared ? K_SH_WGRAD_DOWN : K_WGRAD_DOWN) : (shared ? K_SH_WGRAD_UP : K_WGRAD_UP), s);
+        MOE_TRY(hip_check(gemm_fp8(r, EPI_STORE, RAG_K, s),
+                          down ? "fp8 ffn wgrad down matrix" : "fp8 ffn wgrad first matrix"));
+      }
+      continue;
+    }
     // weight gradients in bf16, as in moe_grouped_ffn_bwd
     GemmArgs r = blank();
     r.a = opnd(go, d, 0, 1);
@@ -1222,6 +1301,36 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
                      shared ? K_SH_WGRAD_UP : K_WGRAD_UP));
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                            const void* x, const void* w13q_t, const int32_t* s13_t,
+                            const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
+                            const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
+                            const void* save_pre, const void* save_h, const void* save_pre_s,
+                            const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                            void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return ffn_bwd_fp8_impl(false, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
+                          ss13_t, sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
+                          dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
+}
+
+int moe_grouped_ffn_bwd_fp8w(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w13q_t, const int32_t* s13_t,
+                             const void* w2q_t, const int32_t* s2_t, const void* sw13q_t,
+                             const int32_t* ss13_t, const void* sw2q_t, const int32_t* ss2_t,
+                             const void* save_pre, const void* save_h, const void* save_pre_s,
+                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return ffn_bwd_fp8_impl(true, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
+                          ss13_t, sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
+                          dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
 }
 
 int moe_combine(const moe_desc* desc, const void* out, const void* out_shared, const float* gate,

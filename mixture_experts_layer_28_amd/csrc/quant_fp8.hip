@@ -132,6 +132,100 @@ __global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
   }
 }
 
+// ---- block scales along the token axis, into the transpose (weight gradients)
+// src: a token-major [R, C] bf16 matrix whose rows are grouped (group g owns
+// rows off[g] .. off[g+1]-1). Column c of group g becomes a run of row c of
+// codes_t [C, Rp]: token j of the group at column pos_g + j, with
+// pos_g = 128 * (ceil(off[g] / 128) + g), so every group starts on a 128-token
+// k-step and the groups never overlap (pos_{g+1} >= pos_g + rows_g + 1).
+// Block b of k-step kt (tokens 128 kt + 32 b .. +31 of the group, the last
+// one partial) gets e = the per-row rule on that block of the column, clipped
+// to [-127, 127]; its byte e + 127 goes to the 32-column interleaved scale
+// words of codes_t's rows (word w = pos_g / 128 + kt of row c at
+// ((c / 32) * Rp / 128 + w) * 32 + c % 32, byte b). Padding tokens of a
+// group's last k-step get code 0 and blocks past the group byte 127; the
+// k-steps between groups are not written.
+//
+// kstep_group_kernel fills tab[q] = the group whose k-steps include padded
+// k-step q, or -1: a binary search over the group starts per q.
+__global__ __launch_bounds__(256) void kstep_group_kernel(const int32_t* __restrict__ off, int G, int64_t nq,
+                                                          int32_t* __restrict__ tab) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nq) return;
+  // the last g with kstart(g) = ceil(off[g] / 128) + g <= q (kstart grows with g)
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)(off[mid] + 127) / 128 + mid <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t ks = (int64_t)(off[lo] + 127) / 128 + lo;
+  const int64_t rows = off[lo + 1] - off[lo];
+  tab[q] = q >= ks && q - ks < (rows + 127) / 128 ? lo : -1;
+}
+
+// bounds[0] = lo, bounds[1] = hi: the one-group bounds of a plain matrix
+__global__ void set_bounds_kernel(int32_t* __restrict__ bounds, int32_t lo, int32_t hi) {
+  if (threadIdx.x == 0) {
+    bounds[0] = lo;
+    bounds[1] = hi;
+  }
+}
+
+constexpr int kTBC = 64;   // columns per workgroup of the token-axis quantizer
+
+// Workgroup (x, q): columns 64x .. 64x+63 of padded k-step q (tab[q]'s group).
+// The 128 x 64 tile is staged in LDS row by row (16-byte chunks); thread
+// (b = tid / 64, c = tid % 64) then takes token block b of column c: its
+// maximum, its exponent byte and its 32 codes (two 16-byte stores).
+__global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
+    const bf16_t* __restrict__ src, int64_t C, const int32_t* __restrict__ off, const int32_t* __restrict__ tab,
+    uint8_t* __restrict__ codes, int64_t Rp, uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTBC];
+  const int64_t q = blockIdx.y, c0 = (int64_t)blockIdx.x * kTBC;
+  const int g = tab[q];
+  if (g < 0) return;
+  const int64_t kt = q - ((int64_t)(off[g] + 127) / 128 + g);
+  const int64_t t0 = off[g] + 128 * kt;
+  const int64_t left = off[g + 1] - t0;
+  const int nv = left < 128 ? (int)left : 128;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ch = tid + 256 * u, r = ch >> 3, cc = ch & 7;
+    const int64_t c = c0 + 8 * cc;
+    const uint4 v = r < nv && c < C ? *reinterpret_cast<const uint4*>(src + (t0 + r) * C + c)
+                                    : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(tile + r * kTBC + 8 * cc) = v;
+  }
+  __syncthreads();
+  const int cl = tid & 63, b = tid >> 6;
+  const int64_t c = c0 + cl;
+  if (c >= C) return;
+  uint32_t m = 0;
+  uint32_t w[16];   // the block's 32 bf16, two to a word, token order
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = tile[(32 * b + 2 * i) * kTBC + cl], hi = tile[(32 * b + 2 * i + 1) * kTBC + cl];
+    w[i] = lo | (hi << 16);
+    m = (lo & 0x7fffu) > m ? (lo & 0x7fffu) : m;
+    m = (hi & 0x7fffu) > m ? (hi & 0x7fffu) : m;
+  }
+  const float amax = bf2f(m);
+  int ex = 0;
+  const float mant = frexpf(amax, &ex);
+  int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  const int64_t kw = (int64_t)(off[g] + 127) / 128 + g + kt;   // k-step word of row c
+  uint2 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = to_e4m3(make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]), e);
+  uint4* dst = reinterpret_cast<uint4*>(codes + c * Rp + 128 * kw + 32 * b);
+  dst[0] = make_uint4(o[0].x, o[0].y, o[1].x, o[1].y);
+  dst[1] = make_uint4(o[2].x, o[2].y, o[3].x, o[3].y);
+  scales[(((c >> 5) * (Rp / 128) + kw) * 32 + (c & 31)) * 4 + b] = (uint8_t)(e + 127);
+}
+
 // ---- per-column quantization into the transpose
 // src: G row-major R x C bf16 matrices; codes: G row-major C x R (the
 // transposes), so codes row c is src column c quantized like a row above.
@@ -406,6 +500,24 @@ hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(kQThreads), 0, st,
                      (const bf16_t*)src, K, ld_src, valid_rows, (uint8_t*)codes, ld_q, sexp);
+  return hipGetLastError();
+}
+
+// Token-axis block quantization of a grouped token-major [R, C] matrix into
+// its transpose (see quant_tblocks_fp8_kernel). off: G + 1 group bounds on the
+// device; tab: nq = Rp / 128 ints of scratch; Rp = 128 * (ceil(R / 128) + G).
+hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
+                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st) {
+  const int64_t Rp = 128 * ((R + 127) / 128 + G), nq = Rp / 128;
+  if (R == 0 || C == 0) return hipSuccess;
+  hipLaunchKernelGGL(kstep_group_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, off, G, nq, tab);
+  hipLaunchKernelGGL(quant_tblocks_fp8_kernel, dim3((unsigned)((C + kTBC - 1) / kTBC), (unsigned)nq), dim3(256), 0,
+                     st, (const bf16_t*)src, C, off, (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_bounds(int32_t* bounds, int32_t lo, int32_t hi, hipStream_t st) {
+  hipLaunchKernelGGL(set_bounds_kernel, dim3(1), dim3(64), 0, st, bounds, lo, hi);
   return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8,
-               MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats,
+from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_BWD_FP8W, MOE_OP_FFN_FWD,
+               MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats,
                bias_update, combine, combine_bwd, fp8_block_scale_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8,
                grouped_ffn_fwd, grouped_ffn_fwd_fp8, grouped_ffn_fwd_fp8b, make_desc, permute,
                permute_bwd, quantize_fp8, quantize_fp8_blocks, quantize_fp8_both,
@@ -46,12 +46,17 @@ class MoELayer:
     bytes, on the block-scaled matrix instructions). The backward's FP8 GEMMs
     keep per-row scales either way; with "block" the backward quantizes the
     weight transposes itself.
+
+    fp8_wgrad (with fp8_bwd) runs the weight gradients on FP8 operands too:
+    the library quantizes dO, H, dpre and x_perm along the token axis (one
+    scale per 32 of an expert's tokens per column) into their transposes.
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
                  bias_gamma: float = 0.0, gumbel_tau: float = 0.0, fp8_fwd: bool = False,
-                 fp8_bwd: bool = False, fp8_scale: str = "row", device="cuda"):
+                 fp8_bwd: bool = False, fp8_scale: str = "row", fp8_wgrad: bool = False,
+                 device="cuda"):
         self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
@@ -62,6 +67,9 @@ class MoELayer:
         if fp8_scale not in ("row", "block"):
             raise ValueError(f"fp8_scale must be 'row' or 'block' (got {fp8_scale!r})")
         self.fp8_block = fp8_fwd and fp8_scale == "block"
+        if fp8_wgrad and not fp8_bwd:
+            raise ValueError("fp8_wgrad runs with the FP8 data gradients: set fp8_bwd too")
+        self.fp8_wgrad = fp8_wgrad
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dt = dt
         P = 2 * f if act == "swiglu" else f
@@ -112,19 +120,23 @@ class MoELayer:
             u8 = torch.uint8
             # per-row exponents (int32), or the block-scale array of the
             # [rows, K] matrix (bytes)
+            # (rows: the operand's leading shape; K: its row length)
             if self.fp8_block:
                 def sc(rows, K):
-                    return z(fp8_block_scale_bytes(rows, K), dtype=u8)
+                    n = 1
+                    for r in rows:
+                        n *= r
+                    return z(fp8_block_scale_bytes(n, K), dtype=u8)
             else:
                 def sc(rows, K):
-                    return z(rows, dtype=i32)
-            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), sc(R, d)
-            self.w13q, self.s13 = z(E, P, d, dtype=u8), sc(E * P, d)
-            self.w2q, self.s2 = z(E, d, f, dtype=u8), sc(E * d, f)
+                    return z(*rows, dtype=i32)
+            self.xq_perm, self.sx_perm = z(R, d, dtype=u8), sc((R,), d)
+            self.w13q, self.s13 = z(E, P, d, dtype=u8), sc((E, P), d)
+            self.w2q, self.s2 = z(E, d, f, dtype=u8), sc((E, d), f)
             sh = bool(n_shared)
-            self.xq, self.sx = (z(T, d, dtype=u8), sc(T, d)) if sh else (None, None)
-            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), sc(P, d)) if sh else (None, None)
-            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), sc(d, f)) if sh else (None, None)
+            self.xq, self.sx = (z(T, d, dtype=u8), sc((T,), d)) if sh else (None, None)
+            self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), sc((1, P), d)) if sh else (None, None)
+            self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), sc((1, d), f)) if sh else (None, None)
         if fp8_bwd:
             u8 = torch.uint8
             sh = bool(n_shared)
@@ -135,7 +147,7 @@ class MoELayer:
         ops = [MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
                MOE_OP_ROUTE_BWD] + \
               ([MOE_OP_FFN_FWD_FP8B if self.fp8_block else MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
-              ([MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
+              ([MOE_OP_FFN_BWD_FP8W if fp8_wgrad else MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
         wsb = max(workspace_size(self.desc, op) for op in ops)
         if fp8_fwd and fp8_bwd:   # both weight orientations from the forward's one pass
             wsb = max(wsb, quantize_fp8_both_ws((E, P, d)), quantize_fp8_both_ws((E, d, f)))
@@ -211,7 +223,8 @@ class MoELayer:
                                 self.w2q_t, self.s2_t, self.sw13q_t, self.ss13_t, self.sw2q_t,
                                 self.ss2_t, self.save_pre, self.save_h, self.save_pre_s,
                                 self.save_h_s, self.dout, dy, self.dx_perm, self.dx_shared,
-                                self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws)
+                                self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws,
+                                fp8_wgrad=self.fp8_wgrad)
         else:
             grouped_ffn_bwd(D, self.x_perm, self.offsets, x, w13, w2, sw13, sw2, self.save_pre,
                             self.save_h, self.save_pre_s, self.save_h_s, self.dout, dy,

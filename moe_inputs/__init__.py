@@ -71,6 +71,7 @@ class Workload:
     fp8: bool = False             # forward GEMMs on E4M3 operands (bf16 activations)
     fp8_scale: str = "row"        # the forward's FP8 scales: "row" or "block" (32 along K)
     fp8_bwd: bool = False         # backward data-gradient GEMMs on E4M3 operands as well
+    fp8_wgrad: bool = False       # and the weight-gradient GEMMs (token-axis block scales)
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -123,6 +124,12 @@ WORKLOADS = {
     "dsv3_ep8_shard_fp8_dgrad_bf16": Workload("dsv3_ep8_shard_fp8_dgrad_bf16", T=8192, d=7168,
                                               E=32, k=8, f=2048, score="sigmoid", n_shared=1,
                                               sel_bias=True, fp8=True, fp8_bwd=True),
+    # every GEMM of the step on FP8 operands (weight gradients: token-axis block scales)
+    "mixtral_fp8_all_bf16": Workload("mixtral_fp8_all_bf16", T=8192, d=4096, E=8, k=2, f=14336,
+                                     cf=1.25, fp8=True, fp8_bwd=True, fp8_wgrad=True),
+    "dsv3_ep8_shard_fp8_all_bf16": Workload("dsv3_ep8_shard_fp8_all_bf16", T=8192, d=7168, E=32,
+                                            k=8, f=2048, score="sigmoid", n_shared=1,
+                                            sel_bias=True, fp8=True, fp8_bwd=True, fp8_wgrad=True),
 }
 
 

@@ -65,7 +65,7 @@ def gpu_layer(w: Workload, g: dict):
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
-                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale)
+                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale, fp8_wgrad=w.fp8_wgrad)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -80,7 +80,7 @@ def oracle_layer(w: Workload, g: dict):
                           w.gumbel_tau, fp8=oracle_fp8(w))
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
                            w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau,
-                           fp8_dgrad=w.fp8_bwd)
+                           fp8_dgrad=w.fp8_bwd, fp8_wgrad=w.fp8_wgrad)
     return fwd, bwd, f
 
 
@@ -255,15 +255,19 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     assert_close("dX_perm", to_np(L.dx_perm[:A])[g_rows[keep]], bwd["dx_perm"][o_rows[keep]], dt, rep,
                  **dxt)
     gw13, gw2 = to_np(L.dw13), to_np(L.dw2)
-    assert_close("dW13", gw13[e_ok], bwd["dw13"][e_ok], dt, rep)
-    assert_close("dW2", gw2[e_ok], bwd["dw2"][e_ok], dt, rep)
+    # FP8 weight gradients: see fp8_wgrad_tol (exact stage check in check_fp8_wgrad)
+    rows = np.diff(off)
+    wgt = fp8_wgrad_tol(int(rows[rows > 0].min(initial=w.T))) if w.fp8_wgrad else {}
+    assert_close("dW13", gw13[e_ok], bwd["dw13"][e_ok], dt, rep, **wgt)
+    assert_close("dW2", gw2[e_ok], bwd["dw2"][e_ok], dt, rep, **wgt)
     empty = [e for e in range(E) if off[e + 1] == off[e]]
     for e in empty:   # an expert without rows has exactly zero gradient
         assert not gw13[e].any() and not gw2[e].any()
     if w.n_shared:
         assert_close("dX_shared", to_np(L.dx_shared), bwd["dx_shared"], dt, rep, **dxt)
-        assert_close("dSW13", to_np(L.dsw13), bwd["dsw13"], dt, rep)
-        assert_close("dSW2", to_np(L.dsw2), bwd["dsw2"], dt, rep)
+        swt = fp8_wgrad_tol(w.T) if w.fp8_wgrad else {}
+        assert_close("dSW13", to_np(L.dsw13), bwd["dsw13"], dt, rep, **swt)
+        assert_close("dSW2", to_np(L.dsw2), bwd["dsw2"], dt, rep, **swt)
     # The router gradient can vanish identically (top-1: the one renormalised
     # gate is constant 1), leaving only fp32 rounding of g (1 - g) dg on the
     # GPU; an absolute floor scaled by the formula's inputs covers that case.
@@ -284,6 +288,8 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     assert_close("dX", to_np(L.dX)[tok_ok], bwd["dX"][tok_ok], dt, rep, **dxo)
     if w.fp8_bwd:
         check_fp8_dgrad(w, L, dev, bwd, rep, g_rows[keep], o_rows[keep], off)
+    if w.fp8_wgrad:
+        check_fp8_wgrad(w, L, dev, rep, off)
     return len(flips)
 
 
@@ -302,6 +308,54 @@ def fp8_fwd_tol(f):
 
 def fp8_dgrad_tol(f):
     return dict(max_rel=max(5e-2, 0.5 / np.sqrt(f)), l1_rel=1.5e-2)
+
+
+# FP8 weight gradients: a weight-gradient element sums n tokens' products, and
+# a token whose bf16 operand (dO, H or dpre) the two sides round differently at
+# an E4M3 boundary moves one term by one E4M3 step (up to 2^-3 of it); against
+# max|dW| of about 4 sqrt(n) rms(a) rms(b) that is up to about 0.5 / sqrt(n)
+# for the smallest expert's n tokens. dpre also carries the FP8 data gradient's
+# bound. The stage check (check_fp8_wgrad) holds each weight gradient of the
+# GPU's own bf16 operands to the bf16 bound.
+def fp8_wgrad_tol(n):
+    return dict(max_rel=max(5e-2, 0.5 / np.sqrt(max(n, 1))), l1_rel=1.5e-2)
+
+
+def check_fp8_wgrad(w, L, dev, rep, off):
+    """The FP8 weight gradients of the GPU's own bf16 operands (dO, H, dpre,
+    x_perm; for the shared expert dY, its H and dpre and x), recomputed by the
+    oracle's expert_wgrad_fp8, to the bf16 bound. The layer's later calls
+    reuse the workspace, so the backward is rerun into a fresh one (it is
+    deterministic: check_fp8_dgrad compares the rerun with the layer bitwise)
+    and dpre is read from there."""
+    import mixture_experts_layer_28_amd as moe
+    A = int(off[-1])
+    R, P = w.T * w.k, (2 * w.f if w.act == "swiglu" else w.f)
+    ws = torch.empty_like(L.ws)
+    like = lambda t: torch.empty_like(t) if t is not None else None   # noqa: E731
+    o = {n: like(getattr(L, n)) for n in ("dx_perm", "dx_shared", "dw13", "dw2", "dsw13", "dsw2")}
+    moe.grouped_ffn_bwd_fp8(L.desc, L.x_perm, L.offsets, dev["x"], L.w13q_t, L.s13_t, L.w2q_t,
+                            L.s2_t, L.sw13q_t, L.ss13_t, L.sw2q_t, L.ss2_t, L.save_pre, L.save_h,
+                            L.save_pre_s, L.save_h_s, L.dout, dev["dy"], o["dx_perm"],
+                            o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws,
+                            fp8_wgrad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o["dw13"], L.dw13) and torch.equal(o["dw2"], L.dw2)
+    dO, H, X = (to_np(t[:A]) for t in (L.dout, L.save_h, L.x_perm))
+    dp = to_np(ws[: R * P * 2].view(torch.bfloat16).view(R, P)[:A])
+    for e in range(w.E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        g13, g2 = O.expert_wgrad_fp8(X[r0:r1], H[r0:r1], dO[r0:r1], dp[r0:r1])
+        assert_close(f"dW13(own) e{e}", to_np(L.dw13[e]), g13, "bf16", rep)
+        assert_close(f"dW2(own) e{e}", to_np(L.dw2[e]), g2, "bf16", rep)
+    if w.n_shared:
+        off_s = (R * P * 2 + 255) // 256 * 256
+        dps = to_np(ws[off_s: off_s + w.T * P * 2].view(torch.bfloat16).view(w.T, P))
+        g13, g2 = O.expert_wgrad_fp8(to_np(dev["x"]), to_np(L.save_h_s), to_np(dev["dy"]), dps)
+        assert_close("dSW13(own)", to_np(L.dsw13[0]), g13, "bf16", rep)
+        assert_close("dSW2(own)", to_np(L.dsw2[0]), g2, "bf16", rep)
 
 
 def _e4m3_rows_ref(M):
@@ -342,7 +396,8 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
     moe.grouped_ffn_bwd_fp8(L.desc, L.x_perm, L.offsets, dev["x"], L.w13q_t, L.s13_t, L.w2q_t,
                             L.s2_t, L.sw13q_t, L.ss13_t, L.sw2q_t, L.ss2_t, L.save_pre, L.save_h,
                             L.save_pre_s, L.save_h_s, L.dout, dev["dy"], o["dx_perm"],
-                            o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws)
+                            o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws,
+                            fp8_wgrad=w.fp8_wgrad)
     torch.cuda.synchronize()
     assert torch.equal(o["dx_perm"][:A], L.dx_perm[:A]), "FP8 backward is not deterministic"
     assert torch.equal(o["dw13"], L.dw13) and torch.equal(o["dw2"], L.dw2)

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 26
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -314,6 +314,32 @@ def test_fp8_block_forward_validation():
         bad = list(ptrs)
         bad[1] = bad_v
         assert call(_desc(), p=bad) == 1
+
+
+def test_fp8_wgrad_backward_validation():
+    """The FP8 weight-gradient backward validates like the FP8 backward, and
+    its workspace adds the token-axis codes and scales of both operands."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE)] * 23
+
+    def call(d, ws_bytes=1 << 40):
+        return L.moe_grouped_ffn_bwd_fp8w(ctypes.byref(d), *ptrs, P(FAKE), ws_bytes, None)
+    assert call(_desc(dtype="f32")) == 2
+    assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
+    d = _desc(T=64, d=64, E=8, k=2, f=64)
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_BWD_FP8, ctypes.byref(a)) == 0
+    assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_BWD_FP8W, ctypes.byref(b)) == 0
+    # Rp = 128 * (ceil(128 / 128) + 8) = 1152: codes 128 x Rp and 64 x Rp,
+    # scales 128 * 9 per 32 rows, a 9-int k-step table, two bounds
+    Rp = 1152
+    extra = (128 * Rp) + (4 * 128 * 9) + (64 * Rp) + (2 * 128 * 9) + 256 + 256
+    assert b.value - a.value == extra
+    assert call(d, ws_bytes=b.value - 1) == 3
+    bad = list(ptrs)
+    bad[3] = None
+    assert L.moe_grouped_ffn_bwd_fp8w(ctypes.byref(_desc()), *bad, P(FAKE), 1 << 40, None) == 1
 
 
 def test_fp8_transposing_quantize_validation():

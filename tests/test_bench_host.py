@@ -39,6 +39,9 @@ def test_fp8_launch_classification_and_labels():
     assert bench.dtype_label(f8) == "fp8-e4m3 fwd GEMMs, bf16 bwd"
     assert bench.dtype_label(f8d) == "fp8-e4m3 fwd and dgrad GEMMs, bf16 wgrad"
     assert bench.dtype_label(WORKLOADS["tiny_fp32"]) == "f32"
+    f8w = WORKLOADS["mixtral_fp8_all_bf16"]
+    assert [bench.is_fp8_gemm(f8w, r) for r in roles] == [True] * 6
+    assert bench.dtype_label(f8w) == "fp8-e4m3 fwd, dgrad and wgrad GEMMs (wgrad: 32-token block scales)"
     assert bench.dtype_label(WORKLOADS["mixtral_fp8b_bf16"]) == \
         "fp8-e4m3 fwd GEMMs (1x32 block scales), bf16 bwd"
 

@@ -11,6 +11,8 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
   mixtral_fp8_dgrad_bf16  the same with FP8 data-gradient GEMMs as well
   mixtral_fp8b_bf16 the Mixtral-like layer with block-scaled FP8 forward GEMMs
                     (one scale per 32 elements along K)
+  mixtral_fp8_all_bf16 every GEMM on FP8 operands (weight gradients with
+                    token-axis block scales)
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -26,8 +28,8 @@ import torch
 
 import oracle as O
 from moe_inputs import WORKLOADS, as_f64, gen_all
-from parity_util import (Report, assert_close, assert_rows_match, bits, fp8_dgrad_tol, gpu_layer,
-                         to_np)
+from parity_util import (Report, assert_close, assert_rows_match, bits, fp8_dgrad_tol, fp8_wgrad_tol,
+                         gpu_layer, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +142,10 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     def wq_t(m):
         return O.quantize_weights_fp8_t(m) if w.fp8_bwd else None
     dxt = fp8_dgrad_tol(w.f) if w.fp8_bwd else {}
+    # FP8 weight gradients: the bound of the smallest sampled expert's rows
+    nrows = [int(pm["offsets"][e + 1] - pm["offsets"][e]) for e in exps]
+    wgt = fp8_wgrad_tol(min([n for n in nrows if n > 0], default=w.T)) if w.fp8_wgrad else {}
+    wgt_s = fp8_wgrad_tol(w.T) if w.fp8_wgrad else {}
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
@@ -177,9 +183,11 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
             _, sv = efwd(Xe, w13f[rows13], w2f[:, J], w.act)
             # hidden columns J only: dH[:, J] needs rows J of w2's transpose
             # (dX of this call is not used: it would need all of dpre's row)
-            _, d13, d2, _ = ebwd(Xe, w13e[rows13], w2e[:, J],
-                                 None if w13t is None else w13t[:, rows13],
-                                 None if w2t is None else w2t[J], sv, dOe)
+            _, d13, d2, dpc = ebwd(Xe, w13e[rows13], w2e[:, J],
+                                   None if w13t is None else w13t[:, rows13],
+                                   None if w2t is None else w2t[J], sv, dOe)
+            if w.fp8_wgrad:   # per-column token-axis quantization: columns separate
+                d13, d2 = O.expert_wgrad_fp8(Xe, sv["H"], dOe, dpc)
             dw13_ref.append(d13)
             dw2_ref.append(d2)
             dw13_got.append(to_np(L.dw13[e][torch.as_tensor(rows13, device="cuda")]))
@@ -201,13 +209,15 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
         J = np.sort(rng.choice(w.f, size=n_col, replace=False))
         rows13 = np.concatenate([J, w.f + J]) if w.act == "swiglu" else J
         _, sv = efwd(x, sw13f[rows13], sw2f[:, J], w.act)
-        _, d13, d2, _ = ebwd(x, sw13[rows13], sw2[:, J],
-                             None if sw13t is None else sw13t[:, rows13],
-                             None if sw2t is None else sw2t[J], sv, dy)
+        _, d13, d2, dpc = ebwd(x, sw13[rows13], sw2[:, J],
+                               None if sw13t is None else sw13t[:, rows13],
+                               None if sw2t is None else sw2t[J], sv, dy)
+        if w.fp8_wgrad:
+            d13, d2 = O.expert_wgrad_fp8(x, sv["H"], dy, dpc)
         assert_close("dSW13[sampled]", to_np(L.dsw13[0][torch.as_tensor(rows13, device="cuda")]),
-                     d13, dt, rep)
+                     d13, dt, rep, **wgt_s)
         assert_close("dSW2[sampled]", to_np(L.dsw2[0][:, torch.as_tensor(J, device="cuda")]), d2,
-                     dt, rep)
+                     dt, rep, **wgt_s)
         del sw13, sw2
     print("[step] sampled oracle done", flush=True)
     for k_ in ref:
@@ -224,8 +234,8 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     assert_close("dlogits", to_np(L.dlogits)[toks], rb["dlogits"], dt, rep, atol=dl_floor)
     assert_close("dX", to_np(L.dX)[toks], dX_ref, dt, rep, **dxt)
     if dw13_ref:
-        assert_close("dW13[sampled]", np.array(dw13_got), np.array(dw13_ref), dt, rep)
-        assert_close("dW2[sampled]", np.array(dw2_got), np.array(dw2_ref), dt, rep)
+        assert_close("dW13[sampled]", np.array(dw13_got), np.array(dw13_ref), dt, rep, **wgt)
+        assert_close("dW2[sampled]", np.array(dw2_got), np.array(dw2_ref), dt, rep, **wgt)
     gdl = to_np(L.dlogits)
     assert_close("dW_r(own dl)", to_np(L.dw_r), gdl.T @ x, dt, rep, rel=2e-5)
     # the whole router backward against the oracle's, on every token, given
@@ -248,7 +258,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
                                   "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16",
-                                  "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16"])
+                                  "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16", "mixtral_fp8_all_bf16"])
 def test_fullsize_sampled(name):
     w = WORKLOADS[name]
     # the oracle's FP8 backward quantizes each sampled expert's weights both

@@ -32,6 +32,10 @@ REDUCED = {
     "mixtral_fp8b_small": WORKLOADS["mixtral_fp8b_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8b_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
                                                       fp8_scale="block"),
+    # every GEMM on FP8 operands (weight gradients: token-axis block scales)
+    "mixtral_fp8_all_small": WORKLOADS["mixtral_fp8_all_bf16"].replace(T=1536, d=512, f=768),
+    "dsv3_fp8_all_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
+                                                         fp8_bwd=True, fp8_wgrad=True),
     # FP8 forward and FP8 data gradients (weight gradients bf16)
     "mixtral_fp8_dgrad_small": WORKLOADS["mixtral_fp8_dgrad_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_dgrad_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
@@ -103,6 +107,19 @@ EDGE = {
                                         n_shared=1, fp8=True, fp8_scale="block"),
     "fp8b_fwd_fp8_dgrad": Workload("f8bd", T=600, d=256, E=4, k=2, f=384, fp8=True,
                                    fp8_bwd=True, fp8_scale="block"),
+    # FP8 weight gradients: ragged experts (rows off every 32- and 128-token
+    # step), K tails, GELU and a shared expert; no routed rows; every token on
+    # one expert (the others empty); and after the block-scaled forward
+    "ragged_fp8_all_gelu_shared": Workload("ragged8w", T=1000, d=144, E=6, k=3, f=208,
+                                           act="gelu", score="sigmoid", n_shared=1,
+                                           sel_bias=True, fp8=True, fp8_bwd=True,
+                                           fp8_wgrad=True),
+    "fp8_all_dropped_shared": Workload("drop8w", T=512, d=256, E=8, k=2, f=256, cf=0.0,
+                                       n_shared=1, fp8=True, fp8_bwd=True, fp8_wgrad=True),
+    "fp8_all_one_expert": Workload("onehot8w", T=700, d=256, E=4, k=1, f=256,
+                                   logit_bias={2: 50.0}, fp8=True, fp8_bwd=True, fp8_wgrad=True),
+    "fp8b_fwd_fp8_all": Workload("f8bw", T=600, d=256, E=4, k=2, f=384, fp8=True, fp8_bwd=True,
+                                 fp8_wgrad=True, fp8_scale="block"),
 }
 
 

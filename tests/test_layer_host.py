@@ -1,0 +1,90 @@
+"""Host-side checks of the layer's call sequence, without a GPU: the library's
+compute entry points are replaced by a recorder (workspace sizes and the
+capacity still come from the real library), and the layer runs a step on CPU
+tensors. Every Python-side shape and argument check of the binding runs, so a
+buffer the layer sizes wrongly for one of its modes fails here."""
+import itertools
+
+import pytest
+import torch
+
+import mixture_experts_layer_28_amd as moe
+from mixture_experts_layer_28_amd.layer import MoELayer
+
+HOST_CALLS = {"moe_workspace_size", "moe_capacity", "moe_last_error", "moe_status_str",
+              "moe_abi_version"}
+
+
+class _Recorder:
+    def __init__(self, real):
+        self.real, self.calls = real, []
+
+    def __getattr__(self, name):
+        if name in HOST_CALLS:
+            return getattr(self.real, name)
+
+        def call(*args):
+            self.calls.append(name)
+            return 0
+        return call
+
+
+@pytest.fixture
+def recorder(monkeypatch):
+    rec = _Recorder(moe.lib())
+    monkeypatch.setattr(moe, "_lib", rec)
+
+    def ptr(t):
+        if t is None:
+            return None
+        assert t.is_contiguous()
+        return t.data_ptr()
+    monkeypatch.setattr(moe, "_p", ptr)
+    monkeypatch.setattr(moe, "_stream", lambda stream=None: None)
+    return rec
+
+
+def _inputs(T, d, E, f, P, n_shared):
+    bf = torch.bfloat16
+    inp = dict(x=torch.zeros(T, d, dtype=bf), w_r=torch.zeros(E, d), w13=torch.zeros(E, P, d, dtype=bf),
+               w2=torch.zeros(E, d, f, dtype=bf), dy=torch.zeros(T, d, dtype=bf),
+               sel_bias=torch.zeros(E))
+    if n_shared:
+        inp["sw13"] = torch.zeros(1, P, d, dtype=bf)
+        inp["sw2"] = torch.zeros(1, d, f, dtype=bf)
+    return inp
+
+
+MODES = [  # (fp8_fwd, fp8_bwd, fp8_scale, fp8_wgrad)
+    (False, False, "row", False), (True, False, "row", False), (True, True, "row", False),
+    (False, True, "row", False), (True, False, "block", False), (True, True, "block", False),
+    (True, True, "row", True), (True, True, "block", True), (False, True, "row", True),
+]
+
+
+@pytest.mark.parametrize("mode,n_shared,act", list(itertools.product(MODES, (0, 1), ("swiglu", "gelu"))))
+def test_layer_step_call_sequence(recorder, mode, n_shared, act):
+    fp8_fwd, fp8_bwd, scale, wgrad = mode
+    T, d, E, k, f = 64, 64, 4, 2, 48
+    P = 2 * f if act == "swiglu" else f
+    L = MoELayer(T, d, E, k, f, n_shared, "bf16", "sigmoid", act, fp8_fwd=fp8_fwd, fp8_bwd=fp8_bwd,
+                 fp8_scale=scale, fp8_wgrad=wgrad, device="cpu")
+    L.step(_inputs(T, d, E, f, P, n_shared))
+    c = recorder.calls
+    assert c[:3] == ["moe_route", "moe_aux_stats", "moe_permute"]
+    fwd = {(False, "row"): "moe_grouped_ffn_fwd", (False, "block"): "moe_grouped_ffn_fwd",
+           (True, "row"): "moe_grouped_ffn_fwd_fp8", (True, "block"): "moe_grouped_ffn_fwd_fp8b"}
+    assert fwd[(fp8_fwd, scale)] in c
+    bwd = "moe_grouped_ffn_bwd_fp8w" if wgrad else ("moe_grouped_ffn_bwd_fp8" if fp8_bwd else
+                                                    "moe_grouped_ffn_bwd")
+    assert c.count(bwd) == 1
+    assert c[-2:] == ["moe_route_bwd", "moe_permute_bwd"]
+    # the block-scaled forward quantizes with block scales only
+    if fp8_fwd and scale == "block":
+        assert "moe_quantize_fp8" not in c and "moe_quantize_fp8_both" not in c
+        assert c.count("moe_quantize_fp8_blocks") == 3 + 3 * n_shared
+
+
+def test_fp8_wgrad_needs_the_fp8_data_gradients():
+    with pytest.raises(ValueError):
+        MoELayer(64, 64, 4, 2, 48, fp8_fwd=True, fp8_wgrad=True, device="cpu")
