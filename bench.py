@@ -191,9 +191,65 @@ STREAM_KERNELS = {"permute": ("perm_count_kernel", "perm_gather_kernel"),
 
 
 def kernel_base_name(name):
-    """'void moe::combine_kernel<unsigned short, 8>(...)' -> 'combine_kernel'."""
-    head = name.split("(")[0].split("<")[0].strip()
+    """'void moe::combine_kernel<unsigned short, 8>(...)' -> 'combine_kernel'
+    (also inside an anonymous namespace)."""
+    head = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0].strip()
     return head.split("::")[-1].split()[-1]
+
+
+def trace_path(workload):
+    return os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+
+
+def summarize_trace(stats_csv, trace_csv, workload, out_path=None):
+    """Text summary of a rocprofv3 --kernel-trace --stats run of this
+    workload's bench (TRACE_COMMAND): every kernel's calls and durations, then
+    the grouped-GEMM launches by role (the library launches them in
+    gemm_roles order once per step), so a role's average duration can be set
+    against the bench's stage of the same name. Writes
+    profiles/kernel_stats_<workload>.txt unless out_path is given."""
+    import csv
+    w = WORKLOADS[workload]
+    stats = sorted(csv.DictReader(open(stats_csv)), key=lambda r: -float(r["TotalDurationNs"]))
+    disp = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    gem = [r for r in disp if "gemm_bf16_kernel" in r["Kernel_Name"] or "gemm_fp8_kernel" in r["Kernel_Name"]
+           or (w.dtype == "fp32" and "gemm_f32_mfma_kernel" in r["Kernel_Name"]
+               and "GemmArgs" in r["Kernel_Name"])]
+    roles = gemm_roles(w)
+    per_role = {}
+    for i, r in enumerate(gem):
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        per_role.setdefault(roles[i % len(roles)], []).append((ns, kernel_base_name(r["Kernel_Name"])))
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/trace -o t "
+           f"--output-format csv -- python3 $R/bench.py --workload {workload} --steps 5 --warmup 2 "
+           "--no-cpu-baseline --no-profile")
+    lines = [f"# rocprofv3 kernel trace summary: MoE layer fwd+bwd, {workload} workload "
+             f"(bench.py --workload {workload}), 2 warmup + 5 timed steps",
+             "# command (on the MI355X, repo root = $R, $OUT = an output directory):",
+             f"#   {cmd}",
+             f"# summarized by: python bench.py --workload {workload} --summarize-trace "
+             "$OUT/trace/t_kernel_stats.csv $OUT/trace/t_kernel_trace.csv", "",
+             "## kernels (from t_kernel_stats.csv, all steps of the run)",
+             " calls     avg_us     min_us     max_us   total_ms    pct  kernel"]
+    for r in stats:
+        lines.append("%6d %10.1f %10.1f %10.1f %10.2f %6.2f  %s" % (
+            int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"]), r["Name"][:110]))
+    if gem:
+        lines += ["", "## grouped-GEMM launches by role (from t_kernel_trace.csv, in launch order per step; "
+                  f"{len(gem)} launches = {len(gem) / len(roles):g} steps x {len(roles)} roles)",
+                  " calls     avg_us     min_us     max_us  role                     kernel"]
+        for role in roles:
+            v = per_role.get(role, [])
+            if not v:
+                continue
+            ds = [ns / 1e3 for ns, _ in v]
+            lines.append("%6d %10.1f %10.1f %10.1f  %-24s %s" % (len(ds), sum(ds) / len(ds), min(ds), max(ds),
+                                                              role, v[0][1]))
+    path = out_path or trace_path(workload)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def summarize_pmc(fetch_csv, write_csv, workload, stats_csv=None):
@@ -507,7 +563,13 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="FETCH_CSV WRITE_CSV [KERNEL_STATS_CSV]: write "
                          "profiles/traffic_<workload>.json from two counter runs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar="CSV",
+                    help="KERNEL_STATS_CSV KERNEL_TRACE_CSV: write profiles/kernel_stats_<workload>.txt "
+                         "from a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
+        return
     if args.summarize_pmc:
         if len(args.summarize_pmc) not in (2, 3):
             ap.error("--summarize-pmc takes FETCH_CSV WRITE_CSV [KERNEL_STATS_CSV]")

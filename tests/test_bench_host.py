@@ -114,3 +114,36 @@ def test_gemm_roofline_picks_the_binding_bound():
     fl, by = bench.gemm_flops(m, 16384), bench.gemm_bytes(m, 16384)
     r = bench.gemm_roofline(m, "gemm_dgrad_up", fl["gemm_dgrad_up"], by["gemm_dgrad_up"], 3.3)
     assert r["bound"] == "mfma" and abs(r["frac"] - fl["gemm_dgrad_up"] / 2.5e15 / 3.3e-3) < 1e-4
+
+
+def test_kernel_base_name_and_trace_summary(tmp_path):
+    assert bench.kernel_base_name("void moe::combine_kernel<unsigned short, 8>(unsigned short const*)") == \
+        "combine_kernel"
+    assert bench.kernel_base_name(
+        "void moe::(anonymous namespace)::gemm_fp8_kernel<0, 1, true>(moe::GemmArgs)") == "gemm_fp8_kernel"
+    w = WORKLOADS["mixtral_fp8_all_bf16"]
+    roles = bench.gemm_roles(w)
+    stats = tmp_path / "s.csv"
+    trace = tmp_path / "t.csv"
+    stats.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+                     '"void moe::(anonymous namespace)::gemm_fp8_kernel<0, 1, true>(moe::GemmArgs)",'
+                     '12,12000,1000,90,900,1100,1\n')
+    rows = ['"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    did = 0
+    for step in range(2):
+        for i, _ in enumerate(roles):
+            did += 1
+            rows.append(f'"KERNEL_DISPATCH",{did},"void moe::(anonymous namespace)::gemm_fp8_kernel<0, 1, true>'
+                        f'(moe::GemmArgs)",{did * 10**6},{did * 10**6 + 1000 * (i + 1)}')
+            did += 1
+            rows.append(f'"KERNEL_DISPATCH",{did},"moe::fill_zero_kernel(unsigned int*)",{did * 10**6},'
+                        f'{did * 10**6 + 5}')
+    trace.write_text("\n".join(rows) + "\n")
+    out = tmp_path / "k.txt"
+    bench.summarize_trace(str(stats), str(trace), w.name, out_path=str(out))
+    text = out.read_text()
+    # each role's launches averaged in launch order (role i took (i + 1) us here)
+    for i, role in enumerate(roles):
+        line = next(ln for ln in text.splitlines() if f" {role} " in ln)
+        assert line.split()[0] == "2" and float(line.split()[1]) == 1.0 * (i + 1)
+    assert "--summarize-trace" in text

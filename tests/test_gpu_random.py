@@ -1,8 +1,8 @@
 """Layer parity on seeded random configurations: expert counts 1-40, top-k up
 to 4, token counts 1-700, widths with K and N tails, SwiGLU or GELU, softmax
 or sigmoid scoring, a shared expert or none, capacity factors from dropping
-most assignments to none, fp32 and bf16, and the FP8 forward and data-gradient
-variants where the widths allow. Every case is compared with the oracle as the
+most assignments to none, fp32 and bf16, and the FP8 variants (per-row or
+block-scaled forward, data gradients, weight gradients) where the widths allow. Every case is compared with the oracle as the
 fixed cases are (tests/test_gpu_layer.py); the draws reach grouped tile counts
 and per-XCD remainders that the fixed cases do not."""
 import numpy as np
@@ -26,17 +26,28 @@ def _draw(i):
     score = str(rng.choice(["softmax", "sigmoid"]))
     cf = [None, 0.5, 1.0, 1.25, 2.0][int(rng.integers(0, 5))]
     fp8 = dtype == "bf16" and d % 16 == 0 and f % 16 == 0 and rng.random() < 0.8
+    n_shared = int(rng.integers(0, 2))
+    sel_bias = score == "sigmoid" and rng.random() < 0.5
+    aux_coef = float(rng.choice([0.0, 0.02]))
+    z_coef = float(rng.choice([0.0, 0.01])) if score == "softmax" else 0.0
+    fp8_bwd = fp8 and rng.random() < 0.6
+    # drawn after the fields above, so the earlier cases keep their draws:
+    # cases from 24 on also pick the block-scaled forward and FP8 weight gradients
+    scale, wgrad = "row", False
+    if 24 <= i < 36:
+        scale = "block" if fp8 and rng.random() < 0.5 else "row"
+        fp8_bwd = fp8_bwd or (fp8 and rng.random() < 0.5)
+        wgrad = fp8_bwd and rng.random() < 0.8
     return Workload(f"rand{i}", T=T, d=d, E=E, k=k, f=f, dtype=dtype, act=act, score=score,
-                    n_shared=int(rng.integers(0, 2)), cf=cf,
-                    sel_bias=score == "sigmoid" and rng.random() < 0.5,
-                    aux_coef=float(rng.choice([0.0, 0.02])),
-                    z_coef=float(rng.choice([0.0, 0.01])) if score == "softmax" else 0.0,
-                    fp8=fp8, fp8_bwd=fp8 and rng.random() < 0.6, seed=i)
+                    n_shared=n_shared, cf=cf, sel_bias=sel_bias, aux_coef=aux_coef, z_coef=z_coef,
+                    fp8=fp8, fp8_bwd=fp8_bwd, fp8_scale=scale, fp8_wgrad=wgrad, seed=i)
 
 
-# 0-23: the sweep; 45: an FP8 forward case with f = 16 where E4M3 boundary
-# steps of H moved O by 4.3% (the case behind the FP8 forward's end-to-end bound)
-@pytest.mark.parametrize("i", list(range(24)) + [45])
+# 0-23: the sweep; 24-35: the sweep with the block-scaled forward and FP8
+# weight gradients in the draw; 45: an FP8 forward case with f = 16 where E4M3
+# boundary steps of H moved O by 4.3% (the case behind the FP8 forward's
+# end-to-end bound)
+@pytest.mark.parametrize("i", list(range(36)) + [45])
 def test_random_layer_parity(i):
     w = _draw(i)
     print(f"[case] random {i} {w}", flush=True)
