@@ -254,28 +254,76 @@ def e4m3_encode(v):
     return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
-def fp8_row_scale_exp(amax):
-    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero row).
-    With amax = m * 2^e0, m in [1, 2), and 448 = 1.75 * 2^8, that is e0 - 8
-    when m <= 1.75 and e0 - 7 otherwise: exact, no division by 448."""
+# The second OCP FP8 format, E5M2 (5 exponent bits, 2 mantissa bits), for the
+# backward's gradient operands as an option (reading: the FP8 recipes' hybrid
+# scheme, E4M3 for weights and activations and E5M2 for gradients; the pages
+# name FP8 training without a format). Same power-of-two scaling rule, with
+# E5M2's largest finite magnitude 57344 = 1.75 * 2^15 in place of 448.
+E5M2_MAX = 57344.0
+
+
+def e5m2_decode(codes):
+    """Value of OCP E5M2 codes: sign bit, 5 exponent bits (bias 15), 2
+    mantissa bits; exponent field 0 holds subnormals m/4 * 2^-14; field 31 is
+    infinity (mantissa 0) or NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = (c & 3).astype(np.float64)
+    mag = np.where(e == 0, m / 4.0 * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(c & 3 == 0, np.inf, np.nan), mag)
+    return sgn * mag
+
+
+def e5m2_encode(v):
+    """Nearest E5M2 code to each value (|v| <= 57344), ties to the even
+    mantissa: the quantum is 2^(floor(log2|v|) - 2) in the normal range and
+    2^-16 below 2^-14, as in e4m3_encode."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E5M2_MAX) or np.any(np.isnan(v)):
+        raise ValueError("e5m2_encode: input outside the finite range")
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, -14)
+    q = np.exp2(e - 2.0)
+    r = np.rint(a / q) * q
+    _, ex2 = np.frexp(r)
+    e2 = ex2 - 1
+    normal = r >= 2.0 ** -14
+    field = np.where(normal, e2 + 15, 0)
+    mant = np.where(normal, r / np.exp2(e2) * 4.0 - 4.0, r / 2.0 ** -16)
+    code = (field << 2) | mant.astype(np.int64)
+    code = np.where(r == 0, 0, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+FP8_FORMATS = {"e4m3": (8, e4m3_encode, e4m3_decode), "e5m2": (15, e5m2_encode, e5m2_decode)}
+
+
+def fp8_row_scale_exp(amax, fmt="e4m3"):
+    """Smallest integer e with amax <= M * 2^e (0 for an all-zero row), M the
+    format's largest finite magnitude, 1.75 * 2^B (B = 8 for E4M3, 15 for
+    E5M2). With amax = m * 2^e0, m in [1, 2), that is e0 - B when m <= 1.75
+    and e0 - B + 1 otherwise: exact, no division by M."""
+    B = FP8_FORMATS[fmt][0]
     amax = np.asarray(amax, dtype=np.float64)
     mant, ex = np.frexp(amax)             # amax = mant * 2^ex, mant in [0.5, 1)
-    e = np.where(2.0 * mant <= 1.75, ex - 9, ex - 8)
+    e = np.where(2.0 * mant <= 1.75, ex - 1 - B, ex - B)
     return np.where(amax == 0, 0, e).astype(np.int64)
 
 
-def quantize_rows_fp8(X):
+def quantize_rows_fp8(X, fmt="e4m3"):
     """Per-row FP8 quantization: codes [n, K] uint8 and scale exponents [n]
-    with X[i] ~= e4m3_decode(codes[i]) * 2^e[i]. Scaling by a power of two is
-    exact, so the only rounding is e4m3_encode's."""
+    with X[i] ~= decode(codes[i]) * 2^e[i] (E4M3 by default, or E5M2).
+    Scaling by a power of two is exact, so the only rounding is the encoder's."""
     X = np.asarray(X, dtype=np.float64)
-    e = fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0))
-    codes = e4m3_encode(X * np.exp2(-e.astype(np.float64))[:, None])
+    e = fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0), fmt)
+    codes = FP8_FORMATS[fmt][1](X * np.exp2(-e.astype(np.float64))[:, None])
     return codes, e
 
 
-def dequantize_rows_fp8(codes, e):
-    return e4m3_decode(codes) * np.exp2(np.asarray(e, dtype=np.float64))[:, None]
+def dequantize_rows_fp8(codes, e, fmt="e4m3"):
+    return FP8_FORMATS[fmt][2](codes) * np.exp2(np.asarray(e, dtype=np.float64))[:, None]
 
 
 def round_bf16(v):
@@ -354,7 +402,7 @@ FP8_BLOCK = 32
 FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -127, 127
 
 
-def quantize_blocks_fp8(X, block=FP8_BLOCK):
+def quantize_blocks_fp8(X, block=FP8_BLOCK, fmt="e4m3"):
     """Per-block FP8 quantization of the rows of X [n, K]: codes [n, K] uint8
     and scale exponents [n, ceil(K / block)] with
     X[i, k] ~= e4m3_decode(codes[i, k]) * 2^e[i, k // block]."""
@@ -365,17 +413,17 @@ def quantize_blocks_fp8(X, block=FP8_BLOCK):
     codes = np.zeros((n, K), dtype=np.uint8)
     for j in range(nb):
         blk = X[:, j * block:(j + 1) * block]
-        ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0)),
+        ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0), fmt),
                      FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX)
         e[:, j] = ej
-        codes[:, j * block:(j + 1) * block] = e4m3_encode(blk * np.exp2(-ej.astype(np.float64))[:, None])
+        codes[:, j * block:(j + 1) * block] = FP8_FORMATS[fmt][1](blk * np.exp2(-ej.astype(np.float64))[:, None])
     return codes, e
 
 
-def dequantize_blocks_fp8(codes, e, block=FP8_BLOCK):
+def dequantize_blocks_fp8(codes, e, block=FP8_BLOCK, fmt="e4m3"):
     e = np.asarray(e, dtype=np.float64)
     K = codes.shape[1]
-    return e4m3_decode(codes) * np.repeat(np.exp2(e), block, axis=1)[:, :K]
+    return FP8_FORMATS[fmt][2](codes) * np.repeat(np.exp2(e), block, axis=1)[:, :K]
 
 
 def quantize_weights_fp8_block(w):
@@ -427,11 +475,12 @@ def quantize_weights_fp8_t(w):
     return dequantize_rows_fp8(*quantize_rows_fp8(np.asarray(w, dtype=np.float64).T))
 
 
-def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act):
+def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act, grad_fmt="e4m3"):
     """expert_backward with its data-gradient GEMMs on FP8 operands. w2td and
     w13td come from quantize_weights_fp8_t(w2) and quantize_weights_fp8_t(w13).
     With bf16 activations, the values that reach a quantizer are the stored
-    bf16 ones: dO, the saved pre-activations a (and b), and dpre.
+    bf16 ones: dO, the saved pre-activations a (and b), and dpre. grad_fmt:
+    the FP8 format of the two gradient operands (dO, dpre), E4M3 or E5M2.
       dH   = deq(q(bf16 dO)) @ w2td^T
       dpre = activation backward of dH on bf16 a (and b)
       dX   = deq(q(bf16 dpre)) @ w13td^T
@@ -439,14 +488,14 @@ def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act):
     Returns (dX, dw13, dw2, dpre) as expert_backward does."""
     H = saved["H"]
     a = round_bf16(saved["a"])
-    dOd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dO)))
+    dOd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dO), grad_fmt), grad_fmt)
     dH = dOd @ w2td.T
     if act == "swiglu":
         b = round_bf16(saved["b"])
         dpre = np.concatenate([dH * b * dsilu(a), dH * silu(a)], axis=1)
     else:
         dpre = dH * dgelu(a)
-    dpd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dpre)))
+    dpd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dpre), grad_fmt), grad_fmt)
     dX = dpd @ w13td.T
     return dX, dpre.T @ X, dO.T @ H, dpre
 
@@ -459,16 +508,18 @@ def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act):
 # tokens of the expert (blocks start at the expert's first row; the last one
 # may be partial), by the block rule of quantize_blocks_fp8 applied to the
 # transposed operands; the values quantized are the stored bf16 ones.
-def expert_wgrad_fp8(X, H, dO, dpre):
+def expert_wgrad_fp8(X, H, dO, dpre, grad_fmt="e4m3"):
     """(dW13, dW2) of one expert with FP8 block-scaled operands along the
     token axis: X [n, d], H [n, f], dO [n, d], dpre [n, 2f|f].
       dW2  = deq(qb(bf16 dO ^T)) @ deq(qb(bf16 H ^T))^T
       dW13 = deq(qb(bf16 dpre ^T)) @ deq(qb(X ^T))^T
     qb: quantize_blocks_fp8 of each row of the transposed operand (a column of
-    the token-major one), blocks of 32 tokens."""
-    def qt(m):
-        return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))
-    return qt(dpre) @ qt(X).T, qt(dO) @ qt(H).T
+    the token-major one), blocks of 32 tokens. grad_fmt: the FP8 format of the
+    gradient operands dO and dpre (X and H are E4M3)."""
+    def qt(m, fmt="e4m3"):
+        mt = round_bf16(np.asarray(m, dtype=np.float64)).T
+        return dequantize_blocks_fp8(*quantize_blocks_fp8(mt, fmt=fmt), fmt=fmt)
+    return qt(dpre, grad_fmt) @ qt(X).T, qt(dO, grad_fmt) @ qt(H).T
 
 
 def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=None, fp8=False):
@@ -500,12 +551,13 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
 
 
 def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=None,
-                         sw2=None, dY=None, fp8_dgrad=False, fp8_wgrad=False):
+                         sw2=None, dY=None, fp8_dgrad=False, fp8_wgrad=False, fp8_grad="e4m3"):
     """Backward of grouped_ffn_forward: per-expert dgrad and wgrad.
     The shared expert's upstream gradient is dY itself (gate 1).
     fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq).
     fp8_wgrad: the weight gradients on FP8 operands (expert_wgrad_fp8, on
-    the expert's own dpre)."""
+    the expert's own dpre). fp8_grad: the FP8 format of the gradient operands
+    of both ("e4m3" or "e5m2")."""
     E = w13.shape[0]
     dX_perm = np.zeros_like(x_perm)
     dw13 = np.zeros_like(w13)
@@ -515,12 +567,12 @@ def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=
     def bwd(X, w13e, w2e, sv, g):
         if fp8_dgrad:
             out = expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),
-                                         quantize_weights_fp8_t(w13e), sv, g, act)
+                                         quantize_weights_fp8_t(w13e), sv, g, act, fp8_grad)
         else:
             out = expert_backward(X, w13e, w2e, sv, g, act)
         if fp8_wgrad:
             dx, _, _, dp = out
-            g13, g2 = expert_wgrad_fp8(X, sv["H"], g, dp)
+            g13, g2 = expert_wgrad_fp8(X, sv["H"], g, dp, fp8_grad)
             out = (dx, g13, g2, dp)
         return out
 
@@ -691,13 +743,14 @@ def layer_forward(x, w_r, w13, w2, k, score="softmax", act="swiglu", cap=None,
 
 
 def layer_backward(fwd, x, w_r, w13, w2, dY, score="softmax", act="swiglu", aux_coef=0.0,
-                   sw13=None, sw2=None, z_coef=0.0, tau=None, fp8_dgrad=False, fp8_wgrad=False):
+                   sw13=None, sw2=None, z_coef=0.0, tau=None, fp8_dgrad=False, fp8_wgrad=False,
+                   fp8_grad="e4m3"):
     """Backward of the layer for upstream dY: combine bwd, grouped FFN bwd,
     router bwd, un-permute."""
     r, p = fwd["router"], fwd["perm"]
     dgate, dO = combine_backward(dY, fwd["O"], r["gates"], p["row_of"])
     g = grouped_ffn_backward(fwd["x_perm"], p["offsets"], w13, w2, fwd["saved"], dO, act, x,
-                             sw13, sw2, dY, fp8_dgrad, fp8_wgrad)
+                             sw13, sw2, dY, fp8_dgrad, fp8_wgrad, fp8_grad)
     rb = router_backward(x, w_r, r["scores"], r["topk_idx"], r["gates"], dgate, score,
                          aux_coef, fwd["stats"]["y"], z_coef, r["logits"], tau)
     dX = permute_backward(g["dx_perm"], p["row_of"], g["dx_shared"], rb["dx_router"])

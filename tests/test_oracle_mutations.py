@@ -134,8 +134,8 @@ MUTANTS = [
      "n = np.floor(a / q + 0.5)",
      [(P.test_e4m3_encode_matches_library_rounding,)]),
     ("FP8 scale exponent one too large at the boundary mantissa",
-     "e = np.where(2.0 * mant <= 1.75, ex - 9, ex - 8)",
-     "e = np.where(2.0 * mant < 1.75, ex - 9, ex - 8)",
+     "e = np.where(2.0 * mant <= 1.75, ex - 1 - B, ex - B)",
+     "e = np.where(2.0 * mant < 1.75, ex - 1 - B, ex - B)",
      [(P.test_fp8_row_scale_is_the_smallest_power_of_two,)]),
     ("data-gradient weights scaled per output channel instead of per input channel",
      "return dequantize_rows_fp8(*quantize_rows_fp8(np.asarray(w, dtype=np.float64).T))",
@@ -146,8 +146,8 @@ MUTANTS = [
      "Hd = dequantize_rows_fp8(*quantize_rows_fp8(H))",
      [(P.test_expert_forward_fp8_brute_force, "swiglu")]),
     ("FP8 block scales: one scale per row instead of per block",
-     "ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0)),",
-     "ej = np.clip(fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0)),",
+     "ej = np.clip(fp8_row_scale_exp(np.abs(blk).max(axis=1, initial=0.0), fmt),",
+     "ej = np.clip(fp8_row_scale_exp(np.abs(X).max(axis=1, initial=0.0), fmt),",
      [(P.test_fp8_blocks_keep_small_blocks_that_a_row_scale_loses,),
       (P.test_fp8_blocks_brute_force_and_partial_last_block,)]),
     ("FP8 block exponent not clipped to the scale range",
@@ -155,13 +155,21 @@ MUTANTS = [
      "FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX = -1000, 1000",
      [(P.test_fp8_block_exponent_is_clipped_to_the_scale_range,)]),
     ("FP8 weight gradients: blocks along each token row instead of along the token axis",
-     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))",
-     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)))).T",
+     "mt = round_bf16(np.asarray(m, dtype=np.float64)).T",
+     "mt = round_bf16(np.asarray(m, dtype=np.float64))",
      [(P.test_expert_wgrad_fp8_brute_force,), (P.test_fp8_wgrad_exact_on_block_exact_columns,)]),
     ("FP8 weight gradients quantize dpre without its bf16 rounding",
-     "return dequantize_blocks_fp8(*quantize_blocks_fp8(round_bf16(np.asarray(m, dtype=np.float64)).T))",
-     "return dequantize_blocks_fp8(*quantize_blocks_fp8(np.asarray(m, dtype=np.float64).T))",
+     "mt = round_bf16(np.asarray(m, dtype=np.float64)).T",
+     "mt = np.asarray(m, dtype=np.float64).T",
      [(P.test_expert_wgrad_fp8_brute_force,)]),
+    ("E5M2 scale taken with E4M3's largest magnitude",
+     'FP8_FORMATS = {"e4m3": (8, e4m3_encode, e4m3_decode), "e5m2": (15, e5m2_encode, e5m2_decode)}',
+     'FP8_FORMATS = {"e4m3": (8, e4m3_encode, e4m3_decode), "e5m2": (8, e5m2_encode, e5m2_decode)}',
+     [(P.test_e5m2_row_scale_is_the_smallest_power_of_two,)]),
+    ("FP8 weight gradients quantize dO in E4M3 whatever the gradient format",
+     "return qt(dpre, grad_fmt) @ qt(X).T, qt(dO, grad_fmt) @ qt(H).T",
+     "return qt(dpre, grad_fmt) @ qt(X).T, qt(dO) @ qt(H).T",
+     [(P.test_expert_wgrad_fp8_e5m2_gradients_brute_force,)]),
 ]
 
 

@@ -319,6 +319,7 @@ FD_VARIANTS = [
 
 @pytest.mark.parametrize("var", FD_VARIANTS)
 def test_gradients_by_central_differences(var):
+    var = dict(var)   # the parametrized dict is shared with other tests
     aux = var.pop("aux_coef")
     # seed chosen so no token sits within 1e-3 of a top-k boundary
     for seed in range(50):
@@ -935,3 +936,117 @@ def test_grouped_backward_fp8_wgrad_is_per_expert():
         # FP8 error of a sum over the expert's rows, relative to its own scale
         err = np.abs(got["dw13"][e] - ref["dw13"][e]).max() / np.abs(ref["dw13"][e]).max()
         assert err < 0.1, (e, err)
+
+
+# ------------------------------------------------ E5M2 gradient operands
+def _torch_e5m2_codes(v):
+    import torch
+    return torch.from_numpy(np.asarray(v, dtype=np.float64)).to(torch.float32) \
+        .to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_e5m2_decode_matches_library_on_every_code():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = O.e5m2_decode(codes)
+    assert (np.isnan(ref) == np.isnan(got)).all() and (np.isinf(ref) == np.isinf(got)).all()
+    fin = ~np.isnan(ref)
+    assert (ref[fin] == got[fin]).all()
+    assert np.nanmax(got[np.isfinite(got)]) == 57344.0 and got[1] == 2.0 ** -16
+
+
+def test_e5m2_encode_matches_library_rounding():
+    """Every finite bf16 value within +-57344, random fp32 values and hand ties,
+    against torch's float32 -> float8_e5m2 cast (round to nearest even)."""
+    u = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    u = u[np.isfinite(u)].astype(np.float64)
+    u = u[np.abs(u) <= 57344]
+    rng = np.random.default_rng(15)
+    r = (rng.standard_normal(20000) * np.exp2(rng.integers(-20, 15, 20000))).astype(np.float32)
+    r = r[np.abs(r) <= 57344].astype(np.float64)
+    for v in (u, r):
+        assert (O.e5m2_encode(v) == _torch_e5m2_codes(v)).all()
+    # ties: 1.125 is halfway between 1.0 (mantissa 0) and 1.25 (mantissa 1) -> 1.0;
+    # 1.375 between 1.25 and 1.5 -> 1.5 (even mantissa 2); 3 * 2^-17 -> 2 * 2^-16
+    assert O.e5m2_encode([1.125, 1.375, 3 * 2.0 ** -17, 2.0 ** -17]).tolist() == [0x3C, 0x3E, 0x02, 0x00]
+    assert O.e5m2_encode([-2.0 ** -18])[0] == 0x80
+
+
+def test_e5m2_row_scale_is_the_smallest_power_of_two():
+    amax = np.array([57344.0, 57345.0, 28672.0, 28673.0, 1.0, 1.75, 1.76, 0.0, 3e-5, 6e8])
+    got = O.fp8_row_scale_exp(amax, "e5m2")
+    for a, e in zip(amax, got):
+        want = 0 if a == 0 else next(x for x in range(-80, 80) if a <= 57344.0 * 2.0 ** x)
+        assert e == want, (a, e, want)
+
+
+def _brute_fp8_rows_e5m2(M):
+    """Dequantized per-row E5M2 by brute force: scale by search, codes by torch's cast."""
+    out = np.zeros_like(M)
+    for i, row in enumerate(M):
+        a = np.abs(row).max()
+        e = 0 if a == 0 else next(x for x in range(-80, 80) if a <= 57344.0 * 2.0 ** x)
+        out[i] = O.e5m2_decode(_torch_e5m2_codes(row / 2.0 ** e)) * 2.0 ** e
+    return out
+
+
+def test_expert_backward_fp8_e5m2_gradients_brute_force():
+    """The FP8 data gradients with E5M2 gradient operands (dO, dpre) against
+    explicit loops over brute-force quantized operands: dO and dpre in E5M2,
+    the transposed weights in E4M3."""
+    rng = np.random.default_rng(19)
+    n, d, f = 4, 32, 16
+    P = 2 * f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 5)
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 4)
+    _, saved = O.expert_forward(X, w13, w2, "swiglu")
+    dO = rng.standard_normal((n, d)) * 0.3
+    dOd = _brute_fp8_rows_e5m2(O.round_bf16(dO))
+    W2t, W13t = _brute_fp8_rows(w2.T.copy()), _brute_fp8_rows(w13.T.copy())
+    dH = np.array([[sum(dOd[t, c] * W2t[j, c] for c in range(d)) for j in range(f)] for t in range(n)])
+    a, b = O.round_bf16(saved["a"]), O.round_bf16(saved["b"])
+    sg = 1 / (1 + np.exp(-a))
+    dpre = np.concatenate([dH * b * sg * (1 + a * (1 - sg)), dH * a * sg], axis=1)
+    dpd = _brute_fp8_rows_e5m2(O.round_bf16(dpre))
+    dX = np.array([[sum(dpd[t, p] * W13t[j, p] for p in range(P)) for j in range(d)] for t in range(n)])
+    gX, _, _, gpre = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2), O.quantize_weights_fp8_t(w13),
+                                              saved, dO, "swiglu", grad_fmt="e5m2")
+    np.testing.assert_allclose(gpre, dpre, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gX, dX, rtol=1e-12, atol=1e-14)
+    # E5M2 keeps one mantissa bit less than E4M3: the two results differ
+    gX4, _, _, _ = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2),
+                                            O.quantize_weights_fp8_t(w13), saved, dO, "swiglu")
+    assert (gX4 != gX).any()
+
+
+def test_expert_wgrad_fp8_e5m2_gradients_brute_force():
+    """FP8 weight gradients with E5M2 gradient columns (dO, dpre) and E4M3
+    activation columns (H, X), blocks of 32 tokens, against explicit loops."""
+    rng = np.random.default_rng(50)
+    n, d, f = 40, 5, 4
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    H = O.round_bf16(rng.standard_normal((n, f)))
+    dO = O.round_bf16(rng.standard_normal((n, d)))
+    dpre = rng.standard_normal((n, 2 * f))
+    for m in (X, H, dO, dpre):
+        m[32:] *= 2.0 ** -12
+
+    def brute_cols(M, e5):
+        out = np.zeros_like(M)
+        for c in range(M.shape[1]):
+            for b0 in range(0, M.shape[0], 32):
+                blk = M[b0:b0 + 32, c]
+                a = np.abs(blk).max()
+                top = 57344.0 if e5 else 448.0
+                e = 0 if a == 0 else next(x for x in range(-200, 200) if a <= top * 2.0 ** x)
+                e = min(max(e, -127), 127)
+                codes = (_torch_e5m2_codes if e5 else _torch_e4m3_codes)(blk / 2.0 ** e)
+                out[b0:b0 + 32, c] = (O.e5m2_decode if e5 else O.e4m3_decode)(codes) * 2.0 ** e
+        return out
+    Xd, Hd = brute_cols(X, False), brute_cols(H, False)
+    dOd, dpd = brute_cols(dO, True), brute_cols(O.round_bf16(dpre), True)
+    g13, g2 = O.expert_wgrad_fp8(X, H, dO, dpre, grad_fmt="e5m2")
+    np.testing.assert_allclose(g2, dOd.T @ Hd, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(g13, dpd.T @ Xd, rtol=1e-12, atol=1e-15)
