@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -65,6 +65,7 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_fn;
 typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_activation;
+typedef enum { MOE_FP8_E4M3 = 0, MOE_FP8_E5M2 = 1 } moe_fp8_format;
 
 /* Layer description (host struct, read during the call only). */
 typedef struct {
@@ -80,6 +81,10 @@ typedef struct {
   float gumbel_tau;  /* noisy-gate temperature ([Balance], section 噪声注入);
                         0 = plain router, > 0 = moe_route takes Gumbel uniforms */
   int64_t capacity;  /* per-expert limit on kept assignments; < 0: no limit */
+  int32_t fp8_grad;  /* moe_fp8_format of the FP8 backward's gradient operands
+                        (dO, dpre): E4M3 (0, the default) or E5M2 (1); the
+                        weights and activations are E4M3 either way */
+  int32_t reserved;  /* 0 */
 } moe_desc;
 
 /* Which call a workspace is for (moe_workspace_size). */
@@ -394,6 +399,10 @@ int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void
  * Each GEMM output element is 2^(e_row + e_channel) * sum_k e4m3 * e4m3,
  * accumulated in float32. The weight gradients dW2 = dO^T H and
  * dW13 = dpre^T X run in bf16 on the bf16 values, as in moe_grouped_ffn_bwd.
+ * With desc->fp8_grad = MOE_FP8_E5M2 the two gradient operands (dO, dpre)
+ * are quantized to OCP E5M2 instead (the same per-row rule with 57344 =
+ * 1.75 * 2^15 in place of 448; the hybrid scheme of FP8 training recipes,
+ * a reading: the pages name no format), against the E4M3 weights.
  * desc->dtype must be MOE_BF16; d and f must be multiples of 16.
  *   w2q_t [E, f, d] uint8, s2_t [E, f] int32    (moe_quantize_fp8_t of w2 [E, d, f])    in
  *   w13q_t [E, d, P] uint8, s13_t [E, d] int32  (moe_quantize_fp8_t of w13 [E, P, d])   in
@@ -422,6 +431,8 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
  * expert's tokens starting on a 128-token step, and runs the block-scaled
  * GEMM over them: each output element is the sum over token blocks of
  * 2^(e_a + e_b) * sum e4m3 * e4m3, accumulated in float32, stored in bf16.
+ * desc->fp8_grad selects the gradient operands' format (dO, dpre) as in
+ * moe_grouped_ffn_bwd_fp8; H and X stay E4M3.
  * Arguments as in moe_grouped_ffn_bwd_fp8.
  *   ws  MOE_OP_FFN_BWD_FP8W bytes (moe_grouped_ffn_bwd_fp8's layout, then
  *       the token-axis codes and scales of the weight gradients' operands:

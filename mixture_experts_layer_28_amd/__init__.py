@@ -16,10 +16,11 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
+MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
  MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD_FP8B,
  MOE_OP_FFN_BWD_FP8W) = range(10)
@@ -42,6 +43,7 @@ class MoeDesc(ctypes.Structure):
         ("k", ctypes.c_int64), ("f", ctypes.c_int64), ("n_shared", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("score", ctypes.c_int32), ("act", ctypes.c_int32),
         ("gumbel_tau", ctypes.c_float), ("capacity", ctypes.c_int64),
+        ("fp8_grad", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -117,8 +119,11 @@ def _check(fn: str, status: int):
 
 
 def make_desc(T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
-              capacity=None, gumbel_tau=0.0) -> MoeDesc:
+              capacity=None, gumbel_tau=0.0, fp8_grad="e4m3") -> MoeDesc:
+    if fp8_grad not in ("e4m3", "e5m2"):
+        raise ValueError(f"fp8_grad must be 'e4m3' or 'e5m2' (got {fp8_grad!r})")
     return MoeDesc(T=T, d=d, E=E, k=k, f=f, n_shared=n_shared,
+                   fp8_grad=MOE_FP8_E5M2 if fp8_grad == "e5m2" else MOE_FP8_E4M3,
                    dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
                    score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
                    act=MOE_SWIGLU if act == "swiglu" else MOE_GELU,

@@ -96,7 +96,9 @@ __device__ __forceinline__ v8i32 join8(int4 lo, int4 hi) {
   return v;
 }
 
-template <int EPI, int RAG, bool BLK>
+// AF: the FP8 format of the A operand (0 = E4M3, 1 = E5M2: the backward's
+// gradient rows); B is always E4M3
+template <int EPI, int RAG, bool BLK, int AF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(GemmArgs p) {
   constexpr int BM = kRows8, BN = kRows8;
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32, NM = MI * NI;
@@ -238,11 +240,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (BLK) {
       constexpr int os = 2 * decltype(SL)::value;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, os, (int)sb_cur[j], os,
+          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, AF, os, (int)sb_cur[j], os,
           (int)sa_cur[i]);
     } else {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
+          join8(fb[j][0], fb[j][1]), join8(fa[i][0], fa[i][1]), acc[i][j], 0, AF, 0, 0, 0, 0);
     }
   };
 
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   });
 }
 
-template <int EPI, int RAG, bool BLK>
+template <int EPI, int RAG, bool BLK, int AF = 0>
 hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
   constexpr int BNo = EPI == EPI_SWIGLU_FWD ? kRows8 / 2 : kRows8;
   const int64_t nt = (p.N + BNo - 1) / BNo;
@@ -517,7 +519,7 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
   // tail split-K: up to tail_cus more items per XCD
   if (RAG == RAG_M && EPI == EPI_STORE && p.tail_ws) nb += 8 * (int64_t)p.tail_cus;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG, BLK>), dim3((unsigned)nb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_fp8_kernel<EPI, RAG, BLK, AF>), dim3((unsigned)nb), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -532,12 +534,27 @@ hipError_t launch_fp8(const GemmArgs& p, hipStream_t s) {
 // Requires K % 16 == 0 (RAG_M, RAG_NONE), 16-byte aligned rows, N % 4 == 0
 // (f % 4 for the fused SwiGLU) and 16-byte aligned scale arrays; the caller
 // checks.
-hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
-  if (!p.a_sexp || !p.b_sexp || p.col_bias) return hipErrorInvalidValue;
+hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s, int a_fmt) {
+  if (!p.a_sexp || !p.b_sexp || p.col_bias || a_fmt < 0 || a_fmt > 1) return hipErrorInvalidValue;
 #define MOE_CASE(E_, R_) \
   if (epi == E_ && rag == R_) return launch_fp8<E_, R_, false>(p, s);
 #define MOE_CASE_BLK(E_, R_) \
   if (epi == E_ && rag == R_) return launch_fp8<E_, R_, true>(p, s);
+#define MOE_CASE_A5(E_, R_, B_) \
+  if (epi == E_ && rag == R_ && (bool)p.blk_scales == B_) return launch_fp8<E_, R_, B_, 1>(p, s);
+  if (a_fmt == 1) {
+    // E5M2 A operand: the backward's gradient rows (data gradients against
+    // the transposed weights, per-row scales) and the weight gradients'
+    // token-axis gradient operand (block scales)
+    MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_M, false)
+    MOE_CASE_A5(EPI_GELU_BWD, RAG_M, false)
+    MOE_CASE_A5(EPI_STORE, RAG_M, false)
+    MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_NONE, false)
+    MOE_CASE_A5(EPI_GELU_BWD, RAG_NONE, false)
+    MOE_CASE_A5(EPI_STORE, RAG_NONE, false)
+    MOE_CASE_A5(EPI_STORE, RAG_K, true)
+    return hipErrorInvalidValue;
+  }
   if (p.blk_scales) {
     // block scales: the forward GEMMs
     MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_M)
@@ -562,6 +579,7 @@ hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s) {
   MOE_CASE(EPI_GELU_BWD, RAG_NONE)
 #undef MOE_CASE
 #undef MOE_CASE_BLK
+#undef MOE_CASE_A5
   return hipErrorInvalidValue;
 }
 

@@ -20,16 +20,17 @@ hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int
                                    const int32_t* valid_rows, void* codes, int64_t ld_q,
                                    uint8_t* scales, hipStream_t st);
 hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
-                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st);
+                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st,
+                                    int fmt = 0);
 hipError_t launch_set_bounds(int32_t* bounds, int32_t lo, int32_t hi, hipStream_t st);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
-hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s);
+hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s, int a_fmt = 0);
 hipError_t launch_quant_fp8_t(const void*, int64_t, int64_t, int64_t, void*, int32_t*, hipStream_t);
 hipError_t launch_quant_fp8_both(const void*, int64_t, int64_t, int64_t, void*, int32_t*, void*,
                                  int32_t*, void*, hipStream_t);
 size_t quant_fp8_both_ws(int64_t, int64_t, int64_t);
 hipError_t launch_quant_fp8(const void*, int64_t, int64_t, int64_t, const int32_t*, void*, int64_t,
-                            int32_t*, hipStream_t);
+                            int32_t*, hipStream_t, int fmt = 0);
 hipError_t gemm_router_logits(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dw(const GemmArgs& p, bool x_bf16, hipStream_t s);
 hipError_t gemm_router_dx(const GemmArgs& p, hipStream_t s);
@@ -188,6 +189,8 @@ int check_desc(const moe_desc* d) {
     return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", d->score);
   if (d->act != MOE_SWIGLU && d->act != MOE_GELU)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", d->act);
+  if (d->fp8_grad != MOE_FP8_E4M3 && d->fp8_grad != MOE_FP8_E5M2)
+    return fail(MOE_ERR_INVALID_ARG, "unknown FP8 gradient format %d", d->fp8_grad);
   if (d->T * d->k >= (int64_t(1) << 31) || d->T * d->E >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k and T*E must be < 2^31");
   {
@@ -1132,6 +1135,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
   const int64_t Rp = wgrad_rp(desc);
+  const int gf = desc->fp8_grad;   // FP8 format of the gradient operands (0 E4M3, 1 E5M2)
   if (fp8w && (std::max(d, P) * Rp >= (int64_t(1) << 31) || std::max(f, d) * Rp >= (int64_t(1) << 31) ||
                !blk_scale_words_fit(std::max(d, P), Rp) || !blk_scale_words_fit(std::max(f, d), Rp)))
     return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients: the token-axis codes exceed 2^31 bytes");
@@ -1179,7 +1183,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     // upstream gradient -> FP8 rows (routed rows beyond offsets[E] skipped)
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s), "fp8 quantize dO"));
+      MOE_TRY(hip_check(launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s, gf), "fp8 quantize dO"));
     }
     // dgrad 1: dH = dO W2 against W2^T in FP8, activation backward in the epilogue
     GemmArgs p = blank();
@@ -1203,12 +1207,12 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     p.max_rows = T * desc->k;
     {
       Scope sc(shared ? K_SH_DGRAD_DOWN : K_DGRAD_DOWN, s);
-      MOE_TRY(hip_check(gemm_fp8(p, epi_b, ragm, s), "fp8 ffn dgrad down matrix"));
+      MOE_TRY(hip_check(gemm_fp8(p, epi_b, ragm, s, gf), "fp8 ffn dgrad down matrix"));
     }
     // the bf16 pre-activation gradient -> FP8 rows
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s), "fp8 quantize dpre"));
+      MOE_TRY(hip_check(launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s, gf), "fp8 quantize dpre"));
     }
     // dgrad 2: dX = dpre W13 against W13^T in FP8
     GemmArgs q = blank();
@@ -1229,7 +1233,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     if (!shared) MOE_TRY(enable_tail(q, tail_w, s));
     {
       Scope sc(shared ? K_SH_DGRAD_UP : K_DGRAD_UP, s);
-      MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, ragm, s), "fp8 ffn dgrad first matrix"));
+      MOE_TRY(hip_check(gemm_fp8(q, EPI_STORE, ragm, s, gf), "fp8 ffn dgrad first matrix"));
     }
     if (fp8w) {
       // weight gradients on token-axis FP8 operands (block scales per 32 of
@@ -1241,16 +1245,16 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
       }
       const int64_t R = shared ? T : T * desc->k;
       const int64_t rp = 128 * ((R + 127) / 128 + G);
-      auto quant_t = [&](const void* src, int64_t C, uint8_t* codes, uint8_t* sc) {
+      auto quant_t = [&](const void* src, int64_t C, uint8_t* codes, uint8_t* sc, int fmt) {
         Scope q(K_QUANT_FP8, s);
-        return hip_check(launch_quant_fp8_tblocks(src, R, C, off, G, ktab, codes, sc, s),
+        return hip_check(launch_quant_fp8_tblocks(src, R, C, off, G, ktab, codes, sc, s, fmt),
                          "fp8 token-axis quantize");
       };
       for (int which = 0; which < 2; ++which) {
         const bool down = which == 0;
         const int64_t M = down ? d : P, N = down ? f : d;
-        MOE_TRY(quant_t(down ? go : dpre, M, qa, qa_s));
-        MOE_TRY(quant_t(down ? hs : xin, N, qb, qb_s));
+        MOE_TRY(quant_t(down ? go : dpre, M, qa, qa_s, gf));   // the gradient operand
+        MOE_TRY(quant_t(down ? hs : xin, N, qb, qb_s, 0));
         GemmArgs r = blank();
         r.a = opnd(qa, rp, 0, 0);
         r.b = opnd(qb, rp, 0, 0);
@@ -1267,7 +1271,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
         r.N = N;
         r.K = R;
         Scope sc(down ? (shared ? K_SH_WGRAD_DOWN : K_WGRAD_DOWN) : (shared ? K_SH_WGRAD_UP : K_WGRAD_UP), s);
-        MOE_TRY(hip_check(gemm_fp8(r, EPI_STORE, RAG_K, s),
+        MOE_TRY(hip_check(gemm_fp8(r, EPI_STORE, RAG_K, s, gf),
                           down ? "fp8 ffn wgrad down matrix" : "fp8 ffn wgrad first matrix"));
       }
       continue;

@@ -4,7 +4,9 @@
 // e_i = the smallest integer with max_k |x[i][k]| <= 448 * 2^e_i (0 for an
 // all-zero row). Multiplying by a power of two is exact, so the conversion
 // instruction's rounding is the only rounding; the codes are a bit-exact
-// function of the input. Inputs must be finite.
+// function of the input. Inputs must be finite. The per-row and token-axis
+// quantizers also write OCP E5M2 (the backward's gradient operands, largest
+// magnitude 1.75 * 2^15 in place of 448).
 //
 // One workgroup of 256 threads per row; each thread keeps up to eight
 // 16-byte chunks of its row in registers between the max pass and the
@@ -34,6 +36,42 @@ __device__ __forceinline__ uint32_t absmax8(uint4 v, uint32_t m) {
   return m;
 }
 
+// FP8 formats: 0 = OCP E4M3 (largest magnitude 1.75 * 2^8), 1 = OCP E5M2
+// (1.75 * 2^15). The scale rule of a maximum amax = mant * 2^ex (mant in
+// [0.5, 1)): the smallest e with amax <= 1.75 * 2^(B + e).
+template <int FMT>
+__device__ __forceinline__ int fp8_scale_exp(uint32_t m_bits, float amax) {
+  constexpr int B = FMT == 1 ? 15 : 8;
+  int ex = 0;
+  const float mant = frexpf(amax, &ex);
+  return m_bits == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 1 - B : ex - B);
+}
+
+// eight bf16 scaled by 2^-e -> eight FP8 codes (byte i = element i), E4M3 or
+// E5M2 (round to nearest even either way)
+template <int FMT = 0>
+__device__ __forceinline__ uint2 to_fp8(uint4 v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float a = ldexpf(bf2f(w[2 * h] & 0xffffu), -e);
+    const float b = ldexpf(bf2f(w[2 * h] >> 16), -e);
+    const float c = ldexpf(bf2f(w[2 * h + 1] & 0xffffu), -e);
+    const float d = ldexpf(bf2f(w[2 * h + 1] >> 16), -e);
+    int r;
+    if constexpr (FMT == 1) {
+      r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+      r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+    } else {
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    }
+    o[h] = (uint32_t)r;
+  }
+  return make_uint2(o[0], o[1]);
+}
+
 // eight bf16 scaled by 2^-e -> eight E4M3 codes (byte i = element i)
 __device__ __forceinline__ uint2 to_e4m3(uint4 v, int e) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -51,6 +89,7 @@ __device__ __forceinline__ uint2 to_e4m3(uint4 v, int e) {
   return make_uint2(o[0], o[1]);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t K, int64_t ld_src, const int32_t* __restrict__ valid_rows,
     uint8_t* __restrict__ codes, int64_t ld_q, int32_t* __restrict__ sexp) {
@@ -81,17 +120,14 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
 #pragma unroll
   for (int w = 1; w < kQThreads / 64; ++w) m = wmax[w] > m ? wmax[w] : m;
   // e: amax = mant * 2^ex (mant in [0.5, 1)); amax <= 1.75 * 2^(8 + e)
-  const float amax = bf2f(m);
-  int ex = 0;
-  const float mant = frexpf(amax, &ex);
-  const int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  const int e = fp8_scale_exp<FMT>(m, bf2f(m));
   if (tid == 0) sexp[row] = e;
 #pragma unroll
   for (int u = 0; u < kQCache; ++u) {
     const int64_t c = tid + (int64_t)u * kQThreads;
-    if (c < nch) q[c] = to_e4m3(cache[u], e);
+    if (c < nch) q[c] = to_fp8<FMT>(cache[u], e);
   }
-  for (int64_t c = tid + (int64_t)kQCache * kQThreads; c < nch; c += kQThreads) q[c] = to_e4m3(s[c], e);
+  for (int64_t c = tid + (int64_t)kQCache * kQThreads; c < nch; c += kQThreads) q[c] = to_fp8<FMT>(s[c], e);
 }
 
 // ---- block scales: one exponent per 32 elements along K
@@ -178,6 +214,7 @@ constexpr int kTBC = 64;   // columns per workgroup of the token-axis quantizer
 // The 128 x 64 tile is staged in LDS row by row (16-byte chunks); thread
 // (b = tid / 64, c = tid % 64) then takes token block b of column c: its
 // maximum, its exponent byte and its 32 codes (two 16-byte stores).
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t C, const int32_t* __restrict__ off, const int32_t* __restrict__ tab,
     uint8_t* __restrict__ codes, int64_t Rp, uint8_t* __restrict__ scales) {
@@ -211,15 +248,13 @@ __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
     m = (lo & 0x7fffu) > m ? (lo & 0x7fffu) : m;
     m = (hi & 0x7fffu) > m ? (hi & 0x7fffu) : m;
   }
-  const float amax = bf2f(m);
-  int ex = 0;
-  const float mant = frexpf(amax, &ex);
-  int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  int e = fp8_scale_exp<FMT>(m, bf2f(m));
   e = e < -127 ? -127 : (e > 127 ? 127 : e);
   const int64_t kw = (int64_t)(off[g] + 127) / 128 + g + kt;   // k-step word of row c
   uint2 o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = to_e4m3(make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]), e);
+  for (int j = 0; j < 4; ++j)
+    o[j] = to_fp8<FMT>(make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]), e);
   uint4* dst = reinterpret_cast<uint4*>(codes + c * Rp + 128 * kw + 32 * b);
   dst[0] = make_uint4(o[0].x, o[0].y, o[1].x, o[1].y);
   dst[1] = make_uint4(o[2].x, o[2].y, o[3].x, o[3].y);
@@ -494,12 +529,17 @@ hipError_t launch_quant_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, 
   return hipGetLastError();
 }
 
+// fmt: 0 = E4M3, 1 = E5M2
 hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                             const int32_t* valid_rows, void* codes, int64_t ld_q, int32_t* sexp,
-                            hipStream_t st) {
+                            hipStream_t st, int fmt) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(kQThreads), 0, st,
-                     (const bf16_t*)src, K, ld_src, valid_rows, (uint8_t*)codes, ld_q, sexp);
+  if (fmt == 1)
+    hipLaunchKernelGGL(quant_rows_fp8_kernel<1>, dim3((unsigned)rows), dim3(kQThreads), 0, st,
+                       (const bf16_t*)src, K, ld_src, valid_rows, (uint8_t*)codes, ld_q, sexp);
+  else
+    hipLaunchKernelGGL(quant_rows_fp8_kernel<0>, dim3((unsigned)rows), dim3(kQThreads), 0, st,
+                       (const bf16_t*)src, K, ld_src, valid_rows, (uint8_t*)codes, ld_q, sexp);
   return hipGetLastError();
 }
 
@@ -507,12 +547,17 @@ hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld
 // its transpose (see quant_tblocks_fp8_kernel). off: G + 1 group bounds on the
 // device; tab: nq = Rp / 128 ints of scratch; Rp = 128 * (ceil(R / 128) + G).
 hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
-                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st) {
+                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st, int fmt) {
   const int64_t Rp = 128 * ((R + 127) / 128 + G), nq = Rp / 128;
   if (R == 0 || C == 0) return hipSuccess;
   hipLaunchKernelGGL(kstep_group_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, off, G, nq, tab);
-  hipLaunchKernelGGL(quant_tblocks_fp8_kernel, dim3((unsigned)((C + kTBC - 1) / kTBC), (unsigned)nq), dim3(256), 0,
-                     st, (const bf16_t*)src, C, off, (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
+  const dim3 grid((unsigned)((C + kTBC - 1) / kTBC), (unsigned)nq);
+  if (fmt == 1)
+    hipLaunchKernelGGL(quant_tblocks_fp8_kernel<1>, grid, dim3(256), 0, st, (const bf16_t*)src, C, off,
+                       (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
+  else
+    hipLaunchKernelGGL(quant_tblocks_fp8_kernel<0>, grid, dim3(256), 0, st, (const bf16_t*)src, C, off,
+                       (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
   return hipGetLastError();
 }
 

@@ -50,14 +50,17 @@ class MoELayer:
     fp8_wgrad (with fp8_bwd) runs the weight gradients on FP8 operands too:
     the library quantizes dO, H, dpre and x_perm along the token axis (one
     scale per 32 of an expert's tokens per column) into their transposes.
+    fp8_grad picks the FP8 format of the backward's gradient operands (dO,
+    dpre): "e4m3" or "e5m2" (weights and activations stay E4M3).
     """
 
     def __init__(self, T, d, E, k, f, n_shared=0, dtype="bf16", score="softmax", act="swiglu",
                  capacity: Optional[int] = None, aux_coef: float = 0.0, z_coef: float = 0.0,
                  bias_gamma: float = 0.0, gumbel_tau: float = 0.0, fp8_fwd: bool = False,
                  fp8_bwd: bool = False, fp8_scale: str = "row", fp8_wgrad: bool = False,
-                 device="cuda"):
-        self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau)
+                 fp8_grad: str = "e4m3", device="cuda"):
+        self.desc = make_desc(T, d, E, k, f, n_shared, dtype, score, act, capacity, gumbel_tau,
+                              fp8_grad)
         self.T, self.d, self.E, self.k, self.f = T, d, E, k, f
         self.n_shared, self.aux_coef, self.z_coef = n_shared, aux_coef, z_coef
         self.bias_gamma = bias_gamma

@@ -72,6 +72,7 @@ class Workload:
     fp8_scale: str = "row"        # the forward's FP8 scales: "row" or "block" (32 along K)
     fp8_bwd: bool = False         # backward data-gradient GEMMs on E4M3 operands as well
     fp8_wgrad: bool = False       # and the weight-gradient GEMMs (token-axis block scales)
+    fp8_grad: str = "e4m3"        # FP8 format of the backward's gradient operands: e4m3 or e5m2
     seed: int = 0
 
     def replace(self, **kw) -> "Workload":
@@ -130,6 +131,10 @@ WORKLOADS = {
     "dsv3_ep8_shard_fp8_all_bf16": Workload("dsv3_ep8_shard_fp8_all_bf16", T=8192, d=7168, E=32,
                                             k=8, f=2048, score="sigmoid", n_shared=1,
                                             sel_bias=True, fp8=True, fp8_bwd=True, fp8_wgrad=True),
+    # and the gradient operands (dO, dpre) in E5M2, the hybrid FP8 scheme
+    "mixtral_fp8_all_e5m2_bf16": Workload("mixtral_fp8_all_e5m2_bf16", T=8192, d=4096, E=8, k=2,
+                                          f=14336, cf=1.25, fp8=True, fp8_bwd=True, fp8_wgrad=True,
+                                          fp8_grad="e5m2"),
 }
 
 

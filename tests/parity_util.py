@@ -65,7 +65,8 @@ def gpu_layer(w: Workload, g: dict):
     cap = moe.capacity(w.T, w.k, w.E, w.cf)
     L = moe.MoELayer(w.T, w.d, w.E, w.k, w.f, w.n_shared, w.dtype, w.score, w.act, cap,
                      w.aux_coef, w.z_coef, w.bias_gamma, w.gumbel_tau or 0.0, fp8_fwd=w.fp8,
-                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale, fp8_wgrad=w.fp8_wgrad)
+                     fp8_bwd=w.fp8_bwd, fp8_scale=w.fp8_scale, fp8_wgrad=w.fp8_wgrad,
+                     fp8_grad=w.fp8_grad)
     dev = {n: to_dev(v) for n, v in g.items()}
     L.step(dev)
     torch.cuda.synchronize()
@@ -80,7 +81,7 @@ def oracle_layer(w: Workload, g: dict):
                           w.gumbel_tau, fp8=oracle_fp8(w))
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
                            w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau,
-                           fp8_dgrad=w.fp8_bwd, fp8_wgrad=w.fp8_wgrad)
+                           fp8_dgrad=w.fp8_bwd, fp8_wgrad=w.fp8_wgrad, fp8_grad=w.fp8_grad)
     return fwd, bwd, f
 
 
@@ -251,13 +252,13 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     # outputs computed from a requantized operand (FP8 data gradients) carry
     # the matrix core's accumulation error amplified by E4M3 rounding: see
     # check_fp8_dgrad for the exact checks and fp8_dgrad_tol for this bound
-    dxt = fp8_dgrad_tol(w.f) if w.fp8_bwd else {}
+    dxt = fp8_dgrad_tol(w.f, w.fp8_grad) if w.fp8_bwd else {}
     assert_close("dX_perm", to_np(L.dx_perm[:A])[g_rows[keep]], bwd["dx_perm"][o_rows[keep]], dt, rep,
                  **dxt)
     gw13, gw2 = to_np(L.dw13), to_np(L.dw2)
     # FP8 weight gradients: see fp8_wgrad_tol (exact stage check in check_fp8_wgrad)
     rows = np.diff(off)
-    wgt = fp8_wgrad_tol(int(rows[rows > 0].min(initial=w.T))) if w.fp8_wgrad else {}
+    wgt = fp8_wgrad_tol(int(rows[rows > 0].min(initial=w.T)), w.fp8_grad) if w.fp8_wgrad else {}
     assert_close("dW13", gw13[e_ok], bwd["dw13"][e_ok], dt, rep, **wgt)
     assert_close("dW2", gw2[e_ok], bwd["dw2"][e_ok], dt, rep, **wgt)
     empty = [e for e in range(E) if off[e + 1] == off[e]]
@@ -265,7 +266,7 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
         assert not gw13[e].any() and not gw2[e].any()
     if w.n_shared:
         assert_close("dX_shared", to_np(L.dx_shared), bwd["dx_shared"], dt, rep, **dxt)
-        swt = fp8_wgrad_tol(w.T) if w.fp8_wgrad else {}
+        swt = fp8_wgrad_tol(w.T, w.fp8_grad) if w.fp8_wgrad else {}
         assert_close("dSW13", to_np(L.dsw13), bwd["dsw13"], dt, rep, **swt)
         assert_close("dSW2", to_np(L.dsw2), bwd["dsw2"], dt, rep, **swt)
     # The router gradient can vanish identically (top-1: the one renormalised
@@ -306,7 +307,11 @@ def fp8_fwd_tol(f):
     return dict(max_rel=max(2e-2, 0.5 / np.sqrt(f)))
 
 
-def fp8_dgrad_tol(f):
+def fp8_dgrad_tol(f, fmt="e4m3"):
+    """E5M2 gradient operands: one E5M2 step is up to 2^-2 of its element,
+    twice E4M3's, so the bound doubles."""
+    if fmt == "e5m2":
+        return dict(max_rel=max(1e-1, 1.0 / np.sqrt(f)), l1_rel=3e-2)
     return dict(max_rel=max(5e-2, 0.5 / np.sqrt(f)), l1_rel=1.5e-2)
 
 
@@ -317,7 +322,9 @@ def fp8_dgrad_tol(f):
 # for the smallest expert's n tokens. dpre also carries the FP8 data gradient's
 # bound. The stage check (check_fp8_wgrad) holds each weight gradient of the
 # GPU's own bf16 operands to the bf16 bound.
-def fp8_wgrad_tol(n):
+def fp8_wgrad_tol(n, fmt="e4m3"):
+    if fmt == "e5m2":
+        return dict(max_rel=max(1e-1, 1.0 / np.sqrt(max(n, 1))), l1_rel=3e-2)
     return dict(max_rel=max(5e-2, 0.5 / np.sqrt(max(n, 1))), l1_rel=1.5e-2)
 
 
@@ -347,15 +354,59 @@ def check_fp8_wgrad(w, L, dev, rep, off):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
             continue
-        g13, g2 = O.expert_wgrad_fp8(X[r0:r1], H[r0:r1], dO[r0:r1], dp[r0:r1])
+        g13, g2 = O.expert_wgrad_fp8(X[r0:r1], H[r0:r1], dO[r0:r1], dp[r0:r1], w.fp8_grad)
         assert_close(f"dW13(own) e{e}", to_np(L.dw13[e]), g13, "bf16", rep)
         assert_close(f"dW2(own) e{e}", to_np(L.dw2[e]), g2, "bf16", rep)
     if w.n_shared:
         off_s = (R * P * 2 + 255) // 256 * 256
         dps = to_np(ws[off_s: off_s + w.T * P * 2].view(torch.bfloat16).view(w.T, P))
-        g13, g2 = O.expert_wgrad_fp8(to_np(dev["x"]), to_np(L.save_h_s), to_np(dev["dy"]), dps)
+        g13, g2 = O.expert_wgrad_fp8(to_np(dev["x"]), to_np(L.save_h_s), to_np(dev["dy"]), dps,
+                                     w.fp8_grad)
         assert_close("dSW13(own)", to_np(L.dsw13[0]), g13, "bf16", rep)
         assert_close("dSW2(own)", to_np(L.dsw2[0]), g2, "bf16", rep)
+
+
+def _fp8_rows_ref(M, fmt="e4m3"):
+    """_e4m3_rows_ref for either FP8 format: the scale by search around
+    log2(amax / M_fmt), the codes by torch's float8_e4m3fn or float8_e5m2 cast."""
+    if fmt == "e4m3":
+        return _e4m3_rows_ref(M)
+    M = np.asarray(M, dtype=np.float64)
+    amax = np.abs(M).max(axis=1, initial=0.0)
+    safe = np.where(amax > 0, amax, 57344.0)
+    e = np.floor(np.log2(safe / 57344.0)).astype(np.int64) - 1
+    for _ in range(3):
+        e = np.where(amax > 57344.0 * np.exp2(e.astype(np.float64)), e + 1, e)
+    e = np.where(amax > 0, e, 0)
+    sc = np.exp2(e.astype(np.float64))[:, None]
+    q = torch.from_numpy(M / sc).to(torch.float32).to(torch.float8_e5m2).to(torch.float64)
+    return q.numpy() * sc
+
+
+def check_grad_codes(w, L, dev, ws, R, P, A, dp, dps):
+    """The FP8 backward's per-row codes and exponents of its gradient
+    operands (the upstream gradient and dpre), read from the workspace it
+    left, against the oracle's quantizer in the chosen format on the same bf16
+    rows."""
+    import mixture_experts_layer_28_amd as moe
+    d = w.d
+    al = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    base = moe.workspace_size(L.desc, moe.MOE_OP_FFN_BWD)
+    raw = ws.cpu().numpy()
+    if dps is not None:
+        rows, g_src, p_src = w.T, to_np(dev["dy"]), dps
+    else:
+        rows, g_src, p_src = A, to_np(L.dout[:A]), dp
+    gq = raw[base: base + R * d].reshape(R, d)[:rows]
+    gs = raw[base + al(R * d): base + al(R * d) + 4 * R].view(np.int32)[:rows]
+    o_pq = base + al(R * d) + al(R * 4)
+    pq = raw[o_pq: o_pq + R * P].reshape(R, P)[:rows]
+    ps = raw[o_pq + al(R * P): o_pq + al(R * P) + 4 * R].view(np.int32)[:rows]
+    for name, q, e, src in (("dO", gq, gs, g_src), ("dpre", pq, ps, p_src)):
+        rc, re_ = O.quantize_rows_fp8(src, w.fp8_grad)
+        assert (e == re_).all(), f"{name} exponents differ ({w.fp8_grad})"
+        bad = np.argwhere(q != rc)
+        assert bad.size == 0, f"{name} {w.fp8_grad} codes differ: {len(bad)}, first {bad[:4].tolist()}"
 
 
 def _e4m3_rows_ref(M):
@@ -409,7 +460,7 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
     for e in range(w.E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi > lo:
-            ref.append(_e4m3_rows_ref(dp[lo:hi]) @ w13t[e].T)
+            ref.append(_fp8_rows_ref(dp[lo:hi], w.fp8_grad) @ w13t[e].T)
             got.append(to_np(L.dx_perm[lo:hi]))
     if got:
         assert_close("dX_perm(own dpre)", np.concatenate(got), np.concatenate(ref), dt, rep)
@@ -418,7 +469,11 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
         dps = to_np(ws[off_s: off_s + w.T * P * 2].view(torch.bfloat16).view(w.T, P))
         assert_close("dpre_shared", dps, bwd["dpre_shared"], dt, rep)
         wst = _decode_codes(L.sw13q_t[0], L.ss13_t[0])
-        assert_close("dX_shared(own dpre)", to_np(L.dx_shared), _e4m3_rows_ref(dps) @ wst.T, dt, rep)
+        assert_close("dX_shared(own dpre)", to_np(L.dx_shared), _fp8_rows_ref(dps, w.fp8_grad) @ wst.T, dt,
+                     rep)
+    # the gradient codes in the workspace, bit for bit (E4M3 or E5M2): the
+    # shared expert's rows overwrite the routed ones when there is one
+    check_grad_codes(w, L, dev, ws, R, P, A, dp, dps if w.n_shared else None)
 
 
 def check_fp8_down_own_h(w, L, f, off, rep):

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -93,6 +93,22 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.moe_bias_update(ctypes.byref(d), FAKE, 1e-3, None, None) == 1
     assert "bias" in L.moe_last_error().decode()
     assert L.moe_bias_update(ctypes.byref(d), FAKE, float("nan"), FAKE, None) == 1
+
+
+def test_fp8_gradient_format_validation():
+    """desc.fp8_grad takes E4M3 (0) or E5M2 (1); anything else fails desc
+    validation before any HIP call."""
+    L = moe.lib()
+    for v, want in ((0, 0), (1, 0), (2, 1), (-1, 1)):
+        d = _desc()
+        d.fp8_grad = v
+        out = ctypes.c_size_t()
+        assert L.moe_workspace_size(ctypes.byref(d), moe.MOE_OP_FFN_BWD_FP8, ctypes.byref(out)) == want
+    with pytest.raises(ValueError):
+        moe.make_desc(64, 64, 8, 2, 64, fp8_grad="e3m4")
+    assert moe.make_desc(64, 64, 8, 2, 64, fp8_grad="e5m2").fp8_grad == moe.MOE_FP8_E5M2
+    # the struct layout the header declares: 6 int64, 3 int32, a float, an int64, 2 int32
+    assert ctypes.sizeof(moe.MoeDesc) == 80 and moe.MoeDesc.fp8_grad.offset == 72
 
 
 def test_noisy_gate_validation():

@@ -105,7 +105,7 @@ def forward_gap(rng, E, n, d, f, block=False):
     return _rel(np.concatenate(got), np.concatenate(ref))
 
 
-def dgrad_gap(rng, E, n, d, f):
+def dgrad_gap(rng, E, n, d, f, fmt="e4m3"):
     """max and L1 relative gap of dX (FP8 data gradients, E experts of n rows)
     between the device emulation and the oracle, on the oracle's own saved
     pre-activations."""
@@ -115,13 +115,13 @@ def dgrad_gap(rng, E, n, d, f):
         dO = _bf16(rng.standard_normal((n, d)))
         _, saved = O.expert_forward(X, w13, w2, "swiglu")
         w2t, w13t = O.quantize_weights_fp8_t(w2), O.quantize_weights_fp8_t(w13)
-        r, _, _, _ = O.expert_backward_fp8_wq(X, w2t, w13t, saved, dO, "swiglu")
+        r, _, _, _ = O.expert_backward_fp8_wq(X, w2t, w13t, saved, dO, "swiglu", fmt)
         a = _bf16(saved["a"]).astype(np.float32)
         b = _bf16(saved["b"]).astype(np.float32)
-        dOd = O.dequantize_rows_fp8(*O.quantize_rows_fp8(dO))
+        dOd = O.dequantize_rows_fp8(*O.quantize_rows_fp8(dO, fmt), fmt)
         dH = _device_matmul(dOd, w2t, rng).astype(np.float32)
         dpre = _bf16(np.concatenate([dH * b * _dsilu32(a), dH * _silu32(a)], axis=1))
-        got.append(O.dequantize_rows_fp8(*O.quantize_rows_fp8(dpre)) @ w13t.T)
+        got.append(O.dequantize_rows_fp8(*O.quantize_rows_fp8(dpre, fmt), fmt) @ w13t.T)
         ref.append(r)
     return _rel(np.concatenate(got), np.concatenate(ref))
 
@@ -134,16 +134,18 @@ SHAPES = [(32, 32, 512, 256), (8, 64, 256, 512), (16, 64, 256, 64), (8, 128, 128
 SEEDS = 3
 
 
-@pytest.mark.parametrize("kind", ["forward", "forward_block", "dgrad"])
+@pytest.mark.parametrize("kind", ["forward", "forward_block", "dgrad", "dgrad_e5m2"])
 def test_fp8_bounds_cover_the_emulated_device(kind):
     """The block-scaled forward is held to the per-row forward's bound: a
     flipped code is one E4M3 step of its element whatever the scale's
     granularity, so the same reasoning gives the same bound."""
     gap = {"forward": forward_gap, "dgrad": dgrad_gap,
-           "forward_block": lambda *a: forward_gap(*a, block=True)}[kind]
+           "forward_block": lambda *a: forward_gap(*a, block=True),
+           "dgrad_e5m2": lambda *a: dgrad_gap(*a, fmt="e5m2")}[kind]
     ratios = []
     for E, n, d, f in SHAPES:
-        tol = fp8_dgrad_tol(f) if kind == "dgrad" else fp8_fwd_tol(f)
+        tol = fp8_dgrad_tol(f, "e5m2" if kind == "dgrad_e5m2" else "e4m3") if kind.startswith("dgrad") \
+            else fp8_fwd_tol(f)
         l1_bound = tol.get("l1_rel", 5e-3)
         for s in range(SEEDS):
             mx, l1 = gap(np.random.default_rng(1000 + s), E, n, d, f)

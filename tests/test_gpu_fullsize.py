@@ -136,16 +136,16 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     # way, and a token row's dO and dpre are quantized on their own.
     def ebwd(X, w13e, w2e, w13t, w2t, sv, dO):
         if w.fp8_bwd:
-            return O.expert_backward_fp8_wq(X, w2t, w13t, sv, dO, w.act)
+            return O.expert_backward_fp8_wq(X, w2t, w13t, sv, dO, w.act, w.fp8_grad)
         return O.expert_backward(X, w13e, w2e, sv, dO, w.act)
 
     def wq_t(m):
         return O.quantize_weights_fp8_t(m) if w.fp8_bwd else None
-    dxt = fp8_dgrad_tol(w.f) if w.fp8_bwd else {}
+    dxt = fp8_dgrad_tol(w.f, w.fp8_grad) if w.fp8_bwd else {}
     # FP8 weight gradients: the bound of the smallest sampled expert's rows
     nrows = [int(pm["offsets"][e + 1] - pm["offsets"][e]) for e in exps]
-    wgt = fp8_wgrad_tol(min([n for n in nrows if n > 0], default=w.T)) if w.fp8_wgrad else {}
-    wgt_s = fp8_wgrad_tol(w.T) if w.fp8_wgrad else {}
+    wgt = fp8_wgrad_tol(min([n for n in nrows if n > 0], default=w.T), w.fp8_grad) if w.fp8_wgrad else {}
+    wgt_s = fp8_wgrad_tol(w.T, w.fp8_grad) if w.fp8_wgrad else {}
     for e in range(E):
         if e not in sampled_e and e not in exps:
             continue
@@ -187,7 +187,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
                                    None if w13t is None else w13t[:, rows13],
                                    None if w2t is None else w2t[J], sv, dOe)
             if w.fp8_wgrad:   # per-column token-axis quantization: columns separate
-                d13, d2 = O.expert_wgrad_fp8(Xe, sv["H"], dOe, dpc)
+                d13, d2 = O.expert_wgrad_fp8(Xe, sv["H"], dOe, dpc, w.fp8_grad)
             dw13_ref.append(d13)
             dw2_ref.append(d2)
             dw13_got.append(to_np(L.dw13[e][torch.as_tensor(rows13, device="cuda")]))
@@ -213,7 +213,7 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
                                None if sw13t is None else sw13t[:, rows13],
                                None if sw2t is None else sw2t[J], sv, dy)
         if w.fp8_wgrad:
-            d13, d2 = O.expert_wgrad_fp8(x, sv["H"], dy, dpc)
+            d13, d2 = O.expert_wgrad_fp8(x, sv["H"], dy, dpc, w.fp8_grad)
         assert_close("dSW13[sampled]", to_np(L.dsw13[0][torch.as_tensor(rows13, device="cuda")]),
                      d13, dt, rep, **wgt_s)
         assert_close("dSW2[sampled]", to_np(L.dsw2[0][:, torch.as_tensor(J, device="cuda")]), d2,

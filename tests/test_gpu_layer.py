@@ -36,6 +36,12 @@ REDUCED = {
     "mixtral_fp8_all_small": WORKLOADS["mixtral_fp8_all_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_all_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
                                                          fp8_bwd=True, fp8_wgrad=True),
+    # and with E5M2 gradient operands (dO, dpre)
+    "mixtral_fp8_all_e5m2_small": WORKLOADS["mixtral_fp8_all_e5m2_bf16"].replace(T=1536, d=512,
+                                                                                f=768),
+    "dsv3_fp8_all_e5m2_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
+                                                              fp8_bwd=True, fp8_wgrad=True,
+                                                              fp8_grad="e5m2"),
     # FP8 forward and FP8 data gradients (weight gradients bf16)
     "mixtral_fp8_dgrad_small": WORKLOADS["mixtral_fp8_dgrad_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_dgrad_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
@@ -120,6 +126,14 @@ EDGE = {
                                    logit_bias={2: 50.0}, fp8=True, fp8_bwd=True, fp8_wgrad=True),
     "fp8b_fwd_fp8_all": Workload("f8bw", T=600, d=256, E=4, k=2, f=384, fp8=True, fp8_bwd=True,
                                  fp8_wgrad=True, fp8_scale="block"),
+    # E5M2 gradient operands: ragged sizes with GELU and a shared expert, and
+    # E5M2 data gradients with bf16 weight gradients after a bf16 forward
+    "ragged_fp8_all_e5m2_gelu_shared": Workload("ragged8e5", T=1000, d=144, E=6, k=3, f=208,
+                                                act="gelu", score="sigmoid", n_shared=1,
+                                                sel_bias=True, fp8=True, fp8_bwd=True,
+                                                fp8_wgrad=True, fp8_grad="e5m2"),
+    "fp8_e5m2_dgrad_only": Workload("dg8e5", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
+                                    fp8_bwd=True, fp8_grad="e5m2"),
 }
 
 

@@ -60,15 +60,19 @@ MODES = [  # (fp8_fwd, fp8_bwd, fp8_scale, fp8_wgrad)
     (False, True, "row", False), (True, False, "block", False), (True, True, "block", False),
     (True, True, "row", True), (True, True, "block", True), (False, True, "row", True),
 ]
+# the gradient format (E4M3, or E5M2 for dO and dpre) only reaches the desc
+GRAD = ["e4m3", "e5m2"]
 
 
-@pytest.mark.parametrize("mode,n_shared,act", list(itertools.product(MODES, (0, 1), ("swiglu", "gelu"))))
-def test_layer_step_call_sequence(recorder, mode, n_shared, act):
+@pytest.mark.parametrize("mode,n_shared,act,grad",
+                         list(itertools.product(MODES, (0, 1), ("swiglu", "gelu"), GRAD)))
+def test_layer_step_call_sequence(recorder, mode, n_shared, act, grad):
     fp8_fwd, fp8_bwd, scale, wgrad = mode
     T, d, E, k, f = 64, 64, 4, 2, 48
     P = 2 * f if act == "swiglu" else f
     L = MoELayer(T, d, E, k, f, n_shared, "bf16", "sigmoid", act, fp8_fwd=fp8_fwd, fp8_bwd=fp8_bwd,
-                 fp8_scale=scale, fp8_wgrad=wgrad, device="cpu")
+                 fp8_scale=scale, fp8_wgrad=wgrad, fp8_grad=grad, device="cpu")
+    assert L.desc.fp8_grad == (1 if grad == "e5m2" else 0)
     L.step(_inputs(T, d, E, f, P, n_shared))
     c = recorder.calls
     assert c[:3] == ["moe_route", "moe_aux_stats", "moe_permute"]
