@@ -13,6 +13,7 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
                     (one scale per 32 elements along K)
   mixtral_fp8_all_bf16 every GEMM on FP8 operands (weight gradients with
                     token-axis block scales)
+  mixtral_fp8_all_e5m2_bf16 the same with E5M2 gradient operands
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -258,7 +259,8 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
                                   "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16",
-                                  "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16", "mixtral_fp8_all_bf16"])
+                                  "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16", "mixtral_fp8_all_bf16",
+                                  "mixtral_fp8_all_e5m2_bf16"])
 def test_fullsize_sampled(name):
     w = WORKLOADS[name]
     # the oracle's FP8 backward quantizes each sampled expert's weights both
