@@ -150,22 +150,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto word0 = [&](int64_t r) __attribute__((always_inline)) {
     return (uint32_t)(((r >> 5) * KWrow) * 32 + (r & 31));
   };
-  uint32_t sa_off[BLK ? MI : 1], sb_off[BLK ? NI : 1];
+  // Per lane, the word of its block-0 row and how many of its 32-row blocks
+  // lie inside the operand: block i's row is 32 i below block 0's, so its
+  // word is 32 i * KWrow further on; blocks past the operand read a fixed
+  // in-range row's word (A: the last row, B: the group's first). A few VALU
+  // operations per load instead of one register per block. The fused SwiGLU
+  // B rows (gate and up halves) keep one offset per block.
+  const uint32_t KW32 = (uint32_t)(KWrow * 32);
+  uint32_t sa_w0 = 0, sa_last = 0, sb_w0 = 0, sb_last = 0;
+  int sa_nv = 0, sb_nv = 0;
+  uint32_t sb_off[BLK && FUSED ? NI : 1];
   uint32_t sa_nxt[BLK ? MI : 1], sb_nxt[BLK ? NI : 1], sa_cur[BLK ? MI : 1], sb_cur[BLK ? NI : 1];
   if constexpr (BLK) {
+    const int64_t arow0 = RAG == RAG_K ? 0 : (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M);
+    const int64_t m0l = t.m0 + wm0 + (lane & 31);
+    sa_w0 = word0(arow0 + m0l);
+    sa_last = word0(arow0 + t.M - 1);
+    sa_nv = m0l < t.M ? (int)((t.M - m0l + 31) / 32) : 0;
+    const int64_t brow0 = (int64_t)t.g * p.b_sexp_gstride;
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int64_t m = t.m0 + wm0 + 32 * i + (lane & 31);
-      const int64_t arow0 = RAG == RAG_K ? 0 : (p.a.rowidx ? t.r0 : (int64_t)t.g * p.M);
-      sa_off[i] = word0(arow0 + (m < t.M ? m : t.M - 1));
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int r = wn0 + 32 * j + (lane & 31);
-      int64_t n;
-      if (FUSED) n = fused_row(r, WN, t.n0, p.fdim);
-      else n = t.n0 + r < p.N ? t.n0 + r : -1;
-      sb_off[j] = word0((int64_t)t.g * p.b_sexp_gstride + (n < 0 ? 0 : n));
+      for (int j = 0; j < NI; ++j) {
+        const int64_t n = fused_row(wn0 + 32 * j + (lane & 31), WN, t.n0, p.fdim);
+        sb_off[j] = word0(brow0 + (n < 0 ? 0 : n));
+      }
+    } else {
+      const int64_t n0l = t.n0 + wn0 + (lane & 31);
+      sb_w0 = word0(brow0 + n0l);
+      sb_last = word0(brow0);
+      sb_nv = n0l < p.N ? (int)((p.N - n0l + 31) / 32) : 0;
     }
   }
 
@@ -193,9 +206,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int64_t kg0 = kbase + kt;
       const uint32_t kg = 32 * (uint32_t)(kpos / kBK8 + (kg0 < KW ? kg0 : KW - 1));
 #pragma unroll
-      for (int i = 0; i < MI; ++i) sa_nxt[i] = swa[sa_off[i] + kg];
+      for (int i = 0; i < MI; ++i) sa_nxt[i] = swa[(i < sa_nv ? sa_w0 + i * KW32 : sa_last) + kg];
 #pragma unroll
-      for (int j = 0; j < NI; ++j) sb_nxt[j] = swb[sb_off[j] + kg];
+      for (int j = 0; j < NI; ++j) {
+        uint32_t o;
+        if constexpr (FUSED) o = sb_off[j];
+        else o = j < sb_nv ? sb_w0 + j * KW32 : sb_last;
+        sb_nxt[j] = swb[o + kg];
+      }
     }
   };
   auto take_scales = [&]() __attribute__((always_inline)) {
