@@ -252,6 +252,47 @@ def summarize_trace(stats_csv, trace_csv, workload, out_path=None):
     print(path)
 
 
+MFMA_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES "
+                "GRBM_GUI_ACTIVE -d $OUT/pmc_mfma_<workload> -o m --output-format csv -- python3 "
+                "$R/bench.py --workload <workload> --steps 2 --warmup 1 --no-cpu-baseline --no-profile")
+
+
+def summarize_mfma(out_path, pairs):
+    """MFMA busy share and shader clock of each grouped-GEMM launch of the last
+    step, from one rocprofv3 --pmc run per workload (MFMA_COMMAND); pairs =
+    [(workload, counter_csv), ...]. MfmaUtil is rocprofv3's derived counter
+    (sum of SQ_VALU_MFMA_BUSY_CYCLES over max GRBM_GUI_ACTIVE times the SIMD
+    count, in %); the clock is GRBM_GUI_ACTIVE summed over the 8 XCDs / 8 / the
+    dispatch's duration."""
+    import csv
+    lines = ["# MFMA busy share and clock per grouped-GEMM launch (rocprofv3 derived counter MfmaUtil =",
+             "#   sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD count) * 100; clock = GRBM_GUI_ACTIVE",
+             "#   (summed over the 8 XCDs) / 8 / the dispatch's duration from the same record)",
+             "# command (on the MI355X, repo root = $R, $OUT = an output directory), once per workload:",
+             f"#   {MFMA_COMMAND}",
+             "# summarized by: python bench.py --summarize-mfma OUT.txt <workload> $OUT/pmc_mfma_<workload>/"
+             "m_counter_collection.csv ...",
+             "# last step's grouped-GEMM launches, in launch order"]
+    for workload, path in pairs:
+        by = {}
+        for r in csv.DictReader(open(path)):
+            by.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = r
+        gem = [by[k] for k in sorted(by)
+               if "GRBM_GUI_ACTIVE" in by[k] and ("gemm_bf16_kernel" in by[k]["GRBM_GUI_ACTIVE"]["Kernel_Name"]
+                                                 or "gemm_fp8_kernel" in by[k]["GRBM_GUI_ACTIVE"]["Kernel_Name"])]
+        roles = gemm_roles(WORKLOADS[workload])
+        last = gem[-len(roles):]
+        lines += ["", f"## {workload}", "launch                 MfmaUtil %   clock MHz   duration us"]
+        for role, d in zip(roles, last):
+            g = d["GRBM_GUI_ACTIVE"]
+            dur = (int(g["End_Timestamp"]) - int(g["Start_Timestamp"])) / 1e3
+            clk = float(g["Counter_Value"]) / 8 / (dur * 1e-6) / 1e6
+            lines.append("%-22s %10.1f %11.0f %13.1f" % (role, float(d["MfmaUtil"]["Counter_Value"]), clk, dur))
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out_path)
+
+
 def summarize_pmc(fetch_csv, write_csv, workload, stats_csv=None):
     """HBM bytes per launch of each grouped-GEMM role and streaming stage from
     two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
@@ -566,7 +607,16 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar="CSV",
                     help="KERNEL_STATS_CSV KERNEL_TRACE_CSV: write profiles/kernel_stats_<workload>.txt "
                          "from a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="ARG",
+                    help="OUT_TXT WORKLOAD CSV [WORKLOAD CSV ...]: MFMA busy share per grouped-GEMM "
+                         "launch from rocprofv3 --pmc MfmaUtil runs, and exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        sm = args.summarize_mfma
+        if len(sm) < 3 or len(sm) % 2 == 0:
+            ap.error("--summarize-mfma takes OUT_TXT followed by WORKLOAD CSV pairs")
+        summarize_mfma(sm[0], list(zip(sm[1::2], sm[2::2])))
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
         return
