@@ -134,6 +134,12 @@ EDGE = {
                                                 fp8_wgrad=True, fp8_grad="e5m2"),
     "fp8_e5m2_dgrad_only": Workload("dg8e5", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
                                     fp8_bwd=True, fp8_grad="e5m2"),
+    # the 1024-expert limit with every FP8 mode at once (block-scaled forward,
+    # FP8 data and weight gradients: a 1024-group k-step table), and one token
+    "max_experts_fp8_all": Workload("e1024f8", T=640, d=64, E=1024, k=4, f=64, aux_coef=0.01,
+                                    fp8=True, fp8_bwd=True, fp8_wgrad=True, fp8_scale="block"),
+    "one_token_fp8_all": Workload("t1f8", T=1, d=128, E=4, k=2, f=96, n_shared=1, fp8=True,
+                                  fp8_bwd=True, fp8_wgrad=True, fp8_grad="e5m2"),
 }
 
 
