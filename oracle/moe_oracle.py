@@ -462,6 +462,59 @@ def expert_forward_fp8_block_wq(X, w13d, w2d, act):
     return Hd @ w2d.T, saved
 
 
+# --------------------------------------- FP8 weights in square blocks
+# [Recipe] §8.1/§9.1 (FP8 training, bf16 activations) fix no granularity for
+# the weights either. Reading taken for the square mode: every weight matrix
+# is quantized once per step in FP8_SQUARE x FP8_SQUARE squares of the stored
+# matrix (rows x columns, from its first row and column; the last ones may be
+# partial), each square with one power-of-two scale chosen by the block rule
+# of quantize_blocks_fp8 on the square's maximum. A square is a block along
+# either dimension, so the one dequantized weight serves the forward (read
+# along its input dimension) and the data gradients (read along its output
+# dimension). Activations and gradients entering a GEMM keep 1 x 32 blocks
+# along that GEMM's reduction axis (quantize_blocks_fp8).
+FP8_SQUARE = 32
+
+
+def quantize_squares_fp8(W, block=FP8_SQUARE, fmt="e4m3"):
+    """Square-block FP8 quantization of W [R, C]: codes [R, C] uint8 and
+    scale exponents [ceil(R / block), ceil(C / block)] with
+    W[i, j] ~= decode(codes[i, j]) * 2^e[i // block, j // block]."""
+    W = np.asarray(W, dtype=np.float64)
+    R, C = W.shape
+    nr, nc = -(-R // block), -(-C // block)
+    e = np.zeros((nr, nc), dtype=np.int64)
+    codes = np.zeros((R, C), dtype=np.uint8)
+    for i in range(nr):
+        for j in range(nc):
+            rs, cs = slice(i * block, (i + 1) * block), slice(j * block, (j + 1) * block)
+            sq = W[rs, cs]
+            eij = int(np.clip(fp8_row_scale_exp(np.abs(sq).max(initial=0.0), fmt),
+                              FP8_BLOCK_EXP_MIN, FP8_BLOCK_EXP_MAX))
+            e[i, j] = eij
+            codes[rs, cs] = FP8_FORMATS[fmt][1](sq * 2.0 ** -eij)
+    return codes, e
+
+
+def dequantize_squares_fp8(codes, e, block=FP8_SQUARE, fmt="e4m3"):
+    R, C = codes.shape
+    s = np.exp2(np.asarray(e, dtype=np.float64))
+    s = np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:R, :C]
+    return FP8_FORMATS[fmt][2](codes) * s
+
+
+def quantize_weights_fp8_square(w):
+    """Dequantized square-block FP8 copy of a weight matrix (same shape)."""
+    return dequantize_squares_fp8(*quantize_squares_fp8(w))
+
+
+def expert_forward_fp8_square(X, w13, w2, act):
+    """expert_forward_fp8_block with square-block weights: X and the bf16 H
+    in 1 x 32 blocks along their rows, w13 and w2 in 32 x 32 squares."""
+    return expert_forward_fp8_block_wq(X, quantize_weights_fp8_square(w13),
+                                       quantize_weights_fp8_square(w2), act)
+
+
 # ------------------------------------------------------------ FP8 backward
 # [Megatron10x] §5.2 trains in FP8 mixed precision and [Recipe] §8.1/§9.1 list
 # FP8 training with bf16 activations; which backward GEMMs run in FP8 is not
@@ -475,28 +528,35 @@ def quantize_weights_fp8_t(w):
     return dequantize_rows_fp8(*quantize_rows_fp8(np.asarray(w, dtype=np.float64).T))
 
 
-def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act, grad_fmt="e4m3"):
+def expert_backward_fp8_wq(X, w2td, w13td, saved, dO, act, grad_fmt="e4m3", grad_scale="row"):
     """expert_backward with its data-gradient GEMMs on FP8 operands. w2td and
-    w13td come from quantize_weights_fp8_t(w2) and quantize_weights_fp8_t(w13).
+    w13td come from quantize_weights_fp8_t(w2) and quantize_weights_fp8_t(w13)
+    (per-row mode), or are the transposes of quantize_weights_fp8_square(w2)
+    and quantize_weights_fp8_square(w13) (square mode).
     With bf16 activations, the values that reach a quantizer are the stored
     bf16 ones: dO, the saved pre-activations a (and b), and dpre. grad_fmt:
-    the FP8 format of the two gradient operands (dO, dpre), E4M3 or E5M2.
+    the FP8 format of the two gradient operands (dO, dpre), E4M3 or E5M2;
+    grad_scale: "row" quantizes them per row, "block" per 1 x 32 block of
+    their rows (the square mode).
       dH   = deq(q(bf16 dO)) @ w2td^T
       dpre = activation backward of dH on bf16 a (and b)
       dX   = deq(q(bf16 dpre)) @ w13td^T
       dW2  = dO^T H,  dW13 = dpre^T X        (unquantized)
     Returns (dX, dw13, dw2, dpre) as expert_backward does."""
+    def qg(m):
+        m = round_bf16(m)
+        if grad_scale == "block":
+            return dequantize_blocks_fp8(*quantize_blocks_fp8(m, fmt=grad_fmt), fmt=grad_fmt)
+        return dequantize_rows_fp8(*quantize_rows_fp8(m, grad_fmt), grad_fmt)
     H = saved["H"]
     a = round_bf16(saved["a"])
-    dOd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dO), grad_fmt), grad_fmt)
-    dH = dOd @ w2td.T
+    dH = qg(dO) @ w2td.T
     if act == "swiglu":
         b = round_bf16(saved["b"])
         dpre = np.concatenate([dH * b * dsilu(a), dH * silu(a)], axis=1)
     else:
         dpre = dH * dgelu(a)
-    dpd = dequantize_rows_fp8(*quantize_rows_fp8(round_bf16(dpre), grad_fmt), grad_fmt)
-    dX = dpd @ w13td.T
+    dX = qg(dpre) @ w13td.T
     return dX, dpre.T @ X, dO.T @ H, dpre
 
 
@@ -528,8 +588,10 @@ def grouped_ffn_forward(x_perm, offsets, w13, w2, act, x=None, sw13=None, sw2=No
     ([Recipe] §2.3 / §9.1: an expert every token passes through) read all of
     x. Returns (O [A,d], Os [T,d] or None, saved). fp8=True runs every
     expert (shared ones included) through expert_forward_fp8 (per-row
-    scales), fp8="block" through expert_forward_fp8_block."""
-    fwd = expert_forward_fp8_block if fp8 == "block" else (expert_forward_fp8 if fp8 else expert_forward)
+    scales), fp8="block" through expert_forward_fp8_block, fp8="square"
+    through expert_forward_fp8_square."""
+    fwd = {"block": expert_forward_fp8_block, "square": expert_forward_fp8_square}.get(
+        fp8, expert_forward_fp8 if fp8 else expert_forward)
     E = w13.shape[0]
     A = int(offsets[E])
     d = w2.shape[1]
@@ -554,7 +616,9 @@ def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=
                          sw2=None, dY=None, fp8_dgrad=False, fp8_wgrad=False, fp8_grad="e4m3"):
     """Backward of grouped_ffn_forward: per-expert dgrad and wgrad.
     The shared expert's upstream gradient is dY itself (gate 1).
-    fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq).
+    fp8_dgrad: the data gradients on FP8 operands (expert_backward_fp8_wq):
+    True with per-row scales, "square" with square-block weights and 1 x 32
+    block gradients.
     fp8_wgrad: the weight gradients on FP8 operands (expert_wgrad_fp8, on
     the expert's own dpre). fp8_grad: the FP8 format of the gradient operands
     of both ("e4m3" or "e5m2")."""
@@ -565,7 +629,11 @@ def grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, act, x=None, sw13=
     dpre_r = np.zeros((x_perm.shape[0], w13.shape[1]))
 
     def bwd(X, w13e, w2e, sv, g):
-        if fp8_dgrad:
+        if fp8_dgrad == "square":
+            out = expert_backward_fp8_wq(X, quantize_weights_fp8_square(w2e).T,
+                                         quantize_weights_fp8_square(w13e).T, sv, g, act, fp8_grad,
+                                         "block")
+        elif fp8_dgrad:
             out = expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),
                                          quantize_weights_fp8_t(w13e), sv, g, act, fp8_grad)
         else:

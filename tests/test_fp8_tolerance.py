@@ -87,12 +87,15 @@ def _q_blocks(m):
     return O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m))
 
 
-def forward_gap(rng, E, n, d, f, block=False):
+def forward_gap(rng, E, n, d, f, block=False, square=False):
     """max and L1 relative gap of the routed O (E experts of n rows) between
     the device emulation and the oracle's FP8 forward (per-row scales, or
-    one scale per 32 elements along K with block=True)."""
+    one scale per 32 elements along K with block=True, and 32 x 32 weight
+    squares with square=True)."""
     q, qw = (_q_blocks, O.quantize_weights_fp8_block) if block else (_q_rows, O.quantize_weights_fp8)
-    efwd = O.expert_forward_fp8_block_wq if block else O.expert_forward_fp8_wq
+    if square:
+        q, qw = _q_blocks, O.quantize_weights_fp8_square
+    efwd = O.expert_forward_fp8_block_wq if block or square else O.expert_forward_fp8_wq
     got, ref = [], []
     for _ in range(E):
         X, w13, w2 = _draw(rng, n, d, f)
@@ -105,23 +108,31 @@ def forward_gap(rng, E, n, d, f, block=False):
     return _rel(np.concatenate(got), np.concatenate(ref))
 
 
-def dgrad_gap(rng, E, n, d, f, fmt="e4m3"):
+def dgrad_gap(rng, E, n, d, f, fmt="e4m3", square=False):
     """max and L1 relative gap of dX (FP8 data gradients, E experts of n rows)
     between the device emulation and the oracle, on the oracle's own saved
-    pre-activations."""
+    pre-activations (per-row scales, or with square=True 32 x 32 weight squares
+    and 1 x 32 gradient blocks)."""
+    def qg(m):
+        if square:
+            return O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m, fmt=fmt), fmt=fmt)
+        return O.dequantize_rows_fp8(*O.quantize_rows_fp8(m, fmt), fmt)
     got, ref = [], []
     for _ in range(E):
         X, w13, w2 = _draw(rng, n, d, f)
         dO = _bf16(rng.standard_normal((n, d)))
         _, saved = O.expert_forward(X, w13, w2, "swiglu")
-        w2t, w13t = O.quantize_weights_fp8_t(w2), O.quantize_weights_fp8_t(w13)
-        r, _, _, _ = O.expert_backward_fp8_wq(X, w2t, w13t, saved, dO, "swiglu", fmt)
+        if square:
+            w2t, w13t = O.quantize_weights_fp8_square(w2).T, O.quantize_weights_fp8_square(w13).T
+        else:
+            w2t, w13t = O.quantize_weights_fp8_t(w2), O.quantize_weights_fp8_t(w13)
+        r, _, _, _ = O.expert_backward_fp8_wq(X, w2t, w13t, saved, dO, "swiglu", fmt,
+                                              "block" if square else "row")
         a = _bf16(saved["a"]).astype(np.float32)
         b = _bf16(saved["b"]).astype(np.float32)
-        dOd = O.dequantize_rows_fp8(*O.quantize_rows_fp8(dO, fmt), fmt)
-        dH = _device_matmul(dOd, w2t, rng).astype(np.float32)
+        dH = _device_matmul(qg(dO), w2t, rng).astype(np.float32)
         dpre = _bf16(np.concatenate([dH * b * _dsilu32(a), dH * _silu32(a)], axis=1))
-        got.append(O.dequantize_rows_fp8(*O.quantize_rows_fp8(dpre, fmt), fmt) @ w13t.T)
+        got.append(qg(dpre) @ w13t.T)
         ref.append(r)
     return _rel(np.concatenate(got), np.concatenate(ref))
 
@@ -134,17 +145,21 @@ SHAPES = [(32, 32, 512, 256), (8, 64, 256, 512), (16, 64, 256, 64), (8, 128, 128
 SEEDS = 3
 
 
-@pytest.mark.parametrize("kind", ["forward", "forward_block", "dgrad", "dgrad_e5m2"])
+@pytest.mark.parametrize("kind", ["forward", "forward_block", "forward_square", "dgrad", "dgrad_e5m2",
+                                  "dgrad_square", "dgrad_square_e5m2"])
 def test_fp8_bounds_cover_the_emulated_device(kind):
-    """The block-scaled forward is held to the per-row forward's bound: a
+    """The block- and square-scaled modes are held to the per-row bounds: a
     flipped code is one E4M3 step of its element whatever the scale's
     granularity, so the same reasoning gives the same bound."""
     gap = {"forward": forward_gap, "dgrad": dgrad_gap,
            "forward_block": lambda *a: forward_gap(*a, block=True),
-           "dgrad_e5m2": lambda *a: dgrad_gap(*a, fmt="e5m2")}[kind]
+           "forward_square": lambda *a: forward_gap(*a, square=True),
+           "dgrad_e5m2": lambda *a: dgrad_gap(*a, fmt="e5m2"),
+           "dgrad_square": lambda *a: dgrad_gap(*a, square=True),
+           "dgrad_square_e5m2": lambda *a: dgrad_gap(*a, fmt="e5m2", square=True)}[kind]
     ratios = []
     for E, n, d, f in SHAPES:
-        tol = fp8_dgrad_tol(f, "e5m2" if kind == "dgrad_e5m2" else "e4m3") if kind.startswith("dgrad") \
+        tol = fp8_dgrad_tol(f, "e5m2" if kind.endswith("e5m2") else "e4m3") if kind.startswith("dgrad") \
             else fp8_fwd_tol(f)
         l1_bound = tol.get("l1_rel", 5e-3)
         for s in range(SEEDS):

@@ -170,6 +170,22 @@ MUTANTS = [
      "return qt(dpre, grad_fmt) @ qt(X).T, qt(dO, grad_fmt) @ qt(H).T",
      "return qt(dpre, grad_fmt) @ qt(X).T, qt(dO) @ qt(H).T",
      [(P.test_expert_wgrad_fp8_e5m2_gradients_brute_force,)]),
+    ("FP8 squares: each row of a square scaled on its own",
+     "eij = int(np.clip(fp8_row_scale_exp(np.abs(sq).max(initial=0.0), fmt),",
+     "eij = int(np.clip(fp8_row_scale_exp(np.abs(sq[:1]).max(initial=0.0), fmt),",
+     [(P.test_fp8_squares_brute_force_with_partial_edges,),
+      (P.test_fp8_squares_share_one_scale_down_the_rows,)]),
+    ("FP8 squares: exponents laid out transposed",
+     "s = np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:R, :C]",
+     "s = np.repeat(np.repeat(s.T, block, axis=0), block, axis=1)[:R, :C]",
+     [(P.test_fp8_squares_brute_force_with_partial_edges,)]),
+    ("square-mode data gradients quantize the gradients per row",
+     'if grad_scale == "block":', 'if grad_scale == "blocks":',
+     [(P.test_expert_backward_fp8_square_brute_force, "swiglu", False)]),
+    ("square-mode data gradients read the weights along their input dimension",
+     "out = expert_backward_fp8_wq(X, quantize_weights_fp8_square(w2e).T,",
+     "out = expert_backward_fp8_wq(X, quantize_weights_fp8_t(w2e),",
+     [(P.test_grouped_square_mode_is_per_expert,)]),
 ]
 
 

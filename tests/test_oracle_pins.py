@@ -1050,3 +1050,217 @@ def test_expert_wgrad_fp8_e5m2_gradients_brute_force():
     g13, g2 = O.expert_wgrad_fp8(X, H, dO, dpre, grad_fmt="e5m2")
     np.testing.assert_allclose(g2, dOd.T @ Hd, rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(g13, dpd.T @ Xd, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------ FP8 square-block weights
+def _brute_fp8_squares(M, block=32):
+    """Dequantized square-block FP8 by brute force: per block x block square
+    (edges partial), the largest magnitude by explicit loops, the exponent by
+    search (clipped to [-127, 127]), codes by torch's own E4M3 cast."""
+    R, C = M.shape
+    out = np.zeros_like(M)
+    for i0 in range(0, R, block):
+        for j0 in range(0, C, block):
+            a = 0.0
+            for i in range(i0, min(i0 + block, R)):
+                for j in range(j0, min(j0 + block, C)):
+                    a = max(a, abs(M[i, j]))
+            e = 0 if a == 0 else next(x for x in range(-200, 200) if a <= 448.0 * 2.0 ** x)
+            e = min(max(e, -127), 127)
+            sq = M[i0:i0 + block, j0:j0 + block]
+            out[i0:i0 + block, j0:j0 + block] = O.e4m3_decode(_torch_e4m3_codes(sq / 2.0 ** e)) * 2.0 ** e
+    return out
+
+
+def _brute_fp8_blocks_fmt(M, e5, block=32):
+    """_brute_fp8_blocks in E4M3 or E5M2 (largest finite 448 or 57344)."""
+    top = 57344.0 if e5 else 448.0
+    out = np.zeros_like(M)
+    for i, row in enumerate(M):
+        for j0 in range(0, row.size, block):
+            blk = row[j0:j0 + block]
+            a = np.abs(blk).max()
+            e = 0 if a == 0 else next(x for x in range(-200, 200) if a <= top * 2.0 ** x)
+            e = min(max(e, -127), 127)
+            codes = (_torch_e5m2_codes if e5 else _torch_e4m3_codes)(blk / 2.0 ** e)
+            out[i, j0:j0 + block] = (O.e5m2_decode if e5 else O.e4m3_decode)(codes) * 2.0 ** e
+    return out
+
+
+def test_fp8_squares_brute_force_with_partial_edges():
+    """Squares of very different magnitude, whole and partial at the bottom
+    and right edges, against the brute force; the exponent array has one
+    entry per square."""
+    rng = np.random.default_rng(60)
+    for R, C in ((32, 32), (70, 45), (33, 64), (96, 100)):
+        W = rng.standard_normal((R, C))
+        W *= np.exp2(rng.integers(-14, 14, (-(-R // 32), -(-C // 32)))).repeat(32, 0).repeat(32, 1)[:R, :C]
+        W = O.round_bf16(W)
+        q, e = O.quantize_squares_fp8(W)
+        assert e.shape == (-(-R // 32), -(-C // 32))
+        np.testing.assert_array_equal(O.dequantize_squares_fp8(q, e), _brute_fp8_squares(W))
+
+
+def test_fp8_squares_of_the_transpose_are_the_transposed_squares():
+    """One square quantization serves both read directions: quantizing W^T
+    gives W's codes and exponents transposed (ragged shape)."""
+    rng = np.random.default_rng(61)
+    W = O.round_bf16(rng.standard_normal((75, 130)) * np.exp2(rng.integers(-9, 9, (75, 1))))
+    q, e = O.quantize_squares_fp8(W)
+    qt, et = O.quantize_squares_fp8(W.T)
+    np.testing.assert_array_equal(qt, q.T)
+    np.testing.assert_array_equal(et, e.T)
+
+
+def test_fp8_squares_equal_row_blocks_when_every_row_holds_the_square_max():
+    """If every row of every square reaches that square's largest magnitude,
+    each 1 x 32 block of a row has the square's scale, so the square codes
+    equal quantize_blocks_fp8's and the exponents repeat down the square."""
+    rng = np.random.default_rng(62)
+    R, C = 64, 96
+    W = O.round_bf16(rng.uniform(-1, 1, (R, C)))
+    for i0 in range(0, R, 32):
+        for j0 in range(0, C, 32):
+            s = 2.0 ** int(rng.integers(-10, 10))
+            W[i0:i0 + 32, j0:j0 + 32] *= s
+            W[i0:i0 + 32, j0 + int(rng.integers(0, 32))] = 1.5 * s * rng.choice([-1.0, 1.0], 32)
+    qs, es = O.quantize_squares_fp8(W)
+    qb, eb = O.quantize_blocks_fp8(W)
+    np.testing.assert_array_equal(qs, qb)
+    np.testing.assert_array_equal(es.repeat(32, axis=0), eb)
+
+
+def test_fp8_squares_share_one_scale_down_the_rows():
+    """A square holds one scale for all its rows: a row 2^-17 below the
+    square's largest row falls into E4M3's subnormal range and loses its
+    precision, where 1 x 32 blocks of its own keep every element within
+    2^-4 (so the two schemes are told apart)."""
+    rng = np.random.default_rng(63)
+    W = O.round_bf16(1.0 + rng.random((32, 32)))
+    W[:, 0] = 1.875                              # every row holds the square's largest value
+    W[1] *= 2.0 ** -17
+    S = O.dequantize_squares_fp8(*O.quantize_squares_fp8(W))
+    B = O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(W))
+    assert (np.abs(B - W) <= 2.0 ** -4 * np.abs(W) * (1 + 1e-12)).all()
+    assert np.abs(S[1] - W[1]).max() > 0.1 * np.abs(W[1]).max()
+    np.testing.assert_array_equal(S[[0] + list(range(2, 32))], B[[0] + list(range(2, 32))])
+
+
+def test_fp8_square_exponent_is_clipped_to_the_scale_range():
+    W = np.zeros((64, 32))
+    W[:32] = 2.0 ** -140                         # wants 2^-148: clipped to 2^-127
+    W[40, 3] = 1.5 * 2.0 ** 100
+    q, e = O.quantize_squares_fp8(W)
+    assert e.tolist() == [[-127], [92]]
+    assert (O.e4m3_decode(q[:32]) == 0).all()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_expert_forward_fp8_square_brute_force(act):
+    """The square-mode forward against explicit loops: X and the bf16 H in
+    brute-force 1 x 32 blocks, w13 and w2 in brute-force 32 x 32 squares
+    (d = 40, f = 24: partial blocks and squares in both GEMMs)."""
+    rng = np.random.default_rng(64)
+    n, d, f = 5, 40, 24
+    P = 2 * f if act == "swiglu" else f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 6)
+    w13[:32, :32] *= 2.0 ** 7                    # squares of different magnitude
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 5)
+    w2[32:] *= 2.0 ** -6
+    Xd, W13d, W2d = _brute_fp8_blocks(X), _brute_fp8_squares(w13), _brute_fp8_squares(w2)
+    pre = np.array([[sum(Xd[t, c] * W13d[j, c] for c in range(d)) for j in range(P)] for t in range(n)])
+    if act == "swiglu":
+        a, b = pre[:, :f], pre[:, f:]
+        H = a / (1 + np.exp(-a)) * b
+    else:
+        H = 0.5 * pre * (1 + sps.erf(pre / np.sqrt(2)))
+    Hd = _brute_fp8_blocks(O.round_bf16(H))
+    out = np.array([[sum(Hd[t, j] * W2d[c, j] for j in range(f)) for c in range(d)] for t in range(n)])
+    got, saved = O.expert_forward_fp8_square(X, w13, w2, act)
+    np.testing.assert_allclose(got, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(saved["H"], H, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("act,e5", [("swiglu", False), ("gelu", False), ("swiglu", True)])
+def test_expert_backward_fp8_square_brute_force(act, e5):
+    """The square-mode data gradients against explicit loops: bf16 dO in
+    brute-force 1 x 32 blocks along d, W2 in brute-force squares read along
+    its output dimension, the activation backward on the bf16 pre-activations,
+    bf16 dpre in 1 x 32 blocks along P, W13 in squares read along P (d = 40,
+    P = 48 or 24: partial blocks); gradients in E4M3 or E5M2."""
+    rng = np.random.default_rng(65)
+    n, d, f = 4, 40, 24
+    P = 2 * f if act == "swiglu" else f
+    X = O.round_bf16(rng.standard_normal((n, d)))
+    w13 = O.round_bf16(rng.standard_normal((P, d)) / 5)
+    w13[32:] *= 2.0 ** -5
+    w2 = O.round_bf16(rng.standard_normal((d, f)) / 4)
+    w2[:, :8] *= 2.0 ** 6
+    _, saved = O.expert_forward(X, w13, w2, act)
+    dO = rng.standard_normal((n, d)) * 0.3
+    dO[:, 32:] *= 2.0 ** -8
+    dOd = _brute_fp8_blocks_fmt(O.round_bf16(dO), e5)
+    W2d, W13d = _brute_fp8_squares(w2), _brute_fp8_squares(w13)     # [d, f], [P, d]
+    dH = np.array([[sum(dOd[t, c] * W2d[c, j] for c in range(d)) for j in range(f)] for t in range(n)])
+    a = O.round_bf16(saved["a"])
+    sg = 1 / (1 + np.exp(-a))
+    if act == "swiglu":
+        b = O.round_bf16(saved["b"])
+        dpre = np.concatenate([dH * b * sg * (1 + a * (1 - sg)), dH * a * sg], axis=1)
+    else:
+        cdf = 0.5 * (1 + sps.erf(a / np.sqrt(2)))
+        dpre = dH * (cdf + a * np.exp(-a * a / 2) / np.sqrt(2 * np.pi))
+    dpd = _brute_fp8_blocks_fmt(O.round_bf16(dpre), e5)
+    dX = np.array([[sum(dpd[t, p] * W13d[p, j] for p in range(P)) for j in range(d)] for t in range(n)])
+    fmt = "e5m2" if e5 else "e4m3"
+    gX, g13, g2, gpre = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_square(w2).T,
+                                                 O.quantize_weights_fp8_square(w13).T, saved, dO, act,
+                                                 fmt, "block")
+    np.testing.assert_allclose(gpre, dpre, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gX, dX, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g2, dO.T @ saved["H"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g13, dpre.T @ X, rtol=1e-12, atol=1e-14)
+    ex, _, _, _ = O.expert_backward(X, w13, w2, saved, dO, act)
+    assert np.abs(gX - ex).max() < 0.15 * np.abs(ex).max()
+
+
+def test_grouped_square_mode_is_per_expert():
+    """grouped_ffn_forward(fp8="square") and grouped_ffn_backward(fp8_dgrad=
+    "square") run each expert (and the shared one) on its own rows through the
+    square-mode expert functions, weights quantized per expert. A few columns
+    of w2 sit 2^-12 below the rest: squares round them into E4M3's subnormal
+    range, one scale per column would not, so the two weight readings differ."""
+    rng = np.random.default_rng(66)
+    d, f, E, T = 32, 16, 3, 10
+    offsets = np.array([0, 4, 4, 9])
+    x = O.round_bf16(rng.standard_normal((T, d)))
+    x_perm = x[[0, 2, 5, 7, 1, 3, 4, 8, 9]]
+    w13 = O.round_bf16(rng.standard_normal((E, 2 * f, d)) / 3 * np.array([1.0, 2.0 ** 9, 2.0 ** -9])[:, None, None])
+    w2 = rng.standard_normal((E, d, f)) / 3
+    w2[:, :, :4] *= 2.0 ** -12                   # columns a per-column scale would keep exact
+    w2 = O.round_bf16(w2)
+    sw13 = O.round_bf16(rng.standard_normal((1, 2 * f, d)) / 3)
+    sw2 = O.round_bf16(rng.standard_normal((1, d, f)) / 3)
+    O_, Os, saved = O.grouped_ffn_forward(x_perm, offsets, w13, w2, "swiglu", x, sw13, sw2, fp8="square")
+    dO = O.round_bf16(rng.standard_normal((9, d)))
+    dY = O.round_bf16(rng.standard_normal((T, d)))
+    g = O.grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, "swiglu", x, sw13, sw2, dY,
+                               fp8_dgrad="square")
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        o, sv = O.expert_forward_fp8_square(x_perm[lo:hi], w13[e], w2[e], "swiglu")
+        np.testing.assert_array_equal(O_[lo:hi], o)
+        dx, _, _, _ = O.expert_backward_fp8_wq(x_perm[lo:hi], O.quantize_weights_fp8_square(w2[e]).T,
+                                               O.quantize_weights_fp8_square(w13[e]).T, sv, dO[lo:hi],
+                                               "swiglu", "e4m3", "block")
+        np.testing.assert_array_equal(g["dx_perm"][lo:hi], dx)
+    os_, svs = O.expert_forward_fp8_square(x, sw13[0], sw2[0], "swiglu")
+    np.testing.assert_array_equal(Os, os_)
+    dxs, _, _, _ = O.expert_backward_fp8_wq(x, O.quantize_weights_fp8_square(sw2[0]).T,
+                                            O.quantize_weights_fp8_square(sw13[0]).T, svs, dY, "swiglu",
+                                            "e4m3", "block")
+    np.testing.assert_array_equal(g["dx_shared"], dxs)
+    per_col = O.grouped_ffn_backward(x_perm, offsets, w13, w2, saved, dO, "swiglu", x, sw13, sw2, dY,
+                                     fp8_dgrad=True)
+    assert (per_col["dx_perm"] != g["dx_perm"]).any()
