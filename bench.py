@@ -122,7 +122,11 @@ def is_fp8_gemm(w, name):
 def dtype_label(w):
     if w.dtype != "bf16":
         return "f32"
-    blk = " (1x32 block scales)" if w.fp8_scale == "block" else ""
+    blk = {"block": " (1x32 block scales)",
+           "square": " (32x32 weight squares, 1x32 activation blocks)"}.get(w.fp8_scale, "")
+    if w.fp8 and w.fp8_bwd and w.fp8_scale == "square":
+        wg = " and wgrad GEMMs (wgrad: 32-token block scales)" if w.fp8_wgrad else " GEMMs, bf16 wgrad"
+        return f"fp8-e4m3 fwd and dgrad{blk}{wg}"
     if w.fp8 and w.fp8_wgrad:
         return f"fp8-e4m3 fwd{blk}, dgrad and wgrad GEMMs (wgrad: 32-token block scales)"
     if w.fp8 and w.fp8_bwd:
@@ -527,6 +531,8 @@ def streamed_oracle_step(w, g, tokens, clock):
         return out
 
     def fwd_e(X, w13e, w2e):
+        if ws.fp8 and ws.fp8_scale == "square":
+            return O.expert_forward_fp8_square(X, w13e, w2e, ws.act)
         if ws.fp8 and ws.fp8_scale == "block":
             return O.expert_forward_fp8_block(X, w13e, w2e, ws.act)
         if ws.fp8:
@@ -534,13 +540,17 @@ def streamed_oracle_step(w, g, tokens, clock):
         return O.expert_forward(X, w13e, w2e, ws.act)
 
     def bwd_e(X, w13e, w2e, sv, dO):
-        if ws.fp8_bwd:
+        if ws.fp8_bwd and ws.fp8_scale == "square":
+            out = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_square(w2e).T,
+                                           O.quantize_weights_fp8_square(w13e).T, sv, dO, ws.act,
+                                           ws.fp8_grad, "block")
+        elif ws.fp8_bwd:
             out = O.expert_backward_fp8_wq(X, O.quantize_weights_fp8_t(w2e),
-                                           O.quantize_weights_fp8_t(w13e), sv, dO, ws.act)
+                                           O.quantize_weights_fp8_t(w13e), sv, dO, ws.act, ws.fp8_grad)
         else:
             out = O.expert_backward(X, w13e, w2e, sv, dO, ws.act)
         if ws.fp8_wgrad:
-            g13, g2 = O.expert_wgrad_fp8(X, sv["H"], dO, out[3])
+            g13, g2 = O.expert_wgrad_fp8(X, sv["H"], dO, out[3], ws.fp8_grad)
             out = (out[0], g13, g2, out[3])
         return out
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -98,7 +98,9 @@ typedef enum {
   MOE_OP_FFN_FWD_FP8 = 6,
   MOE_OP_FFN_BWD_FP8 = 7,
   MOE_OP_FFN_FWD_FP8B = 8,
-  MOE_OP_FFN_BWD_FP8W = 9
+  MOE_OP_FFN_BWD_FP8W = 9,
+  MOE_OP_FFN_BWD_FP8B = 10,
+  MOE_OP_FFN_BWD_FP8BW = 11
 } moe_op;
 
 /* ---------------------------------------------------------------- router
@@ -389,6 +391,34 @@ int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void
                           int32_t* scale_exp, void* codes_t, int32_t* scale_exp_t, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* Square-block weights. The pages fix no scale granularity for the weights
+ * either; the third FP8 mode quantizes each weight matrix once in 32 x 32
+ * squares (rows x columns of the stored matrix, from its first row and
+ * column, the last ones partial), each with the block rule of
+ * moe_quantize_fp8_blocks on the square's maximum. A square is a 1 x 32
+ * block of every row it covers in the matrix and in its transpose, so the
+ * forward (rows) and the data gradients (the transpose) share one
+ * quantization.
+ *
+ * moe_quantize_fp8_squares: for G row-major R x C bf16 matrices,
+ *   e[g][i][j] = clip(smallest integer e with max over square (i, j) of
+ *                     |src[g]| <= 448 * 2^e, -127, 127) (0 for an all-zero square),
+ *   codes[g][r][c] = codes_t[g][c][r] = E4M3 nearest (ties to even) of
+ *                    src[g][r][c] * 2^-e[g][r/32][c/32],
+ * and the block-scale bytes of both layouts: scales as moe_quantize_fp8_blocks
+ * writes them for the [G*R, C] matrix of codes (row g*R + r, block c/32 holds
+ * e[g][r/32][c/32] + 127), scales_t for the [G*C, R] matrix of codes_t (row
+ * g*C + c, block r/32). One read of src writes both. Bit-exact function of
+ * the input; inputs must be finite. No desc: a plain matrix operation.
+ *   src       [G, R, C] bf16                                          in
+ *   codes     [G, R, C] uint8, scales MOE_FP8_BLOCK_SCALE_BYTES(G*R, C) out
+ *   codes_t   [G, C, R] uint8, scales_t MOE_FP8_BLOCK_SCALE_BYTES(G*C, R) out
+ * Constraints: R and C multiples of 16 in [16, 2^22]; 0 <= G <= 65535; each
+ * scale array under 2^31 words; every pointer 16-byte aligned.
+ */
+int moe_quantize_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                             uint8_t* scales, void* codes_t, uint8_t* scales_t, void* stream);
+
 /* moe_grouped_ffn_bwd_fp8: moe_grouped_ffn_bwd with its two data-gradient
  * GEMMs on FP8 operands. Per group:
  *   1. the upstream gradient rows are quantized per row;
@@ -446,6 +476,48 @@ int moe_grouped_ffn_bwd_fp8w(const moe_desc* desc, const void* x_perm, const int
                              const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
                              void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* moe_grouped_ffn_bwd_fp8b: moe_grouped_ffn_bwd_fp8 with block scales (the
+ * square mode's data gradients). The upstream gradient rows and the bf16 dpre
+ * are quantized with moe_quantize_fp8_blocks' rule along their reduction axis
+ * (d for dH, P for dX; E4M3 or, with desc->fp8_grad = MOE_FP8_E5M2, E5M2),
+ * and the weight operands are the transposed square-block codes of
+ * moe_quantize_fp8_squares. Each output element of dH and dX is the sum over
+ * blocks b of 2^(e_grad[b] + e_weight[b]) * sum_{k in b} code * code,
+ * accumulated in float32. The weight gradients run in bf16 as in
+ * moe_grouped_ffn_bwd_fp8. SB(r, K) = MOE_FP8_BLOCK_SCALE_BYTES(r, K).
+ *   w2q_t [E, f, d] uint8, b2_t SB(E*f, d) bytes  (codes_t, scales_t of
+ *     moe_quantize_fp8_squares on w2 [E, d, f])                              in
+ *   w13q_t [E, d, P] uint8, b13_t SB(E*d, P) bytes (the same on w13 [E, P, d]) in
+ *   sw2q_t, sb2_t (SB(f, d)), sw13q_t, sb13_t (SB(d, P)): the shared
+ *     expert's, or NULL                                                      in
+ *   the other arguments are as in moe_grouped_ffn_bwd_fp8
+ *   ws  MOE_OP_FFN_BWD_FP8B bytes (moe_grouped_ffn_bwd's layout, then the
+ *       FP8 codes and block scales of dO and dpre)                     scratch
+ */
+int moe_grouped_ffn_bwd_fp8b(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w13q_t, const uint8_t* b13_t,
+                             const void* w2q_t, const uint8_t* b2_t, const void* sw13q_t,
+                             const uint8_t* sb13_t, const void* sw2q_t, const uint8_t* sb2_t,
+                             const void* save_pre, const void* save_h, const void* save_pre_s,
+                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* moe_grouped_ffn_bwd_fp8bw: moe_grouped_ffn_bwd_fp8b with the weight
+ * gradients on token-axis FP8 operands as in moe_grouped_ffn_bwd_fp8w.
+ * Arguments as in moe_grouped_ffn_bwd_fp8b.
+ *   ws  MOE_OP_FFN_BWD_FP8BW bytes (moe_grouped_ffn_bwd_fp8b's layout, then
+ *       the token-axis buffers of moe_grouped_ffn_bwd_fp8w)            scratch
+ */
+int moe_grouped_ffn_bwd_fp8bw(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                              const void* x, const void* w13q_t, const uint8_t* b13_t,
+                              const void* w2q_t, const uint8_t* b2_t, const void* sw13q_t,
+                              const uint8_t* sb13_t, const void* sw2q_t, const uint8_t* sb2_t,
+                              const void* save_pre, const void* save_h, const void* save_pre_s,
+                              const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                              void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine: the weighted sum of [Recipe] §2.1/§2.2 (the combine step of

@@ -16,14 +16,14 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
  MOE_OP_ROUTE_BWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_FWD_FP8B,
- MOE_OP_FFN_BWD_FP8W) = range(10)
+ MOE_OP_FFN_BWD_FP8W, MOE_OP_FFN_BWD_FP8B, MOE_OP_FFN_BWD_FP8BW) = range(12)
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -33,7 +33,8 @@ EXPORTS = (
     "moe_profile_enable", "moe_profile_read", "moe_quantize_fp8", "moe_grouped_ffn_fwd_fp8",
     "moe_quantize_fp8_t", "moe_grouped_ffn_bwd_fp8", "moe_quantize_fp8_both",
     "moe_permute_noalloc", "moe_quantize_fp8_blocks", "moe_grouped_ffn_fwd_fp8b",
-    "moe_grouped_ffn_bwd_fp8w",
+    "moe_grouped_ffn_bwd_fp8w", "moe_quantize_fp8_squares", "moe_grouped_ffn_bwd_fp8b",
+    "moe_grouped_ffn_bwd_fp8bw",
 )
 
 
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
                                       _P, ctypes.c_size_t, _P],
             "moe_grouped_ffn_bwd_fp8": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
             "moe_grouped_ffn_bwd_fp8w": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
+            "moe_quantize_fp8_squares": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P,
+                                         _P],
+            "moe_grouped_ffn_bwd_fp8b": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
+            "moe_grouped_ffn_bwd_fp8bw": [DP] + [_P] * 24 + [ctypes.c_size_t, _P],
             "moe_combine": [DP] + [_P] * 6,
             "moe_combine_bwd": [DP] + [_P] * 7,
             "moe_grouped_ffn_bwd": [DP] + [_P] * 20 + [ctypes.c_size_t, _P],
@@ -322,14 +327,36 @@ def quantize_fp8_both(src, codes, scale_exp, codes_t, scale_exp_t, ws, stream=No
         _stream(stream)))
 
 
+def quantize_fp8_squares(src, codes, scales, codes_t, scales_t, stream=None):
+    """Square-block E4M3 quantization of bf16 matrices src [..., R, C] (32 x
+    32 squares, one exponent each) into both layouts from one read: codes
+    [..., R, C] with scales (fp8_block_scale_bytes(G*R, C) uint8) and the
+    transposes' codes_t [..., C, R] with scales_t (fp8_block_scale_bytes(G*C, R)),
+    G the number of matrices."""
+    R, C = src.shape[-2], src.shape[-1]
+    G = src.numel() // (R * C) if R * C else 0
+    lead = src.shape[:-2]
+    if codes.shape != src.shape or codes_t.shape != lead + (C, R) or \
+            scales.numel() != fp8_block_scale_bytes(G * R, C) or \
+            scales_t.numel() != fp8_block_scale_bytes(G * C, R):
+        raise ValueError("codes [..., R, C], codes_t [..., C, R], scales and scales_t of "
+                         "fp8_block_scale_bytes(G*R, C) and (G*C, R) bytes")
+    _check("moe_quantize_fp8_squares", lib().moe_quantize_fp8_squares(
+        _p(src), G, R, C, _p(codes), _p(scales), _p(codes_t), _p(scales_t), _stream(stream)))
+
+
 def grouped_ffn_bwd_fp8(desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t, ss13_t,
                         sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy, dx_perm,
-                        dx_shared, dw13, dw2, dsw13, dsw2, ws=None, stream=None, fp8_wgrad=False):
+                        dx_shared, dw13, dw2, dsw13, dsw2, ws=None, stream=None, fp8_wgrad=False,
+                        block=False):
     """The FP8 backward (data gradients on FP8 operands); fp8_wgrad runs the
     weight gradients on token-axis block-scaled FP8 operands as well
-    (moe_grouped_ffn_bwd_fp8w, workspace MOE_OP_FFN_BWD_FP8W)."""
+    (moe_grouped_ffn_bwd_fp8w, workspace MOE_OP_FFN_BWD_FP8W). block: the
+    data gradients on block scales against square-block weights, s13_t ..
+    ss2_t being their scale bytes (moe_grouped_ffn_bwd_fp8b / _fp8bw,
+    workspace MOE_OP_FFN_BWD_FP8B / MOE_OP_FFN_BWD_FP8BW)."""
     wp, wn = _ws(ws)
-    name = "moe_grouped_ffn_bwd_fp8w" if fp8_wgrad else "moe_grouped_ffn_bwd_fp8"
+    name = "moe_grouped_ffn_bwd_fp8" + ("b" if block else "") + ("w" if fp8_wgrad else "")
     _check(name, getattr(lib(), name)(
         ctypes.byref(desc), _p(x_perm), _p(offsets), _p(x), _p(w13q_t), _p(s13_t), _p(w2q_t),
         _p(s2_t), _p(sw13q_t), _p(ss13_t), _p(sw2q_t), _p(ss2_t), _p(save_pre), _p(save_h),

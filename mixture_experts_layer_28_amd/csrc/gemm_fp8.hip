@@ -1,7 +1,8 @@
 // Grouped GEMM on FP8 (OCP E4M3) operands on the gfx950 matrix cores
 // (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation), for the forward of the
 // expert FFN and the backward's data gradients (whose weight operand is the
-// transposed weight, quantized per input channel). Both operands are
+// transposed weight, quantized per input channel, or in square blocks with
+// block scales below). Both operands are
 // K-contiguous byte matrices with one
 // power-of-two scale per row (2^a_sexp[m] for the input rows, 2^b_sexp[n]
 // for the weight rows); the epilogue applies them exactly with ldexp, so
@@ -562,25 +563,36 @@ hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s, int a_fm
   if (epi == E_ && rag == R_ && (bool)p.blk_scales == B_) return launch_fp8<E_, R_, B_, 1>(p, s);
   if (a_fmt == 1) {
     // E5M2 A operand: the backward's gradient rows (data gradients against
-    // the transposed weights, per-row scales) and the weight gradients'
-    // token-axis gradient operand (block scales)
+    // the transposed weights, per-row or block scales) and the weight
+    // gradients' token-axis gradient operand (block scales)
     MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_M, false)
     MOE_CASE_A5(EPI_GELU_BWD, RAG_M, false)
     MOE_CASE_A5(EPI_STORE, RAG_M, false)
     MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_NONE, false)
     MOE_CASE_A5(EPI_GELU_BWD, RAG_NONE, false)
     MOE_CASE_A5(EPI_STORE, RAG_NONE, false)
+    MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_M, true)
+    MOE_CASE_A5(EPI_GELU_BWD, RAG_M, true)
+    MOE_CASE_A5(EPI_STORE, RAG_M, true)
+    MOE_CASE_A5(EPI_SWIGLU_BWD, RAG_NONE, true)
+    MOE_CASE_A5(EPI_GELU_BWD, RAG_NONE, true)
+    MOE_CASE_A5(EPI_STORE, RAG_NONE, true)
     MOE_CASE_A5(EPI_STORE, RAG_K, true)
     return hipErrorInvalidValue;
   }
   if (p.blk_scales) {
-    // block scales: the forward GEMMs
+    // block scales: the forward GEMMs, the data gradients (dH with the
+    // activation backward, dX as a plain store)
     MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_M)
     MOE_CASE_BLK(EPI_GELU_FWD, RAG_M)
     MOE_CASE_BLK(EPI_STORE, RAG_M)
     MOE_CASE_BLK(EPI_SWIGLU_FWD, RAG_NONE)
     MOE_CASE_BLK(EPI_GELU_FWD, RAG_NONE)
     MOE_CASE_BLK(EPI_STORE, RAG_NONE)
+    MOE_CASE_BLK(EPI_SWIGLU_BWD, RAG_M)
+    MOE_CASE_BLK(EPI_GELU_BWD, RAG_M)
+    MOE_CASE_BLK(EPI_SWIGLU_BWD, RAG_NONE)
+    MOE_CASE_BLK(EPI_GELU_BWD, RAG_NONE)
     // and the weight gradients on token-axis transposes
     MOE_CASE_BLK(EPI_STORE, RAG_K)
     return hipErrorInvalidValue;

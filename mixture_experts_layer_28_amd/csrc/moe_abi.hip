@@ -18,7 +18,9 @@ namespace moe {
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                                    const int32_t* valid_rows, void* codes, int64_t ld_q,
-                                   uint8_t* scales, hipStream_t st);
+                                   uint8_t* scales, hipStream_t st, int fmt = 0);
+hipError_t launch_quant_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                                    uint8_t* scales, void* codes_t, uint8_t* scales_t, hipStream_t st);
 hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
                                     int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st,
                                     int fmt = 0);
@@ -285,6 +287,16 @@ bool blk_scale_words_fit(int64_t rows, int64_t K) {
   return blk_scale_bytes(rows, K) / 4 < ((size_t)1 << 31);
 }
 
+// The token-axis codes and block scales of the FP8 weight gradients' two
+// operands (largest of the two GEMMs; the shared expert's fit in the routed
+// ones), the k-step table and two ints of bounds.
+size_t wgrad_fp8_ws_bytes(const moe_desc* d) {
+  const int64_t Rp = wgrad_rp(d), P = pre_cols(d);
+  const int64_t ma = std::max(d->d, P), mb = std::max(d->f, d->d);
+  return align256((size_t)ma * Rp) + align256(blk_scale_bytes(ma, Rp)) + align256((size_t)mb * Rp) +
+         align256(blk_scale_bytes(mb, Rp)) + align256((size_t)(Rp / 128) * 4) + 256;
+}
+
 size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
   switch (op) {
@@ -315,23 +327,22 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
       return b + tail_ws_bytes(kTailCusMax);
     }
     case MOE_OP_FFN_BWD_FP8:
+    case MOE_OP_FFN_BWD_FP8B: {
       // the bf16 backward's pre-activation gradients, then FP8 codes and
-      // exponents of the upstream gradient and of the pre-activation gradient
-      // (routed rows; the shared expert's T rows reuse them afterwards)
-      return ws_bytes_for(d, MOE_OP_FFN_BWD) + align256((size_t)T * d->k * d->d) +
-             align256((size_t)T * d->k * 4) + align256((size_t)T * d->k * pre_cols(d)) +
-             align256((size_t)T * d->k * 4);
-    case MOE_OP_FFN_BWD_FP8W: {
-      // the FP8 backward's buffers, then the token-axis codes and block
-      // scales of the weight gradients' two operands (largest of the two
-      // GEMMs; the shared expert's fit in the routed ones), the k-step table
-      // and two ints of bounds
-      const int64_t Rp = wgrad_rp(d), P = pre_cols(d);
-      const int64_t ma = std::max(d->d, P), mb = std::max(d->f, d->d);
-      return ws_bytes_for(d, MOE_OP_FFN_BWD_FP8) + align256((size_t)ma * Rp) +
-             align256(blk_scale_bytes(ma, Rp)) + align256((size_t)mb * Rp) +
-             align256(blk_scale_bytes(mb, Rp)) + align256((size_t)(Rp / 128) * 4) + 256;
+      // scales (an int32 per row, or block scales) of the upstream gradient
+      // and of the pre-activation gradient (routed rows; the shared expert's
+      // T rows reuse them afterwards)
+      const int64_t R = T * d->k, P = pre_cols(d);
+      const bool blk = op == MOE_OP_FFN_BWD_FP8B;
+      return ws_bytes_for(d, MOE_OP_FFN_BWD) + align256((size_t)R * d->d) +
+             align256(blk ? blk_scale_bytes(R, d->d) : (size_t)R * 4) + align256((size_t)R * P) +
+             align256(blk ? blk_scale_bytes(R, P) : (size_t)R * 4);
     }
+    case MOE_OP_FFN_BWD_FP8W:
+    case MOE_OP_FFN_BWD_FP8BW:
+      // the FP8 backward's buffers, then the weight gradients' token-axis ones
+      return ws_bytes_for(d, op == MOE_OP_FFN_BWD_FP8W ? MOE_OP_FFN_BWD_FP8 : MOE_OP_FFN_BWD_FP8B) +
+             wgrad_fp8_ws_bytes(d);
     case MOE_OP_FFN_FWD_FP8B: {
       // FP8 codes and block scales of H between the two GEMMs, then the
       // down-projection's split-K tail
@@ -478,7 +489,7 @@ int moe_workspace_size(const moe_desc* desc, int op, size_t* bytes) {
   g_err[0] = 0;
   MOE_TRY(check_desc(desc));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_BWD_FP8W)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_BWD_FP8BW)
     return fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
   *bytes = ws_bytes_for(desc, op);
   return MOE_OK;
@@ -1058,6 +1069,32 @@ int moe_quantize_fp8_t(const void* src, int64_t G, int64_t R, int64_t C, void* c
                    "fp8 transposing quantize");
 }
 
+int moe_quantize_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                             uint8_t* scales, void* codes_t, uint8_t* scales_t, void* stream) {
+  g_err[0] = 0;
+  if (G < 0 || G > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "G must be in [0, 65535] (got %lld)", (long long)G);
+  if (R < 16 || R % 16 || R > (int64_t(1) << 22))
+    return fail(MOE_ERR_INVALID_ARG, "R must be a positive multiple of 16, at most 2^22 (got %lld)",
+                (long long)R);
+  if (C < 16 || C % 16 || C > (int64_t(1) << 22))
+    return fail(MOE_ERR_INVALID_ARG, "C must be a positive multiple of 16, at most 2^22 (got %lld)",
+                (long long)C);
+  MOE_TRY(need(src, "src"));
+  MOE_TRY(need(codes, "codes"));
+  MOE_TRY(need(scales, "scales"));
+  MOE_TRY(need(codes_t, "codes_t"));
+  MOE_TRY(need(scales_t, "scales_t"));
+  if (!blk_scale_words_fit(G * R, C) || !blk_scale_words_fit(G * C, R))
+    return fail(MOE_ERR_INVALID_ARG, "block scales of %lld matrices of %lld x %lld exceed 2^31 words",
+                (long long)G, (long long)R, (long long)C);
+  if (G == 0) return MOE_OK;
+  Scope sc(K_QUANT_FP8, (hipStream_t)stream);
+  return hip_check(launch_quant_fp8_squares(src, G, R, C, codes, scales, codes_t, scales_t,
+                                            (hipStream_t)stream),
+                   "fp8 quantize squares");
+}
+
 int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
                           int32_t* scale_exp, void* codes_t, int32_t* scale_exp_t, void* ws,
                           size_t ws_bytes, void* stream) {
@@ -1091,9 +1128,12 @@ int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void
 
 namespace {
 
-// The FP8 backward: data gradients on per-row FP8 operands, weight gradients
-// in bf16 (fp8w = false) or on token-axis block-scaled FP8 operands.
-int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+// The FP8 backward: data gradients on per-row FP8 operands (blk = false:
+// s13_t .. ss2_t are int32 exponents) or on block-scaled ones (blk: they are
+// the square-block weights' scale bytes), weight gradients in bf16
+// (fp8w = false) or on token-axis block-scaled FP8 operands.
+int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_perm,
+                     const int32_t* offsets,
                      const void* x, const void* w13q_t, const int32_t* s13_t, const void* w2q_t,
                      const int32_t* s2_t, const void* sw13q_t, const int32_t* ss13_t,
                      const void* sw2q_t, const int32_t* ss2_t, const void* save_pre,
@@ -1131,7 +1171,9 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     MOE_TRY(need(dsw13, "dsw13"));
     MOE_TRY(need(dsw2, "dsw2"));
   }
-  MOE_TRY(check_ws(desc, fp8w ? MOE_OP_FFN_BWD_FP8W : MOE_OP_FFN_BWD_FP8, ws, ws_bytes));
+  const int op = blk ? (fp8w ? MOE_OP_FFN_BWD_FP8BW : MOE_OP_FFN_BWD_FP8B)
+                     : (fp8w ? MOE_OP_FFN_BWD_FP8W : MOE_OP_FFN_BWD_FP8);
+  MOE_TRY(check_ws(desc, op, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   const int64_t T = desc->T, d = desc->d, f = desc->f, P = pre_cols(desc);
   const int64_t Rp = wgrad_rp(desc);
@@ -1139,6 +1181,9 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
   if (fp8w && (std::max(d, P) * Rp >= (int64_t(1) << 31) || std::max(f, d) * Rp >= (int64_t(1) << 31) ||
                !blk_scale_words_fit(std::max(d, P), Rp) || !blk_scale_words_fit(std::max(f, d), Rp)))
     return fail(MOE_ERR_UNSUPPORTED, "FP8 weight gradients: the token-axis codes exceed 2^31 bytes");
+  if (blk && (!blk_scale_words_fit(T * desc->k, d) || !blk_scale_words_fit(T * desc->k, P) ||
+              !blk_scale_words_fit(desc->E * f, d) || !blk_scale_words_fit(desc->E * d, P)))
+    return fail(MOE_ERR_UNSUPPORTED, "block scales of this layer exceed 2^31 words");
   if (T == 0) {
     // no rows: every weight gradient is zero
     MOE_TRY(hip_check(launch_fill_zero(dw13, (size_t)desc->E * P * d * 2, s), "zero dw13"));
@@ -1156,13 +1201,17 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
   // the bf16 backward's layout: after the dpre regions, the dX GEMM's split-K tail
   char* tail_w = (char*)dpre_s + (desc->n_shared ? align256((size_t)T * P * 2) : 0);
   char* w8 = wb + ws_bytes_for(desc, MOE_OP_FFN_BWD);
+  // codes and scales of dO and dpre: an int32 exponent per row, or block
+  // scale bytes (blk)
+  const int64_t RK = T * desc->k;
   uint8_t* gq = (uint8_t*)w8;
-  int32_t* gs = (int32_t*)(w8 + align256((size_t)T * desc->k * d));
-  uint8_t* pq = (uint8_t*)((char*)gs + align256((size_t)T * desc->k * 4));
-  int32_t* ps = (int32_t*)((char*)pq + align256((size_t)T * desc->k * P));
+  int32_t* gs = (int32_t*)(w8 + align256((size_t)RK * d));
+  uint8_t* pq = (uint8_t*)((char*)gs + align256(blk ? blk_scale_bytes(RK, d) : (size_t)RK * 4));
+  int32_t* ps = (int32_t*)((char*)pq + align256((size_t)RK * P));
   // FP8 weight gradients: token-axis codes and scales of the two operands,
   // the k-step -> group table and the shared expert's one-group bounds
-  char* w9 = w8 + (ws_bytes_for(desc, MOE_OP_FFN_BWD_FP8) - ws_bytes_for(desc, MOE_OP_FFN_BWD));
+  char* w9 = w8 + (ws_bytes_for(desc, blk ? MOE_OP_FFN_BWD_FP8B : MOE_OP_FFN_BWD_FP8) -
+                   ws_bytes_for(desc, MOE_OP_FFN_BWD));
   uint8_t* qa = (uint8_t*)w9;
   uint8_t* qa_s = qa + align256((size_t)std::max(d, P) * Rp);
   uint8_t* qb = qa_s + align256(blk_scale_bytes(std::max(d, P), Rp));
@@ -1183,7 +1232,9 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     // upstream gradient -> FP8 rows (routed rows beyond offsets[E] skipped)
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s, gf), "fp8 quantize dO"));
+      MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(go, rows, d, d, valid, gq, d, (uint8_t*)gs, s, gf)
+                            : launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s, gf),
+                        "fp8 quantize dO"));
     }
     // dgrad 1: dH = dO W2 against W2^T in FP8, activation backward in the epilogue
     GemmArgs p = blank();
@@ -1192,6 +1243,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     p.a_sexp = gs;
     p.b_sexp = shared ? ss2_t : s2_t;
     p.b_sexp_gstride = f;
+    p.blk_scales = blk;
     p.c = dpre;
     p.ldc = P;
     p.c_rowidx = 1;
@@ -1212,7 +1264,9 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     // the bf16 pre-activation gradient -> FP8 rows
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s, gf), "fp8 quantize dpre"));
+      MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(dpre, rows, P, P, valid, pq, P, (uint8_t*)ps, s, gf)
+                            : launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s, gf),
+                        "fp8 quantize dpre"));
     }
     // dgrad 2: dX = dpre W13 against W13^T in FP8
     GemmArgs q = blank();
@@ -1221,6 +1275,7 @@ int ffn_bwd_fp8_impl(bool fp8w, const moe_desc* desc, const void* x_perm, const 
     q.a_sexp = ps;
     q.b_sexp = shared ? ss13_t : s13_t;
     q.b_sexp_gstride = d;
+    q.blk_scales = blk;
     q.c = shared ? dx_shared : dx_perm;
     q.ldc = d;
     q.c_rowidx = 1;
@@ -1319,7 +1374,7 @@ int moe_grouped_ffn_bwd_fp8(const moe_desc* desc, const void* x_perm, const int3
                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
                             void* ws, size_t ws_bytes, void* stream) {
-  return ffn_bwd_fp8_impl(false, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
+  return ffn_bwd_fp8_impl(false, false, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
                           ss13_t, sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
                           dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
 }
@@ -1332,8 +1387,36 @@ int moe_grouped_ffn_bwd_fp8w(const moe_desc* desc, const void* x_perm, const int
                              const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
                              void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
                              void* ws, size_t ws_bytes, void* stream) {
-  return ffn_bwd_fp8_impl(true, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
+  return ffn_bwd_fp8_impl(false, true, desc, x_perm, offsets, x, w13q_t, s13_t, w2q_t, s2_t, sw13q_t,
                           ss13_t, sw2q_t, ss2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
+                          dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
+}
+
+int moe_grouped_ffn_bwd_fp8b(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w13q_t, const uint8_t* b13_t,
+                             const void* w2q_t, const uint8_t* b2_t, const void* sw13q_t,
+                             const uint8_t* sb13_t, const void* sw2q_t, const uint8_t* sb2_t,
+                             const void* save_pre, const void* save_h, const void* save_pre_s,
+                             const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                             void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return ffn_bwd_fp8_impl(true, false, desc, x_perm, offsets, x, w13q_t, (const int32_t*)b13_t, w2q_t,
+                          (const int32_t*)b2_t, sw13q_t, (const int32_t*)sb13_t, sw2q_t,
+                          (const int32_t*)sb2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
+                          dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
+}
+
+int moe_grouped_ffn_bwd_fp8bw(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                              const void* x, const void* w13q_t, const uint8_t* b13_t,
+                              const void* w2q_t, const uint8_t* b2_t, const void* sw13q_t,
+                              const uint8_t* sb13_t, const void* sw2q_t, const uint8_t* sb2_t,
+                              const void* save_pre, const void* save_h, const void* save_pre_s,
+                              const void* save_h_s, const void* dout, const void* dy, void* dx_perm,
+                              void* dx_shared, void* dw13, void* dw2, void* dsw13, void* dsw2,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return ffn_bwd_fp8_impl(true, true, desc, x_perm, offsets, x, w13q_t, (const int32_t*)b13_t, w2q_t,
+                          (const int32_t*)b2_t, sw13q_t, (const int32_t*)sb13_t, sw2q_t,
+                          (const int32_t*)sb2_t, save_pre, save_h, save_pre_s, save_h_s, dout, dy,
                           dx_perm, dx_shared, dw13, dw2, dsw13, dsw2, ws, ws_bytes, stream);
 }
 

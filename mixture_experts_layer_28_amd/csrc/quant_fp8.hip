@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_fp8_kernel(
 // line. One thread per 8 elements (a 16-byte chunk); the four threads of a
 // block agree on its maximum through two lane swaps. Grid: x = rows,
 // y = chunks of 256 threads over 16 * KW chunks per row.
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t K, int64_t ld_src, const int32_t* __restrict__ valid_rows,
     uint8_t* __restrict__ codes, int64_t ld_q, uint8_t* __restrict__ scales, int64_t KW) {
@@ -156,12 +157,9 @@ __global__ __launch_bounds__(256) void quant_blocks_fp8_kernel(
     const uint32_t t = __shfl_xor(m, o, 64);
     m = t > m ? t : m;
   }
-  const float amax = bf2f(m);
-  int ex = 0;
-  const float mant = frexpf(amax, &ex);
-  int e = m == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
+  int e = fp8_scale_exp<FMT>(m, bf2f(m));
   e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  if (c < nch) *reinterpret_cast<uint2*>(codes + row * ld_q + 8 * c) = to_e4m3(v, e);
+  if (c < nch) *reinterpret_cast<uint2*>(codes + row * ld_q + 8 * c) = to_fp8<FMT>(v, e);
   if ((c & 3) == 0) {
     const int64_t b = c >> 2;   // block
     scales[(((row >> 5) * KW + (b >> 2)) * 32 + (row & 31)) * 4 + (b & 3)] = (uint8_t)(e + 127);
@@ -483,6 +481,109 @@ __global__ __launch_bounds__(256) void colmax_reduce_fp8_kernel(const uint16_t* 
   sexp[g * C + col] = mm == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 9 : ex - 8);
 }
 
+// ---- square blocks: one exponent per 32 x 32 square of a weight, both layouts
+// G row-major R x C bf16 matrices. Square (i, j) (rows 32i .. 32i+31, columns
+// 32j .. 32j+31 of one matrix, partial at its edges) gets e = the per-row rule
+// on the square's maximum, clipped to [-127, 127]. A square is a 1 x 32 block
+// of every row it covers, in the matrix and in its transpose, so one read
+// writes:
+//   codes [G*R, C]   and its block-scale words (rows G*R, K = C), and
+//   codes_t [G, C, R] and its block-scale words (rows G*C, K = R),
+// in moe_quantize_fp8_blocks' 32-row interleaved layout (byte e + 127; blocks
+// past the edge hold 127), with the same code in both layouts.
+// Workgroup (x, y, g): the 128 x 128 tile at rows 128y, columns 128x of
+// matrix g; wave w takes the tile's rows 32w .. 32w+31 (one row of squares).
+// Load i of lane l reads 16 bytes (8 columns) of row 32w + 4i + (l >> 4),
+// chunk l & 15, so 16 lanes cover a 256-byte row piece; each lane's 8 chunks
+// lie in one square (column block (l & 15) / 4), whose maximum comes from
+// lane swaps over the 16 lanes of that square. The codes go to global memory
+// (128 bytes per row piece per load) and to LDS; then lane l of wave w reads
+// the 4 x 4 byte blocks of columns 4(8w + (l & 7)) .. +3, rows
+// 16(l >> 3) .. +15, transposes them and stores 16 codes to each of its 4
+// output rows: every store instruction writes eight whole 128-byte lines.
+// The scale words of both layouts come from the 16 square exponents in LDS.
+constexpr int kSqT = 128;                  // tile edge
+constexpr int kSqLd = kSqT + 4;            // LDS row stride in bytes (conflict-free dword reads)
+
+__global__ __launch_bounds__(256) void quant_squares_fp8_kernel(
+    const bf16_t* __restrict__ src, int64_t R, int64_t C, uint8_t* __restrict__ codes,
+    uint32_t* __restrict__ scales, uint8_t* __restrict__ codes_t, uint32_t* __restrict__ scales_t) {
+  __shared__ __attribute__((aligned(16))) uint8_t q_s[kSqT * kSqLd];
+  __shared__ uint32_t e_s[4][4];               // byte e + 127 of square (row block, column block)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t g = blockIdx.z, r0 = (int64_t)blockIdx.y * kSqT, c0 = (int64_t)blockIdx.x * kSqT;
+  const bf16_t* x = src + g * R * C;
+  // phase 1 (C % 8 == 0: an 8-column chunk is inside or outside whole)
+  const int ch = lane & 15, rl = lane >> 4;
+  const int64_t col = c0 + 8 * ch;
+  uint4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = r0 + 32 * wave + 4 * i + rl;
+    v[i] = row < R && col < C ? *reinterpret_cast<const uint4*>(x + row * C + col) : make_uint4(0, 0, 0, 0);
+    m = absmax8(v[i], m);
+  }
+  // the square's 16 lanes: lane bits 0, 1 (its 4 chunks) and 4, 5 (row groups)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    if (o == 4 || o == 8) continue;
+    const uint32_t t = __shfl_xor(m, o, 64);
+    m = t > m ? t : m;
+  }
+  int e = fp8_scale_exp<0>(m, bf2f(m));
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  if ((lane & 0x33) == 0) e_s[wave][ch >> 2] = (uint32_t)(e + 127);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rloc = 32 * wave + 4 * i + rl;
+    const int64_t row = r0 + rloc;
+    const uint2 q = to_fp8<0>(v[i], e);
+    if (row < R && col < C) *reinterpret_cast<uint2*>(codes + (g * R + row) * C + col) = q;
+    *reinterpret_cast<uint32_t*>(q_s + rloc * kSqLd + 8 * ch) = q.x;
+    *reinterpret_cast<uint32_t*>(q_s + rloc * kSqLd + 8 * ch + 4) = q.y;
+  }
+  __syncthreads();
+  // the rows' scale words: tile row t takes the four column blocks' bytes of
+  // its row block
+  if (tid < kSqT && r0 + tid < R) {
+    const int rb = tid >> 5;
+    const int64_t rowg = g * R + r0 + tid, KW = (C + kSqT - 1) / kSqT;
+    scales[((rowg >> 5) * KW + c0 / kSqT) * 32 + (rowg & 31)] =
+        e_s[rb][0] | (e_s[rb][1] << 8) | (e_s[rb][2] << 16) | (e_s[rb][3] << 24);
+  }
+  // phase 2: output rows (tile columns) 4cq .. 4cq+3, k (tile rows) 16rq .. 16rq+15
+  const int cq = 8 * wave + (lane & 7), rq = lane >> 3;
+  uint32_t o[4][4];   // o[c][i]: output row 4cq + c, k 16rq + 4i .. +3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      w[s2] = *reinterpret_cast<const uint32_t*>(q_s + (16 * rq + 4 * i + s2) * kSqLd + 4 * cq);
+    // 4 x 4 byte transpose: byte c of rows 0..3 -> bytes 0..3 of o[c][i]
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c][i] = ((w[0] >> (8 * c)) & 0xffu) | (((w[1] >> (8 * c)) & 0xffu) << 8) |
+                (((w[2] >> (8 * c)) & 0xffu) << 16) | (((w[3] >> (8 * c)) & 0xffu) << 24);
+  }
+  const int64_t k0 = r0 + 16 * rq;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t col = c0 + 4 * cq + c;
+    if (col < C && k0 < R)
+      *reinterpret_cast<uint4*>(codes_t + (g * C + col) * R + k0) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+  }
+  // transposed scale words: output row c0 + t takes the four row blocks' bytes
+  // of its column block
+  if (tid < kSqT && c0 + tid < C) {
+    const int cb = tid >> 5;
+    const int64_t rowt = g * C + c0 + tid, KWt = (R + kSqT - 1) / kSqT;
+    scales_t[((rowt >> 5) * KWt + r0 / kSqT) * 32 + (rowt & 31)] =
+        e_s[0][cb] | (e_s[1][cb] << 8) | (e_s[2][cb] << 16) | (e_s[3][cb] << 24);
+  }
+}
+
 }  // namespace
 
 size_t quant_fp8_both_ws(int64_t G, int64_t R, int64_t C) {
@@ -569,14 +670,31 @@ hipError_t launch_set_bounds(int32_t* bounds, int32_t lo, int32_t hi, hipStream_
 // Block-scaled rows: codes [rows, K] (row stride ld_q) and 32-row
 // interleaved scale words (ceil(rows / 32) * 32 * ceil(K / 128) words).
 // K % 8 == 0, 16-byte aligned source rows.
+// fmt: 0 = E4M3, 1 = E5M2.
 hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int64_t ld_src,
                                    const int32_t* valid_rows, void* codes, int64_t ld_q,
-                                   uint8_t* scales, hipStream_t st) {
+                                   uint8_t* scales, hipStream_t st, int fmt) {
   if (rows == 0 || K == 0) return hipSuccess;
   const int64_t KW = (K + 127) / 128;
   const dim3 grid((unsigned)rows, (unsigned)((KW * 16 + 255) / 256));
-  hipLaunchKernelGGL(quant_blocks_fp8_kernel, grid, dim3(256), 0, st, (const bf16_t*)src, K, ld_src,
-                     valid_rows, (uint8_t*)codes, ld_q, scales, KW);
+  if (fmt == 1)
+    hipLaunchKernelGGL(quant_blocks_fp8_kernel<1>, grid, dim3(256), 0, st, (const bf16_t*)src, K, ld_src,
+                       valid_rows, (uint8_t*)codes, ld_q, scales, KW);
+  else
+    hipLaunchKernelGGL(quant_blocks_fp8_kernel<0>, grid, dim3(256), 0, st, (const bf16_t*)src, K, ld_src,
+                       valid_rows, (uint8_t*)codes, ld_q, scales, KW);
+  return hipGetLastError();
+}
+
+// Square-block weights, both layouts (quant_squares_fp8_kernel). R % 16 == 0,
+// C % 16 == 0; scales: ceil(G*R / 32) * 32 * ceil(C / 128) words, scales_t:
+// ceil(G*C / 32) * 32 * ceil(R / 128) words.
+hipError_t launch_quant_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
+                                    uint8_t* scales, void* codes_t, uint8_t* scales_t, hipStream_t st) {
+  if (G == 0 || R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + kSqT - 1) / kSqT), (unsigned)((R + kSqT - 1) / kSqT), (unsigned)G);
+  hipLaunchKernelGGL(quant_squares_fp8_kernel, grid, dim3(256), 0, st, (const bf16_t*)src, R, C,
+                     (uint8_t*)codes, (uint32_t*)scales, (uint8_t*)codes_t, (uint32_t*)scales_t);
   return hipGetLastError();
 }
 

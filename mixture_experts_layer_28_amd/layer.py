@@ -9,12 +9,13 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_BWD_FP8W, MOE_OP_FFN_FWD,
-               MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats,
-               bias_update, combine, combine_bwd, fp8_block_scale_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8,
-               grouped_ffn_fwd, grouped_ffn_fwd_fp8, grouped_ffn_fwd_fp8b, make_desc, permute,
-               permute_bwd, quantize_fp8, quantize_fp8_blocks, quantize_fp8_both,
-               quantize_fp8_both_ws, quantize_fp8_t, route, route_bwd, workspace_size)
+from . import (MOE_OP_AUX_STATS, MOE_OP_FFN_BWD, MOE_OP_FFN_BWD_FP8, MOE_OP_FFN_BWD_FP8B, MOE_OP_FFN_BWD_FP8BW,
+               MOE_OP_FFN_BWD_FP8W, MOE_OP_FFN_FWD, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_FWD_FP8B, MOE_OP_PERMUTE,
+               MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, aux_stats, bias_update, combine, combine_bwd,
+               fp8_block_scale_bytes, grouped_ffn_bwd, grouped_ffn_bwd_fp8, grouped_ffn_fwd,
+               grouped_ffn_fwd_fp8, grouped_ffn_fwd_fp8b, make_desc, permute, permute_bwd, quantize_fp8,
+               quantize_fp8_blocks, quantize_fp8_both, quantize_fp8_both_ws, quantize_fp8_squares,
+               quantize_fp8_t, route, route_bwd, workspace_size)
 
 
 class MoELayer:
@@ -41,11 +42,14 @@ class MoELayer:
     bf16. The transposed codes a forward made serve the next backward on the
     same weight tensors (weights do not change between the two).
 
-    fp8_scale picks the forward's scaling: "row" (one power-of-two scale per
-    operand row) or "block" (one per 32 elements along K of each row, e8m0
-    bytes, on the block-scaled matrix instructions). The backward's FP8 GEMMs
-    keep per-row scales either way; with "block" the backward quantizes the
-    weight transposes itself.
+    fp8_scale picks the scaling: "row" (one power-of-two scale per operand
+    row), "block" (forward only: one per 32 elements along K of each row, e8m0
+    bytes, on the block-scaled matrix instructions; the backward's FP8 GEMMs
+    keep per-row scales and quantize the weight transposes themselves), or
+    "square" (weights in 32 x 32 squares, one quantization per weight serving
+    the forward and the data gradients, written in both layouts from one
+    read; activations and gradients in blocks of 32 along K, forward and data
+    gradients on the block-scaled instructions).
 
     fp8_wgrad (with fp8_bwd) runs the weight gradients on FP8 operands too:
     the library quantizes dO, H, dpre and x_perm along the token axis (one
@@ -67,9 +71,10 @@ class MoELayer:
         self.fp8_fwd, self.fp8_bwd = fp8_fwd, fp8_bwd
         if (fp8_fwd or fp8_bwd) and dtype != "bf16":
             raise ValueError("the FP8 GEMMs keep bf16 activations: dtype must be bf16")
-        if fp8_scale not in ("row", "block"):
-            raise ValueError(f"fp8_scale must be 'row' or 'block' (got {fp8_scale!r})")
-        self.fp8_block = fp8_fwd and fp8_scale == "block"
+        if fp8_scale not in ("row", "block", "square"):
+            raise ValueError(f"fp8_scale must be 'row', 'block' or 'square' (got {fp8_scale!r})")
+        self.fp8_square = fp8_scale == "square" and (fp8_fwd or fp8_bwd)
+        self.fp8_block = fp8_fwd and fp8_scale in ("block", "square")
         if fp8_wgrad and not fp8_bwd:
             raise ValueError("fp8_wgrad runs with the FP8 data gradients: set fp8_bwd too")
         self.fp8_wgrad = fp8_wgrad
@@ -119,20 +124,23 @@ class MoELayer:
         self.dx_router = z(T, d, dtype=f32)
         self.dw_r = z(E, d, dtype=f32)
         self.dX = z(T, d)
-        if fp8_fwd:
-            u8 = torch.uint8
-            # per-row exponents (int32), or the block-scale array of the
-            # [rows, K] matrix (bytes)
-            # (rows: the operand's leading shape; K: its row length)
-            if self.fp8_block:
-                def sc(rows, K):
-                    n = 1
-                    for r in rows:
-                        n *= r
-                    return z(fp8_block_scale_bytes(n, K), dtype=u8)
-            else:
-                def sc(rows, K):
-                    return z(*rows, dtype=i32)
+        u8 = torch.uint8
+
+        # per-row exponents (int32), or the block-scale array of the
+        # [rows, K] matrix (bytes)
+        # (rows: the operand's leading shape; K: its row length)
+        def sc_blk(rows, K):
+            n = 1
+            for r in rows:
+                n *= r
+            return z(fp8_block_scale_bytes(n, K), dtype=u8)
+
+        def sc_row(rows, K):
+            return z(*rows, dtype=i32)
+        # the square quantizer writes both layouts: rows for the forward,
+        # transposes for the data gradients
+        if fp8_fwd or self.fp8_square:
+            sc = sc_blk if self.fp8_block or self.fp8_square else sc_row
             self.xq_perm, self.sx_perm = z(R, d, dtype=u8), sc((R,), d)
             self.w13q, self.s13 = z(E, P, d, dtype=u8), sc((E, P), d)
             self.w2q, self.s2 = z(E, d, f, dtype=u8), sc((E, d), f)
@@ -140,19 +148,23 @@ class MoELayer:
             self.xq, self.sx = (z(T, d, dtype=u8), sc((T,), d)) if sh else (None, None)
             self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), sc((1, P), d)) if sh else (None, None)
             self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), sc((1, d), f)) if sh else (None, None)
-        if fp8_bwd:
-            u8 = torch.uint8
+        if fp8_bwd or self.fp8_square:
             sh = bool(n_shared)
-            self.w13q_t, self.s13_t = z(E, d, P, dtype=u8), z(E, d, dtype=i32)
-            self.w2q_t, self.s2_t = z(E, f, d, dtype=u8), z(E, f, dtype=i32)
-            self.sw13q_t, self.ss13_t = (z(1, d, P, dtype=u8), z(1, d, dtype=i32)) if sh else (None, None)
-            self.sw2q_t, self.ss2_t = (z(1, f, d, dtype=u8), z(1, f, dtype=i32)) if sh else (None, None)
+            sct = sc_blk if self.fp8_square else sc_row
+            self.w13q_t, self.s13_t = z(E, d, P, dtype=u8), sct((E, d), P)
+            self.w2q_t, self.s2_t = z(E, f, d, dtype=u8), sct((E, f), d)
+            self.sw13q_t, self.ss13_t = (z(1, d, P, dtype=u8), sct((1, d), P)) if sh else (None, None)
+            self.sw2q_t, self.ss2_t = (z(1, f, d, dtype=u8), sct((1, f), d)) if sh else (None, None)
+        if self.fp8_square:
+            bwd_op = MOE_OP_FFN_BWD_FP8BW if fp8_wgrad else MOE_OP_FFN_BWD_FP8B
+        else:
+            bwd_op = MOE_OP_FFN_BWD_FP8W if fp8_wgrad else MOE_OP_FFN_BWD_FP8
         ops = [MOE_OP_ROUTE, MOE_OP_AUX_STATS, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD,
                MOE_OP_ROUTE_BWD] + \
               ([MOE_OP_FFN_FWD_FP8B if self.fp8_block else MOE_OP_FFN_FWD_FP8] if fp8_fwd else []) + \
-              ([MOE_OP_FFN_BWD_FP8W if fp8_wgrad else MOE_OP_FFN_BWD_FP8] if fp8_bwd else [])
+              ([bwd_op] if fp8_bwd else [])
         wsb = max(workspace_size(self.desc, op) for op in ops)
-        if fp8_fwd and fp8_bwd:   # both weight orientations from the forward's one pass
+        if fp8_fwd and fp8_bwd and not self.fp8_square:   # both orientations from the forward's pass
             wsb = max(wsb, quantize_fp8_both_ws((E, P, d)), quantize_fp8_both_ws((E, d, f)))
         self._wt_from = None      # weights whose transposed codes the forward made
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
@@ -170,12 +182,17 @@ class MoELayer:
         if self.fp8_block:
             quantize_fp8_blocks(self.x_perm, self.xq_perm, self.sx_perm,
                                 valid_rows=self.offsets[self.E:])
-            quantize_fp8_blocks(w13, self.w13q, self.s13)
-            quantize_fp8_blocks(w2, self.w2q, self.s2)
+            if self.fp8_square:
+                # both layouts from one read; the backward reuses the transposes
+                self._quantize_squares(w13, w2, sw13, sw2)
+            else:
+                quantize_fp8_blocks(w13, self.w13q, self.s13)
+                quantize_fp8_blocks(w2, self.w2q, self.s2)
             if self.n_shared:
                 quantize_fp8_blocks(x, self.xq, self.sx)
-                quantize_fp8_blocks(sw13, self.sw13q, self.ss13)
-                quantize_fp8_blocks(sw2, self.sw2q, self.ss2)
+                if not self.fp8_square:
+                    quantize_fp8_blocks(sw13, self.sw13q, self.ss13)
+                    quantize_fp8_blocks(sw2, self.sw2q, self.ss2)
             grouped_ffn_fwd_fp8b(D, self.xq_perm, self.sx_perm, self.offsets, self.xq, self.sx,
                                  self.w13q, self.s13, self.w2q, self.s2, self.sw13q, self.ss13,
                                  self.sw2q, self.ss2, self.save_pre, self.save_h, self.save_pre_s,
@@ -209,10 +226,28 @@ class MoELayer:
         combine(D, self.out, self.out_shared, self.gate, self.row_of, self.Y)
         return self.Y
 
+    def _quantize_squares(self, w13, w2, sw13, sw2):
+        quantize_fp8_squares(w13, self.w13q, self.s13, self.w13q_t, self.s13_t)
+        quantize_fp8_squares(w2, self.w2q, self.s2, self.w2q_t, self.s2_t)
+        if self.n_shared:
+            quantize_fp8_squares(sw13, self.sw13q, self.ss13, self.sw13q_t, self.ss13_t)
+            quantize_fp8_squares(sw2, self.sw2q, self.ss2, self.sw2q_t, self.ss2_t)
+        self._wt_from = (w13.data_ptr(), w2.data_ptr())
+
     def backward(self, dy, x, w_r, w13, w2, sw13=None, sw2=None):
         D = self.desc
         combine_bwd(D, dy, self.out, self.gate, self.row_of, self.dgate, self.dout)
-        if self.fp8_bwd:
+        if self.fp8_bwd and self.fp8_square:
+            if self._wt_from != (w13.data_ptr(), w2.data_ptr()):
+                self._quantize_squares(w13, w2, sw13, sw2)
+            self._wt_from = None
+            grouped_ffn_bwd_fp8(D, self.x_perm, self.offsets, x, self.w13q_t, self.s13_t,
+                                self.w2q_t, self.s2_t, self.sw13q_t, self.ss13_t, self.sw2q_t,
+                                self.ss2_t, self.save_pre, self.save_h, self.save_pre_s,
+                                self.save_h_s, self.dout, dy, self.dx_perm, self.dx_shared,
+                                self.dw13, self.dw2, self.dsw13, self.dsw2, self.ws,
+                                fp8_wgrad=self.fp8_wgrad, block=True)
+        elif self.fp8_bwd:
             # the forward already made the transposed codes of these weights
             # (FP8 forward); otherwise quantize them here
             if self._wt_from != (w13.data_ptr(), w2.data_ptr()):

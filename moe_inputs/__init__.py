@@ -33,7 +33,8 @@ Routing variants and the per-GPU shard:
   dsv3_ep8_shard_bf16 the DeepSeek-like layer's local share under 8-way expert
                       parallelism: 32 experts, about 2048 rows each
 FP8 variants (*_fp8_*: per-row scales, *_fp8b_*: one scale per 32 elements
-along K) of the Mixtral-like layer and of that shard.
+along K, *_fp8sq_*: 32 x 32 weight squares with 32-element activation and
+gradient blocks) of the Mixtral-like layer and of that shard.
 """
 from __future__ import annotations
 
@@ -69,7 +70,7 @@ class Workload:
     bias_gamma: float = 0.0       # aux-loss-free bias update speed (needs sel_bias)
     gumbel_tau: Optional[float] = None   # noisy gate temperature; draws uniforms [T, E]
     fp8: bool = False             # forward GEMMs on E4M3 operands (bf16 activations)
-    fp8_scale: str = "row"        # the forward's FP8 scales: "row" or "block" (32 along K)
+    fp8_scale: str = "row"        # FP8 scales: "row", "block" (32 along K, forward) or "square"
     fp8_bwd: bool = False         # backward data-gradient GEMMs on E4M3 operands as well
     fp8_wgrad: bool = False       # and the weight-gradient GEMMs (token-axis block scales)
     fp8_grad: str = "e4m3"        # FP8 format of the backward's gradient operands: e4m3 or e5m2
@@ -135,6 +136,17 @@ WORKLOADS = {
     "mixtral_fp8_all_e5m2_bf16": Workload("mixtral_fp8_all_e5m2_bf16", T=8192, d=4096, E=8, k=2,
                                           f=14336, cf=1.25, fp8=True, fp8_bwd=True, fp8_wgrad=True,
                                           fp8_grad="e5m2"),
+    # square-block weights: the forward and data gradients on block scales, one
+    # weight quantization for both
+    "mixtral_fp8sq_dgrad_bf16": Workload("mixtral_fp8sq_dgrad_bf16", T=8192, d=4096, E=8, k=2,
+                                         f=14336, cf=1.25, fp8=True, fp8_bwd=True, fp8_scale="square"),
+    "mixtral_fp8sq_all_bf16": Workload("mixtral_fp8sq_all_bf16", T=8192, d=4096, E=8, k=2, f=14336,
+                                       cf=1.25, fp8=True, fp8_bwd=True, fp8_wgrad=True,
+                                       fp8_scale="square"),
+    "dsv3_ep8_shard_fp8sq_all_bf16": Workload("dsv3_ep8_shard_fp8sq_all_bf16", T=8192, d=7168, E=32,
+                                              k=8, f=2048, score="sigmoid", n_shared=1,
+                                              sel_bias=True, fp8=True, fp8_bwd=True, fp8_wgrad=True,
+                                              fp8_scale="square"),
 }
 
 

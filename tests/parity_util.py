@@ -53,11 +53,40 @@ def bits(t):
 
 # -------------------------------------------------------------- runners
 def oracle_fp8(w: Workload):
-    """The oracle's fp8 argument for a workload: False, True (per-row scales)
-    or "block"."""
+    """The oracle's fp8 argument for a workload: False, True (per-row scales),
+    "block" or "square"."""
     if not w.fp8:
         return False
-    return "block" if w.fp8_scale == "block" else True
+    return w.fp8_scale if w.fp8_scale in ("block", "square") else True
+
+
+def oracle_fp8_dgrad(w: Workload):
+    """The oracle's fp8_dgrad argument: False, True (per-row) or "square"."""
+    if not w.fp8_bwd:
+        return False
+    return "square" if w.fp8_scale == "square" else True
+
+
+def block_bytes(buf, rows, K):
+    """[rows, 4 * ceil(K / 128)] bytes (row, block) out of the 32-row
+    interleaved scale array: word w of row r is word (r // 32 * KW + w) * 32
+    + r % 32, its byte j the scale of block 4w + j."""
+    KW = -(-K // 128)
+    words = np.asarray(buf, dtype=np.uint8).view("<u4")
+    r = np.arange(rows)[:, None]
+    w = np.arange(KW)[None, :]
+    sel = words[(r // 32 * KW + w) * 32 + r % 32]                      # [rows, KW]
+    return ((sel[:, :, None] >> (8 * np.arange(4, dtype=np.uint32))) & 0xFF).reshape(rows, 4 * KW)
+
+
+def decode_block_codes(codes, scales, row0=0):
+    """Dequantized rows of device E4M3 codes [n, K] whose block-scale bytes
+    are rows row0 .. row0+n-1 of the interleaved array scales."""
+    c = codes.cpu()
+    n, K = c.shape
+    v = c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    b = block_bytes(scales.cpu().numpy(), row0 + n, K)[row0:, : -(-K // 32)].astype(np.float64)
+    return v * np.repeat(np.exp2(b - 127.0), 32, axis=1)[:, :K]
 
 
 def gpu_layer(w: Workload, g: dict):
@@ -81,7 +110,7 @@ def oracle_layer(w: Workload, g: dict):
                           w.gumbel_tau, fp8=oracle_fp8(w))
     bwd = O.layer_backward(fwd, f["x"], f["w_r"], f["w13"], f["w2"], f["dy"], w.score, w.act,
                            w.aux_coef, f["sw13"], f["sw2"], w.z_coef, w.gumbel_tau,
-                           fp8_dgrad=w.fp8_bwd, fp8_wgrad=w.fp8_wgrad, fp8_grad=w.fp8_grad)
+                           fp8_dgrad=oracle_fp8_dgrad(w), fp8_wgrad=w.fp8_wgrad, fp8_grad=w.fp8_grad)
     return fwd, bwd, f
 
 
@@ -345,7 +374,7 @@ def check_fp8_wgrad(w, L, dev, rep, off):
                             L.s2_t, L.sw13q_t, L.ss13_t, L.sw2q_t, L.ss2_t, L.save_pre, L.save_h,
                             L.save_pre_s, L.save_h_s, L.dout, dev["dy"], o["dx_perm"],
                             o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws,
-                            fp8_wgrad=True)
+                            fp8_wgrad=True, block=w.fp8_scale == "square")
     torch.cuda.synchronize()
     assert torch.equal(o["dw13"], L.dw13) and torch.equal(o["dw2"], L.dw2)
     dO, H, X = (to_np(t[:A]) for t in (L.dout, L.save_h, L.x_perm))
@@ -384,12 +413,13 @@ def _fp8_rows_ref(M, fmt="e4m3"):
 
 
 def check_grad_codes(w, L, dev, ws, R, P, A, dp, dps):
-    """The FP8 backward's per-row codes and exponents of its gradient
-    operands (the upstream gradient and dpre), read from the workspace it
-    left, against the oracle's quantizer in the chosen format on the same bf16
-    rows."""
+    """The FP8 backward's codes and scales of its gradient operands (the
+    upstream gradient and dpre), read from the workspace it left, against the
+    oracle's quantizer in the chosen format on the same bf16 rows: per-row
+    exponents, or (square mode) the block-scale bytes of 32-element blocks."""
     import mixture_experts_layer_28_amd as moe
     d = w.d
+    blk = w.fp8_scale == "square"
     al = lambda x: (x + 255) // 256 * 256   # noqa: E731
     base = moe.workspace_size(L.desc, moe.MOE_OP_FFN_BWD)
     raw = ws.cpu().numpy()
@@ -397,14 +427,21 @@ def check_grad_codes(w, L, dev, ws, R, P, A, dp, dps):
         rows, g_src, p_src = w.T, to_np(dev["dy"]), dps
     else:
         rows, g_src, p_src = A, to_np(L.dout[:A]), dp
+    gsb = moe.fp8_block_scale_bytes(R, d) if blk else 4 * R
+    psb = moe.fp8_block_scale_bytes(R, P) if blk else 4 * R
     gq = raw[base: base + R * d].reshape(R, d)[:rows]
-    gs = raw[base + al(R * d): base + al(R * d) + 4 * R].view(np.int32)[:rows]
-    o_pq = base + al(R * d) + al(R * 4)
+    gs = raw[base + al(R * d): base + al(R * d) + gsb]
+    o_pq = base + al(R * d) + al(gsb)
     pq = raw[o_pq: o_pq + R * P].reshape(R, P)[:rows]
-    ps = raw[o_pq + al(R * P): o_pq + al(R * P) + 4 * R].view(np.int32)[:rows]
-    for name, q, e, src in (("dO", gq, gs, g_src), ("dpre", pq, ps, p_src)):
-        rc, re_ = O.quantize_rows_fp8(src, w.fp8_grad)
-        assert (e == re_).all(), f"{name} exponents differ ({w.fp8_grad})"
+    ps = raw[o_pq + al(R * P): o_pq + al(R * P) + psb]
+    for name, q, sbuf, src, K in (("dO", gq, gs, g_src, d), ("dpre", pq, ps, p_src, P)):
+        if blk:
+            rc, re_ = O.quantize_blocks_fp8(src, fmt=w.fp8_grad)
+            got_e = block_bytes(sbuf, rows, K)[:, : re_.shape[1]].astype(np.int64) - 127
+        else:
+            rc, re_ = O.quantize_rows_fp8(src, w.fp8_grad)
+            got_e = sbuf.view(np.int32)[:rows]
+        assert (got_e == re_).all(), f"{name} exponents differ ({w.fp8_grad})"
         bad = np.argwhere(q != rc)
         assert bad.size == 0, f"{name} {w.fp8_grad} codes differ: {len(bad)}, first {bad[:4].tolist()}"
 
@@ -436,7 +473,8 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
     into fresh buffers (bitwise identical: deterministic); read its bf16
     pre-activation gradient dpre from the workspace and compare it with the
     oracle's; and check dX against the FP8 product of the GPU's own dpre,
-    requantized by _e4m3_rows_ref, with the GPU's transposed weight codes."""
+    requantized by _e4m3_rows_ref (square mode: the oracle's 32-element
+    blocks), with the GPU's transposed weight codes."""
     import mixture_experts_layer_28_amd as moe
     dt = w.dtype
     A = int(off[-1])
@@ -448,19 +486,29 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
                             L.s2_t, L.sw13q_t, L.ss13_t, L.sw2q_t, L.ss2_t, L.save_pre, L.save_h,
                             L.save_pre_s, L.save_h_s, L.dout, dev["dy"], o["dx_perm"],
                             o["dx_shared"], o["dw13"], o["dw2"], o["dsw13"], o["dsw2"], ws,
-                            fp8_wgrad=w.fp8_wgrad)
+                            fp8_wgrad=w.fp8_wgrad, block=w.fp8_scale == "square")
     torch.cuda.synchronize()
     assert torch.equal(o["dx_perm"][:A], L.dx_perm[:A]), "FP8 backward is not deterministic"
     assert torch.equal(o["dw13"], L.dw13) and torch.equal(o["dw2"], L.dw2)
     dpre = ws[: R * P * 2].view(torch.bfloat16).view(R, P)
     assert_close("dpre", to_np(dpre[:A])[g_rows], bwd["dpre"][o_rows], dt, rep)
-    w13t = [_decode_codes(L.w13q_t[e], L.s13_t[e]) for e in range(w.E)]   # [d, P] each
+    sq = w.fp8_scale == "square"
+    if sq:
+        w13t = decode_block_codes(L.w13q_t.reshape(w.E * w.d, P), L.s13_t).reshape(w.E, w.d, P)
+
+        def qg(m):
+            return O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m, fmt=w.fp8_grad), fmt=w.fp8_grad)
+    else:
+        w13t = [_decode_codes(L.w13q_t[e], L.s13_t[e]) for e in range(w.E)]   # [d, P] each
+
+        def qg(m):
+            return _fp8_rows_ref(m, w.fp8_grad)
     dp = to_np(dpre[:A])
     got, ref = [], []
     for e in range(w.E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi > lo:
-            ref.append(_fp8_rows_ref(dp[lo:hi], w.fp8_grad) @ w13t[e].T)
+            ref.append(qg(dp[lo:hi]) @ w13t[e].T)
             got.append(to_np(L.dx_perm[lo:hi]))
     if got:
         assert_close("dX_perm(own dpre)", np.concatenate(got), np.concatenate(ref), dt, rep)
@@ -468,9 +516,8 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
         off_s = (R * P * 2 + 255) // 256 * 256
         dps = to_np(ws[off_s: off_s + w.T * P * 2].view(torch.bfloat16).view(w.T, P))
         assert_close("dpre_shared", dps, bwd["dpre_shared"], dt, rep)
-        wst = _decode_codes(L.sw13q_t[0], L.ss13_t[0])
-        assert_close("dX_shared(own dpre)", to_np(L.dx_shared), _fp8_rows_ref(dps, w.fp8_grad) @ wst.T, dt,
-                     rep)
+        wst = decode_block_codes(L.sw13q_t[0], L.ss13_t) if sq else _decode_codes(L.sw13q_t[0], L.ss13_t[0])
+        assert_close("dX_shared(own dpre)", to_np(L.dx_shared), qg(dps) @ wst.T, dt, rep)
     # the gradient codes in the workspace, bit for bit (E4M3 or E5M2): the
     # shared expert's rows overwrite the routed ones when there is one
     check_grad_codes(w, L, dev, ws, R, P, A, dp, dps if w.n_shared else None)
@@ -479,11 +526,11 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
 def check_fp8_down_own_h(w, L, f, off, rep):
     """FP8 down-projection of the GPU's own bf16 H (routed experts, and the
     shared expert on all tokens), recomputed by the oracle: E4M3 codes of H
-    against the quantized W2 (per row, or per 32-element block with
-    fp8_scale "block"), held to the bf16 bound."""
-    if w.fp8_scale == "block":
+    against the quantized W2 (per row, per 32-element block with fp8_scale
+    "block", 32 x 32 squares with "square"), held to the bf16 bound."""
+    if w.fp8_scale in ("block", "square"):
         qa = lambda m: O.dequantize_blocks_fp8(*O.quantize_blocks_fp8(m))   # noqa: E731
-        qw = O.quantize_weights_fp8_block
+        qw = O.quantize_weights_fp8_square if w.fp8_scale == "square" else O.quantize_weights_fp8_block
     else:
         qa = lambda m: O.dequantize_rows_fp8(*O.quantize_rows_fp8(m))   # noqa: E731
         qw = O.quantize_weights_fp8

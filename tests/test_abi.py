@@ -21,11 +21,11 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = moe.lib()
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 29
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
 
 
 # fake, aligned, non-null device addresses: validation must fail (or, for
@@ -413,3 +413,65 @@ def test_fp8_quantize_both_validation():
     # 2 * ceil(64 / 64) * 48 * 2 = 192 bytes -> 256 needed
     assert call(ws_bytes=255) == 3 and call(ws=0) == 3
     assert call(G=0) == 0
+
+
+def test_fp8_square_quantize_validation():
+    """Bad shapes and pointers fail before any HIP call; G = 0 is a no-op."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ok = dict(src=FAKE, G=2, R=64, C=48, codes=FAKE, sc=FAKE, codes_t=FAKE, sc_t=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        ptr = lambda v: P(v) if v else None   # noqa: E731
+        return L.moe_quantize_fp8_squares(ptr(a["src"]), a["G"], a["R"], a["C"], ptr(a["codes"]),
+                                          ptr(a["sc"]), ptr(a["codes_t"]), ptr(a["sc_t"]), None)
+    for bad in (dict(R=8), dict(R=72), dict(R=0), dict(C=8), dict(C=40), dict(C=1 << 23),
+                dict(R=1 << 23), dict(G=-1), dict(G=70000), dict(src=0), dict(codes=FAKE + 8),
+                dict(sc=0), dict(sc=FAKE + 4), dict(codes_t=0), dict(sc_t=FAKE + 2),
+                # 2^15 matrices of 2^17 rows x 1 word: the row-layout scales reach 2^31 words
+                dict(G=1 << 15, R=1 << 17, C=16)):
+        assert call(**bad) == 1, bad
+        assert L.moe_last_error().decode()
+    assert call(G=0) == 0
+
+
+@pytest.mark.parametrize("name,op", [("moe_grouped_ffn_bwd_fp8b", moe.MOE_OP_FFN_BWD_FP8B),
+                                     ("moe_grouped_ffn_bwd_fp8bw", moe.MOE_OP_FFN_BWD_FP8BW)])
+def test_fp8_block_backward_validation(name, op):
+    """The block-scaled FP8 backward validates like the per-row one; its
+    workspace holds block-scale bytes of dO and dpre in place of one int32
+    per row, and the weight-gradient form adds the token-axis buffers of
+    moe_grouped_ffn_bwd_fp8w."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE)] * 23
+    fn = getattr(L, name)
+
+    def call(d, ws_bytes=1 << 40, p=ptrs):
+        return fn(ctypes.byref(d), *p, P(FAKE), ws_bytes, None)
+    assert call(_desc(dtype="f32")) == 2
+    assert call(_desc(d=72)) == 2 and call(_desc(f=72)) == 2
+    d = _desc(T=64, d=256, E=8, k=2, f=128)
+    sz = {}
+    for o in (moe.MOE_OP_FFN_BWD_FP8, moe.MOE_OP_FFN_BWD_FP8W, op):
+        v = ctypes.c_size_t()
+        assert L.moe_workspace_size(ctypes.byref(d), o, ctypes.byref(v)) == 0
+        sz[o] = v.value
+    al = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    R, P2 = 128, 256
+    # block scales of [128, 256] and [128, 256]: 4 groups of 32 rows x 2 words x 128 bytes
+    blk = al(moe.fp8_block_scale_bytes(R, 256)) + al(moe.fp8_block_scale_bytes(R, P2))
+    row = al(4 * R) + al(4 * R)
+    if op == moe.MOE_OP_FFN_BWD_FP8B:
+        assert sz[op] - sz[moe.MOE_OP_FFN_BWD_FP8] == blk - row
+    else:
+        assert sz[op] - sz[moe.MOE_OP_FFN_BWD_FP8W] == blk - row
+    assert call(d, ws_bytes=sz[op] - 1) == 3
+    # a NULL or misaligned transposed weight or scale array is rejected
+    for i in (3, 4):
+        for bad_v in (None, P(FAKE + 4)):
+            bad = list(ptrs)
+            bad[i] = bad_v
+            assert call(_desc(), p=bad) == 1

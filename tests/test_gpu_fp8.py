@@ -6,6 +6,7 @@ import torch
 
 import oracle as O
 from moe_inputs import bf16_bits_to_f32, to_bf16_bits
+from parity_util import block_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -147,18 +148,6 @@ def _block_rows(rows, K, seed):
     return to_bf16_bits(f)
 
 
-def _block_bytes(buf, rows, K):
-    """[rows, 4 * ceil(K / 128)] bytes (row, block) out of the 32-row
-    interleaved scale array: word w of row r is word (r // 32 * KW + w) * 32
-    + r % 32, its byte j the scale of block 4w + j."""
-    KW = -(-K // 128)
-    words = np.asarray(buf, dtype=np.uint8).view("<u4")
-    r = np.arange(rows)[:, None]
-    w = np.arange(KW)[None, :]
-    sel = words[(r // 32 * KW + w) * 32 + r % 32]                      # [rows, KW]
-    return ((sel[:, :, None] >> (8 * np.arange(4, dtype=np.uint32))) & 0xFF).reshape(rows, 4 * KW)
-
-
 @pytest.mark.parametrize("rows,K", [(9, 16), (11, 48), (12, 208), (10, 4096), (5, 14336),
                                     (9, 2064), (3, 16400), (70, 272)])
 def test_quantize_blocks_bit_exact(rows, K):
@@ -179,7 +168,7 @@ def test_quantize_blocks_bit_exact(rows, K):
     ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
     nb = ref_e.shape[1]
     raw = scales.cpu().numpy()
-    got_s = _block_bytes(raw, rows, K).astype(np.int64)
+    got_s = block_bytes(raw, rows, K).astype(np.int64)
     assert (got_s[:, :nb] == ref_e + 127).all(), np.argwhere(got_s[:, :nb] != ref_e + 127)[:5]
     assert (got_s[:, nb:] == 127).all()
     # the padding rows of the last group of 32 are not written
@@ -205,6 +194,62 @@ def test_quantize_blocks_respects_device_row_bound():
     moe.quantize_fp8_blocks(x, codes, scales, valid_rows=valid)
     torch.cuda.synchronize()
     ref_c, ref_e = O.quantize_blocks_fp8(bf16_bits_to_f32(bits).astype(np.float64))
-    got_c, got_s = codes.cpu().numpy(), _block_bytes(scales.cpu().numpy(), rows, K).astype(np.int64)
+    got_c, got_s = codes.cpu().numpy(), block_bytes(scales.cpu().numpy(), rows, K).astype(np.int64)
     assert (got_c[:6] == ref_c[:6]).all() and (got_s[:6, :3] == ref_e[:6] + 127).all()
     assert (got_c[6:] == 0xAB).all() and (got_s[6:] == 0xCD).all()
+
+
+# ------------------------------------------------------------ square blocks
+def _square_mats(G, R, C, seed):
+    """G bf16 matrices R x C whose 32 x 32 squares are each scaled by their
+    own power of two in 2^-40 .. 2^40, one square zeroed and one pushed below
+    the scale range (its exponent clips at -127)."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal((G, R, C)).astype(np.float32)
+    sh = rng.integers(-40, 41, (G, -(-R // 32), -(-C // 32))).astype(np.float32)
+    f *= np.exp2(sh).repeat(32, axis=1).repeat(32, axis=2)[:, :R, :C]
+    if R > 32 and C > 32:
+        f[0, 32:64, :32] = 0.0
+        f[-1, :32, 32:64] = rng.standard_normal((32, min(32, C - 32))).astype(np.float32) * 2.0 ** -124
+    return to_bf16_bits(f)
+
+
+@pytest.mark.parametrize("G,R,C", [(1, 16, 16), (1, 32, 32), (3, 48, 80), (2, 272, 400),
+                                   (4, 144, 2064), (1, 512, 4096), (8, 128, 128)])
+def test_quantize_squares_bit_exact(G, R, C):
+    """moe_quantize_fp8_squares equals the oracle's square quantization in
+    both layouts: the codes of each matrix and of its transpose, and the
+    block-scale bytes of both (square (i, j)'s exponent + 127 on every row of
+    the square, 127 for the padding blocks up to a whole word), on partial
+    squares at the bottom and right edges and tiles of 128 cut by the edges."""
+    import mixture_experts_layer_28_amd as moe
+    print(f"[case] quantize squares G={G} R={R} C={C}", flush=True)
+    bits = _square_mats(G, R, C, seed=G * 7 + R + C)
+    x = _dev_bf16(bits)
+    codes = torch.empty(G, R, C, dtype=torch.uint8, device="cuda")
+    codes_t = torch.empty(G, C, R, dtype=torch.uint8, device="cuda")
+    sb = torch.full((moe.fp8_block_scale_bytes(G * R, C),), 0xEE, dtype=torch.uint8, device="cuda")
+    sbt = torch.full((moe.fp8_block_scale_bytes(G * C, R),), 0xEE, dtype=torch.uint8, device="cuda")
+    moe.quantize_fp8_squares(x, codes, sb, codes_t, sbt)
+    torch.cuda.synchronize()
+    f = bf16_bits_to_f32(bits).astype(np.float64)
+    got_c, got_ct = codes.cpu().numpy(), codes_t.cpu().numpy()
+    rows_b = block_bytes(sb.cpu().numpy(), G * R, C).astype(np.int64).reshape(G, R, -1)
+    cols_b = block_bytes(sbt.cpu().numpy(), G * C, R).astype(np.int64).reshape(G, C, -1)
+    nbc, nbr = -(-C // 32), -(-R // 32)
+    for g in range(G):
+        rc, re_ = O.quantize_squares_fp8(f[g])
+        bad = np.argwhere(got_c[g] != rc)
+        assert bad.size == 0, f"matrix {g}: {len(bad)} codes differ, first {bad[:5].tolist()}"
+        bad = np.argwhere(got_ct[g] != rc.T)
+        assert bad.size == 0, f"matrix {g}: {len(bad)} transposed codes differ, first {bad[:5].tolist()}"
+        want = np.repeat(re_, 32, axis=0)[:R] + 127                       # [R, nbc]
+        assert (rows_b[g][:, :nbc] == want).all(), np.argwhere(rows_b[g][:, :nbc] != want)[:5]
+        assert (rows_b[g][:, nbc:] == 127).all()
+        want_t = np.repeat(re_.T, 32, axis=0)[:C] + 127                   # [C, nbr]
+        assert (cols_b[g][:, :nbr] == want_t).all(), np.argwhere(cols_b[g][:, :nbr] != want_t)[:5]
+        assert (cols_b[g][:, nbr:] == 127).all()
+    if R > 32 and C > 32:
+        e0 = O.quantize_squares_fp8(f[0])[1]
+        el = O.quantize_squares_fp8(f[-1])[1]
+        assert e0[1, 0] == 0 and el[0, 1] == -127      # the zero and the clipped square

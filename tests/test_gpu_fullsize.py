@@ -14,6 +14,8 @@ launches it (same workload presets, same layer object, one fwd+bwd step):
   mixtral_fp8_all_bf16 every GEMM on FP8 operands (weight gradients with
                     token-axis block scales)
   mixtral_fp8_all_e5m2_bf16 the same with E5M2 gradient operands
+  mixtral_fp8sq_all_bf16 every GEMM on FP8 operands with 32 x 32 weight
+                    squares (forward and data gradients on block scales)
 
 The oracle checks the whole router, statistics and permutation, and sampled
 tokens / sampled hidden columns of the FFN outputs and gradients, computed
@@ -124,24 +126,32 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
     # quantize exactly as in the whole GEMM; each expert's weights are
     # quantized once (w13d, w2d) and sliced like the bf16 ones
     # (block scales: the same holds, blocks run along a row)
+    # (square-block weights: each expert's weight is quantized whole, then
+    # sliced; both GEMM directions read the same dequantized matrix)
     blk = w.fp8 and w.fp8_scale == "block"
+    sq = w.fp8_scale == "square"
 
     def wq(m):
         if not w.fp8:
             return m
+        if sq:
+            return O.quantize_weights_fp8_square(m)
         return O.quantize_weights_fp8_block(m) if blk else O.quantize_weights_fp8(m)
-    efwd = (O.expert_forward_fp8_block_wq if blk else O.expert_forward_fp8_wq) if w.fp8 \
+    efwd = (O.expert_forward_fp8_block_wq if blk or sq else O.expert_forward_fp8_wq) if w.fp8 \
         else O.expert_forward
     # FP8 data gradients: the weights quantized per input channel (rows of the
     # transpose), once per expert; any subset of those rows quantizes the same
     # way, and a token row's dO and dpre are quantized on their own.
     def ebwd(X, w13e, w2e, w13t, w2t, sv, dO):
         if w.fp8_bwd:
-            return O.expert_backward_fp8_wq(X, w2t, w13t, sv, dO, w.act, w.fp8_grad)
+            return O.expert_backward_fp8_wq(X, w2t, w13t, sv, dO, w.act, w.fp8_grad,
+                                            "block" if sq else "row")
         return O.expert_backward(X, w13e, w2e, sv, dO, w.act)
 
     def wq_t(m):
-        return O.quantize_weights_fp8_t(m) if w.fp8_bwd else None
+        if not w.fp8_bwd:
+            return None
+        return O.quantize_weights_fp8_square(m).T if sq else O.quantize_weights_fp8_t(m)
     dxt = fp8_dgrad_tol(w.f, w.fp8_grad) if w.fp8_bwd else {}
     # FP8 weight gradients: the bound of the smallest sampled expert's rows
     nrows = [int(pm["offsets"][e + 1] - pm["offsets"][e]) for e in exps]
@@ -260,11 +270,11 @@ def check_sampled(w, n_tok=24, n_exp=2, n_col=4, seed=123, expert_subset=None):
 @pytest.mark.parametrize("name", ["mixtral_bf16", "skewed_bf16", "skewed_nocap_bf16",
                                   "finegrained_bf16", "dsv3_bf16", "mixtral_fp8_bf16",
                                   "mixtral_fp8_dgrad_bf16", "mixtral_fp8b_bf16", "mixtral_fp8_all_bf16",
-                                  "mixtral_fp8_all_e5m2_bf16"])
+                                  "mixtral_fp8_all_e5m2_bf16", "mixtral_fp8sq_all_bf16"])
 def test_fullsize_sampled(name):
     w = WORKLOADS[name]
     # the oracle's FP8 backward quantizes each sampled expert's weights both
     # ways (about 45 s per Mixtral-like expert on the host), and its block
     # quantizer walks the weights block by block: two experts
-    slow = w.fp8_bwd or w.fp8_scale == "block"
+    slow = w.fp8_bwd or w.fp8_scale in ("block", "square")
     check_sampled(w, expert_subset=(2, 5) if slow else None)

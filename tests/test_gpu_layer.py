@@ -46,6 +46,14 @@ REDUCED = {
     "mixtral_fp8_dgrad_small": WORKLOADS["mixtral_fp8_dgrad_bf16"].replace(T=1536, d=512, f=768),
     "dsv3_fp8_dgrad_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
                                                            fp8_bwd=True),
+    # square-block weights: forward and data gradients on block scales (and the
+    # weight gradients on token-axis blocks; E5M2 gradient operands)
+    "mixtral_fp8sq_dgrad_small": WORKLOADS["mixtral_fp8sq_dgrad_bf16"].replace(T=1536, d=512, f=768),
+    "dsv3_fp8sq_all_small": WORKLOADS["dsv3_bf16"].replace(T=1024, d=512, f=256, fp8=True,
+                                                           fp8_bwd=True, fp8_wgrad=True,
+                                                           fp8_scale="square"),
+    "mixtral_fp8sq_all_e5m2_small": WORKLOADS["mixtral_fp8sq_all_bf16"].replace(T=1536, d=512, f=768,
+                                                                               fp8_grad="e5m2"),
 }
 
 EDGE = {
@@ -140,6 +148,19 @@ EDGE = {
                                     fp8=True, fp8_bwd=True, fp8_wgrad=True, fp8_scale="block"),
     "one_token_fp8_all": Workload("t1f8", T=1, d=128, E=4, k=2, f=96, n_shared=1, fp8=True,
                                   fp8_bwd=True, fp8_wgrad=True, fp8_grad="e5m2"),
+    # square-block weights: partial squares at both edges (d 144, f 208) with
+    # GELU and a shared expert; no routed rows; square data gradients after a
+    # bf16 forward (the backward quantizes the squares), E5M2; 1024 experts
+    "ragged_fp8sq_gelu_shared": Workload("ragged8sq", T=1000, d=144, E=6, k=3, f=208, act="gelu",
+                                         score="sigmoid", n_shared=1, sel_bias=True, fp8=True,
+                                         fp8_bwd=True, fp8_scale="square"),
+    "fp8sq_all_dropped_shared": Workload("drop8sq", T=512, d=256, E=8, k=2, f=256, cf=0.0,
+                                         n_shared=1, fp8=True, fp8_bwd=True, fp8_wgrad=True,
+                                         fp8_scale="square"),
+    "fp8sq_e5m2_dgrad_only": Workload("dg8sq", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
+                                      fp8_bwd=True, fp8_scale="square", fp8_grad="e5m2"),
+    "max_experts_fp8sq_all": Workload("e1024sq", T=640, d=64, E=1024, k=4, f=64, aux_coef=0.01,
+                                      fp8=True, fp8_bwd=True, fp8_wgrad=True, fp8_scale="square"),
 }
 
 
@@ -186,6 +207,27 @@ def test_fp8_block_scales_follow_the_blocks():
     g["w13"] = to_bf16_bits(bf16_bits_to_f32(g["w13"]) / col(sx))
     g["w_r"] = (g["w_r"] / col(sx)).astype(np.float32)
     g["w2"] = to_bf16_bits(bf16_bits_to_f32(g["w2"]) * col(sw))
+    rep, flips, L, dev = run_and_compare(w, g)
+    print(rep, flush=True)
+
+
+def test_fp8_square_scales_follow_the_squares():
+    """Weights whose 32 x 32 squares span many binades: each square of w13
+    and w2 scaled by its own 2^s, s in [-5, 5]. A square's byte applied to
+    another square (a transposed or shifted scale array, the forward's row
+    layout read as the transpose's) then misses the oracle's square-scaled
+    forward and data gradients by far more than the FP8 bound."""
+    from moe_inputs import bf16_bits_to_f32, to_bf16_bits
+    w = WORKLOADS["mixtral_fp8sq_dgrad_bf16"].replace(T=768, d=384, f=512, seed=6)
+    print(f"[case] fp8 square scales {w}", flush=True)
+    g = gen_all(w)
+    rng = np.random.default_rng(12)
+
+    def squares(m):
+        E, R, C = m.shape
+        s = np.exp2(rng.integers(-5, 6, (E, R // 32, C // 32))).astype(np.float32)
+        return to_bf16_bits(bf16_bits_to_f32(m) * s.repeat(32, axis=1).repeat(32, axis=2))
+    g["w13"], g["w2"] = squares(g["w13"]), squares(g["w2"])
     rep, flips, L, dev = run_and_compare(w, g)
     print(rep, flush=True)
 

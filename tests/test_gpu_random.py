@@ -2,7 +2,8 @@
 to 4, token counts 1-700, widths with K and N tails, SwiGLU or GELU, softmax
 or sigmoid scoring, a shared expert or none, capacity factors from dropping
 most assignments to none, fp32 and bf16, and the FP8 variants (per-row or
-block-scaled forward, data gradients, weight gradients) where the widths allow. Every case is compared with the oracle as the
+block-scaled forward, square-block weights, data gradients, weight gradients,
+E5M2 gradients) where the widths allow. Every case is compared with the oracle as the
 fixed cases are (tests/test_gpu_layer.py); the draws reach grouped tile counts
 and per-XCD remainders that the fixed cases do not."""
 import numpy as np
@@ -33,21 +34,29 @@ def _draw(i):
     fp8_bwd = fp8 and rng.random() < 0.6
     # drawn after the fields above, so the earlier cases keep their draws:
     # cases from 24 on also pick the block-scaled forward and FP8 weight gradients
-    scale, wgrad = "row", False
+    scale, wgrad, gfmt = "row", False, "e4m3"
     if 24 <= i < 36:
         scale = "block" if fp8 and rng.random() < 0.5 else "row"
         fp8_bwd = fp8_bwd or (fp8 and rng.random() < 0.5)
         wgrad = fp8_bwd and rng.random() < 0.8
+    if 36 <= i < 44:
+        # square-block weights, the forward or the data gradients or both
+        fp8_bwd = fp8_bwd or (fp8 and rng.random() < 0.7)
+        fp8 = fp8 and (not fp8_bwd or rng.random() < 0.8)
+        scale = "square" if fp8 or fp8_bwd else "row"
+        wgrad = fp8_bwd and rng.random() < 0.6
+        gfmt = "e5m2" if fp8_bwd and rng.random() < 0.4 else "e4m3"
     return Workload(f"rand{i}", T=T, d=d, E=E, k=k, f=f, dtype=dtype, act=act, score=score,
                     n_shared=n_shared, cf=cf, sel_bias=sel_bias, aux_coef=aux_coef, z_coef=z_coef,
-                    fp8=fp8, fp8_bwd=fp8_bwd, fp8_scale=scale, fp8_wgrad=wgrad, seed=i)
+                    fp8=fp8, fp8_bwd=fp8_bwd, fp8_scale=scale, fp8_wgrad=wgrad, fp8_grad=gfmt,
+                    seed=i)
 
 
 # 0-23: the sweep; 24-35: the sweep with the block-scaled forward and FP8
-# weight gradients in the draw; 45: an FP8 forward case with f = 16 where E4M3
-# boundary steps of H moved O by 4.3% (the case behind the FP8 forward's
-# end-to-end bound)
-@pytest.mark.parametrize("i", list(range(36)) + [45])
+# weight gradients in the draw; 36-43: with square-block weights and E5M2
+# gradients; 45: an FP8 forward case with f = 16 where E4M3 boundary steps of
+# H moved O by 4.3% (the case behind the FP8 forward's end-to-end bound)
+@pytest.mark.parametrize("i", list(range(44)) + [45])
 def test_random_layer_parity(i):
     w = _draw(i)
     print(f"[case] random {i} {w}", flush=True)

@@ -59,6 +59,8 @@ MODES = [  # (fp8_fwd, fp8_bwd, fp8_scale, fp8_wgrad)
     (False, False, "row", False), (True, False, "row", False), (True, True, "row", False),
     (False, True, "row", False), (True, False, "block", False), (True, True, "block", False),
     (True, True, "row", True), (True, True, "block", True), (False, True, "row", True),
+    (True, False, "square", False), (True, True, "square", False), (False, True, "square", False),
+    (True, True, "square", True), (False, True, "square", True),
 ]
 # the gradient format (E4M3, or E5M2 for dO and dpre) only reaches the desc
 GRAD = ["e4m3", "e5m2"]
@@ -77,16 +79,27 @@ def test_layer_step_call_sequence(recorder, mode, n_shared, act, grad):
     c = recorder.calls
     assert c[:3] == ["moe_route", "moe_aux_stats", "moe_permute"]
     fwd = {(False, "row"): "moe_grouped_ffn_fwd", (False, "block"): "moe_grouped_ffn_fwd",
-           (True, "row"): "moe_grouped_ffn_fwd_fp8", (True, "block"): "moe_grouped_ffn_fwd_fp8b"}
+           (False, "square"): "moe_grouped_ffn_fwd",
+           (True, "row"): "moe_grouped_ffn_fwd_fp8", (True, "block"): "moe_grouped_ffn_fwd_fp8b",
+           (True, "square"): "moe_grouped_ffn_fwd_fp8b"}
     assert fwd[(fp8_fwd, scale)] in c
-    bwd = "moe_grouped_ffn_bwd_fp8w" if wgrad else ("moe_grouped_ffn_bwd_fp8" if fp8_bwd else
-                                                    "moe_grouped_ffn_bwd")
+    if fp8_bwd:
+        bwd = "moe_grouped_ffn_bwd_fp8" + ("b" if scale == "square" else "") + ("w" if wgrad else "")
+    else:
+        bwd = "moe_grouped_ffn_bwd"
     assert c.count(bwd) == 1
     assert c[-2:] == ["moe_route_bwd", "moe_permute_bwd"]
     # the block-scaled forward quantizes with block scales only
     if fp8_fwd and scale == "block":
         assert "moe_quantize_fp8" not in c and "moe_quantize_fp8_both" not in c
         assert c.count("moe_quantize_fp8_blocks") == 3 + 3 * n_shared
+    # square weights: one square quantization per weight and step (by the
+    # forward when it runs in FP8, else by the backward), activations in blocks
+    if scale == "square":
+        assert "moe_quantize_fp8" not in c and "moe_quantize_fp8_both" not in c
+        assert "moe_quantize_fp8_t" not in c
+        assert c.count("moe_quantize_fp8_squares") == 2 + 2 * n_shared
+        assert c.count("moe_quantize_fp8_blocks") == (1 + n_shared if fp8_fwd else 0)
 
 
 def test_fp8_wgrad_needs_the_fp8_data_gradients():
