@@ -507,8 +507,11 @@ int moe_grouped_ffn_bwd_fp8b(const moe_desc* desc, const void* x_perm, const int
 /* moe_grouped_ffn_bwd_fp8bw: moe_grouped_ffn_bwd_fp8b with the weight
  * gradients on token-axis FP8 operands as in moe_grouped_ffn_bwd_fp8w.
  * Arguments as in moe_grouped_ffn_bwd_fp8b.
+ * dO and dpre are each read once for their row blocks and their token-axis
+ * blocks.
  *   ws  MOE_OP_FFN_BWD_FP8BW bytes (moe_grouped_ffn_bwd_fp8b's layout, then
- *       the token-axis buffers of moe_grouped_ffn_bwd_fp8w)            scratch
+ *       the token-axis buffers of moe_grouped_ffn_bwd_fp8w, then dO's
+ *       token-axis codes and scales, d * (T*k + 128 E) bytes and more)  scratch
  */
 int moe_grouped_ffn_bwd_fp8bw(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                               const void* x, const void* w13q_t, const uint8_t* b13_t,

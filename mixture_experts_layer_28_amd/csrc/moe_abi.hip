@@ -23,7 +23,7 @@ hipError_t launch_quant_fp8_squares(const void* src, int64_t G, int64_t R, int64
                                     uint8_t* scales, void* codes_t, uint8_t* scales_t, hipStream_t st);
 hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
                                     int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st,
-                                    int fmt = 0);
+                                    int fmt = 0, void* rcodes = nullptr, uint8_t* rscales = nullptr);
 hipError_t launch_set_bounds(int32_t* bounds, int32_t lo, int32_t hi, hipStream_t st);
 hipError_t gemm_f32(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t gemm_fp8(const GemmArgs& p, int epi, int rag, hipStream_t s, int a_fmt = 0);
@@ -339,10 +339,15 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
              align256(blk ? blk_scale_bytes(R, P) : (size_t)R * 4);
     }
     case MOE_OP_FFN_BWD_FP8W:
-    case MOE_OP_FFN_BWD_FP8BW:
       // the FP8 backward's buffers, then the weight gradients' token-axis ones
-      return ws_bytes_for(d, op == MOE_OP_FFN_BWD_FP8W ? MOE_OP_FFN_BWD_FP8 : MOE_OP_FFN_BWD_FP8B) +
-             wgrad_fp8_ws_bytes(d);
+      return ws_bytes_for(d, MOE_OP_FFN_BWD_FP8) + wgrad_fp8_ws_bytes(d);
+    case MOE_OP_FFN_BWD_FP8BW: {
+      // the same on the block-scaled backward, plus dO's token-axis codes and
+      // scales: they are written with its row blocks before dH and kept for dW2
+      const int64_t Rp = wgrad_rp(d);
+      return ws_bytes_for(d, MOE_OP_FFN_BWD_FP8B) + wgrad_fp8_ws_bytes(d) + align256((size_t)d->d * Rp) +
+             align256(blk_scale_bytes(d->d, Rp));
+    }
     case MOE_OP_FFN_FWD_FP8B: {
       // FP8 codes and block scales of H between the two GEMMs, then the
       // down-projection's split-K tail
@@ -1218,6 +1223,12 @@ int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_pe
   uint8_t* qb_s = qb + align256((size_t)std::max(f, d) * Rp);
   int32_t* ktab = (int32_t*)(qb_s + align256(blk_scale_bytes(std::max(f, d), Rp)));
   int32_t* bounds = (int32_t*)((char*)ktab + align256((size_t)(Rp / 128) * 4));
+  // block scales with FP8 weight gradients: dO and dpre are each read once
+  // for both their row blocks (the data gradients) and their token-axis
+  // blocks (the weight gradients); dO's token-axis codes wait in qd for dW2
+  const bool fuse = blk && fp8w;
+  uint8_t* qd = fuse ? (uint8_t*)w9 + wgrad_fp8_ws_bytes(desc) : nullptr;
+  uint8_t* qd_s = fuse ? qd + align256((size_t)d * Rp) : nullptr;
   const int epi_b = desc->act == MOE_SWIGLU ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
   for (int shared = 0; shared <= (int)desc->n_shared; ++shared) {
     const int ragm = shared ? RAG_NONE : RAG_M;
@@ -1229,12 +1240,22 @@ int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_pe
     const void* go = shared ? dy : dout;            // upstream gradient rows
     const void* xin = shared ? x : x_perm;
     const void* hs = shared ? save_h_s : save_h;
+    // group bounds of the token-axis quantizers (the shared expert: one group)
+    const int32_t* off = offsets;
+    if (fp8w && shared) {
+      MOE_TRY(hip_check(launch_set_bounds(bounds, 0, (int32_t)T, s), "shared bounds"));
+      off = bounds;
+    }
     // upstream gradient -> FP8 rows (routed rows beyond offsets[E] skipped)
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(go, rows, d, d, valid, gq, d, (uint8_t*)gs, s, gf)
-                            : launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s, gf),
-                        "fp8 quantize dO"));
+      if (fuse)
+        MOE_TRY(hip_check(launch_quant_fp8_tblocks(go, rows, d, off, G, ktab, qd, qd_s, s, gf, gq, (uint8_t*)gs),
+                          "fp8 quantize dO (rows and token axis)"));
+      else
+        MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(go, rows, d, d, valid, gq, d, (uint8_t*)gs, s, gf)
+                              : launch_quant_fp8(go, rows, d, d, valid, gq, d, gs, s, gf),
+                          "fp8 quantize dO"));
     }
     // dgrad 1: dH = dO W2 against W2^T in FP8, activation backward in the epilogue
     GemmArgs p = blank();
@@ -1264,9 +1285,13 @@ int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_pe
     // the bf16 pre-activation gradient -> FP8 rows
     {
       Scope sc(K_QUANT_FP8, s);
-      MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(dpre, rows, P, P, valid, pq, P, (uint8_t*)ps, s, gf)
-                            : launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s, gf),
-                        "fp8 quantize dpre"));
+      if (fuse)
+        MOE_TRY(hip_check(launch_quant_fp8_tblocks(dpre, rows, P, off, G, ktab, qa, qa_s, s, gf, pq, (uint8_t*)ps),
+                          "fp8 quantize dpre (rows and token axis)"));
+      else
+        MOE_TRY(hip_check(blk ? launch_quant_fp8_blocks(dpre, rows, P, P, valid, pq, P, (uint8_t*)ps, s, gf)
+                              : launch_quant_fp8(dpre, rows, P, P, valid, pq, P, ps, s, gf),
+                          "fp8 quantize dpre"));
     }
     // dgrad 2: dX = dpre W13 against W13^T in FP8
     GemmArgs q = blank();
@@ -1293,12 +1318,7 @@ int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_pe
     if (fp8w) {
       // weight gradients on token-axis FP8 operands (block scales per 32 of
       // each expert's tokens): dW2 = dO^T H, then dW13 = dpre^T X
-      const int32_t* off = offsets;
-      if (shared) {
-        MOE_TRY(hip_check(launch_set_bounds(bounds, 0, (int32_t)T, s), "shared bounds"));
-        off = bounds;
-      }
-      const int64_t R = shared ? T : T * desc->k;
+      const int64_t R = rows;
       const int64_t rp = 128 * ((R + 127) / 128 + G);
       auto quant_t = [&](const void* src, int64_t C, uint8_t* codes, uint8_t* sc, int fmt) {
         Scope q(K_QUANT_FP8, s);
@@ -1308,12 +1328,14 @@ int ffn_bwd_fp8_impl(bool blk, bool fp8w, const moe_desc* desc, const void* x_pe
       for (int which = 0; which < 2; ++which) {
         const bool down = which == 0;
         const int64_t M = down ? d : P, N = down ? f : d;
-        MOE_TRY(quant_t(down ? go : dpre, M, qa, qa_s, gf));   // the gradient operand
+        // the gradient operand (already quantized with its row blocks when fused)
+        if (!fuse) MOE_TRY(quant_t(down ? go : dpre, M, qa, qa_s, gf));
         MOE_TRY(quant_t(down ? hs : xin, N, qb, qb_s, 0));
+        const bool kept = fuse && down;   // dO's token-axis codes in qd
         GemmArgs r = blank();
-        r.a = opnd(qa, rp, 0, 0);
+        r.a = opnd(kept ? qd : qa, rp, 0, 0);
         r.b = opnd(qb, rp, 0, 0);
-        r.a_sexp = (const int32_t*)qa_s;
+        r.a_sexp = (const int32_t*)(kept ? qd_s : qa_s);
         r.b_sexp = (const int32_t*)qb_s;
         r.b_sexp_gstride = 0;
         r.blk_scales = 1;

@@ -212,10 +212,18 @@ constexpr int kTBC = 64;   // columns per workgroup of the token-axis quantizer
 // The 128 x 64 tile is staged in LDS row by row (16-byte chunks); thread
 // (b = tid / 64, c = tid % 64) then takes token block b of column c: its
 // maximum, its exponent byte and its 32 codes (two 16-byte stores).
-template <int FMT>
+// ROWS: the same read also quantizes the tile's rows in 1 x 32 blocks along
+// C, exactly as quant_blocks_fp8_kernel does (row codes [R, C] and their
+// interleaved scale bytes, the rows of the group only): a thread's four
+// chunks share one column chunk, and the four lanes of a 32-column block
+// agree on its maximum by two lane swaps. The workgroup at the start of a
+// 128-column word also writes 127 into the word's bytes past C that no
+// workgroup covers.
+template <int FMT, bool ROWS>
 __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t C, const int32_t* __restrict__ off, const int32_t* __restrict__ tab,
-    uint8_t* __restrict__ codes, int64_t Rp, uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ codes, int64_t Rp, uint8_t* __restrict__ scales, uint8_t* __restrict__ rcodes,
+    uint8_t* __restrict__ rscales) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTBC];
   const int64_t q = blockIdx.y, c0 = (int64_t)blockIdx.x * kTBC;
   const int g = tab[q];
@@ -232,6 +240,26 @@ __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
     const uint4 v = r < nv && c < C ? *reinterpret_cast<const uint4*>(src + (t0 + r) * C + c)
                                     : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(tile + r * kTBC + 8 * cc) = v;
+    if constexpr (ROWS) {
+      uint32_t m = absmax8(v, 0);
+#pragma unroll
+      for (int o = 1; o < 4; o <<= 1) {
+        const uint32_t t = __shfl_xor(m, o, 64);
+        m = t > m ? t : m;
+      }
+      int e = fp8_scale_exp<FMT>(m, bf2f(m));
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      if (r < nv) {
+        const int64_t row = t0 + r;
+        if (c < C) *reinterpret_cast<uint2*>(rcodes + row * C + c) = to_fp8<FMT>(v, e);
+        if ((cc & 3) == 0) {
+          const int64_t b = (c0 >> 5) + (cc >> 2), KW = (C + 127) / 128;
+          uint8_t* wd = rscales + (((row >> 5) * KW + (b >> 2)) * 32 + (row & 31)) * 4;
+          wd[b & 3] = (uint8_t)(e + 127);
+          if ((c0 & 127) == 0 && c0 + kTBC >= C) wd[(b & 3) + 2] = 127;   // no workgroup at c0 + 64
+        }
+      }
+    }
   }
   __syncthreads();
   const int cl = tid & 63, b = tid >> 6;
@@ -647,18 +675,32 @@ hipError_t launch_quant_fp8(const void* src, int64_t rows, int64_t K, int64_t ld
 // Token-axis block quantization of a grouped token-major [R, C] matrix into
 // its transpose (see quant_tblocks_fp8_kernel). off: G + 1 group bounds on the
 // device; tab: nq = Rp / 128 ints of scratch; Rp = 128 * (ceil(R / 128) + G).
+// rcodes / rscales (both or neither): also the rows' 1 x 32 block
+// quantization of src (codes [R, C], row stride C, and 32-row interleaved
+// scale bytes), the rows of the groups only. C % 8 == 0.
 hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const int32_t* off, int G,
-                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st, int fmt) {
+                                    int32_t* tab, void* codes_t, uint8_t* scales, hipStream_t st, int fmt,
+                                    void* rcodes, uint8_t* rscales) {
   const int64_t Rp = 128 * ((R + 127) / 128 + G), nq = Rp / 128;
   if (R == 0 || C == 0) return hipSuccess;
   hipLaunchKernelGGL(kstep_group_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, off, G, nq, tab);
   const dim3 grid((unsigned)((C + kTBC - 1) / kTBC), (unsigned)nq);
-  if (fmt == 1)
-    hipLaunchKernelGGL(quant_tblocks_fp8_kernel<1>, grid, dim3(256), 0, st, (const bf16_t*)src, C, off,
-                       (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
+  const bf16_t* x = (const bf16_t*)src;
+  uint8_t* ct = (uint8_t*)codes_t;
+  uint8_t* rc = (uint8_t*)rcodes;
+  const bool rows = rcodes != nullptr;
+  if (fmt == 1 && rows)
+    hipLaunchKernelGGL((quant_tblocks_fp8_kernel<1, true>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
+                       rc, rscales);
+  else if (fmt == 1)
+    hipLaunchKernelGGL((quant_tblocks_fp8_kernel<1, false>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
+                       rc, rscales);
+  else if (rows)
+    hipLaunchKernelGGL((quant_tblocks_fp8_kernel<0, true>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
+                       rc, rscales);
   else
-    hipLaunchKernelGGL(quant_tblocks_fp8_kernel<0>, grid, dim3(256), 0, st, (const bf16_t*)src, C, off,
-                       (const int32_t*)tab, (uint8_t*)codes_t, Rp, scales);
+    hipLaunchKernelGGL((quant_tblocks_fp8_kernel<0, false>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
+                       rc, rscales);
   return hipGetLastError();
 }
 

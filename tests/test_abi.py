@@ -443,7 +443,8 @@ def test_fp8_block_backward_validation(name, op):
     """The block-scaled FP8 backward validates like the per-row one; its
     workspace holds block-scale bytes of dO and dpre in place of one int32
     per row, and the weight-gradient form adds the token-axis buffers of
-    moe_grouped_ffn_bwd_fp8w."""
+    moe_grouped_ffn_bwd_fp8w and a second one for dO's token-axis codes
+    (kept from the data gradients to dW2)."""
     L = moe.lib()
     P = ctypes.c_void_p
     ptrs = [P(FAKE)] * 23
@@ -467,7 +468,10 @@ def test_fp8_block_backward_validation(name, op):
     if op == moe.MOE_OP_FFN_BWD_FP8B:
         assert sz[op] - sz[moe.MOE_OP_FFN_BWD_FP8] == blk - row
     else:
-        assert sz[op] - sz[moe.MOE_OP_FFN_BWD_FP8W] == blk - row
+        # plus dO's token-axis codes (d x Rp, Rp = 128 * (ceil(128 / 128) + 8)) and scales
+        Rp = 1152
+        assert sz[op] - sz[moe.MOE_OP_FFN_BWD_FP8W] == blk - row + al(256 * Rp) + \
+            al(moe.fp8_block_scale_bytes(256, Rp))
     assert call(d, ws_bytes=sz[op] - 1) == 3
     # a NULL or misaligned transposed weight or scale array is rejected
     for i in (3, 4):
