@@ -206,26 +206,26 @@ __global__ void set_bounds_kernel(int32_t* __restrict__ bounds, int32_t lo, int3
   }
 }
 
-constexpr int kTBC = 64;   // columns per workgroup of the token-axis quantizer
-
-// Workgroup (x, q): columns 64x .. 64x+63 of padded k-step q (tab[q]'s group).
-// The 128 x 64 tile is staged in LDS row by row (16-byte chunks); thread
-// (b = tid / 64, c = tid % 64) then takes token block b of column c: its
-// maximum, its exponent byte and its 32 codes (two 16-byte stores).
+// Workgroup (x, q): columns CW x .. CW x + CW-1 of padded k-step q (tab[q]'s
+// group), CW = 64, or 128 with ROWS. The 128 x CW tile is staged in LDS row
+// by row (16-byte chunks); thread t then takes token blocks b of column
+// c = t % CW (b = t / CW for CW = 64, 2 (t / 128) and the next for CW = 128):
+// each block's maximum, its exponent byte and its 32 codes (two 16-byte
+// stores).
 // ROWS: the same read also quantizes the tile's rows in 1 x 32 blocks along
 // C, exactly as quant_blocks_fp8_kernel does (row codes [R, C] and their
-// interleaved scale bytes, the rows of the group only): a thread's four
-// chunks share one column chunk, and the four lanes of a 32-column block
-// agree on its maximum by two lane swaps. The workgroup at the start of a
-// 128-column word also writes 127 into the word's bytes past C that no
-// workgroup covers.
+// interleaved scale words, the rows of the group only): a thread's chunks
+// share one column chunk, the four lanes of a 32-column block agree on its
+// maximum by two lane swaps, and a row's 128 columns are one whole scale
+// word (gathered by lane swaps) and one 128-byte line of codes.
 template <int FMT, bool ROWS>
 __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
     const bf16_t* __restrict__ src, int64_t C, const int32_t* __restrict__ off, const int32_t* __restrict__ tab,
     uint8_t* __restrict__ codes, int64_t Rp, uint8_t* __restrict__ scales, uint8_t* __restrict__ rcodes,
-    uint8_t* __restrict__ rscales) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTBC];
-  const int64_t q = blockIdx.y, c0 = (int64_t)blockIdx.x * kTBC;
+    uint32_t* __restrict__ rscales) {
+  constexpr int CW = ROWS ? 128 : 64, NCH = CW / 8, NU = 128 * NCH / 256, NB = CW / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * CW];
+  const int64_t q = blockIdx.y, c0 = (int64_t)blockIdx.x * CW;
   const int g = tab[q];
   if (g < 0) return;
   const int64_t kt = q - ((int64_t)(off[g] + 127) / 128 + g);
@@ -234,12 +234,12 @@ __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
   const int nv = left < 128 ? (int)left : 128;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ch = tid + 256 * u, r = ch >> 3, cc = ch & 7;
+  for (int u = 0; u < NU; ++u) {
+    const int ch = tid + 256 * u, r = ch / NCH, cc = ch % NCH;
     const int64_t c = c0 + 8 * cc;
     const uint4 v = r < nv && c < C ? *reinterpret_cast<const uint4*>(src + (t0 + r) * C + c)
                                     : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(tile + r * kTBC + 8 * cc) = v;
+    *reinterpret_cast<uint4*>(tile + r * CW + 8 * cc) = v;
     if constexpr (ROWS) {
       uint32_t m = absmax8(v, 0);
 #pragma unroll
@@ -249,42 +249,48 @@ __global__ __launch_bounds__(256) void quant_tblocks_fp8_kernel(
       }
       int e = fp8_scale_exp<FMT>(m, bf2f(m));
       e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      // the row's word: blocks 0..3 from the lanes of chunks 0, 4, 8, 12
+      const uint32_t by = (uint32_t)(e + 127);
+      const uint32_t b1 = (uint32_t)__shfl_xor((int)by, 4, 64), b2 = (uint32_t)__shfl_xor((int)by, 8, 64),
+                     b3 = (uint32_t)__shfl_xor((int)by, 12, 64);
       if (r < nv) {
         const int64_t row = t0 + r;
         if (c < C) *reinterpret_cast<uint2*>(rcodes + row * C + c) = to_fp8<FMT>(v, e);
-        if ((cc & 3) == 0) {
-          const int64_t b = (c0 >> 5) + (cc >> 2), KW = (C + 127) / 128;
-          uint8_t* wd = rscales + (((row >> 5) * KW + (b >> 2)) * 32 + (row & 31)) * 4;
-          wd[b & 3] = (uint8_t)(e + 127);
-          if ((c0 & 127) == 0 && c0 + kTBC >= C) wd[(b & 3) + 2] = 127;   // no workgroup at c0 + 64
+        if (cc == 0) {
+          const int64_t KW = (C + 127) / 128;
+          rscales[((row >> 5) * KW + (c0 >> 7)) * 32 + (row & 31)] = by | (b1 << 8) | (b2 << 16) | (b3 << 24);
         }
       }
     }
   }
   __syncthreads();
-  const int cl = tid & 63, b = tid >> 6;
+  const int cl = tid % CW;
   const int64_t c = c0 + cl;
   if (c >= C) return;
-  uint32_t m = 0;
-  uint32_t w[16];   // the block's 32 bf16, two to a word, token order
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t lo = tile[(32 * b + 2 * i) * kTBC + cl], hi = tile[(32 * b + 2 * i + 1) * kTBC + cl];
-    w[i] = lo | (hi << 16);
-    m = (lo & 0x7fffu) > m ? (lo & 0x7fffu) : m;
-    m = (hi & 0x7fffu) > m ? (hi & 0x7fffu) : m;
-  }
-  int e = fp8_scale_exp<FMT>(m, bf2f(m));
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
   const int64_t kw = (int64_t)(off[g] + 127) / 128 + g + kt;   // k-step word of row c
-  uint2 o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = to_fp8<FMT>(make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]), e);
-  uint4* dst = reinterpret_cast<uint4*>(codes + c * Rp + 128 * kw + 32 * b);
-  dst[0] = make_uint4(o[0].x, o[0].y, o[1].x, o[1].y);
-  dst[1] = make_uint4(o[2].x, o[2].y, o[3].x, o[3].y);
-  scales[(((c >> 5) * (Rp / 128) + kw) * 32 + (c & 31)) * 4 + b] = (uint8_t)(e + 127);
+  for (int j = 0; j < NB; ++j) {
+    const int b = (tid / CW) * NB + j;
+    uint32_t m = 0;
+    uint32_t w[16];   // the block's 32 bf16, two to a word, token order
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t lo = tile[(32 * b + 2 * i) * CW + cl], hi = tile[(32 * b + 2 * i + 1) * CW + cl];
+      w[i] = lo | (hi << 16);
+      m = (lo & 0x7fffu) > m ? (lo & 0x7fffu) : m;
+      m = (hi & 0x7fffu) > m ? (hi & 0x7fffu) : m;
+    }
+    int e = fp8_scale_exp<FMT>(m, bf2f(m));
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    uint2 o[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      o[jj] = to_fp8<FMT>(make_uint4(w[4 * jj], w[4 * jj + 1], w[4 * jj + 2], w[4 * jj + 3]), e);
+    uint4* dst = reinterpret_cast<uint4*>(codes + c * Rp + 128 * kw + 32 * b);
+    dst[0] = make_uint4(o[0].x, o[0].y, o[1].x, o[1].y);
+    dst[1] = make_uint4(o[2].x, o[2].y, o[3].x, o[3].y);
+    scales[(((c >> 5) * (Rp / 128) + kw) * 32 + (c & 31)) * 4 + b] = (uint8_t)(e + 127);
+  }
 }
 
 // ---- per-column quantization into the transpose
@@ -684,23 +690,25 @@ hipError_t launch_quant_fp8_tblocks(const void* src, int64_t R, int64_t C, const
   const int64_t Rp = 128 * ((R + 127) / 128 + G), nq = Rp / 128;
   if (R == 0 || C == 0) return hipSuccess;
   hipLaunchKernelGGL(kstep_group_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, off, G, nq, tab);
-  const dim3 grid((unsigned)((C + kTBC - 1) / kTBC), (unsigned)nq);
+  const bool rows = rcodes != nullptr;
+  const int64_t cw = rows ? 128 : 64;   // the kernel's tile width
+  const dim3 grid((unsigned)((C + cw - 1) / cw), (unsigned)nq);
   const bf16_t* x = (const bf16_t*)src;
   uint8_t* ct = (uint8_t*)codes_t;
   uint8_t* rc = (uint8_t*)rcodes;
-  const bool rows = rcodes != nullptr;
+  uint32_t* rs = (uint32_t*)rscales;
   if (fmt == 1 && rows)
     hipLaunchKernelGGL((quant_tblocks_fp8_kernel<1, true>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
-                       rc, rscales);
+                       rc, rs);
   else if (fmt == 1)
     hipLaunchKernelGGL((quant_tblocks_fp8_kernel<1, false>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
-                       rc, rscales);
+                       rc, rs);
   else if (rows)
     hipLaunchKernelGGL((quant_tblocks_fp8_kernel<0, true>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
-                       rc, rscales);
+                       rc, rs);
   else
     hipLaunchKernelGGL((quant_tblocks_fp8_kernel<0, false>), grid, dim3(256), 0, st, x, C, off, tab, ct, Rp, scales,
-                       rc, rscales);
+                       rc, rs);
   return hipGetLastError();
 }
 
