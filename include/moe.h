@@ -413,6 +413,9 @@ int moe_quantize_fp8_both(const void* src, int64_t G, int64_t R, int64_t C, void
  *   src       [G, R, C] bf16                                          in
  *   codes     [G, R, C] uint8, scales MOE_FP8_BLOCK_SCALE_BYTES(G*R, C) out
  *   codes_t   [G, C, R] uint8, scales_t MOE_FP8_BLOCK_SCALE_BYTES(G*C, R) out
+ * Either layout may be skipped: codes and scales both NULL (only the
+ * transposes, for FP8 data gradients after a bf16 forward), or codes_t and
+ * scales_t both NULL (only the rows, for an FP8 forward alone); not both.
  * Constraints: R and C multiples of 16 in [16, 2^22]; 0 <= G <= 65535; each
  * scale array under 2^31 words; every pointer 16-byte aligned.
  */

@@ -332,15 +332,18 @@ def quantize_fp8_squares(src, codes, scales, codes_t, scales_t, stream=None):
     32 squares, one exponent each) into both layouts from one read: codes
     [..., R, C] with scales (fp8_block_scale_bytes(G*R, C) uint8) and the
     transposes' codes_t [..., C, R] with scales_t (fp8_block_scale_bytes(G*C, R)),
-    G the number of matrices."""
+    G the number of matrices. Either pair may be None (that layout is skipped)."""
     R, C = src.shape[-2], src.shape[-1]
     G = src.numel() // (R * C) if R * C else 0
     lead = src.shape[:-2]
-    if codes.shape != src.shape or codes_t.shape != lead + (C, R) or \
-            scales.numel() != fp8_block_scale_bytes(G * R, C) or \
-            scales_t.numel() != fp8_block_scale_bytes(G * C, R):
-        raise ValueError("codes [..., R, C], codes_t [..., C, R], scales and scales_t of "
-                         "fp8_block_scale_bytes(G*R, C) and (G*C, R) bytes")
+    if (codes is None) != (scales is None) or (codes_t is None) != (scales_t is None):
+        raise ValueError("codes and scales (and codes_t and scales_t) are given together")
+    if codes is not None and (codes.shape != src.shape or
+                              scales.numel() != fp8_block_scale_bytes(G * R, C)):
+        raise ValueError("codes [..., R, C] and scales of fp8_block_scale_bytes(G*R, C) bytes")
+    if codes_t is not None and (codes_t.shape != lead + (C, R) or
+                                scales_t.numel() != fp8_block_scale_bytes(G * C, R)):
+        raise ValueError("codes_t [..., C, R] and scales_t of fp8_block_scale_bytes(G*C, R) bytes")
     _check("moe_quantize_fp8_squares", lib().moe_quantize_fp8_squares(
         _p(src), G, R, C, _p(codes), _p(scales), _p(codes_t), _p(scales_t), _stream(stream)))
 

@@ -1086,10 +1086,13 @@ int moe_quantize_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, v
     return fail(MOE_ERR_INVALID_ARG, "C must be a positive multiple of 16, at most 2^22 (got %lld)",
                 (long long)C);
   MOE_TRY(need(src, "src"));
-  MOE_TRY(need(codes, "codes"));
-  MOE_TRY(need(scales, "scales"));
-  MOE_TRY(need(codes_t, "codes_t"));
-  MOE_TRY(need(scales_t, "scales_t"));
+  if (!codes != !scales || !codes_t != !scales_t)
+    return fail(MOE_ERR_INVALID_ARG, "codes and scales (and codes_t and scales_t) are given together");
+  if (!codes && !codes_t) return fail(MOE_ERR_INVALID_ARG, "codes and codes_t are both NULL");
+  MOE_TRY(opt(codes, "codes"));
+  MOE_TRY(opt(scales, "scales"));
+  MOE_TRY(opt(codes_t, "codes_t"));
+  MOE_TRY(opt(scales_t, "scales_t"));
   if (!blk_scale_words_fit(G * R, C) || !blk_scale_words_fit(G * C, R))
     return fail(MOE_ERR_INVALID_ARG, "block scales of %lld matrices of %lld x %lld exceed 2^31 words",
                 (long long)G, (long long)R, (long long)C);

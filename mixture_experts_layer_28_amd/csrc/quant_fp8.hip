@@ -524,7 +524,8 @@ __global__ __launch_bounds__(256) void colmax_reduce_fp8_kernel(const uint16_t* 
 //   codes [G*R, C]   and its block-scale words (rows G*R, K = C), and
 //   codes_t [G, C, R] and its block-scale words (rows G*C, K = R),
 // in moe_quantize_fp8_blocks' 32-row interleaved layout (byte e + 127; blocks
-// past the edge hold 127), with the same code in both layouts.
+// past the edge hold 127), with the same code in both layouts. A layout whose
+// codes pointer is null is skipped.
 // Workgroup (x, y, g): the 128 x 128 tile at rows 128y, columns 128x of
 // matrix g; wave w takes the tile's rows 32w .. 32w+31 (one row of squares).
 // Load i of lane l reads 16 bytes (8 columns) of row 32w + 4i + (l >> 4),
@@ -573,19 +574,20 @@ __global__ __launch_bounds__(256) void quant_squares_fp8_kernel(
     const int rloc = 32 * wave + 4 * i + rl;
     const int64_t row = r0 + rloc;
     const uint2 q = to_fp8<0>(v[i], e);
-    if (row < R && col < C) *reinterpret_cast<uint2*>(codes + (g * R + row) * C + col) = q;
+    if (codes && row < R && col < C) *reinterpret_cast<uint2*>(codes + (g * R + row) * C + col) = q;
     *reinterpret_cast<uint32_t*>(q_s + rloc * kSqLd + 8 * ch) = q.x;
     *reinterpret_cast<uint32_t*>(q_s + rloc * kSqLd + 8 * ch + 4) = q.y;
   }
   __syncthreads();
   // the rows' scale words: tile row t takes the four column blocks' bytes of
   // its row block
-  if (tid < kSqT && r0 + tid < R) {
+  if (codes && tid < kSqT && r0 + tid < R) {
     const int rb = tid >> 5;
     const int64_t rowg = g * R + r0 + tid, KW = (C + kSqT - 1) / kSqT;
     scales[((rowg >> 5) * KW + c0 / kSqT) * 32 + (rowg & 31)] =
         e_s[rb][0] | (e_s[rb][1] << 8) | (e_s[rb][2] << 16) | (e_s[rb][3] << 24);
   }
+  if (!codes_t) return;
   // phase 2: output rows (tile columns) 4cq .. 4cq+3, k (tile rows) 16rq .. 16rq+15
   const int cq = 8 * wave + (lane & 7), rq = lane >> 3;
   uint32_t o[4][4];   // o[c][i]: output row 4cq + c, k 16rq + 4i .. +3
@@ -736,9 +738,10 @@ hipError_t launch_quant_fp8_blocks(const void* src, int64_t rows, int64_t K, int
   return hipGetLastError();
 }
 
-// Square-block weights, both layouts (quant_squares_fp8_kernel). R % 16 == 0,
-// C % 16 == 0; scales: ceil(G*R / 32) * 32 * ceil(C / 128) words, scales_t:
-// ceil(G*C / 32) * 32 * ceil(R / 128) words.
+// Square-block weights, both layouts (quant_squares_fp8_kernel; codes or
+// codes_t null: that layout is skipped). R % 16 == 0, C % 16 == 0; scales:
+// ceil(G*R / 32) * 32 * ceil(C / 128) words, scales_t: ceil(G*C / 32) * 32 *
+// ceil(R / 128) words.
 hipError_t launch_quant_fp8_squares(const void* src, int64_t G, int64_t R, int64_t C, void* codes,
                                     uint8_t* scales, void* codes_t, uint8_t* scales_t, hipStream_t st) {
   if (G == 0 || R == 0 || C == 0) return hipSuccess;

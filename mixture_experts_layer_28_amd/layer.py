@@ -137,10 +137,10 @@ class MoELayer:
 
         def sc_row(rows, K):
             return z(*rows, dtype=i32)
-        # the square quantizer writes both layouts: rows for the forward,
-        # transposes for the data gradients
-        if fp8_fwd or self.fp8_square:
-            sc = sc_blk if self.fp8_block or self.fp8_square else sc_row
+        # row layouts for the FP8 forward, transposes for the FP8 data gradients
+        # (the square quantizer writes whichever of the two the layer runs)
+        if fp8_fwd:
+            sc = sc_blk if self.fp8_block else sc_row
             self.xq_perm, self.sx_perm = z(R, d, dtype=u8), sc((R,), d)
             self.w13q, self.s13 = z(E, P, d, dtype=u8), sc((E, P), d)
             self.w2q, self.s2 = z(E, d, f, dtype=u8), sc((E, d), f)
@@ -148,7 +148,7 @@ class MoELayer:
             self.xq, self.sx = (z(T, d, dtype=u8), sc((T,), d)) if sh else (None, None)
             self.sw13q, self.ss13 = (z(1, P, d, dtype=u8), sc((1, P), d)) if sh else (None, None)
             self.sw2q, self.ss2 = (z(1, d, f, dtype=u8), sc((1, d), f)) if sh else (None, None)
-        if fp8_bwd or self.fp8_square:
+        if fp8_bwd:
             sh = bool(n_shared)
             sct = sc_blk if self.fp8_square else sc_row
             self.w13q_t, self.s13_t = z(E, d, P, dtype=u8), sct((E, d), P)
@@ -227,11 +227,15 @@ class MoELayer:
         return self.Y
 
     def _quantize_squares(self, w13, w2, sw13, sw2):
-        quantize_fp8_squares(w13, self.w13q, self.s13, self.w13q_t, self.s13_t)
-        quantize_fp8_squares(w2, self.w2q, self.s2, self.w2q_t, self.s2_t)
+        """Square-block codes of the weights in the layouts this layer runs:
+        rows for the FP8 forward, transposes for the FP8 data gradients."""
+        def pair(codes, scales, on):
+            return (getattr(self, codes), getattr(self, scales)) if on else (None, None)
+        names = [(w13, "w13q", "s13"), (w2, "w2q", "s2")]
         if self.n_shared:
-            quantize_fp8_squares(sw13, self.sw13q, self.ss13, self.sw13q_t, self.ss13_t)
-            quantize_fp8_squares(sw2, self.sw2q, self.ss2, self.sw2q_t, self.ss2_t)
+            names += [(sw13, "sw13q", "ss13"), (sw2, "sw2q", "ss2")]
+        for w, c, sc in names:
+            quantize_fp8_squares(w, *pair(c, sc, self.fp8_fwd), *pair(c + "_t", sc + "_t", self.fp8_bwd))
         self._wt_from = (w13.data_ptr(), w2.data_ptr())
 
     def backward(self, dy, x, w_r, w13, w2, sw13=None, sw2=None):

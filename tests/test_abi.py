@@ -431,10 +431,13 @@ def test_fp8_square_quantize_validation():
                 dict(R=1 << 23), dict(G=-1), dict(G=70000), dict(src=0), dict(codes=FAKE + 8),
                 dict(sc=0), dict(sc=FAKE + 4), dict(codes_t=0), dict(sc_t=FAKE + 2),
                 # 2^15 matrices of 2^17 rows x 1 word: the row-layout scales reach 2^31 words
-                dict(G=1 << 15, R=1 << 17, C=16)):
+                dict(G=1 << 15, R=1 << 17, C=16),
+                # a layout's codes and scales come together, and one layout at least
+                dict(codes=0), dict(sc_t=0), dict(codes=0, sc=0, codes_t=0, sc_t=0)):
         assert call(**bad) == 1, bad
         assert L.moe_last_error().decode()
     assert call(G=0) == 0
+    assert call(G=0, codes=0, sc=0) == 0 and call(G=0, codes_t=0, sc_t=0) == 0
 
 
 @pytest.mark.parametrize("name,op", [("moe_grouped_ffn_bwd_fp8b", moe.MOE_OP_FFN_BWD_FP8B),

@@ -253,3 +253,30 @@ def test_quantize_squares_bit_exact(G, R, C):
         e0 = O.quantize_squares_fp8(f[0])[1]
         el = O.quantize_squares_fp8(f[-1])[1]
         assert e0[1, 0] == 0 and el[0, 1] == -127      # the zero and the clipped square
+
+
+@pytest.mark.parametrize("G,R,C", [(3, 48, 80), (2, 272, 400)])
+def test_quantize_squares_one_layout(G, R, C):
+    """With one layout's pointers NULL the square quantizer writes the other
+    one alone, identical to the both-layouts call."""
+    import mixture_experts_layer_28_amd as moe
+    print(f"[case] quantize squares, one layout G={G} R={R} C={C}", flush=True)
+    x = _dev_bf16(_square_mats(G, R, C, seed=G + R * 3 + C))
+    SB, SBt = moe.fp8_block_scale_bytes(G * R, C), moe.fp8_block_scale_bytes(G * C, R)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    both = [torch.empty(G, R, C, **u8), torch.empty(SB, **u8), torch.empty(G, C, R, **u8), torch.empty(SBt, **u8)]
+    moe.quantize_fp8_squares(x, *both)
+    rows = [torch.empty(G, R, C, **u8), torch.empty(SB, **u8)]
+    cols = [torch.empty(G, C, R, **u8), torch.empty(SBt, **u8)]
+    moe.quantize_fp8_squares(x, *rows, None, None)
+    moe.quantize_fp8_squares(x, None, None, *cols)
+    torch.cuda.synchronize()
+    assert torch.equal(rows[0], both[0]) and torch.equal(cols[0], both[2])
+    # scale words of padding rows past G*R (or G*C) in the last group of 32 are not written
+    nr, nc = G * R, G * C
+    KW, KWt = -(-C // 128), -(-R // 128)
+    wr, wb = rows[1].cpu().numpy().view("<u4"), both[1].cpu().numpy().view("<u4")
+    wc, wbt = cols[1].cpu().numpy().view("<u4"), both[3].cpu().numpy().view("<u4")
+    idx = lambda n, kw: np.array([(r // 32 * kw + w) * 32 + r % 32 for r in range(n) for w in range(kw)])  # noqa: E731
+    assert (wr[idx(nr, KW)] == wb[idx(nr, KW)]).all()
+    assert (wc[idx(nc, KWt)] == wbt[idx(nc, KWt)]).all()

@@ -150,7 +150,8 @@ EDGE = {
                                   fp8_bwd=True, fp8_wgrad=True, fp8_grad="e5m2"),
     # square-block weights: partial squares at both edges (d 144, f 208) with
     # GELU and a shared expert; no routed rows; square data gradients after a
-    # bf16 forward (the backward quantizes the squares), E5M2; 1024 experts
+    # bf16 forward (the backward quantizes the transposes only), E5M2; the
+    # square forward alone (rows only); 1024 experts
     "ragged_fp8sq_gelu_shared": Workload("ragged8sq", T=1000, d=144, E=6, k=3, f=208, act="gelu",
                                          score="sigmoid", n_shared=1, sel_bias=True, fp8=True,
                                          fp8_bwd=True, fp8_scale="square"),
@@ -159,6 +160,8 @@ EDGE = {
                                          fp8_scale="square"),
     "fp8sq_e5m2_dgrad_only": Workload("dg8sq", T=600, d=256, E=4, k=2, f=384, aux_coef=0.02,
                                       fp8_bwd=True, fp8_scale="square", fp8_grad="e5m2"),
+    "fp8sq_fwd_only": Workload("fw8sq", T=600, d=256, E=4, k=2, f=384, n_shared=1, fp8=True,
+                               fp8_scale="square"),
     "max_experts_fp8sq_all": Workload("e1024sq", T=640, d=64, E=1024, k=4, f=64, aux_coef=0.01,
                                       fp8=True, fp8_bwd=True, fp8_wgrad=True, fp8_scale="square"),
 }
