@@ -143,11 +143,12 @@ class Scope {
     if (!P.on.load(std::memory_order_relaxed)) return;
     a_ = P.take();
     b_ = P.take();
-    if (a_ && b_) hipEventRecord(a_, s_);
+    // profiling only: a failed record leaves this launch's time unread
+    if (a_ && b_) (void)hipEventRecord(a_, s_);
   }
   ~Scope() {
     if (!a_ || !b_) return;
-    hipEventRecord(b_, s_);
+    (void)hipEventRecord(b_, s_);
     Prof& P = prof();
     std::lock_guard<std::mutex> g(P.mu);
     P.recs.push_back({id_, a_, b_});

@@ -724,9 +724,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   }
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    if (j >= k) break;
-    const float sj = wave_sum(part[j]);
-    if (lane == 0) dgate[t * k + j] = rb[j] == kOOB ? 0.f : sj;
+    if (j < k) {   // k is uniform: every lane of the wave takes the same branch
+      const float sj = wave_sum(part[j]);
+      if (lane == 0) dgate[t * k + j] = rb[j] == kOOB ? 0.f : sj;
+    }
   }
 }
 
