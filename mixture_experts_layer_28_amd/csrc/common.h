@@ -61,6 +61,57 @@ template <> struct Vec8<float> {
   }
 };
 
+// ------------------------------------------------------------ FP8 codes
+// Largest |bf16| bit pattern of eight packed bf16 and m (finite inputs:
+// the patterns order like the magnitudes).
+__device__ __forceinline__ uint32_t absmax8(uint4 v, uint32_t m) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // |bf16| bit patterns order like their magnitudes (finite inputs)
+    const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  return m;
+}
+
+// FP8 formats: 0 = OCP E4M3 (largest magnitude 1.75 * 2^8), 1 = OCP E5M2
+// (1.75 * 2^15). The scale rule of a maximum amax = mant * 2^ex (mant in
+// [0.5, 1)): the smallest e with amax <= 1.75 * 2^(B + e).
+template <int FMT>
+__device__ __forceinline__ int fp8_scale_exp(uint32_t m_bits, float amax) {
+  constexpr int B = FMT == 1 ? 15 : 8;
+  int ex = 0;
+  const float mant = frexpf(amax, &ex);
+  return m_bits == 0 ? 0 : (2.0f * mant <= 1.75f ? ex - 1 - B : ex - B);
+}
+
+// eight bf16 scaled by 2^-e -> eight FP8 codes (byte i = element i), E4M3 or
+// E5M2 (round to nearest even either way)
+template <int FMT = 0>
+__device__ __forceinline__ uint2 to_fp8(uint4 v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float a = ldexpf(bf2f(w[2 * h] & 0xffffu), -e);
+    const float b = ldexpf(bf2f(w[2 * h] >> 16), -e);
+    const float c = ldexpf(bf2f(w[2 * h + 1] & 0xffffu), -e);
+    const float d = ldexpf(bf2f(w[2 * h + 1] >> 16), -e);
+    int r;
+    if constexpr (FMT == 1) {
+      r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+      r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+    } else {
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    }
+    o[h] = (uint32_t)r;
+  }
+  return make_uint2(o[0], o[1]);
+}
+
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
 

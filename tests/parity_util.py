@@ -257,6 +257,8 @@ def compare_layer(w: Workload, L, dev, fwd, bwd, f, rep: Report):
     o_tol = {}
     if w.fp8:
         check_fp8_down_own_h(w, L, f, off, rep)
+        if w.fp8_scale in ("block", "square"):
+            check_fp8_h_codes(w, L, dev, off)
         o_tol = fp8_fwd_tol(w.f)
     assert_close("O", to_np(L.out[:A])[g_rows], fwd["O"][o_rows], dt, rep, **o_tol)
     if w.n_shared:
@@ -521,6 +523,43 @@ def check_fp8_dgrad(w, L, dev, bwd, rep, g_rows, o_rows, off):
     # the gradient codes in the workspace, bit for bit (E4M3 or E5M2): the
     # shared expert's rows overwrite the routed ones when there is one
     check_grad_codes(w, L, dev, ws, R, P, A, dp, dps if w.n_shared else None)
+
+
+def check_fp8_h_codes(w, L, dev, off):
+    """The block-scaled forward writes H's FP8 codes and block-scale bytes in
+    its up-projection's epilogue: rerun the forward into fresh buffers (it is
+    deterministic: the rerun's H and O equal the layer's bitwise) and compare
+    the codes and exponents it leaves in the workspace with the oracle's
+    block quantizer on the same bf16 H, bit for bit (routed rows, and the
+    shared expert's)."""
+    import mixture_experts_layer_28_amd as moe
+    A, R, f = int(off[-1]), w.T * w.k, w.f
+    al = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    ws = torch.empty_like(L.ws)
+    like = lambda t: torch.empty_like(t) if t is not None else None   # noqa: E731
+    o = {n: like(getattr(L, n)) for n in ("save_pre", "save_h", "save_pre_s", "save_h_s", "out", "out_shared")}
+    moe.grouped_ffn_fwd_fp8b(L.desc, L.xq_perm, L.sx_perm, L.offsets, L.xq, L.sx, L.w13q, L.s13, L.w2q, L.s2,
+                             L.sw13q, L.ss13, L.sw2q, L.ss2, o["save_pre"], o["save_h"], o["save_pre_s"],
+                             o["save_h_s"], o["out"], o["out_shared"], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o["save_h"][:A], L.save_h[:A]) and torch.equal(o["out"][:A], L.out[:A])
+    raw = ws.cpu().numpy()
+    SB = moe.fp8_block_scale_bytes(R, f)
+    parts = [(A, 0, al(R * f), to_np(L.save_h[:A]))]
+    if w.n_shared:
+        base = al(R * f) + al(SB)
+        parts.append((w.T, base, base + al(w.T * f), to_np(L.save_h_s)))
+    for rows, c0, s0, H in parts:
+        if rows == 0:
+            continue
+        codes = raw[c0: c0 + rows * f].reshape(rows, f)
+        rc, re_ = O.quantize_blocks_fp8(H)
+        bad = np.argwhere(codes != rc)
+        assert bad.size == 0, f"H codes differ: {len(bad)}, first {bad[:4].tolist()}"
+        got = block_bytes(raw[s0:], rows, f).astype(np.int64)
+        nb = re_.shape[1]
+        assert (got[:, :nb] - 127 == re_).all(), "H block exponents differ"
+        assert (got[:, nb:] == 127).all(), "H padding blocks are not 127"
 
 
 def check_fp8_down_own_h(w, L, f, off, rep):
