@@ -106,6 +106,9 @@ typedef enum {
 /* ---------------------------------------------------------------- router
  * moe_route: [Recipe] §2.2 (router math): logits l = x W_r^T (+ logit_bias),
  * computed in float32 ([Recipe] §1 and §9.2: router kept in fp32);
+ * in a bf16 layer with E > 8 and E a multiple of 8 the product runs on the
+ * bf16 matrix cores over an exact three-term bf16 split of W_r (each
+ * product x * term is exact, sums are float32), otherwise on float32 ones;
  * scores s = softmax(l) (max-subtracted) or sigmoid(l); selection key
  * s (+ sel_bias, the aux-loss-free bias of [Recipe] §5.3 that steers top-k
  * only); the k experts with the largest keys, ties to the lower index, kept
@@ -125,8 +128,9 @@ typedef enum {
  *   gate       [T, k] float                  out
  *   scores     [T, E] float                  out
  *   lse        [T] float or NULL             out (log sum_e exp(l_te), for the z-loss)
- *   ws         MOE_OP_ROUTE bytes            scratch (E > 8: the logits, and when
- *              few tiles cover T x E the split-K partials of x W_r^T)
+ *   ws         MOE_OP_ROUTE bytes            scratch (E > 8: the logits, and the
+ *              partial products of x W_r^T: split-K partials, or for the
+ *              bf16 split the three terms of W_r and their products)
  */
 int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
               const float* sel_bias, const float* gumbel_u, int32_t* topk_idx, float* gate,
@@ -559,7 +563,9 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
  * With the noisy gate (desc->gumbel_tau = tau > 0) the terms above are taken
  * with respect to the noisy logits (l + g) / tau, and dlogits (the gradient
  * with respect to l) is their sum divided by tau.
- * dw_r = dl^T x, dx_router = dl W_r (float32).
+ * dw_r = dl^T x, dx_router = dl W_r (float32; dw_r under the same rule
+ * as moe_route's logits: in a bf16 layer with E > 8 and E % 8 == 0 it runs
+ * on the bf16 matrix cores over an exact three-term bf16 split of dl).
  *   x [T, d] dt, w_r [E, d], scores [T, E], topk_idx, gate, dgate [T, k]   in
  *   y [E] float (from moe_aux_stats; may be NULL when aux_coef == 0)        in
  *   lse [T] float (from moe_route; may be NULL when z_coef == 0)            in

@@ -179,6 +179,7 @@ enum Epi : int {
   EPI_GELU_FWD = 2,    // C = H = gelu(acc), aux = a = acc
   EPI_SWIGLU_BWD = 3,  // acc = dH; reads aux = [a | b]; C = [da | db]
   EPI_GELU_BWD = 4,    // acc = dH; reads aux = a; C = da
+  EPI_STORE_F32 = 5,   // bf16 GEMM with a float32 C = acc (router partial products)
 };
 
 // How the groups (experts) of one grouped GEMM are shaped.

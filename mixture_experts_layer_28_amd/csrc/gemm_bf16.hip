@@ -503,6 +503,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (m >= t.M || !nok) return;
         if (EPI == EPI_STORE) {
           store8_nt(cb + m * p.ldc + n8, v);
+        } else if (EPI == EPI_STORE_F32) {
+          // float32 partial products, read back at once by the fold kernel:
+          // ordinary (cached) stores
+          float* cf = reinterpret_cast<float*>(p.c) +
+                      (p.c_rowidx ? t.r0 * p.ldc : (int64_t)t.g * p.c_gstride) + m * p.ldc + n8;
+          f32x4 lo4, hi4;
+          lo4[0] = v[0]; lo4[1] = v[1]; lo4[2] = v[2]; lo4[3] = v[3];
+          hi4[0] = v[4]; hi4[1] = v[5]; hi4[2] = v[6]; hi4[3] = v[7];
+          *reinterpret_cast<f32x4*>(cf) = lo4;
+          *reinterpret_cast<f32x4*>(cf + 4) = hi4;
         } else if (EPI == EPI_GELU_FWD) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = gelu_f(v[e]);
@@ -574,6 +584,8 @@ hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hi
   MOE_CASE(true, false, EPI_GELU_BWD, RAG_NONE)
   MOE_CASE(true, false, EPI_STORE, RAG_NONE)
   MOE_CASE(false, false, EPI_STORE, RAG_NONE)
+  MOE_CASE(true, true, EPI_STORE_F32, RAG_NONE)
+  MOE_CASE(false, false, EPI_STORE_F32, RAG_NONE)
 #undef MOE_CASE
   return hipErrorInvalidValue;
 }

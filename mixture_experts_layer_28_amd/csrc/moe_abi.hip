@@ -55,6 +55,10 @@ hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, con
 hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
+hipError_t launch_split_bf16x3(const float*, int64_t, int64_t, bf16_t*, int64_t, int64_t, hipStream_t);
+hipError_t launch_fold_bf16x3(const float*, int, int64_t, int64_t, int64_t, int64_t, int64_t,
+                              const float*, float*, hipStream_t);
+hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
 hipError_t launch_router_dw_small(const float*, const void*, bool, int, int, int64_t, float*,
                                   hipStream_t);
 int router_dw_small_chunks(int T);
@@ -98,7 +102,7 @@ enum KernelId {
   K_FWD_UP, K_FWD_DOWN, K_DGRAD_DOWN, K_DGRAD_UP, K_WGRAD_DOWN, K_WGRAD_UP,
   K_SH_FWD_UP, K_SH_FWD_DOWN, K_SH_DGRAD_DOWN, K_SH_DGRAD_UP, K_SH_WGRAD_DOWN, K_SH_WGRAD_UP,
   K_COMBINE, K_COMBINE_BWD, K_ROUTER_DLOGITS, K_ROUTER_DW, K_ROUTER_DW_REDUCE, K_ROUTER_DX,
-  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_QUANT_FP8, K_ROUTER_LOGITS_REDUCE, K_COUNT
+  K_UNPERMUTE, K_FILL, K_BIAS_UPDATE, K_QUANT_FP8, K_ROUTER_LOGITS_REDUCE, K_ROUTER_SPLIT, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
   "router_logits", "router_topk", "aux_stats", "permute",
@@ -107,7 +111,7 @@ const char* const kKernelNames[K_COUNT] = {
   "gemm_shared_fwd_up", "gemm_shared_fwd_down", "gemm_shared_dgrad_down", "gemm_shared_dgrad_up",
   "gemm_shared_wgrad_down", "gemm_shared_wgrad_up",
   "combine", "combine_bwd", "router_dlogits", "router_dw", "router_dw_reduce", "router_dx",
-  "unpermute", "fill_zero", "bias_update", "quant_fp8", "router_logits_reduce",
+  "unpermute", "fill_zero", "bias_update", "quant_fp8", "router_logits_reduce", "router_split",
 };
 
 struct ProfRec {
@@ -241,6 +245,28 @@ int route_bwd_splits(const moe_desc* d) {
   return (int)s;
 }
 
+// Router products of bf16 layers with E > 8 (E a multiple of 8) run on the
+// bf16 matrix cores: the float32 operand (W_r forward, the logit gradient
+// backward) is split exactly into three bf16 terms and the three products are
+// folded in float32. Each GEMM is split into S partitions along K (d forward,
+// T backward, each a whole number of 64-deep k-steps) so that its 256 x 256
+// tiles cover up to 256 CUs. 0 = not this path.
+constexpr int64_t kX3Cus = 256;
+int router_x3_fwd_splits(const moe_desc* d) {
+  if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return 0;
+  const int64_t tiles = ((d->T + 255) / 256) * ((3 * d->E + 255) / 256);
+  for (int s = 4; s > 1; --s)
+    if (s * tiles <= kX3Cus && d->d % (64 * s) == 0) return s;
+  return 1;
+}
+int router_x3_bwd_splits(const moe_desc* d) {
+  if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return 0;
+  const int64_t tiles = ((3 * d->E + 255) / 256) * ((d->d + 255) / 256);
+  for (int s = 4; s > 1; --s)
+    if (s * tiles <= kX3Cus && d->T % (64 * s) == 0) return s;
+  return 1;
+}
+
 // Split-K of the last, partial round of tiles (bf16 plain-store grouped GEMMs)
 // sizes its workspace for at most kTailCusMax CUs per XCD.
 constexpr int kTailCusMax = 32;
@@ -302,6 +328,9 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
   const int64_t T = d->T, E = d->E;
   switch (op) {
     case MOE_OP_ROUTE: {
+      if (const int X = router_x3_fwd_splits(d))
+        return align256((size_t)T * E * 4) + align256((size_t)3 * E * d->d * 2) +
+               (size_t)X * T * 3 * E * 4;
       const int S = route_fwd_splits(d);
       return align256((size_t)T * E * 4) + (S > 1 ? (size_t)S * T * E * 4 : 0);
     }
@@ -317,6 +346,8 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
              (d->dtype == MOE_BF16 ? tail_ws_bytes(kTailCusMax) : 0);
     case MOE_OP_ROUTE_BWD: {
       if (E <= 8) return align256((size_t)router_dw_small_chunks((int)T) * E * d->d * 4);
+      if (const int X = router_x3_bwd_splits(d))
+        return align256((size_t)T * 3 * E * 2) + (size_t)X * 3 * E * d->d * 4;
       const int S = route_bwd_splits(d);
       return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
     }
@@ -542,9 +573,44 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
                                          desc->gumbel_tau, s),
                      "router (fused)");
   }
+  float* logits = (float*)ws;
+  if (const int X = router_x3_fwd_splits(desc)) {
+    // logits = x [hi | mid | lo]^T per K partition on the bf16 matrix cores,
+    // then (lo + mid) + hi folded over the partitions in order, + logit_bias
+    const int64_t T = desc->T, E = desc->E, d = desc->d, Ks = d / X;
+    bf16_t* w3 = (bf16_t*)((char*)ws + align256((size_t)T * E * 4));
+    float* part = (float*)((char*)w3 + align256((size_t)3 * E * d * 2));
+    {
+      Scope sc(K_ROUTER_SPLIT, s);
+      MOE_TRY(hip_check(launch_split_bf16x3(w_r, E, d, w3, d, E * d, s), "router weight split"));
+    }
+    GemmArgs p = blank();
+    p.a = opnd(x, d, Ks, 0);
+    p.b = opnd(w3, d, Ks, 0);
+    p.c = part;
+    p.ldc = 3 * E;
+    p.c_gstride = T * 3 * E;
+    p.G = X;
+    p.M = T;
+    p.N = 3 * E;
+    p.K = Ks;
+    {
+      Scope sc(K_ROUTER_LOGITS, s);
+      MOE_TRY(hip_check(gemm_bf16(p, true, true, EPI_STORE_F32, RAG_NONE, s), "router logits"));
+    }
+    {
+      Scope sc(K_ROUTER_LOGITS_REDUCE, s);
+      MOE_TRY(hip_check(launch_fold_bf16x3(part, X, T * 3 * E, E, 3 * E, T, E, logit_bias, logits, s),
+                        "router logits fold"));
+    }
+    Scope sc(K_ROUTER_TOPK, s);
+    return hip_check(launch_router_topk(logits, (int)desc->T, (int)desc->E, (int)desc->k,
+                                        desc->score, sel_bias, topk_idx, gate, scores, lse, gumbel_u,
+                                        desc->gumbel_tau, s),
+                     "router top-k");
+  }
   // logits = x W_r^T (+ logit_bias); with split-K the partitions land after
   // the logits (partition 0 carries the bias) and are folded in order
-  float* logits = (float*)ws;
   const int S = route_fwd_splits(desc);
   float* part = (float*)((char*)ws + align256((size_t)desc->T * desc->E * 4));
   GemmArgs p = blank();
@@ -1528,6 +1594,35 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
       Scope sc(K_ROUTER_DW_REDUCE, s);
       MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
                         "router dw reduce"));
+    }
+  } else if (const int X = router_x3_bwd_splits(desc)) {
+    // dw_r = [hi | mid | lo]^T x of the split logit gradient per token
+    // partition on the bf16 matrix cores, (lo + mid) + hi folded in order
+    const int64_t d = desc->d, Ts = (int64_t)T / X;
+    bf16_t* dl3 = (bf16_t*)ws;
+    float* part = (float*)((char*)ws + align256((size_t)T * 3 * E * 2));
+    {
+      Scope sc(K_ROUTER_SPLIT, s);
+      MOE_TRY(hip_check(launch_split_bf16x3(dlogits, T, E, dl3, 3 * E, E, s), "router dlogits split"));
+    }
+    GemmArgs p = blank();
+    p.a = opnd(dl3, 3 * E, Ts * 3 * E, 0);
+    p.b = opnd(x, d, Ts * d, 0);
+    p.c = part;
+    p.ldc = d;
+    p.c_gstride = 3 * E * d;
+    p.G = X;
+    p.M = 3 * E;
+    p.N = d;
+    p.K = Ts;
+    {
+      Scope sc(K_ROUTER_DW, s);
+      MOE_TRY(hip_check(gemm_bf16(p, false, false, EPI_STORE_F32, RAG_NONE, s), "router dw"));
+    }
+    {
+      Scope sc(K_ROUTER_DW_REDUCE, s);
+      MOE_TRY(hip_check(launch_fold_bf16x3(part, X, 3 * E * d, E * d, d, E, d, nullptr, dw_r, s),
+                        "router dw fold"));
     }
   } else {
   // dw_r = dl^T x, split over tokens, partials folded in a fixed order

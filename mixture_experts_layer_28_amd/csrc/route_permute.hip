@@ -1036,4 +1036,91 @@ hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out,
   return hipGetLastError();
 }
 
+// ------------------------------------------- router products on bf16 matrix cores
+// A float32 value v splits exactly into three bf16 terms, v = hi + mid + lo:
+// hi = bf16(v) leaves a remainder of at most 16 significant bits (exact in
+// float32), mid = bf16 of that remainder leaves at most 8, which lo then holds
+// exactly (round to nearest even at every step; values near the bottom of the
+// float32 range, where lo would be subnormal, are the exception and do not
+// arise for router weights or logit gradients). With x in bf16, every product
+// x * hi, x * mid, x * lo is exact in float32, so a bf16 MFMA GEMM over the
+// three terms, accumulated in float32, is a float32 product of x and the
+// float32 operand. Split s of element (r, c) goes to dst[r * ldd + s * sst + c].
+__global__ __launch_bounds__(256) void split_bf16x3_kernel(const float* __restrict__ src, int64_t rows,
+                                                           int64_t cols, bf16_t* __restrict__ dst,
+                                                           int64_t ldd, int64_t sst) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4-column group
+  const int64_t cq = cols >> 2;
+  if (q >= rows * cq) return;
+  const int64_t r = q / cq, c = (q - r * cq) << 2;
+  const float4 v = *reinterpret_cast<const float4*>(src + r * cols + c);
+  const float in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t t[3][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = f2bf(in[e]);
+    const float r1 = in[e] - bf2f(h);
+    const uint32_t m = f2bf(r1);
+    const float r2 = r1 - bf2f(m);
+    t[0][e] = h;
+    t[1][e] = m;
+    t[2][e] = f2bf(r2);
+  }
+#pragma unroll
+  for (int sp = 0; sp < 3; ++sp) {
+    uint2 w;
+    w.x = t[sp][0] | (t[sp][1] << 16);
+    w.y = t[sp][2] | (t[sp][3] << 16);
+    *reinterpret_cast<uint2*>(dst + r * ldd + sp * sst + c) = w;
+  }
+}
+
+hipError_t launch_split_bf16x3(const float* src, int64_t rows, int64_t cols, bf16_t* dst, int64_t ldd,
+                               int64_t sst, hipStream_t st) {
+  const int64_t n = rows * (cols >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_bf16x3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                     rows, cols, dst, ldd, sst);
+  return hipGetLastError();
+}
+
+// out[r * cols + c] = bias[c] (if any) + sum over partitions g = 0..S-1 of
+// ((lo + mid) + hi), the three split products of partition g at
+// part[g * gst + s * sst + r * ld + c] (s = 0 hi, 1 mid, 2 lo); a fixed order.
+__global__ __launch_bounds__(256) void fold_bf16x3_kernel(const float* __restrict__ part, int S,
+                                                          int64_t gst, int64_t sst, int64_t ld,
+                                                          int64_t rows, int64_t cols,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cq = cols >> 2;
+  if (q >= rows * cq) return;
+  const int64_t r = q / cq, c = (q - r * cq) << 2;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < S; ++g) {
+    const float* b = part + g * gst + r * ld + c;
+    const float4 h = *reinterpret_cast<const float4*>(b);
+    const float4 m = *reinterpret_cast<const float4*>(b + sst);
+    const float4 l = *reinterpret_cast<const float4*>(b + 2 * sst);
+    acc.x += (l.x + m.x) + h.x;
+    acc.y += (l.y + m.y) + h.y;
+    acc.z += (l.z + m.z) + h.z;
+    acc.w += (l.w + m.w) + h.w;
+  }
+  if (bias) {
+    acc.x += bias[c]; acc.y += bias[c + 1]; acc.z += bias[c + 2]; acc.w += bias[c + 3];
+  }
+  *reinterpret_cast<float4*>(out + r * cols + c) = acc;
+}
+
+hipError_t launch_fold_bf16x3(const float* part, int S, int64_t gst, int64_t sst, int64_t ld,
+                              int64_t rows, int64_t cols, const float* bias, float* out,
+                              hipStream_t st) {
+  const int64_t n = rows * (cols >> 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_bf16x3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, S,
+                     gst, sst, ld, rows, cols, bias, out);
+  return hipGetLastError();
+}
+
 }  // namespace moe
