@@ -205,6 +205,13 @@ def trace_path(workload):
     return os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
 
 
+def is_grouped_gemm(name):
+    """A launch of one of the layer's grouped GEMMs (bf16 or FP8 kernel),
+    not one of the router's float32-output products on the bf16 kernel
+    (epilogue 5, gemm_bf16_kernel<5, ...>)."""
+    return ("gemm_bf16_kernel" in name and "gemm_bf16_kernel<5," not in name) or "gemm_fp8_kernel" in name
+
+
 def summarize_trace(stats_csv, trace_csv, workload, out_path=None):
     """Text summary of a rocprofv3 --kernel-trace --stats run of this
     workload's bench (TRACE_COMMAND): every kernel's calls and durations, then
@@ -216,7 +223,7 @@ def summarize_trace(stats_csv, trace_csv, workload, out_path=None):
     w = WORKLOADS[workload]
     stats = sorted(csv.DictReader(open(stats_csv)), key=lambda r: -float(r["TotalDurationNs"]))
     disp = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
-    gem = [r for r in disp if "gemm_bf16_kernel" in r["Kernel_Name"] or "gemm_fp8_kernel" in r["Kernel_Name"]
+    gem = [r for r in disp if is_grouped_gemm(r["Kernel_Name"])
            or (w.dtype == "fp32" and "gemm_f32_mfma_kernel" in r["Kernel_Name"]
                and "GemmArgs" in r["Kernel_Name"])]
     roles = gemm_roles(w)
@@ -282,8 +289,7 @@ def summarize_mfma(out_path, pairs):
         for r in csv.DictReader(open(path)):
             by.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = r
         gem = [by[k] for k in sorted(by)
-               if "GRBM_GUI_ACTIVE" in by[k] and ("gemm_bf16_kernel" in by[k]["GRBM_GUI_ACTIVE"]["Kernel_Name"]
-                                                 or "gemm_fp8_kernel" in by[k]["GRBM_GUI_ACTIVE"]["Kernel_Name"])]
+               if "GRBM_GUI_ACTIVE" in by[k] and is_grouped_gemm(by[k]["GRBM_GUI_ACTIVE"]["Kernel_Name"])]
         roles = gemm_roles(WORKLOADS[workload])
         last = gem[-len(roles):]
         lines += ["", f"## {workload}", "launch                 MfmaUtil %   clock MHz   duration us"]
@@ -314,7 +320,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, stats_csv=None):
         # the calibration pass is the last multiply kernel before the layer's own
         calib = [float(r["Counter_Value"]) for r in rows
                  if "elementwise" in r["Kernel_Name"] and "Mul" in r["Kernel_Name"]]
-        gem = [float(r["Counter_Value"]) for r in rows if "gemm_bf16_kernel" in r["Kernel_Name"]]
+        gem = [float(r["Counter_Value"]) for r in rows if is_grouped_gemm(r["Kernel_Name"])]
         per_role = {}
         for i, v in enumerate(gem):
             per_role.setdefault(roles[i % len(roles)], []).append(v)

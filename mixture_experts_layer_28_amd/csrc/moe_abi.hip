@@ -252,8 +252,11 @@ int route_bwd_splits(const moe_desc* d) {
 // T backward, each a whole number of 64-deep k-steps) so that its 256 x 256
 // tiles cover up to 256 CUs. 0 = not this path.
 constexpr int64_t kX3Cus = 256;
+// (The GEMM addresses each operand through 32-bit byte offsets: the split
+// terms must stay under 2 GiB.)
 int router_x3_fwd_splits(const moe_desc* d) {
   if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return 0;
+  if (3 * d->E * d->d * 2 >= (int64_t(1) << 31)) return 0;
   const int64_t tiles = ((d->T + 255) / 256) * ((3 * d->E + 255) / 256);
   for (int s = 4; s > 1; --s)
     if (s * tiles <= kX3Cus && d->d % (64 * s) == 0) return s;
@@ -261,6 +264,7 @@ int router_x3_fwd_splits(const moe_desc* d) {
 }
 int router_x3_bwd_splits(const moe_desc* d) {
   if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return 0;
+  if (d->T * 3 * d->E * 2 >= (int64_t(1) << 31)) return 0;
   const int64_t tiles = ((3 * d->E + 255) / 256) * ((d->d + 255) / 256);
   for (int s = 4; s > 1; --s)
     if (s * tiles <= kX3Cus && d->T % (64 * s) == 0) return s;
