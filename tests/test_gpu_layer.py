@@ -86,6 +86,12 @@ EDGE = {
                                    logit_bias={3: 1.5, 17: -2.0}, aux_coef=0.02, z_coef=0.01),
     "router_splitk_ktail_fp32": Workload("rsplit32", T=515, d=1032, E=20, k=2, f=48,
                                          dtype="fp32", logit_bias={0: 1.0}, aux_coef=0.05),
+    # bf16 router products on the bf16 matrix cores (E a multiple of 8): d = 1032
+    # and T = 515 leave one partition each with a K tail (8 columns of x, 3
+    # tokens), dense dl from the aux and z losses, a logit bias in the fold
+    "router_bf16_split_ktail": Workload("rx3tail", T=515, d=1032, E=24, k=3, f=64,
+                                        logit_bias={5: 1.25, 20: -0.75}, aux_coef=0.05,
+                                        z_coef=0.02),
     # FP8 forward with ragged T, E, a K tail (d = 144 = 2*64 + 16) and N tails
     # (f = 208), GELU and a shared expert
     "ragged_fp8_gelu_shared": Workload("ragged8", T=1000, d=144, E=6, k=3, f=208, act="gelu",
