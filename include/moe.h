@@ -565,7 +565,9 @@ int moe_combine_bwd(const moe_desc* desc, const void* dy, const void* out, const
  * with respect to l) is their sum divided by tau.
  * dw_r = dl^T x, dx_router = dl W_r (float32; dw_r under the same rule
  * as moe_route's logits: in a bf16 layer with E > 8 and E % 8 == 0 it runs
- * on the bf16 matrix cores over an exact three-term bf16 split of dl).
+ * on the bf16 matrix cores over an exact three-term bf16 split of dl; in such
+ * a layer a dense dl (aux_coef or z_coef nonzero) takes dx_router there too,
+ * over the six largest products of the two operands' terms).
  *   x [T, d] dt, w_r [E, d], scores [T, E], topk_idx, gate, dgate [T, k]   in
  *   y [E] float (from moe_aux_stats; may be NULL when aux_coef == 0)        in
  *   lse [T] float (from moe_route; may be NULL when z_coef == 0)            in

@@ -585,6 +585,7 @@ hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hi
   MOE_CASE(true, false, EPI_STORE, RAG_NONE)
   MOE_CASE(false, false, EPI_STORE, RAG_NONE)
   MOE_CASE(true, true, EPI_STORE_F32, RAG_NONE)
+  MOE_CASE(true, false, EPI_STORE_F32, RAG_NONE)
   MOE_CASE(false, false, EPI_STORE_F32, RAG_NONE)
 #undef MOE_CASE
   return hipErrorInvalidValue;

@@ -55,7 +55,8 @@ hipError_t launch_router_dlogits(const float*, const int32_t*, const float*, con
 hipError_t launch_router_dx_sparse(const float*, const int32_t*, const float*, int, int, int,
                                    int64_t, float*, hipStream_t);
 hipError_t launch_splitk_reduce(const float*, int, int64_t, float*, hipStream_t);
-hipError_t launch_split_bf16x3(const float*, int64_t, int64_t, bf16_t*, int64_t, int64_t, hipStream_t);
+hipError_t launch_split_bf16x3(const float*, int64_t, int64_t, bf16_t*, int64_t, int64_t, hipStream_t,
+                               int nb = 3, int code = 0x24);
 hipError_t launch_fold_bf16x3(const float*, int, int64_t, int64_t, int64_t, int64_t, int64_t,
                               const float*, float*, hipStream_t);
 hipError_t gemm_bf16(const GemmArgs& p, bool akm, bool bkm, int epi, int rag, hipStream_t s);
@@ -262,6 +263,16 @@ int router_x3_fwd_splits(const moe_desc* d) {
     if (s * tiles <= kX3Cus && d->d % (64 * s) == 0) return s;
   return 1;
 }
+// The dense dx_router = dl W_r of the same layers (when the aux or z term
+// makes dl dense), both operands float32: one bf16 product over K' = 6E, the
+// term pairs (hi, hi), (hi, mid), (mid, hi), (hi, lo), (mid, mid), (lo, hi)
+// of dl and W_r laid side by side along K (the pairs dropped are below 2^-24
+// of the product). Whether this path applies.
+bool router_x3_dense_dx(const moe_desc* d) {
+  if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return false;
+  return d->T * 6 * d->E * 2 < (int64_t(1) << 31) && 6 * d->E * d->d * 2 < (int64_t(1) << 31);
+}
+
 int router_x3_bwd_splits(const moe_desc* d) {
   if (d->dtype != MOE_BF16 || d->E <= 8 || d->E % 8) return 0;
   if (d->T * 3 * d->E * 2 >= (int64_t(1) << 31)) return 0;
@@ -350,8 +361,14 @@ size_t ws_bytes_for(const moe_desc* d, int op) {
              (d->dtype == MOE_BF16 ? tail_ws_bytes(kTailCusMax) : 0);
     case MOE_OP_ROUTE_BWD: {
       if (E <= 8) return align256((size_t)router_dw_small_chunks((int)T) * E * d->d * 4);
-      if (const int X = router_x3_bwd_splits(d))
-        return align256((size_t)T * 3 * E * 2) + (size_t)X * 3 * E * d->d * 4;
+      if (const int X = router_x3_bwd_splits(d)) {
+        // dW_r's split and partial products; the dense dx_router's two
+        // operands reuse the region afterwards
+        const size_t dw = align256((size_t)T * 3 * E * 2) + (size_t)X * 3 * E * d->d * 4;
+        const size_t dx = router_x3_dense_dx(d)
+                              ? align256((size_t)T * 6 * E * 2) + (size_t)6 * E * d->d * 2 : 0;
+        return dw > dx ? dw : dx;
+      }
       const int S = route_bwd_splits(d);
       return S > 1 ? align256((size_t)S * E * d->d * 4) : 0;
     }
@@ -1650,6 +1667,34 @@ int moe_route_bwd(const moe_desc* desc, const void* x, const float* w_r, const f
     MOE_TRY(hip_check(launch_splitk_reduce((const float*)ws, S, (int64_t)E * desc->d, dw_r, s),
                       "router dw reduce"));
   }
+  }
+  if ((aux_coef != 0.0f || z_coef != 0.0f) && router_x3_bwd_splits(desc) && router_x3_dense_dx(desc)) {
+    // A' = [dl_hi | dl_hi | dl_mid | dl_hi | dl_mid | dl_lo] (T x 6E) against
+    // B' = [W_hi; W_mid; W_hi; W_lo; W_mid; W_hi] (6E x d, read K-strided);
+    // term codes per block, two bits each from block 0 up
+    const int64_t d = desc->d;
+    bf16_t* a6 = (bf16_t*)ws;
+    bf16_t* b6 = (bf16_t*)((char*)ws + align256((size_t)T * 6 * E * 2));
+    const int code_a = 0 | 0 << 2 | 1 << 4 | 0 << 6 | 1 << 8 | 2 << 10;
+    const int code_b = 0 | 1 << 2 | 0 << 4 | 2 << 6 | 1 << 8 | 0 << 10;
+    {
+      Scope sc(K_ROUTER_SPLIT, s);
+      MOE_TRY(hip_check(launch_split_bf16x3(dlogits, T, E, a6, 6 * E, E, s, 6, code_a),
+                        "router dlogits split (dx)"));
+      MOE_TRY(hip_check(launch_split_bf16x3(w_r, E, d, b6, d, E * d, s, 6, code_b),
+                        "router weight split (dx)"));
+    }
+    GemmArgs q = blank();
+    q.a = opnd(a6, 6 * E, 0, 0);
+    q.b = opnd(b6, d, 0, 0);
+    q.c = dx_router;
+    q.ldc = d;
+    q.G = 1;
+    q.M = T;
+    q.N = d;
+    q.K = 6 * E;
+    Scope sc(K_ROUTER_DX, s);
+    return hip_check(gemm_bf16(q, true, false, EPI_STORE_F32, RAG_NONE, s), "router dx");
   }
   Scope sc(K_ROUTER_DX, s);
   // dx_router = dl W_r; dl is nonzero only on the chosen experts unless a loss term is dense

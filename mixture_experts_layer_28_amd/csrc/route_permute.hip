@@ -1045,10 +1045,12 @@ hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out,
 // arise for router weights or logit gradients). With x in bf16, every product
 // x * hi, x * mid, x * lo is exact in float32, so a bf16 MFMA GEMM over the
 // three terms, accumulated in float32, is a float32 product of x and the
-// float32 operand. Split s of element (r, c) goes to dst[r * ldd + s * sst + c].
+// float32 operand. Block j (0 <= j < nb) of element (r, c) is
+// dst[r * ldd + j * sst + c] and holds term (code >> 2j) & 3 (0 hi, 1 mid,
+// 2 lo): code 0x24 writes hi, mid, lo to blocks 0, 1, 2.
 __global__ __launch_bounds__(256) void split_bf16x3_kernel(const float* __restrict__ src, int64_t rows,
                                                            int64_t cols, bf16_t* __restrict__ dst,
-                                                           int64_t ldd, int64_t sst) {
+                                                           int64_t ldd, int64_t sst, int nb, int code) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4-column group
   const int64_t cq = cols >> 2;
   if (q >= rows * cq) return;
@@ -1066,21 +1068,25 @@ __global__ __launch_bounds__(256) void split_bf16x3_kernel(const float* __restri
     t[1][e] = m;
     t[2][e] = f2bf(r2);
   }
+  uint2 w[3];
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp) {
-    uint2 w;
-    w.x = t[sp][0] | (t[sp][1] << 16);
-    w.y = t[sp][2] | (t[sp][3] << 16);
-    *reinterpret_cast<uint2*>(dst + r * ldd + sp * sst + c) = w;
+    w[sp].x = t[sp][0] | (t[sp][1] << 16);
+    w[sp].y = t[sp][2] | (t[sp][3] << 16);
+  }
+  for (int j = 0; j < nb; ++j) {
+    const int sp = (code >> (2 * j)) & 3;
+    *reinterpret_cast<uint2*>(dst + r * ldd + j * sst + c) = sp == 0 ? w[0] : (sp == 1 ? w[1] : w[2]);
   }
 }
 
 hipError_t launch_split_bf16x3(const float* src, int64_t rows, int64_t cols, bf16_t* dst, int64_t ldd,
-                               int64_t sst, hipStream_t st) {
+                               int64_t sst, hipStream_t st, int nb, int code) {
   const int64_t n = rows * (cols >> 2);
   if (n == 0) return hipSuccess;
+  if (nb < 1 || nb > 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_bf16x3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
-                     rows, cols, dst, ldd, sst);
+                     rows, cols, dst, ldd, sst, nb, code);
   return hipGetLastError();
 }
 
